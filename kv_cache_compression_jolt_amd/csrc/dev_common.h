@@ -1,0 +1,88 @@
+// Device-side helpers shared by the libjolt kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jolt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+// fp32 -> bf16 round to nearest even (finite values)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// ---------------------------------------------------------------- counter RNG
+// SplitMix64 output function (Steele, Lea & Flood 2014), used as a counter hash.
+__host__ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+// key of an item's streams
+__host__ __device__ __forceinline__ uint64_t item_key(uint64_t seed, uint32_t item_id) {
+    return mix64(mix64(seed) + (uint64_t)item_id);
+}
+// +1 / -1 for counter `idx` of stream `stream`: bit 63 of the hash set -> -1
+__host__ __device__ __forceinline__ float rademacher(uint64_t key, uint32_t stream, uint64_t idx) {
+    uint64_t w = mix64(key + ((uint64_t)stream << 56) + idx);
+    return (w >> 63) ? -1.0f : 1.0f;
+}
+
+// ---------------------------------------------------------------- MFMA fragments
+// A 32x32 output tile of v_mfma_f32_32x32x16_bf16 / _32x32x2f32: lane l holds
+// column n = l % 32 and rows m = 8*(j/4) + 4*(l/32) + (j%4), j = 0..15.
+// Operand fragments: lane l holds row (A) / column (B) l % 32 and the 8
+// consecutive K indices k0 + 8*(l/32) + i, i = 0..7 (the same K mapping on
+// both operands, so any hardware K permutation cancels).
+struct FragBF16 { bf16x8 v; };
+struct FragF32 { float v[8]; };
+
+__device__ __forceinline__ FragBF16 load_frag(const uint16_t *p) {
+    FragBF16 f;
+    uint4 raw = *reinterpret_cast<const uint4 *>(p);
+    f.v = __builtin_bit_cast(bf16x8, raw);
+    return f;
+}
+__device__ __forceinline__ FragF32 load_frag(const float *p) {
+    FragF32 f;
+    float4 a = *reinterpret_cast<const float4 *>(p);
+    float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+}
+__device__ __forceinline__ FragBF16 zero_frag(const uint16_t *) { FragBF16 f; f.v = bf16x8{}; return f; }
+__device__ __forceinline__ FragF32 zero_frag(const float *) {
+    FragF32 f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+    return f;
+}
+__device__ __forceinline__ void mfma(const FragBF16 &a, const FragBF16 &b, f32x16 &acc) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma(const FragF32 &a, const FragF32 &b, f32x16 &acc) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ int frag_row(int lane, int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> { typedef FragBF16 Frag; static constexpr int bytes = 2; };
+template <> struct Elem<float> { typedef FragF32 Frag; static constexpr int bytes = 4; };
+
+__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+}  // namespace jolt

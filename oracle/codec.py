@@ -79,7 +79,7 @@ def encode(X: np.ndarray, p: StoredParams, bits: int, seed: int, item_id: int,
     rp = wht.rotate(R, s)
     x32 = rp.astype(np.float32).reshape(-1, quant.GROUP)
     q, sbits = quant.quantize_groups(x32, bits)
-    words = quant.pack_bitplanes(quant.codes_from_q(q, bits), bits)
+    words = quant.pack_codes(quant.codes_from_q(q, bits), bits)
     return Encoded(rt, rf, bits, p, words, sbits, x32)
 
 
@@ -88,7 +88,7 @@ def decode(enc: Encoded, L: int, H: int, T: int, d: int, seed: int, item_id: int
     Xhat = low_rank(enc.params, L, H, T, d, dtype)
     Xt = Xhat
     if enc.bits > 0:
-        u = quant.unpack_bitplanes(enc.words, enc.bits)
+        u = quant.unpack_codes(enc.words, enc.bits)
         q = quant.q_from_codes(u, enc.bits)
         rtil_rot = quant.dequantize_groups(q, enc.scale_bits).reshape(L, H, T, d)
         s = rotation_signs(seed, item_id, d)

@@ -1,4 +1,4 @@
-"""ORACLE (test infrastructure only): b-bit residual quantizer and bit-plane packing.
+"""ORACLE (test infrastructure only): b-bit residual quantizer and group bit-stream packing.
 
 Pages: "a rotated low-bit quantizer captures the truncation residual" (landing
 page abstract); the residual bit-width b is allocated per group together with
@@ -14,10 +14,12 @@ are reproducible bit for bit:
   u      = q + 2^(b-1)                             (code, in [1, 2^b - 1])
   decode = q * scale
 
-Packing: per group and bit-plane p < b, one little-endian uint64 whose bit j
-is bit p of u_j; the words of group g sit at byte 8 * (g * b + p).  Groups run
-over (layer, head, token, feature / 64) in row-major order; the bf16 scales form
-an array in the same order.
+Packing (the pages fix no layout): each group is one little-endian bit stream
+of 64 b bits = 8 b bytes, element j's code in stream bits [b j, b j + b), bit k
+of the stream being bit (k mod 8) of byte k / 8.  Group g starts at byte 8 b g.
+Groups run over (layer, head, token, feature / 64) in row-major order; the bf16
+scales form an array in the same order.  The same bytes read as b
+little-endian uint64 words per group are the "codes" array.
 """
 from __future__ import annotations
 
@@ -86,27 +88,22 @@ def q_from_codes(u: np.ndarray, bits: int) -> np.ndarray:
     return u.astype(np.int64) - (1 << (bits - 1))
 
 
-def pack_bitplanes(u: np.ndarray, bits: int) -> np.ndarray:
-    """u: (G, 64) codes -> (G, bits) uint64 words, word p bit j = bit p of u[j]."""
+def pack_codes(u: np.ndarray, bits: int) -> np.ndarray:
+    """u: (G, 64) codes -> (G, bits) uint64 words of the group bit stream."""
     u = np.asarray(u, dtype=np.uint64)
     G = u.shape[0]
-    words = np.zeros((G, bits), dtype=np.uint64)
-    shifts = np.arange(GROUP, dtype=np.uint64)
-    for p in range(bits):
-        plane = (u >> np.uint64(p)) & np.uint64(1)
-        words[:, p] = np.bitwise_or.reduce(plane << shifts[None, :], axis=1)
-    return words
+    planes = ((u[:, :, None] >> np.arange(bits, dtype=np.uint64)[None, None, :]) & np.uint64(1))
+    stream = planes.reshape(G, GROUP * bits).astype(np.uint8)       # stream bit k = element k // b, bit k % b
+    by = np.packbits(stream, axis=1, bitorder="little")              # (G, 8 b) bytes
+    return by.view("<u8").reshape(G, bits).astype(np.uint64)
 
 
-def unpack_bitplanes(words: np.ndarray, bits: int) -> np.ndarray:
-    words = np.asarray(words, dtype=np.uint64)
+def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
+    words = np.ascontiguousarray(np.asarray(words, dtype=np.uint64)).astype("<u8")
     G = words.shape[0]
-    u = np.zeros((G, GROUP), dtype=np.uint64)
-    shifts = np.arange(GROUP, dtype=np.uint64)
-    for p in range(bits):
-        plane = (words[:, p:p + 1] >> shifts[None, :]) & np.uint64(1)
-        u |= plane << np.uint64(p)
-    return u
+    by = words.view(np.uint8).reshape(G, 8 * bits)
+    stream = np.unpackbits(by, axis=1, bitorder="little").reshape(G, GROUP, bits).astype(np.uint64)
+    return np.sum(stream << np.arange(bits, dtype=np.uint64)[None, None, :], axis=2).astype(np.uint64)
 
 
 def words_to_bytes(words: np.ndarray) -> bytes:

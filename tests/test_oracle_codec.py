@@ -43,7 +43,7 @@ def test_closed_loop_identities(item, rt, rf, b):
     s = rng.rotation_signs(it.seed, it.item_id, d)
     r_rot = wht.rotate(X - Xhat, s).reshape(-1, 64)
     scale = quant.bf16_bits_to_f32(enc.scale_bits).astype(np.float64)
-    deq = quant.dequantize_groups(quant.q_from_codes(quant.unpack_bitplanes(enc.words, b), b),
+    deq = quant.dequantize_groups(quant.q_from_codes(quant.unpack_codes(enc.words, b), b),
                                   enc.scale_bits)
     # per rotated coordinate: |r' - q s| <= s / 2 (+ the fp32 rounding of r')
     assert np.all(np.abs(r_rot - deq) <= scale[:, None] / 2 + 2.0 ** -23 * np.abs(r_rot))

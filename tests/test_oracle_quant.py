@@ -17,12 +17,16 @@ def test_worked_examples(golden_dir):
         q, s = quant.quantize_groups(x, b)
         assert q[0].tolist() == ex["q"], ex["note"]
         assert int(s[0]) == int(ex["scale_bf16"], 16), ex["note"]
-        w = quant.pack_bitplanes(quant.codes_from_q(q, b), b)
+        w = quant.pack_codes(quant.codes_from_q(q, b), b)
         assert ["0x%016x" % int(v) for v in w[0]] == ex["words"], ex["note"]
-        # bytes: word p of group g at byte offset 8 * (g * b + p), little endian
+        # bytes: word p of the group at byte offset 8 p, little endian
         raw = quant.words_to_bytes(w)
         for p, hw in enumerate(ex["words"]):
             assert raw[8 * p:8 * p + 8] == int(hw, 16).to_bytes(8, "little")
+        # element j's code sits in stream bits [b j, b j + b)
+        stream = int.from_bytes(raw, "little")
+        for j, qj in enumerate(ex["q"]):
+            assert (stream >> (b * j)) & ((1 << b) - 1) == qj + (1 << (b - 1))
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
@@ -41,7 +45,7 @@ def test_error_bound_range_symmetry(bits):
     assert np.array_equal(q2, -q) and np.array_equal(s2, s)
     u = quant.codes_from_q(q, bits)
     assert u.min() >= 1 and u.max() <= (1 << bits) - 1
-    assert np.array_equal(quant.unpack_bitplanes(quant.pack_bitplanes(u, bits), bits), u)
+    assert np.array_equal(quant.unpack_codes(quant.pack_codes(u, bits), bits), u)
 
 
 def test_bf16_rounding_half_even():
