@@ -1,0 +1,25 @@
+// Host-side internals shared by api.cpp and plan.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "../../include/libjolt.h"
+#include "dev_common.h"
+#include "payload.h"
+
+struct jolt_handle_s;
+
+namespace jolt {
+
+jolt_status fail(jolt_handle h, jolt_status s, const char *fmt, ...);
+jolt_status hip_fail(jolt_handle h, hipError_t e, const char *where);
+void clear_err(jolt_handle h);
+jolt_status check_item(jolt_handle h, const jolt_item &it);
+jolt_status check_alloc(jolt_handle h, const jolt_item &it, const jolt_alloc &a);
+jolt_status check_items_uniform(jolt_handle h, const jolt_item *items, int n);
+
+// plan.cpp
+jolt_status check_config(jolt_handle h, const jolt_config &cfg, const jolt_item *items, int n);
+jolt_status store_params(jolt_handle h, const PlanLayout &pl, const jolt_item *items, int n, const jolt_alloc *alloc,
+                         const void *plan_ws, void *const *payload_dev, hipStream_t st);
+
+}  // namespace jolt

@@ -61,6 +61,21 @@ __device__ __forceinline__ FragF32 load_frag(const float *p) {
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
     return f;
 }
+// element-wise load of min(8, count) values (count may be <= 0), zero fill; any alignment
+__device__ __forceinline__ FragBF16 load_frag_n(const uint16_t *p, int count) {
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = (i < count) ? p[i] : (uint16_t)0;
+    FragBF16 f;
+    f.v = __builtin_bit_cast(bf16x8, e);
+    return f;
+}
+__device__ __forceinline__ FragF32 load_frag_n(const float *p, int count) {
+    FragF32 f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = (i < count) ? p[i] : 0.f;
+    return f;
+}
 __device__ __forceinline__ FragBF16 zero_frag(const uint16_t *) { FragBF16 f; f.v = bf16x8{}; return f; }
 __device__ __forceinline__ FragF32 zero_frag(const float *) {
     FragF32 f;

@@ -1,0 +1,639 @@
+// Residual codec kernels for gfx950: the fused residual -> rotate -> quantize ->
+// pack encoder, the fused decoder, W~ construction, and the plain per-row /
+// per-group kernels behind the test hooks.
+//
+// Method ("A JoLT for the KV cache", landing page abstract; author page
+// abstract): the truncation residual of the partial Tucker approximation is
+// rotated by a Johnson-Lindenstrauss rotation and quantized to a few bits.
+// Here the rotation of a (layer, head, token) row of d features is
+// r' = (1/sqrt d) H_d (s o r) (Sylvester Hadamard, seeded signs s); each group
+// of 64 rotated values gets a bf16 absmax scale and b-bit symmetric codes,
+// packed as one little-endian bit stream per group (element j in bits
+// [b j, b j + b)).  The residual is taken against the reconstruction the
+// decoder forms from the stored parameters: X^_lh = U~_t W~_lh.
+//
+// Register layout of the fused kernels.  A wave owns 32 tokens of one (layer,
+// head).  X^ is an MFMA product D[f][t] = sum_k W~t[f][k] U~_t[t][k]
+// (v_mfma_f32_32x32x16_bf16, or 32x32x2f32 for fp32 caches); lane l then
+// holds token l % 32 and, for each 32-feature block mf, features
+// f = 32 mf + 8 (j / 4) + 4 (l / 32) + (j % 4), j = 0..15.  Six of the
+// log2(d) butterfly stages are in-register; the stage over feature bit 2
+// (the lane half) uses v_permlane32_swap on register pairs that differ in the
+// top feature bit, which leaves each lane holding one whole 64-group
+// (d = 128) or half of it (d = 64).  Group absmax and packing are then
+// in-lane, and each lane stores its group's codes contiguously.
+#include "dev_common.h"
+#include "jolt_internal.h"
+
+namespace jolt {
+
+// ------------------------------------------------------------------ helpers
+__device__ __forceinline__ uint32_t pack_lowbytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    // [a.b0, b.b0, c.b0, d.b0]
+    uint32_t p01 = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+    uint32_t p23 = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+}
+
+// swap lanes 32..63 of x with lanes 0..31 of y
+__device__ __forceinline__ void swap_halves(float &x, float &y) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+// Pack NE codes (magic-float bit patterns whose low byte is the code) of
+// width BITS into the little-endian stream words w[BITS * NE / 32].
+template <int BITS, int NE>
+__device__ __forceinline__ void pack_codes(const uint32_t *t, uint32_t *w) {
+    constexpr int NW = BITS * NE / 32;
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) w[k] = pack_lowbytes(t[4 * k], t[4 * k + 1], t[4 * k + 2], t[4 * k + 3]);
+    } else if constexpr (BITS == 4) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            const uint32_t *s = t + 8 * k;
+            uint32_t ev = pack_lowbytes(s[0], s[2], s[4], s[6]);
+            uint32_t od = pack_lowbytes(s[1], s[3], s[5], s[7]);
+            w[k] = ev | (od << 4);
+        }
+    } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            const uint32_t *s = t + 16 * k;
+            uint32_t b0 = pack_lowbytes(s[0], s[4], s[8], s[12]);
+            uint32_t b1 = pack_lowbytes(s[1], s[5], s[9], s[13]);
+            uint32_t b2 = pack_lowbytes(s[2], s[6], s[10], s[14]);
+            uint32_t b3 = pack_lowbytes(s[3], s[7], s[11], s[15]);
+            w[k] = b0 | (b1 << 2) | (b2 << 4) | (b3 << 6);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) w[k] = 0;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const uint32_t u = t[e] & ((1u << BITS) - 1u);
+            const int pos = BITS * e;
+            w[pos >> 5] |= u << (pos & 31);
+            if ((pos & 31) + BITS > 32) w[(pos >> 5) + 1] |= u >> (32 - (pos & 31));
+        }
+    }
+}
+
+// Unpack NE codes of width BITS from w into floats q = u - 2^(BITS-1).
+template <int BITS, int NE>
+__device__ __forceinline__ void unpack_codes(const uint32_t *w, float *u) {
+    constexpr int NW = BITS * NE / 32;
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u[4 * k + i] = (float)((w[k] >> (8 * i)) & 0xFFu);
+    } else if constexpr (BITS == 4) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = (w[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u[8 * k + 2 * i] = (float)((lo >> (8 * i)) & 0xFFu);
+                u[8 * k + 2 * i + 1] = (float)((hi >> (8 * i)) & 0xFFu);
+            }
+        }
+    } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t v = (w[k] >> (2 * r)) & 0x03030303u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[16 * k + 4 * i + r] = (float)((v >> (8 * i)) & 0xFFu);
+            }
+    } else {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int pos = BITS * e;
+            uint32_t v = w[pos >> 5] >> (pos & 31);
+            if ((pos & 31) + BITS > 32) v |= w[(pos >> 5) + 1] << (32 - (pos & 31));
+            u[e] = (float)(v & ((1u << BITS) - 1u));
+        }
+    }
+}
+
+template <typename T> struct Store;
+template <> struct Store<uint16_t> {
+    // round to bf16 (RNE) pairs
+    static __device__ __forceinline__ void put4(uint8_t *dst, float a, float b, float c, float d) {
+        uint2 v;
+        v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+        v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+        *reinterpret_cast<uint2 *>(dst) = v;
+    }
+    static __device__ __forceinline__ void get4(const uint8_t *src, float *o) {
+        uint2 v = *reinterpret_cast<const uint2 *>(src);
+        o[0] = __uint_as_float(v.x << 16);
+        o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        o[2] = __uint_as_float(v.y << 16);
+        o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    }
+    static constexpr uint32_t kSignBit = 0x8000u;
+    static constexpr int kPerDword = 2;
+};
+template <> struct Store<float> {
+    static __device__ __forceinline__ void put4(uint8_t *dst, float a, float b, float c, float d) {
+        uint2 *p = reinterpret_cast<uint2 *>(dst);
+        p[0] = make_uint2(__float_as_uint(a), __float_as_uint(b));
+        p[1] = make_uint2(__float_as_uint(c), __float_as_uint(d));
+    }
+    static __device__ __forceinline__ void get4(const uint8_t *src, float *o) {
+        const uint2 *p = reinterpret_cast<const uint2 *>(src);
+        uint2 a = p[0], b = p[1];
+        o[0] = __uint_as_float(a.x); o[1] = __uint_as_float(a.y);
+        o[2] = __uint_as_float(b.x); o[3] = __uint_as_float(b.y);
+    }
+    static constexpr uint32_t kSignBit = 0x80000000u;
+    static constexpr int kPerDword = 1;
+};
+
+// XOR mask that flips the signs of the features held by a 16-byte chunk
+template <typename T>
+__device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t *sign_bits, int chunk) {
+    constexpr int per = 16 / sizeof(T);          // features per chunk
+    uint32_t m[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        const int f = chunk * per + i;
+        const uint32_t s = (sign_bits[f >> 5] >> (f & 31)) & 1u;
+        const int dw = i / Store<T>::kPerDword;
+        const int sh = (i % Store<T>::kPerDword) * 16;
+        m[dw] |= (s * Store<T>::kSignBit) << sh;
+    }
+    return make_uint4(m[0], m[1], m[2], m[3]);
+}
+
+// ------------------------------------------------------------------ X^ via MFMA
+// acc[mf] += sum_k wt[f][k] * ut[t][k], f = 32 mf + row, t = token of the lane
+template <typename T, int NMF>
+__device__ __forceinline__ void xhat_mfma(const T *wt, int rtp, const T *ut, int rt, int tok, bool tv,
+                                          int lane, f32x16 *acc) {
+    const int ln = lane & 31, h = lane >> 5;
+    const bool vec = (rt & 7) == 0;        // rows of U~_t are 16-byte aligned
+    for (int k0 = 0; k0 < rt; k0 += 16) {
+        const int kk = k0 + 8 * h;
+        typename Elem<T>::Frag b = !(tv && kk < rt) ? zero_frag(ut)
+                                   : vec ? load_frag(ut + (size_t)tok * rt + kk)
+                                         : load_frag_n(ut + (size_t)tok * rt + kk, rt - kk);
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf) {
+            typename Elem<T>::Frag a = load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk);
+            mfma(a, b, acc[mf]);
+        }
+    }
+}
+
+template <typename T, int D>
+struct Tile {
+    static constexpr int RB = D * (int)sizeof(T);   // row bytes
+    static constexpr int RS = RB + 8;              // LDS row stride (8-byte aligned rows)
+    static constexpr int CPR = RB / 16;            // 16-byte chunks per row
+    static constexpr int NMF = D / 32;
+    static constexpr int NE = 16 * NMF / 2 * 2 / (D == 128 ? 1 : 1);  // values per lane
+};
+
+// ------------------------------------------------------------------ fused encoder
+template <typename T, int D, int BITS>
+__global__ __launch_bounds__(256) void k_encode(CodecBatch batch) {
+    typedef Tile<T, D> TL;
+    constexpr int NMF = TL::NMF;
+    constexpr int HALF = NMF / 2;
+    constexpr int NE = 32 * NMF / 2 * 2 / 2;       // values per lane: 64 (d=128) or 32 (d=64)
+    static_assert(NE == 16 * NMF, "layout");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * TL::RS];
+    const CodecItem &it = batch.it[blockIdx.z];
+    const int lh = blockIdx.y;
+    if (lh >= it.LH || (int)blockIdx.x * 128 >= it.T) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ln = lane & 31, h = lane >> 5;
+    const int t0 = blockIdx.x * 128 + wave * 32;
+    const int tok = t0 + ln;
+    const bool tv = tok < it.T;
+    uint8_t *buf = lds[wave];
+
+    // stage the wave's 32 rows of X into LDS with the rotation signs applied
+    {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T) * TL::RB;
+        const uint4 sm = chunk_sign_mask<T>(it.sign_bits, lane % TL::CPR);
+#pragma unroll
+        for (int i = 0; i < 32 * TL::CPR / 64; ++i) {
+            const int c = i * 64 + lane, row = c / TL::CPR, ch = c % TL::CPR;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (t0 + row < it.T) v = *reinterpret_cast<const uint4 *>(src + (size_t)(t0 + row) * TL::RB + ch * 16);
+            v.x ^= sm.x; v.y ^= sm.y; v.z ^= sm.z; v.w ^= sm.w;
+            uint2 *d = reinterpret_cast<uint2 *>(buf + row * TL::RS + ch * 16);
+            d[0] = make_uint2(v.x, v.y);
+            d[1] = make_uint2(v.z, v.w);
+        }
+    }
+
+    // s o X^ (signs are folded into wt)
+    f32x16 acc[NMF];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
+    xhat_mfma<T, NMF>(reinterpret_cast<const T *>(it.wt) + (size_t)lh * D * it.rtp, it.rtp,
+                      reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+    __syncthreads();
+
+    // residual in the MFMA layout
+    float r[NMF][16];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            float xv[4];
+            Store<T>::get4(buf + ln * TL::RS + (32 * mf + 8 * jb + 4 * h) * (int)sizeof(T), xv);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) r[mf][4 * jb + c] = xv[c] - acc[mf][4 * jb + c];
+        }
+
+    // in-register Hadamard stages: feature bits 0, 1, 3, 4 (j bits) and the mf bits
+#pragma unroll
+    for (int jbit = 1; jbit < 16; jbit <<= 1)
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (!(j & jbit)) {
+                    const float a = r[mf][j], b = r[mf][j | jbit];
+                    r[mf][j] = a + b;
+                    r[mf][j | jbit] = a - b;
+                }
+#pragma unroll
+    for (int mbit = 1; mbit < NMF; mbit <<= 1)
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf)
+            if (!(mf & mbit))
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float a = r[mf][j], b = r[mf | mbit][j];
+                    r[mf][j] = a + b;
+                    r[mf | mbit][j] = a - b;
+                }
+
+    // feature bit 2 across lane halves; afterwards the lane half is the top
+    // feature bit and y[e] holds in-group element e (+ 32 h for d = 64)
+    const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
+    float y[NE];
+#pragma unroll
+    for (int mp = 0; mp < HALF; ++mp)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            float u = r[mp][j], w = r[mp + HALF][j];
+            swap_halves(u, w);
+            const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
+            y[e] = (u + w) * isd;
+            y[e + 4] = (u - w) * isd;
+        }
+
+    // group absmax, bf16 scale, codes
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) amax = fmaxf(amax, fabsf(y[e]));
+    if (D == 64) amax = fmaxf(amax, __shfl_xor(amax, 32));
+    constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+    const float s32 = amax / qmax;
+    const uint16_t sbits = f32_to_bf16(s32);
+    const float scale = bf16_to_f32(sbits);
+    const float inv = (scale == 0.f) ? 0.f : 1.0f / scale;
+    constexpr float magic = 12582912.0f + (float)(1 << (BITS - 1));
+    uint32_t tq[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        float v = y[e] * inv;
+        v = fminf(fmaxf(v, -qmax), qmax);
+        tq[e] = __float_as_uint(v + magic);
+    }
+    constexpr int NW = BITS * NE / 32;
+    uint32_t w[NW];
+    pack_codes<BITS, NE>(tq, w);
+    if (tv) {
+        const size_t row = (size_t)lh * it.T + tok;
+        const size_t grp = row * (D / 64) + (D == 128 ? h : 0);
+        uint8_t *dst = it.codes + grp * 8 * BITS + (D == 64 ? h * 4 * BITS : 0);
+        if constexpr (NW % 2 == 0) {
+#pragma unroll
+            for (int k = 0; k < NW; k += 2) *reinterpret_cast<uint2 *>(dst + 4 * k) = make_uint2(w[k], w[k + 1]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NW; ++k) *reinterpret_cast<uint32_t *>(dst + 4 * k) = w[k];
+        }
+        if (D == 128 || h == 0) it.scales[grp] = sbits;
+    }
+}
+
+// ------------------------------------------------------------------ fused decoder
+template <typename T, int D, int BITS>
+__global__ __launch_bounds__(256) void k_decode(CodecBatch batch) {
+    typedef Tile<T, D> TL;
+    constexpr int NMF = TL::NMF;
+    constexpr int HALF = NMF / 2;
+    constexpr int NE = 16 * NMF;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * TL::RS];
+    const CodecItem &it = batch.it[blockIdx.z];
+    const int lh = blockIdx.y;
+    if (lh >= it.LH || (int)blockIdx.x * 128 >= it.T) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ln = lane & 31, h = lane >> 5;
+    const int t0 = blockIdx.x * 128 + wave * 32;
+    const int tok = t0 + ln;
+    const bool tv = tok < it.T;
+    uint8_t *buf = lds[wave];
+
+    f32x16 acc[NMF];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
+    xhat_mfma<T, NMF>(reinterpret_cast<const T *>(it.wt) + (size_t)lh * D * it.rtp, it.rtp,
+                      reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+
+    float r[NMF][16];
+    if constexpr (BITS > 0) {
+        // codes of the lane's group (or half group) -> scaled values
+        const size_t row = (size_t)lh * it.T + (tv ? tok : 0);
+        const size_t grp = row * (D / 64) + (D == 128 ? h : 0);
+        constexpr int NW = BITS * NE / 32;
+        uint32_t w[NW];
+        const uint8_t *src = it.codes + grp * 8 * BITS + (D == 64 ? h * 4 * BITS : 0);
+        if constexpr (NW % 2 == 0) {
+#pragma unroll
+            for (int k = 0; k < NW; k += 2) {
+                uint2 v = *reinterpret_cast<const uint2 *>(src + 4 * k);
+                w[k] = v.x; w[k + 1] = v.y;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NW; ++k) w[k] = *reinterpret_cast<const uint32_t *>(src + 4 * k);
+        }
+        const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
+        const float sc = bf16_to_f32(it.scales[grp]) * isd;
+        const float off = (float)(1 << (BITS - 1));
+        float y[NE];
+        unpack_codes<BITS, NE>(w, y);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) y[e] = fmaf(y[e], sc, -off * sc);
+        // back to the register pairs of the swap stage: y[e], e = (j&3) + 4 sd + 8 (j>>2) + 32 mp
+        // in-register stages over the in-group bits (incl. feature bit 2 = sd)
+#pragma unroll
+        for (int bit = 1; bit < NE; bit <<= 1)
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                if (!(e & bit)) {
+                    const float a = y[e], b = y[e | bit];
+                    y[e] = a + b;
+                    y[e | bit] = a - b;
+                }
+        // top feature bit across lane halves; lane half becomes feature bit 2 again
+#pragma unroll
+        for (int mp = 0; mp < HALF; ++mp)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
+                float u = y[e], v = y[e + 4];
+                swap_halves(u, v);
+                r[mp][j] = u + v;
+                r[mp + HALF][j] = u - v;
+            }
+    } else {
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) r[mf][j] = 0.f;
+    }
+
+    // s o X~ = s o X^ + rotated-back residual; stage rows in LDS, store with signs
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const int j = 4 * jb;
+            Store<T>::put4(buf + ln * TL::RS + (32 * mf + 8 * jb + 4 * h) * (int)sizeof(T),
+                           r[mf][j] + acc[mf][j], r[mf][j + 1] + acc[mf][j + 1],
+                           r[mf][j + 2] + acc[mf][j + 2], r[mf][j + 3] + acc[mf][j + 3]);
+        }
+    __syncthreads();
+    {
+        uint8_t *dst = reinterpret_cast<uint8_t *>(it.out) + ((size_t)lh * it.T) * TL::RB;
+        const uint4 sm = chunk_sign_mask<T>(it.sign_bits, lane % TL::CPR);
+#pragma unroll
+        for (int i = 0; i < 32 * TL::CPR / 64; ++i) {
+            const int c = i * 64 + lane, row = c / TL::CPR, ch = c % TL::CPR;
+            const uint2 *s = reinterpret_cast<const uint2 *>(buf + row * TL::RS + ch * 16);
+            uint2 a = s[0], b = s[1];
+            uint4 v = make_uint4(a.x ^ sm.x, a.y ^ sm.y, b.x ^ sm.z, b.y ^ sm.w);
+            if (t0 + row < it.T) *reinterpret_cast<uint4 *>(dst + (size_t)(t0 + row) * TL::RB + ch * 16) = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ W~ construction
+// wt[lh][f][k] = s_f * round(sum_j core[lh][k][j] * uf[f][j]) for k < rt, 0 for rt <= k < rtp.
+// One wave per (32 features, 32 ranks) tile: D[m = f][n = k] with K = j.
+template <typename T>
+__global__ __launch_bounds__(64) void k_build_wt(WtBatch batch, int D) {
+    const WtItem &it = batch.it[blockIdx.z / 1];
+    const int lh = blockIdx.y;
+    const int f0 = (blockIdx.x % (D / 32)) * 32, k0 = (blockIdx.x / (D / 32)) * 32;
+    if (lh >= it.LH || k0 >= it.rtp) return;
+    const int lane = threadIdx.x, ln = lane & 31, h = lane >> 5;
+    const T *uf = reinterpret_cast<const T *>(it.uf);
+    const T *core = reinterpret_cast<const T *>(it.core) + (size_t)lh * it.rt * it.rf;
+    f32x16 acc = f32x16{};
+    const int kr = k0 + ln;
+    for (int j0 = 0; j0 < it.rf; j0 += 16) {
+        const int jj = j0 + 8 * h;
+        typename Elem<T>::Frag a = load_frag_n(uf + (size_t)(f0 + ln) * it.rf + jj, it.rf - jj);
+        typename Elem<T>::Frag b = (kr < it.rt) ? load_frag_n(core + (size_t)kr * it.rf + jj, it.rf - jj)
+                                                : zero_frag(core);
+        mfma(a, b, acc);
+    }
+    T *wt = reinterpret_cast<T *>(it.wt) + (size_t)lh * D * it.rtp;
+    if (kr < it.rtp) {
+#pragma unroll
+        for (int jr = 0; jr < 16; ++jr) {
+            const int f = f0 + frag_row(lane, jr);
+            const bool neg = (it.sign_bits[f >> 5] >> (f & 31)) & 1u;
+            float v = (kr < it.rt) ? acc[jr] : 0.f;
+            if (sizeof(T) == 2) {
+                uint16_t b = f32_to_bf16(v);
+                if (neg) b ^= 0x8000u;
+                reinterpret_cast<uint16_t *>(wt)[(size_t)f * it.rtp + kr] = b;
+            } else {
+                reinterpret_cast<float *>(wt)[(size_t)f * it.rtp + kr] = neg ? -v : v;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ test-hook kernels
+// One thread per row: plain Hadamard butterflies.
+__global__ void k_rotate_rows(const float *in, float *out, int64_t rows, int d, uint32_t s0, uint32_t s1,
+                              uint32_t s2, uint32_t s3, int inverse) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const uint32_t sb[4] = {s0, s1, s2, s3};
+    float v[128];
+    for (int f = 0; f < d; ++f) {
+        const float x = in[r * d + f];
+        const bool neg = (sb[f >> 5] >> (f & 31)) & 1u;
+        v[f] = (!inverse && neg) ? -x : x;
+    }
+    for (int hs = 1; hs < d; hs <<= 1)
+        for (int i = 0; i < d; ++i)
+            if (!(i & hs)) {
+                const float a = v[i], b = v[i | hs];
+                v[i] = a + b;
+                v[i | hs] = a - b;
+            }
+    const float isd = 1.0f / sqrtf((float)d);
+    for (int f = 0; f < d; ++f) {
+        const bool neg = (sb[f >> 5] >> (f & 31)) & 1u;
+        const float x = v[f] * isd;
+        out[r * d + f] = (inverse && neg) ? -x : x;
+    }
+}
+
+// One thread per 64-group: the quantizer definition step by step.
+__global__ void k_quant_pack_groups(const float *x, int64_t groups, int bits, uint8_t *codes, uint16_t *scales) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= groups) return;
+    const float *p = x + g * 64;
+    float amax = 0.f;
+    for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(p[j]));
+    const float qmax = (float)((1 << (bits - 1)) - 1);
+    const float s32 = amax / qmax;
+    const uint16_t sb = f32_to_bf16(s32);
+    const float scale = bf16_to_f32(sb);
+    const float inv = 1.0f / scale;
+    uint64_t st[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < 64; ++j) {
+        float q = 0.f;
+        if (scale != 0.f) {
+            const float yv = p[j] * inv;
+            q = fminf(fmaxf(rintf(yv), -qmax), qmax);
+        }
+        const uint64_t u = (uint64_t)((int)q + (1 << (bits - 1)));
+        const int pos = bits * j;
+        st[pos >> 6] |= u << (pos & 63);
+        if ((pos & 63) + bits > 64) st[(pos >> 6) + 1] |= u >> (64 - (pos & 63));
+    }
+    uint64_t *dst = reinterpret_cast<uint64_t *>(codes + g * 8 * bits);
+    for (int k = 0; k < bits; ++k) dst[k] = st[k];
+    scales[g] = sb;
+}
+
+__global__ void k_unpack_dequant_groups(const uint8_t *codes, const uint16_t *scales, int64_t groups, int bits,
+                                        float *out) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= groups) return;
+    const uint64_t *src = reinterpret_cast<const uint64_t *>(codes + g * 8 * bits);
+    uint64_t st[9];
+    for (int k = 0; k < bits; ++k) st[k] = src[k];
+    st[bits] = 0;
+    const float scale = bf16_to_f32(scales[g]);
+    for (int j = 0; j < 64; ++j) {
+        const int pos = bits * j;
+        uint64_t v = st[pos >> 6] >> (pos & 63);
+        if ((pos & 63) + bits > 64) v |= st[(pos >> 6) + 1] << (64 - (pos & 63));
+        const int u = (int)(v & ((1u << bits) - 1u));
+        out[g * 64 + j] = (float)(u - (1 << (bits - 1))) * scale;
+    }
+}
+
+__global__ void k_rademacher_fill(uint64_t key, uint32_t stream, uint64_t first, int64_t count, float *out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    out[i] = rademacher(key, stream, first + (uint64_t)i);
+}
+
+// ------------------------------------------------------------------ launchers
+template <typename T, int D>
+static hipError_t encode_bits(const CodecBatch &b, int bits, dim3 grid, hipStream_t s) {
+    switch (bits) {
+        case 2: hipLaunchKernelGGL((k_encode<T, D, 2>), grid, dim3(256), 0, s, b); break;
+        case 3: hipLaunchKernelGGL((k_encode<T, D, 3>), grid, dim3(256), 0, s, b); break;
+        case 4: hipLaunchKernelGGL((k_encode<T, D, 4>), grid, dim3(256), 0, s, b); break;
+        case 5: hipLaunchKernelGGL((k_encode<T, D, 5>), grid, dim3(256), 0, s, b); break;
+        case 6: hipLaunchKernelGGL((k_encode<T, D, 6>), grid, dim3(256), 0, s, b); break;
+        case 7: hipLaunchKernelGGL((k_encode<T, D, 7>), grid, dim3(256), 0, s, b); break;
+        case 8: hipLaunchKernelGGL((k_encode<T, D, 8>), grid, dim3(256), 0, s, b); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+template <typename T, int D>
+static hipError_t decode_bits(const CodecBatch &b, int bits, dim3 grid, hipStream_t s) {
+    switch (bits) {
+        case 0: hipLaunchKernelGGL((k_decode<T, D, 0>), grid, dim3(256), 0, s, b); break;
+        case 2: hipLaunchKernelGGL((k_decode<T, D, 2>), grid, dim3(256), 0, s, b); break;
+        case 3: hipLaunchKernelGGL((k_decode<T, D, 3>), grid, dim3(256), 0, s, b); break;
+        case 4: hipLaunchKernelGGL((k_decode<T, D, 4>), grid, dim3(256), 0, s, b); break;
+        case 5: hipLaunchKernelGGL((k_decode<T, D, 5>), grid, dim3(256), 0, s, b); break;
+        case 6: hipLaunchKernelGGL((k_decode<T, D, 6>), grid, dim3(256), 0, s, b); break;
+        case 7: hipLaunchKernelGGL((k_decode<T, D, 7>), grid, dim3(256), 0, s, b); break;
+        case 8: hipLaunchKernelGGL((k_decode<T, D, 8>), grid, dim3(256), 0, s, b); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_encode(const CodecBatch &b, int dtype, int D, int bits, int maxT, int maxLH, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    dim3 grid((maxT + 127) / 128, maxLH, b.n);
+    if (dtype == JOLT_BF16) return D == 128 ? encode_bits<uint16_t, 128>(b, bits, grid, s)
+                                            : encode_bits<uint16_t, 64>(b, bits, grid, s);
+    return D == 128 ? encode_bits<float, 128>(b, bits, grid, s) : encode_bits<float, 64>(b, bits, grid, s);
+}
+hipError_t launch_decode(const CodecBatch &b, int dtype, int D, int bits, int maxT, int maxLH, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    dim3 grid((maxT + 127) / 128, maxLH, b.n);
+    if (dtype == JOLT_BF16) return D == 128 ? decode_bits<uint16_t, 128>(b, bits, grid, s)
+                                            : decode_bits<uint16_t, 64>(b, bits, grid, s);
+    return D == 128 ? decode_bits<float, 128>(b, bits, grid, s) : decode_bits<float, 64>(b, bits, grid, s);
+}
+hipError_t launch_build_wt(const WtBatch &b, int dtype, int D, int maxLH, int maxRtp, hipStream_t s) {
+    if (b.n <= 0 || maxRtp <= 0) return hipSuccess;
+    dim3 grid((D / 32) * ((maxRtp + 31) / 32), maxLH, b.n);
+    if (dtype == JOLT_BF16) hipLaunchKernelGGL(k_build_wt<uint16_t>, grid, dim3(64), 0, s, b, D);
+    else hipLaunchKernelGGL(k_build_wt<float>, grid, dim3(64), 0, s, b, D);
+    return hipGetLastError();
+}
+hipError_t launch_rotate(const float *in, float *out, int64_t rows, int d, const uint32_t *sb, int inverse,
+                         hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rotate_rows, dim3((unsigned)((rows + 127) / 128)), dim3(128), 0, s, in, out, rows, d,
+                       sb[0], sb[1], sb[2], sb[3], inverse);
+    return hipGetLastError();
+}
+hipError_t launch_quantize_pack(const float *rot, int64_t rows, int d, int bits, uint8_t *codes, uint16_t *scales,
+                                hipStream_t s) {
+    const int64_t groups = rows * d / 64;
+    if (groups <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quant_pack_groups, dim3((unsigned)((groups + 127) / 128)), dim3(128), 0, s, rot, groups,
+                       bits, codes, scales);
+    return hipGetLastError();
+}
+hipError_t launch_unpack_dequant(const uint8_t *codes, const uint16_t *scales, int64_t rows, int d, int bits,
+                                 float *out, hipStream_t s) {
+    const int64_t groups = rows * d / 64;
+    if (groups <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_unpack_dequant_groups, dim3((unsigned)((groups + 127) / 128)), dim3(128), 0, s, codes,
+                       scales, groups, bits, out);
+    return hipGetLastError();
+}
+hipError_t launch_rademacher(uint64_t key, uint32_t stream, uint64_t first, int64_t count, float *out,
+                             hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rademacher_fill, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, key, stream,
+                       first, count, out);
+    return hipGetLastError();
+}
+
+}  // namespace jolt

@@ -1,0 +1,706 @@
+// Plan-stage kernels for gfx950: the passes over the cache tensor (MFMA), the
+// small dense fp32 linear algebra (GEMM, Cholesky, triangular solve, Jacobi
+// eigensolver) and the parameter store.
+//
+// Method ("A JoLT for the KV cache", landing page abstract): partial Tucker
+// decomposition of the grouped cache tensor along the token and feature modes;
+// the token factor by an exact token-mode SVD (eigenvectors of A A^T, A the
+// token unfolding) or by FlashJoLT's randomized approximation (range finder of
+// Halko, Martinsson & Tropp: sketch, orthonormalise, power iteration, small SVD
+// of B = Q^T A); the feature factor from the d x d feature Gram.
+//
+// MFMA fragment convention (v_mfma_f32_32x32x16_bf16 / 32x32x2f32): lane l
+// supplies row l % 32 of A and column l % 32 of B with the 8 consecutive K
+// indices k0 + 8 (l / 32) + i; the 32x32 fp32 result sits at
+// D[8 (j / 4) + 4 (l / 32) + j % 4][l % 32], j = 0..15.
+#include <float.h>
+
+#include "dev_common.h"
+#include "plan_kernels.h"
+
+namespace jolt {
+
+// ====================================================================== X-pass A M
+// WG: 4 waves x 32 tokens; each wave owns NF column fragments (32 columns each).
+template <typename T, int NF>
+__global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d) {
+    const XmItem &it = batch.it[blockIdx.z];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
+    const int t0 = blockIdx.x * 128 + wave * 32;
+    const int c0 = blockIdx.y * (32 * NF);
+    if (t0 >= it.T || c0 >= it.ncols) return;
+    const T *x = reinterpret_cast<const T *>(it.x);
+    const T *m = reinterpret_cast<const T *>(it.m);
+    const int n = it.LH * d;
+    const int tok = t0 + ln;                // T is a multiple of 64, so always valid
+    f32x16 acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
+    int ncf = (it.ncols - c0 + 31) / 32;
+    if (ncf > NF) ncf = NF;
+    for (int k0 = 0; k0 < n; k0 += 16) {
+        const int lh = k0 / d, f0 = k0 - lh * d + 8 * h;
+        typename Elem<T>::Frag a = load_frag(x + ((size_t)lh * it.T + tok) * d + f0);
+        const T *mb = m + (size_t)lh * it.m_blk + f0;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (f < ncf) {
+                const int c = c0 + 32 * f + ln;
+                typename Elem<T>::Frag b = (c < it.ncols) ? load_frag(mb + (size_t)c * it.m_c) : zero_frag(m);
+                mfma(a, b, acc[f]);
+            }
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int c = c0 + 32 * f + ln;
+        if (f < ncf && c < it.ncols) {
+            float *o = it.out + (size_t)c * it.ldo + t0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 8 * q + 4 * h;
+                *reinterpret_cast<float4 *>(o + r) =
+                    make_float4(acc[f][4 * q], acc[f][4 * q + 1], acc[f][4 * q + 2], acc[f][4 * q + 3]);
+            }
+        }
+    }
+}
+
+// ====================================================================== staging helper
+// 64 rows x d features (row stride d) -> LDS transposed xs[f][r] with row pitch XP.
+template <typename T>
+__device__ __forceinline__ void stage_transposed(const T *src, int d, T *xs, int XP) {
+    constexpr int PER = 16 / sizeof(T);
+    const int chunks = 64 * d / PER;
+    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+        const int r = c / (d / PER), f = (c % (d / PER)) * PER;
+        const uint4 v = *reinterpret_cast<const uint4 *>(src + (size_t)r * d + f);
+        const T *e = reinterpret_cast<const T *>(&v);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) xs[(f + i) * XP + r] = e[i];
+    }
+}
+
+// ====================================================================== X-pass Q^T A
+// WG per (item, lh, split): 4 waves; wave w -> feature fragment w % (d/32),
+// column fragments [(w / (d/32)) * NF, ...).
+template <typename T, int NF, bool LO>
+__global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d) {
+    constexpr int XP = 64 + 16 / sizeof(T);
+    __shared__ __attribute__((aligned(16))) T xs[128 * XP];
+    const XtqItem &it = batch.it[blockIdx.z];
+    const int lh = blockIdx.y, sp = blockIdx.x;
+    if (lh >= it.LH || sp >= it.nsplit) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
+    const int nmf = d / 32;
+    const int mf = wave % nmf, cgrp = wave / nmf;
+    const int c0 = cgrp * NF * 32;
+    const T *x = reinterpret_cast<const T *>(it.x) + (size_t)lh * it.T * d;
+    const T *qh = reinterpret_cast<const T *>(it.qh);
+    const T *ql = reinterpret_cast<const T *>(it.ql);
+    const int tb = sp * it.tsplit, te = min(it.T, tb + it.tsplit);
+    f32x16 acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
+    for (int t0 = tb; t0 < te; t0 += 64) {
+        __syncthreads();
+        stage_transposed<T>(x + (size_t)t0 * d, d, xs, XP);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 64; kk += 16) {
+            typename Elem<T>::Frag a;
+            {
+                const T *p = xs + (32 * mf + ln) * XP + kk + 8 * h;
+                if constexpr (sizeof(T) == 2) {
+                    const uint2 *q = reinterpret_cast<const uint2 *>(p);
+                    uint2 u0 = q[0], u1 = q[1];
+                    a.v = __builtin_bit_cast(bf16x8, make_uint4(u0.x, u0.y, u1.x, u1.y));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) reinterpret_cast<float *>(&a)[i] = reinterpret_cast<const float *>(p)[i];
+                }
+            }
+            const int t = t0 + kk + 8 * h;
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const int c = c0 + 32 * f + ln;
+                if (c < it.ncols) {
+                    mfma(a, load_frag(qh + (size_t)c * it.ldq + t), acc[f]);
+                    if constexpr (LO) mfma(a, load_frag(ql + (size_t)c * it.ldq + t), acc[f]);
+                }
+            }
+        }
+    }
+    const int n = it.LH * d;
+    float *out = it.out + (size_t)sp * it.ncols * n;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int c = c0 + 32 * f + ln;
+        if (c < it.ncols) {
+            float *o = out + (size_t)c * n + (size_t)lh * d + 32 * mf;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 8 * q + 4 * h;
+                *reinterpret_cast<float4 *>(o + r) =
+                    make_float4(acc[f][4 * q], acc[f][4 * q + 1], acc[f][4 * q + 2], acc[f][4 * q + 3]);
+            }
+        }
+    }
+}
+
+// ====================================================================== feature Gram
+template <typename T>
+__global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
+    constexpr int XP = 64 + 16 / sizeof(T);
+    __shared__ __attribute__((aligned(16))) T xs[128 * XP];
+    const GramItem &it = batch.it[blockIdx.z];
+    const int p = blockIdx.x;
+    if (p >= it.P) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
+    const int nmf = d / 32;                    // 4 or 2 fragments per side
+    const T *x = reinterpret_cast<const T *>(it.x);
+    const int64_t rb = (int64_t)p * it.chunk;
+    const int64_t re = min(it.rows, rb + it.chunk);
+    // fragment pairs owned by this wave: (mf, nf) = q / nmf, q % nmf, q = wave + 4 i
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    const int nq = nmf * nmf;
+    for (int64_t r0 = rb; r0 < re; r0 += 64) {
+        __syncthreads();
+        stage_transposed<T>(x + r0 * d, d, xs, XP);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 64; kk += 16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = wave + 4 * i;
+                if (q < nq) {
+                    const int mf = q / nmf, nf = q % nmf;
+                    typename Elem<T>::Frag a, b;
+                    const T *pa = xs + (32 * mf + ln) * XP + kk + 8 * h;
+                    const T *pb = xs + (32 * nf + ln) * XP + kk + 8 * h;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        reinterpret_cast<T *>(&a)[e] = pa[e];
+                        reinterpret_cast<T *>(&b)[e] = pb[e];
+                    }
+                    mfma(a, b, acc[i]);
+                }
+            }
+        }
+    }
+    float *out = it.out + (size_t)p * d * d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = wave + 4 * i;
+        if (q < nq) {
+            const int mf = q / nmf, nf = q % nmf;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) out[(size_t)(32 * mf + frag_row(lane, j)) * d + 32 * nf + ln] = acc[i][j];
+        }
+    }
+}
+
+// ====================================================================== fp32 GEMM
+// 64x64 tile, 16-deep K slices staged in LDS, 4x4 outputs per thread.
+__global__ __launch_bounds__(256) void k_gemm(GemmBatch batch, int maxSplit) {
+    __shared__ float As[16][64 + 4];
+    __shared__ float Bs[16][64 + 4];
+    const int z = blockIdx.z;
+    const GemmItem &it0 = batch.it[z % batch.n];
+    const int sp = (z / batch.n) % maxSplit, bi = (z / batch.n) / maxSplit;
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    if (sp >= it0.nsplit || bi >= it0.nb || i0 >= it0.M || j0 >= it0.N) return;
+    GemmItem it = it0;
+    it.a += bi * it0.a_z;
+    it.b += bi * it0.b_z;
+    it.c += bi * it0.c_z;
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    const int kb = sp * it.kchunk, ke = min(it.K, kb + it.kchunk);
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+    const bool a_kfast = it.a_k == 1, b_jfast = it.b_j == 1;
+    for (int k0 = kb; k0 < ke; k0 += 16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            int ii, kk;
+            if (a_kfast) { ii = e / 16; kk = e % 16; } else { ii = e % 64; kk = e / 64; }
+            const int gi = i0 + ii, gk = k0 + kk;
+            As[kk][ii] = (gi < it.M && gk < ke) ? it.a[(int64_t)gi * it.a_i + (int64_t)gk * it.a_k] : 0.f;
+            int jj, kb2;
+            if (b_jfast) { kb2 = e / 64; jj = e % 64; } else { kb2 = e % 16; jj = e / 16; }
+            const int gj = j0 + jj, gk2 = k0 + kb2;
+            Bs[kb2][jj] = (gj < it.N && gk2 < ke) ? it.b[(int64_t)gk2 * it.b_k + (int64_t)gj * it.b_j] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) av[a] = As[kk][ty * 4 + a];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bv[b] = Bs[kk][tx * 4 + b];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(av[a], bv[b], acc[a][b]);
+        }
+        __syncthreads();
+    }
+    float *c = it.c + (int64_t)sp * it.c_split;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int gi = i0 + ty * 4 + a, gj = j0 + tx * 4 + b;
+            if (gi < it.M && gj < it.N) c[(int64_t)gi * it.c_i + (int64_t)gj * it.c_j] = acc[a][b];
+        }
+}
+
+// ====================================================================== split reduction
+__global__ void k_reduce(ReduceBatch batch) {
+    const ReduceItem &it = batch.it[blockIdx.y];
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= it.count) return;
+    float s = 0.f;
+    for (int p = 0; p < it.nsplit; ++p) s += it.part[(int64_t)p * it.stride + i];
+    it.out[i] = s;
+}
+
+// ====================================================================== Cholesky
+// One WG per matrix; the lower triangle is held packed in LDS:
+// L(i, j) at i (i + 1) / 2 + j.  Right-looking: pivot, scale the column, rank-1
+// update of the trailing triangle.  Pivots at or below the shift floor are
+// clamped so rank-deficient sketches still give a usable basis.
+__global__ __launch_bounds__(1024) void k_cholesky(CholBatch batch) {
+    extern __shared__ float lp[];
+    __shared__ float s_red[32];
+    __shared__ float s_shift;
+    const CholItem &it = batch.it[blockIdx.x];
+    const int k = it.k, tid = threadIdx.x, nt = blockDim.x;
+    // trace for the shift
+    float tr = 0.f;
+    for (int i = tid; i < k; i += nt) tr += it.g[(size_t)i * it.ld + i];
+    for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o);
+    if ((tid & 63) == 0) s_red[tid >> 6] = tr;
+    __syncthreads();
+    if (tid == 0) {
+        float t = 0.f;
+        for (int w = 0; w < (nt + 63) / 64; ++w) t += s_red[w];
+        s_shift = it.rel_shift * t / (float)k;
+        if (!(s_shift > 0.f)) s_shift = FLT_MIN;
+    }
+    __syncthreads();
+    const float shift = s_shift;
+    for (int e = tid; e < k * (k + 1) / 2; e += nt) {
+        int i = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
+        while (i * (i + 1) / 2 > e) --i;
+        while ((i + 1) * (i + 2) / 2 <= e) ++i;
+        const int j = e - i * (i + 1) / 2;
+        float v = 0.5f * (it.g[(size_t)i * it.ld + j] + it.g[(size_t)j * it.ld + i]);
+        if (i == j) v += shift;
+        lp[e] = v;
+    }
+    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63, nw = nt >> 6;
+    for (int j = 0; j < k; ++j) {
+        const int jj = j * (j + 1) / 2 + j;
+        if (tid == 0) lp[jj] = sqrtf(fmaxf(lp[jj], shift));
+        __syncthreads();
+        const float piv = lp[jj];
+        for (int i = j + 1 + tid; i < k; i += nt) lp[i * (i + 1) / 2 + j] /= piv;
+        __syncthreads();
+        for (int i = j + 1 + wave; i < k; i += nw) {
+            const float lij = lp[i * (i + 1) / 2 + j];
+            float *row = lp + i * (i + 1) / 2;
+            for (int c = j + 1 + lane; c <= i; c += 64) row[c] -= lij * lp[c * (c + 1) / 2 + j];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < k * k; e += nt) {
+        const int i = e / k, j = e % k;
+        it.l[(size_t)i * it.ld + j] = (j <= i) ? lp[i * (i + 1) / 2 + j] : 0.f;
+    }
+}
+
+// ====================================================================== triangular solve
+// WG: 32 columns of y; 1024 threads = 32 columns x 32 partial-sum lanes.
+// Row i of the result: q[i] = (y[i] - sum_{c<i} L[i][c] q[c]) / L[i][i].
+__global__ __launch_bounds__(1024) void k_trsm(TrsmBatch batch) {
+    extern __shared__ float qs[];             // [k][33]
+    const TrsmItem &it = batch.it[blockIdx.y];
+    const int t0 = blockIdx.x * 32;
+    if (t0 >= it.len) return;
+    const int tid = threadIdx.x, col = tid >> 5, cl = tid & 31;
+    const int k = it.k;
+    for (int e = tid; e < k * 32; e += 1024) {
+        const int r = e / 32, c = e % 32;
+        qs[r * 33 + c] = (t0 + c < it.len) ? it.y[(size_t)r * it.ldy + t0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int i = 0; i < k; ++i) {
+        const float *li = it.l + (size_t)i * it.ld;
+        float s = 0.f;
+        for (int c = cl; c < i; c += 32) s = fmaf(li[c], qs[c * 33 + col], s);
+        for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
+        if (cl == 0) qs[i * 33 + col] = (qs[i * 33 + col] - s) / li[i];
+        __syncthreads();
+    }
+    for (int e = tid; e < k * 32; e += 1024) {
+        const int r = e / 32, c = e % 32;
+        if (t0 + c < it.len) it.q[(size_t)r * it.ldy + t0 + c] = qs[r * 33 + c];
+    }
+}
+
+// ====================================================================== Jacobi (LDS)
+// Two-sided Jacobi, parallel (round-robin) ordering: each of the m - 1 rounds of a
+// sweep pairs all indices disjointly; the round's rotations zero a[p][q] by the
+// symmetric 2x2 Schur decomposition and are applied together block by block,
+// A <- J^T A J, V <- V J (Golub & Van Loan, Matrix Computations, sec. 8.5).
+// A rotation is skipped when |a_pq| <= tol sqrt(|a_pp a_qq|); a sweep with no
+// rotation ends the iteration.
+__device__ __forceinline__ int rr_pos(int i, int round, int m) {
+    if (i == 0) return 0;
+    return 1 + ((i - 1 - round) % (m - 1) + (m - 1)) % (m - 1);
+}
+
+__global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_sweeps) {
+    extern __shared__ float sm[];
+    __shared__ int sP[kJacobiMaxN / 2 + 1], sQ[kJacobiMaxN / 2 + 1];
+    __shared__ float sC[kJacobiMaxN / 2 + 1], sS[kJacobiMaxN / 2 + 1];
+    __shared__ int s_rot;
+    const JacItem &it = batch.it[blockIdx.x];
+    const int n = it.n, m = n + (n & 1), half = m / 2;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    float *A = sm, *V = sm + m * m;
+    for (int e = tid; e < m * m; e += nt) {
+        const int r = e / m, c = e % m;
+        A[e] = (r < n && c < n) ? 0.5f * (it.a[(size_t)r * it.lda + c] + it.a[(size_t)c * it.lda + r]) : 0.f;
+        V[e] = (r == c) ? 1.f : 0.f;
+    }
+    __syncthreads();
+    const float tol = 1.0e-6f;
+    int sweeps = 0;
+    bool done = false;
+    for (; sweeps < max_sweeps && !done; ++sweeps) {
+        if (tid == 0) s_rot = 0;
+        __syncthreads();
+        for (int round = 0; round < m - 1; ++round) {
+            if (tid < half) {
+                int p = rr_pos(tid, round, m), q = rr_pos(m - 1 - tid, round, m);
+                if (p > q) { const int t = p; p = q; q = t; }
+                const float apq = A[p * m + q], app = A[p * m + p], aqq = A[q * m + q];
+                float c = 1.f, s = 0.f;
+                if (fabsf(apq) > tol * sqrtf(fabsf(app) * fabsf(aqq)) && fabsf(apq) > 1e-30f) {
+                    const float tau = (aqq - app) / (2.f * apq);
+                    const float t = (tau >= 0.f) ? 1.f / (tau + sqrtf(1.f + tau * tau))
+                                                 : -1.f / (-tau + sqrtf(1.f + tau * tau));
+                    c = 1.f / sqrtf(1.f + t * t);
+                    s = t * c;
+                    s_rot = 1;
+                }
+                sP[tid] = p; sQ[tid] = q; sC[tid] = c; sS[tid] = s;
+            }
+            __syncthreads();
+            for (int e = tid; e < half * half; e += nt) {
+                const int i = e / half, j = e % half;
+                const int pi = sP[i], qi = sQ[i], pj = sP[j], qj = sQ[j];
+                const float ci = sC[i], si = sS[i], cj = sC[j], sj = sS[j];
+                const float b00 = A[pi * m + pj], b01 = A[pi * m + qj], b10 = A[qi * m + pj], b11 = A[qi * m + qj];
+                const float m00 = cj * b00 - sj * b01, m01 = sj * b00 + cj * b01;
+                const float m10 = cj * b10 - sj * b11, m11 = sj * b10 + cj * b11;
+                float n00 = ci * m00 - si * m10, n01 = ci * m01 - si * m11;
+                float n10 = si * m00 + ci * m10, n11 = si * m01 + ci * m11;
+                if (i == j) { n01 = 0.f; n10 = 0.f; }
+                A[pi * m + pj] = n00; A[pi * m + qj] = n01; A[qi * m + pj] = n10; A[qi * m + qj] = n11;
+            }
+            for (int e = tid; e < m * half; e += nt) {
+                const int r = e / half, j = e % half;
+                const int pj = sP[j], qj = sQ[j];
+                const float cj = sC[j], sj = sS[j];
+                const float a = V[r * m + pj], b = V[r * m + qj];
+                V[r * m + pj] = cj * a - sj * b;
+                V[r * m + qj] = sj * a + cj * b;
+            }
+            __syncthreads();
+        }
+        done = (s_rot == 0);
+        __syncthreads();
+    }
+    if (tid == 0 && it.sweeps_out) *it.sweeps_out = done ? sweeps : -1;
+    // sort descending (ties by index), sign-normalise, write out
+    for (int i = tid; i < n; i += nt) {
+        const float li = A[i * m + i];
+        int rank = 0;
+        for (int j = 0; j < n; ++j) {
+            const float lj = A[j * m + j];
+            rank += (lj > li) || (lj == li && j < i);
+        }
+        int best = 0;
+        float bm = -1.f;
+        for (int r = 0; r < n; ++r) {
+            const float v = fabsf(V[r * m + i]);
+            if (v > bm) { bm = v; best = r; }
+        }
+        const float sg = V[best * m + i] < 0.f ? -1.f : 1.f;
+        it.lam[rank] = li;
+        for (int r = 0; r < n; ++r) it.vec[(size_t)r * it.ldv + rank] = sg * V[r * m + i];
+    }
+}
+
+// ====================================================================== small helpers
+__global__ void k_to_bf16(const float *in, uint16_t *hi, uint16_t *lo, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    const float v = in[i];
+    const uint16_t h = f32_to_bf16(v);
+    hi[i] = h;
+    if (lo) lo[i] = f32_to_bf16(v - bf16_to_f32(h));
+}
+
+// omt[c][r] = Omega[r][c] (+-1, counter r * k + c of stream 1), zero rows c >= k
+__global__ void k_gen_omega(uint16_t *omt, float *omt32, uint64_t key, int k, int kp, int64_t n) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (int64_t)kp * n) return;
+    const int c = (int)(e / n);
+    const int64_t r = e % n;
+    const float v = (c < k) ? rademacher(key, 1, (uint64_t)r * k + c) : 0.f;
+    if (omt) omt[e] = f32_to_bf16(v);
+    if (omt32) omt32[e] = v;
+}
+
+__global__ void k_energy(const float *core, float *energy, int LH, int rt_max, int d) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= rt_max * d) return;
+    float s = 0.f;
+    for (int lh = 0; lh < LH; ++lh) {
+        const float v = core[(size_t)lh * rt_max * d + e];
+        s = fmaf(v, v, s);
+    }
+    energy[e] = s;
+}
+
+__global__ void k_trace(const float *g, int d, double *out) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        double s = 0.0;
+        for (int i = 0; i < d; ++i) s += (double)g[(size_t)i * d + i];
+        *out = s;
+    }
+}
+
+__global__ void k_transpose(const float *in, float *out, int rows, int cols, int ldi, int ldo) {
+    __shared__ float tile[32][33];
+    const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+    for (int i = threadIdx.y; i < 32; i += blockDim.y) {
+        const int r = r0 + i, c = c0 + threadIdx.x;
+        if (r < rows && c < cols) tile[i][threadIdx.x] = in[(size_t)r * ldi + c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.y; i < 32; i += blockDim.y) {
+        const int c = c0 + i, r = r0 + threadIdx.x;
+        if (r < rows && c < cols) out[(size_t)c * ldo + r] = tile[threadIdx.x][i];
+    }
+}
+
+__global__ void k_zero(uint32_t *p, size_t words) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < words) p[i] = 0;
+}
+
+// ====================================================================== parameter store
+template <typename T>
+__device__ __forceinline__ void put_param(uint8_t *base, size_t idx, float v) {
+    if (sizeof(T) == 2) reinterpret_cast<uint16_t *>(base)[idx] = f32_to_bf16(v);
+    else reinterpret_cast<float *>(base)[idx] = v;
+}
+
+template <typename T>
+__global__ void k_store(StoreBatch batch) {
+    const StoreItem &it = batch.it[blockIdx.y];
+    const size_t n_ut = (size_t)it.T * it.rt, n_uf = (size_t)it.d * it.rf, n_c = (size_t)it.LH * it.rt * it.rf;
+    const size_t total = n_ut + n_uf + n_c + 16;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+        if (e < n_ut) {
+            const size_t t = e / it.rt, r = e % it.rt;
+            put_param<T>(it.pay + it.off_ut, e, it.ut[r * it.T + t]);
+        } else if (e < n_ut + n_uf) {
+            const size_t q = e - n_ut, f = q / it.rf, j = q % it.rf;
+            put_param<T>(it.pay + it.off_uf, q, it.uf[f * it.d + j]);
+        } else if (e < n_ut + n_uf + n_c) {
+            const size_t q = e - n_ut - n_uf;
+            const size_t lh = q / ((size_t)it.rt * it.rf), rem = q % ((size_t)it.rt * it.rf);
+            const size_t r = rem / it.rf, j = rem % it.rf;
+            put_param<T>(it.pay + it.off_core, q, it.core[(lh * it.rt_max + r) * it.d + j]);
+        } else {
+            const size_t w = e - n_ut - n_uf - n_c;
+            reinterpret_cast<uint32_t *>(it.pay)[w] = it.header[w];
+        }
+    }
+}
+
+// ====================================================================== launchers
+static int dyn_lds_set = 0;
+static void ensure_lds_attrs() {
+    if (dyn_lds_set) return;
+    hipFuncSetAttribute(reinterpret_cast<const void *>(k_jacobi_lds), hipFuncAttributeMaxDynamicSharedMemorySize,
+                        160 * 1024);
+    hipFuncSetAttribute(reinterpret_cast<const void *>(k_cholesky), hipFuncAttributeMaxDynamicSharedMemorySize,
+                        160 * 1024);
+    hipFuncSetAttribute(reinterpret_cast<const void *>(k_trsm), hipFuncAttributeMaxDynamicSharedMemorySize,
+                        160 * 1024);
+    dyn_lds_set = 1;
+}
+
+template <typename T>
+static hipError_t xm_nf(const XmBatch &b, int d, dim3 g, int nf, hipStream_t s) {
+    switch (nf) {
+        case 1: hipLaunchKernelGGL((k_xm<T, 1>), g, dim3(256), 0, s, b, d); break;
+        case 2: hipLaunchKernelGGL((k_xm<T, 2>), g, dim3(256), 0, s, b, d); break;
+        case 3: hipLaunchKernelGGL((k_xm<T, 3>), g, dim3(256), 0, s, b, d); break;
+        case 4: hipLaunchKernelGGL((k_xm<T, 4>), g, dim3(256), 0, s, b, d); break;
+        case 5: hipLaunchKernelGGL((k_xm<T, 5>), g, dim3(256), 0, s, b, d); break;
+        case 6: hipLaunchKernelGGL((k_xm<T, 6>), g, dim3(256), 0, s, b, d); break;
+        case 7: hipLaunchKernelGGL((k_xm<T, 7>), g, dim3(256), 0, s, b, d); break;
+        case 8: hipLaunchKernelGGL((k_xm<T, 8>), g, dim3(256), 0, s, b, d); break;
+        case 9: hipLaunchKernelGGL((k_xm<T, 9>), g, dim3(256), 0, s, b, d); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    int nf = (maxCols + 31) / 32;
+    int gy = 1;
+    if (nf > 9) { gy = (nf + 3) / 4; nf = 4; }
+    dim3 g((maxT + 127) / 128, gy, b.n);
+    return dtype == JOLT_BF16 ? xm_nf<uint16_t>(b, d, g, nf, s) : xm_nf<float>(b, d, g, nf, s);
+}
+
+template <typename T, bool LO>
+static hipError_t xtq_nf(const XtqBatch &b, int d, dim3 g, int nf, hipStream_t s) {
+    switch (nf) {
+        case 1: hipLaunchKernelGGL((k_xtq<T, 1, LO>), g, dim3(256), 0, s, b, d); break;
+        case 2: hipLaunchKernelGGL((k_xtq<T, 2, LO>), g, dim3(256), 0, s, b, d); break;
+        case 3: hipLaunchKernelGGL((k_xtq<T, 3, LO>), g, dim3(256), 0, s, b, d); break;
+        case 4: hipLaunchKernelGGL((k_xtq<T, 4, LO>), g, dim3(256), 0, s, b, d); break;
+        case 5: hipLaunchKernelGGL((k_xtq<T, 5, LO>), g, dim3(256), 0, s, b, d); break;
+        case 6: hipLaunchKernelGGL((k_xtq<T, 6, LO>), g, dim3(256), 0, s, b, d); break;
+        case 7: hipLaunchKernelGGL((k_xtq<T, 7, LO>), g, dim3(256), 0, s, b, d); break;
+        case 8: hipLaunchKernelGGL((k_xtq<T, 8, LO>), g, dim3(256), 0, s, b, d); break;
+        case 9: hipLaunchKernelGGL((k_xtq<T, 9, LO>), g, dim3(256), 0, s, b, d); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_xtq(const XtqBatch &b, int dtype, int d, int maxLH, int maxSplit, int maxCols, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    const int cgroups = 4 / (d / 32);                    // waves sharing one feature fragment
+    const int nf = ((maxCols + 31) / 32 + cgroups - 1) / cgroups;
+    dim3 g(maxSplit, maxLH, b.n);
+    const bool lo = b.it[0].ql != nullptr;
+    if (dtype == JOLT_BF16) return lo ? xtq_nf<uint16_t, true>(b, d, g, nf, s) : xtq_nf<uint16_t, false>(b, d, g, nf, s);
+    return xtq_nf<float, false>(b, d, g, nf, s);
+}
+
+hipError_t launch_gram_rows(const GramBatch &b, int dtype, int d, int maxP, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    dim3 g(maxP, 1, b.n);
+    if (dtype == JOLT_BF16) hipLaunchKernelGGL(k_gram_rows<uint16_t>, g, dim3(256), 0, s, b, d);
+    else hipLaunchKernelGGL(k_gram_rows<float>, g, dim3(256), 0, s, b, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    dim3 g((maxN + 63) / 64, (maxM + 63) / 64, b.n * maxSplit * maxNb);
+    hipLaunchKernelGGL(k_gemm, g, dim3(256), 0, s, b, maxSplit);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s) {
+    if (b.n <= 0 || maxCount <= 0) return hipSuccess;
+    dim3 g((unsigned)((maxCount + 255) / 256), b.n);
+    hipLaunchKernelGGL(k_reduce, g, dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    ensure_lds_attrs();
+    const size_t lds = (size_t)maxK * (maxK + 1) / 2 * sizeof(float);
+    hipLaunchKernelGGL(k_cholesky, dim3(b.n), dim3(1024), lds, s, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    ensure_lds_attrs();
+    const size_t lds = (size_t)maxK * 33 * sizeof(float);
+    hipLaunchKernelGGL(k_trsm, dim3((maxLen + 31) / 32, b.n), dim3(1024), lds, s, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    ensure_lds_attrs();
+    const int m = maxN + (maxN & 1);
+    const size_t lds = (size_t)2 * m * m * sizeof(float);
+    hipLaunchKernelGGL(k_jacobi_lds, dim3(b.n), dim3(1024), lds, s, b, max_sweeps);
+    return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float *in, uint16_t *hi, uint16_t *lo, int64_t count, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_to_bf16, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, in, hi, lo, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_gen_omega(uint16_t *omt, float *omt32, uint64_t key, int k, int kp, int64_t n, hipStream_t s) {
+    const int64_t cnt = (int64_t)kp * n;
+    if (cnt <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gen_omega, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s, omt, omt32, key, k, kp, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_energy(const float *core, float *energy, int LH, int rt_max, int d, hipStream_t s) {
+    const int cnt = rt_max * d;
+    if (cnt <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_energy, dim3((cnt + 255) / 256), dim3(256), 0, s, core, energy, LH, rt_max, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_trace(const float *g, int d, double *out, hipStream_t s) {
+    hipLaunchKernelGGL(k_trace, dim3(1), dim3(64), 0, s, g, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const float *in, float *out, int rows, int cols, int ldi, int ldo, hipStream_t s) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_transpose, dim3((cols + 31) / 32, (rows + 31) / 32), dim3(32, 8), 0, s, in, out, rows, cols,
+                       ldi, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
+    const size_t words = bytes / 4;
+    if (words == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, static_cast<uint32_t *>(p), words);
+    return hipGetLastError();
+}
+
+hipError_t launch_store(const StoreBatch &b, int dtype, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    dim3 g(512, b.n);
+    if (dtype == JOLT_BF16) hipLaunchKernelGGL(k_store<uint16_t>, g, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL(k_store<float>, g, dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+
+}  // namespace jolt

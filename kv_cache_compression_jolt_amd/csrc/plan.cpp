@@ -1,0 +1,607 @@
+// jolt_plan: factor every item, then allocate (r_t, r_f, b) with the single dual.
+//
+// Per item ("A JoLT for the KV cache", landing page abstract; author page abstract):
+//   feature factor  U_f = eigenvectors of G_f = sum over (layer, head, token) of x x^T
+//   token factor    exact:      eigenvectors of A A^T (A = token unfolding, T x L H d)
+//                   randomized: FlashJoLT range finder (Halko, Martinsson & Tropp,
+//                               SIAM Review 2011, Alg. 4.4 + Alg. 5.1): Y = A Omega,
+//                               Q = orth(Y); q times Q = orth(A orth(A^T Q));
+//                               B = Q^T A; W = B B^T = U~ L U~^T; U_t = Q U~
+//   core            C_lh = U_t^T X_lh U_f, energy E[i][j] = sum_lh C_lh[i][j]^2, ||X||^2
+// then one sync, the distortion / byte tables on the host and the dual (planner.cpp).
+//
+// orth() is shifted Cholesky QR (Fukaya et al. 2020): G = Y Y^T + s I = L L^T,
+// Q = L^{-1} Y (rows are the basis vectors), once for the intermediate bases
+// and twice for the final one.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "api_internal.h"
+#include "jolt_internal.h"
+#include "plan_kernels.h"
+#include "planner.h"
+
+namespace jolt {
+
+namespace {
+
+struct Bump {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + std::max<size_t>(bytes, 1), 256);
+        return o;
+    }
+};
+
+struct Dims {
+    int L, H, T, d, LH, n;       // n = L H d
+    int e;                        // element bytes of the item dtype
+    int k, kp;                    // sketch width and its 32-padding
+    int rt_max, rf_max, rtp32;
+    int xs_split, xs_tsplit;      // Q^T A passes: splits over tokens
+    int gf_P, gf_chunk;           // feature Gram partial sums
+    int gT_split, gT_chunk;       // Gram of a T-long basis
+    int gN_split, gN_chunk;       // Gram of an n-long basis
+};
+
+struct Scratch {
+    size_t omt, yt, qh, ql, zt, zb, xpart, gpart, gram, lmat, wmat, vmat, lamk, sweeps;
+    size_t gfpart, gf, pmat, gt, vt, lamT, uh, ul;
+};
+
+int clampi(int v, int lo, int hi) { return std::max(lo, std::min(hi, v)); }
+
+Dims dims_for(const jolt_config &cfg, const jolt_item &it, int rt_max, int rf_max) {
+    Dims D;
+    D.L = it.L; D.H = it.H; D.T = it.T; D.d = it.d;
+    D.LH = it.L * it.H;
+    D.n = D.LH * it.d;
+    D.e = elem_bytes(it.dtype);
+    D.rt_max = rt_max; D.rf_max = rf_max;
+    D.rtp32 = round_up(std::max(rt_max, 1), 32);
+    D.k = (cfg.mode == JOLT_TOKEN_RANDOMIZED) ? rt_max + cfg.oversample : 0;
+    D.kp = round_up(std::max(D.k, 1), 32);
+    D.xs_split = clampi(D.T / 4096, 1, 16);
+    D.xs_tsplit = round_up((D.T + D.xs_split - 1) / D.xs_split, 64);
+    D.xs_split = (D.T + D.xs_tsplit - 1) / D.xs_tsplit;
+    const int64_t rows = (int64_t)D.LH * D.T;
+    D.gf_P = (int)std::min<int64_t>(64, std::max<int64_t>(1, rows / 512));
+    D.gf_chunk = round_up((int)((rows + D.gf_P - 1) / D.gf_P), 64);
+    D.gf_P = (int)((rows + D.gf_chunk - 1) / D.gf_chunk);
+    D.gT_split = clampi(D.T / 512, 1, 64);
+    D.gT_chunk = round_up((D.T + D.gT_split - 1) / D.gT_split, 16);
+    D.gT_split = (D.T + D.gT_chunk - 1) / D.gT_chunk;
+    D.gN_split = clampi(D.n / 512, 1, 64);
+    D.gN_chunk = round_up((D.n + D.gN_split - 1) / D.gN_split, 16);
+    D.gN_split = (D.n + D.gN_chunk - 1) / D.gN_chunk;
+    return D;
+}
+
+void reserve_scratch(const jolt_config &cfg, const Dims &D, Bump &b, Scratch &s) {
+    std::memset(&s, 0, sizeof s);
+    const size_t T = D.T, n = D.n, kp = D.kp, d = D.d;
+    s.gfpart = b.take((size_t)D.gf_P * d * d * 4);
+    s.gf = b.take(d * d * 4);
+    if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
+        s.omt = b.take(kp * n * D.e);
+        s.yt = b.take(kp * T * 4);
+        if (D.e == 2) {
+            s.qh = b.take(kp * T * 2);
+            s.ql = b.take(kp * T * 2);
+            s.zb = b.take(kp * n * 2);
+        }
+        s.zt = b.take(kp * n * 4);
+        s.xpart = b.take((size_t)D.xs_split * kp * n * 4);
+        s.gpart = b.take((size_t)std::max(D.gT_split, D.gN_split) * kp * kp * 4);
+        s.gram = b.take(kp * kp * 4);
+        s.lmat = b.take(kp * kp * 4);
+        s.wmat = b.take(kp * kp * 4);
+        s.vmat = b.take(kp * kp * 4);
+        s.lamk = b.take(kp * 4);
+        s.pmat = b.take((size_t)D.rt_max * n * 4);
+    } else {
+        s.gt = b.take(T * T * 4);
+        s.vt = b.take(T * T * 4);
+        s.lamT = b.take(T * 4);
+        s.uh = b.take((size_t)D.rtp32 * T * D.e);
+        if (D.e == 2) s.ul = b.take((size_t)D.rtp32 * T * 2);
+        s.xpart = b.take((size_t)D.xs_split * D.rtp32 * n * 4);
+        s.pmat = b.take((size_t)D.rtp32 * n * 4);
+    }
+    s.sweeps = b.take(16);
+}
+
+struct Ctx {
+    jolt_handle h;
+    hipStream_t st;
+    int dtype, d;
+};
+
+#define HIPCHK(expr, where)                                   \
+    do {                                                      \
+        hipError_t e_ = (expr);                               \
+        if (e_ != hipSuccess) return hip_fail(c.h, e_, where); \
+    } while (0)
+
+}  // namespace
+
+// ------------------------------------------------------------------ config and layout
+jolt_status check_config(jolt_handle h, const jolt_config &cfg, const jolt_item *items, int n) {
+    if (cfg.mode != JOLT_TOKEN_EXACT && cfg.mode != JOLT_TOKEN_RANDOMIZED) return fail(h, JOLT_E_INVALID, "mode");
+    if (cfg.group_size != 64) return fail(h, JOLT_E_UNSUPPORTED, "group_size must be 64");
+    if (cfg.rank_step < 1) return fail(h, JOLT_E_INVALID, "rank_step must be >= 1");
+    if (cfg.rt_max < 0 || cfg.rt_max > 256) return fail(h, JOLT_E_INVALID, "rt_max must be in [0, 256]");
+    if (cfg.oversample < 0 || cfg.power_iters < 0 || cfg.power_iters > 8) return fail(h, JOLT_E_INVALID, "p / q");
+    if (cfg.bits_mask == 0 || (cfg.bits_mask & ~0x1FDu)) return fail(h, JOLT_E_INVALID, "bits_mask: b in {0, 2..8}");
+    if (cfg.budget_bytes >= 0) {
+        if (!(cfg.delta_b[0] == 1.0)) return fail(h, JOLT_E_INVALID, "delta_b[0] must be 1");
+        for (int b = 2; b <= 8; ++b)
+            if ((cfg.bits_mask >> b) & 1u)
+                if (!(cfg.delta_b[b] > 0.0) || !std::isfinite(cfg.delta_b[b]))
+                    return fail(h, JOLT_E_INVALID, "delta_b[%d] must be positive", b);
+    } else {
+        if (cfg.fixed_rt < 0 || cfg.fixed_rf < 0 || cfg.fixed_rt > cfg.rt_max ||
+            cfg.fixed_bits < 0 || cfg.fixed_bits == 1 || cfg.fixed_bits > 8)
+            return fail(h, JOLT_E_INVALID, "fixed ranks / bits");
+    }
+    for (int i = 0; i < n; ++i) {
+        const jolt_item &it = items[i];
+        if (it.T % 64) return fail(h, JOLT_E_UNSUPPORTED, "plan: T must be a multiple of 64");
+        const int rf_max = cfg.rf_max ? cfg.rf_max : it.d;
+        if (rf_max > it.d || rf_max < 0) return fail(h, JOLT_E_INVALID, "rf_max > d");
+        if (cfg.budget_bytes < 0 && cfg.fixed_rf > rf_max) return fail(h, JOLT_E_INVALID, "fixed_rf > rf_max");
+        if (cfg.rt_max > it.T) return fail(h, JOLT_E_INVALID, "rt_max > T");
+        if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
+            const int k = cfg.rt_max + cfg.oversample;
+            if (k < 1 || k > it.T || k > it.L * it.H * it.d)
+                return fail(h, JOLT_E_INVALID, "sketch width rt_max + oversample must be in [1, min(T, L H d)]");
+            if (k > kJacobiMaxN) return fail(h, JOLT_E_UNSUPPORTED, "sketch width above %d not supported", kJacobiMaxN);
+        } else {
+            if (it.T > kJacobiMaxN) return fail(h, JOLT_E_UNSUPPORTED, "exact mode: T above %d not supported", kJacobiMaxN);
+        }
+    }
+    return JOLT_OK;
+}
+
+jolt_status plan_layout(const jolt_config &cfg, const jolt_item *items, int n, PlanLayout *out) {
+    jolt_status s = check_config(nullptr, cfg, items, n);
+    if (s) return s;
+    PlanLayout pl;
+    pl.rt_max = cfg.rt_max;
+    pl.rf_max = n > 0 ? (cfg.rf_max ? cfg.rf_max : items[0].d) : 0;
+    pl.k = cfg.mode == JOLT_TOKEN_RANDOMIZED ? cfg.rt_max + cfg.oversample : 0;
+    pl.kp = round_up(std::max(pl.k, 1), 32);
+    Bump b;
+    pl.item.resize(n);
+    for (int i = 0; i < n; ++i) {
+        const jolt_item &it = items[i];
+        const size_t rt = std::max(pl.rt_max, 1), T = it.T, d = it.d, LH = (size_t)it.L * it.H;
+        FactorOffsets &o = pl.item[i];
+        o.ut = b.take(rt * T * 4);
+        o.uf = b.take(d * d * 4);
+        o.lam_t = b.take(std::max<size_t>(rt, 256) * 4);
+        o.lam_f = b.take(d * 4);
+        o.core = b.take(LH * rt * d * 4);
+        o.energy = b.take(rt * d * 4);
+        o.normx2 = b.take(8);
+    }
+    pl.scratch = b.off;
+    size_t worst = 0;
+    for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
+        Bump sb;
+        for (int i = c0; i < std::min(n, c0 + kMaxBatch); ++i) {
+            Dims D = dims_for(cfg, items[i], pl.rt_max, pl.rf_max);
+            Scratch S;
+            reserve_scratch(cfg, D, sb, S);
+        }
+        worst = std::max(worst, sb.off);
+    }
+    pl.scratch_bytes = worst;
+    pl.total = pl.scratch + worst;
+    *out = pl;
+    return JOLT_OK;
+}
+
+// ------------------------------------------------------------------ device pipeline
+namespace {
+
+jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, const int *k,
+                      const int *kp, const int *len, const int *split, const int *chunk, int passes) {
+    for (int pass = 0; pass < passes; ++pass) {
+        GemmBatch gb{};
+        ReduceBatch rb{};
+        CholBatch cb{};
+        TrsmBatch tb{};
+        int maxK = 0, maxLen = 0, maxS = 0;
+        for (int i = 0; i < nb; ++i) {
+            GemmItem &g = gb.it[gb.n++];
+            g.a = y[i]; g.b = y[i]; g.c = gpart[i];
+            g.a_i = len[i]; g.a_k = 1; g.b_k = 1; g.b_j = len[i];
+            g.c_i = kp[i]; g.c_j = 1; g.c_split = (int64_t)kp[i] * kp[i];
+            g.a_z = g.b_z = g.c_z = 0;
+            g.M = k[i]; g.N = k[i]; g.K = len[i]; g.kchunk = chunk[i]; g.nsplit = split[i]; g.nb = 1;
+            ReduceItem &r = rb.it[rb.n++];
+            r.part = gpart[i]; r.out = gram[i]; r.stride = (int64_t)kp[i] * kp[i]; r.count = (int64_t)kp[i] * kp[i];
+            r.nsplit = split[i];
+            CholItem &ch = cb.it[cb.n++];
+            ch.g = gram[i]; ch.l = lmat[i]; ch.k = k[i]; ch.ld = kp[i]; ch.rel_shift = 1.0f / 1048576.0f;
+            TrsmItem &t = tb.it[tb.n++];
+            t.l = lmat[i]; t.y = y[i]; t.q = y[i]; t.k = k[i]; t.ld = kp[i]; t.len = len[i]; t.ldy = len[i];
+            maxK = std::max(maxK, k[i]);
+            maxLen = std::max(maxLen, len[i]);
+            maxS = std::max(maxS, split[i]);
+        }
+        HIPCHK(launch_gemm(gb, maxK, maxK, maxS, 1, c.st), "orth gram");
+        int64_t maxCount = 0;
+        for (int i = 0; i < nb; ++i) maxCount = std::max<int64_t>(maxCount, (int64_t)kp[i] * kp[i]);
+        HIPCHK(launch_reduce(rb, maxCount, c.st), "orth reduce");
+        HIPCHK(launch_cholesky(cb, maxK, c.st), "orth cholesky");
+        HIPCHK(launch_trsm(tb, maxK, maxLen, c.st), "orth trsm");
+    }
+    return JOLT_OK;
+}
+
+jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items, int i0,
+                      int nb, const void *const *x_dev, uint8_t *ws) {
+    const int d = c.d, dt = c.dtype;
+    const bool bf = dt == JOLT_BF16;
+    std::vector<Dims> D(nb);
+    std::vector<Scratch> S(nb);
+    Bump sb;
+    for (int i = 0; i < nb; ++i) {
+        D[i] = dims_for(cfg, items[i0 + i], pl.rt_max, pl.rf_max);
+        reserve_scratch(cfg, D[i], sb, S[i]);
+    }
+    uint8_t *scr = ws + pl.scratch;
+    auto P = [&](size_t off) { return scr + off; };
+    auto F = [&](size_t off) { return reinterpret_cast<float *>(scr + off); };
+    auto W = [&](int i, size_t off) { return ws + off; };
+    int maxT = 0, maxLH = 0;
+    for (int i = 0; i < nb; ++i) { maxT = std::max(maxT, D[i].T); maxLH = std::max(maxLH, D[i].LH); }
+
+    // ---- feature Gram, ||X||^2
+    {
+        GramBatch gb{};
+        ReduceBatch rb{};
+        int maxP = 0;
+        for (int i = 0; i < nb; ++i) {
+            GramItem &g = gb.it[gb.n++];
+            g.x = x_dev[i0 + i]; g.out = F(S[i].gfpart);
+            g.rows = (int64_t)D[i].LH * D[i].T; g.chunk = D[i].gf_chunk; g.P = D[i].gf_P;
+            maxP = std::max(maxP, g.P);
+            ReduceItem &r = rb.it[rb.n++];
+            r.part = F(S[i].gfpart); r.out = F(S[i].gf); r.stride = (int64_t)d * d; r.count = (int64_t)d * d;
+            r.nsplit = D[i].gf_P;
+        }
+        HIPCHK(launch_gram_rows(gb, dt, d, maxP, c.st), "feature gram");
+        HIPCHK(launch_reduce(rb, (int64_t)d * d, c.st), "feature gram reduce");
+        for (int i = 0; i < nb; ++i)
+            HIPCHK(launch_trace(F(S[i].gf), d, reinterpret_cast<double *>(W(i, pl.item[i0 + i].normx2)), c.st),
+                   "trace");
+        JacBatch jb{};
+        for (int i = 0; i < nb; ++i) {
+            JacItem &j = jb.it[jb.n++];
+            j.a = F(S[i].gf); j.vec = reinterpret_cast<float *>(ws + pl.item[i0 + i].uf);
+            j.lam = reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_f);
+            j.n = d; j.lda = d; j.ldv = d;
+            j.sweeps_out = reinterpret_cast<int *>(P(S[i].sweeps));
+        }
+        HIPCHK(launch_jacobi_lds(jb, d, cfg.max_sweeps > 0 ? cfg.max_sweeps : 30, c.st), "feature eig");
+    }
+
+    if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
+        std::vector<float *> yv(nb), zv(nb), gram(nb), gpart(nb), lmat(nb);
+        std::vector<int> kk(nb), kpp(nb), lenT(nb), lenN(nb), sT(nb), cT(nb), sN(nb), cN(nb);
+        for (int i = 0; i < nb; ++i) {
+            const jolt_item &it = items[i0 + i];
+            HIPCHK(launch_gen_omega(bf ? reinterpret_cast<uint16_t *>(P(S[i].omt)) : nullptr,
+                                    bf ? nullptr : F(S[i].omt), item_key(it.seed, it.item_id), D[i].k, D[i].kp,
+                                    D[i].n, c.st),
+                   "omega");
+            yv[i] = F(S[i].yt); zv[i] = F(S[i].zt); gram[i] = F(S[i].gram); gpart[i] = F(S[i].gpart);
+            lmat[i] = F(S[i].lmat);
+            kk[i] = D[i].k; kpp[i] = D[i].kp; lenT[i] = D[i].T; lenN[i] = D[i].n;
+            sT[i] = D[i].gT_split; cT[i] = D[i].gT_chunk; sN[i] = D[i].gN_split; cN[i] = D[i].gN_chunk;
+        }
+        auto xm = [&](bool first) -> jolt_status {
+            XmBatch xb{};
+            int maxC = 0;
+            for (int i = 0; i < nb; ++i) {
+                XmItem &x = xb.it[xb.n++];
+                x.x = x_dev[i0 + i];
+                x.m = first ? (const void *)P(S[i].omt) : (bf ? (const void *)P(S[i].zb) : (const void *)P(S[i].zt));
+                x.out = F(S[i].yt);
+                x.m_c = D[i].n; x.m_blk = d;
+                x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].kp; x.ldo = D[i].T;
+                maxC = std::max(maxC, x.ncols);
+            }
+            HIPCHK(launch_xm(xb, dt, d, maxT, maxC, c.st), "sketch A M");
+            return JOLT_OK;
+        };
+        auto xtq = [&](bool hilo) -> jolt_status {
+            XtqBatch xb{};
+            ReduceBatch rb{};
+            int maxS = 0, maxC = 0;
+            int64_t maxCount = 0;
+            for (int i = 0; i < nb; ++i) {
+                XtqItem &x = xb.it[xb.n++];
+                x.x = x_dev[i0 + i];
+                x.qh = bf ? (const void *)P(S[i].qh) : (const void *)P(S[i].yt);
+                x.ql = (bf && hilo) ? (const void *)P(S[i].ql) : nullptr;
+                x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].kp; x.ldq = D[i].T;
+                x.tsplit = D[i].xs_tsplit; x.nsplit = D[i].xs_split;
+                x.out = x.nsplit == 1 ? F(S[i].zt) : F(S[i].xpart);
+                maxS = std::max(maxS, x.nsplit);
+                maxC = std::max(maxC, x.ncols);
+                if (x.nsplit > 1) {
+                    ReduceItem &r = rb.it[rb.n++];
+                    r.part = F(S[i].xpart); r.out = F(S[i].zt);
+                    r.stride = (int64_t)D[i].kp * D[i].n; r.count = r.stride; r.nsplit = x.nsplit;
+                    maxCount = std::max(maxCount, r.count);
+                }
+            }
+            HIPCHK(launch_xtq(xb, dt, d, maxLH, maxS, maxC, c.st), "sketch Q^T A");
+            HIPCHK(launch_reduce(rb, maxCount, c.st), "sketch reduce");
+            return JOLT_OK;
+        };
+        auto to_bf = [&](bool from_y, bool lo) -> jolt_status {
+            if (!bf) return JOLT_OK;
+            for (int i = 0; i < nb; ++i) {
+                if (from_y)
+                    HIPCHK(launch_to_bf16(F(S[i].yt), reinterpret_cast<uint16_t *>(P(S[i].qh)),
+                                          lo ? reinterpret_cast<uint16_t *>(P(S[i].ql)) : nullptr,
+                                          (int64_t)D[i].kp * D[i].T, c.st),
+                           "to bf16");
+                else
+                    HIPCHK(launch_to_bf16(F(S[i].zt), reinterpret_cast<uint16_t *>(P(S[i].zb)), nullptr,
+                                          (int64_t)D[i].kp * D[i].n, c.st),
+                           "to bf16");
+            }
+            return JOLT_OK;
+        };
+        jolt_status s;
+        if ((s = xm(true))) return s;                                                        // Y = A Omega
+        if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
+                           lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2)))
+            return s;
+        for (int q = 0; q < cfg.power_iters; ++q) {
+            if ((s = to_bf(true, false))) return s;
+            if ((s = xtq(false))) return s;                                                 // Z = A^T Q
+            if ((s = orth_rows(c, nb, zv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
+                               lenN.data(), sN.data(), cN.data(), 1)))
+                return s;
+            if ((s = to_bf(false, false))) return s;
+            if ((s = xm(false))) return s;                                                  // Y = A Z
+            if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
+                               lenT.data(), sT.data(), cT.data(), q + 1 == cfg.power_iters ? 2 : 1)))
+                return s;
+        }
+        if ((s = to_bf(true, true))) return s;
+        if ((s = xtq(true))) return s;                                                      // B = Q^T A (hi + lo)
+        // W = B B^T, eig
+        {
+            GemmBatch gb{};
+            ReduceBatch rb{};
+            int maxK = 0, maxS = 0;
+            int64_t maxCount = 0;
+            for (int i = 0; i < nb; ++i) {
+                GemmItem &g = gb.it[gb.n++];
+                g.a = zv[i]; g.b = zv[i]; g.c = gpart[i];
+                g.a_i = D[i].n; g.a_k = 1; g.b_k = 1; g.b_j = D[i].n;
+                g.c_i = D[i].kp; g.c_j = 1; g.c_split = (int64_t)D[i].kp * D[i].kp;
+                g.M = g.N = D[i].k; g.K = D[i].n; g.kchunk = D[i].gN_chunk; g.nsplit = D[i].gN_split; g.nb = 1;
+                ReduceItem &r = rb.it[rb.n++];
+                r.part = gpart[i]; r.out = F(S[i].wmat); r.stride = g.c_split; r.count = g.c_split; r.nsplit = g.nsplit;
+                maxK = std::max(maxK, D[i].k); maxS = std::max(maxS, g.nsplit);
+                maxCount = std::max(maxCount, r.count);
+            }
+            HIPCHK(launch_gemm(gb, maxK, maxK, maxS, 1, c.st), "B B^T");
+            HIPCHK(launch_reduce(rb, maxCount, c.st), "B B^T reduce");
+            JacBatch jb{};
+            for (int i = 0; i < nb; ++i) {
+                JacItem &j = jb.it[jb.n++];
+                j.a = F(S[i].wmat); j.vec = F(S[i].vmat); j.lam = F(S[i].lamk);
+                j.n = D[i].k; j.lda = D[i].kp; j.ldv = D[i].kp;
+                j.sweeps_out = reinterpret_cast<int *>(P(S[i].sweeps)) + 1;
+            }
+            HIPCHK(launch_jacobi_lds(jb, maxK, cfg.max_sweeps > 0 ? cfg.max_sweeps : 30, c.st), "small eig");
+        }
+        // U_t^T = U~^T Q, P = U~^T B, lambda_t
+        {
+            GemmBatch gu{}, gp{};
+            int maxN = 0, maxNn = 0;
+            for (int i = 0; i < nb; ++i) {
+                GemmItem &g = gu.it[gu.n++];
+                g.a = F(S[i].vmat); g.b = yv[i]; g.c = reinterpret_cast<float *>(ws + pl.item[i0 + i].ut);
+                g.a_i = 1; g.a_k = D[i].kp; g.b_k = D[i].T; g.b_j = 1; g.c_i = D[i].T; g.c_j = 1; g.c_split = 0;
+                g.M = pl.rt_max; g.N = D[i].T; g.K = D[i].k; g.kchunk = D[i].k; g.nsplit = 1; g.nb = 1;
+                GemmItem &q = gp.it[gp.n++];
+                q.a = F(S[i].vmat); q.b = zv[i]; q.c = F(S[i].pmat);
+                q.a_i = 1; q.a_k = D[i].kp; q.b_k = D[i].n; q.b_j = 1; q.c_i = D[i].n; q.c_j = 1; q.c_split = 0;
+                q.M = pl.rt_max; q.N = D[i].n; q.K = D[i].k; q.kchunk = D[i].k; q.nsplit = 1; q.nb = 1;
+                maxN = std::max(maxN, D[i].T); maxNn = std::max(maxNn, D[i].n);
+                HIPCHK(hipMemcpyAsync(ws + pl.item[i0 + i].lam_t, P(S[i].lamk), (size_t)pl.rt_max * 4,
+                                      hipMemcpyDeviceToDevice, c.st),
+                       "lambda_t");
+            }
+            if (pl.rt_max > 0) {
+                HIPCHK(launch_gemm(gu, pl.rt_max, maxN, 1, 1, c.st), "U_t");
+                HIPCHK(launch_gemm(gp, pl.rt_max, maxNn, 1, 1, c.st), "P");
+            }
+        }
+    } else {
+        return fail(c.h, JOLT_E_UNSUPPORTED, "exact token mode is not available in this build");
+    }
+
+    // core[lh] = P[:, lh d : lh d + d] U_f, energy
+    if (pl.rt_max > 0) {
+        GemmBatch gb{};
+        int maxNb = 0;
+        for (int i = 0; i < nb; ++i) {
+            GemmItem &g = gb.it[gb.n++];
+            g.a = F(S[i].pmat); g.b = reinterpret_cast<const float *>(ws + pl.item[i0 + i].uf);
+            g.c = reinterpret_cast<float *>(ws + pl.item[i0 + i].core);
+            g.a_i = D[i].n; g.a_k = 1; g.b_k = d; g.b_j = 1; g.c_i = d; g.c_j = 1; g.c_split = 0;
+            g.a_z = d; g.b_z = 0; g.c_z = (int64_t)pl.rt_max * d;
+            g.M = pl.rt_max; g.N = d; g.K = d; g.kchunk = d; g.nsplit = 1; g.nb = D[i].LH;
+            maxNb = std::max(maxNb, g.nb);
+        }
+        HIPCHK(launch_gemm(gb, pl.rt_max, d, 1, maxNb, c.st), "core");
+        for (int i = 0; i < nb; ++i)
+            HIPCHK(launch_energy(reinterpret_cast<const float *>(ws + pl.item[i0 + i].core),
+                                 reinterpret_cast<float *>(ws + pl.item[i0 + i].energy), D[i].LH, pl.rt_max, d, c.st),
+                   "energy");
+    }
+    return JOLT_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ parameter store (jolt_compress)
+jolt_status store_params(jolt_handle h, const PlanLayout &pl, const jolt_item *items, int n, const jolt_alloc *alloc,
+                         const void *plan_ws, void *const *payload_dev, hipStream_t st) {
+    const uint8_t *ws = static_cast<const uint8_t *>(plan_ws);
+    StoreBatch b{};
+    b.n = 0;
+    const int dt = items[0].dtype;
+    for (int i = 0; i < n; ++i) {
+        const jolt_item &it = items[i];
+        PayloadLayout p = payload_layout(it, alloc[i].rt, alloc[i].rf, alloc[i].bits);
+        StoreItem &s = b.it[b.n++];
+        s.ut = reinterpret_cast<const float *>(ws + pl.item[i].ut);
+        s.uf = reinterpret_cast<const float *>(ws + pl.item[i].uf);
+        s.core = reinterpret_cast<const float *>(ws + pl.item[i].core);
+        s.pay = static_cast<uint8_t *>(payload_dev[i]);
+        s.off_ut = p.ut; s.off_uf = p.uf; s.off_core = p.core;
+        s.T = it.T; s.d = it.d; s.LH = it.L * it.H; s.rt_max = pl.rt_max; s.rt = p.rt; s.rf = p.rf;
+        jolt_alloc a = alloc[i];
+        uint8_t hdr[64];
+        make_header(it, a, hdr);
+        std::memcpy(s.header, hdr, 64);
+        if (b.n == kMaxBatch || i == n - 1) {
+            hipError_t e = launch_store(b, dt, st);
+            if (e != hipSuccess) return hip_fail(h, e, "store params");
+            b.n = 0;
+        }
+    }
+    return JOLT_OK;
+}
+
+}  // namespace jolt
+
+using namespace jolt;
+
+extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jolt_item *items, int32_t n,
+                                 const void *const *x_dev, void *plan_ws, size_t plan_ws_bytes, void *stream,
+                                 jolt_alloc *alloc_host, double *lambda_out) {
+    if (!h || !cfg) return JOLT_E_INVALID;
+    clear_err(h);
+    jolt_status s = check_items_uniform(h, items, n);
+    if (s) return s;
+    if (n == 0) return JOLT_OK;
+    if (!x_dev || !plan_ws || !alloc_host) return fail(h, JOLT_E_INVALID, "NULL array");
+    for (int i = 0; i < n; ++i)
+        if (!x_dev[i]) return fail(h, JOLT_E_INVALID, "x_dev[%d] is NULL", i);
+    s = check_config(h, *cfg, items, n);
+    if (s) return s;
+    PlanLayout pl;
+    s = plan_layout(*cfg, items, n, &pl);
+    if (s) return fail(h, s, "layout");
+    if (plan_ws_bytes < pl.total)
+        return fail(h, JOLT_E_WORKSPACE, "plan workspace: need %zu bytes, have %zu", pl.total, plan_ws_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(plan_ws);
+    Ctx c{h, st, items[0].dtype, items[0].d};
+    bool noconv = false;
+    for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
+        const int nb = std::min(kMaxBatch, n - c0);
+        s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws);
+        if (s) return s;
+        // sweep counters of this chunk (the chunk's scratch is reused by the next one)
+        std::vector<Scratch> S(nb);
+        Bump sb;
+        for (int i = 0; i < nb; ++i) {
+            Dims D = dims_for(*cfg, items[c0 + i], pl.rt_max, pl.rf_max);
+            reserve_scratch(*cfg, D, sb, S[i]);
+        }
+        for (int i = 0; i < nb; ++i) {
+            int sw[2] = {0, 0};
+            hipError_t e = hipMemcpyAsync(sw, ws + pl.scratch + S[i].sweeps, sizeof sw, hipMemcpyDeviceToHost, st);
+            if (e == hipSuccess) e = hipStreamSynchronize(st);
+            if (e != hipSuccess) return hip_fail(h, e, "sweep counters");
+            if (sw[0] < 0 || (cfg->mode == JOLT_TOKEN_RANDOMIZED && sw[1] < 0)) noconv = true;
+        }
+    }
+    // energy tables and ||X||^2 back to the host (the one synchronisation)
+    const int rt_max = pl.rt_max;
+    std::vector<std::vector<float>> E(n);
+    std::vector<double> nx2(n);
+    for (int i = 0; i < n; ++i) {
+        E[i].resize((size_t)std::max(rt_max, 1) * items[i].d);
+        hipError_t e = hipSuccess;
+        if (rt_max > 0)
+            e = hipMemcpyAsync(E[i].data(), ws + pl.item[i].energy, (size_t)rt_max * items[i].d * 4,
+                               hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(&nx2[i], ws + pl.item[i].normx2, 8, hipMemcpyDeviceToHost, st);
+        if (e != hipSuccess) return hip_fail(h, e, "table readback");
+    }
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(h, e, "plan");
+
+    const int rf_max = pl.rf_max;
+    if (cfg->budget_bytes < 0) {
+        for (int i = 0; i < n; ++i) {
+            jolt_alloc &a = alloc_host[i];
+            a.rt = cfg->fixed_rt; a.rf = cfg->fixed_rf; a.bits = cfg->fixed_bits; a.reserved = 0;
+            if (a.rt == 0 || a.rf == 0) a.rt = a.rf = 0;
+            a.bytes = jolt_item_bytes(&items[i], a.rt, a.rf, a.bits);
+            double S = 0.0;
+            for (int r = 0; r < a.rt; ++r)
+                for (int f = 0; f < a.rf; ++f) S += (double)E[i][(size_t)r * items[i].d + f];
+            a.distortion = std::max(0.0, nx2[i] - S);
+        }
+        if (lambda_out) *lambda_out = -1.0;
+        return noconv ? fail(h, JOLT_E_NOCONV, "eigensolver hit its sweep cap") : JOLT_OK;
+    }
+    std::vector<Cand> cand = candidate_grid(rt_max, rf_max, cfg->rank_step, cfg->bits_mask);
+    const int nc = (int)cand.size();
+    std::vector<std::vector<double>> Dt(n, std::vector<double>(nc));
+    std::vector<std::vector<int64_t>> Bt(n, std::vector<int64_t>(nc));
+    std::vector<double> prefix((size_t)std::max(rt_max, 1) * std::max(rf_max, 1));
+    for (int i = 0; i < n; ++i) {
+        const int d = items[i].d;
+        for (int r = 0; r < rt_max; ++r)
+            for (int f = 0; f < rf_max; ++f) {
+                double v = (double)E[i][(size_t)r * d + f];
+                if (r > 0) v += prefix[(size_t)(r - 1) * rf_max + f];
+                if (f > 0) v += prefix[(size_t)r * rf_max + f - 1];
+                if (r > 0 && f > 0) v -= prefix[(size_t)(r - 1) * rf_max + f - 1];
+                prefix[(size_t)r * rf_max + f] = v;
+            }
+        distortion_table(prefix.data(), rf_max, nx2[i], cfg->delta_b, cand, Dt[i].data());
+        for (int j = 0; j < nc; ++j)
+            Bt[i][j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
+    }
+    std::vector<int32_t> ncand(n, nc);
+    std::vector<const Cand *> cp(n, cand.data());
+    std::vector<const double *> dp(n);
+    std::vector<const int64_t *> bp(n);
+    for (int i = 0; i < n; ++i) { dp[i] = Dt[i].data(); bp[i] = Bt[i].data(); }
+    std::vector<int> choice(n);
+    double lam = 0.0;
+    s = allocate(n, ncand.data(), cp.data(), dp.data(), bp.data(), cfg->budget_bytes, choice.data(), &lam);
+    for (int i = 0; i < n; ++i) {
+        const Cand &cc = cand[choice[i]];
+        alloc_host[i].rt = cc.rt; alloc_host[i].rf = cc.rf; alloc_host[i].bits = cc.bits; alloc_host[i].reserved = 0;
+        alloc_host[i].bytes = Bt[i][choice[i]];
+        alloc_host[i].distortion = Dt[i][choice[i]];
+    }
+    if (lambda_out) *lambda_out = lam;
+    if (s == JOLT_E_INFEASIBLE) return fail(h, s, "budget below the sum of minimum item bytes");
+    if (noconv) return fail(h, JOLT_E_NOCONV, "eigensolver hit its sweep cap");
+    return JOLT_OK;
+}

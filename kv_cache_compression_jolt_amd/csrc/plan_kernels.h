@@ -1,0 +1,121 @@
+// Launch interfaces of the plan-stage kernels (factorisation of the cache).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "jolt_internal.h"
+
+namespace jolt {
+
+// X-pass "A M": out[c][t] = sum_kk X(t, kk) M(c, kk), kk = (lh, f) over all heads and
+// layers, X(t, kk) = x[lh][t][f].  M(c, kk) = m + c * m_c + (kk / d) * m_blk + kk % d.
+struct XmItem {
+    const void *x;
+    const void *m;
+    float *out;          // [ncols][ldo]
+    int64_t m_c, m_blk;
+    int T, LH, ncols, ldo;
+};
+struct XmBatch { XmItem it[kMaxBatch]; int n; };
+hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, hipStream_t s);
+
+// X-pass "Q^T A": out[s][c][lh d + f] = sum_{t in split s} q[c][t] x[lh][t][f]
+// (q in the X dtype; an optional second operand ql is added: hi + lo split).
+struct XtqItem {
+    const void *x;
+    const void *qh;
+    const void *ql;      // may be null
+    float *out;          // [nsplit][ncols][LH d]
+    int T, LH, ncols, ldq, tsplit, nsplit;
+};
+struct XtqBatch { XtqItem it[kMaxBatch]; int n; };
+hipError_t launch_xtq(const XtqBatch &b, int dtype, int d, int maxLH, int maxSplit, int maxCols, hipStream_t s);
+
+// feature Gram partials: out[p][f1][f2] = sum over rows of chunk p of x[r][f1] x[r][f2]
+struct GramItem {
+    const void *x;
+    float *out;          // [P][d][d]
+    int64_t rows;
+    int chunk, P;
+};
+struct GramBatch { GramItem it[kMaxBatch]; int n; };
+hipError_t launch_gram_rows(const GramBatch &b, int dtype, int d, int maxP, hipStream_t s);
+
+// generic batched fp32 GEMM with element strides and split-K partial outputs
+// C[bi](i, j) (+split s) = sum_{k in split s} A[bi](i, k) B[bi](k, j); bi < nb is an
+// inner batch with its own base strides (a_z, b_z, c_z).
+struct GemmItem {
+    const float *a, *b;
+    float *c;
+    int64_t a_i, a_k, b_k, b_j, c_i, c_j, c_split;
+    int64_t a_z, b_z, c_z;
+    int M, N, K, kchunk, nsplit, nb;
+};
+struct GemmBatch { GemmItem it[kMaxBatch]; int n; };
+hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s);
+
+// out[i] = sum_s part[s * stride + i], i < count (fixed order); optional double trace
+struct ReduceItem {
+    const float *part;
+    float *out;
+    int64_t stride, count;
+    int nsplit;
+};
+struct ReduceBatch { ReduceItem it[kMaxBatch]; int n; };
+hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s);
+
+// Cholesky of G + shift I (k x k, ld) -> lower L written to l (k x k, ld), zeros above
+struct CholItem {
+    const float *g;
+    float *l;
+    int k, ld;
+    float rel_shift;     // shift = rel_shift * trace(G) / k
+};
+struct CholBatch { CholItem it[kMaxBatch]; int n; };
+hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s);
+
+// rows 0..k-1 of y[k][len] <- L^{-1} y   (forward substitution, in place allowed)
+struct TrsmItem {
+    const float *l;
+    const float *y;
+    float *q;
+    int k, ld, len, ldy;
+};
+struct TrsmBatch { TrsmItem it[kMaxBatch]; int n; };
+hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
+
+// symmetric eigen-decomposition by parallel-order two-sided Jacobi in LDS (n <= 142)
+// vec[r][c] = component r of eigenvector c, eigenvalues descending, sign-normalised.
+struct JacItem {
+    const float *a;
+    float *vec;
+    float *lam;
+    int n, lda, ldv;
+    int *sweeps_out;     // sweeps used, or -1 if the cap was hit
+};
+struct JacBatch { JacItem it[64]; int n; };
+constexpr int kJacobiMaxN = 142;
+hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s);
+
+// elementwise conversions
+hipError_t launch_to_bf16(const float *in, uint16_t *hi, uint16_t *lo, int64_t count, hipStream_t s);
+hipError_t launch_gen_omega(uint16_t *omt, float *omt32, uint64_t key, int k, int kp, int64_t n, hipStream_t s);
+hipError_t launch_energy(const float *core, float *energy, int LH, int rt_max, int d, hipStream_t s);
+hipError_t launch_trace(const float *g, int d, double *out, hipStream_t s);
+hipError_t launch_transpose(const float *in, float *out, int rows, int cols, int ldi, int ldo, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+
+// stored parameters -> payload (rounded to the item dtype) + header
+struct StoreItem {
+    const float *ut;     // [rt_max][T]
+    const float *uf;     // [d][d]
+    const float *core;   // [LH][rt_max][d]
+    uint8_t *pay;
+    size_t off_ut, off_uf, off_core;
+    int T, d, LH, rt_max, rt, rf;
+    uint32_t header[16];
+};
+struct StoreBatch { StoreItem it[kMaxBatch]; int n; };
+hipError_t launch_store(const StoreBatch &b, int dtype, hipStream_t s);
+
+}  // namespace jolt

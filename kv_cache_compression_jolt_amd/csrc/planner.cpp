@@ -1,0 +1,152 @@
+// Host planner: byte accounting, distortion tables and the single-Lagrangian-dual
+// allocation of (token rank, feature rank, residual bits).
+//
+// Method ("A JoLT for the KV cache": author page abstract, landing page abstract;
+// podcast section "The Core Mechanism"): one Lagrangian dual allocates the Tucker
+// ranks and the residual bit-widths together, per layer group and separately for
+// K and V, under one byte budget, instead of pre-splitting the budget.
+//
+// For a dual value lambda every item independently takes the candidate that
+// minimises D + lambda * bytes (ties: fewer bytes, then smaller r_t, r_f, b).
+// Only vertices of the lower convex hull of an item's (bytes, D) points can win;
+// between consecutive vertices the choice flips at slope s = dD / dbytes.  Total
+// bytes is a non-increasing step function of lambda, so lambda* (the least lambda
+// whose allocation fits the budget) is 0 or one of the slopes; it is found by
+// bisection over the sorted slopes.  All arithmetic is fp64 / int64; the build
+// uses -ffp-contract=off so the slope and hull tests round the same way every time.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "planner.h"
+
+namespace jolt {
+
+int64_t item_bytes_impl(int L, int H, int T, int d, int e, int rt, int rf, int bits) {
+    if (rt == 0 || rf == 0) rt = rf = 0;
+    const int64_t N = (int64_t)L * H * T * d;
+    int64_t params = (int64_t)e * ((int64_t)T * rt + (int64_t)d * rf + (int64_t)L * H * rt * rf);
+    int64_t resid = bits > 0 ? (N * bits / 8 + 2 * N / 64) : 0;
+    return params + resid;
+}
+
+std::vector<Cand> candidate_grid(int rt_max, int rf_max, int step, uint32_t bits_mask) {
+    std::vector<Cand> out;
+    for (int b = 0; b <= 8; ++b) {
+        if (!(bits_mask & (1u << b))) continue;
+        out.push_back({0, 0, b});
+        for (int rt = step; rt <= rt_max; rt += step)
+            for (int rf = step; rf <= rf_max; rf += step) out.push_back({rt, rf, b});
+    }
+    std::sort(out.begin(), out.end(), [](const Cand &a, const Cand &b) {
+        if (a.rt != b.rt) return a.rt < b.rt;
+        if (a.rf != b.rf) return a.rf < b.rf;
+        return a.bits < b.bits;
+    });
+    return out;
+}
+
+namespace {
+
+struct ItemHull {
+    std::vector<int> v;        // candidate indices, bytes ascending
+    std::vector<double> s;     // slope between v[j] and v[j+1] (decreasing)
+};
+
+bool key_less(const Cand &ca, double Da, int64_t Ba, const Cand &cb, double Db, int64_t Bb) {
+    if (Ba != Bb) return Ba < Bb;
+    if (Da != Db) return Da < Db;
+    if (ca.rt != cb.rt) return ca.rt < cb.rt;
+    if (ca.rf != cb.rf) return ca.rf < cb.rf;
+    return ca.bits < cb.bits;
+}
+
+ItemHull build_hull(int nc, const Cand *cand, const double *D, const int64_t *B) {
+    std::vector<int> order(nc);
+    std::iota(order.begin(), order.end(), 0);
+    std::sort(order.begin(), order.end(), [&](int a, int b) {
+        return key_less(cand[a], D[a], B[a], cand[b], D[b], B[b]);
+    });
+    // staircase: one point per byte count, strictly falling D
+    std::vector<int> stair;
+    for (int i : order) {
+        if (!stair.empty() && B[stair.back()] == B[i]) continue;
+        if (!stair.empty() && !(D[i] < D[stair.back()])) continue;
+        stair.push_back(i);
+    }
+    ItemHull h;
+    for (int i : stair) {
+        while (h.v.size() >= 2) {
+            const int o = h.v[h.v.size() - 2], a = h.v.back();
+            const double cross = (double)(B[a] - B[o]) * (D[i] - D[o]) - (D[a] - D[o]) * (double)(B[i] - B[o]);
+            if (cross <= 0.0) h.v.pop_back();
+            else break;
+        }
+        h.v.push_back(i);
+    }
+    for (size_t j = 0; j + 1 < h.v.size(); ++j) {
+        const int a = h.v[j], b = h.v[j + 1];
+        h.s.push_back((D[a] - D[b]) / (double)(B[b] - B[a]));
+    }
+    return h;
+}
+
+// vertex chosen at lambda: v[J], J = #{j : s_j > lambda}
+int vertex_at(const ItemHull &h, double lam) {
+    int J = 0;
+    for (double s : h.s) J += (s > lam);
+    return h.v[J];
+}
+
+}  // namespace
+
+jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, const double *const *D,
+                     const int64_t *const *B, int64_t budget, int *choice, double *lambda_out) {
+    std::vector<ItemHull> hulls(n);
+    int64_t min_total = 0;
+    for (int i = 0; i < n; ++i) {
+        if (n_cand[i] <= 0) return JOLT_E_INVALID;
+        hulls[i] = build_hull(n_cand[i], cand[i], D[i], B[i]);
+        min_total += B[i][hulls[i].v[0]];
+    }
+    if (min_total > budget) {
+        for (int i = 0; i < n; ++i) choice[i] = hulls[i].v[0];
+        if (lambda_out) *lambda_out = INFINITY;
+        return JOLT_E_INFEASIBLE;
+    }
+    auto total = [&](double lam) {
+        int64_t t = 0;
+        for (int i = 0; i < n; ++i) t += B[i][vertex_at(hulls[i], lam)];
+        return t;
+    };
+    double lam = 0.0;
+    if (total(0.0) > budget) {
+        std::vector<double> sl;
+        for (auto &h : hulls) sl.insert(sl.end(), h.s.begin(), h.s.end());
+        std::sort(sl.begin(), sl.end());
+        sl.erase(std::unique(sl.begin(), sl.end()), sl.end());
+        size_t lo = 0, hi = sl.size() - 1;   // total(sl.back()) == min_total <= budget
+        while (lo < hi) {
+            const size_t mid = (lo + hi) / 2;
+            if (total(sl[mid]) <= budget) hi = mid;
+            else lo = mid + 1;
+        }
+        lam = sl[lo];
+    }
+    for (int i = 0; i < n; ++i) choice[i] = vertex_at(hulls[i], lam);
+    if (lambda_out) *lambda_out = lam;
+    return JOLT_OK;
+}
+
+void distortion_table(const double *prefix /* (rt_max) x (rf_max), inclusive 2-D prefix sums */, int rf_max,
+                      double normx2, const double *delta, const std::vector<Cand> &cand, double *D) {
+    for (size_t i = 0; i < cand.size(); ++i) {
+        const Cand &c = cand[i];
+        const double S = (c.rt == 0 || c.rf == 0) ? 0.0 : prefix[(size_t)(c.rt - 1) * rf_max + (c.rf - 1)];
+        D[i] = delta[c.bits] * std::max(0.0, normx2 - S);
+    }
+}
+
+}  // namespace jolt

@@ -1,0 +1,113 @@
+"""GPU parity of jolt_plan / jolt_compress / jolt_decompress against the oracle.
+
+Free-running comparison (each side computes its own factors and allocation):
+  * factor subspaces: largest principal-angle sine <= 1e-2 for every leading
+    block whose eigengap exceeds 1e-3 of the top eigenvalue;
+  * ||X||^2 and the energy table agree to fp32 accuracy on the leading block;
+  * the chosen allocation fits the budget;
+  * the GPU reconstruction error <= 1.05 x the oracle's error + 1e-4.
+"""
+import ctypes
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import pipeline as opipe
+from tests.gpu_util import jolt_binding, out_values, rel, to_device, torch_cuda
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DELTA = json.load(open(os.path.join(ROOT, "tests", "golden", "delta_b.json")))["delta"]
+
+
+def _sine(A, B):
+    Qa = np.linalg.qr(A)[0]
+    Qb = np.linalg.qr(B)[0]
+    s = np.linalg.svd(Qa - Qb @ (Qb.T @ Qa), compute_uv=False)
+    return float(s.max()) if s.size else 0.0
+
+
+def _gap_blocks(lam, tol=1e-3):
+    """Leading block sizes r with lam[r-1] - lam[r] > tol * lam[0]."""
+    return [r for r in range(1, len(lam)) if lam[r - 1] - lam[r] > tol * lam[0]]
+
+
+def _fetch(torch, ptr, count, dtype=np.float32):
+    """Copy `count` values from a device pointer into a host numpy array."""
+    torch.cuda.synchronize()
+    out = np.empty(count, dtype=dtype)
+    hip = _hip()
+    rc = hip.hipMemcpy(out.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(ptr), out.nbytes, 2)
+    assert rc == 0
+    return out
+
+
+_HIP = None
+
+
+def _hip():
+    global _HIP
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _HIP.hipMemcpy.restype = ctypes.c_int
+    return _HIP
+
+
+@pytest.mark.parametrize("shape", [(2, 4, 512, 128, 64), (4, 8, 1024, 128, 128)], ids=["small", "c2shape"])
+def test_randomized_plan_parity(shape):
+    torch = torch_cuda()
+    jb = jolt_binding()
+    L, H, T, d, rt_max = shape
+    n_items = 4 if T < 1024 else 2
+    cfg = synth.config("mistral7b_gqa_1k", L=L, H=H, T=T, d=d)
+    items = synth.make_items(cfg, n_items)
+    budget = synth.budget_for_ratio(cfg, 2.0, n_items=n_items)
+    p = opipe.Params(mode="randomized", rt_max=rt_max, budget=budget, delta=DELTA)
+    ref = opipe.plan([i.x for i in items], [i.seed for i in items], [i.item_id for i in items], "bf16", p)
+    jitems = [jb.make_item(L, H, T, d, "bf16", i.item_id, i.seed) for i in items]
+    jcfg = jb.make_config("randomized", rt_max=rt_max, budget=budget, delta=DELTA)
+    J = jb.Jolt(jcfg, jitems)
+    xs = [to_device(i, torch) for i in items]
+    print("plan", shape, flush=True)
+    allocs, lam = J.plan(xs)
+    torch.cuda.synchronize()
+    assert J.status == jb.JOLT_OK
+    assert sum(a.bytes for a in allocs) <= budget
+    for i, (it, f) in enumerate(zip(items, ref.factors)):
+        v = J.factors(i)
+        Ut = _fetch(torch, v.ut, rt_max * T).reshape(rt_max, T).T
+        Uf = _fetch(torch, v.uf, d * d).reshape(d, d)
+        lam_t = _fetch(torch, v.lam_t, rt_max)
+        lam_f = _fetch(torch, v.lam_f, d)
+        nx2 = _fetch(torch, v.normx2, 1, np.float64)[0]
+        E = _fetch(torch, v.energy, rt_max * d).reshape(rt_max, d)
+        assert abs(nx2 / f.normX2 - 1) < 1e-5
+        assert np.max(np.abs(lam_f - f.lam_f)) <= 1e-4 * f.lam_f[0]
+        assert np.max(np.abs(lam_t - f.lam_t)) <= 1e-3 * f.lam_t[0]
+        assert np.max(np.abs(Ut.T @ Ut - np.eye(rt_max))) < 1e-3
+        assert np.max(np.abs(Uf.T @ Uf - np.eye(d))) < 1e-4
+        for r in _gap_blocks(f.lam_f):
+            assert _sine(Uf[:, :r], f.U_f[:, :r]) <= 1e-2, ("feature", r)
+        for r in _gap_blocks(f.lam_t):
+            assert _sine(Ut[:, :r], f.U_t[:, :r]) <= 1e-2, ("token", r)
+        assert np.max(np.abs(E - f.E)) <= 1e-3 * f.E.max()
+    # compress / decompress, free running
+    pays = J.alloc_payloads(allocs)
+    J.compress(xs, pays, allocs)
+    outs = [torch.empty_like(x) for x in xs]
+    J.decompress(pays, outs, allocs)
+    torch.cuda.synchronize()
+    for it, a, f, o, oa in zip(items, allocs, ref.factors, outs, ref.alloc):
+        enc = opipe.compress_item(it.x, f, oa, it.seed, it.item_id, "bf16")
+        xr = opipe.decompress_item(enc, it.x.shape, it.seed, it.item_id, "bf16")
+        e_ref = rel(xr, it.x)
+        e_gpu = rel(out_values(o, "bf16"), it.x)
+        print("item", it.item_id, "gpu", (a.rt, a.rf, a.bits), e_gpu, "oracle", oa, e_ref, flush=True)
+        assert e_gpu <= 1.05 * e_ref + 1e-4
+        hdr = pays[items.index(it)][:64].cpu().numpy().tobytes()
+        assert jb.jolt_payload_validate(hdr, jitems[items.index(it)], a) == jb.JOLT_OK
+    J.close()
