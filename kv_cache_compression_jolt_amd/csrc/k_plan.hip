@@ -544,16 +544,24 @@ __global__ void k_store(StoreBatch batch) {
 }
 
 // ====================================================================== launchers
-static int dyn_lds_set = 0;
-static void ensure_lds_attrs() {
-    if (dyn_lds_set) return;
-    hipFuncSetAttribute(reinterpret_cast<const void *>(k_jacobi_lds), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
-    hipFuncSetAttribute(reinterpret_cast<const void *>(k_cholesky), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
-    hipFuncSetAttribute(reinterpret_cast<const void *>(k_trsm), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
-    dyn_lds_set = 1;
+// Dynamic LDS above the default cap needs the per-kernel attribute; the cap
+// plus the kernel's static LDS must stay within the 160 KB of a workgroup.
+static hipError_t allow_dynamic_lds(const void *fn) {
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, fn);
+    if (e != hipSuccess) return e;
+    const int cap = 160 * 1024 - (int)fa.sharedSizeBytes;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+}
+static hipError_t ensure_lds_attrs() {
+    static hipError_t state = hipErrorNotReady;
+    if (state == hipErrorNotReady) {
+        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds));
+        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_cholesky));
+        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_trsm));
+        state = e;
+    }
+    return state;
 }
 
 template <typename T>
@@ -633,7 +641,7 @@ hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s) 
 
 hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    ensure_lds_attrs();
+    if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
     const size_t lds = (size_t)maxK * (maxK + 1) / 2 * sizeof(float);
     hipLaunchKernelGGL(k_cholesky, dim3(b.n), dim3(1024), lds, s, b);
     return hipGetLastError();
@@ -641,7 +649,7 @@ hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s) {
 
 hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    ensure_lds_attrs();
+    if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
     const size_t lds = (size_t)maxK * 33 * sizeof(float);
     hipLaunchKernelGGL(k_trsm, dim3((maxLen + 31) / 32, b.n), dim3(1024), lds, s, b);
     return hipGetLastError();
@@ -649,7 +657,7 @@ hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) 
 
 hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    ensure_lds_attrs();
+    if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
     const int m = maxN + (maxN & 1);
     const size_t lds = (size_t)2 * m * m * sizeof(float);
     hipLaunchKernelGGL(k_jacobi_lds, dim3(b.n), dim3(1024), lds, s, b, max_sweeps);
