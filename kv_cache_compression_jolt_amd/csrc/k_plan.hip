@@ -15,6 +15,8 @@
 // D[8 (j / 4) + 4 (l / 32) + j % 4][l % 32], j = 0..15.
 #include <float.h>
 
+#include <algorithm>
+
 #include "dev_common.h"
 #include "plan_kernels.h"
 
@@ -407,25 +409,34 @@ __global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_swe
                 sP[tid] = p; sQ[tid] = q; sC[tid] = c; sS[tid] = s;
             }
             __syncthreads();
-            for (int e = tid; e < half * half; e += nt) {
-                const int i = e / half, j = e % half;
-                const int pi = sP[i], qi = sQ[i], pj = sP[j], qj = sQ[j];
-                const float ci = sC[i], si = sS[i], cj = sC[j], sj = sS[j];
-                const float b00 = A[pi * m + pj], b01 = A[pi * m + qj], b10 = A[qi * m + pj], b11 = A[qi * m + qj];
-                const float m00 = cj * b00 - sj * b01, m01 = sj * b00 + cj * b01;
-                const float m10 = cj * b10 - sj * b11, m11 = sj * b10 + cj * b11;
-                float n00 = ci * m00 - si * m10, n01 = ci * m01 - si * m11;
-                float n10 = si * m00 + ci * m10, n11 = si * m01 + ci * m11;
-                if (i == j) { n01 = 0.f; n10 = 0.f; }
-                A[pi * m + pj] = n00; A[pi * m + qj] = n01; A[qi * m + pj] = n10; A[qi * m + qj] = n11;
+            // 32 x 32 thread grid: rows of pair blocks by ti, columns by tj
+            const int ti = tid >> 5, tj = tid & 31;
+            for (int i = ti; i < half; i += nt >> 5) {
+                const int pi = sP[i], qi = sQ[i];
+                const float ci = sC[i], si = sS[i];
+                float *rp = A + pi * m, *rq = A + qi * m;
+                for (int j = tj; j < half; j += 32) {
+                    const int pj = sP[j], qj = sQ[j];
+                    const float cj = sC[j], sj = sS[j];
+                    if (si == 0.f && sj == 0.f) continue;
+                    const float b00 = rp[pj], b01 = rp[qj], b10 = rq[pj], b11 = rq[qj];
+                    const float m00 = cj * b00 - sj * b01, m01 = sj * b00 + cj * b01;
+                    const float m10 = cj * b10 - sj * b11, m11 = sj * b10 + cj * b11;
+                    float n01 = ci * m01 - si * m11, n10 = si * m00 + ci * m10;
+                    if (i == j) { n01 = 0.f; n10 = 0.f; }
+                    rp[pj] = ci * m00 - si * m10; rp[qj] = n01;
+                    rq[pj] = n10; rq[qj] = si * m01 + ci * m11;
+                }
             }
-            for (int e = tid; e < m * half; e += nt) {
-                const int r = e / half, j = e % half;
+            for (int j = tj; j < half; j += 32) {
                 const int pj = sP[j], qj = sQ[j];
                 const float cj = sC[j], sj = sS[j];
-                const float a = V[r * m + pj], b = V[r * m + qj];
-                V[r * m + pj] = cj * a - sj * b;
-                V[r * m + qj] = sj * a + cj * b;
+                if (sj == 0.f) continue;
+                for (int r = ti; r < m; r += nt >> 5) {
+                    const float a = V[r * m + pj], b = V[r * m + qj];
+                    V[r * m + pj] = cj * a - sj * b;
+                    V[r * m + qj] = sj * a + cj * b;
+                }
             }
             __syncthreads();
         }
@@ -433,6 +444,15 @@ __global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_swe
         __syncthreads();
     }
     if (tid == 0 && it.sweeps_out) *it.sweeps_out = done ? sweeps : -1;
+    if (it.raw) {
+        // rotation close to the identity for a nearly diagonal input (block Jacobi inner solve)
+        for (int e = tid; e < n * n; e += nt) {
+            const int r = e / n, c = e % n;
+            it.vec[(size_t)r * it.ldv + c] = V[r * m + c];
+        }
+        for (int i = tid; i < n; i += nt) it.lam[i] = A[i * m + i];
+        return;
+    }
     // sort descending (ties by index), sign-normalise, write out
     for (int i = tid; i < n; i += nt) {
         const float li = A[i * m + i];
@@ -450,6 +470,94 @@ __global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_swe
         const float sg = V[best * m + i] < 0.f ? -1.f : 1.f;
         it.lam[rank] = li;
         for (int r = 0; r < n; ++r) it.vec[(size_t)r * it.ldv + rank] = sg * V[r * m + i];
+    }
+}
+
+// ====================================================================== block Jacobi helpers
+// Large symmetric problems (n > 142) run block Jacobi: the padded N x N matrix
+// (N = 64 NB) is kept with the block pairs of the current round adjacent, each
+// 128 x 128 pair sub-matrix is diagonalised by k_jacobi_lds, and the block
+// rotations are applied with the fp32 GEMM.  These kernels set up, permute,
+// measure and finish that iteration.
+
+// a[N][N] = g (n x n, ld) padded with zeros, v = I
+__global__ void k_eig_init(EigBatch batch) {
+    const EigItem &it = batch.it[blockIdx.y];
+    const int64_t NN = (int64_t)it.N * it.N;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < NN; e += (int64_t)gridDim.x * blockDim.x) {
+        const int r = (int)(e / it.N), c = (int)(e % it.N);
+        it.a[e] = (r < it.n && c < it.n) ? 0.5f * (it.g[(size_t)r * it.ldg + c] + it.g[(size_t)c * it.ldg + r]) : 0.f;
+        it.v[e] = (r == c) ? 1.f : 0.f;
+    }
+}
+
+// 64-wide blocks: a_out[B'][C'] = a_in[src[B']][src[C']], v_out[:, B'] = v_in[:, src[B']]
+__global__ void k_block_permute(EigBatch batch, BlockPerm perm) {
+    const EigItem &it = batch.it[blockIdx.y];
+    const int64_t NN = (int64_t)it.N * it.N;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < NN; e += (int64_t)gridDim.x * blockDim.x) {
+        const int r = (int)(e / it.N), c = (int)(e % it.N);
+        const int sr = perm.src[r >> 6] * 64 + (r & 63), sc = perm.src[c >> 6] * 64 + (c & 63);
+        it.t[e] = it.a[(size_t)sr * it.N + sc];
+        it.vt[e] = it.v[(size_t)r * it.N + sc];
+    }
+}
+
+// out[0] = sum of squares off the diagonal, out[1] = total
+__global__ void k_offnorm(EigBatch batch) {
+    const EigItem &it = batch.it[blockIdx.x];
+    __shared__ float s0[32], s1[32];
+    float off = 0.f, tot = 0.f;
+    const int64_t NN = (int64_t)it.N * it.N;
+    for (int64_t e = threadIdx.x; e < NN; e += blockDim.x) {
+        const float v = it.a[e];
+        const float q = v * v;
+        tot += q;
+        if (e / it.N != e % it.N) off += q;
+    }
+    for (int o = 32; o > 0; o >>= 1) { off += __shfl_xor(off, o); tot += __shfl_xor(tot, o); }
+    if ((threadIdx.x & 63) == 0) { s0[threadIdx.x >> 6] = off; s1[threadIdx.x >> 6] = tot; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = 0.f, b = 0.f;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) { a += s0[w]; b += s1[w]; }
+        it.norms[0] = a;
+        it.norms[1] = b;
+    }
+}
+
+// eigenpairs (diag(a), v columns) sorted descending, padding vectors last,
+// columns sign-normalised; vec[r][c] (ld ldv) for r, c < n, lam[c]
+__global__ void k_eig_finish(EigBatch batch) {
+    const EigItem &it = batch.it[blockIdx.y];
+    const int N = it.N, n = it.n;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < N; i += gridDim.x * blockDim.x) {
+        // a padding vector has its weight on rows >= n
+        float wpad = 0.f;
+        for (int r = n; r < N; ++r) wpad += it.v[(size_t)r * N + i] * it.v[(size_t)r * N + i];
+        const bool pad = wpad > 0.5f;
+        const float li = it.a[(size_t)i * N + i];
+        int rank = 0;
+        for (int j = 0; j < N; ++j) {
+            float wj = 0.f;
+            for (int r = n; r < N; ++r) wj += it.v[(size_t)r * N + j] * it.v[(size_t)r * N + j];
+            const bool pj = wj > 0.5f;
+            const float lj = it.a[(size_t)j * N + j];
+            bool before;
+            if (pad != pj) before = !pj;                // real vectors first
+            else before = (lj > li) || (lj == li && j < i);
+            rank += before;
+        }
+        if (pad || rank >= n) continue;
+        int best = 0;
+        float bm = -1.f;
+        for (int r = 0; r < n; ++r) {
+            const float v = fabsf(it.v[(size_t)r * N + i]);
+            if (v > bm) { bm = v; best = r; }
+        }
+        const float sg = it.v[(size_t)best * N + i] < 0.f ? -1.f : 1.f;
+        it.lam[rank] = li;
+        for (int r = 0; r < n; ++r) it.vec[(size_t)r * it.ldv + rank] = sg * it.v[(size_t)r * N + i];
     }
 }
 
@@ -661,6 +769,27 @@ hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStr
     const int m = maxN + (maxN & 1);
     const size_t lds = (size_t)2 * m * m * sizeof(float);
     hipLaunchKernelGGL(k_jacobi_lds, dim3(b.n), dim3(1024), lds, s, b, max_sweeps);
+    return hipGetLastError();
+}
+
+hipError_t launch_eig_init(const EigBatch &b, int maxN, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_eig_init, dim3(std::min(1024, (maxN * maxN + 255) / 256), b.n), dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+hipError_t launch_block_permute(const EigBatch &b, const BlockPerm &p, int maxN, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_block_permute, dim3(std::min(2048, (maxN * maxN + 255) / 256), b.n), dim3(256), 0, s, b, p);
+    return hipGetLastError();
+}
+hipError_t launch_offnorm(const EigBatch &b, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_offnorm, dim3(b.n), dim3(1024), 0, s, b);
+    return hipGetLastError();
+}
+hipError_t launch_eig_finish(const EigBatch &b, int maxN, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_eig_finish, dim3((maxN + 63) / 64, b.n), dim3(64), 0, s, b);
     return hipGetLastError();
 }
 

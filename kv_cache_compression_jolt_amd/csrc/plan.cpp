@@ -50,7 +50,14 @@ struct Dims {
 struct Scratch {
     size_t omt, yt, qh, ql, zt, zb, xpart, gpart, gram, lmat, wmat, vmat, lamk, sweeps;
     size_t gfpart, gf, pmat, gt, vt, lamT, uh, ul;
+    size_t eA, eT, eV, eVT, eR, eRlam, eNorm, eSw;     // block Jacobi (n > 142)
+    int eN;                                             // padded size, 0 if unused
 };
+
+// size of the eigenproblem solved for the token factor
+int token_eig_n(const jolt_config &cfg, const Dims &D) {
+    return cfg.mode == JOLT_TOKEN_RANDOMIZED ? D.k : D.T;
+}
 
 int clampi(int v, int lo, int hi) { return std::max(lo, std::min(hi, v)); }
 
@@ -112,6 +119,20 @@ void reserve_scratch(const jolt_config &cfg, const Dims &D, Bump &b, Scratch &s)
         s.pmat = b.take((size_t)D.rtp32 * n * 4);
     }
     s.sweeps = b.take(16);
+    const int ne = token_eig_n(cfg, D);
+    s.eN = 0;
+    if (ne > kJacobiMaxN) {
+        const size_t N = (size_t)round_up(ne, 128), P = N / 128;
+        s.eN = (int)N;
+        s.eA = b.take(N * N * 4);
+        s.eT = b.take(N * N * 4);
+        s.eV = b.take(N * N * 4);
+        s.eVT = b.take(N * N * 4);
+        s.eR = b.take(P * 128 * 128 * 4);
+        s.eRlam = b.take(P * 128 * 4);
+        s.eNorm = b.take(16);
+        s.eSw = b.take(P * 4);
+    }
 }
 
 struct Ctx {
@@ -158,9 +179,9 @@ jolt_status check_config(jolt_handle h, const jolt_config &cfg, const jolt_item 
             const int k = cfg.rt_max + cfg.oversample;
             if (k < 1 || k > it.T || k > it.L * it.H * it.d)
                 return fail(h, JOLT_E_INVALID, "sketch width rt_max + oversample must be in [1, min(T, L H d)]");
-            if (k > kJacobiMaxN) return fail(h, JOLT_E_UNSUPPORTED, "sketch width above %d not supported", kJacobiMaxN);
+            if (k > 2048) return fail(h, JOLT_E_UNSUPPORTED, "sketch width above 2048 not supported");
         } else {
-            if (it.T > kJacobiMaxN) return fail(h, JOLT_E_UNSUPPORTED, "exact mode: T above %d not supported", kJacobiMaxN);
+            if (it.T > 2048) return fail(h, JOLT_E_UNSUPPORTED, "exact mode: T above 2048 not supported (T x T eigensolve)");
         }
     }
     return JOLT_OK;
@@ -208,6 +229,152 @@ jolt_status plan_layout(const jolt_config &cfg, const jolt_item *items, int n, P
 // ------------------------------------------------------------------ device pipeline
 namespace {
 
+
+// ------------------------------------------------------------------ eigensolvers
+// Symmetric eigen-decompositions (descending, sign-normalised eigenvectors).
+// n <= 142: one workgroup per matrix, Jacobi in LDS (k_jacobi_lds).
+// n > 142: block Jacobi over 64-wide blocks (see k_plan.hip): every round the
+// pair sub-matrices (128 x 128) are diagonalised in LDS and the rotations are
+// applied to the whole matrix and to V with the fp32 GEMM; sweeps repeat until
+// off(A) <= 4e-6 ||A||_F (checked on the host once per sweep).
+struct EigReq {
+    const float *g;
+    int ldg, n;
+    float *vec;
+    int ldv;
+    float *lam;
+    int *sw;
+    const Scratch *S;
+};
+
+int rr_pos_host(int i, int round, int m) {
+    if (i == 0) return 0;
+    return 1 + (((i - 1 - round) % (m - 1)) + (m - 1)) % (m - 1);
+}
+
+jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint8_t *scr, int max_sweeps,
+                      bool *noconv) {
+    auto F = [&](size_t off) { return reinterpret_cast<float *>(scr + off); };
+    EigBatch eb{};
+    for (const EigReq &r : reqs) {
+        EigItem &e = eb.it[eb.n++];
+        e.g = r.g; e.ldg = r.ldg; e.n = r.n; e.N = N;
+        e.a = F(r.S->eA); e.t = F(r.S->eT); e.v = F(r.S->eV); e.vt = F(r.S->eVT);
+        e.norms = F(r.S->eNorm); e.vec = r.vec; e.ldv = r.ldv; e.lam = r.lam;
+    }
+    HIPCHK(launch_eig_init(eb, N, c.st), "eig init");
+    const int NB = N / 64, P = N / 128;
+    std::vector<int> cur(NB), desired(NB);
+    for (int b = 0; b < NB; ++b) cur[b] = b;
+    const float tol2 = 4e-6f * 4e-6f;
+    bool converged = false;
+    const int inner_sweeps = 4;
+    for (int sweep = 0; sweep < max_sweeps && !converged; ++sweep) {
+        for (int round = 0; round < NB - 1; ++round) {
+            for (int p = 0; p < NB / 2; ++p) {
+                desired[2 * p] = rr_pos_host(p, round, NB);
+                desired[2 * p + 1] = rr_pos_host(NB - 1 - p, round, NB);
+            }
+            BlockPerm bp{};
+            for (int b = 0; b < NB; ++b)
+                for (int q = 0; q < NB; ++q)
+                    if (cur[q] == desired[b]) bp.src[b] = q;
+            HIPCHK(launch_block_permute(eb, bp, N, c.st), "eig permute");
+            for (int i = 0; i < eb.n; ++i) {
+                std::swap(eb.it[i].a, eb.it[i].t);
+                std::swap(eb.it[i].v, eb.it[i].vt);
+            }
+            cur = desired;
+            // pair sub-problems
+            JacBatch jb{};
+            for (size_t i = 0; i < reqs.size(); ++i) {
+                for (int p = 0; p < P; ++p) {
+                    JacItem &j = jb.it[jb.n++];
+                    j.a = eb.it[i].a + (size_t)128 * p * N + 128 * p;
+                    j.lda = N;
+                    j.vec = F(reqs[i].S->eR) + (size_t)p * 128 * 128;
+                    j.ldv = 128;
+                    j.lam = F(reqs[i].S->eRlam) + 128 * p;
+                    j.n = 128;
+                    j.raw = 1;
+                    j.sweeps_out = reinterpret_cast<int *>(scr + reqs[i].S->eSw) + p;
+                    if (jb.n == 64) {
+                        HIPCHK(launch_jacobi_lds(jb, 128, inner_sweeps, c.st), "eig pairs");
+                        jb.n = 0;
+                    }
+                }
+            }
+            HIPCHK(launch_jacobi_lds(jb, 128, inner_sweeps, c.st), "eig pairs");
+            // A <- J^T A J (rows into t, then columns back into a), V <- V J
+            GemmBatch rows{}, cols{}, vup{};
+            for (size_t i = 0; i < reqs.size(); ++i) {
+                const float *R = F(reqs[i].S->eR);
+                EigItem &e = eb.it[i];
+                GemmItem &g = rows.it[rows.n++];
+                g.a = R; g.a_i = 1; g.a_k = 128; g.a_z = 128 * 128;
+                g.b = e.a; g.b_k = N; g.b_j = 1; g.b_z = (int64_t)128 * N;
+                g.c = e.t; g.c_i = N; g.c_j = 1; g.c_z = (int64_t)128 * N; g.c_split = 0;
+                g.M = 128; g.N = N; g.K = 128; g.kchunk = 128; g.nsplit = 1; g.nb = P;
+                GemmItem &h = cols.it[cols.n++];
+                h.a = e.t; h.a_i = N; h.a_k = 1; h.a_z = 128;
+                h.b = R; h.b_k = 128; h.b_j = 1; h.b_z = 128 * 128;
+                h.c = e.a; h.c_i = N; h.c_j = 1; h.c_z = 128; h.c_split = 0;
+                h.M = N; h.N = 128; h.K = 128; h.kchunk = 128; h.nsplit = 1; h.nb = P;
+                GemmItem &v = vup.it[vup.n++];
+                v = h;
+                v.a = e.v; v.c = e.vt;
+            }
+            HIPCHK(launch_gemm(rows, 128, N, 1, P, c.st), "eig rows");
+            HIPCHK(launch_gemm(cols, N, 128, 1, P, c.st), "eig cols");
+            HIPCHK(launch_gemm(vup, N, 128, 1, P, c.st), "eig vectors");
+            for (int i = 0; i < eb.n; ++i) std::swap(eb.it[i].v, eb.it[i].vt);
+        }
+        HIPCHK(launch_offnorm(eb, c.st), "eig offnorm");
+        converged = true;
+        for (int i = 0; i < eb.n; ++i) {
+            float nr[2];
+            HIPCHK(hipMemcpyAsync(nr, eb.it[i].norms, sizeof nr, hipMemcpyDeviceToHost, c.st), "eig norms");
+            HIPCHK(hipStreamSynchronize(c.st), "eig norms");
+            if (!(nr[0] <= tol2 * nr[1])) converged = false;
+        }
+    }
+    if (!converged && noconv) *noconv = true;
+    HIPCHK(launch_eig_finish(eb, N, c.st), "eig finish");
+    return JOLT_OK;
+}
+
+jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr, int max_sweeps, bool *noconv) {
+    JacBatch jb{};
+    int maxN = 0;
+    std::vector<std::vector<EigReq>> large;
+    std::vector<int> largeN;
+    for (const EigReq &r : reqs) {
+        if (r.n <= kJacobiMaxN) {
+            JacItem &j = jb.it[jb.n++];
+            j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
+            j.raw = 0;
+            maxN = std::max(maxN, r.n);
+            if (jb.n == 64) {
+                HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
+                jb.n = 0;
+                maxN = 0;
+            }
+        } else {
+            const int N = round_up(r.n, 128);
+            size_t g = 0;
+            while (g < largeN.size() && largeN[g] != N) ++g;
+            if (g == largeN.size()) { largeN.push_back(N); large.emplace_back(); }
+            large[g].push_back(r);
+        }
+    }
+    HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
+    for (size_t g = 0; g < large.size(); ++g) {
+        jolt_status s = eig_block(c, large[g], largeN[g], scr, max_sweeps, noconv);
+        if (s) return s;
+    }
+    return JOLT_OK;
+}
+
 jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, const int *k,
                       const int *kp, const int *len, const int *split, const int *chunk, int passes) {
     for (int pass = 0; pass < passes; ++pass) {
@@ -245,7 +412,8 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
 }
 
 jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items, int i0,
-                      int nb, const void *const *x_dev, uint8_t *ws) {
+                      int nb, const void *const *x_dev, uint8_t *ws, bool *noconv) {
+    const int max_sweeps = cfg.max_sweeps > 0 ? cfg.max_sweeps : 30;
     const int d = c.d, dt = c.dtype;
     const bool bf = dt == JOLT_BF16;
     std::vector<Dims> D(nb);
@@ -260,7 +428,11 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
     auto F = [&](size_t off) { return reinterpret_cast<float *>(scr + off); };
     auto W = [&](int i, size_t off) { return ws + off; };
     int maxT = 0, maxLH = 0;
-    for (int i = 0; i < nb; ++i) { maxT = std::max(maxT, D[i].T); maxLH = std::max(maxLH, D[i].LH); }
+    for (int i = 0; i < nb; ++i) {
+        maxT = std::max(maxT, D[i].T);
+        maxLH = std::max(maxLH, D[i].LH);
+        HIPCHK(launch_zero(P(S[i].sweeps), 16, c.st), "zero sweeps");
+    }
 
     // ---- feature Gram, ||X||^2
     {
@@ -281,16 +453,13 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         for (int i = 0; i < nb; ++i)
             HIPCHK(launch_trace(F(S[i].gf), d, reinterpret_cast<double *>(W(i, pl.item[i0 + i].normx2)), c.st),
                    "trace");
-        JacBatch jb{};
-        for (int i = 0; i < nb; ++i) {
-            JacItem &j = jb.it[jb.n++];
-            j.a = F(S[i].gf); j.vec = reinterpret_cast<float *>(ws + pl.item[i0 + i].uf);
-            j.lam = reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_f);
-            j.n = d; j.lda = d; j.ldv = d;
-            j.sweeps_out = reinterpret_cast<int *>(P(S[i].sweeps));
-        }
-        HIPCHK(launch_jacobi_lds(jb, d, cfg.max_sweeps > 0 ? cfg.max_sweeps : 30, c.st), "feature eig");
     }
+    // feature eigenproblems join the token eigenproblems in one launch
+    std::vector<EigReq> eigs;
+    for (int i = 0; i < nb; ++i)
+        eigs.push_back(EigReq{F(S[i].gf), d, d, reinterpret_cast<float *>(ws + pl.item[i0 + i].uf), d,
+                              reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_f),
+                              reinterpret_cast<int *>(P(S[i].sweeps)), &S[i]});
 
     if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
         std::vector<float *> yv(nb), zv(nb), gram(nb), gpart(nb), lmat(nb);
@@ -400,14 +569,11 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             }
             HIPCHK(launch_gemm(gb, maxK, maxK, maxS, 1, c.st), "B B^T");
             HIPCHK(launch_reduce(rb, maxCount, c.st), "B B^T reduce");
-            JacBatch jb{};
-            for (int i = 0; i < nb; ++i) {
-                JacItem &j = jb.it[jb.n++];
-                j.a = F(S[i].wmat); j.vec = F(S[i].vmat); j.lam = F(S[i].lamk);
-                j.n = D[i].k; j.lda = D[i].kp; j.ldv = D[i].kp;
-                j.sweeps_out = reinterpret_cast<int *>(P(S[i].sweeps)) + 1;
-            }
-            HIPCHK(launch_jacobi_lds(jb, maxK, cfg.max_sweeps > 0 ? cfg.max_sweeps : 30, c.st), "small eig");
+            for (int i = 0; i < nb; ++i)
+                eigs.push_back(EigReq{F(S[i].wmat), D[i].kp, D[i].k, F(S[i].vmat), D[i].kp, F(S[i].lamk),
+                                      reinterpret_cast<int *>(P(S[i].sweeps)) + 1, &S[i]});
+            jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
+            if (es) return es;
         }
         // U_t^T = U~^T Q, P = U~^T B, lambda_t
         {
@@ -433,7 +599,62 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             }
         }
     } else {
-        return fail(c.h, JOLT_E_UNSUPPORTED, "exact token mode is not available in this build");
+        // exact token factor: eigenvectors of G_t = A A^T (T x T)
+        XmBatch xb{};
+        int maxC = 0;
+        for (int i = 0; i < nb; ++i) {
+            XmItem &x = xb.it[xb.n++];
+            x.x = x_dev[i0 + i]; x.m = x_dev[i0 + i]; x.out = F(S[i].gt);
+            x.m_c = d; x.m_blk = (int64_t)D[i].T * d;
+            x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].T; x.ldo = D[i].T;
+            maxC = std::max(maxC, x.ncols);
+        }
+        HIPCHK(launch_xm(xb, dt, d, maxT, maxC, c.st), "token Gram");
+        for (int i = 0; i < nb; ++i)
+            eigs.push_back(EigReq{F(S[i].gt), D[i].T, D[i].T, F(S[i].vt), D[i].T, F(S[i].lamT),
+                                  reinterpret_cast<int *>(P(S[i].sweeps)) + 1, &S[i]});
+        jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
+        if (es) return es;
+        // U_t^T rows = leading eigenvectors; P = U_t^T A (hi + lo split for bf16 caches)
+        XtqBatch qb{};
+        ReduceBatch rb{};
+        int maxS = 0, maxCols = 0;
+        int64_t maxCount = 0;
+        for (int i = 0; i < nb; ++i) {
+            float *ut = reinterpret_cast<float *>(ws + pl.item[i0 + i].ut);
+            HIPCHK(launch_transpose(F(S[i].vt), ut, D[i].T, pl.rt_max, D[i].T, D[i].T, c.st), "U_t");
+            HIPCHK(hipMemcpyAsync(ws + pl.item[i0 + i].lam_t, P(S[i].lamT), (size_t)pl.rt_max * 4,
+                                  hipMemcpyDeviceToDevice, c.st), "lambda_t");
+            const int64_t rows_pad = (int64_t)D[i].rtp32 * D[i].T;
+            if (bf) {
+                HIPCHK(launch_zero(P(S[i].uh), rows_pad * 2, c.st), "zero");
+                HIPCHK(launch_zero(P(S[i].ul), rows_pad * 2, c.st), "zero");
+                HIPCHK(launch_to_bf16(ut, reinterpret_cast<uint16_t *>(P(S[i].uh)),
+                                      reinterpret_cast<uint16_t *>(P(S[i].ul)), (int64_t)pl.rt_max * D[i].T, c.st),
+                       "U_t split");
+            } else {
+                HIPCHK(launch_zero(P(S[i].uh), rows_pad * 4, c.st), "zero");
+                HIPCHK(hipMemcpyAsync(P(S[i].uh), ut, (size_t)pl.rt_max * D[i].T * 4, hipMemcpyDeviceToDevice, c.st),
+                       "U_t copy");
+            }
+            XtqItem &x = qb.it[qb.n++];
+            x.x = x_dev[i0 + i]; x.qh = P(S[i].uh); x.ql = bf ? (const void *)P(S[i].ul) : nullptr;
+            x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].rtp32; x.ldq = D[i].T;
+            x.tsplit = D[i].xs_tsplit; x.nsplit = D[i].xs_split;
+            x.out = x.nsplit == 1 ? F(S[i].pmat) : F(S[i].xpart);
+            maxS = std::max(maxS, x.nsplit);
+            maxCols = std::max(maxCols, x.ncols);
+            if (x.nsplit > 1) {
+                ReduceItem &r = rb.it[rb.n++];
+                r.part = F(S[i].xpart); r.out = F(S[i].pmat);
+                r.stride = (int64_t)D[i].rtp32 * D[i].n; r.count = r.stride; r.nsplit = x.nsplit;
+                maxCount = std::max(maxCount, r.count);
+            }
+        }
+        if (pl.rt_max > 0) {
+            HIPCHK(launch_xtq(qb, dt, d, maxLH, maxS, maxCols, c.st), "U_t^T A");
+            HIPCHK(launch_reduce(rb, maxCount, c.st), "U_t^T A reduce");
+        }
     }
 
     // core[lh] = P[:, lh d : lh d + d] U_f, energy
@@ -518,7 +739,7 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     bool noconv = false;
     for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
         const int nb = std::min(kMaxBatch, n - c0);
-        s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws);
+        s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv);
         if (s) return s;
         // sweep counters of this chunk (the chunk's scratch is reused by the next one)
         std::vector<Scratch> S(nb);

@@ -91,11 +91,28 @@ struct JacItem {
     float *vec;
     float *lam;
     int n, lda, ldv;
+    int raw;             // 1: eigenpairs in Jacobi order (no sort / sign change)
     int *sweeps_out;     // sweeps used, or -1 if the cap was hit
 };
 struct JacBatch { JacItem it[64]; int n; };
 constexpr int kJacobiMaxN = 142;
 hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s);
+
+// block Jacobi state of one large symmetric matrix (N = padded size, multiple of 128)
+struct EigItem {
+    const float *g;      // input n x n (ld ldg)
+    float *a, *t;        // N x N working matrix and its permuted copy
+    float *v, *vt;       // N x N rotations and its permuted copy
+    float *norms;        // [2]: off-diagonal and total sum of squares
+    float *vec, *lam;    // outputs: n x n (ld ldv) and n
+    int n, N, ldg, ldv;
+};
+struct EigBatch { EigItem it[kMaxBatch]; int n; };
+struct BlockPerm { int src[32]; };
+hipError_t launch_eig_init(const EigBatch &b, int maxN, hipStream_t s);
+hipError_t launch_block_permute(const EigBatch &b, const BlockPerm &p, int maxN, hipStream_t s);
+hipError_t launch_offnorm(const EigBatch &b, hipStream_t s);
+hipError_t launch_eig_finish(const EigBatch &b, int maxN, hipStream_t s);
 
 // elementwise conversions
 hipError_t launch_to_bf16(const float *in, uint16_t *hi, uint16_t *lo, int64_t count, hipStream_t s);
