@@ -14,6 +14,7 @@
 // indices k0 + 8 (l / 32) + i; the 32x32 fp32 result sits at
 // D[8 (j / 4) + 4 (l / 32) + j % 4][l % 32], j = 0..15.
 #include <float.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -309,44 +310,85 @@ __global__ __launch_bounds__(1024) void k_cholesky(CholBatch batch) {
         lp[e] = v;
     }
     __syncthreads();
-    const int wave = tid >> 6, lane = tid & 63, nw = nt >> 6;
+    // Column j is left unscaled while it updates the trailing triangle
+    // (L(i,c) -= L(i,j) L(c,j) / d_j with d_j the pivot before the square root);
+    // every column is scaled by 1 / sqrt(d_j) at the end.  One barrier per column.
+    const int ti = tid >> 5, tj = tid & 31, nti = nt >> 5;
     for (int j = 0; j < k; ++j) {
         const int jj = j * (j + 1) / 2 + j;
-        if (tid == 0) lp[jj] = sqrtf(fmaxf(lp[jj], shift));
-        __syncthreads();
-        const float piv = lp[jj];
-        for (int i = j + 1 + tid; i < k; i += nt) lp[i * (i + 1) / 2 + j] /= piv;
-        __syncthreads();
-        for (int i = j + 1 + wave; i < k; i += nw) {
-            const float lij = lp[i * (i + 1) / 2 + j];
+        const float dj = fmaxf(lp[jj], shift);
+        const float rdj = 1.f / dj;
+        for (int i = j + 1 + ti; i < k; i += nti) {
+            const float lij = lp[i * (i + 1) / 2 + j] * rdj;
             float *row = lp + i * (i + 1) / 2;
-            for (int c = j + 1 + lane; c <= i; c += 64) row[c] -= lij * lp[c * (c + 1) / 2 + j];
+            for (int c = j + 1 + tj; c <= i; c += 32) row[c] -= lij * lp[c * (c + 1) / 2 + j];
+        }
+        __syncthreads();
+    }
+    // scale the columns: L(i, j) = lp(i, j) / sqrt(d_j), L(j, j) = sqrt(d_j)
+    for (int e = tid; e < k * (k + 1) / 2; e += nt) {
+        int i = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
+        while (i * (i + 1) / 2 > e) --i;
+        while ((i + 1) * (i + 2) / 2 <= e) ++i;
+        const int j = e - i * (i + 1) / 2;
+        const float dj = fmaxf(lp[j * (j + 1) / 2 + j], shift);
+        const float v = (i == j) ? sqrtf(dj) : lp[e] / sqrtf(dj);
+        if (!it.inverse) it.l[(size_t)i * it.ld + j] = v;
+        else lp[k * (k + 1) / 2 + e] = v;      // scaled L goes to the second half
+    }
+    if (!it.inverse) {
+        for (int e = tid; e < k * k; e += nt) {
+            const int i = e / k, j = e % k;
+            if (j > i) it.l[(size_t)i * it.ld + j] = 0.f;
+        }
+        return;
+    }
+    __syncthreads();
+    // X = L^{-1} by rows: X[i][j] = (delta_ij - sum_{c=j}^{i-1} L[i][c] X[c][j]) / L[i][i];
+    // 32 lanes per output element, one barrier per row.  L (packed) now sits in the
+    // second half of the LDS block, X overwrites the first half.
+    const float *lq = lp + k * (k + 1) / 2;
+    float *xp = lp;
+    const int grp = tid >> 5, ln = tid & 31, ngrp = nt >> 5;
+    for (int i = 0; i < k; ++i) {
+        const float *li = lq + i * (i + 1) / 2;
+        const float rii = 1.f / li[i];
+        for (int j = grp; j <= i; j += ngrp) {
+            float acc = 0.f;
+            for (int c = j + ln; c < i; c += 32) acc = fmaf(li[c], xp[c * (c + 1) / 2 + j], acc);
+            for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 32);
+            if (ln == 0) xp[i * (i + 1) / 2 + j] = ((i == j ? 1.f : 0.f) - acc) * rii;
         }
         __syncthreads();
     }
     for (int e = tid; e < k * k; e += nt) {
         const int i = e / k, j = e % k;
-        it.l[(size_t)i * it.ld + j] = (j <= i) ? lp[i * (i + 1) / 2 + j] : 0.f;
+        it.l[(size_t)i * it.ld + j] = (j <= i) ? xp[i * (i + 1) / 2 + j] : 0.f;
     }
 }
 
 // ====================================================================== triangular solve
 // WG: 32 columns of y; 1024 threads = 32 columns x 32 partial-sum lanes.
 // Row i of the result: q[i] = (y[i] - sum_{c<i} L[i][c] q[c]) / L[i][i].
-__global__ __launch_bounds__(1024) void k_trsm(TrsmBatch batch) {
-    extern __shared__ float qs[];             // [k][33]
+__global__ __launch_bounds__(1024) void k_trsm(TrsmBatch batch, int l_in_lds) {
+    extern __shared__ float sh[];
     const TrsmItem &it = batch.it[blockIdx.y];
     const int t0 = blockIdx.x * 32;
     if (t0 >= it.len) return;
     const int tid = threadIdx.x, col = tid >> 5, cl = tid & 31;
     const int k = it.k;
+    float *qs = sh;                        // [k][33]
+    float *ls = sh + k * 33;               // packed lower triangle of L (when it fits)
     for (int e = tid; e < k * 32; e += 1024) {
         const int r = e / 32, c = e % 32;
         qs[r * 33 + c] = (t0 + c < it.len) ? it.y[(size_t)r * it.ldy + t0 + c] : 0.f;
     }
+    if (l_in_lds)
+        for (int i = tid >> 5; i < k; i += 32)
+            for (int c = tid & 31; c <= i; c += 32) ls[i * (i + 1) / 2 + c] = it.l[(size_t)i * it.ld + c];
     __syncthreads();
     for (int i = 0; i < k; ++i) {
-        const float *li = it.l + (size_t)i * it.ld;
+        const float *li = l_in_lds ? ls + i * (i + 1) / 2 : it.l + (size_t)i * it.ld;
         float s = 0.f;
         for (int c = cl; c < i; c += 32) s = fmaf(li[c], qs[c * 33 + col], s);
         for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
@@ -356,6 +398,29 @@ __global__ __launch_bounds__(1024) void k_trsm(TrsmBatch batch) {
     for (int e = tid; e < k * 32; e += 1024) {
         const int r = e / 32, c = e % 32;
         if (t0 + c < it.len) it.q[(size_t)r * it.ldy + t0 + c] = qs[r * 33 + c];
+    }
+}
+
+// ====================================================================== y <- L^{-1} y (explicit inverse)
+// WG of 256 threads owns 64 columns of y[k][len] for all k rows: loads them to
+// LDS, multiplies by the lower-triangular X = L^{-1} (rows of X read from
+// global memory, shared by all lanes) and writes back in place.
+__global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch) {
+    extern __shared__ float ys[];          // [k][65]
+    const TrsmItem &it = batch.it[blockIdx.y];
+    const int t0 = blockIdx.x * 64;
+    if (t0 >= it.len) return;
+    const int k = it.k, tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int e = threadIdx.x; e < k * 64; e += 256) {
+        const int r = e >> 6, c = e & 63;
+        ys[r * 65 + c] = (t0 + c < it.len) ? it.y[(size_t)r * it.ldy + t0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int i = ty; i < k; i += 4) {
+        const float *xi = it.l + (size_t)i * it.ld;
+        float acc = 0.f;
+        for (int c = 0; c <= i; ++c) acc = fmaf(xi[c], ys[c * 65 + tx], acc);
+        if (t0 + tx < it.len) it.q[(size_t)i * it.ldy + t0 + tx] = acc;
     }
 }
 
@@ -371,34 +436,51 @@ __device__ __forceinline__ int rr_pos(int i, int round, int m) {
     return 1 + ((i - 1 - round) % (m - 1) + (m - 1)) % (m - 1);
 }
 
-__global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_sweeps) {
+template <int NT>
+__global__ __launch_bounds__(NT) void k_jacobi_lds(JacBatch batch, int max_sweeps) {
     extern __shared__ float sm[];
     __shared__ int sP[kJacobiMaxN / 2 + 1], sQ[kJacobiMaxN / 2 + 1];
     __shared__ float sC[kJacobiMaxN / 2 + 1], sS[kJacobiMaxN / 2 + 1];
     __shared__ int s_rot;
     const JacItem &it = batch.it[blockIdx.x];
     const int n = it.n, m = n + (n & 1), half = m / 2;
-    const int tid = threadIdx.x, nt = blockDim.x;
-    float *A = sm, *V = sm + m * m;
+    const int tid = threadIdx.x;
+    constexpr int nt = NT;
+    __shared__ float s_fro[32];
+    float *A = sm, *Vt = sm + m * m;           // Vt[c][r] = component r of vector c
+    float fro = 0.f;
     for (int e = tid; e < m * m; e += nt) {
         const int r = e / m, c = e % m;
-        A[e] = (r < n && c < n) ? 0.5f * (it.a[(size_t)r * it.lda + c] + it.a[(size_t)c * it.lda + r]) : 0.f;
-        V[e] = (r == c) ? 1.f : 0.f;
+        const float v = (r < n && c < n) ? 0.5f * (it.a[(size_t)r * it.lda + c] + it.a[(size_t)c * it.lda + r]) : 0.f;
+        A[e] = v;
+        fro += v * v;
+        Vt[e] = (r == c) ? 1.f : 0.f;
+    }
+    for (int o = 32; o > 0; o >>= 1) fro += __shfl_xor(fro, o);
+    if ((tid & 63) == 0) s_fro[tid >> 6] = fro;
+    __syncthreads();
+    if (tid == 0) {
+        float t = 0.f;
+        for (int w = 0; w < (nt >> 6); ++w) t += s_fro[w];
+        s_fro[0] = sqrtf(t);
     }
     __syncthreads();
     const float tol = 1.0e-6f;
+    // below this an off-diagonal entry is at the fp32 rounding level of the whole matrix
+    const float abs_floor = 2.0e-7f * s_fro[0];
     int sweeps = 0;
     bool done = false;
     for (; sweeps < max_sweeps && !done; ++sweeps) {
         if (tid == 0) s_rot = 0;
         __syncthreads();
         for (int round = 0; round < m - 1; ++round) {
-            if (tid < half) {
-                int p = rr_pos(tid, round, m), q = rr_pos(m - 1 - tid, round, m);
+            for (int pr = tid; pr < half; pr += nt) {
+                int p = rr_pos(pr, round, m), q = rr_pos(m - 1 - pr, round, m);
                 if (p > q) { const int t = p; p = q; q = t; }
                 const float apq = A[p * m + q], app = A[p * m + p], aqq = A[q * m + q];
                 float c = 1.f, s = 0.f;
-                if (fabsf(apq) > tol * sqrtf(fabsf(app) * fabsf(aqq)) && fabsf(apq) > 1e-30f) {
+                if (fabsf(apq) > tol * sqrtf(fabsf(app) * fabsf(aqq)) && fabsf(apq) > abs_floor &&
+                    fabsf(apq) > 1e-30f) {
                     const float tau = (aqq - app) / (2.f * apq);
                     const float t = (tau >= 0.f) ? 1.f / (tau + sqrtf(1.f + tau * tau))
                                                  : -1.f / (-tau + sqrtf(1.f + tau * tau));
@@ -406,7 +488,7 @@ __global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_swe
                     s = t * c;
                     s_rot = 1;
                 }
-                sP[tid] = p; sQ[tid] = q; sC[tid] = c; sS[tid] = s;
+                sP[pr] = p; sQ[pr] = q; sC[pr] = c; sS[pr] = s;
             }
             __syncthreads();
             // 32 x 32 thread grid: rows of pair blocks by ti, columns by tj
@@ -428,14 +510,15 @@ __global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_swe
                     rq[pj] = n10; rq[qj] = si * m01 + ci * m11;
                 }
             }
-            for (int j = tj; j < half; j += 32) {
-                const int pj = sP[j], qj = sQ[j];
+            // V <- V J on the transposed copy: two contiguous rows per pair
+            for (int j = ti; j < half; j += nt >> 5) {
                 const float cj = sC[j], sj = sS[j];
                 if (sj == 0.f) continue;
-                for (int r = ti; r < m; r += nt >> 5) {
-                    const float a = V[r * m + pj], b = V[r * m + qj];
-                    V[r * m + pj] = cj * a - sj * b;
-                    V[r * m + qj] = sj * a + cj * b;
+                float *vp = Vt + sP[j] * m, *vq = Vt + sQ[j] * m;
+                for (int r = tj; r < m; r += 32) {
+                    const float a = vp[r], b = vq[r];
+                    vp[r] = cj * a - sj * b;
+                    vq[r] = sj * a + cj * b;
                 }
             }
             __syncthreads();
@@ -448,7 +531,7 @@ __global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_swe
         // rotation close to the identity for a nearly diagonal input (block Jacobi inner solve)
         for (int e = tid; e < n * n; e += nt) {
             const int r = e / n, c = e % n;
-            it.vec[(size_t)r * it.ldv + c] = V[r * m + c];
+            it.vec[(size_t)r * it.ldv + c] = Vt[c * m + r];
         }
         for (int i = tid; i < n; i += nt) it.lam[i] = A[i * m + i];
         return;
@@ -464,12 +547,12 @@ __global__ __launch_bounds__(1024) void k_jacobi_lds(JacBatch batch, int max_swe
         int best = 0;
         float bm = -1.f;
         for (int r = 0; r < n; ++r) {
-            const float v = fabsf(V[r * m + i]);
+            const float v = fabsf(Vt[i * m + r]);
             if (v > bm) { bm = v; best = r; }
         }
-        const float sg = V[best * m + i] < 0.f ? -1.f : 1.f;
+        const float sg = Vt[i * m + best] < 0.f ? -1.f : 1.f;
         it.lam[rank] = li;
-        for (int r = 0; r < n; ++r) it.vec[(size_t)r * it.ldv + rank] = sg * V[r * m + i];
+        for (int r = 0; r < n; ++r) it.vec[(size_t)r * it.ldv + rank] = sg * Vt[i * m + r];
     }
 }
 
@@ -558,6 +641,57 @@ __global__ void k_eig_finish(EigBatch batch) {
         const float sg = it.v[(size_t)best * N + i] < 0.f ? -1.f : 1.f;
         it.lam[rank] = li;
         for (int r = 0; r < n; ++r) it.vec[(size_t)r * it.ldv + rank] = sg * it.v[(size_t)r * N + i];
+    }
+}
+
+// ====================================================================== batched small kernels
+__global__ void k_trace_batch(SmallBatch batch) {
+    const SmallItem &it = batch.it[blockIdx.x];
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < it.a; i += blockDim.x) s += (double)it.in[(size_t)i * it.a + i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *it.out64 = red[0];
+}
+
+__global__ void k_energy_batch(SmallBatch batch) {
+    const SmallItem &it = batch.it[blockIdx.y];
+    const int LH = it.a, rt_max = it.b, d = it.c;
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= rt_max * d) return;
+    float s = 0.f;
+    for (int lh = 0; lh < LH; ++lh) {
+        const float v = it.in[(size_t)lh * rt_max * d + e];
+        s = fmaf(v, v, s);
+    }
+    it.out32[e] = s;
+}
+
+__global__ void k_to_bf16_batch(SmallBatch batch) {
+    const SmallItem &it = batch.it[blockIdx.y];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < it.count; i += (int64_t)gridDim.x * blockDim.x) {
+        const float v = it.in[i];
+        const uint16_t h = f32_to_bf16(v);
+        it.hi[i] = h;
+        if (it.lo) it.lo[i] = f32_to_bf16(v - bf16_to_f32(h));
+    }
+}
+
+__global__ void k_gen_omega_batch(SmallBatch batch) {
+    const SmallItem &it = batch.it[blockIdx.y];
+    const int k = it.a, kp = it.b;
+    const int64_t n = it.count / kp;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < it.count; e += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(e / n);
+        const int64_t r = e % n;
+        const float v = (c < k) ? rademacher(it.key, 1, (uint64_t)r * k + c) : 0.f;
+        if (it.hi) it.hi[e] = f32_to_bf16(v);
+        if (it.out32) it.out32[e] = v;
     }
 }
 
@@ -664,9 +798,12 @@ static hipError_t allow_dynamic_lds(const void *fn) {
 static hipError_t ensure_lds_attrs() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
-        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds));
+        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<256>));
+        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<512>));
+        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<1024>));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_cholesky));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_trsm));
+        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_apply_linv));
         state = e;
     }
     return state;
@@ -750,16 +887,28 @@ hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s) 
 hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
-    const size_t lds = (size_t)maxK * (maxK + 1) / 2 * sizeof(float);
+    bool inv = false;
+    for (int i = 0; i < b.n; ++i) inv |= b.it[i].inverse != 0;
+    const size_t lds = (size_t)maxK * (maxK + 1) / 2 * sizeof(float) * (inv ? 2 : 1);
     hipLaunchKernelGGL(k_cholesky, dim3(b.n), dim3(1024), lds, s, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
+    const size_t lds = (size_t)maxK * 65 * sizeof(float);
+    hipLaunchKernelGGL(k_apply_linv, dim3((maxLen + 63) / 64, b.n), dim3(256), lds, s, b);
     return hipGetLastError();
 }
 
 hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
-    const size_t lds = (size_t)maxK * 33 * sizeof(float);
-    hipLaunchKernelGGL(k_trsm, dim3((maxLen + 31) / 32, b.n), dim3(1024), lds, s, b);
+    size_t lds = ((size_t)maxK * 33 + (size_t)maxK * (maxK + 1) / 2) * sizeof(float);
+    const int l_in_lds = lds <= 150 * 1024;
+    if (!l_in_lds) lds = (size_t)maxK * 33 * sizeof(float);
+    hipLaunchKernelGGL(k_trsm, dim3((maxLen + 31) / 32, b.n), dim3(1024), lds, s, b, l_in_lds);
     return hipGetLastError();
 }
 
@@ -768,7 +917,15 @@ hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStr
     if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
     const int m = maxN + (maxN & 1);
     const size_t lds = (size_t)2 * m * m * sizeof(float);
-    hipLaunchKernelGGL(k_jacobi_lds, dim3(b.n), dim3(1024), lds, s, b, max_sweeps);
+    static int nt = 0;
+    if (!nt) {
+        const char *v = getenv("JOLT_JACOBI_THREADS");
+        nt = v ? atoi(v) : 1024;
+        if (nt != 256 && nt != 512 && nt != 1024) nt = 1024;
+    }
+    if (nt == 256) hipLaunchKernelGGL(k_jacobi_lds<256>, dim3(b.n), dim3(256), lds, s, b, max_sweeps);
+    else if (nt == 512) hipLaunchKernelGGL(k_jacobi_lds<512>, dim3(b.n), dim3(512), lds, s, b, max_sweeps);
+    else hipLaunchKernelGGL(k_jacobi_lds<1024>, dim3(b.n), dim3(1024), lds, s, b, max_sweeps);
     return hipGetLastError();
 }
 
@@ -790,6 +947,29 @@ hipError_t launch_offnorm(const EigBatch &b, hipStream_t s) {
 hipError_t launch_eig_finish(const EigBatch &b, int maxN, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_eig_finish, dim3((maxN + 63) / 64, b.n), dim3(64), 0, s, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_trace_batch(const SmallBatch &b, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_trace_batch, dim3(b.n), dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+hipError_t launch_energy_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s) {
+    if (b.n <= 0 || maxCount <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_energy_batch, dim3((unsigned)((maxCount + 255) / 256), b.n), dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+hipError_t launch_to_bf16_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s) {
+    if (b.n <= 0 || maxCount <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_to_bf16_batch, dim3((unsigned)std::min<int64_t>(2048, (maxCount + 255) / 256), b.n), dim3(256),
+                       0, s, b);
+    return hipGetLastError();
+}
+hipError_t launch_gen_omega_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s) {
+    if (b.n <= 0 || maxCount <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gen_omega_batch, dim3((unsigned)std::min<int64_t>(2048, (maxCount + 255) / 256), b.n),
+                       dim3(256), 0, s, b);
     return hipGetLastError();
 }
 

@@ -24,11 +24,12 @@ void make_header(const jolt_item &it, const jolt_alloc &a, uint8_t out[64]);
 
 // Per-item factor storage inside plan_ws, followed by per-chunk scratch.
 struct FactorOffsets {
-    size_t ut, uf, lam_t, lam_f, core, energy, normx2;
+    size_t ut, uf, lam_t, lam_f, core, energy, normx2, sweeps;
 };
 struct PlanLayout {
     int rt_max, rf_max, k, kp;              // k = sketch width (randomized) ; kp = padded
     std::vector<FactorOffsets> item;
+    size_t readback, readback_stride;        // energy | ||X||^2 | sweep counters, one block per item
     size_t scratch;                          // start of the scratch region
     size_t scratch_bytes;                    // per chunk
     size_t total;

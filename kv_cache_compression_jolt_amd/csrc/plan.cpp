@@ -15,6 +15,8 @@
 // and twice for the final one.
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -197,17 +199,26 @@ jolt_status plan_layout(const jolt_config &cfg, const jolt_item *items, int n, P
     pl.kp = round_up(std::max(pl.k, 1), 32);
     Bump b;
     pl.item.resize(n);
+    // host-bound results of all items in one block: [energy rt x d | normx2 | sweeps]
+    size_t dmax = 0;
+    for (int i = 0; i < n; ++i) dmax = std::max<size_t>(dmax, items[i].d);
+    const size_t rt1 = std::max(pl.rt_max, 1);
+    pl.readback_stride = align_up(rt1 * dmax * 4 + 8 + 16, 256);
+    pl.readback = b.take(pl.readback_stride * std::max(n, 1));
     for (int i = 0; i < n; ++i) {
         const jolt_item &it = items[i];
-        const size_t rt = std::max(pl.rt_max, 1), T = it.T, d = it.d, LH = (size_t)it.L * it.H;
+        const size_t rt = rt1, T = it.T, d = it.d, LH = (size_t)it.L * it.H;
         FactorOffsets &o = pl.item[i];
         o.ut = b.take(rt * T * 4);
         o.uf = b.take(d * d * 4);
-        o.lam_t = b.take(std::max<size_t>(rt, 256) * 4);
+        const size_t nlam = std::max<size_t>(std::max<size_t>(rt, 256),
+                                             std::max<size_t>(round_up(pl.k, 32), cfg.mode == JOLT_TOKEN_EXACT ? T : 0));
+        o.lam_t = b.take(nlam * 4);
         o.lam_f = b.take(d * 4);
         o.core = b.take(LH * rt * d * 4);
-        o.energy = b.take(rt * d * 4);
-        o.normx2 = b.take(8);
+        o.energy = pl.readback + i * pl.readback_stride;
+        o.normx2 = o.energy + rt1 * dmax * 4;
+        o.sweeps = o.normx2 + 8;
     }
     pl.scratch = b.off;
     size_t worst = 0;
@@ -267,6 +278,7 @@ jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint
     std::vector<int> cur(NB), desired(NB);
     for (int b = 0; b < NB; ++b) cur[b] = b;
     const float tol2 = 4e-6f * 4e-6f;
+    float prev = 1.f;
     bool converged = false;
     const int inner_sweeps = 4;
     for (int sweep = 0; sweep < max_sweeps && !converged; ++sweep) {
@@ -330,13 +342,23 @@ jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint
             for (int i = 0; i < eb.n; ++i) std::swap(eb.it[i].v, eb.it[i].vt);
         }
         HIPCHK(launch_offnorm(eb, c.st), "eig offnorm");
-        converged = true;
+        // stop at the tolerance, or once the off-diagonal norm stops falling
+        // (quadratic convergence has reached the fp32 rounding floor)
+        float worst = 0.f;
         for (int i = 0; i < eb.n; ++i) {
             float nr[2];
             HIPCHK(hipMemcpyAsync(nr, eb.it[i].norms, sizeof nr, hipMemcpyDeviceToHost, c.st), "eig norms");
             HIPCHK(hipStreamSynchronize(c.st), "eig norms");
-            if (!(nr[0] <= tol2 * nr[1])) converged = false;
+            const float rel2 = nr[1] > 0.f ? nr[0] / nr[1] : 0.f;
+            worst = std::max(worst, rel2);
         }
+        if (getenv("JOLT_DEBUG")) fprintf(stderr, "libjolt: block Jacobi N=%d sweep %d off %.3e\n", N, sweep, sqrtf(worst));
+        if (worst <= tol2) converged = true;
+        else if (sweep > 0 && worst > 0.25f * prev) {
+            converged = true;
+            if (worst > 1e-8f && noconv) *noconv = true;       // stalled above 1e-4 relative
+        }
+        prev = worst;
     }
     if (!converged && noconv) *noconv = true;
     HIPCHK(launch_eig_finish(eb, N, c.st), "eig finish");
@@ -395,6 +417,7 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
             r.nsplit = split[i];
             CholItem &ch = cb.it[cb.n++];
             ch.g = gram[i]; ch.l = lmat[i]; ch.k = k[i]; ch.ld = kp[i]; ch.rel_shift = 1.0f / 1048576.0f;
+            ch.inverse = k[i] <= kCholInverseMaxK;
             TrsmItem &t = tb.it[tb.n++];
             t.l = lmat[i]; t.y = y[i]; t.q = y[i]; t.k = k[i]; t.ld = kp[i]; t.len = len[i]; t.ldy = len[i];
             maxK = std::max(maxK, k[i]);
@@ -406,7 +429,8 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
         for (int i = 0; i < nb; ++i) maxCount = std::max<int64_t>(maxCount, (int64_t)kp[i] * kp[i]);
         HIPCHK(launch_reduce(rb, maxCount, c.st), "orth reduce");
         HIPCHK(launch_cholesky(cb, maxK, c.st), "orth cholesky");
-        HIPCHK(launch_trsm(tb, maxK, maxLen, c.st), "orth trsm");
+        if (maxK <= kCholInverseMaxK) HIPCHK(launch_apply_linv(tb, maxK, maxLen, c.st), "orth L^-1 Y");
+        else HIPCHK(launch_trsm(tb, maxK, maxLen, c.st), "orth trsm");
     }
     return JOLT_OK;
 }
@@ -424,6 +448,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         reserve_scratch(cfg, D[i], sb, S[i]);
     }
     uint8_t *scr = ws + pl.scratch;
+    if (i0 == 0) HIPCHK(launch_zero(ws + pl.readback, pl.readback_stride * pl.item.size(), c.st), "zero readback");
     auto P = [&](size_t off) { return scr + off; };
     auto F = [&](size_t off) { return reinterpret_cast<float *>(scr + off); };
     auto W = [&](int i, size_t off) { return ws + off; };
@@ -431,7 +456,6 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
     for (int i = 0; i < nb; ++i) {
         maxT = std::max(maxT, D[i].T);
         maxLH = std::max(maxLH, D[i].LH);
-        HIPCHK(launch_zero(P(S[i].sweeps), 16, c.st), "zero sweeps");
     }
 
     // ---- feature Gram, ||X||^2
@@ -450,26 +474,35 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         }
         HIPCHK(launch_gram_rows(gb, dt, d, maxP, c.st), "feature gram");
         HIPCHK(launch_reduce(rb, (int64_t)d * d, c.st), "feature gram reduce");
-        for (int i = 0; i < nb; ++i)
-            HIPCHK(launch_trace(F(S[i].gf), d, reinterpret_cast<double *>(W(i, pl.item[i0 + i].normx2)), c.st),
-                   "trace");
+        SmallBatch tb{};
+        for (int i = 0; i < nb; ++i) {
+            SmallItem &t = tb.it[tb.n++];
+            t.in = F(S[i].gf); t.out64 = reinterpret_cast<double *>(W(i, pl.item[i0 + i].normx2)); t.a = d;
+        }
+        HIPCHK(launch_trace_batch(tb, c.st), "trace");
     }
     // feature eigenproblems join the token eigenproblems in one launch
     std::vector<EigReq> eigs;
     for (int i = 0; i < nb; ++i)
         eigs.push_back(EigReq{F(S[i].gf), d, d, reinterpret_cast<float *>(ws + pl.item[i0 + i].uf), d,
                               reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_f),
-                              reinterpret_cast<int *>(P(S[i].sweeps)), &S[i]});
+                              reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps), &S[i]});
 
     if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
         std::vector<float *> yv(nb), zv(nb), gram(nb), gpart(nb), lmat(nb);
         std::vector<int> kk(nb), kpp(nb), lenT(nb), lenN(nb), sT(nb), cT(nb), sN(nb), cN(nb);
+        SmallBatch ob{};
+        int64_t maxOm = 0;
         for (int i = 0; i < nb; ++i) {
             const jolt_item &it = items[i0 + i];
-            HIPCHK(launch_gen_omega(bf ? reinterpret_cast<uint16_t *>(P(S[i].omt)) : nullptr,
-                                    bf ? nullptr : F(S[i].omt), item_key(it.seed, it.item_id), D[i].k, D[i].kp,
-                                    D[i].n, c.st),
-                   "omega");
+            SmallItem &o = ob.it[ob.n++];
+            o.hi = bf ? reinterpret_cast<uint16_t *>(P(S[i].omt)) : nullptr;
+            o.out32 = bf ? nullptr : F(S[i].omt);
+            o.key = item_key(it.seed, it.item_id); o.a = D[i].k; o.b = D[i].kp; o.count = (int64_t)D[i].kp * D[i].n;
+            maxOm = std::max(maxOm, o.count);
+        }
+        HIPCHK(launch_gen_omega_batch(ob, maxOm, c.st), "omega");
+        for (int i = 0; i < nb; ++i) {
             yv[i] = F(S[i].yt); zv[i] = F(S[i].zt); gram[i] = F(S[i].gram); gpart[i] = F(S[i].gpart);
             lmat[i] = F(S[i].lmat);
             kk[i] = D[i].k; kpp[i] = D[i].kp; lenT[i] = D[i].T; lenN[i] = D[i].n;
@@ -518,17 +551,17 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         };
         auto to_bf = [&](bool from_y, bool lo) -> jolt_status {
             if (!bf) return JOLT_OK;
+            SmallBatch cb{};
+            int64_t maxC = 0;
             for (int i = 0; i < nb; ++i) {
-                if (from_y)
-                    HIPCHK(launch_to_bf16(F(S[i].yt), reinterpret_cast<uint16_t *>(P(S[i].qh)),
-                                          lo ? reinterpret_cast<uint16_t *>(P(S[i].ql)) : nullptr,
-                                          (int64_t)D[i].kp * D[i].T, c.st),
-                           "to bf16");
-                else
-                    HIPCHK(launch_to_bf16(F(S[i].zt), reinterpret_cast<uint16_t *>(P(S[i].zb)), nullptr,
-                                          (int64_t)D[i].kp * D[i].n, c.st),
-                           "to bf16");
+                SmallItem &t = cb.it[cb.n++];
+                t.in = from_y ? F(S[i].yt) : F(S[i].zt);
+                t.hi = reinterpret_cast<uint16_t *>(from_y ? P(S[i].qh) : P(S[i].zb));
+                t.lo = (from_y && lo) ? reinterpret_cast<uint16_t *>(P(S[i].ql)) : nullptr;
+                t.count = (int64_t)D[i].kp * (from_y ? D[i].T : D[i].n);
+                maxC = std::max(maxC, t.count);
             }
+            HIPCHK(launch_to_bf16_batch(cb, maxC, c.st), "to bf16");
             return JOLT_OK;
         };
         jolt_status s;
@@ -570,8 +603,9 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             HIPCHK(launch_gemm(gb, maxK, maxK, maxS, 1, c.st), "B B^T");
             HIPCHK(launch_reduce(rb, maxCount, c.st), "B B^T reduce");
             for (int i = 0; i < nb; ++i)
-                eigs.push_back(EigReq{F(S[i].wmat), D[i].kp, D[i].k, F(S[i].vmat), D[i].kp, F(S[i].lamk),
-                                      reinterpret_cast<int *>(P(S[i].sweeps)) + 1, &S[i]});
+                eigs.push_back(EigReq{F(S[i].wmat), D[i].kp, D[i].k, F(S[i].vmat), D[i].kp,
+                                      reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),
+                                      reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i]});
             jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
             if (es) return es;
         }
@@ -589,9 +623,6 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
                 q.a_i = 1; q.a_k = D[i].kp; q.b_k = D[i].n; q.b_j = 1; q.c_i = D[i].n; q.c_j = 1; q.c_split = 0;
                 q.M = pl.rt_max; q.N = D[i].n; q.K = D[i].k; q.kchunk = D[i].k; q.nsplit = 1; q.nb = 1;
                 maxN = std::max(maxN, D[i].T); maxNn = std::max(maxNn, D[i].n);
-                HIPCHK(hipMemcpyAsync(ws + pl.item[i0 + i].lam_t, P(S[i].lamk), (size_t)pl.rt_max * 4,
-                                      hipMemcpyDeviceToDevice, c.st),
-                       "lambda_t");
             }
             if (pl.rt_max > 0) {
                 HIPCHK(launch_gemm(gu, pl.rt_max, maxN, 1, 1, c.st), "U_t");
@@ -611,8 +642,9 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         }
         HIPCHK(launch_xm(xb, dt, d, maxT, maxC, c.st), "token Gram");
         for (int i = 0; i < nb; ++i)
-            eigs.push_back(EigReq{F(S[i].gt), D[i].T, D[i].T, F(S[i].vt), D[i].T, F(S[i].lamT),
-                                  reinterpret_cast<int *>(P(S[i].sweeps)) + 1, &S[i]});
+            eigs.push_back(EigReq{F(S[i].gt), D[i].T, D[i].T, F(S[i].vt), D[i].T,
+                                  reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),
+                                  reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i]});
         jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
         if (es) return es;
         // U_t^T rows = leading eigenvectors; P = U_t^T A (hi + lo split for bf16 caches)
@@ -623,8 +655,6 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         for (int i = 0; i < nb; ++i) {
             float *ut = reinterpret_cast<float *>(ws + pl.item[i0 + i].ut);
             HIPCHK(launch_transpose(F(S[i].vt), ut, D[i].T, pl.rt_max, D[i].T, D[i].T, c.st), "U_t");
-            HIPCHK(hipMemcpyAsync(ws + pl.item[i0 + i].lam_t, P(S[i].lamT), (size_t)pl.rt_max * 4,
-                                  hipMemcpyDeviceToDevice, c.st), "lambda_t");
             const int64_t rows_pad = (int64_t)D[i].rtp32 * D[i].T;
             if (bf) {
                 HIPCHK(launch_zero(P(S[i].uh), rows_pad * 2, c.st), "zero");
@@ -671,10 +701,14 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             maxNb = std::max(maxNb, g.nb);
         }
         HIPCHK(launch_gemm(gb, pl.rt_max, d, 1, maxNb, c.st), "core");
-        for (int i = 0; i < nb; ++i)
-            HIPCHK(launch_energy(reinterpret_cast<const float *>(ws + pl.item[i0 + i].core),
-                                 reinterpret_cast<float *>(ws + pl.item[i0 + i].energy), D[i].LH, pl.rt_max, d, c.st),
-                   "energy");
+        SmallBatch eb{};
+        for (int i = 0; i < nb; ++i) {
+            SmallItem &t = eb.it[eb.n++];
+            t.in = reinterpret_cast<const float *>(ws + pl.item[i0 + i].core);
+            t.out32 = reinterpret_cast<float *>(ws + pl.item[i0 + i].energy);
+            t.a = D[i].LH; t.b = pl.rt_max; t.c = d;
+        }
+        HIPCHK(launch_energy_batch(eb, (int64_t)pl.rt_max * d, c.st), "energy");
     }
     return JOLT_OK;
 }
@@ -741,37 +775,27 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
         const int nb = std::min(kMaxBatch, n - c0);
         s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv);
         if (s) return s;
-        // sweep counters of this chunk (the chunk's scratch is reused by the next one)
-        std::vector<Scratch> S(nb);
-        Bump sb;
-        for (int i = 0; i < nb; ++i) {
-            Dims D = dims_for(*cfg, items[c0 + i], pl.rt_max, pl.rf_max);
-            reserve_scratch(*cfg, D, sb, S[i]);
-        }
-        for (int i = 0; i < nb; ++i) {
-            int sw[2] = {0, 0};
-            hipError_t e = hipMemcpyAsync(sw, ws + pl.scratch + S[i].sweeps, sizeof sw, hipMemcpyDeviceToHost, st);
-            if (e == hipSuccess) e = hipStreamSynchronize(st);
-            if (e != hipSuccess) return hip_fail(h, e, "sweep counters");
-            if (sw[0] < 0 || (cfg->mode == JOLT_TOKEN_RANDOMIZED && sw[1] < 0)) noconv = true;
-        }
     }
-    // energy tables and ||X||^2 back to the host (the one synchronisation)
+    // energy tables, ||X||^2 and sweep counters back to the host (the one synchronisation)
     const int rt_max = pl.rt_max;
+    std::vector<uint8_t> rb(pl.readback_stride * n);
+    hipError_t e = hipMemcpyAsync(rb.data(), ws + pl.readback, rb.size(), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(h, e, "plan");
     std::vector<std::vector<float>> E(n);
     std::vector<double> nx2(n);
     for (int i = 0; i < n; ++i) {
-        E[i].resize((size_t)std::max(rt_max, 1) * items[i].d);
-        hipError_t e = hipSuccess;
-        if (rt_max > 0)
-            e = hipMemcpyAsync(E[i].data(), ws + pl.item[i].energy, (size_t)rt_max * items[i].d * 4,
-                               hipMemcpyDeviceToHost, st);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(&nx2[i], ws + pl.item[i].normx2, 8, hipMemcpyDeviceToHost, st);
-        if (e != hipSuccess) return hip_fail(h, e, "table readback");
+        const uint8_t *blk = rb.data() + (pl.item[i].energy - pl.readback);
+        const size_t d = items[i].d;
+        E[i].assign((size_t)std::max(rt_max, 1) * d, 0.f);
+        // energy rows were written with leading dimension d
+        std::memcpy(E[i].data(), blk, (size_t)rt_max * d * 4);
+        std::memcpy(&nx2[i], rb.data() + (pl.item[i].normx2 - pl.readback), 8);
+        int sw[2];
+        std::memcpy(sw, rb.data() + (pl.item[i].sweeps - pl.readback), 8);
+        if (sw[0] < 0 || sw[1] < 0) noconv = true;
+        if (getenv("JOLT_DEBUG")) fprintf(stderr, "libjolt: item %d eig sweeps feature %d token %d\n", i, sw[0], sw[1]);
     }
-    hipError_t e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(h, e, "plan");
 
     const int rf_max = pl.rf_max;
     if (cfg->budget_bytes < 0) {

@@ -67,9 +67,10 @@ hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s);
 // Cholesky of G + shift I (k x k, ld) -> lower L written to l (k x k, ld), zeros above
 struct CholItem {
     const float *g;
-    float *l;
+    float *l;            // L, or L^{-1} when inverse != 0 (k <= 200)
     int k, ld;
     float rel_shift;     // shift = rel_shift * trace(G) / k
+    int inverse;
 };
 struct CholBatch { CholItem it[kMaxBatch]; int n; };
 hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s);
@@ -83,6 +84,9 @@ struct TrsmItem {
 };
 struct TrsmBatch { TrsmItem it[kMaxBatch]; int n; };
 hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
+// y <- X y with X = L^{-1} lower triangular (in place; k <= 600)
+hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
+constexpr int kCholInverseMaxK = 200;
 
 // symmetric eigen-decomposition by parallel-order two-sided Jacobi in LDS (n <= 142)
 // vec[r][c] = component r of eigenvector c, eigenvalues descending, sign-normalised.
@@ -113,6 +117,22 @@ hipError_t launch_eig_init(const EigBatch &b, int maxN, hipStream_t s);
 hipError_t launch_block_permute(const EigBatch &b, const BlockPerm &p, int maxN, hipStream_t s);
 hipError_t launch_offnorm(const EigBatch &b, hipStream_t s);
 hipError_t launch_eig_finish(const EigBatch &b, int maxN, hipStream_t s);
+
+// batched small kernels (one launch for all items of a chunk)
+struct SmallItem {
+    const float *in;     // trace: G (d x d); energy: core; to_bf16: source
+    float *out32;        // energy: E; gen_omega: fp32 Omega^T
+    double *out64;       // trace
+    uint16_t *hi, *lo;   // to_bf16 / gen_omega (bf16 Omega^T)
+    int64_t count;       // elements (to_bf16, gen_omega: kp * n)
+    uint64_t key;        // gen_omega
+    int a, b, c;         // trace: d; energy: LH, rt_max, d; gen_omega: k, kp, (n in count / kp)
+};
+struct SmallBatch { SmallItem it[kMaxBatch]; int n; };
+hipError_t launch_trace_batch(const SmallBatch &b, hipStream_t s);
+hipError_t launch_energy_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s);
+hipError_t launch_to_bf16_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s);
+hipError_t launch_gen_omega_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s);
 
 // elementwise conversions
 hipError_t launch_to_bf16(const float *in, uint16_t *hi, uint16_t *lo, int64_t count, hipStream_t s);
