@@ -26,12 +26,13 @@ namespace jolt {
 // ====================================================================== X-pass A M
 // WG: 4 waves x 32 tokens; each wave owns NF column fragments (32 columns each).
 template <typename T, int NF>
-__global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d) {
+__global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles) {
     const XmItem &it = batch.it[blockIdx.z];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
     const int t0 = blockIdx.x * 128 + wave * 32;
-    const int c0 = blockIdx.y * (32 * NF);
-    if (t0 >= it.T || c0 >= it.ncols) return;
+    const int c0 = (blockIdx.y % ncol_tiles) * (32 * NF);
+    const int sp = blockIdx.y / ncol_tiles;
+    if (t0 >= it.T || c0 >= it.ncols || sp >= it.nsplit) return;
     const T *x = reinterpret_cast<const T *>(it.x);
     const T *m = reinterpret_cast<const T *>(it.m);
     const int n = it.LH * d;
@@ -41,7 +42,8 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d) {
     for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
     int ncf = (it.ncols - c0 + 31) / 32;
     if (ncf > NF) ncf = NF;
-    for (int k0 = 0; k0 < n; k0 += 16) {
+    const int kb = sp * it.lh_split * d, ke = min(n, kb + it.lh_split * d);
+    for (int k0 = kb; k0 < ke; k0 += 16) {
         const int lh = k0 / d, f0 = k0 - lh * d + 8 * h;
         typename Elem<T>::Frag a = load_frag(x + ((size_t)lh * it.T + tok) * d + f0);
         const T *mb = m + (size_t)lh * it.m_blk + f0;
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d) {
     for (int f = 0; f < NF; ++f) {
         const int c = c0 + 32 * f + ln;
         if (f < ncf && c < it.ncols) {
-            float *o = it.out + (size_t)c * it.ldo + t0;
+            float *o = it.out + (size_t)sp * it.ncols * it.ldo + (size_t)c * it.ldo + t0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = 8 * q + 4 * h;
@@ -798,9 +800,7 @@ static hipError_t allow_dynamic_lds(const void *fn) {
 static hipError_t ensure_lds_attrs() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
-        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<256>));
-        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<512>));
-        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<1024>));
+        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<1024>));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_cholesky));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_trsm));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_apply_linv));
@@ -810,29 +810,29 @@ static hipError_t ensure_lds_attrs() {
 }
 
 template <typename T>
-static hipError_t xm_nf(const XmBatch &b, int d, dim3 g, int nf, hipStream_t s) {
+static hipError_t xm_nf(const XmBatch &b, int d, dim3 g, int nf, int tiles, hipStream_t s) {
     switch (nf) {
-        case 1: hipLaunchKernelGGL((k_xm<T, 1>), g, dim3(256), 0, s, b, d); break;
-        case 2: hipLaunchKernelGGL((k_xm<T, 2>), g, dim3(256), 0, s, b, d); break;
-        case 3: hipLaunchKernelGGL((k_xm<T, 3>), g, dim3(256), 0, s, b, d); break;
-        case 4: hipLaunchKernelGGL((k_xm<T, 4>), g, dim3(256), 0, s, b, d); break;
-        case 5: hipLaunchKernelGGL((k_xm<T, 5>), g, dim3(256), 0, s, b, d); break;
-        case 6: hipLaunchKernelGGL((k_xm<T, 6>), g, dim3(256), 0, s, b, d); break;
-        case 7: hipLaunchKernelGGL((k_xm<T, 7>), g, dim3(256), 0, s, b, d); break;
-        case 8: hipLaunchKernelGGL((k_xm<T, 8>), g, dim3(256), 0, s, b, d); break;
-        case 9: hipLaunchKernelGGL((k_xm<T, 9>), g, dim3(256), 0, s, b, d); break;
+        case 1: hipLaunchKernelGGL((k_xm<T, 1>), g, dim3(256), 0, s, b, d, tiles); break;
+        case 2: hipLaunchKernelGGL((k_xm<T, 2>), g, dim3(256), 0, s, b, d, tiles); break;
+        case 3: hipLaunchKernelGGL((k_xm<T, 3>), g, dim3(256), 0, s, b, d, tiles); break;
+        case 4: hipLaunchKernelGGL((k_xm<T, 4>), g, dim3(256), 0, s, b, d, tiles); break;
+        case 5: hipLaunchKernelGGL((k_xm<T, 5>), g, dim3(256), 0, s, b, d, tiles); break;
+        case 6: hipLaunchKernelGGL((k_xm<T, 6>), g, dim3(256), 0, s, b, d, tiles); break;
+        case 7: hipLaunchKernelGGL((k_xm<T, 7>), g, dim3(256), 0, s, b, d, tiles); break;
+        case 8: hipLaunchKernelGGL((k_xm<T, 8>), g, dim3(256), 0, s, b, d, tiles); break;
+        case 9: hipLaunchKernelGGL((k_xm<T, 9>), g, dim3(256), 0, s, b, d, tiles); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, hipStream_t s) {
+hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, int maxSplit, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     int nf = (maxCols + 31) / 32;
-    int gy = 1;
-    if (nf > 9) { gy = (nf + 3) / 4; nf = 4; }
-    dim3 g((maxT + 127) / 128, gy, b.n);
-    return dtype == JOLT_BF16 ? xm_nf<uint16_t>(b, d, g, nf, s) : xm_nf<float>(b, d, g, nf, s);
+    int tiles = 1;
+    if (nf > 9) { tiles = (nf + 3) / 4; nf = 4; }
+    dim3 g((maxT + 127) / 128, tiles * maxSplit, b.n);
+    return dtype == JOLT_BF16 ? xm_nf<uint16_t>(b, d, g, nf, tiles, s) : xm_nf<float>(b, d, g, nf, tiles, s);
 }
 
 template <typename T, bool LO>
@@ -917,15 +917,7 @@ hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStr
     if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
     const int m = maxN + (maxN & 1);
     const size_t lds = (size_t)2 * m * m * sizeof(float);
-    static int nt = 0;
-    if (!nt) {
-        const char *v = getenv("JOLT_JACOBI_THREADS");
-        nt = v ? atoi(v) : 1024;
-        if (nt != 256 && nt != 512 && nt != 1024) nt = 1024;
-    }
-    if (nt == 256) hipLaunchKernelGGL(k_jacobi_lds<256>, dim3(b.n), dim3(256), lds, s, b, max_sweeps);
-    else if (nt == 512) hipLaunchKernelGGL(k_jacobi_lds<512>, dim3(b.n), dim3(512), lds, s, b, max_sweeps);
-    else hipLaunchKernelGGL(k_jacobi_lds<1024>, dim3(b.n), dim3(1024), lds, s, b, max_sweeps);
+    hipLaunchKernelGGL(k_jacobi_lds<1024>, dim3(b.n), dim3(1024), lds, s, b, max_sweeps);
     return hipGetLastError();
 }
 

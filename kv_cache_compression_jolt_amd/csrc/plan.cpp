@@ -47,10 +47,11 @@ struct Dims {
     int gf_P, gf_chunk;           // feature Gram partial sums
     int gT_split, gT_chunk;       // Gram of a T-long basis
     int gN_split, gN_chunk;       // Gram of an n-long basis
+    int xm_split, xm_lh;          // A M passes: K split over (layer, head) blocks
 };
 
 struct Scratch {
-    size_t omt, yt, qh, ql, zt, zb, xpart, gpart, gram, lmat, wmat, vmat, lamk, sweeps;
+    size_t omt, yt, ypart, qh, ql, zt, zb, xpart, gpart, gram, lmat, wmat, vmat, lamk, sweeps;
     size_t gfpart, gf, pmat, gt, vt, lamT, uh, ul;
     size_t eA, eT, eV, eVT, eR, eRlam, eNorm, eSw;     // block Jacobi (n > 142)
     int eN;                                             // padded size, 0 if unused
@@ -86,6 +87,11 @@ Dims dims_for(const jolt_config &cfg, const jolt_item &it, int rt_max, int rf_ma
     D.gN_split = clampi(D.n / 512, 1, 64);
     D.gN_chunk = round_up((D.n + D.gN_split - 1) / D.gN_split, 16);
     D.gN_split = (D.n + D.gN_chunk - 1) / D.gN_chunk;
+    // enough workgroups for 256 CUs: T / 128 token tiles per item, 16 items per launch
+    D.xm_split = clampi(2048 / std::max(1, (D.T / 128) * kMaxBatch), 1, 8);
+    D.xm_split = std::min(D.xm_split, D.LH);
+    D.xm_lh = (D.LH + D.xm_split - 1) / D.xm_split;
+    D.xm_split = (D.LH + D.xm_lh - 1) / D.xm_lh;
     return D;
 }
 
@@ -97,6 +103,7 @@ void reserve_scratch(const jolt_config &cfg, const Dims &D, Bump &b, Scratch &s)
     if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
         s.omt = b.take(kp * n * D.e);
         s.yt = b.take(kp * T * 4);
+        s.ypart = D.xm_split > 1 ? b.take((size_t)D.xm_split * kp * T * 4) : 0;
         if (D.e == 2) {
             s.qh = b.take(kp * T * 2);
             s.ql = b.take(kp * T * 2);
@@ -510,17 +517,28 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         }
         auto xm = [&](bool first) -> jolt_status {
             XmBatch xb{};
-            int maxC = 0;
+            ReduceBatch rb{};
+            int maxC = 0, maxS = 0;
+            int64_t maxCount = 0;
             for (int i = 0; i < nb; ++i) {
                 XmItem &x = xb.it[xb.n++];
                 x.x = x_dev[i0 + i];
                 x.m = first ? (const void *)P(S[i].omt) : (bf ? (const void *)P(S[i].zb) : (const void *)P(S[i].zt));
-                x.out = F(S[i].yt);
                 x.m_c = D[i].n; x.m_blk = d;
                 x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].kp; x.ldo = D[i].T;
+                x.lh_split = D[i].xm_lh; x.nsplit = D[i].xm_split;
+                x.out = x.nsplit > 1 ? F(S[i].ypart) : F(S[i].yt);
                 maxC = std::max(maxC, x.ncols);
+                maxS = std::max(maxS, x.nsplit);
+                if (x.nsplit > 1) {
+                    ReduceItem &r = rb.it[rb.n++];
+                    r.part = F(S[i].ypart); r.out = F(S[i].yt);
+                    r.stride = (int64_t)D[i].kp * D[i].T; r.count = r.stride; r.nsplit = x.nsplit;
+                    maxCount = std::max(maxCount, r.count);
+                }
             }
-            HIPCHK(launch_xm(xb, dt, d, maxT, maxC, c.st), "sketch A M");
+            HIPCHK(launch_xm(xb, dt, d, maxT, maxC, maxS, c.st), "sketch A M");
+            HIPCHK(launch_reduce(rb, maxCount, c.st), "sketch reduce");
             return JOLT_OK;
         };
         auto xtq = [&](bool hilo) -> jolt_status {
@@ -638,9 +656,10 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             x.x = x_dev[i0 + i]; x.m = x_dev[i0 + i]; x.out = F(S[i].gt);
             x.m_c = d; x.m_blk = (int64_t)D[i].T * d;
             x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].T; x.ldo = D[i].T;
+            x.lh_split = D[i].LH; x.nsplit = 1;
             maxC = std::max(maxC, x.ncols);
         }
-        HIPCHK(launch_xm(xb, dt, d, maxT, maxC, c.st), "token Gram");
+        HIPCHK(launch_xm(xb, dt, d, maxT, maxC, 1, c.st), "token Gram");
         for (int i = 0; i < nb; ++i)
             eigs.push_back(EigReq{F(S[i].gt), D[i].T, D[i].T, F(S[i].vt), D[i].T,
                                   reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),

@@ -12,12 +12,13 @@ namespace jolt {
 struct XmItem {
     const void *x;
     const void *m;
-    float *out;          // [ncols][ldo]
+    float *out;          // [ncols][ldo], or split s at out + s * ncols * ldo
     int64_t m_c, m_blk;
     int T, LH, ncols, ldo;
+    int lh_split, nsplit;   // K split: (layer, head) blocks per split, number of splits
 };
 struct XmBatch { XmItem it[kMaxBatch]; int n; };
-hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, hipStream_t s);
+hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, int maxSplit, hipStream_t s);
 
 // X-pass "Q^T A": out[s][c][lh d + f] = sum_{t in split s} q[c][t] x[lh][t][f]
 // (q in the X dtype; an optional second operand ql is added: hi + lo split).
