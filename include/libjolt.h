@@ -213,6 +213,18 @@ jolt_status jolt_unpack_dequant(jolt_handle h, const uint64_t *codes, const uint
 jolt_status jolt_rademacher(jolt_handle h, uint64_t seed, uint32_t item_id, uint32_t stream_id,
                             uint64_t first, int64_t count, float *out, void *stream);
 
+/* The plan's symmetric eigensolver on caller matrices (device).  count
+ * matrices of order n <= 142: matrix i starts at a + i * mat_stride, row
+ * stride lda, and only its symmetric part (A + A^T) / 2 is used.  Matrix i's
+ * eigenvalues go to lam + i n in descending order and its eigenvectors to the
+ * columns of vec + i n n (row stride n), each column's entry of largest
+ * magnitude (first such row) positive.  info (count int32, device) receives
+ * 0 when the Householder-tridiagonal solver (n <= 140) produced the result,
+ * the sweep count when the Jacobi solver did (n > 140, force_jacobi != 0, or
+ * numerically repeated eigenvalues), -1 when Jacobi hit its sweep cap. */
+jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const float *a, int32_t lda, int64_t mat_stride,
+                      float *vec, float *lam, int32_t *info, int32_t force_jacobi, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

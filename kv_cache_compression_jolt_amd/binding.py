@@ -55,7 +55,7 @@ EXPORTED = [
     "jolt_item_bytes", "jolt_payload_size", "jolt_payload_layout", "jolt_payload_header",
     "jolt_payload_validate", "jolt_plan", "jolt_compress", "jolt_encode_residual", "jolt_decompress",
     "jolt_plan_factors", "jolt_plan_from_tables", "jolt_rotate", "jolt_quantize_pack",
-    "jolt_unpack_dequant", "jolt_rademacher",
+    "jolt_unpack_dequant", "jolt_rademacher", "jolt_eigh",
 ]
 
 _lib = None
@@ -99,6 +99,7 @@ def lib():
             "jolt_quantize_pack": (I32, [P, P, I64, I32, I32, P, P, P]),
             "jolt_unpack_dequant": (I32, [P, P, P, I64, I32, I32, P, P]),
             "jolt_rademacher": (I32, [P, U64, U32, U32, U64, I64, P, P]),
+            "jolt_eigh": (I32, [P, I32, I32, P, I32, I64, P, P, P, I32, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -242,6 +243,11 @@ def jolt_unpack_dequant(h, codes_ptr, scales_ptr, rows, d, bits, out_ptr, stream
 def jolt_rademacher(h, seed, item_id, stream_id, first, count, out_ptr, stream):
     _check(lib().jolt_rademacher(h, seed, item_id, stream_id, first, count, C.c_void_p(out_ptr),
                                  C.c_void_p(stream)), h)
+
+
+def jolt_eigh(h, n, count, a_ptr, lda, mat_stride, vec_ptr, lam_ptr, info_ptr, force_jacobi, stream):
+    _check(lib().jolt_eigh(h, n, count, C.c_void_p(a_ptr), lda, mat_stride, C.c_void_p(vec_ptr),
+                           C.c_void_p(lam_ptr), C.c_void_p(info_ptr), int(force_jacobi), C.c_void_p(stream)), h)
 
 
 # ------------------------------------------------------------------ helpers

@@ -13,6 +13,7 @@
 #include "api_internal.h"
 #include "jolt_internal.h"
 #include "payload.h"
+#include "plan_kernels.h"
 #include "planner.h"
 
 using namespace jolt;
@@ -407,4 +408,34 @@ extern "C" jolt_status jolt_rademacher(jolt_handle h, uint64_t seed, uint32_t it
     hipError_t e = launch_rademacher(item_key(seed, item_id), stream_id, first, count, out,
                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "rademacher");
+}
+
+extern "C" jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const float *a, int32_t lda,
+                                 int64_t mat_stride, float *vec, float *lam, int32_t *info, int32_t force_jacobi,
+                                 void *stream) {
+    if (!h) return JOLT_E_INVALID;
+    clear_err(h);
+    if (n < 1 || n > kJacobiMaxN || count < 0 || lda < n || mat_stride < (int64_t)(n - 1) * lda + n)
+        return fail(h, JOLT_E_INVALID, "eigh: bad sizes (n=%d count=%d lda=%d)", n, count, lda);
+    if (count > 0 && (!a || !vec || !lam || !info)) return fail(h, JOLT_E_INVALID, "eigh: null pointer");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool tri = !force_jacobi && n <= kTriMaxN;
+    for (int i0 = 0; i0 < count; i0 += 64) {
+        JacBatch b{};
+        for (int i = i0; i < count && b.n < 64; ++i) {
+            JacItem &j = b.it[b.n++];
+            j.a = a + (size_t)i * mat_stride;
+            j.lda = lda;
+            j.vec = vec + (size_t)i * n * n;
+            j.ldv = n;
+            j.lam = lam + (size_t)i * n;
+            j.n = n;
+            j.raw = 0;
+            j.sweeps_out = info + i;
+        }
+        hipError_t e = tri ? launch_eig_tridiag(b, n, st) : launch_jacobi_lds(b, n, 30, st);
+        if (e == hipSuccess && tri) e = launch_jacobi_lds(b, n, 30, st, 1);
+        if (e != hipSuccess) return hip_fail(h, e, "eigh");
+    }
+    return JOLT_OK;
 }

@@ -439,12 +439,13 @@ __device__ __forceinline__ int rr_pos(int i, int round, int m) {
 }
 
 template <int NT>
-__global__ __launch_bounds__(NT) void k_jacobi_lds(JacBatch batch, int max_sweeps) {
+__global__ __launch_bounds__(NT) void k_jacobi_lds(JacBatch batch, int max_sweeps, int retry_only) {
     extern __shared__ float sm[];
     __shared__ int sP[kJacobiMaxN / 2 + 1], sQ[kJacobiMaxN / 2 + 1];
     __shared__ float sC[kJacobiMaxN / 2 + 1], sS[kJacobiMaxN / 2 + 1];
     __shared__ int s_rot;
     const JacItem &it = batch.it[blockIdx.x];
+    if (retry_only && (!it.sweeps_out || *it.sweeps_out != kEigRetry)) return;
     const int n = it.n, m = n + (n & 1), half = m / 2;
     const int tid = threadIdx.x;
     constexpr int nt = NT;
@@ -529,6 +530,18 @@ __global__ __launch_bounds__(NT) void k_jacobi_lds(JacBatch batch, int max_sweep
         __syncthreads();
     }
     if (tid == 0 && it.sweeps_out) *it.sweeps_out = done ? sweeps : -1;
+    // The accumulated rotations are orthogonal only to rounding, and over
+    // ~10^3 rotations per index the rounding drifts their scale: with
+    // V = U S (U orthogonal, S = diag |v_i|) the diagonal of V^T A V is
+    // |v_i|^2 lambda_i.  Take lambda_i = a_ii / |v_i|^2 and unit vectors.
+    for (int i = tid; i < n; i += nt) {
+        float s2 = 0.f;
+        for (int r = 0; r < n; ++r) s2 = fmaf(Vt[i * m + r], Vt[i * m + r], s2);
+        const float inv = 1.f / sqrtf(s2);
+        A[i * m + i] = A[i * m + i] / s2;
+        for (int r = 0; r < n; ++r) Vt[i * m + r] *= inv;
+    }
+    __syncthreads();
     if (it.raw) {
         // rotation close to the identity for a nearly diagonal input (block Jacobi inner solve)
         for (int e = tid; e < n * n; e += nt) {
@@ -912,12 +925,12 @@ hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) 
     return hipGetLastError();
 }
 
-hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s) {
+hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s, int retry_only) {
     if (b.n <= 0) return hipSuccess;
     if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
     const int m = maxN + (maxN & 1);
     const size_t lds = (size_t)2 * m * m * sizeof(float);
-    hipLaunchKernelGGL(k_jacobi_lds<1024>, dim3(b.n), dim3(1024), lds, s, b, max_sweeps);
+    hipLaunchKernelGGL(k_jacobi_lds<1024>, dim3(b.n), dim3(1024), lds, s, b, max_sweeps, retry_only);
     return hipGetLastError();
 }
 

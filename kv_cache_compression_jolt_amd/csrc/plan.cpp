@@ -373,12 +373,27 @@ jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint
 }
 
 jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr, int max_sweeps, bool *noconv) {
-    JacBatch jb{};
-    int maxN = 0;
+    JacBatch jb{}, tb{};
+    int maxN = 0, maxT = 0;
     std::vector<std::vector<EigReq>> large;
     std::vector<int> largeN;
+    // tridiagonal solver first, Jacobi for what it hands back
+    auto flush_tri = [&]() -> jolt_status {
+        HIPCHK(launch_eig_tridiag(tb, maxT, c.st), "eig (tridiagonal)");
+        HIPCHK(launch_jacobi_lds(tb, maxT, max_sweeps, c.st, 1), "eig (Jacobi retry)");
+        tb.n = 0;
+        maxT = 0;
+        return JOLT_OK;
+    };
     for (const EigReq &r : reqs) {
-        if (r.n <= kJacobiMaxN) {
+        if (r.n <= kTriMaxN && r.sw) {
+            JacItem &j = tb.it[tb.n++];
+            j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
+            j.raw = 0;
+            maxT = std::max(maxT, r.n);
+            if (tb.n == 64)
+                if (jolt_status s = flush_tri()) return s;
+        } else if (r.n <= kJacobiMaxN) {
             JacItem &j = jb.it[jb.n++];
             j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
             j.raw = 0;
@@ -397,6 +412,8 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
         }
     }
     HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
+    if (tb.n)
+        if (jolt_status s = flush_tri()) return s;
     for (size_t g = 0; g < large.size(); ++g) {
         jolt_status s = eig_block(c, large[g], largeN[g], scr, max_sweeps, noconv);
         if (s) return s;

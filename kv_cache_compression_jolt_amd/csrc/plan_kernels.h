@@ -101,7 +101,15 @@ struct JacItem {
 };
 struct JacBatch { JacItem it[64]; int n; };
 constexpr int kJacobiMaxN = 142;
-hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s);
+// retry_only: solve only the items whose sweeps_out holds kEigRetry
+hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s, int retry_only = 0);
+
+// Householder tridiagonal eigensolver for n <= kTriMaxN (same outputs as the
+// Jacobi kernel; sweeps_out is required and receives 0, or kEigRetry when the
+// matrix must be handed to the Jacobi kernel)
+constexpr int kTriMaxN = 140;
+constexpr int kEigRetry = -2;
+hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s);
 
 // block Jacobi state of one large symmetric matrix (N = padded size, multiple of 128)
 struct EigItem {
