@@ -3,6 +3,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Phase timestamps for one workgroup of a kernel: a no-op unless a
+// measurement build defines JOLT_PROBE(slot) to record the cycle counter.
+#ifndef JOLT_PROBE
+#define JOLT_PROBE(slot) ((void)0)
+#endif
+
 namespace jolt {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -89,6 +95,23 @@ __device__ __forceinline__ void mfma(const FragBF16 &a, const FragBF16 &b, f32x1
 __device__ __forceinline__ void mfma(const FragF32 &a, const FragF32 &b, f32x16 &acc) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- wave reductions (all 64 lanes)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+    return v;
 }
 
 __device__ __forceinline__ int frag_row(int lane, int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }

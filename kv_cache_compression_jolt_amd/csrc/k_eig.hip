@@ -31,22 +31,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kRowBatch = 5;           // rows per wave per load batch in the rank-2 update
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-    return v;
-}
 
 // C (n x n) tile (tm, tn) of sum_k A(m, k) B(k, n) on v_mfma_f32_32x32x2f32, with
 // A(m, k) = a[k * lda_k + m * lda_m] and B(k, n) = b[k * ld + n]; out of range
@@ -100,6 +86,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     float *Qt = sm + boff;  // Qt[c * ld + r] = Q[r][c]; later V = Q Z (row-major)
     float *sp = sbuf, *su = sbuf + kTriMaxN;
 
+    JOLT_PROBE(0);
     if (tid == 0) s_fail = 0;
     for (int e = tid; e < n * n; e += kThreads) {
         const int r = e / n, c = e - r * n;
@@ -113,6 +100,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     // tau = 2 / v^T v.  Then p = tau A22 v, w = p - (tau p^T v / 2) v,
     // A22 -= v w^T + w v^T and Q[:, j+1:] -= tau (Q[:, j+1:] v) v^T.
     const int rl = lane & 15, q4 = lane >> 4;
+    JOLT_PROBE(1);
     for (int j = 0; j + 2 < n; ++j) {
         __syncthreads();
         const int s = n - j - 1;
@@ -147,7 +135,22 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
             float acc = 0.f;
             if (r < rows) {
                 const float *col = isp ? (A + (j + 1) * ld + j + 1 + r) : (Qt + (j + 1) * ld + r);
-                for (int c = q4; c < s; c += 4) acc = fmaf(col[c * ld], c == 0 ? v0 : rowj[c], acc);
+                // 8 independent products in flight per lane
+                float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                int c = q4;
+                for (; c + 28 < s; c += 32) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int cc = c + 4 * u;
+                        a8[u] = fmaf(col[cc * ld], cc == 0 ? v0 : rowj[cc], a8[u]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int cc = c + 4 * u;
+                    if (cc < s) a8[u] = fmaf(col[cc * ld], cc == 0 ? v0 : rowj[cc], a8[u]);
+                }
+                acc = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
             }
             acc += __shfl_xor(acc, 16);
             acc += __shfl_xor(acc, 32);
@@ -169,23 +172,37 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
             wr[t] = r < s ? sp[r] - hk * vr[t] : 0.f;
             ur[t] = r < n ? su[r] : 0.f;
         }
-        for (int c = wid; c < s; c += kWaves) {
-            const float vc = c == 0 ? v0 : rowj[c];
-            const float wc = sp[c] - hk * vc;
-            float *arow = A + (j + 1 + c) * ld + j + 1;
-            // (v_c w_r) + (w_c v_r): the same two products and one sum as the
-            // mirrored entry, so A keeps exact symmetry (no contraction)
+        // rows c = wid + 16 g of A22 and of Q^T: all loads of a batch of rows
+        // first, then the updates (one LDS round trip per batch)
+        for (int c0 = wid; c0 < s; c0 += kWaves * kRowBatch) {
+            float av[kRowBatch][3], qv[kRowBatch][3], vcs[kRowBatch], wcs[kRowBatch];
 #pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                const int r = lane + 64 * t;
-                if (r < s) arow[r] = arow[r] - (vc * wr[t] + wc * vr[t]);
+            for (int g = 0; g < kRowBatch; ++g) {
+                const int c = c0 + kWaves * g;
+                const bool ok = c < s;
+                const float vc = ok ? (c == 0 ? v0 : rowj[c]) : 0.f;
+                vcs[g] = vc;
+                wcs[g] = ok ? sp[c] - hk * vc : 0.f;
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    const int r = lane + 64 * t;
+                    av[g][t] = (ok && r < s) ? A[(j + 1 + c) * ld + j + 1 + r] : 0.f;
+                    qv[g][t] = (ok && r < n) ? Qt[(j + 1 + c) * ld + r] : 0.f;
+                }
             }
-            float *qrow = Qt + (j + 1 + c) * ld;
-            const float tv = tau * vc;
 #pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                const int r = lane + 64 * t;
-                if (r < n) qrow[r] = fmaf(-tv, ur[t], qrow[r]);
+            for (int g = 0; g < kRowBatch; ++g) {
+                const int c = c0 + kWaves * g;
+                if (c >= s) continue;
+                const float vc = vcs[g], wc = wcs[g], tv = tau * vc;
+                // (v_c w_r) + (w_c v_r): the same two products and one sum as the
+                // mirrored entry, so A keeps exact symmetry (no contraction)
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    const int r = lane + 64 * t;
+                    if (r < s) A[(j + 1 + c) * ld + j + 1 + r] = av[g][t] - (vc * wr[t] + wc * vr[t]);
+                    if (r < n) Qt[(j + 1 + c) * ld + r] = fmaf(-tv, ur[t], qv[g][t]);
+                }
             }
         }
     }
@@ -200,6 +217,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     __syncthreads();
 
     // ---------------------------------------------------------------- 2. eigenvalues
+    JOLT_PROBE(2);
     float glo = FLT_MAX, ghi = -FLT_MAX;
     for (int i = lane; i < n; i += 64) {
         const float rad = (i > 0 ? fabsf(se[i - 1]) : 0.f) + (i + 1 < n ? fabsf(se[i]) : 0.f);
@@ -239,6 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     __syncthreads();
 
     // ---------------------------------------------------------------- 3. vectors of T
+    JOLT_PROBE(3);
     float *Z = A;      // Z[i * ld + k]: column k belongs to the k-th smallest eigenvalue
     if (tid < n) {
         const int k = tid;
@@ -298,6 +317,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     }
 
     // ---------------------------------------------------------------- 4. V = Q Z
+    JOLT_PROBE(4);
     const int nt = (n + 31) >> 5, ntiles = nt * nt;
     float *V = Qt;     // V[r * ld + c], kept in the Q buffer from here on
     {
@@ -310,6 +330,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     __syncthreads();
 
     // ---------------------------------------------------------------- 5. Newton-Schulz steps
+    JOLT_PROBE(5);
     // G = V^T V and M = (3 I - G) / 2 (M in the Z buffer); V <- V M
     for (int step = 0;; ++step) {
         float dev = 0.f;
@@ -356,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     const float *W = V;
 
     // ---------------------------------------------------------------- output
+    JOLT_PROBE(6);
     if (tid < n) {
         const int k = tid, col = n - 1 - k;
         int best = 0;

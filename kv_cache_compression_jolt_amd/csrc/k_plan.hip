@@ -207,66 +207,6 @@ __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
     }
 }
 
-// ====================================================================== fp32 GEMM
-// 64x64 tile, 16-deep K slices staged in LDS, 4x4 outputs per thread.
-__global__ __launch_bounds__(256) void k_gemm(GemmBatch batch, int maxSplit) {
-    __shared__ float As[16][64 + 4];
-    __shared__ float Bs[16][64 + 4];
-    const int z = blockIdx.z;
-    const GemmItem &it0 = batch.it[z % batch.n];
-    const int sp = (z / batch.n) % maxSplit, bi = (z / batch.n) / maxSplit;
-    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-    if (sp >= it0.nsplit || bi >= it0.nb || i0 >= it0.M || j0 >= it0.N) return;
-    GemmItem it = it0;
-    it.a += bi * it0.a_z;
-    it.b += bi * it0.b_z;
-    it.c += bi * it0.c_z;
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    const int kb = sp * it.kchunk, ke = min(it.K, kb + it.kchunk);
-    float acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-    const bool a_kfast = it.a_k == 1, b_jfast = it.b_j == 1;
-    for (int k0 = kb; k0 < ke; k0 += 16) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + 256 * q;
-            int ii, kk;
-            if (a_kfast) { ii = e / 16; kk = e % 16; } else { ii = e % 64; kk = e / 64; }
-            const int gi = i0 + ii, gk = k0 + kk;
-            As[kk][ii] = (gi < it.M && gk < ke) ? it.a[(int64_t)gi * it.a_i + (int64_t)gk * it.a_k] : 0.f;
-            int jj, kb2;
-            if (b_jfast) { kb2 = e / 64; jj = e % 64; } else { kb2 = e % 16; jj = e / 16; }
-            const int gj = j0 + jj, gk2 = k0 + kb2;
-            Bs[kb2][jj] = (gj < it.N && gk2 < ke) ? it.b[(int64_t)gk2 * it.b_k + (int64_t)gj * it.b_j] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            float av[4], bv[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) av[a] = As[kk][ty * 4 + a];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) bv[b] = Bs[kk][tx * 4 + b];
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(av[a], bv[b], acc[a][b]);
-        }
-        __syncthreads();
-    }
-    float *c = it.c + (int64_t)sp * it.c_split;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int gi = i0 + ty * 4 + a, gj = j0 + tx * 4 + b;
-            if (gi < it.M && gj < it.N) c[(int64_t)gi * it.c_i + (int64_t)gj * it.c_j] = acc[a][b];
-        }
-}
-
 // ====================================================================== split reduction
 __global__ void k_reduce(ReduceBatch batch) {
     const ReduceItem &it = batch.it[blockIdx.y];
@@ -335,37 +275,11 @@ __global__ __launch_bounds__(1024) void k_cholesky(CholBatch batch) {
         const int j = e - i * (i + 1) / 2;
         const float dj = fmaxf(lp[j * (j + 1) / 2 + j], shift);
         const float v = (i == j) ? sqrtf(dj) : lp[e] / sqrtf(dj);
-        if (!it.inverse) it.l[(size_t)i * it.ld + j] = v;
-        else lp[k * (k + 1) / 2 + e] = v;      // scaled L goes to the second half
-    }
-    if (!it.inverse) {
-        for (int e = tid; e < k * k; e += nt) {
-            const int i = e / k, j = e % k;
-            if (j > i) it.l[(size_t)i * it.ld + j] = 0.f;
-        }
-        return;
-    }
-    __syncthreads();
-    // X = L^{-1} by rows: X[i][j] = (delta_ij - sum_{c=j}^{i-1} L[i][c] X[c][j]) / L[i][i];
-    // 32 lanes per output element, one barrier per row.  L (packed) now sits in the
-    // second half of the LDS block, X overwrites the first half.
-    const float *lq = lp + k * (k + 1) / 2;
-    float *xp = lp;
-    const int grp = tid >> 5, ln = tid & 31, ngrp = nt >> 5;
-    for (int i = 0; i < k; ++i) {
-        const float *li = lq + i * (i + 1) / 2;
-        const float rii = 1.f / li[i];
-        for (int j = grp; j <= i; j += ngrp) {
-            float acc = 0.f;
-            for (int c = j + ln; c < i; c += 32) acc = fmaf(li[c], xp[c * (c + 1) / 2 + j], acc);
-            for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 32);
-            if (ln == 0) xp[i * (i + 1) / 2 + j] = ((i == j ? 1.f : 0.f) - acc) * rii;
-        }
-        __syncthreads();
+        it.l[(size_t)i * it.ld + j] = v;
     }
     for (int e = tid; e < k * k; e += nt) {
         const int i = e / k, j = e % k;
-        it.l[(size_t)i * it.ld + j] = (j <= i) ? xp[i * (i + 1) / 2 + j] : 0.f;
+        if (j > i) it.l[(size_t)i * it.ld + j] = 0.f;
     }
 }
 
@@ -400,29 +314,6 @@ __global__ __launch_bounds__(1024) void k_trsm(TrsmBatch batch, int l_in_lds) {
     for (int e = tid; e < k * 32; e += 1024) {
         const int r = e / 32, c = e % 32;
         if (t0 + c < it.len) it.q[(size_t)r * it.ldy + t0 + c] = qs[r * 33 + c];
-    }
-}
-
-// ====================================================================== y <- L^{-1} y (explicit inverse)
-// WG of 256 threads owns 64 columns of y[k][len] for all k rows: loads them to
-// LDS, multiplies by the lower-triangular X = L^{-1} (rows of X read from
-// global memory, shared by all lanes) and writes back in place.
-__global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch) {
-    extern __shared__ float ys[];          // [k][65]
-    const TrsmItem &it = batch.it[blockIdx.y];
-    const int t0 = blockIdx.x * 64;
-    if (t0 >= it.len) return;
-    const int k = it.k, tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int e = threadIdx.x; e < k * 64; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        ys[r * 65 + c] = (t0 + c < it.len) ? it.y[(size_t)r * it.ldy + t0 + c] : 0.f;
-    }
-    __syncthreads();
-    for (int i = ty; i < k; i += 4) {
-        const float *xi = it.l + (size_t)i * it.ld;
-        float acc = 0.f;
-        for (int c = 0; c <= i; ++c) acc = fmaf(xi[c], ys[c * 65 + tx], acc);
-        if (t0 + tx < it.len) it.q[(size_t)i * it.ldy + t0 + tx] = acc;
     }
 }
 
@@ -816,7 +707,6 @@ static hipError_t ensure_lds_attrs() {
         hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<1024>));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_cholesky));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_trsm));
-        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_apply_linv));
         state = e;
     }
     return state;
@@ -883,13 +773,6 @@ hipError_t launch_gram_rows(const GramBatch &b, int dtype, int d, int maxP, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s) {
-    if (b.n <= 0) return hipSuccess;
-    dim3 g((maxN + 63) / 64, (maxM + 63) / 64, b.n * maxSplit * maxNb);
-    hipLaunchKernelGGL(k_gemm, g, dim3(256), 0, s, b, maxSplit);
-    return hipGetLastError();
-}
-
 hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s) {
     if (b.n <= 0 || maxCount <= 0) return hipSuccess;
     dim3 g((unsigned)((maxCount + 255) / 256), b.n);
@@ -899,19 +782,18 @@ hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s) 
 
 hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    // items with inverse != 0 go to the fused elimination, the rest to the factor
+    CholBatch inv{}, fac{};
+    int maxInv = 0, maxFac = 0;
+    for (int i = 0; i < b.n; ++i) {
+        if (b.it[i].inverse) { inv.it[inv.n++] = b.it[i]; maxInv = std::max(maxInv, b.it[i].k); }
+        else { fac.it[fac.n++] = b.it[i]; maxFac = std::max(maxFac, b.it[i].k); }
+    }
+    if (hipError_t e = launch_chol_inv(inv, maxInv, s); e != hipSuccess) return e;
+    if (fac.n == 0) return hipSuccess;
     if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
-    bool inv = false;
-    for (int i = 0; i < b.n; ++i) inv |= b.it[i].inverse != 0;
-    const size_t lds = (size_t)maxK * (maxK + 1) / 2 * sizeof(float) * (inv ? 2 : 1);
-    hipLaunchKernelGGL(k_cholesky, dim3(b.n), dim3(1024), lds, s, b);
-    return hipGetLastError();
-}
-
-hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
-    if (b.n <= 0) return hipSuccess;
-    if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
-    const size_t lds = (size_t)maxK * 65 * sizeof(float);
-    hipLaunchKernelGGL(k_apply_linv, dim3((maxLen + 63) / 64, b.n), dim3(256), lds, s, b);
+    const size_t lds = (size_t)maxFac * (maxFac + 1) / 2 * sizeof(float);
+    hipLaunchKernelGGL(k_cholesky, dim3(fac.n), dim3(1024), lds, s, fac);
     return hipGetLastError();
 }
 

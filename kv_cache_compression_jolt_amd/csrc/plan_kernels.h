@@ -68,7 +68,7 @@ hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s);
 // Cholesky of G + shift I (k x k, ld) -> lower L written to l (k x k, ld), zeros above
 struct CholItem {
     const float *g;
-    float *l;            // L, or L^{-1} when inverse != 0 (k <= 200)
+    float *l;            // L, or L^{-1} when inverse != 0 (k <= kCholInverseMaxK)
     int k, ld;
     float rel_shift;     // shift = rel_shift * trace(G) / k
     int inverse;
@@ -87,7 +87,9 @@ struct TrsmBatch { TrsmItem it[kMaxBatch]; int n; };
 hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
 // y <- X y with X = L^{-1} lower triangular (in place; k <= 600)
 hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
-constexpr int kCholInverseMaxK = 200;
+constexpr int kCholInverseMaxK = 192;
+// the fused elimination behind launch_cholesky for the inverse != 0 items
+hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s);
 
 // symmetric eigen-decomposition by parallel-order two-sided Jacobi in LDS (n <= 142)
 // vec[r][c] = component r of eigenvector c, eigenvalues descending, sign-normalised.
