@@ -25,6 +25,23 @@ namespace jolt {
 
 // ====================================================================== X-pass A M
 // WG: 4 waves x 32 tokens; each wave owns NF column fragments (32 columns each).
+// The K range of a workgroup is a whole number of 64-feature chunks (d is a
+// multiple of 64); each chunk's fragment loads (U of A, U NF of M) are issued
+// before its MFMAs, with no branches in between.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag frag_select(bool keep, const typename Elem<T>::Frag &f) {
+    typename Elem<T>::Frag z = f;
+    if constexpr (sizeof(T) == 2) {
+        uint4 u = __builtin_bit_cast(uint4, f.v);
+        u.x = keep ? u.x : 0u; u.y = keep ? u.y : 0u; u.z = keep ? u.z : 0u; u.w = keep ? u.w : 0u;
+        z.v = __builtin_bit_cast(bf16x8, u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z.v[i] = keep ? f.v[i] : 0.f;
+    }
+    return z;
+}
+
 template <typename T, int NF>
 __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles) {
     const XmItem &it = batch.it[blockIdx.z];
@@ -40,26 +57,37 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles
     f32x16 acc[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
-    int ncf = (it.ncols - c0 + 31) / 32;
-    if (ncf > NF) ncf = NF;
-    const int kb = sp * it.lh_split * d, ke = min(n, kb + it.lh_split * d);
-    for (int k0 = kb; k0 < ke; k0 += 16) {
-        const int lh = k0 / d, f0 = k0 - lh * d + 8 * h;
-        typename Elem<T>::Frag a = load_frag(x + ((size_t)lh * it.T + tok) * d + f0);
-        const T *mb = m + (size_t)lh * it.m_blk + f0;
+    const T *mcol[NF];
+    bool cval[NF];
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            if (f < ncf) {
-                const int c = c0 + 32 * f + ln;
-                typename Elem<T>::Frag b = (c < it.ncols) ? load_frag(mb + (size_t)c * it.m_c) : zero_frag(m);
-                mfma(a, b, acc[f]);
-            }
+    for (int f = 0; f < NF; ++f) {
+        const int c = c0 + 32 * f + ln;
+        cval[f] = c < it.ncols;
+        mcol[f] = m + (size_t)(cval[f] ? c : 0) * it.m_c + 8 * h;
+    }
+    // K steps per chunk: as many as the registers for the staged fragments allow
+    constexpr int U = sizeof(T) == 2 ? (NF <= 5 ? 4 : 2) : (NF <= 5 ? 2 : 1);
+    const int kb = sp * it.lh_split * d, ke = min(n, kb + it.lh_split * d);
+    for (int k0 = kb; k0 < ke; k0 += 16 * U) {
+        const int lh = k0 / d, fb = k0 - lh * d;
+        const T *xa = x + ((size_t)lh * it.T + tok) * d + fb + 8 * h;
+        const size_t mo = (size_t)lh * it.m_blk + fb;
+        typename Elem<T>::Frag a[U], b[U][NF];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = load_frag(xa + 16 * u);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) b[u][f] = load_frag(mcol[f] + mo + 16 * u);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int f = 0; f < NF; ++f) mfma(a[u], frag_select<T>(cval[f], b[u][f]), acc[f]);
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         const int c = c0 + 32 * f + ln;
-        if (f < ncf && c < it.ncols) {
+        if (c < it.ncols) {
             float *o = it.out + (size_t)sp * it.ncols * it.ldo + (size_t)c * it.ldo + t0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -578,6 +606,40 @@ __global__ void k_energy_batch(SmallBatch batch) {
     it.out32[e] = s;
 }
 
+// One workgroup per item: step x step block sums, then prefix sums along the
+// rows and down the columns of the grid (in place, fp64), then the fixed-rank sum.
+__global__ __launch_bounds__(256) void k_energy_grid(GridBatch batch) {
+    __shared__ double red[4];
+    const GridItem &it = batch.it[blockIdx.x];
+    const int tid = threadIdx.x, nr = it.nr, nf = it.nf, st = it.step, d = it.d;
+    for (int c = tid; c < nr * nf; c += 256) {
+        const int bi = c / nf, bj = c - bi * nf;
+        double s = 0.0;
+        for (int r = bi * st; r < (bi + 1) * st; ++r)
+            for (int f = bj * st; f < (bj + 1) * st; ++f) s += (double)it.E[(size_t)r * d + f];
+        it.S[c] = s;
+    }
+    __syncthreads();
+    for (int bi = tid; bi < nr; bi += 256)
+        for (int bj = 1; bj < nf; ++bj) it.S[bi * nf + bj] += it.S[bi * nf + bj - 1];
+    __syncthreads();
+    for (int bj = tid; bj < nf; bj += 256)
+        for (int bi = 1; bi < nr; ++bi) it.S[bi * nf + bj] += it.S[(bi - 1) * nf + bj];
+    if (it.frt > 0 && it.frf > 0) {
+        double s = 0.0;
+        for (int e = tid; e < it.frt * it.frf; e += 256) {
+            const int r = e / it.frf, f = e - r * it.frf;
+            s += (double)it.E[(size_t)r * d + f];
+        }
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        if ((tid & 63) == 0) red[tid >> 6] = s;
+        __syncthreads();
+        if (tid == 0) *it.s_fixed = (red[0] + red[1]) + (red[2] + red[3]);
+    } else if (tid == 0) {
+        *it.s_fixed = 0.0;
+    }
+}
+
 __global__ void k_to_bf16_batch(SmallBatch batch) {
     const SmallItem &it = batch.it[blockIdx.y];
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < it.count; i += (int64_t)gridDim.x * blockDim.x) {
@@ -845,6 +907,11 @@ hipError_t launch_trace_batch(const SmallBatch &b, hipStream_t s) {
 hipError_t launch_energy_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s) {
     if (b.n <= 0 || maxCount <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_energy_batch, dim3((unsigned)((maxCount + 255) / 256), b.n), dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+hipError_t launch_energy_grid(const GridBatch &b, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_energy_grid, dim3(b.n), dim3(256), 0, s, b);
     return hipGetLastError();
 }
 hipError_t launch_to_bf16_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s) {

@@ -24,12 +24,15 @@ void make_header(const jolt_item &it, const jolt_alloc &a, uint8_t out[64]);
 
 // Per-item factor storage inside plan_ws, followed by per-chunk scratch.
 struct FactorOffsets {
-    size_t ut, uf, lam_t, lam_f, core, energy, normx2, sweeps;
+    size_t ut, uf, lam_t, lam_f, core, energy, grid, sfixed, normx2, sweeps;
 };
 struct PlanLayout {
     int rt_max, rf_max, k, kp;              // k = sketch width (randomized) ; kp = padded
+    int step, grid_nr, grid_nf;              // candidate rank step; captured-energy grid (rt_max / step) x (rf_max / step)
     std::vector<FactorOffsets> item;
-    size_t readback, readback_stride;        // energy | ||X||^2 | sweep counters, one block per item
+    // host-bound results, one block per item: captured-energy grid S (fp64) |
+    // S at the fixed ranks | ||X||^2 | eigensolver status
+    size_t readback, readback_stride;
     size_t scratch;                          // start of the scratch region
     size_t scratch_bytes;                    // per chunk
     size_t total;

@@ -14,6 +14,7 @@
 // Q = L^{-1} Y (rows are the basis vectors), once for the intermediate bases
 // and twice for the final one.
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -206,11 +207,14 @@ jolt_status plan_layout(const jolt_config &cfg, const jolt_item *items, int n, P
     pl.kp = round_up(std::max(pl.k, 1), 32);
     Bump b;
     pl.item.resize(n);
-    // host-bound results of all items in one block: [energy rt x d | normx2 | sweeps]
-    size_t dmax = 0;
-    for (int i = 0; i < n; ++i) dmax = std::max<size_t>(dmax, items[i].d);
+    // host-bound results of all items in one block, per item:
+    // [S grid (grid_nr x grid_nf doubles) | S at the fixed ranks | ||X||^2 | status]
     const size_t rt1 = std::max(pl.rt_max, 1);
-    pl.readback_stride = align_up(rt1 * dmax * 4 + 8 + 16, 256);
+    pl.step = std::max(cfg.rank_step, 1);
+    pl.grid_nr = pl.rt_max / pl.step;
+    pl.grid_nf = pl.rf_max / pl.step;
+    const size_t cells = std::max(pl.grid_nr * pl.grid_nf, 1);
+    pl.readback_stride = align_up(cells * 8 + 8 + 8 + 16, 256);
     pl.readback = b.take(pl.readback_stride * std::max(n, 1));
     for (int i = 0; i < n; ++i) {
         const jolt_item &it = items[i];
@@ -223,8 +227,10 @@ jolt_status plan_layout(const jolt_config &cfg, const jolt_item *items, int n, P
         o.lam_t = b.take(nlam * 4);
         o.lam_f = b.take(d * 4);
         o.core = b.take(LH * rt * d * 4);
-        o.energy = pl.readback + i * pl.readback_stride;
-        o.normx2 = o.energy + rt1 * dmax * 4;
+        o.energy = b.take(rt * d * 4);
+        o.grid = pl.readback + i * pl.readback_stride;
+        o.sfixed = o.grid + cells * 8;
+        o.normx2 = o.sfixed + 8;
         o.sweeps = o.normx2 + 8;
     }
     pl.scratch = b.off;
@@ -745,6 +751,17 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             t.a = D[i].LH; t.b = pl.rt_max; t.c = d;
         }
         HIPCHK(launch_energy_batch(eb, (int64_t)pl.rt_max * d, c.st), "energy");
+        GridBatch gbt{};
+        for (int i = 0; i < nb; ++i) {
+            GridItem &g = gbt.it[gbt.n++];
+            g.E = reinterpret_cast<const float *>(ws + pl.item[i0 + i].energy);
+            g.S = reinterpret_cast<double *>(ws + pl.item[i0 + i].grid);
+            g.s_fixed = reinterpret_cast<double *>(ws + pl.item[i0 + i].sfixed);
+            g.d = d; g.step = pl.step; g.nr = pl.grid_nr; g.nf = pl.grid_nf;
+            g.frt = cfg.budget_bytes < 0 ? std::min(cfg.fixed_rt, pl.rt_max) : 0;
+            g.frf = cfg.budget_bytes < 0 ? std::min(cfg.fixed_rf, d) : 0;
+        }
+        HIPCHK(launch_energy_grid(gbt, c.st), "energy grid");
     }
     return JOLT_OK;
 }
@@ -807,6 +824,9 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     uint8_t *ws = static_cast<uint8_t *>(plan_ws);
     Ctx c{h, st, items[0].dtype, items[0].d};
     bool noconv = false;
+    // JOLT_TIMING=1: host-side phase times of this call on stderr
+    static const bool timing = getenv("JOLT_TIMING") != nullptr;
+    const auto t_start = std::chrono::steady_clock::now();
     for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
         const int nb = std::min(kMaxBatch, n - c0);
         s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv);
@@ -816,16 +836,26 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     const int rt_max = pl.rt_max;
     std::vector<uint8_t> rb(pl.readback_stride * n);
     hipError_t e = hipMemcpyAsync(rb.data(), ws + pl.readback, rb.size(), hipMemcpyDeviceToHost, st);
+    const auto t_launched = std::chrono::steady_clock::now();
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(h, e, "plan");
-    std::vector<std::vector<float>> E(n);
-    std::vector<double> nx2(n);
+    const auto t_synced = std::chrono::steady_clock::now();
+    auto report = [&]() {
+        if (!timing) return;
+        auto us = [](std::chrono::steady_clock::time_point a, std::chrono::steady_clock::time_point b) {
+            return std::chrono::duration<double, std::micro>(b - a).count();
+        };
+        const auto t_end = std::chrono::steady_clock::now();
+        fprintf(stderr, "libjolt plan: launch %.1f us, wait for device %.1f us, tables + dual %.1f us\n",
+                us(t_start, t_launched), us(t_launched, t_synced), us(t_synced, t_end));
+    };
+    const size_t cells = (size_t)std::max(pl.grid_nr * pl.grid_nf, 1);
+    std::vector<const double *> grid(n);
+    std::vector<double> nx2(n), sfix(n);
     for (int i = 0; i < n; ++i) {
-        const uint8_t *blk = rb.data() + (pl.item[i].energy - pl.readback);
-        const size_t d = items[i].d;
-        E[i].assign((size_t)std::max(rt_max, 1) * d, 0.f);
-        // energy rows were written with leading dimension d
-        std::memcpy(E[i].data(), blk, (size_t)rt_max * d * 4);
+        grid[i] = reinterpret_cast<const double *>(rb.data() + (pl.item[i].grid - pl.readback));
+        (void)cells;
+        std::memcpy(&sfix[i], rb.data() + (pl.item[i].sfixed - pl.readback), 8);
         std::memcpy(&nx2[i], rb.data() + (pl.item[i].normx2 - pl.readback), 8);
         int sw[2];
         std::memcpy(sw, rb.data() + (pl.item[i].sweeps - pl.readback), 8);
@@ -840,30 +870,19 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
             a.rt = cfg->fixed_rt; a.rf = cfg->fixed_rf; a.bits = cfg->fixed_bits; a.reserved = 0;
             if (a.rt == 0 || a.rf == 0) a.rt = a.rf = 0;
             a.bytes = jolt_item_bytes(&items[i], a.rt, a.rf, a.bits);
-            double S = 0.0;
-            for (int r = 0; r < a.rt; ++r)
-                for (int f = 0; f < a.rf; ++f) S += (double)E[i][(size_t)r * items[i].d + f];
+            const double S = (a.rt == 0 || a.rf == 0) ? 0.0 : sfix[i];
             a.distortion = std::max(0.0, nx2[i] - S);
         }
         if (lambda_out) *lambda_out = -1.0;
+        report();
         return noconv ? fail(h, JOLT_E_NOCONV, "eigensolver hit its sweep cap") : JOLT_OK;
     }
     std::vector<Cand> cand = candidate_grid(rt_max, rf_max, cfg->rank_step, cfg->bits_mask);
     const int nc = (int)cand.size();
     std::vector<std::vector<double>> Dt(n, std::vector<double>(nc));
     std::vector<std::vector<int64_t>> Bt(n, std::vector<int64_t>(nc));
-    std::vector<double> prefix((size_t)std::max(rt_max, 1) * std::max(rf_max, 1));
     for (int i = 0; i < n; ++i) {
-        const int d = items[i].d;
-        for (int r = 0; r < rt_max; ++r)
-            for (int f = 0; f < rf_max; ++f) {
-                double v = (double)E[i][(size_t)r * d + f];
-                if (r > 0) v += prefix[(size_t)(r - 1) * rf_max + f];
-                if (f > 0) v += prefix[(size_t)r * rf_max + f - 1];
-                if (r > 0 && f > 0) v -= prefix[(size_t)(r - 1) * rf_max + f - 1];
-                prefix[(size_t)r * rf_max + f] = v;
-            }
-        distortion_table(prefix.data(), rf_max, nx2[i], cfg->delta_b, cand, Dt[i].data());
+        distortion_table(grid[i], pl.grid_nf, pl.step, nx2[i], cfg->delta_b, cand, Dt[i].data());
         for (int j = 0; j < nc; ++j)
             Bt[i][j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
     }
@@ -882,6 +901,7 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
         alloc_host[i].distortion = Dt[i][choice[i]];
     }
     if (lambda_out) *lambda_out = lam;
+    report();
     if (s == JOLT_E_INFEASIBLE) return fail(h, s, "budget below the sum of minimum item bytes");
     if (noconv) return fail(h, JOLT_E_NOCONV, "eigensolver hit its sweep cap");
     return JOLT_OK;

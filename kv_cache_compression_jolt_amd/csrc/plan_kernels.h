@@ -142,6 +142,17 @@ struct SmallItem {
 struct SmallBatch { SmallItem it[kMaxBatch]; int n; };
 hipError_t launch_trace_batch(const SmallBatch &b, hipStream_t s);
 hipError_t launch_energy_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s);
+
+// captured energy on the candidate grid, in fp64:
+// S[i][j] = sum_{r < step (i+1), f < step (j+1)} E[r][f] (E rows of length d),
+// and s_fixed = sum_{r < frt, f < frf} E[r][f] when frt > 0
+struct GridItem {
+    const float *E;
+    double *S, *s_fixed;
+    int d, step, nr, nf, frt, frf;
+};
+struct GridBatch { GridItem it[kMaxBatch]; int n; };
+hipError_t launch_energy_grid(const GridBatch &b, hipStream_t s);
 hipError_t launch_to_bf16_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s);
 hipError_t launch_gen_omega_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s);
 

@@ -55,20 +55,24 @@ struct ItemHull {
     std::vector<double> s;     // slope between v[j] and v[j+1] (decreasing)
 };
 
-bool key_less(const Cand &ca, double Da, int64_t Ba, const Cand &cb, double Db, int64_t Bb) {
-    if (Ba != Bb) return Ba < Bb;
-    if (Da != Db) return Da < Db;
-    if (ca.rt != cb.rt) return ca.rt < cb.rt;
-    if (ca.rf != cb.rf) return ca.rf < cb.rf;
-    return ca.bits < cb.bits;
-}
+struct Pt {
+    int64_t B;
+    double D;
+    int rt, rf, bits, idx;
+};
 
 ItemHull build_hull(int nc, const Cand *cand, const double *D, const int64_t *B) {
-    std::vector<int> order(nc);
-    std::iota(order.begin(), order.end(), 0);
-    std::sort(order.begin(), order.end(), [&](int a, int b) {
-        return key_less(cand[a], D[a], B[a], cand[b], D[b], B[b]);
+    std::vector<Pt> pts(nc);
+    for (int i = 0; i < nc; ++i) pts[i] = {B[i], D[i], cand[i].rt, cand[i].rf, cand[i].bits, i};
+    std::sort(pts.begin(), pts.end(), [](const Pt &a, const Pt &b) {
+        if (a.B != b.B) return a.B < b.B;
+        if (a.D != b.D) return a.D < b.D;
+        if (a.rt != b.rt) return a.rt < b.rt;
+        if (a.rf != b.rf) return a.rf < b.rf;
+        return a.bits < b.bits;
     });
+    std::vector<int> order(nc);
+    for (int i = 0; i < nc; ++i) order[i] = pts[i].idx;
     // staircase: one point per byte count, strictly falling D
     std::vector<int> stair;
     for (int i : order) {
@@ -140,11 +144,11 @@ jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, cons
     return JOLT_OK;
 }
 
-void distortion_table(const double *prefix /* (rt_max) x (rf_max), inclusive 2-D prefix sums */, int rf_max,
-                      double normx2, const double *delta, const std::vector<Cand> &cand, double *D) {
+void distortion_table(const double *grid /* captured energy S at (rt, rf) = (step (i+1), step (j+1)) */, int nf,
+                      int step, double normx2, const double *delta, const std::vector<Cand> &cand, double *D) {
     for (size_t i = 0; i < cand.size(); ++i) {
         const Cand &c = cand[i];
-        const double S = (c.rt == 0 || c.rf == 0) ? 0.0 : prefix[(size_t)(c.rt - 1) * rf_max + (c.rf - 1)];
+        const double S = (c.rt == 0 || c.rf == 0) ? 0.0 : grid[(size_t)(c.rt / step - 1) * nf + (c.rf / step - 1)];
         D[i] = delta[c.bits] * std::max(0.0, normx2 - S);
     }
 }

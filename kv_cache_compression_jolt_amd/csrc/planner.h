@@ -16,7 +16,7 @@ int64_t item_bytes_impl(int L, int H, int T, int d, int e, int rt, int rf, int b
 std::vector<Cand> candidate_grid(int rt_max, int rf_max, int step, uint32_t bits_mask);
 jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, const double *const *D,
                      const int64_t *const *B, int64_t budget, int *choice, double *lambda_out);
-void distortion_table(const double *prefix, int rf_max, double normx2, const double *delta,
+void distortion_table(const double *grid, int nf, int step, double normx2, const double *delta,
                       const std::vector<Cand> &cand, double *D);
 
 }  // namespace jolt
