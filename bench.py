@@ -10,14 +10,22 @@ caches (see synth/), standing in for real Mistral-7B-v0.3 caches.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Prints one JSON line.  The metric is KV tokens compressed per second, counted
-per layer group (groups x tokens / compress time); decompress GB/s and the
-roofline of the dominant kernel ride along.
+per layer group (groups x tokens / (plan + compress time)); decompress GB/s,
+per-kernel times and the roofline of the dominant kernel ride along.
+
+Roofline: during the warmup steps every kernel timer of the library is on
+(jolt_kernel_timer: a HIP event pair around each launch, on the launch
+stream); the kernel with the most device time per step is the dominant one.
+In the timed steps only its timer is on, and its average launch duration is
+what the roofline divides the kernel's algorithmic work per launch by.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,6 +33,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+KERNELS = ["k_eig_tridiag", "k_chol_inv", "k_apply_linv", "k_gemm", "k_reduce", "k_xm", "k_xtq", "k_gram_rows",
+           "k_build_wt", "k_encode", "k_decode", "k_jacobi_lds"]
+KERNEL_SOURCE = {"k_eig_tridiag": "k_eig.hip", "k_chol_inv": "k_orth.hip", "k_apply_linv": "k_orth.hip",
+                 "k_gemm": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
+                 "k_encode": "k_codec.hip", "k_decode": "k_codec.hip", "k_build_wt": "k_codec.hip"}
 
 
 def parse():
@@ -35,9 +51,63 @@ def parse():
     ap.add_argument("--config", default="mistral7b_gqa_1k")
     ap.add_argument("--ratio", type=float, default=2.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-items", type=int, default=2, help="items in the oracle's timed sample")
+    ap.add_argument("--cpu-items", type=int, default=16, help="items in the oracle's timed sample")
     ap.add_argument("--profile", action="store_true", help="few steps, no CPU baseline (for rocprofv3)")
     return ap.parse_args()
+
+
+def work_per_step(cfg, jitems, allocs):
+    """Algorithmic work of each kernel over one step: (kind, amount), kind 'bytes'
+    (HBM bytes read + written once) or 'flops'."""
+    k = cfg.rt_max + cfg.oversample
+    q = cfg.power_iters
+    out = {}
+    xb = sum(2 * cfg.elems_per_item for _ in jitems)             # one read of every cache tensor
+    n_lhd = [it.L * it.H * it.d for it in jitems]
+    # passes over X: A M (1 + q launches), Q^T A (q + 1 launches, the last with hi + lo Q), feature Gram
+    out["k_xm"] = ("bytes", (1 + q) * xb + sum((1 + q) * (2 * n * k + 4 * it.T * k) for n, it in zip(n_lhd, jitems)))
+    out["k_xtq"] = ("bytes", (q + 1) * xb + sum(2 * it.T * k * (q + 2) + (q + 1) * 4 * k * n
+                                                for n, it in zip(n_lhd, jitems)))
+    out["k_gram_rows"] = ("bytes", xb + sum(4 * it.d * it.d for it in jitems))
+    # dense symmetric eigendecomposition with vectors: 4/3 n^3 (tridiagonal) + 4/3 n^3 (Q) + 2 n^3 (Q Z)
+    out["k_eig_tridiag"] = ("flops", sum((4.0 / 3 + 4.0 / 3 + 2.0) * (k ** 3 + it.d ** 3) for it in jitems))
+    # CholeskyQR inverse factor: n^3 / 3 (factor) + n^3 / 3 (inverse), 2 q + 2 factorizations
+    out["k_chol_inv"] = ("flops", sum((2 * q + 2) * (2.0 / 3) * k ** 3 for _ in jitems))
+    # decode: payload in, dense out; encode: dense in, codes + scales out (+ stored params)
+    dec = enc = 0
+    for it, a in zip(jitems, allocs):
+        N = it.L * it.H * it.T * it.d
+        rt = a.rt if a.rf else 0
+        params = 2 * (it.T * rt + it.d * a.rf + it.L * it.H * rt * a.rf)
+        resid = (N * a.bits // 8 + 2 * N // 64) if a.bits else 0
+        dec += params + resid + 2 * N
+        enc += 2 * N + params + resid
+    out["k_decode"] = ("bytes", dec)
+    out["k_encode"] = ("bytes", enc)
+    return out
+
+
+def source_hash(kernel):
+    f = KERNEL_SOURCE.get(kernel)
+    if not f:
+        return None
+    with open(os.path.join(ROOT, "kv_cache_compression_jolt_amd", "csrc", f), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def pmc_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    kernel and workload, or None if there is none or the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_pmc.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source sha256\[:16\]: (\w+)", txt)
+    b = re.search(r"hbm bytes per launch: ([0-9.eE+]+)", txt)
+    if not m or not b or m.group(1) != source_hash(kernel):
+        return None
+    return float(b.group(1))
 
 
 def main():
@@ -85,47 +155,70 @@ def main():
         J.decompress(pays, outs, allocs)
         if ev: ev[3].record(stream)
 
-    for _ in range(args.warmup):
+    step()                       # first launches of every kernel (code objects load here)
+    torch.cuda.synchronize()
+    # warmup with every kernel timer on: per-kernel device time per step
+    for kname in KERNELS:
+        jb.jolt_kernel_timer(J.h, kname, True)
+    for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
+    per_step = {}
+    for kname in KERNELS:
+        ms, n = jb.jolt_kernel_time(J.h, kname)
+        jb.jolt_kernel_timer(J.h, kname, False)
+        if n:
+            per_step[kname] = (ms / max(args.warmup, 1), n / max(args.warmup, 1))
+    dominant = max(per_step, key=lambda kname: per_step[kname][0])
+    jb.jolt_kernel_timer(J.h, dominant, True)
+
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
+    for kk in range(args.steps):
+        step(evs[kk])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    dom_ms, dom_launches = jb.jolt_kernel_time(J.h, dominant)
+    jb.jolt_kernel_timer(J.h, dominant, False)
     plan_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     comp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     step_ms = wall * 1e3 / args.steps
 
-    # dominant streaming kernel: the fused decoder, timed alone (HIP events on its stream)
-    reps = 20
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        J.decompress(pays, outs, allocs)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dec_only_ms = e0.elapsed_time(e1) / reps
+    work = work_per_step(cfg, jitems, allocs)
+    launch_ms = dom_ms / max(dom_launches, 1)
+    launches_per_step = dom_launches / args.steps
+    if dominant in work:
+        dom_kind, amount = work[dominant]
+        per_launch = amount / max(launches_per_step, 1e-9)
+        if dom_kind == "bytes":
+            achieved = per_launch / (launch_ms * 1e-3) / 1e9
+            peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
+        else:
+            achieved = per_launch / (launch_ms * 1e-3) / 1e12
+            peak, unit, bound = FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s", "alu"
+    else:
+        dom_kind, per_launch, achieved, peak, unit, bound = "unknown", None, None, None, None, "unknown"
+    traffic = pmc_traffic(dominant, cfg.name)
 
     N = cfg.elems_per_item
     dense_bytes = sum(2 * N for _ in items)
-    read_bytes = 0
-    for it, a in zip(jitems, allocs):
-        rt = a.rt if a.rf else 0
-        params = 2 * (it.T * rt + it.d * a.rf + it.L * it.H * rt * a.rf)
-        resid = (N * a.bits // 8 + 2 * N // 64) if a.bits else 0
-        read_bytes += params + resid
-    alg_bytes = read_bytes + dense_bytes          # decoder: payload in, dense cache out
-    achieved = alg_bytes / (dec_only_ms * 1e-3) / 1e9
-
     layer_group_tokens = cfg.groups * cfg.sequences * cfg.T
-    compress_ms = plan_ms + comp_ms
-    value = layer_group_tokens / (compress_ms * 1e-3)
+    value = layer_group_tokens / ((plan_ms + comp_ms) * 1e-3)
     total_bytes = sum(a.bytes for a in allocs)
+
+    kernel_table = {}
+    for kname, (ms, n) in sorted(per_step.items(), key=lambda kv: -kv[1][0]):
+        row = {"ms_per_step": round(ms, 4), "launches_per_step": round(n, 2)}
+        if kname in work:
+            kind, amount = work[kname]
+            if kind == "bytes":
+                row["GBps"] = round(amount / (ms * 1e-3) / 1e9, 1)
+                row["hbm_frac"] = round(amount / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            else:
+                row["TFLOPs"] = round(amount / (ms * 1e-3) / 1e12, 3)
+        kernel_table[kname] = row
 
     out = {
         "metric": "KV tokens compressed/sec per layer group (+ decompress GB/s; % MFMA/HBM peak)",
@@ -148,10 +241,14 @@ def main():
         "compressed_bytes": int(total_bytes),
         "compression_ratio": round(dense_bytes / total_bytes, 4),
         "allocation": sorted(set((a.rt, a.rf, a.bits) for a in allocs)),
-        "roofline": {"kernel": "fused decode (unpack, dequant, inverse rotation, + U_t W~ via MFMA)",
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "launch_ms": round(dec_only_ms, 5), "algorithmic_bytes_per_launch": int(alg_bytes)},
+        "roofline": {"kernel": dominant, "bound": bound,
+                     "achieved": None if achieved is None else round(achieved, 3),
+                     "peak": peak, "unit": unit,
+                     "frac": None if achieved is None else round(achieved / peak, 5),
+                     "traffic": traffic,
+                     "launch_ms": round(launch_ms, 5), "launches_per_step": round(launches_per_step, 2),
+                     "algorithmic_per_launch": per_launch, "algorithmic_kind": dom_kind},
+        "kernels": kernel_table,
         "input_gen_s": round(gen_s, 2),
     }
 
@@ -165,7 +262,6 @@ def main():
 
 def cpu_baseline(cfg, items, budget, delta, m, layer_group_tokens):
     """The oracle (fp64 numpy + C Jacobi) on a sample of m items, same pipeline."""
-    import numpy as np
     from oracle import pipeline as opipe
     sample = items[:m]
     # the sample's share of the global budget keeps the allocation comparable

@@ -225,6 +225,19 @@ jolt_status jolt_rademacher(jolt_handle h, uint64_t seed, uint32_t item_id, uint
 jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const float *a, int32_t lda, int64_t mat_stride,
                       float *vec, float *lam, int32_t *info, int32_t force_jacobi, void *stream);
 
+/* ---- measurement hooks -------------------------------------------------- */
+/* Launch timing of one of the library's kernels, named as in its source
+ * ("k_decode", "k_encode", "k_xm", "k_xtq", "k_eig_tridiag", "k_chol_inv",
+ * "k_apply_linv", "k_gemm", "k_gram_rows", "k_reduce", "k_build_wt",
+ * "k_jacobi_lds").  While a kernel's timer is on, each of its launches is
+ * bracketed by a HIP event pair on its launch stream.  enable != 0 turns the
+ * timer on and resets it; enable == 0 turns it off (the totals are kept).
+ * Process-wide; h is used for error reporting only. */
+jolt_status jolt_kernel_timer(jolt_handle h, const char *kernel, int32_t enable);
+/* Total device time (ms) and number of timed launches of a kernel since its
+ * timer was last turned on.  Waits for the recorded events. */
+jolt_status jolt_kernel_time(jolt_handle h, const char *kernel, double *total_ms, int64_t *launches);
+
 #ifdef __cplusplus
 }
 #endif

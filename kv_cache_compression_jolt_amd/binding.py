@@ -55,7 +55,7 @@ EXPORTED = [
     "jolt_item_bytes", "jolt_payload_size", "jolt_payload_layout", "jolt_payload_header",
     "jolt_payload_validate", "jolt_plan", "jolt_compress", "jolt_encode_residual", "jolt_decompress",
     "jolt_plan_factors", "jolt_plan_from_tables", "jolt_rotate", "jolt_quantize_pack",
-    "jolt_unpack_dequant", "jolt_rademacher", "jolt_eigh",
+    "jolt_unpack_dequant", "jolt_rademacher", "jolt_eigh", "jolt_kernel_timer", "jolt_kernel_time",
 ]
 
 _lib = None
@@ -100,6 +100,8 @@ def lib():
             "jolt_unpack_dequant": (I32, [P, P, P, I64, I32, I32, P, P]),
             "jolt_rademacher": (I32, [P, U64, U32, U32, U64, I64, P, P]),
             "jolt_eigh": (I32, [P, I32, I32, P, I32, I64, P, P, P, I32, P]),
+            "jolt_kernel_timer": (I32, [P, C.c_char_p, I32]),
+            "jolt_kernel_time": (I32, [P, C.c_char_p, C.POINTER(D), C.POINTER(I64)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -248,6 +250,17 @@ def jolt_rademacher(h, seed, item_id, stream_id, first, count, out_ptr, stream):
 def jolt_eigh(h, n, count, a_ptr, lda, mat_stride, vec_ptr, lam_ptr, info_ptr, force_jacobi, stream):
     _check(lib().jolt_eigh(h, n, count, C.c_void_p(a_ptr), lda, mat_stride, C.c_void_p(vec_ptr),
                            C.c_void_p(lam_ptr), C.c_void_p(info_ptr), int(force_jacobi), C.c_void_p(stream)), h)
+
+
+def jolt_kernel_timer(h, kernel: str, enable: bool):
+    _check(lib().jolt_kernel_timer(h, kernel.encode(), int(bool(enable))), h)
+
+
+def jolt_kernel_time(h, kernel: str):
+    """(total device ms, launches) of a kernel since its timer was turned on."""
+    ms, n = C.c_double(0.0), C.c_int64(0)
+    _check(lib().jolt_kernel_time(h, kernel.encode(), C.byref(ms), C.byref(n)), h)
+    return ms.value, n.value
 
 
 # ------------------------------------------------------------------ helpers

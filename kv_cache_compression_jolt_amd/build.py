@@ -17,7 +17,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libjolt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "plan.cpp", "planner.cpp", "payload.cpp", "k_codec.hip", "k_plan.hip", "k_eig.hip", "k_orth.hip", "k_gemm.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "planner.cpp", "payload.cpp", "ktimer.cpp", "k_codec.hip", "k_plan.hip", "k_eig.hip", "k_orth.hip", "k_gemm.hip"]
 HEADERS = ["dev_common.h", "jolt_internal.h", "plan_kernels.h", "planner.h", "payload.h", "api_internal.h"]
 
 FLAGS = [

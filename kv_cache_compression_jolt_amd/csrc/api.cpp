@@ -13,6 +13,7 @@
 #include "api_internal.h"
 #include "jolt_internal.h"
 #include "payload.h"
+#include "ktimer.h"
 #include "plan_kernels.h"
 #include "planner.h"
 
@@ -438,4 +439,20 @@ extern "C" jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const 
         if (e != hipSuccess) return hip_fail(h, e, "eigh");
     }
     return JOLT_OK;
+}
+
+extern "C" jolt_status jolt_kernel_timer(jolt_handle h, const char *kernel, int32_t enable) {
+    if (!h) return JOLT_E_INVALID;
+    clear_err(h);
+    if (!kernel || !*kernel) return fail(h, JOLT_E_INVALID, "kernel_timer: no kernel name");
+    hipError_t e = ktimer_enable(kernel, enable != 0);
+    return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "kernel_timer");
+}
+
+extern "C" jolt_status jolt_kernel_time(jolt_handle h, const char *kernel, double *total_ms, int64_t *launches) {
+    if (!h) return JOLT_E_INVALID;
+    clear_err(h);
+    if (!kernel || !total_ms || !launches) return fail(h, JOLT_E_INVALID, "kernel_time: null argument");
+    hipError_t e = ktimer_read(kernel, total_ms, launches);
+    return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "kernel_time");
 }

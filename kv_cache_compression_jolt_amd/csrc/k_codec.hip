@@ -24,6 +24,7 @@
 // in-lane, and each lane stores its group's codes contiguously.
 #include "dev_common.h"
 #include "jolt_internal.h"
+#include "ktimer.h"
 
 namespace jolt {
 
@@ -586,6 +587,7 @@ static hipError_t decode_bits(const CodecBatch &b, int bits, dim3 grid, hipStrea
 
 hipError_t launch_encode(const CodecBatch &b, int dtype, int D, int bits, int maxT, int maxLH, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    KTimeScope kts("k_encode", s);
     dim3 grid((maxT + 127) / 128, maxLH, b.n);
     if (dtype == JOLT_BF16) return D == 128 ? encode_bits<uint16_t, 128>(b, bits, grid, s)
                                             : encode_bits<uint16_t, 64>(b, bits, grid, s);
@@ -593,6 +595,7 @@ hipError_t launch_encode(const CodecBatch &b, int dtype, int D, int bits, int ma
 }
 hipError_t launch_decode(const CodecBatch &b, int dtype, int D, int bits, int maxT, int maxLH, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    KTimeScope kts("k_decode", s);
     dim3 grid((maxT + 127) / 128, maxLH, b.n);
     if (dtype == JOLT_BF16) return D == 128 ? decode_bits<uint16_t, 128>(b, bits, grid, s)
                                             : decode_bits<uint16_t, 64>(b, bits, grid, s);
@@ -600,6 +603,7 @@ hipError_t launch_decode(const CodecBatch &b, int dtype, int D, int bits, int ma
 }
 hipError_t launch_build_wt(const WtBatch &b, int dtype, int D, int maxLH, int maxRtp, hipStream_t s) {
     if (b.n <= 0 || maxRtp <= 0) return hipSuccess;
+    KTimeScope kts("k_build_wt", s);
     dim3 grid((D / 32) * ((maxRtp + 31) / 32), maxLH, b.n);
     if (dtype == JOLT_BF16) hipLaunchKernelGGL(k_build_wt<uint16_t>, grid, dim3(64), 0, s, b, D);
     else hipLaunchKernelGGL(k_build_wt<float>, grid, dim3(64), 0, s, b, D);

@@ -24,6 +24,7 @@
 
 #include "dev_common.h"
 #include "plan_kernels.h"
+#include "ktimer.h"
 
 namespace jolt {
 
@@ -421,6 +422,7 @@ hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
     for (int i = 0; i < b.n; ++i)
         if (!b.it[i].sweeps_out || b.it[i].n > maxN) return hipErrorInvalidValue;
     if (hipError_t e = allow_lds_tri(); e != hipSuccess) return e;
+    KTimeScope kts("k_eig_tridiag", s);
     const int ld = maxN | 1;
     hipLaunchKernelGGL(k_eig_tridiag, dim3(b.n), dim3(kThreads), eig_tridiag_lds_bytes(maxN), s, b, ld, maxN * ld);
     return hipGetLastError();

@@ -8,6 +8,7 @@
 // coalesced along whichever index has stride 1.
 #include "dev_common.h"
 #include "plan_kernels.h"
+#include "ktimer.h"
 
 namespace jolt {
 
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmBatch batch, int maxSplit) {
 
 hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    KTimeScope kts("k_gemm", s);
     dim3 g((maxN + 63) / 64, (maxM + 63) / 64, b.n * maxSplit * maxNb);
     hipLaunchKernelGGL(k_gemm, g, dim3(256), 0, s, b, maxSplit);
     return hipGetLastError();

@@ -20,6 +20,7 @@
 
 #include "dev_common.h"
 #include "plan_kernels.h"
+#include "ktimer.h"
 
 namespace jolt {
 
@@ -267,6 +268,7 @@ hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     if (maxK > kCholInverseMaxK) return hipErrorInvalidValue;
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
+    KTimeScope kts("k_chol_inv", s);
     const int P = (maxK + 31) / 32 * 32, ld = P + 1;
     hipLaunchKernelGGL(k_chol_inv, dim3(b.n), dim3(512), (size_t)P * ld * sizeof(float), s, b, ld);
     return hipGetLastError();
@@ -275,6 +277,7 @@ hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s) {
 hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
+    KTimeScope kts("k_apply_linv", s);
     const int ldl = maxK | 1;
     size_t lds = (size_t)maxK * 68 * sizeof(float);
     const size_t with_l = lds + (size_t)maxK * ldl * sizeof(float);

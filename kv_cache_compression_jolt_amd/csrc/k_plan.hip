@@ -20,6 +20,7 @@
 
 #include "dev_common.h"
 #include "plan_kernels.h"
+#include "ktimer.h"
 
 namespace jolt {
 
@@ -793,6 +794,7 @@ static hipError_t xm_nf(const XmBatch &b, int d, dim3 g, int nf, int tiles, hipS
 
 hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, int maxSplit, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    KTimeScope kts("k_xm", s);
     int nf = (maxCols + 31) / 32;
     int tiles = 1;
     if (nf > 9) { tiles = (nf + 3) / 4; nf = 4; }
@@ -819,6 +821,7 @@ static hipError_t xtq_nf(const XtqBatch &b, int d, dim3 g, int nf, hipStream_t s
 
 hipError_t launch_xtq(const XtqBatch &b, int dtype, int d, int maxLH, int maxSplit, int maxCols, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    KTimeScope kts("k_xtq", s);
     const int cgroups = 4 / (d / 32);                    // waves sharing one feature fragment
     const int nf = ((maxCols + 31) / 32 + cgroups - 1) / cgroups;
     dim3 g(maxSplit, maxLH, b.n);
@@ -829,6 +832,7 @@ hipError_t launch_xtq(const XtqBatch &b, int dtype, int d, int maxLH, int maxSpl
 
 hipError_t launch_gram_rows(const GramBatch &b, int dtype, int d, int maxP, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    KTimeScope kts("k_gram_rows", s);
     dim3 g(maxP, 1, b.n);
     if (dtype == JOLT_BF16) hipLaunchKernelGGL(k_gram_rows<uint16_t>, g, dim3(256), 0, s, b, d);
     else hipLaunchKernelGGL(k_gram_rows<float>, g, dim3(256), 0, s, b, d);
@@ -837,6 +841,7 @@ hipError_t launch_gram_rows(const GramBatch &b, int dtype, int d, int maxP, hipS
 
 hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s) {
     if (b.n <= 0 || maxCount <= 0) return hipSuccess;
+    KTimeScope kts("k_reduce", s);
     dim3 g((unsigned)((maxCount + 255) / 256), b.n);
     hipLaunchKernelGGL(k_reduce, g, dim3(256), 0, s, b);
     return hipGetLastError();
@@ -872,6 +877,7 @@ hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) 
 hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s, int retry_only) {
     if (b.n <= 0) return hipSuccess;
     if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
+    KTimeScope kts("k_jacobi_lds", s);
     const int m = maxN + (maxN & 1);
     const size_t lds = (size_t)2 * m * m * sizeof(float);
     hipLaunchKernelGGL(k_jacobi_lds<1024>, dim3(b.n), dim3(1024), lds, s, b, max_sweeps, retry_only);
