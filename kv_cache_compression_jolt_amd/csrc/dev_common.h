@@ -114,6 +114,26 @@ __device__ __forceinline__ float wave_min(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------- XCD-aware block ids
+// The GPU deals workgroups round-robin over its 8 XCDs (each with its own L2).
+// xcd_block() permutes the linear workgroup id so that each XCD gets one
+// contiguous range of logical workgroups: neighbours in (x, y, z) order, which
+// share operands (the same item, the same layer-head), then hit the same L2.
+// Grids whose size is not a multiple of 8 keep the identity order.
+struct Block3 { int x, y, z; };
+__device__ __forceinline__ Block3 xcd_block() {
+    constexpr int kXcd = 8;
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int total = gx * gy * gridDim.z;
+    int w = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    if (total % kXcd == 0) w = (w % kXcd) * (total / kXcd) + w / kXcd;
+    Block3 b;
+    b.x = w % gx;
+    b.y = (w / gx) % gy;
+    b.z = w / (gx * gy);
+    return b;
+}
+
 __device__ __forceinline__ int frag_row(int lane, int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
 
 template <typename T> struct Elem;

@@ -210,12 +210,13 @@ __global__ __launch_bounds__(256) void k_encode(CodecBatch batch) {
     constexpr int NE = 32 * NMF / 2 * 2 / 2;       // values per lane: 64 (d=128) or 32 (d=64)
     static_assert(NE == 16 * NMF, "layout");
     __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * TL::RS];
-    const CodecItem &it = batch.it[blockIdx.z];
-    const int lh = blockIdx.y;
-    if (lh >= it.LH || (int)blockIdx.x * 128 >= it.T) return;
+    const Block3 blk = xcd_block();
+    const CodecItem &it = batch.it[blk.z];
+    const int lh = blk.y;
+    if (lh >= it.LH || blk.x * 128 >= it.T) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 31, h = lane >> 5;
-    const int t0 = blockIdx.x * 128 + wave * 32;
+    const int t0 = blk.x * 128 + wave * 32;
     const int tok = t0 + ln;
     const bool tv = tok < it.T;
     uint8_t *buf = lds[wave];
@@ -339,12 +340,13 @@ __global__ __launch_bounds__(256) void k_decode(CodecBatch batch) {
     constexpr int HALF = NMF / 2;
     constexpr int NE = 16 * NMF;
     __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * TL::RS];
-    const CodecItem &it = batch.it[blockIdx.z];
-    const int lh = blockIdx.y;
-    if (lh >= it.LH || (int)blockIdx.x * 128 >= it.T) return;
+    const Block3 blk = xcd_block();
+    const CodecItem &it = batch.it[blk.z];
+    const int lh = blk.y;
+    if (lh >= it.LH || blk.x * 128 >= it.T) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 31, h = lane >> 5;
-    const int t0 = blockIdx.x * 128 + wave * 32;
+    const int t0 = blk.x * 128 + wave * 32;
     const int tok = t0 + ln;
     const bool tv = tok < it.T;
     uint8_t *buf = lds[wave];
@@ -439,21 +441,41 @@ __global__ __launch_bounds__(256) void k_decode(CodecBatch batch) {
 // One wave per (32 features, 32 ranks) tile: D[m = f][n = k] with K = j.
 template <typename T>
 __global__ __launch_bounds__(64) void k_build_wt(WtBatch batch, int D) {
-    const WtItem &it = batch.it[blockIdx.z / 1];
-    const int lh = blockIdx.y;
-    const int f0 = (blockIdx.x % (D / 32)) * 32, k0 = (blockIdx.x / (D / 32)) * 32;
+    const Block3 blk = xcd_block();
+    const WtItem &it = batch.it[blk.z];
+    const int lh = blk.y;
+    const int f0 = (blk.x % (D / 32)) * 32, k0 = (blk.x / (D / 32)) * 32;
     if (lh >= it.LH || k0 >= it.rtp) return;
     const int lane = threadIdx.x, ln = lane & 31, h = lane >> 5;
     const T *uf = reinterpret_cast<const T *>(it.uf);
     const T *core = reinterpret_cast<const T *>(it.core) + (size_t)lh * it.rt * it.rf;
     f32x16 acc = f32x16{};
     const int kr = k0 + ln;
-    for (int j0 = 0; j0 < it.rf; j0 += 16) {
-        const int jj = j0 + 8 * h;
-        typename Elem<T>::Frag a = load_frag_n(uf + (size_t)(f0 + ln) * it.rf + jj, it.rf - jj);
-        typename Elem<T>::Frag b = (kr < it.rt) ? load_frag_n(core + (size_t)kr * it.rf + jj, it.rf - jj)
-                                                : zero_frag(core);
-        mfma(a, b, acc);
+    const T *ua = uf + (size_t)(f0 + ln) * it.rf;
+    const T *cb = core + (size_t)(kr < it.rt ? kr : 0) * it.rf;
+    if (it.rf % 16 == 0) {
+        // whole fragments: 16-byte loads, all of a row's fragments in flight together
+        for (int j0 = 0; j0 < it.rf; j0 += 64) {
+            typename Elem<T>::Frag a[4], b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int jj = j0 + 16 * u + 8 * h;
+                if (jj < it.rf) {
+                    a[u] = load_frag(ua + jj);
+                    b[u] = load_frag(cb + jj);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (j0 + 16 * u < it.rf) mfma(a[u], kr < it.rt ? b[u] : zero_frag(core), acc);
+        }
+    } else {
+        for (int j0 = 0; j0 < it.rf; j0 += 16) {
+            const int jj = j0 + 8 * h;
+            typename Elem<T>::Frag a = load_frag_n(ua + jj, it.rf - jj);
+            typename Elem<T>::Frag b = (kr < it.rt) ? load_frag_n(cb + jj, it.rf - jj) : zero_frag(core);
+            mfma(a, b, acc);
+        }
     }
     T *wt = reinterpret_cast<T *>(it.wt) + (size_t)lh * D * it.rtp;
     if (kr < it.rtp) {

@@ -45,11 +45,12 @@ __device__ __forceinline__ typename Elem<T>::Frag frag_select(bool keep, const t
 
 template <typename T, int NF>
 __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles) {
-    const XmItem &it = batch.it[blockIdx.z];
+    const Block3 blk = xcd_block();
+    const XmItem &it = batch.it[blk.z];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
-    const int t0 = blockIdx.x * 128 + wave * 32;
-    const int c0 = (blockIdx.y % ncol_tiles) * (32 * NF);
-    const int sp = blockIdx.y / ncol_tiles;
+    const int t0 = blk.x * 128 + wave * 32;
+    const int c0 = (blk.y % ncol_tiles) * (32 * NF);
+    const int sp = blk.y / ncol_tiles;
     if (t0 >= it.T || c0 >= it.ncols || sp >= it.nsplit) return;
     const T *x = reinterpret_cast<const T *>(it.x);
     const T *m = reinterpret_cast<const T *>(it.m);
@@ -122,8 +123,9 @@ template <typename T, int NF, bool LO>
 __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d) {
     constexpr int XP = 64 + 16 / sizeof(T);
     __shared__ __attribute__((aligned(16))) T xs[128 * XP];
-    const XtqItem &it = batch.it[blockIdx.z];
-    const int lh = blockIdx.y, sp = blockIdx.x;
+    const Block3 blk = xcd_block();
+    const XtqItem &it = batch.it[blk.z];
+    const int lh = blk.y, sp = blk.x;
     if (lh >= it.LH || sp >= it.nsplit) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
     const int nmf = d / 32;
