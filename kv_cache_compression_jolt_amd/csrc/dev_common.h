@@ -97,21 +97,62 @@ __device__ __forceinline__ void mfma(const FragF32 &a, const FragF32 &b, f32x16 
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------- wave reductions (all 64 lanes)
+// Orders one wave's LDS stores before its later LDS loads of other lanes'
+// values (no workgroup barrier: only the calling wave takes part).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- wave reductions
+// Sums within aligned lane groups of 4, 8 and 16 use DPP lane moves inside a
+// row of 16 lanes (quad permutes, then the half-row and row mirrors), which
+// cost a VALU op each instead of an LDS-crossbar round trip.  Every lane of a
+// group ends with the same value: each step adds a pair in both orders.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- 7 - i within 8
+constexpr int kDppMirror = 0x140;       // lane i <- 15 - i within 16
+
+__device__ __forceinline__ float group4_sum(float v) {
+    v += dpp_move<kDppXor1>(v);
+    return v + dpp_move<kDppXor2>(v);
+}
+__device__ __forceinline__ float group8_sum(float v) {
+    v = group4_sum(v);
+    return v + dpp_move<kDppHalfMirror>(v);
+}
+__device__ __forceinline__ float group16_sum(float v) {
+    v = group8_sum(v);
+    return v + dpp_move<kDppMirror>(v);
+}
+__device__ __forceinline__ float lane_bcast(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// whole-wave sum: row sums, then the four rows read out and added in a fixed
+// order (the result is wave-uniform)
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v = group16_sum(v);
+    return (lane_bcast(v, 0) + lane_bcast(v, 16)) + (lane_bcast(v, 32) + lane_bcast(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = fmaxf(v, dpp_move<kDppXor1>(v));
+    v = fmaxf(v, dpp_move<kDppXor2>(v));
+    v = fmaxf(v, dpp_move<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_move<kDppMirror>(v));
+    return fmaxf(fmaxf(lane_bcast(v, 0), lane_bcast(v, 16)), fmaxf(lane_bcast(v, 32), lane_bcast(v, 48)));
 }
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-    return v;
+    v = fminf(v, dpp_move<kDppXor1>(v));
+    v = fminf(v, dpp_move<kDppXor2>(v));
+    v = fminf(v, dpp_move<kDppHalfMirror>(v));
+    v = fminf(v, dpp_move<kDppMirror>(v));
+    return fminf(fminf(lane_bcast(v, 0), lane_bcast(v, 16)), fminf(lane_bcast(v, 32), lane_bcast(v, 48)));
 }
 
 // ---------------------------------------------------------------- XCD-aware block ids

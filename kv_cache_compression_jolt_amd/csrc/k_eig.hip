@@ -2,14 +2,18 @@
 // workgroup of 1024 threads per matrix, all of it resident in LDS.
 //
 //   1. Householder tridiagonalization Q^T A Q = T (Golub & Van Loan, Matrix
-//      Computations, sec. 8.3.1), with Q accumulated in the same steps;
-//   2. every eigenvalue of T by bisection on Sturm counts (sec. 8.4.1), one
-//      lane per eigenvalue, to a relative width of 2 eps;
+//      Computations, sec. 8.3.1) in panels of 32 columns: within a panel the
+//      trailing matrix is left as stored and corrected on the fly by the
+//      panel's V and W (the latrd form), then updated once on fp32 MFMA;
+//      the reflectors stay in the rows of A;
+//   2. every eigenvalue of T by multisection on Sturm counts (sec. 8.4.1),
+//      four lanes per eigenvalue, to a relative width of 2 eps;
 //   3. every eigenvector of T from a twisted factorization of T - lambda I
 //      (Dhillon & Parlett, Orthogonal eigenvectors and relative gaps, 2004):
 //      forward and backward LDL^T pivots, the twist index where |gamma| is
 //      smallest, and the two one-sided recurrences from it;
-//   4. V = Q Z on fp32 MFMA;
+//   4. V = Q Z with the reflectors applied 32 at a time in compact WY form
+//      (Schreiber & Van Loan 1989) on fp32 MFMA;
 //   5. Newton-Schulz polar steps V <- V (3 I - V^T V) / 2 (at most 3, until
 //      V^T V is within 4e-6 of I), which restore the orthogonality that vectors
 //      of close eigenvalues lose.
@@ -22,6 +26,8 @@
 // (first such row) is positive.
 #include <float.h>
 
+#include <algorithm>
+
 #include "dev_common.h"
 #include "plan_kernels.h"
 #include "ktimer.h"
@@ -32,12 +38,18 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRowBatch = 5;           // rows per wave per load batch in the rank-2 update
 
 
 // C (n x n) tile (tm, tn) of sum_k A(m, k) B(k, n) on v_mfma_f32_32x32x2f32, with
 // A(m, k) = a[k * lda_k + m * lda_m] and B(k, n) = b[k * ld + n]; out of range
 // entries read as zero.
+// p[i] where ok, else 0: the load is always issued, so i must address the
+// buffer even where ok is false; a select, not a branch, drops the value
+__device__ __forceinline__ float ld_or_zero(const float *p, int i, bool ok) {
+    const float v = p[i];
+    return ok ? v : 0.f;
+}
+
 __device__ __forceinline__ f32x16 mfma_tile(const float *a, int lda_k, int lda_m, const float *b, int ld, int n,
                                             int tm, int tn, int lane) {
     f32x16 acc;
@@ -45,12 +57,38 @@ __device__ __forceinline__ f32x16 mfma_tile(const float *a, int lda_k, int lda_m
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
     const int m = tm * 32 + (lane & 31), col = tn * 32 + (lane & 31), kh = lane >> 5;
     const bool mv = m < n, cv = col < n;
+    const int mc = min(m, n - 1), cc = min(col, n - 1);
     for (int k0 = 0; k0 < n; k0 += 2) {
-        const int kk = k0 + kh;
+        const int kk = k0 + kh, kc = min(kk, n - 1);
         const bool kv = kk < n;
-        const float av = (mv && kv) ? a[kk * lda_k + m * lda_m] : 0.f;
-        const float bv = (cv && kv) ? b[kk * ld + col] : 0.f;
+        const float av = ld_or_zero(a, kc * lda_k + mc * lda_m, mv && kv);
+        const float bv = ld_or_zero(b, kc * ld + cc, cv && kv);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Tile (tm, tn) of V + V E for symmetric E: E(k, c) is read as E[c * ld + k],
+// so both operands are rows of contiguous k; products in bf16, sums in fp32.
+__device__ __forceinline__ f32x16 ns_tile(const float *V, const float *E, int ld, int n, int tm, int tn, int lane) {
+    const int m = tm * 32 + (lane & 31), c = tn * 32 + (lane & 31), kh = 8 * (lane >> 5);
+    const int mc = min(m, n - 1), cc = min(c, n - 1);
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int row = tm * 32 + frag_row(lane, q);
+        acc[q] = ld_or_zero(V, min(row, n - 1) * ld + cc, row < n && c < n);
+    }
+    for (int k0 = 0; k0 < n; k0 += 16) {
+        uint16_t ea[8], eb[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = k0 + kh + i, kc = min(kk, n - 1);
+            ea[i] = f32_to_bf16(ld_or_zero(V, mc * ld + kc, kk < n && m < n));
+            eb[i] = f32_to_bf16(ld_or_zero(E, cc * ld + kc, kk < n && c < n));
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ea), __builtin_bit_cast(bf16x8, eb),
+                                                     acc, 0, 0, 0);
     }
     return acc;
 }
@@ -74,136 +112,209 @@ __device__ __forceinline__ void store_tiles(float *dst, const f32x16 &a0, const 
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld, int boff) {
+// Scratch tile q (q < 5, 32 x 32, row stride *ts) for the back-transform:
+// in the free lower triangle of the A buffer when it has 128 rows or more
+// (off-diagonal blocks (2,0) (3,0) (3,1) (1,0) (2,1)), else in a separate
+// region.
+__device__ __forceinline__ float *scratch_tile(float *A, int ld, float *sep, int q, int *ts) {
+    if (!sep) {
+        const int R[5] = {2, 3, 3, 1, 2}, C[5] = {0, 0, 1, 0, 1};
+        *ts = ld;
+        return A + 32 * R[q] * ld + 32 * C[q];
+    }
+    *ts = 33;
+    return sep + q * 32 * 33;
+}
+
+// Column c = lane % 32 of T for a full block of 32 reflectors, in registers:
+// solves (diag(1 / tau) + strict_upper(G)) t = e_c from the last row up and
+// stores T(i, c), i <= c, at D[c * ld + i].  On entry G(i, r), i < r, is at
+// D[r * ld + i].
+__device__ __forceinline__ void wblock_t_full(float *D, int ld, const float *tau, int c, int lane) {
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = i == c ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 31; r >= 0; --r) {
+        const float xr = tau[r] * x[r];
+        x[r] = xr;
+        const float *Gc = D + r * ld;
+#pragma unroll
+        for (int i = 0; i < r; ++i) x[i] = fmaf(-Gc[i], xr, x[i]);
+        // row r is finished here, and the next row's loads start after it: no
+        // loaded value is kept live across rows
+#pragma unroll
+        for (int g = 0; g < 32; g += 8)
+            asm volatile("" : "+v"(x[g]), "+v"(x[g + 1]), "+v"(x[g + 2]), "+v"(x[g + 3]), "+v"(x[g + 4]),
+                         "+v"(x[g + 5]), "+v"(x[g + 6]), "+v"(x[g + 7])::"memory");
+    }
+    wave_lds_sync();
+    if (lane < 32)
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if (i <= c) D[c * ld + i] = x[i];
+}
+
+__global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld, int boff, int poff, int soff) {
     extern __shared__ float sm[];
-    __shared__ float sd[kTriMaxN], se[kTriMaxN], slam[kTriMaxN];
-    __shared__ __align__(8) float sbuf[2 * kTriMaxN + 2];
+    __shared__ float sd[kTriMaxN], se[kTriMaxN], slam[kTriMaxN], stau[kTriMaxN];
+    __shared__ float sx0[kTriMaxN], sx1[kTriMaxN], sp[kTriMaxN], sy[64];
+    __shared__ float2 sde[kTriMaxN];
     __shared__ float sred[2 * kWaves];
     __shared__ int s_fail;
     const JacItem &it = batch.it[blockIdx.x];
     const int n = it.n;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    float *A = sm;          // A[r * ld + c]; later Z, then M, then the final vectors
-    float *Qt = sm + boff;  // Qt[c * ld + r] = Q[r][c]; later V = Q Z (row-major)
-    float *sp = sbuf, *su = sbuf + kTriMaxN;
+    float *A = sm;          // A[r * ld + c]; reflectors in its rows after phase 1; later M
+    float *B1 = sm + boff;  // panel vectors in phase 1; then Z, transformed in place into V
+    float *sep = soff >= 0 ? sm + soff : nullptr;
+    constexpr int PS = 33;  // row stride of the panel vectors
+    float *Vp = B1, *Wp = B1 + poff;
 
     JOLT_PROBE(0);
     if (tid == 0) s_fail = 0;
     for (int e = tid; e < n * n; e += kThreads) {
         const int r = e / n, c = e - r * n;
         A[r * ld + c] = 0.5f * (it.a[(size_t)r * it.lda + c] + it.a[(size_t)c * it.lda + r]);
-        Qt[r * ld + c] = (r == c) ? 1.f : 0.f;
     }
 
     // ---------------------------------------------------------------- 1. tridiagonalize
-    // Step j reflects x = A[j+1:, j] (read as row j, A stays exactly symmetric)
-    // onto beta e_1 with H = I - tau v v^T, v = x - beta e_1 (unnormalised),
-    // tau = 2 / v^T v.  Then p = tau A22 v, w = p - (tau p^T v / 2) v,
-    // A22 -= v w^T + w v^T and Q[:, j+1:] -= tau (Q[:, j+1:] v) v^T.
-    const int rl = lane & 15, q4 = lane >> 4;
+    // Blocked Householder reduction (Golub & Van Loan sec. 8.3.1 in the
+    // panel form of LAPACK's latrd): within a panel of up to 32 columns the
+    // trailing matrix is not updated; step j works on the current column
+    //   x = A(j:, j) - V(j:, :jj) W(j, :jj)^T - W(j:, :jj) V(j, :jj)^T,
+    // reflects x(j+1:) onto beta e_1 with H = I - tau v v^T (v unnormalised,
+    // tau = 2 / v^T v), and appends v to V and
+    //   w = p - (tau p^T v / 2) v,  p = tau (A22 - V W^T - W V^T) v
+    // to W, with p^T v = tau (v^T A22 v - 2 (W^T v) . (V^T v)).  At the end of
+    // the panel A22 -= V W^T + W V^T on MFMA.  Reflector j is kept in row j.
     JOLT_PROBE(1);
-    for (int j = 0; j + 2 < n; ++j) {
+    float *sxa = sx0, *sxb = sx1;
+    for (int p0 = 0; p0 + 2 < n; p0 += 32) {
+        const int nb = min(32, n - 2 - p0);
         __syncthreads();
-        const int s = n - j - 1;
-        const float *rowj = A + j * ld + j + 1;
-        float part = 0.f;
-        for (int c = 1 + lane; c < s; c += 64) {
-            const float x = rowj[c];
-            part += x * x;
-        }
-        const float xn2 = wave_sum(part);     // identical in every wave
-        const float x0 = rowj[0];
-        float beta = x0, v0 = 0.f, tau = 0.f;
-        if (xn2 > 0.f) {
-            const float alpha = sqrtf(x0 * x0 + xn2);
-            beta = x0 >= 0.f ? -alpha : alpha;
-            v0 = x0 - beta;
-            tau = 2.f / (v0 * v0 + xn2);
-        }
-        if (tid == 0) {
-            sd[j] = A[j * ld + j];
-            se[j] = beta;
-        }
-        if (tau == 0.f) continue;             // x already a multiple of e_1
-
-        // p (rows of A22, read as columns by symmetry) and u = Q[:, j+1:] v:
-        // 16 rows per wave pass, 4 lanes per row splitting the sum
-        const int ngp = (s + 15) >> 4, ngu = (n + 15) >> 4;
-        for (int g = wid; g < ngp + ngu; g += kWaves) {
-            const bool isp = g < ngp;
-            const int r = (isp ? g : g - ngp) * 16 + rl;
-            const int rows = isp ? s : n;
-            float acc = 0.f;
-            if (r < rows) {
-                const float *col = isp ? (A + (j + 1) * ld + j + 1 + r) : (Qt + (j + 1) * ld + r);
-                // 8 independent products in flight per lane
-                float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                int c = q4;
-                for (; c + 28 < s; c += 32) {
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int cc = c + 4 * u;
-                        a8[u] = fmaf(col[cc * ld], cc == 0 ? v0 : rowj[cc], a8[u]);
+        for (int r = p0 + tid; r < n; r += kThreads) sxa[r] = A[p0 * ld + r];
+        __syncthreads();
+        for (int jj = 0; jj < nb; ++jj) {
+            const int j = p0 + jj, s = n - j - 1;
+            float part = 0.f;
+            for (int c = 1 + lane; c < s; c += 64) {
+                const float x = sxa[j + 1 + c];
+                part += x * x;
+            }
+            const float xn2 = wave_sum(part);     // identical in every wave
+            const float x0 = sxa[j + 1];
+            float beta = x0, v0 = 0.f, tau = 0.f;
+            if (xn2 > 0.f) {
+                const float alpha = sqrtf(x0 * x0 + xn2);
+                beta = x0 >= 0.f ? -alpha : alpha;
+                v0 = x0 - beta;
+                tau = 2.f / (v0 * v0 + xn2);
+            }
+            if (tid == 0) {
+                sd[j] = sxa[j];
+                se[j] = beta;
+                stau[j] = tau;
+            }
+            for (int c = tid; c < s; c += kThreads) {
+                const float vc = c == 0 ? v0 : sxa[j + 1 + c];
+                Vp[(j + 1 + c) * PS + jj] = vc;
+                A[j * ld + j + 1 + c] = vc;
+            }
+            // sp = A22 v (A22 as stored: the panel's updates are not applied yet),
+            // 8 lanes per row, rows of A22 read as its columns
+            for (int c = tid >> 3; c < s; c += kThreads / 8) {
+                const int l8 = tid & 7;
+                const float *col = A + (j + 1) * ld + j + 1 + c;
+                float a0 = 0.f, a1 = 0.f;
+                int cc = l8;
+                for (; cc + 8 < s; cc += 16) {
+                    a0 = fmaf(col[cc * ld], cc == 0 ? v0 : sxa[j + 1 + cc], a0);
+                    a1 = fmaf(col[(cc + 8) * ld], sxa[j + 9 + cc], a1);
+                }
+                if (cc < s) a0 = fmaf(col[cc * ld], cc == 0 ? v0 : sxa[j + 1 + cc], a0);
+                const float acc = group8_sum(a0 + a1);
+                if (l8 == 0) sp[c] = acc;
+            }
+            // sy[m] = (W^T v)_m, sy[32 + m] = (V^T v)_m: 16 lanes per output
+            {
+                const int o = tid >> 4, m = o & 31, l16 = tid & 15;
+                const float *vec = o < 32 ? Wp : Vp;
+                float acc = 0.f;
+                if (m < jj)
+                    for (int c = l16; c < s; c += 16)
+                        acc = fmaf(vec[(j + 1 + c) * PS + m], c == 0 ? v0 : sxa[j + 1 + c], acc);
+                acc = group16_sum(acc);
+                if (l16 == 0) sy[o] = acc;
+            }
+            __syncthreads();
+            // p = tau (A22 v - V W^T v - W V^T v), w = p - hk v, and the next column
+            // x = A(:, j+1) - V W(j+1, :)^T - W V(j+1, :)^T; 4 lanes per row share
+            // the sums over the panel's previous columns m (m = l4 mod 4)
+            float kp = 0.f;
+            for (int c = lane; c < s; c += 64) kp = fmaf(sp[c], c == 0 ? v0 : sxa[j + 1 + c], kp);
+            kp = wave_sum(kp);
+            const bool next = jj + 1 < nb;
+            {
+                const int l4 = tid & 3, c = tid >> 2, r = j + 1 + c;
+                const bool live = c < s;
+                float cw = 0.f, cx = 0.f, cw1 = 0.f, yy = 0.f;
+                for (int m = l4; m < jj; m += 4) {
+                    const float y1 = sy[m], y2 = sy[32 + m];
+                    const float bv = Vp[(j + 1) * PS + m], bw = Wp[(j + 1) * PS + m];
+                    yy = fmaf(y1, y2, yy);
+                    cw1 = fmaf(bv, y1, fmaf(bw, y2, cw1));
+                    if (live) {
+                        const float rv = Vp[r * PS + m], rw = Wp[r * PS + m];
+                        cw = fmaf(rv, y1, fmaf(rw, y2, cw));
+                        cx = fmaf(rv, bw, fmaf(rw, bv, cx));
                     }
                 }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int cc = c + 4 * u;
-                    if (cc < s) a8[u] = fmaf(col[cc * ld], cc == 0 ? v0 : rowj[cc], a8[u]);
+                cw = group4_sum(cw);
+                cx = group4_sum(cx);
+                cw1 = group4_sum(cw1);
+                yy = group4_sum(yy);
+                const float hk = 0.5f * tau * (tau * (kp - 2.f * yy));
+                if (live && l4 == 0) {
+                    const float vc = c == 0 ? v0 : sxa[r];
+                    const float w = tau * (sp[c] - cw) - hk * vc;
+                    Wp[r * PS + jj] = w;
+                    if (next) {
+                        const float w0 = tau * (sp[0] - cw1) - hk * v0;
+                        sxb[r] = A[(j + 1) * ld + r] - cx - fmaf(vc, w0, w * v0);
+                    }
                 }
-                acc = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
             }
-            acc += __shfl_xor(acc, 16);
-            acc += __shfl_xor(acc, 32);
-            if (q4 == 0 && r < rows) {
-                if (isp) sp[r] = tau * acc;
-                else su[r] = acc;
-            }
+            float *t = sxa;
+            sxa = sxb;
+            sxb = t;
+            __syncthreads();
         }
-        __syncthreads();
-
-        float kp = 0.f;
-        for (int c = lane; c < s; c += 64) kp = fmaf(sp[c], c == 0 ? v0 : rowj[c], kp);
-        const float hk = 0.5f * tau * wave_sum(kp);
-        float vr[3], wr[3], ur[3];
+        // trailing update A22 -= V W^T + W V^T (rows, columns >= q0), K = 2 nb
+        const int q0 = p0 + nb;
+        const int tt = (n - q0 + 31) >> 5, ntl = tt * tt;
+        for (int t = wid; t < ntl; t += kWaves) {
+            const int R0 = q0 + 32 * (t / tt), C0 = q0 + 32 * (t % tt);
+            const int rr = R0 + (lane & 31), cc = C0 + (lane & 31), kh = lane >> 5;
+            const int rc = min(rr, n - 1), ccl = min(cc, n - 1);
+            f32x16 acc;
 #pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            const int r = lane + 64 * t;
-            vr[t] = r < s ? (r == 0 ? v0 : rowj[r]) : 0.f;
-            wr[t] = r < s ? sp[r] - hk * vr[t] : 0.f;
-            ur[t] = r < n ? su[r] : 0.f;
-        }
-        // rows c = wid + 16 g of A22 and of Q^T: all loads of a batch of rows
-        // first, then the updates (one LDS round trip per batch)
-        for (int c0 = wid; c0 < s; c0 += kWaves * kRowBatch) {
-            float av[kRowBatch][3], qv[kRowBatch][3], vcs[kRowBatch], wcs[kRowBatch];
-#pragma unroll
-            for (int g = 0; g < kRowBatch; ++g) {
-                const int c = c0 + kWaves * g;
-                const bool ok = c < s;
-                const float vc = ok ? (c == 0 ? v0 : rowj[c]) : 0.f;
-                vcs[g] = vc;
-                wcs[g] = ok ? sp[c] - hk * vc : 0.f;
-#pragma unroll
-                for (int t = 0; t < 3; ++t) {
-                    const int r = lane + 64 * t;
-                    av[g][t] = (ok && r < s) ? A[(j + 1 + c) * ld + j + 1 + r] : 0.f;
-                    qv[g][t] = (ok && r < n) ? Qt[(j + 1 + c) * ld + r] : 0.f;
-                }
+            for (int q = 0; q < 16; ++q) {
+                const int row = R0 + frag_row(lane, q);
+                acc[q] = ld_or_zero(A, min(row, n - 1) * ld + ccl, row < n && cc < n);
+            }
+            for (int k0 = 0; k0 < 2 * nb; k0 += 2) {
+                const int k = k0 + kh;
+                const bool first = k < nb;
+                const int m = first ? k : k - nb;
+                const float a = -ld_or_zero(first ? Vp : Wp, rc * PS + m, rr < n);
+                const float b = ld_or_zero(first ? Wp : Vp, ccl * PS + m, cc < n);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
             }
 #pragma unroll
-            for (int g = 0; g < kRowBatch; ++g) {
-                const int c = c0 + kWaves * g;
-                if (c >= s) continue;
-                const float vc = vcs[g], wc = wcs[g], tv = tau * vc;
-                // (v_c w_r) + (w_c v_r): the same two products and one sum as the
-                // mirrored entry, so A keeps exact symmetry (no contraction)
-#pragma unroll
-                for (int t = 0; t < 3; ++t) {
-                    const int r = lane + 64 * t;
-                    if (r < s) A[(j + 1 + c) * ld + j + 1 + r] = av[g][t] - (vc * wr[t] + wc * vr[t]);
-                    if (r < n) Qt[(j + 1 + c) * ld + r] = fmaf(-tv, ur[t], qv[g][t]);
-                }
+            for (int q = 0; q < 16; ++q) {
+                const int row = R0 + frag_row(lane, q);
+                if (row < n && cc < n) A[row * ld + cc] = acc[q];
             }
         }
     }
@@ -234,32 +345,48 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     // relative width 2 eps |lambda|, floored at eps ||T|| / 1024 (vectors of
     // close eigenvalues stay near orthogonal only with accurate shifts)
     const float floor_tol = eps * tnorm * (1.f / 1024.f);
-    float2 *sde = reinterpret_cast<float2 *>(sbuf);    // {d_i, e_{i-1}^2}
+    // sde[i] = {d_i, e_{i-1}^2}
     for (int i = tid; i < n; i += kThreads) sde[i] = make_float2(sd[i], i > 0 ? se[i - 1] * se[i - 1] : 0.f);
     __syncthreads();
-    if (tid < n) {
-        // the tid-th smallest eigenvalue: count(x) = #{i : q_i(x) < 0}
-        float a = lo, b = hi;
-        for (int iter = 0; iter < 64 && b - a > 2.f * eps * fmaxf(fabsf(a), fabsf(b)) + floor_tol; ++iter) {
-            const float x = 0.5f * (a + b);
-            int cnt = 0;
-            float qv = 1.f;
-            for (int i = 0; i < n; ++i) {
-                const float2 de = sde[i];
-                qv = (de.x - x) - de.y * __builtin_amdgcn_rcpf(qv);
-                if (fabsf(qv) < pivmin) qv = -pivmin;
-                cnt += qv < 0.f;
+    // multisection: the 4 lanes of quad k hold the k-th smallest eigenvalue's
+    // interval [a, b) (count(a) <= k < count(b), count(x) = #{i : q_i(x) < 0})
+    // and each round count it at the 4 points a + (b - a) (q + 1) / 5; the
+    // interval shrinks to the fifth that starts below the first point whose
+    // count exceeds k.  All four lanes compute the same points from the same
+    // a and b, so they stay in step.
+    {
+        const int k = tid >> 2, q = tid & 3;
+        if (k < n) {
+            float a = lo, b = hi;
+            for (int round = 0; round < 28 && b - a > 2.f * eps * fmaxf(fabsf(a), fabsf(b)) + floor_tol; ++round) {
+                const float w = (b - a) * 0.2f;
+                const float x = a + w * (float)(q + 1);
+                int cnt = 0;
+                float qv = 1.f;
+                for (int i = 0; i < n; ++i) {
+                    const float2 de = sde[i];
+                    qv = (de.x - x) - de.y * __builtin_amdgcn_rcpf(qv);
+                    if (fabsf(qv) < pivmin) qv = -pivmin;
+                    cnt += qv < 0.f;
+                }
+                // first point of the quad past the k-th eigenvalue (4 if none)
+                float first = cnt > k ? (float)q : 4.f;
+                first = fminf(first, dpp_move<kDppXor1>(first));
+                first = fminf(first, dpp_move<kDppXor2>(first));
+                const int m = (int)first;
+                const float na = m > 0 ? a + w * (float)m : a;
+                const float nb = m < 4 ? a + w * (float)(m + 1) : b;
+                a = na;
+                b = nb;
             }
-            if (cnt > tid) b = x;
-            else a = x;
+            if (q == 0) slam[k] = 0.5f * (a + b);
         }
-        slam[tid] = 0.5f * (a + b);
     }
     __syncthreads();
 
     // ---------------------------------------------------------------- 3. vectors of T
     JOLT_PROBE(3);
-    float *Z = A;      // Z[i * ld + k]: column k belongs to the k-th smallest eigenvalue
+    float *Z = B1;     // Z[i * ld + k]: column k belongs to the k-th smallest eigenvalue
     if (tid < n) {
         const int k = tid;
         const float lam = slam[k];
@@ -267,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
         if (fabsf(dp) < pivmin) dp = -pivmin;
         Z[k] = dp;
         for (int i = 1; i < n; ++i) {
-            dp = (sd[i] - lam) - sde[i].y / dp;
+            dp = (sd[i] - lam) - sde[i].y * __builtin_amdgcn_rcpf(dp);
             if (fabsf(dp) < pivmin) dp = -pivmin;
             Z[i * ld + k] = dp;
         }
@@ -276,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
         float best = fabsf(Z[(n - 1) * ld + k]);
         int r = n - 1;
         for (int i = n - 2; i >= 0; --i) {
-            dm = (sd[i] - lam) - sde[i + 1].y / dm;
+            dm = (sd[i] - lam) - sde[i + 1].y * __builtin_amdgcn_rcpf(dm);
             if (fabsf(dm) < pivmin) dm = -pivmin;
             const float g = fabsf(Z[i * ld + k] + dm - (sd[i] - lam));
             if (g <= best) {
@@ -287,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
         // z_r = 1; z_i = -(e_i / D+_i) z_{i+1} above r; z_{i+1} = -(e_i / D-_{i+1}) z_i below
         float nrm = 1.f, z = 1.f;
         for (int i = r - 1; i >= 0; --i) {
-            z = -(se[i] / Z[i * ld + k]) * z;
+            z = -(se[i] * __builtin_amdgcn_rcpf(Z[i * ld + k])) * z;
             Z[i * ld + k] = z;
             nrm += z * z;
         }
@@ -295,14 +422,14 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
         if (fabsf(dm) < pivmin) dm = -pivmin;
         if (r < n - 1) Z[(n - 1) * ld + k] = dm;
         for (int i = n - 2; i > r; --i) {
-            dm = (sd[i] - lam) - sde[i + 1].y / dm;
+            dm = (sd[i] - lam) - sde[i + 1].y * __builtin_amdgcn_rcpf(dm);
             if (fabsf(dm) < pivmin) dm = -pivmin;
             Z[i * ld + k] = dm;
         }
         Z[r * ld + k] = 1.f;
         z = 1.f;
         for (int i = r; i + 1 < n; ++i) {
-            z = -(se[i] / Z[(i + 1) * ld + k]) * z;
+            z = -(se[i] * __builtin_amdgcn_rcpf(Z[(i + 1) * ld + k])) * z;
             Z[(i + 1) * ld + k] = z;
             nrm += z * z;
         }
@@ -318,28 +445,140 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     }
 
     // ---------------------------------------------------------------- 4. V = Q Z
+    // Q = H_0 H_1 ... H_{n-3} is applied to Z a block of 32 reflectors at a time,
+    // last block first, in compact WY form: H_b0 ... H_b0+31 = I - Y T Y^T with
+    // T upper triangular and T^-1 = diag(1 / tau) + strict_upper(Y^T Y)
+    // (Schreiber & Van Loan's storage-efficient WY; the inverse form follows
+    // from the column recurrence of T), and Z <- Z - Y (T (Y^T Z)).
     JOLT_PROBE(4);
     const int nt = (n + 31) >> 5, ntiles = nt * nt;
-    float *V = Qt;     // V[r * ld + c], kept in the Q buffer from here on
+    float *V = B1;     // V[r * ld + c]
     {
-        f32x16 acc0 = {}, acc1 = {};
-        if (wid < ntiles) acc0 = mfma_tile(Qt, ld, 1, Z, ld, n, wid / nt, wid % nt, lane);
-        if (wid + kWaves < ntiles) acc1 = mfma_tile(Qt, ld, 1, Z, ld, n, (wid + kWaves) / nt, (wid + kWaves) % nt, lane);
+        const int mref = n > 2 ? n - 2 : 0, nblk = (mref + 31) >> 5;
+        const int m32 = lane & 31, kh = lane >> 5;
+        // Y(r, i) = v_{b0+i}(r): reflector b0 + i, nonzero for r > b0 + i
+        auto Y = [&](int b0, int nbk, int r, int i) {
+            return ld_or_zero(A, (b0 + min(i, nbk - 1)) * ld + min(r, n - 1), i < nbk && r > b0 + i && r < n);
+        };
+        // T_b for every block, one wave each.  G = Y^T Y goes first to the free
+        // strict lower triangle of diagonal block b (G(i, c), i < c, at
+        // A[(b0 + c) * ld + b0 + i]; the reflectors sit above the diagonal); lane c
+        // then solves (diag(1 / tau) + strict_upper(G)) t = e_c by substitution
+        // from the last row up (no division: t_r = tau_r x_r) and stores column c
+        // of T, T(i, c) for i <= c, over G's column at the same places.  Rows and
+        // columns past the block's nbk reflectors are never read.
+        for (int b = wid; b < nblk; b += kWaves) {
+            const int b0 = 32 * b, nbk = min(32, mref - b0);
+            f32x16 g = {};
+            for (int k0 = b0; k0 < n; k0 += 2) {
+                const float y = Y(b0, nbk, k0 + kh, m32);
+                g = __builtin_amdgcn_mfma_f32_32x32x2f32(y, y, g, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int r = frag_row(lane, q);
+                if (r < m32 && m32 < nbk) A[(b0 + m32) * ld + b0 + r] = g[q];
+            }
+            wave_lds_sync();
+            if (nbk == 32) {
+                wblock_t_full(A + b0 * ld + b0, ld, stau + b0, m32, lane);
+            } else {
+                // the last, partial block: the solve runs in scratch tile b,
+                // X(i, c) at tX[i * tsx + c]
+                int tsx = 0;
+                float *tX = scratch_tile(A, ld, sep, b, &tsx);
+                if (lane < 32)
+                    for (int i = 0; i < nbk; ++i) tX[i * tsx + m32] = i == m32 ? 1.f : 0.f;
+                wave_lds_sync();
+                for (int r = nbk - 1; r >= 0; --r) {
+                    const float xr = stau[b0 + r] * tX[r * tsx + m32];
+                    const float *Gc = A + (b0 + r) * ld + b0;
+                    if (lane < 32) {
+                        tX[r * tsx + m32] = xr;
+                        for (int i = 0; i < r; ++i) tX[i * tsx + m32] = fmaf(-Gc[i], xr, tX[i * tsx + m32]);
+                    }
+                    wave_lds_sync();
+                }
+                if (lane < 32 && m32 < nbk)
+                    for (int i = 0; i <= m32; ++i) A[(b0 + m32) * ld + b0 + i] = tX[i * tsx + m32];
+            }
+        }
         __syncthreads();
-        store_tiles(V, acc0, acc1, ld, n, nt, ntiles, wid, lane);
+        for (int b = nblk - 1; b >= 0; --b) {
+            const int b0 = 32 * b, nbk = min(32, mref - b0);
+            if (wid < nt) {
+                // M = T (Y^T Z) for column chunk wid
+                int tsm = 0;
+                float *tM = scratch_tile(A, ld, sep, wid, &tsm);
+                const int col = 32 * wid + m32, colc = min(col, n - 1);
+                f32x16 acc = {};
+                for (int k0 = b0; k0 < n; k0 += 2) {
+                    const int k = k0 + kh;
+                    const float bz = ld_or_zero(Z, min(k, n - 1) * ld + colc, k < n && col < n);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Y(b0, nbk, k, m32), bz, acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q) tM[frag_row(lane, q) * tsm + m32] = acc[q];
+                wave_lds_sync();
+                f32x16 acc2 = {};
+#pragma unroll
+                for (int k0 = 0; k0 < 32; k0 += 2) {
+                    const int k = k0 + kh;
+                    // T(m32, k) at A[(b0 + k) * ld + b0 + m32], k >= m32
+                    const float t = ld_or_zero(A, (b0 + min(k, nbk - 1)) * ld + b0 + m32, k >= m32 && k < nbk);
+                    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(t, tM[k * tsm + m32], acc2, 0, 0, 0);
+                }
+                wave_lds_sync();
+#pragma unroll
+                for (int q = 0; q < 16; ++q) tM[frag_row(lane, q) * tsm + m32] = acc2[q];
+            }
+            __syncthreads();
+            // Z -= Y M on the row blocks that Y touches (rows > b0)
+            const int nrt = nt - b;
+            for (int t = wid; t < nrt * nt; t += kWaves) {
+                const int rt = b + t / nt, c = t % nt;
+                int tsm = 0;
+                const float *tM = scratch_tile(A, ld, sep, c, &tsm);
+                const int col = 32 * c + m32, colc = min(col, n - 1);
+                f32x16 acc;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int row = 32 * rt + frag_row(lane, q);
+                    acc[q] = ld_or_zero(Z, min(row, n - 1) * ld + colc, row < n && col < n);
+                }
+#pragma unroll
+                for (int k0 = 0; k0 < 32; k0 += 2) {
+                    const int k = k0 + kh;
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(-Y(b0, nbk, 32 * rt + m32, k), tM[k * tsm + m32], acc,
+                                                               0, 0, 0);
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int row = 32 * rt + frag_row(lane, q);
+                    if (row < n && col < n) Z[row * ld + col] = acc[q];
+                }
+            }
+            __syncthreads();
+        }
     }
-    __syncthreads();
 
     // ---------------------------------------------------------------- 5. Newton-Schulz steps
+    // V <- V (3 I - V^T V) / 2 = V + V E with E = (I - V^T V) / 2.  V^T V is
+    // symmetric: its upper tiles are formed (fp32 MFMA) and E goes to both
+    // triangles of the A buffer.  V E is a small correction, formed with bf16
+    // products (relative error ~2^-9 of a term of size |E|); V's span is kept
+    // exactly, whatever E's precision.
     JOLT_PROBE(5);
-    // G = V^T V and M = (3 I - G) / 2 (M in the Z buffer); V <- V M
+    const int ntri = nt * (nt + 1) / 2;     // <= kWaves for n <= 160
     for (int step = 0;; ++step) {
         float dev = 0.f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = wid + u * kWaves;
-            if (t >= ntiles) continue;
-            const int tm = t / nt, tn = t % nt, col = tn * 32 + (lane & 31);
+        if (wid < ntri) {
+            int t = wid, tm = 0;
+            while (t >= nt - tm) {
+                t -= nt - tm;
+                ++tm;
+            }
+            const int tn = tm + t, col = tn * 32 + (lane & 31);
             const f32x16 g = mfma_tile(V, ld, 1, V, ld, n, tm, tn, lane);
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
@@ -349,7 +588,9 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
                     const float gv = g[jj];
                     dev = fmaxf(dev, fabsf(gv - id));
                     if (!(gv == gv)) dev = FLT_MAX;
-                    A[row * ld + col] = 1.5f * id - 0.5f * gv;
+                    const float e = 0.5f * (id - gv);
+                    A[row * ld + col] = e;
+                    A[col * ld + row] = e;
                 }
             }
         }
@@ -367,10 +608,9 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
             }
             break;
         }
-        // V M: A(m, k) = V[m][k], read down the rows of V
         f32x16 acc0 = {}, acc1 = {};
-        if (wid < ntiles) acc0 = mfma_tile(V, 1, ld, A, ld, n, wid / nt, wid % nt, lane);
-        if (wid + kWaves < ntiles) acc1 = mfma_tile(V, 1, ld, A, ld, n, (wid + kWaves) / nt, (wid + kWaves) % nt, lane);
+        if (wid < ntiles) acc0 = ns_tile(V, A, ld, n, wid / nt, wid % nt, lane);
+        if (wid + kWaves < ntiles) acc1 = ns_tile(V, A, ld, n, (wid + kWaves) / nt, (wid + kWaves) % nt, lane);
         __syncthreads();
         store_tiles(V, acc0, acc1, ld, n, nt, ntiles, wid, lane);
         __syncthreads();
@@ -411,9 +651,18 @@ static hipError_t allow_lds_tri() {
     return state;
 }
 
-size_t eig_tridiag_lds_bytes(int maxN) {
-    const int ld = maxN | 1;
-    return (size_t)2 * maxN * ld * sizeof(float);
+// dynamic LDS layout for a batch of order <= maxN (floats):
+// [A: maxN x ld | B1: max(maxN x ld, 2 maxN x 33) | scratch tiles (maxN < 128 only)]
+struct TriLayout { int ld, boff, poff, soff; size_t bytes; };
+static TriLayout tri_layout(int maxN) {
+    TriLayout L;
+    L.ld = maxN | 1;
+    L.boff = maxN * L.ld;
+    L.poff = maxN * 33;
+    const int b1 = std::max(maxN * L.ld, 2 * maxN * 33);
+    L.soff = maxN >= 128 ? -1 : L.boff + b1;
+    L.bytes = (size_t)(L.boff + b1 + (L.soff >= 0 ? 5 * 32 * 33 : 0)) * sizeof(float);
+    return L;
 }
 
 hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
@@ -423,8 +672,8 @@ hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
         if (!b.it[i].sweeps_out || b.it[i].n > maxN) return hipErrorInvalidValue;
     if (hipError_t e = allow_lds_tri(); e != hipSuccess) return e;
     KTimeScope kts("k_eig_tridiag", s);
-    const int ld = maxN | 1;
-    hipLaunchKernelGGL(k_eig_tridiag, dim3(b.n), dim3(kThreads), eig_tridiag_lds_bytes(maxN), s, b, ld, maxN * ld);
+    const TriLayout L = tri_layout(maxN);
+    hipLaunchKernelGGL(k_eig_tridiag, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff, L.poff, L.soff);
     return hipGetLastError();
 }
 
