@@ -118,6 +118,7 @@ constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;   // lane i <- 7 - i within 8
 constexpr int kDppMirror = 0x140;       // lane i <- 15 - i within 16
+constexpr int kDppRowBcast15 = 0x142;   // rows 1 and 3 <- lane 15 of the row below
 
 __device__ __forceinline__ float group4_sum(float v) {
     v += dpp_move<kDppXor1>(v);

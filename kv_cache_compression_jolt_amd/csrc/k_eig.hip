@@ -38,6 +38,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+// row stride of the panel's V and W: with an even stride every per-step
+// access pattern over them meets each LDS bank at most twice per wave
+constexpr int kPanelStride = 34;
 
 
 // C (n x n) tile (tm, tn) of sum_k A(m, k) B(k, n) on v_mfma_f32_32x32x2f32, with
@@ -68,27 +71,16 @@ __device__ __forceinline__ f32x16 mfma_tile(const float *a, int lda_k, int lda_m
     return acc;
 }
 
-// Tile (tm, tn) of V + V E for symmetric E: E(k, c) is read as E[c * ld + k],
-// so both operands are rows of contiguous k; products in bf16, sums in fp32.
+// Tile (tm, tn) of V + V E on fp32 MFMA.  Both factors stay in fp32: a
+// rounded V would put error vectors outside V's span into every column, and
+// the next polar step would spread them into the accurate columns.
 __device__ __forceinline__ f32x16 ns_tile(const float *V, const float *E, int ld, int n, int tm, int tn, int lane) {
-    const int m = tm * 32 + (lane & 31), c = tn * 32 + (lane & 31), kh = 8 * (lane >> 5);
-    const int mc = min(m, n - 1), cc = min(c, n - 1);
-    f32x16 acc;
+    f32x16 acc = mfma_tile(V, 1, ld, E, ld, n, tm, tn, lane);
+    const int c = tn * 32 + (lane & 31), cc = min(c, n - 1);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int row = tm * 32 + frag_row(lane, q);
-        acc[q] = ld_or_zero(V, min(row, n - 1) * ld + cc, row < n && c < n);
-    }
-    for (int k0 = 0; k0 < n; k0 += 16) {
-        uint16_t ea[8], eb[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kk = k0 + kh + i, kc = min(kk, n - 1);
-            ea[i] = f32_to_bf16(ld_or_zero(V, mc * ld + kc, kk < n && m < n));
-            eb[i] = f32_to_bf16(ld_or_zero(E, cc * ld + kc, kk < n && c < n));
-        }
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ea), __builtin_bit_cast(bf16x8, eb),
-                                                     acc, 0, 0, 0);
+        acc[q] += ld_or_zero(V, min(row, n - 1) * ld + cc, row < n && c < n);
     }
     return acc;
 }
@@ -168,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     float *A = sm;          // A[r * ld + c]; reflectors in its rows after phase 1; later M
     float *B1 = sm + boff;  // panel vectors in phase 1; then Z, transformed in place into V
     float *sep = soff >= 0 ? sm + soff : nullptr;
-    constexpr int PS = 33;  // row stride of the panel vectors
+    constexpr int PS = kPanelStride;
     float *Vp = B1, *Wp = B1 + poff;
 
     JOLT_PROBE(0);
@@ -190,17 +182,37 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     // the panel A22 -= V W^T + W V^T on MFMA.  Reflector j is kept in row j.
     JOLT_PROBE(1);
     float *sxa = sx0, *sxb = sx1;
+    // Within a panel A22 is read-only, so each lane keeps its share in
+    // registers for the panel's steps: lane l32 of half h of wave w holds
+    // A(R_p, C_u), R_p = 2 w + h + 32 p, C_u = l32 + 32 u (p, u < 5).
+    const int l32 = lane & 31, half = lane >> 5, hw = 2 * wid + half;
     for (int p0 = 0; p0 + 2 < n; p0 += 32) {
         const int nb = min(32, n - 2 - p0);
         __syncthreads();
         for (int r = p0 + tid; r < n; r += kThreads) sxa[r] = A[p0 * ld + r];
+        float areg[5][5];
+#pragma unroll
+        for (int pp = 0; pp < 5; ++pp)
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                const int R = hw + 32 * pp, C = l32 + 32 * u;
+                areg[pp][u] = ld_or_zero(A, min(R, n - 1) * ld + min(C, n - 1), R < n && C < n);
+            }
+        for (int e = tid; e < (n - p0) * 32; e += kThreads) {
+            const int r = p0 + (e >> 5), m = e & 31;
+            Vp[r * PS + m] = 0.f;
+            Wp[r * PS + m] = 0.f;
+        }
+        if (tid < 64) sy[tid] = 0.f;
         __syncthreads();
         for (int jj = 0; jj < nb; ++jj) {
             const int j = p0 + jj, s = n - j - 1;
             float part = 0.f;
-            for (int c = 1 + lane; c < s; c += 64) {
-                const float x = sxa[j + 1 + c];
-                part += x * x;
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int c = 1 + lane + 64 * t;
+                const float x = ld_or_zero(sxa, j + 1 + min(c, s - 1), c < s);
+                part = fmaf(x, x, part);
             }
             const float xn2 = wave_sum(part);     // identical in every wave
             const float x0 = sxa[j + 1];
@@ -209,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
                 const float alpha = sqrtf(x0 * x0 + xn2);
                 beta = x0 >= 0.f ? -alpha : alpha;
                 v0 = x0 - beta;
-                tau = 2.f / (v0 * v0 + xn2);
+                tau = 2.f * __builtin_amdgcn_rcpf(v0 * v0 + xn2);
             }
             if (tid == 0) {
                 sd[j] = sxa[j];
@@ -221,54 +233,88 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
                 Vp[(j + 1 + c) * PS + jj] = vc;
                 A[j * ld + j + 1 + c] = vc;
             }
-            // sp = A22 v (A22 as stored: the panel's updates are not applied yet),
-            // 8 lanes per row, rows of A22 read as its columns
-            for (int c = tid >> 3; c < s; c += kThreads / 8) {
-                const int l8 = tid & 7;
-                const float *col = A + (j + 1) * ld + j + 1 + c;
-                float a0 = 0.f, a1 = 0.f;
-                int cc = l8;
-                for (; cc + 8 < s; cc += 16) {
-                    a0 = fmaf(col[cc * ld], cc == 0 ? v0 : sxa[j + 1 + cc], a0);
-                    a1 = fmaf(col[(cc + 8) * ld], sxa[j + 9 + cc], a1);
-                }
-                if (cc < s) a0 = fmaf(col[cc * ld], cc == 0 ? v0 : sxa[j + 1 + cc], a0);
-                const float acc = group8_sum(a0 + a1);
-                if (l8 == 0) sp[c] = acc;
+            // v in registers at the lanes' columns (zero outside j+1..n-1)
+            float vr[5];
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                const int C = l32 + 32 * u;
+                vr[u] = C == j + 1 ? v0 : ld_or_zero(sxa, min(C, n - 1), C > j + 1 && C < n);
             }
-            // sy[m] = (W^T v)_m, sy[32 + m] = (V^T v)_m: 16 lanes per output
+            // sp = A22 v from the register copy (the panel's updates are not
+            // applied to A22 yet): 5 products per row, then the sum over the
+            // 32 lanes of the half (rows of 16 by DPP, then the lower row's
+            // total from its lane 15 into the upper row)
             {
-                const int o = tid >> 4, m = o & 31, l16 = tid & 15;
-                const float *vec = o < 32 ? Wp : Vp;
-                float acc = 0.f;
-                if (m < jj)
-                    for (int c = l16; c < s; c += 16)
-                        acc = fmaf(vec[(j + 1 + c) * PS + m], c == 0 ? v0 : sxa[j + 1 + c], acc);
-                acc = group16_sum(acc);
-                if (l16 == 0) sy[o] = acc;
+                float acc[5];
+#pragma unroll
+                for (int pp = 0; pp < 5; ++pp) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 5; ++u) t = fmaf(areg[pp][u], vr[u], t);
+                    acc[pp] = t;
+                }
+#pragma unroll
+                for (int pp = 0; pp < 5; ++pp) {
+                    acc[pp] = group16_sum(acc[pp]);
+                    acc[pp] += dpp_move<kDppRowBcast15>(acc[pp]);
+                }
+                if (l32 == 16)
+#pragma unroll
+                    for (int pp = 0; pp < 5; ++pp) {
+                        const int R = hw + 32 * pp;
+                        if (R > j && R < n) sp[R - j - 1] = acc[pp];
+                    }
+            }
+            // sy[m] = (W^T v)_m, sy[32 + m] = (V^T v)_m: half-wave hw takes
+            // outputs hw and hw + 32 of the 2 jj, over the same lane columns
+#pragma unroll
+            for (int oo = 0; oo < 2; ++oo) {
+                const int o = hw + 32 * oo;
+                if (o < 2 * jj) {
+                    const float *vec = o < jj ? Wp + o : Vp + (o - jj);
+                    float acc = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 5; ++u) {
+                        const int C = l32 + 32 * u;
+                        acc = fmaf(ld_or_zero(vec, min(C, n - 1) * PS, C > j && C < n), vr[u], acc);
+                    }
+                    acc = group16_sum(acc);
+                    acc += dpp_move<kDppRowBcast15>(acc);
+                    if (l32 == 16) sy[o < jj ? o : 32 + (o - jj)] = acc;
+                }
             }
             __syncthreads();
             // p = tau (A22 v - V W^T v - W V^T v), w = p - hk v, and the next column
             // x = A(:, j+1) - V W(j+1, :)^T - W V(j+1, :)^T; 4 lanes per row share
             // the sums over the panel's previous columns m (m = l4 mod 4)
             float kp = 0.f;
-            for (int c = lane; c < s; c += 64) kp = fmaf(sp[c], c == 0 ? v0 : sxa[j + 1 + c], kp);
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int c = lane + 64 * t, cc = min(c, s - 1);
+                const float vc = c == 0 ? v0 : sxa[j + 1 + cc];
+                kp = fmaf(ld_or_zero(sp, cc, c < s), vc, kp);
+            }
             kp = wave_sum(kp);
             const bool next = jj + 1 < nb;
-            {
-                const int l4 = tid & 3, c = tid >> 2, r = j + 1 + c;
+            // waves past the last row skip; all 8 sums over m are issued at once
+            // (the panel's V, W and the dot slots past jj hold zeros, and
+            // column jj of row j+1 is masked: it is written in this part)
+            if (16 * wid < s) {
+                const int l4 = tid & 3, c = tid >> 2, r = j + 1 + c, rc = min(r, n - 1);
                 const bool live = c < s;
                 float cw = 0.f, cx = 0.f, cw1 = 0.f, yy = 0.f;
-                for (int m = l4; m < jj; m += 4) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int m = l4 + 4 * t;
+                    const bool on = m < jj;
                     const float y1 = sy[m], y2 = sy[32 + m];
-                    const float bv = Vp[(j + 1) * PS + m], bw = Wp[(j + 1) * PS + m];
+                    const float bv = ld_or_zero(Vp, (j + 1) * PS + m, on);
+                    const float bw = ld_or_zero(Wp, (j + 1) * PS + m, on);
+                    const float rv = Vp[rc * PS + m], rw = Wp[rc * PS + m];
                     yy = fmaf(y1, y2, yy);
                     cw1 = fmaf(bv, y1, fmaf(bw, y2, cw1));
-                    if (live) {
-                        const float rv = Vp[r * PS + m], rw = Wp[r * PS + m];
-                        cw = fmaf(rv, y1, fmaf(rw, y2, cw));
-                        cx = fmaf(rv, bw, fmaf(rw, bv, cx));
-                    }
+                    cw = fmaf(rv, y1, fmaf(rw, y2, cw));
+                    cx = fmaf(rv, bw, fmaf(rw, bv, cx));
                 }
                 cw = group4_sum(cw);
                 cx = group4_sum(cx);
@@ -564,10 +610,8 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
 
     // ---------------------------------------------------------------- 5. Newton-Schulz steps
     // V <- V (3 I - V^T V) / 2 = V + V E with E = (I - V^T V) / 2.  V^T V is
-    // symmetric: its upper tiles are formed (fp32 MFMA) and E goes to both
-    // triangles of the A buffer.  V E is a small correction, formed with bf16
-    // products (relative error ~2^-9 of a term of size |E|); V's span is kept
-    // exactly, whatever E's precision.
+    // symmetric: its upper tiles are formed and E goes to both triangles of
+    // the A buffer; V + V E is formed with V E as the small term.
     JOLT_PROBE(5);
     const int ntri = nt * (nt + 1) / 2;     // <= kWaves for n <= 160
     for (int step = 0;; ++step) {
@@ -652,14 +696,14 @@ static hipError_t allow_lds_tri() {
 }
 
 // dynamic LDS layout for a batch of order <= maxN (floats):
-// [A: maxN x ld | B1: max(maxN x ld, 2 maxN x 33) | scratch tiles (maxN < 128 only)]
+// [A: maxN x ld | B1: max(maxN x ld, 2 maxN x kPanelStride) | scratch tiles (maxN < 128 only)]
 struct TriLayout { int ld, boff, poff, soff; size_t bytes; };
 static TriLayout tri_layout(int maxN) {
     TriLayout L;
     L.ld = maxN | 1;
     L.boff = maxN * L.ld;
-    L.poff = maxN * 33;
-    const int b1 = std::max(maxN * L.ld, 2 * maxN * 33);
+    L.poff = maxN * kPanelStride;
+    const int b1 = std::max(maxN * L.ld, 2 * maxN * kPanelStride);
     L.soff = maxN >= 128 ? -1 : L.boff + b1;
     L.bytes = (size_t)(L.boff + b1 + (L.soff >= 0 ? 5 * 32 * 33 : 0)) * sizeof(float);
     return L;
