@@ -25,78 +25,132 @@
 namespace jolt {
 
 // ====================================================================== X-pass A M
-// WG: 4 waves x 32 tokens; each wave owns NF column fragments (32 columns each).
-// The K range of a workgroup is a whole number of 64-feature chunks (d is a
-// multiple of 64); each chunk's fragment loads (U of A, U NF of M) are issued
-// before its MFMAs, with no branches in between.
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::Frag frag_select(bool keep, const typename Elem<T>::Frag &f) {
-    typename Elem<T>::Frag z = f;
-    if constexpr (sizeof(T) == 2) {
-        uint4 u = __builtin_bit_cast(uint4, f.v);
-        u.x = keep ? u.x : 0u; u.y = keep ? u.y : 0u; u.z = keep ? u.z : 0u; u.w = keep ? u.w : 0u;
-        z.v = __builtin_bit_cast(bf16x8, u);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) z.v[i] = keep ? f.v[i] : 0.f;
-    }
-    return z;
-}
+// out[s][c][t] = sum over the split's features k of x[t][k] m[k][c] (x the token
+// unfolding, m the sketch operand stored as m[c][k]).
+//
+// WG: 4 waves x 64 tokens (two 32-token row fragments per wave) and NF column
+// fragments of 32.  The K range (lh_split whole (layer, head) blocks) runs in
+// chunks of 64 features.  A chunk of m (NF*32 columns x 64) is staged once per
+// WG in LDS, double buffered, and read by all four waves; x fragments come
+// straight from global memory, each element once, one chunk ahead.
+template <typename T, int KC_>
+struct XmTile {
+    static constexpr int PER = 16 / sizeof(T);     // elements per 16-byte piece
+    static constexpr int KC = KC_;                 // K chunk
+    static constexpr int KP = KC + PER;            // LDS row pitch (elements)
+    static constexpr int U = KC / 16;              // MFMA K steps per chunk
+};
 
-template <typename T, int NF>
+template <typename T, int NF, int KC_>
 __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles) {
+    using Frag = typename Elem<T>::Frag;
+    using Tile = XmTile<T, KC_>;
+    constexpr int PER = Tile::PER, KC = Tile::KC, KP = Tile::KP, U = Tile::U;
+    constexpr int ROWS = 32 * NF;
+    constexpr int PIECES = ROWS * KC / PER;                 // 16-byte pieces per m chunk
+    constexpr int PPT = (PIECES + 255) / 256;               // per thread
+    extern __shared__ __attribute__((aligned(16))) unsigned char xm_lds[];
+    T *ms = reinterpret_cast<T *>(xm_lds);                  // [2][ROWS][KP]
     const Block3 blk = xcd_block();
     const XmItem &it = batch.it[blk.z];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
-    const int t0 = blk.x * 128 + wave * 32;
-    const int c0 = (blk.y % ncol_tiles) * (32 * NF);
+    const int tw = blk.x * 256 + wave * 64;                 // this wave's first token
+    const int c0 = (blk.y % ncol_tiles) * ROWS;
     const int sp = blk.y / ncol_tiles;
-    if (t0 >= it.T || c0 >= it.ncols || sp >= it.nsplit) return;
+    if (blk.x * 256 >= it.T || c0 >= it.ncols || sp >= it.nsplit) return;
+    const bool wv = tw < it.T;                              // T is a multiple of 64
     const T *x = reinterpret_cast<const T *>(it.x);
     const T *m = reinterpret_cast<const T *>(it.m);
     const int n = it.LH * d;
-    const int tok = t0 + ln;                // T is a multiple of 64, so always valid
-    f32x16 acc[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
-    const T *mcol[NF];
-    bool cval[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        const int c = c0 + 32 * f + ln;
-        cval[f] = c < it.ncols;
-        mcol[f] = m + (size_t)(cval[f] ? c : 0) * it.m_c + 8 * h;
-    }
-    // K steps per chunk: as many as the registers for the staged fragments allow
-    constexpr int U = sizeof(T) == 2 ? (NF <= 5 ? 4 : 2) : (NF <= 5 ? 2 : 1);
     const int kb = sp * it.lh_split * d, ke = min(n, kb + it.lh_split * d);
-    for (int k0 = kb; k0 < ke; k0 += 16 * U) {
+    const int nck = (ke - kb) / KC;
+
+    // m chunk staging: piece p -> row p / (KC / PER), 16 bytes at column (p % (KC / PER)) * PER
+    uint4 stg[PPT];
+    auto load_m = [&](int k0) {
         const int lh = k0 / d, fb = k0 - lh * d;
-        const T *xa = x + ((size_t)lh * it.T + tok) * d + fb + 8 * h;
-        const size_t mo = (size_t)lh * it.m_blk + fb;
-        typename Elem<T>::Frag a[U], b[U][NF];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            a[u] = load_frag(xa + 16 * u);
-#pragma unroll
-            for (int f = 0; f < NF; ++f) b[u][f] = load_frag(mcol[f] + mo + 16 * u);
+        for (int q = 0; q < PPT; ++q) {
+            const int p = threadIdx.x + 256 * q;
+            const int r = p / (KC / PER), kk = (p % (KC / PER)) * PER;
+            const int c = c0 + r;
+            const bool ok = p < PIECES && c < it.ncols;
+            const T *src = m + (size_t)(ok ? c : 0) * it.m_c + (size_t)lh * it.m_blk + fb + (ok ? kk : 0);
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            stg[q] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
         }
+    };
+    auto store_m = [&](int buf) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int q = 0; q < PPT; ++q) {
+            const int p = threadIdx.x + 256 * q;
+            if (p < PIECES) {
+                const int r = p / (KC / PER), kk = (p % (KC / PER)) * PER;
+                *reinterpret_cast<uint4 *>(ms + ((size_t)buf * ROWS + r) * KP + kk) = stg[q];
+            }
+        }
+    };
+    // x fragments of a chunk: rows tw + 32 r + ln, K = 16 u + 8 h + (0..7)
+    Frag an[2][U], a[2][U];
+    auto load_x = [&](int k0) {
+        const int lh = k0 / d, fb = k0 - lh * d;
 #pragma unroll
-            for (int f = 0; f < NF; ++f) mfma(a[u], frag_select<T>(cval[f], b[u][f]), acc[f]);
+        for (int r = 0; r < 2; ++r) {
+            const int tok = wv ? tw + 32 * r + ln : 0;
+            const T *xa = x + ((size_t)lh * it.T + tok) * d + fb + 8 * h;
+#pragma unroll
+            for (int u = 0; u < U; ++u) an[r][u] = load_frag(xa + 16 * u);
+        }
+    };
+
+    f32x16 acc[2][NF];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[r][f] = f32x16{};
+    if (nck > 0) {
+        load_m(kb);
+        load_x(kb);
+        store_m(0);
     }
+    for (int ci = 0; ci < nck; ++ci) {
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int u = 0; u < U; ++u) a[r][u] = an[r][u];
+        const bool more = ci + 1 < nck;
+        if (more) {
+            load_m(kb + (ci + 1) * KC);
+            load_x(kb + (ci + 1) * KC);
+        }
+        const T *mb = ms + (size_t)(ci & 1) * ROWS * KP;
+        if (wv) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                    const Frag b = load_frag(mb + (32 * f + ln) * KP + 16 * u + 8 * h);
+                    mfma(a[0][u], b, acc[0][f]);
+                    mfma(a[1][u], b, acc[1][f]);
+                }
+        }
+        if (more) store_m((ci + 1) & 1);
+    }
+    if (!wv) return;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         const int c = c0 + 32 * f + ln;
         if (c < it.ncols) {
-            float *o = it.out + (size_t)sp * it.ncols * it.ldo + (size_t)c * it.ldo + t0;
+            float *o = it.out + (size_t)sp * it.ncols * it.ldo + (size_t)c * it.ldo + tw;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = 8 * q + 4 * h;
-                *reinterpret_cast<float4 *>(o + r) =
-                    make_float4(acc[f][4 * q], acc[f][4 * q + 1], acc[f][4 * q + 2], acc[f][4 * q + 3]);
-            }
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = 32 * r + 8 * q + 4 * h;
+                    *reinterpret_cast<float4 *>(o + row) = make_float4(acc[r][f][4 * q], acc[r][f][4 * q + 1],
+                                                                       acc[r][f][4 * q + 2], acc[r][f][4 * q + 3]);
+                }
         }
     }
 }
@@ -117,68 +171,182 @@ __device__ __forceinline__ void stage_transposed(const T *src, int d, T *xs, int
 }
 
 // ====================================================================== X-pass Q^T A
-// WG per (item, lh, split): 4 waves; wave w -> feature fragment w % (d/32),
-// column fragments [(w / (d/32)) * NF, ...).
+// out[s][c][F] = sum over the split's tokens t of q[c][t] x[t][F], F = lh d + f
+// the global feature index (the token unfolding's column).
+//
+// WG: a tile of 256 features (4 waves x 2 row fragments of 32) and NF column
+// fragments of 32.  Per chunk of 64 tokens the WG stages, once, x's tile
+// transposed to xs[F][t] (token pairs packed in 32-bit words for bf16) and the
+// chunk of q (hi and lo parts when LO) as qs[c][t]; the next chunk is loaded
+// into registers meanwhile.  Each wave then reads 2 x fragments and NF (2 NF)
+// q fragments per 16 tokens from LDS.
 template <typename T, int NF, bool LO>
-__global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d) {
-    constexpr int XP = 64 + 16 / sizeof(T);
-    __shared__ __attribute__((aligned(16))) T xs[128 * XP];
+struct XtqTile {
+    static constexpr int PER = 16 / sizeof(T);
+    static constexpr int FT = 256;                       // features per WG
+    static constexpr int TC = 64;                        // tokens per chunk
+    static constexpr int XP = TC + PER;                  // LDS pitch of xs and qs rows
+    static constexpr int QR = 32 * NF * (LO ? 2 : 1);    // q rows staged (hi rows, then lo rows)
+    static constexpr int XPIECES = FT * TC / PER / (sizeof(T) == 2 ? 2 : 1);  // loads of x per chunk
+    static constexpr int XPT = XPIECES / 256;
+    static constexpr int QPIECES = QR * TC / PER;
+    static constexpr int QPT = (QPIECES + 255) / 256;
+    static constexpr size_t lds_bytes = (size_t)(FT + QR) * XP * sizeof(T);
+};
+
+template <typename T, int NF, bool LO>
+__global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit) {
+    using Tile = XtqTile<T, NF, LO>;
+    using Frag = typename Elem<T>::Frag;
+    constexpr int PER = Tile::PER, FT = Tile::FT, TC = Tile::TC, XP = Tile::XP, QR = Tile::QR;
+    constexpr int XPT = Tile::XPT, QPT = Tile::QPT, QPIECES = Tile::QPIECES;
+    constexpr bool BF = sizeof(T) == 2;
+    extern __shared__ __attribute__((aligned(16))) unsigned char xtq_lds[];
+    T *xs = reinterpret_cast<T *>(xtq_lds);               // [FT][XP]
+    T *qs = xs + FT * XP;                                 // [QR][XP]
     const Block3 blk = xcd_block();
     const XtqItem &it = batch.it[blk.z];
-    const int lh = blk.y, sp = blk.x;
-    if (lh >= it.LH || sp >= it.nsplit) return;
+    const int n = it.LH * d;
+    const int F0 = blk.y * FT, sp = blk.x % maxSplit, c0 = (blk.x / maxSplit) * 32 * NF;
+    if (F0 >= n || sp >= it.nsplit || c0 >= it.ncols) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
-    const int nmf = d / 32;
-    const int mf = wave % nmf, cgrp = wave / nmf;
-    const int c0 = cgrp * NF * 32;
-    const T *x = reinterpret_cast<const T *>(it.x) + (size_t)lh * it.T * d;
+    const T *x = reinterpret_cast<const T *>(it.x);
     const T *qh = reinterpret_cast<const T *>(it.qh);
     const T *ql = reinterpret_cast<const T *>(it.ql);
     const int tb = sp * it.tsplit, te = min(it.T, tb + it.tsplit);
-    f32x16 acc[NF];
+    const int nck = (te - tb) / TC;                       // T is a multiple of 64
+
+    // x staging.  bf16: piece = 2 consecutive tokens x 8 features (two 16-byte
+    // loads), lanes: 8 token pairs x 8 feature groups; fp32: piece = 1 token x 4
+    // features, lanes: 16 tokens x 4 feature groups.
+    constexpr int TPL = BF ? 8 : 16;                      // token slots per wave pass
+    constexpr int FGL = 64 / TPL;                         // feature groups per wave pass
+    uint4 xr[XPT][BF ? 2 : 1];
+    auto load_x = [&](int t0) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
-    for (int t0 = tb; t0 < te; t0 += 64) {
-        __syncthreads();
-        stage_transposed<T>(x + (size_t)t0 * d, d, xs, XP);
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 64; kk += 16) {
-            typename Elem<T>::Frag a;
-            {
-                const T *p = xs + (32 * mf + ln) * XP + kk + 8 * h;
-                if constexpr (sizeof(T) == 2) {
-                    const uint2 *q = reinterpret_cast<const uint2 *>(p);
-                    uint2 u0 = q[0], u1 = q[1];
-                    a.v = __builtin_bit_cast(bf16x8, make_uint4(u0.x, u0.y, u1.x, u1.y));
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) reinterpret_cast<float *>(&a)[i] = reinterpret_cast<const float *>(p)[i];
-                }
+        for (int q = 0; q < XPT; ++q) {
+            const int pass = wave + 4 * q;                // 0 .. 4 XPT - 1
+            const int tl = lane % TPL, fg = lane / TPL;
+            const int tpass = pass % (TC / (BF ? 2 : 1) / TPL), fpass = pass / (TC / (BF ? 2 : 1) / TPL);
+            const int t = t0 + (tpass * TPL + tl) * (BF ? 2 : 1);
+            const int F = F0 + (fpass * FGL + fg) * PER;
+            const bool ok = F < n;
+            const int Fc = ok ? F : 0;
+            const int lh = Fc / d, f = Fc - lh * d;
+            const T *src = x + ((size_t)lh * it.T + t) * d + f;
+            const uint4 v0 = *reinterpret_cast<const uint4 *>(src);
+            xr[q][0] = ok ? v0 : make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (BF) {
+                const uint4 v1 = *reinterpret_cast<const uint4 *>(src + d);
+                xr[q][1] = ok ? v1 : make_uint4(0u, 0u, 0u, 0u);
             }
-            const int t = t0 + kk + 8 * h;
+        }
+    };
+    auto store_x = [&]() {
+#pragma unroll
+        for (int q = 0; q < XPT; ++q) {
+            const int pass = wave + 4 * q;
+            const int tl = lane % TPL, fg = lane / TPL;
+            const int tpass = pass % (TC / (BF ? 2 : 1) / TPL), fpass = pass / (TC / (BF ? 2 : 1) / TPL);
+            const int tt = (tpass * TPL + tl) * (BF ? 2 : 1);
+            const int fr = (fpass * FGL + fg) * PER;
+            if constexpr (BF) {
+                const uint32_t *a0 = reinterpret_cast<const uint32_t *>(&xr[q][0]);
+                const uint32_t *a1 = reinterpret_cast<const uint32_t *>(&xr[q][1]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    // features 2w, 2w+1 of tokens tt, tt+1 -> (t, t+1) word in rows fr+2w, fr+2w+1
+                    const uint32_t lo = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
+                    *reinterpret_cast<uint32_t *>(xs + (fr + 2 * w) * XP + tt) = lo;
+                    *reinterpret_cast<uint32_t *>(xs + (fr + 2 * w + 1) * XP + tt) = hi;
+                }
+            } else {
+                const float *a0 = reinterpret_cast<const float *>(&xr[q][0]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) xs[(fr + w) * XP + tt] = a0[w];
+            }
+        }
+    };
+    // q staging: row r < 32 NF is hi column c0 + r, else lo column r - 32 NF
+    uint4 qr[QPT];
+    auto load_q = [&](int t0) {
+#pragma unroll
+        for (int q = 0; q < QPT; ++q) {
+            const int p = threadIdx.x + 256 * q;
+            const int r = p / (TC / PER), tt = (p % (TC / PER)) * PER;
+            const int c = c0 + (r < 32 * NF ? r : r - 32 * NF);
+            const bool ok = p < QPIECES && c < it.ncols;
+            const T *base = (LO && r >= 32 * NF) ? ql : qh;
+            const uint4 v = *reinterpret_cast<const uint4 *>(base + (size_t)(ok ? c : 0) * it.ldq + t0 + (ok ? tt : 0));
+            qr[q] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_q = [&]() {
+#pragma unroll
+        for (int q = 0; q < QPT; ++q) {
+            const int p = threadIdx.x + 256 * q;
+            if (p < QPIECES) {
+                const int r = p / (TC / PER), tt = (p % (TC / PER)) * PER;
+                *reinterpret_cast<uint4 *>(qs + r * XP + tt) = qr[q];
+            }
+        }
+    };
+
+    f32x16 acc[2][NF];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[r][f] = f32x16{};
+    const int fw = 64 * wave;                             // this wave's first feature in the tile
+    if (nck > 0) {
+        load_x(tb);
+        load_q(tb);
+    }
+    for (int ci = 0; ci < nck; ++ci) {
+        __syncthreads();                                  // the previous chunk's reads are done
+        store_x();
+        store_q();
+        __syncthreads();
+        if (ci + 1 < nck) {
+            load_x(tb + (ci + 1) * TC);
+            load_q(tb + (ci + 1) * TC);
+        }
+#pragma unroll
+        for (int kk = 0; kk < TC; kk += 16) {
+            Frag a[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) a[r] = load_frag(xs + (fw + 32 * r + ln) * XP + kk + 8 * h);
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-                const int c = c0 + 32 * f + ln;
-                if (c < it.ncols) {
-                    mfma(a, load_frag(qh + (size_t)c * it.ldq + t), acc[f]);
-                    if constexpr (LO) mfma(a, load_frag(ql + (size_t)c * it.ldq + t), acc[f]);
+                const Frag b = load_frag(qs + (32 * f + ln) * XP + kk + 8 * h);
+                mfma(a[0], b, acc[0][f]);
+                mfma(a[1], b, acc[1][f]);
+                if constexpr (LO) {
+                    const Frag bl = load_frag(qs + (32 * NF + 32 * f + ln) * XP + kk + 8 * h);
+                    mfma(a[0], bl, acc[0][f]);
+                    mfma(a[1], bl, acc[1][f]);
                 }
             }
         }
     }
-    const int n = it.LH * d;
     float *out = it.out + (size_t)sp * it.ncols * n;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         const int c = c0 + 32 * f + ln;
         if (c < it.ncols) {
-            float *o = out + (size_t)c * n + (size_t)lh * d + 32 * mf;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = 8 * q + 4 * h;
-                *reinterpret_cast<float4 *>(o + r) =
-                    make_float4(acc[f][4 * q], acc[f][4 * q + 1], acc[f][4 * q + 2], acc[f][4 * q + 3]);
+            for (int r = 0; r < 2; ++r) {
+                const int Fr = F0 + fw + 32 * r;
+                if (Fr < n) {
+                    float *o = out + (size_t)c * n + Fr;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int row = 8 * q + 4 * h;
+                        *reinterpret_cast<float4 *>(o + row) = make_float4(acc[r][f][4 * q], acc[r][f][4 * q + 1],
+                                                                           acc[r][f][4 * q + 2], acc[r][f][4 * q + 3]);
+                    }
+                }
             }
         }
     }
@@ -777,59 +945,79 @@ static hipError_t ensure_lds_attrs() {
     return state;
 }
 
+template <typename T, int NF, int KC>
+static hipError_t xm_launch(const XmBatch &b, int d, dim3 g, int tiles, hipStream_t s) {
+    const size_t lds = (size_t)2 * 32 * NF * XmTile<T, KC>::KP * sizeof(T);
+    static hipError_t attr = hipErrorNotReady;
+    if (attr == hipErrorNotReady) attr = allow_dynamic_lds(reinterpret_cast<const void *>(k_xm<T, NF, KC>));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((k_xm<T, NF, KC>), g, dim3(256), lds, s, b, d, tiles);
+    return hipGetLastError();
+}
+
+// chunks of 64 features (128 measured slower: the wider tile spills)
 template <typename T>
 static hipError_t xm_nf(const XmBatch &b, int d, dim3 g, int nf, int tiles, hipStream_t s) {
     switch (nf) {
-        case 1: hipLaunchKernelGGL((k_xm<T, 1>), g, dim3(256), 0, s, b, d, tiles); break;
-        case 2: hipLaunchKernelGGL((k_xm<T, 2>), g, dim3(256), 0, s, b, d, tiles); break;
-        case 3: hipLaunchKernelGGL((k_xm<T, 3>), g, dim3(256), 0, s, b, d, tiles); break;
-        case 4: hipLaunchKernelGGL((k_xm<T, 4>), g, dim3(256), 0, s, b, d, tiles); break;
-        case 5: hipLaunchKernelGGL((k_xm<T, 5>), g, dim3(256), 0, s, b, d, tiles); break;
-        case 6: hipLaunchKernelGGL((k_xm<T, 6>), g, dim3(256), 0, s, b, d, tiles); break;
-        case 7: hipLaunchKernelGGL((k_xm<T, 7>), g, dim3(256), 0, s, b, d, tiles); break;
-        case 8: hipLaunchKernelGGL((k_xm<T, 8>), g, dim3(256), 0, s, b, d, tiles); break;
-        case 9: hipLaunchKernelGGL((k_xm<T, 9>), g, dim3(256), 0, s, b, d, tiles); break;
-        default: return hipErrorInvalidValue;
+        case 1: return xm_launch<T, 1, 64>(b, d, g, tiles, s);
+        case 2: return xm_launch<T, 2, 64>(b, d, g, tiles, s);
+        case 3: return xm_launch<T, 3, 64>(b, d, g, tiles, s);
+        case 4: return xm_launch<T, 4, 64>(b, d, g, tiles, s);
+        default: break;
     }
-    return hipGetLastError();
+    if constexpr (sizeof(T) == 2) {      // wider tiles fit the registers in bf16 only
+        if (nf == 5) return xm_launch<T, 5, 64>(b, d, g, tiles, s);
+        if (nf == 6) return xm_launch<T, 6, 64>(b, d, g, tiles, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, int maxSplit, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    if (d % 64) return hipErrorInvalidValue;
     KTimeScope kts("k_xm", s);
     int nf = (maxCols + 31) / 32;
     int tiles = 1;
-    if (nf > 9) { tiles = (nf + 3) / 4; nf = 4; }
-    dim3 g((maxT + 127) / 128, tiles * maxSplit, b.n);
+    if (nf > (dtype == JOLT_BF16 ? 6 : 4)) { tiles = (nf + 3) / 4; nf = 4; }
+    dim3 g((maxT + 255) / 256, tiles * maxSplit, b.n);
     return dtype == JOLT_BF16 ? xm_nf<uint16_t>(b, d, g, nf, tiles, s) : xm_nf<float>(b, d, g, nf, tiles, s);
 }
 
+template <typename T, int NF, bool LO>
+static hipError_t xtq_launch(const XtqBatch &b, int d, dim3 g, int maxSplit, hipStream_t s) {
+    static hipError_t attr = hipErrorNotReady;
+    if (attr == hipErrorNotReady) attr = allow_dynamic_lds(reinterpret_cast<const void *>(k_xtq<T, NF, LO>));
+    if (attr != hipSuccess) return attr;
+    const size_t lds = XtqTile<T, NF, LO>::lds_bytes;
+    hipLaunchKernelGGL((k_xtq<T, NF, LO>), g, dim3(256), lds, s, b, d, maxSplit);
+    return hipGetLastError();
+}
+
 template <typename T, bool LO>
-static hipError_t xtq_nf(const XtqBatch &b, int d, dim3 g, int nf, hipStream_t s) {
+static hipError_t xtq_nf(const XtqBatch &b, int d, dim3 g, int nf, int maxSplit, hipStream_t s) {
     switch (nf) {
-        case 1: hipLaunchKernelGGL((k_xtq<T, 1, LO>), g, dim3(256), 0, s, b, d); break;
-        case 2: hipLaunchKernelGGL((k_xtq<T, 2, LO>), g, dim3(256), 0, s, b, d); break;
-        case 3: hipLaunchKernelGGL((k_xtq<T, 3, LO>), g, dim3(256), 0, s, b, d); break;
-        case 4: hipLaunchKernelGGL((k_xtq<T, 4, LO>), g, dim3(256), 0, s, b, d); break;
-        case 5: hipLaunchKernelGGL((k_xtq<T, 5, LO>), g, dim3(256), 0, s, b, d); break;
-        case 6: hipLaunchKernelGGL((k_xtq<T, 6, LO>), g, dim3(256), 0, s, b, d); break;
-        case 7: hipLaunchKernelGGL((k_xtq<T, 7, LO>), g, dim3(256), 0, s, b, d); break;
-        case 8: hipLaunchKernelGGL((k_xtq<T, 8, LO>), g, dim3(256), 0, s, b, d); break;
-        case 9: hipLaunchKernelGGL((k_xtq<T, 9, LO>), g, dim3(256), 0, s, b, d); break;
+        case 1: return xtq_launch<T, 1, LO>(b, d, g, maxSplit, s);
+        case 2: return xtq_launch<T, 2, LO>(b, d, g, maxSplit, s);
+        case 3: return xtq_launch<T, 3, LO>(b, d, g, maxSplit, s);
+        case 4: return xtq_launch<T, 4, LO>(b, d, g, maxSplit, s);
+        case 5: return xtq_launch<T, 5, LO>(b, d, g, maxSplit, s);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_xtq(const XtqBatch &b, int dtype, int d, int maxLH, int maxSplit, int maxCols, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    if (d % 32) return hipErrorInvalidValue;
+    for (int i = 0; i < b.n; ++i)
+        if (b.it[i].T % 64 || b.it[i].tsplit % 64) return hipErrorInvalidValue;
     KTimeScope kts("k_xtq", s);
-    const int cgroups = 4 / (d / 32);                    // waves sharing one feature fragment
-    const int nf = ((maxCols + 31) / 32 + cgroups - 1) / cgroups;
-    dim3 g(maxSplit, maxLH, b.n);
+    // column tiles of at most 5 fragments (160 columns)
+    const int frags = (maxCols + 31) / 32, ctiles = (frags + 4) / 5, nf = (frags + ctiles - 1) / ctiles;
+    dim3 g(maxSplit * ctiles, (maxLH * d + 255) / 256, b.n);
     const bool lo = b.it[0].ql != nullptr;
-    if (dtype == JOLT_BF16) return lo ? xtq_nf<uint16_t, true>(b, d, g, nf, s) : xtq_nf<uint16_t, false>(b, d, g, nf, s);
-    return xtq_nf<float, false>(b, d, g, nf, s);
+    if (dtype == JOLT_BF16)
+        return lo ? xtq_nf<uint16_t, true>(b, d, g, nf, maxSplit, s) : xtq_nf<uint16_t, false>(b, d, g, nf, maxSplit, s);
+    return xtq_nf<float, false>(b, d, g, nf, maxSplit, s);
 }
 
 hipError_t launch_gram_rows(const GramBatch &b, int dtype, int d, int maxP, hipStream_t s) {

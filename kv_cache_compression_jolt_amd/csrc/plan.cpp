@@ -88,8 +88,8 @@ Dims dims_for(const jolt_config &cfg, const jolt_item &it, int rt_max, int rf_ma
     D.gN_split = clampi(D.n / 512, 1, 64);
     D.gN_chunk = round_up((D.n + D.gN_split - 1) / D.gN_split, 16);
     D.gN_split = (D.n + D.gN_chunk - 1) / D.gN_chunk;
-    // enough workgroups for 256 CUs: T / 128 token tiles per item, 16 items per launch
-    D.xm_split = clampi(2048 / std::max(1, (D.T / 128) * kMaxBatch), 1, 8);
+    // about one workgroup per CU: ceil(T / 256) token tiles per item, 16 items per launch
+    D.xm_split = clampi(256 / std::max(1, ((D.T + 255) / 256) * kMaxBatch), 1, 8);
     D.xm_split = std::min(D.xm_split, D.LH);
     D.xm_lh = (D.LH + D.xm_split - 1) / D.xm_split;
     D.xm_split = (D.LH + D.xm_lh - 1) / D.xm_lh;
