@@ -97,6 +97,13 @@ __device__ __forceinline__ void mfma(const FragF32 &a, const FragF32 &b, f32x16 
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
+// p[i] where ok, else 0: the load is always issued, so i must address the
+// buffer even where ok is false; a select, not a branch, drops the value
+__device__ __forceinline__ float ld_or_zero(const float *p, int i, bool ok) {
+    const float v = p[i];
+    return ok ? v : 0.f;
+}
+
 // Orders one wave's LDS stores before its later LDS loads of other lanes'
 // values (no workgroup barrier: only the calling wave takes part).
 __device__ __forceinline__ void wave_lds_sync() {

@@ -46,13 +46,6 @@ constexpr int kPanelStride = 34;
 // C (n x n) tile (tm, tn) of sum_k A(m, k) B(k, n) on v_mfma_f32_32x32x2f32, with
 // A(m, k) = a[k * lda_k + m * lda_m] and B(k, n) = b[k * ld + n]; out of range
 // entries read as zero.
-// p[i] where ok, else 0: the load is always issued, so i must address the
-// buffer even where ok is false; a select, not a branch, drops the value
-__device__ __forceinline__ float ld_or_zero(const float *p, int i, bool ok) {
-    const float v = p[i];
-    return ok ? v : 0.f;
-}
-
 __device__ __forceinline__ f32x16 mfma_tile(const float *a, int lda_k, int lda_m, const float *b, int ld, int n,
                                             int tm, int tn, int lane) {
     f32x16 acc;

@@ -200,51 +200,77 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
     }
 }
 
-__global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch, int ldl, int stage_l) {
+__global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch, int ldx, int stage_x) {
     extern __shared__ float sh[];
     constexpr int YS = 68;                  // row stride of the staged Y block
     const TrsmItem &it = batch.it[blockIdx.y];
     const int t0 = blockIdx.x * 64;
     if (t0 >= it.len) return;
     const int k = it.k, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    float *Ys = sh;                         // [k][YS]
-    float *Ls = sh + k * YS;                // [k][ldl] when staged
-    // staging: rows by wave, columns by lane, several rows in flight per lane
-    const bool cv = t0 + lane < it.len;
+    const int ntm = (k + 31) >> 5, P = 32 * ntm;
+    float *Ys = sh;                         // [P][YS], rows >= k and columns past len zero
+    float *Xs = sh + P * YS;                // [P][ldx] when staged, zero outside the k x k lower triangle
+    // staging: one row per wave and pass, 64 columns by lane; loads are clamped
+    // into the buffers and the out-of-range values replaced by zeros
+    const int col = t0 + lane, colc = min(col, it.len - 1);
 #pragma unroll 8
-    for (int r = wid; r < k; r += 4) Ys[r * YS + lane] = cv ? it.y[(size_t)r * it.ldy + t0 + lane] : 0.f;
-    if (stage_l) {
+    for (int r = wid; r < P; r += 4)
+        Ys[r * YS + lane] = ld_or_zero(it.y, min(r, k - 1) * it.ldy + colc, r < k && col < it.len);
+    if (stage_x) {
 #pragma unroll 4
-        for (int r = wid; r < k; r += 4) {
+        for (int r = wid; r < P; r += 4) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 3; ++u) {
                 const int c = lane + 64 * u;
-                if (c <= r) Ls[r * ldl + c] = it.l[(size_t)r * it.ld + c];      // lower triangle only
+                if (c < P) Xs[r * ldx + c] = ld_or_zero(it.l, min(r, k - 1) * it.ld + min(c, k - 1), r < k && c < k);
             }
         }
     }
     __syncthreads();
-    const float *A = stage_l ? Ls : it.l;
-    const int lda = stage_l ? ldl : it.ld;
-    const int ntm = (k + 31) >> 5, ntiles = ntm * 2;
-    for (int t = wid; t < ntiles; t += 4) {
-        const int tm = t >> 1, tn = t & 1;
-        const int m = tm * 32 + (lane & 31), n = tn * 32 + (lane & 31), kh = lane >> 5;
-        f32x16 acc = {};
-        const int kend = min(k, 32 * (tm + 1));      // L^{-1} is lower triangular
-        for (int k0 = 0; k0 < kend; k0 += 2) {
-            const int kk = k0 + kh;
-            const float a = (m < k && kk <= m) ? A[(size_t)m * lda + kk] : 0.f;
-            const float b = kk < k ? Ys[kk * YS + n] : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-        }
-        const int col = t0 + n;
-        if (col < it.len)
+    // row blocks to waves, largest first, each to the least loaded wave (a row
+    // block tm costs tm + 1 K-steps of 32: X is lower triangular)
+    int load[4] = {0, 0, 0, 0}, mine = 0;
+    for (int tm = ntm - 1; tm >= 0; --tm) {
+        int w = 0;
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int row = tm * 32 + frag_row(lane, jj);
-                if (row < k) it.q[(size_t)row * it.ldy + col] = acc[jj];
+        for (int v = 1; v < 4; ++v)
+            if (load[v] < load[w]) w = v;
+        load[w] += tm + 1;
+        if (w == wid) mine |= 1 << tm;
+    }
+    const int m32 = lane & 31, kh = lane >> 5;
+    for (int tm = ntm - 1; tm >= 0; --tm) {
+        if (!(mine >> tm & 1)) continue;
+        const int m = 32 * tm + m32, mc = min(m, k - 1);
+        f32x16 acc0 = {}, acc1 = {};
+        const int kend = 32 * (tm + 1);
+        if (stage_x) {
+            const float *xr = Xs + m * ldx;
+#pragma unroll 8
+            for (int k0 = 0; k0 < kend; k0 += 2) {
+                const int kk = k0 + kh;
+                const float a = xr[kk];
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ys[kk * YS + m32], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ys[kk * YS + 32 + m32], acc1, 0, 0, 0);
             }
+        } else {
+            const float *xr = it.l + (size_t)mc * it.ld;
+#pragma unroll 8
+            for (int k0 = 0; k0 < kend; k0 += 2) {
+                const int kk = k0 + kh;
+                const float a = ld_or_zero(xr, min(kk, k - 1), m < k && kk < k);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ys[kk * YS + m32], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ys[kk * YS + 32 + m32], acc1, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const int row = 32 * tm + frag_row(lane, jj);
+            if (row < k) {
+                if (t0 + m32 < it.len) it.q[(size_t)row * it.ldy + t0 + m32] = acc0[jj];
+                if (t0 + 32 + m32 < it.len) it.q[(size_t)row * it.ldy + t0 + 32 + m32] = acc1[jj];
+            }
+        }
     }
 }
 
@@ -276,14 +302,15 @@ hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s) {
 
 hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
+    if (maxK > kCholInverseMaxK) return hipErrorInvalidValue;
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
     KTimeScope kts("k_apply_linv", s);
-    const int ldl = maxK | 1;
-    size_t lds = (size_t)maxK * 68 * sizeof(float);
-    const size_t with_l = lds + (size_t)maxK * ldl * sizeof(float);
-    const int stage_l = with_l <= 150 * 1024;
-    if (stage_l) lds = with_l;
-    hipLaunchKernelGGL(k_apply_linv, dim3((maxLen + 63) / 64, b.n), dim3(256), lds, s, b, ldl, stage_l);
+    const int P = (maxK + 31) / 32 * 32, ldx = P + 1;
+    size_t lds = (size_t)P * 68 * sizeof(float);
+    const size_t with_x = lds + (size_t)P * ldx * sizeof(float);
+    const int stage_x = with_x <= 150 * 1024;
+    if (stage_x) lds = with_x;
+    hipLaunchKernelGGL(k_apply_linv, dim3((maxLen + 63) / 64, b.n), dim3(256), lds, s, b, ldx, stage_x);
     return hipGetLastError();
 }
 

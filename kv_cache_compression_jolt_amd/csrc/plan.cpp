@@ -879,25 +879,48 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     }
     std::vector<Cand> cand = candidate_grid(rt_max, rf_max, cfg->rank_step, cfg->bits_mask);
     const int nc = (int)cand.size();
-    std::vector<std::vector<double>> Dt(n, std::vector<double>(nc));
-    std::vector<std::vector<int64_t>> Bt(n, std::vector<int64_t>(nc));
+    // each candidate's energy-grid cell (-1 for rank 0)
+    std::vector<int> cell(nc);
+    for (int j = 0; j < nc; ++j)
+        cell[j] = (cand[j].rt == 0 || cand[j].rf == 0)
+                      ? -1 : (cand[j].rt / pl.step - 1) * pl.grid_nf + (cand[j].rf / pl.step - 1);
+    // byte tables and their order, shared by the items of one shape (dtype and d
+    // are common to the call; L, H, T may differ)
+    struct Shape { int L, H, T; std::vector<int64_t> B; std::vector<int> order; };
+    std::vector<Shape> shapes;
+    std::vector<int> shape_of(n);
     for (int i = 0; i < n; ++i) {
-        distortion_table(grid[i], pl.grid_nf, pl.step, nx2[i], cfg->delta_b, cand, Dt[i].data());
-        for (int j = 0; j < nc; ++j)
-            Bt[i][j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
+        int k = 0;
+        while (k < (int)shapes.size() &&
+               !(shapes[k].L == items[i].L && shapes[k].H == items[i].H && shapes[k].T == items[i].T))
+            ++k;
+        if (k == (int)shapes.size()) {
+            Shape sh{items[i].L, items[i].H, items[i].T, std::vector<int64_t>(nc), {}};
+            for (int j = 0; j < nc; ++j) sh.B[j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
+            sh.order = byte_order(nc, cand.data(), sh.B.data());
+            shapes.push_back(std::move(sh));
+        }
+        shape_of[i] = k;
     }
+    std::vector<std::vector<double>> Dt(n, std::vector<double>(nc));
+    for (int i = 0; i < n; ++i) distortion_table_cells(grid[i], cell.data(), nx2[i], cfg->delta_b, cand, Dt[i].data());
     std::vector<int32_t> ncand(n, nc);
     std::vector<const Cand *> cp(n, cand.data());
     std::vector<const double *> dp(n);
     std::vector<const int64_t *> bp(n);
-    for (int i = 0; i < n; ++i) { dp[i] = Dt[i].data(); bp[i] = Bt[i].data(); }
+    std::vector<const int *> op(n);
+    for (int i = 0; i < n; ++i) {
+        dp[i] = Dt[i].data();
+        bp[i] = shapes[shape_of[i]].B.data();
+        op[i] = shapes[shape_of[i]].order.data();
+    }
     std::vector<int> choice(n);
     double lam = 0.0;
-    s = allocate(n, ncand.data(), cp.data(), dp.data(), bp.data(), cfg->budget_bytes, choice.data(), &lam);
+    s = allocate(n, ncand.data(), cp.data(), dp.data(), bp.data(), cfg->budget_bytes, choice.data(), &lam, op.data());
     for (int i = 0; i < n; ++i) {
         const Cand &cc = cand[choice[i]];
         alloc_host[i].rt = cc.rt; alloc_host[i].rf = cc.rf; alloc_host[i].bits = cc.bits; alloc_host[i].reserved = 0;
-        alloc_host[i].bytes = Bt[i][choice[i]];
+        alloc_host[i].bytes = bp[i][choice[i]];
         alloc_host[i].distortion = Dt[i][choice[i]];
     }
     if (lambda_out) *lambda_out = lam;

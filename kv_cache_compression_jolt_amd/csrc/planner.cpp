@@ -33,19 +33,27 @@ int64_t item_bytes_impl(int L, int H, int T, int d, int e, int rt, int rf, int b
 }
 
 std::vector<Cand> candidate_grid(int rt_max, int rf_max, int step, uint32_t bits_mask) {
+    // generated in (rt, rf, bits) order: the rank-0 candidates first, one per bit width
     std::vector<Cand> out;
-    for (int b = 0; b <= 8; ++b) {
-        if (!(bits_mask & (1u << b))) continue;
-        out.push_back({0, 0, b});
-        for (int rt = step; rt <= rt_max; rt += step)
-            for (int rf = step; rf <= rf_max; rf += step) out.push_back({rt, rf, b});
-    }
-    std::sort(out.begin(), out.end(), [](const Cand &a, const Cand &b) {
-        if (a.rt != b.rt) return a.rt < b.rt;
-        if (a.rf != b.rf) return a.rf < b.rf;
-        return a.bits < b.bits;
-    });
+    for (int b = 0; b <= 8; ++b)
+        if (bits_mask & (1u << b)) out.push_back({0, 0, b});
+    for (int rt = step; rt <= rt_max; rt += step)
+        for (int rf = step; rf <= rf_max; rf += step)
+            for (int b = 0; b <= 8; ++b)
+                if (bits_mask & (1u << b)) out.push_back({rt, rf, b});
     return out;
+}
+
+std::vector<int> byte_order(int nc, const Cand *cand, const int64_t *B) {
+    std::vector<int> order(nc);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+        if (B[a] != B[b]) return B[a] < B[b];
+        if (cand[a].rt != cand[b].rt) return cand[a].rt < cand[b].rt;
+        if (cand[a].rf != cand[b].rf) return cand[a].rf < cand[b].rf;
+        return cand[a].bits < cand[b].bits;
+    });
+    return order;
 }
 
 namespace {
@@ -61,24 +69,18 @@ struct Pt {
     int rt, rf, bits, idx;
 };
 
-ItemHull build_hull(int nc, const Cand *cand, const double *D, const int64_t *B) {
-    std::vector<Pt> pts(nc);
-    for (int i = 0; i < nc; ++i) pts[i] = {B[i], D[i], cand[i].rt, cand[i].rf, cand[i].bits, i};
-    std::sort(pts.begin(), pts.end(), [](const Pt &a, const Pt &b) {
-        if (a.B != b.B) return a.B < b.B;
-        if (a.D != b.D) return a.D < b.D;
-        if (a.rt != b.rt) return a.rt < b.rt;
-        if (a.rf != b.rf) return a.rf < b.rf;
-        return a.bits < b.bits;
-    });
-    std::vector<int> order(nc);
-    for (int i = 0; i < nc; ++i) order[i] = pts[i].idx;
-    // staircase: one point per byte count, strictly falling D
+// `order`: candidate indices by (bytes, rt, rf, bits)
+ItemHull build_hull(int nc, const int *order, const double *D, const int64_t *B) {
+    // staircase: per byte count the point of least D (ties: the earliest in
+    // order, i.e. smaller rt, rf, bits), kept only where D strictly falls
     std::vector<int> stair;
-    for (int i : order) {
-        if (!stair.empty() && B[stair.back()] == B[i]) continue;
-        if (!stair.empty() && !(D[i] < D[stair.back()])) continue;
-        stair.push_back(i);
+    for (int p = 0; p < nc;) {
+        int best = order[p], q = p + 1;
+        for (; q < nc && B[order[q]] == B[best]; ++q)
+            if (D[order[q]] < D[best]) best = order[q];
+        p = q;
+        if (!stair.empty() && !(D[best] < D[stair.back()])) continue;
+        stair.push_back(best);
     }
     ItemHull h;
     for (int i : stair) {
@@ -107,12 +109,18 @@ int vertex_at(const ItemHull &h, double lam) {
 }  // namespace
 
 jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, const double *const *D,
-                     const int64_t *const *B, int64_t budget, int *choice, double *lambda_out) {
+                     const int64_t *const *B, int64_t budget, int *choice, double *lambda_out,
+                     const int *const *order) {
     std::vector<ItemHull> hulls(n);
     int64_t min_total = 0;
     for (int i = 0; i < n; ++i) {
         if (n_cand[i] <= 0) return JOLT_E_INVALID;
-        hulls[i] = build_hull(n_cand[i], cand[i], D[i], B[i]);
+        if (order && order[i]) {
+            hulls[i] = build_hull(n_cand[i], order[i], D[i], B[i]);
+        } else {
+            const std::vector<int> o = byte_order(n_cand[i], cand[i], B[i]);
+            hulls[i] = build_hull(n_cand[i], o.data(), D[i], B[i]);
+        }
         min_total += B[i][hulls[i].v[0]];
     }
     if (min_total > budget) {
@@ -150,6 +158,14 @@ void distortion_table(const double *grid /* captured energy S at (rt, rf) = (ste
         const Cand &c = cand[i];
         const double S = (c.rt == 0 || c.rf == 0) ? 0.0 : grid[(size_t)(c.rt / step - 1) * nf + (c.rf / step - 1)];
         D[i] = delta[c.bits] * std::max(0.0, normx2 - S);
+    }
+}
+
+void distortion_table_cells(const double *grid, const int *cell, double normx2, const double *delta,
+                            const std::vector<Cand> &cand, double *D) {
+    for (size_t i = 0; i < cand.size(); ++i) {
+        const double S = cell[i] < 0 ? 0.0 : grid[cell[i]];
+        D[i] = delta[cand[i].bits] * std::max(0.0, normx2 - S);
     }
 }
 

@@ -14,9 +14,17 @@ struct Cand {
 
 int64_t item_bytes_impl(int L, int H, int T, int d, int e, int rt, int rf, int bits);
 std::vector<Cand> candidate_grid(int rt_max, int rf_max, int step, uint32_t bits_mask);
+// candidate indices sorted by (bytes, rt, rf, bits)
+std::vector<int> byte_order(int nc, const Cand *cand, const int64_t *B);
+// order[i] (optional, may be null or hold nulls): item i's byte_order, when the
+// caller shares one among items of the same shape
 jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, const double *const *D,
-                     const int64_t *const *B, int64_t budget, int *choice, double *lambda_out);
+                     const int64_t *const *B, int64_t budget, int *choice, double *lambda_out,
+                     const int *const *order = nullptr);
 void distortion_table(const double *grid, int nf, int step, double normx2, const double *delta,
                       const std::vector<Cand> &cand, double *D);
+// the same with each candidate's grid cell precomputed (-1: rank 0, S = 0)
+void distortion_table_cells(const double *grid, const int *cell, double normx2, const double *delta,
+                            const std::vector<Cand> &cand, double *D);
 
 }  // namespace jolt
