@@ -18,6 +18,8 @@
 // MFMA; the block is staged in LDS first, so the product can overwrite Y.
 #include <float.h>
 
+#include <algorithm>
+
 #include "dev_common.h"
 #include "plan_kernels.h"
 #include "ktimer.h"
@@ -200,77 +202,88 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
     }
 }
 
-__global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch, int ldx, int stage_x) {
+// One wave per 32-row block tm of Q (K = 32 (tm + 1): X is lower triangular).
+// X is staged in LDS once per workgroup (zero outside the k x k triangle; read
+// from global memory when it does not fit), and the workgroup walks column
+// blocks of 64 (cb = blockIdx.x, + gridDim.x, ...): each block of Y (all P
+// rows, zero past k and len) goes through LDS, the next one is loaded into
+// registers while the current one is multiplied.
+constexpr int kApplyYS = 68;                // row stride of a staged Y block
+
+template <bool XLDS>
+__global__ __launch_bounds__(64 * kCholInverseMaxK / 32) void k_apply_linv(TrsmBatch batch, int ldx) {
     extern __shared__ float sh[];
-    constexpr int YS = 68;                  // row stride of the staged Y block
     const TrsmItem &it = batch.it[blockIdx.y];
-    const int t0 = blockIdx.x * 64;
-    if (t0 >= it.len) return;
-    const int k = it.k, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int ntm = (k + 31) >> 5, P = 32 * ntm;
-    float *Ys = sh;                         // [P][YS], rows >= k and columns past len zero
-    float *Xs = sh + P * YS;                // [P][ldx] when staged, zero outside the k x k lower triangle
-    // staging: one row per wave and pass, 64 columns by lane; loads are clamped
-    // into the buffers and the out-of-range values replaced by zeros
-    const int col = t0 + lane, colc = min(col, it.len - 1);
-#pragma unroll 8
-    for (int r = wid; r < P; r += 4)
-        Ys[r * YS + lane] = ld_or_zero(it.y, min(r, k - 1) * it.ldy + colc, r < k && col < it.len);
-    if (stage_x) {
-#pragma unroll 4
-        for (int r = wid; r < P; r += 4) {
-#pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const int c = lane + 64 * u;
-                if (c < P) Xs[r * ldx + c] = ld_or_zero(it.l, min(r, k - 1) * it.ld + min(c, k - 1), r < k && c < k);
-            }
+    const int k = it.k, ntm = (k + 31) >> 5, P = 32 * ntm, nthr = 64 * ntm;
+    const int ncb = (it.len + 63) >> 6;
+    if ((int)blockIdx.x >= ncb || (int)threadIdx.x >= nthr) return;      // whole waves leave together
+    const int tid = threadIdx.x, lane = tid & 63, tm = tid >> 6;
+    const int m32 = lane & 31, kh = lane >> 5, m = 32 * tm + m32, mc = min(m, k - 1);
+    float *ys = sh;                             // [P][kApplyYS]
+    float *xs = sh + P * kApplyYS;              // [P][ldx] when XLDS
+    if constexpr (XLDS) {
+        for (int e = tid; e < P * P / 4; e += nthr) {
+            const int r = e / (P / 4), c = 4 * (e % (P / 4));
+            const bool ok = r < k && c < k;
+            float4 v = *reinterpret_cast<const float4 *>(it.l + (size_t)(ok ? r : 0) * it.ld + (ok ? c : 0));
+            if (!ok) v = make_float4(0.f, 0.f, 0.f, 0.f);
+            float *d = xs + r * ldx + c;
+            d[0] = c < k ? v.x : 0.f;
+            d[1] = c + 1 < k ? v.y : 0.f;
+            d[2] = c + 2 < k ? v.z : 0.f;
+            d[3] = c + 3 < k ? v.w : 0.f;
         }
     }
-    __syncthreads();
-    // row blocks to waves, largest first, each to the least loaded wave (a row
-    // block tm costs tm + 1 K-steps of 32: X is lower triangular)
-    int load[4] = {0, 0, 0, 0}, mine = 0;
-    for (int tm = ntm - 1; tm >= 0; --tm) {
-        int w = 0;
+    // staging of a Y block: P rows x 16 float4 = exactly 8 pieces per thread
+    constexpr int kPer = 8;
+    float4 stg[kPer];
+    auto load_y = [&](int cb) {
+        const int c0 = cb * 64;
 #pragma unroll
-        for (int v = 1; v < 4; ++v)
-            if (load[v] < load[w]) w = v;
-        load[w] += tm + 1;
-        if (w == wid) mine |= 1 << tm;
-    }
-    const int m32 = lane & 31, kh = lane >> 5;
-    for (int tm = ntm - 1; tm >= 0; --tm) {
-        if (!(mine >> tm & 1)) continue;
-        const int m = 32 * tm + m32, mc = min(m, k - 1);
+        for (int q = 0; q < kPer; ++q) {
+            const int p = tid + nthr * q;
+            const int r = p >> 4, c = c0 + 4 * (p & 15);
+            const bool ok = r < k && c < it.len;     // len is a multiple of 4
+            const float4 v = *reinterpret_cast<const float4 *>(it.y + (size_t)(ok ? r : 0) * it.ldy + (ok ? c : 0));
+            stg[q] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto store_y = [&]() {
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int p = tid + nthr * q;
+            *reinterpret_cast<float4 *>(ys + (p >> 4) * kApplyYS + 4 * (p & 15)) = stg[q];
+        }
+    };
+    const int kend = 32 * (tm + 1);
+    const float *xrow = XLDS ? xs + m * ldx : it.l + (size_t)mc * it.ld;
+    int cb = blockIdx.x;
+    load_y(cb);
+    for (;;) {
+        __syncthreads();                        // the previous block's reads of ys are done
+        store_y();
+        __syncthreads();
+        const int next = cb + gridDim.x;
+        if (next < ncb) load_y(next);
         f32x16 acc0 = {}, acc1 = {};
-        const int kend = 32 * (tm + 1);
-        if (stage_x) {
-            const float *xr = Xs + m * ldx;
 #pragma unroll 8
-            for (int k0 = 0; k0 < kend; k0 += 2) {
-                const int kk = k0 + kh;
-                const float a = xr[kk];
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ys[kk * YS + m32], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ys[kk * YS + 32 + m32], acc1, 0, 0, 0);
-            }
-        } else {
-            const float *xr = it.l + (size_t)mc * it.ld;
-#pragma unroll 8
-            for (int k0 = 0; k0 < kend; k0 += 2) {
-                const int kk = k0 + kh;
-                const float a = ld_or_zero(xr, min(kk, k - 1), m < k && kk < k);
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ys[kk * YS + m32], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ys[kk * YS + 32 + m32], acc1, 0, 0, 0);
-            }
+        for (int k0 = 0; k0 < kend; k0 += 2) {
+            const int kk = k0 + kh;
+            const float a = XLDS ? xrow[kk] : ld_or_zero(xrow, min(kk, k - 1), m < k && kk < k);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, ys[kk * kApplyYS + m32], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, ys[kk * kApplyYS + 32 + m32], acc1, 0, 0, 0);
         }
+        const int c0 = cb * 64;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
             const int row = 32 * tm + frag_row(lane, jj);
             if (row < k) {
-                if (t0 + m32 < it.len) it.q[(size_t)row * it.ldy + t0 + m32] = acc0[jj];
-                if (t0 + 32 + m32 < it.len) it.q[(size_t)row * it.ldy + t0 + 32 + m32] = acc1[jj];
+                if (c0 + m32 < it.len) it.q[(size_t)row * it.ldy + c0 + m32] = acc0[jj];
+                if (c0 + 32 + m32 < it.len) it.q[(size_t)row * it.ldy + c0 + 32 + m32] = acc1[jj];
             }
         }
+        if (next >= ncb) break;
+        cb = next;
     }
 }
 
@@ -284,7 +297,8 @@ static hipError_t orth_lds_attrs() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
         hipError_t e = allow_lds(reinterpret_cast<const void *>(k_chol_inv));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<true>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<false>));
         state = e;
     }
     return state;
@@ -303,14 +317,19 @@ hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s) {
 hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     if (maxK > kCholInverseMaxK) return hipErrorInvalidValue;
+    for (int i = 0; i < b.n; ++i)
+        if (b.it[i].len % 4 || b.it[i].ldy % 4 || b.it[i].ld % 4) return hipErrorInvalidValue;
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
     KTimeScope kts("k_apply_linv", s);
-    const int P = (maxK + 31) / 32 * 32, ldx = P + 1;
-    size_t lds = (size_t)P * 68 * sizeof(float);
-    const size_t with_x = lds + (size_t)P * ldx * sizeof(float);
-    const int stage_x = with_x <= 150 * 1024;
-    if (stage_x) lds = with_x;
-    hipLaunchKernelGGL(k_apply_linv, dim3((maxLen + 63) / 64, b.n), dim3(256), lds, s, b, ldx, stage_x);
+    const int ntm = (maxK + 31) / 32, P = 32 * ntm, ldx = P + 1;
+    const size_t ylds = (size_t)P * kApplyYS * sizeof(float);
+    const size_t xlds = (size_t)P * ldx * sizeof(float);
+    const bool xin = ylds + xlds <= 150 * 1024;
+    // about two workgroups per CU over the batch; each walks its column blocks
+    const int ncb = (maxLen + 63) / 64;
+    const int gx = std::max(1, std::min(ncb, (512 + b.n - 1) / b.n));
+    if (xin) hipLaunchKernelGGL(k_apply_linv<true>, dim3(gx, b.n), dim3(64 * ntm), ylds + xlds, s, b, ldx);
+    else hipLaunchKernelGGL(k_apply_linv<false>, dim3(gx, b.n), dim3(64 * ntm), ylds, s, b, ldx);
     return hipGetLastError();
 }
 
