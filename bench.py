@@ -36,10 +36,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
-KERNELS = ["k_eig_tridiag", "k_chol_inv", "k_apply_linv", "k_gemm", "k_reduce", "k_xm", "k_xtq", "k_gram_rows",
-           "k_build_wt", "k_encode", "k_decode", "k_jacobi_lds"]
+KERNELS = ["k_eig_tridiag", "k_chol_inv", "k_apply_linv", "k_sym_gram", "k_gemm", "k_reduce", "k_xm", "k_xtq",
+           "k_gram_rows", "k_build_wt", "k_encode", "k_decode", "k_jacobi_lds"]
 KERNEL_SOURCE = {"k_eig_tridiag": "k_eig.hip", "k_chol_inv": "k_orth.hip", "k_apply_linv": "k_orth.hip",
-                 "k_gemm": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
+                 "k_gemm": "k_gemm.hip", "k_sym_gram": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
                  "k_encode": "k_codec.hip", "k_decode": "k_codec.hip", "k_build_wt": "k_codec.hip"}
 
 
@@ -73,6 +73,14 @@ def work_per_step(cfg, jitems, allocs):
     out["k_eig_tridiag"] = ("flops", sum((4.0 / 3 + 4.0 / 3 + 2.0) * (k ** 3 + it.d ** 3) for it in jitems))
     # CholeskyQR inverse factor: n^3 / 3 (factor) + n^3 / 3 (inverse), 2 q + 2 factorizations
     out["k_chol_inv"] = ("flops", sum((2 * q + 2) * (2.0 / 3) * k ** 3 for _ in jitems))
+    # CholeskyQR Grams and B B^T (symmetric: k (k + 1) len flops each) and the L^-1
+    # applies (triangular: k (k + 1) len): T-long panels 1 + 2 q times (the last
+    # twice), n-long panels q times, plus B B^T over n
+    passes_t = q + 2
+    out["k_sym_gram"] = ("flops", sum(k * (k + 1) * (passes_t * it.T + (q + 1) * n) for n, it in zip(n_lhd, jitems)))
+    out["k_apply_linv"] = ("flops", sum(k * (k + 1) * (passes_t * it.T + q * n) for n, it in zip(n_lhd, jitems)))
+    # U_t = Q U~ and P = U~^T B
+    out["k_gemm"] = ("flops", sum(2 * cfg.rt_max * k * (it.T + n) for n, it in zip(n_lhd, jitems)))
     # decode: payload in, dense out; encode: dense in, codes + scales out (+ stored params)
     dec = enc = 0
     for it, a in zip(jitems, allocs):

@@ -1,5 +1,6 @@
-// Generic batched fp32 GEMM of the planner (Gram of sketch panels, B B^T,
-// core projection, U_t = Q U~, block-Jacobi rotations) on fp32 MFMA.
+// Batched fp32 GEMMs of the planner on fp32 MFMA: a generic one (core
+// projection, U_t = Q U~, block-Jacobi rotations) and the symmetric Gram of the
+// rows of a panel (CholeskyQR Grams, B B^T).
 //
 // One workgroup computes a 64 x 64 tile of C (4 waves, 2 x 2 tiles of 32 x 32 on
 // v_mfma_f32_32x32x2f32).  K is staged through LDS 32 deep; the next slice is
@@ -90,6 +91,106 @@ __global__ __launch_bounds__(256) void k_gemm(GemmBatch batch, int maxSplit) {
             const int gi = i0 + wm * 32 + frag_row(lane, jj);
             if (gi < it.M) c[(int64_t)gi * it.c_i + (int64_t)gj * it.c_j] = acc[jj];
         }
+}
+
+// ---------------------------------------------------------------- symmetric Gram
+// WG (8 waves) per (split, item): the split's columns of Y go through LDS in
+// chunks of 64 (P rows, zero past k and len; the next chunk is loaded into
+// registers meanwhile); wave w owns upper tiles (tm <= tn) w, w + 8, w + 16 of
+// the 32 x 32 tile grid, whose MFMA operands are both rows of the staged chunk.
+constexpr int kSgKC = 64, kSgPitch = kSgKC + 1;
+
+__global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
+    extern __shared__ float ysg[];          // [P][kSgPitch]
+    const SymGramItem &it = batch.it[blockIdx.y];
+    const int sp = blockIdx.x;
+    if (sp >= it.nsplit) return;
+    const int k = it.k, ntm = (k + 31) >> 5, P = 32 * ntm, ntiles = ntm * (ntm + 1) / 2;
+    const int tb = sp * it.chunk, te = min(it.len, tb + it.chunk);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, m32 = lane & 31, kh = lane >> 5;
+    int tmv[3], tnv[3];
+    bool tv[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        int t = wid + 8 * u, tm = 0;
+        tv[u] = t < ntiles;
+        if (!tv[u]) t = 0;
+        while (t >= ntm - tm) {
+            t -= ntm - tm;
+            ++tm;
+        }
+        tmv[u] = tm;
+        tnv[u] = tm + t;
+    }
+    constexpr int kPieces = (kSymGramMaxK * kSgKC / 4 + 511) / 512;     // float4 per thread
+    float4 stg[kPieces];
+    auto load = [&](int t0) {
+#pragma unroll
+        for (int q = 0; q < kPieces; ++q) {
+            const int p = tid + 512 * q;
+            const int r = p >> 4, c = t0 + 4 * (p & 15);
+            const bool ok = r < k && c < te;                 // te is a multiple of 4
+            const float4 v = *reinterpret_cast<const float4 *>(it.y + (size_t)(ok ? r : 0) * it.ldy + (ok ? c : 0));
+            stg[q] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int q = 0; q < kPieces; ++q) {
+            const int p = tid + 512 * q;
+            if (p < P * (kSgKC / 4)) {
+                float *d = ysg + (p >> 4) * kSgPitch + 4 * (p & 15);
+                d[0] = stg[q].x;
+                d[1] = stg[q].y;
+                d[2] = stg[q].z;
+                d[3] = stg[q].w;
+            }
+        }
+    };
+    f32x16 acc[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) acc[u] = f32x16{};
+    if (tb < te) load(tb);
+    for (int t0 = tb; t0 < te; t0 += kSgKC) {
+        __syncthreads();
+        store();
+        __syncthreads();
+        if (t0 + kSgKC < te) load(t0 + kSgKC);
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            if (!tv[u]) continue;
+            const float *ra = ysg + (32 * tmv[u] + m32) * kSgPitch + kh;
+            const float *rb = ysg + (32 * tnv[u] + m32) * kSgPitch + kh;
+#pragma unroll 8
+            for (int k0 = 0; k0 < kSgKC; k0 += 2)
+                acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(ra[k0], rb[k0], acc[u], 0, 0, 0);
+        }
+    }
+    float *out = it.part + (size_t)sp * it.kp * it.kp;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        if (!tv[u]) continue;
+        const int col = 32 * tnv[u] + m32;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = 32 * tmv[u] + frag_row(lane, q);
+            out[(size_t)row * it.kp + col] = acc[u][q];
+            if (tmv[u] != tnv[u]) out[(size_t)col * it.kp + row] = acc[u][q];
+        }
+    }
+}
+
+hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    if (maxK > kSymGramMaxK) return hipErrorInvalidValue;
+    for (int i = 0; i < b.n; ++i) {
+        const SymGramItem &it = b.it[i];
+        if (it.len % 4 || it.ldy % 4 || it.chunk % kSgKC || it.kp < 32 * ((it.k + 31) / 32)) return hipErrorInvalidValue;
+    }
+    KTimeScope kts("k_sym_gram", s);
+    const size_t lds = (size_t)32 * ((maxK + 31) / 32) * kSgPitch * sizeof(float);
+    hipLaunchKernelGGL(k_sym_gram, dim3(maxSplit, b.n), dim3(512), lds, s, b);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s) {

@@ -82,11 +82,13 @@ Dims dims_for(const jolt_config &cfg, const jolt_item &it, int rt_max, int rf_ma
     D.gf_P = (int)std::min<int64_t>(64, std::max<int64_t>(1, rows / 512));
     D.gf_chunk = round_up((int)((rows + D.gf_P - 1) / D.gf_P), 64);
     D.gf_P = (int)((rows + D.gf_chunk - 1) / D.gf_chunk);
-    D.gT_split = clampi(D.T / 512, 1, 64);
-    D.gT_chunk = round_up((D.T + D.gT_split - 1) / D.gT_split, 16);
+    // symmetric Grams of k-row panels: up to 16 splits of whole 64-column chunks
+    // (16 items x 16 splits fill the CUs)
+    D.gT_split = clampi(D.T / 64, 1, 16);
+    D.gT_chunk = round_up((D.T + D.gT_split - 1) / D.gT_split, 64);
     D.gT_split = (D.T + D.gT_chunk - 1) / D.gT_chunk;
-    D.gN_split = clampi(D.n / 512, 1, 64);
-    D.gN_chunk = round_up((D.n + D.gN_split - 1) / D.gN_split, 16);
+    D.gN_split = clampi(D.n / 64, 1, 16);
+    D.gN_chunk = round_up((D.n + D.gN_split - 1) / D.gN_split, 64);
     D.gN_split = (D.n + D.gN_chunk - 1) / D.gN_chunk;
     // about one workgroup per CU: ceil(T / 256) token tiles per item, 16 items per launch
     D.xm_split = clampi(256 / std::max(1, ((D.T + 255) / 256) * kMaxBatch), 1, 8);
@@ -427,21 +429,35 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
     return JOLT_OK;
 }
 
+// Grams of k-row panels (part[s] = partial sums of split s): the symmetric
+// kernel up to kSymGramMaxK rows, the generic GEMM beyond
+hipError_t panel_grams(const SymGramBatch &gb, int maxK, int maxS, hipStream_t st) {
+    if (maxK <= kSymGramMaxK) return launch_sym_gram(gb, maxK, maxS, st);
+    GemmBatch g{};
+    for (int i = 0; i < gb.n; ++i) {
+        const SymGramItem &s = gb.it[i];
+        GemmItem &m = g.it[g.n++];
+        m.a = s.y; m.b = s.y; m.c = s.part;
+        m.a_i = s.ldy; m.a_k = 1; m.b_k = 1; m.b_j = s.ldy;
+        m.c_i = s.kp; m.c_j = 1; m.c_split = (int64_t)s.kp * s.kp;
+        m.a_z = m.b_z = m.c_z = 0;
+        m.M = s.k; m.N = s.k; m.K = s.len; m.kchunk = s.chunk; m.nsplit = s.nsplit; m.nb = 1;
+    }
+    return launch_gemm(g, maxK, maxK, maxS, 1, st);
+}
+
 jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, const int *k,
                       const int *kp, const int *len, const int *split, const int *chunk, int passes) {
     for (int pass = 0; pass < passes; ++pass) {
-        GemmBatch gb{};
+        SymGramBatch gb{};
         ReduceBatch rb{};
         CholBatch cb{};
         TrsmBatch tb{};
         int maxK = 0, maxLen = 0, maxS = 0;
         for (int i = 0; i < nb; ++i) {
-            GemmItem &g = gb.it[gb.n++];
-            g.a = y[i]; g.b = y[i]; g.c = gpart[i];
-            g.a_i = len[i]; g.a_k = 1; g.b_k = 1; g.b_j = len[i];
-            g.c_i = kp[i]; g.c_j = 1; g.c_split = (int64_t)kp[i] * kp[i];
-            g.a_z = g.b_z = g.c_z = 0;
-            g.M = k[i]; g.N = k[i]; g.K = len[i]; g.kchunk = chunk[i]; g.nsplit = split[i]; g.nb = 1;
+            SymGramItem &g = gb.it[gb.n++];
+            g.y = y[i]; g.part = gpart[i]; g.k = k[i]; g.kp = kp[i]; g.len = len[i]; g.ldy = len[i];
+            g.chunk = chunk[i]; g.nsplit = split[i];
             ReduceItem &r = rb.it[rb.n++];
             r.part = gpart[i]; r.out = gram[i]; r.stride = (int64_t)kp[i] * kp[i]; r.count = (int64_t)kp[i] * kp[i];
             r.nsplit = split[i];
@@ -454,7 +470,7 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
             maxLen = std::max(maxLen, len[i]);
             maxS = std::max(maxS, split[i]);
         }
-        HIPCHK(launch_gemm(gb, maxK, maxK, maxS, 1, c.st), "orth gram");
+        HIPCHK(panel_grams(gb, maxK, maxS, c.st), "orth gram");
         int64_t maxCount = 0;
         for (int i = 0; i < nb; ++i) maxCount = std::max<int64_t>(maxCount, (int64_t)kp[i] * kp[i]);
         HIPCHK(launch_reduce(rb, maxCount, c.st), "orth reduce");
@@ -626,22 +642,21 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         if ((s = xtq(true))) return s;                                                      // B = Q^T A (hi + lo)
         // W = B B^T, eig
         {
-            GemmBatch gb{};
+            SymGramBatch gb{};
             ReduceBatch rb{};
             int maxK = 0, maxS = 0;
             int64_t maxCount = 0;
             for (int i = 0; i < nb; ++i) {
-                GemmItem &g = gb.it[gb.n++];
-                g.a = zv[i]; g.b = zv[i]; g.c = gpart[i];
-                g.a_i = D[i].n; g.a_k = 1; g.b_k = 1; g.b_j = D[i].n;
-                g.c_i = D[i].kp; g.c_j = 1; g.c_split = (int64_t)D[i].kp * D[i].kp;
-                g.M = g.N = D[i].k; g.K = D[i].n; g.kchunk = D[i].gN_chunk; g.nsplit = D[i].gN_split; g.nb = 1;
+                SymGramItem &g = gb.it[gb.n++];
+                g.y = zv[i]; g.part = gpart[i]; g.k = D[i].k; g.kp = D[i].kp; g.len = D[i].n; g.ldy = D[i].n;
+                g.chunk = D[i].gN_chunk; g.nsplit = D[i].gN_split;
                 ReduceItem &r = rb.it[rb.n++];
-                r.part = gpart[i]; r.out = F(S[i].wmat); r.stride = g.c_split; r.count = g.c_split; r.nsplit = g.nsplit;
+                r.part = gpart[i]; r.out = F(S[i].wmat); r.stride = (int64_t)D[i].kp * D[i].kp;
+                r.count = r.stride; r.nsplit = g.nsplit;
                 maxK = std::max(maxK, D[i].k); maxS = std::max(maxS, g.nsplit);
                 maxCount = std::max(maxCount, r.count);
             }
-            HIPCHK(launch_gemm(gb, maxK, maxK, maxS, 1, c.st), "B B^T");
+            HIPCHK(panel_grams(gb, maxK, maxS, c.st), "B B^T");
             HIPCHK(launch_reduce(rb, maxCount, c.st), "B B^T reduce");
             for (int i = 0; i < nb; ++i)
                 eigs.push_back(EigReq{F(S[i].wmat), D[i].kp, D[i].k, F(S[i].vmat), D[i].kp,

@@ -55,6 +55,18 @@ struct GemmItem {
 struct GemmBatch { GemmItem it[kMaxBatch]; int n; };
 hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s);
 
+// Symmetric Gram of the rows of Y (k x len, row stride ldy): part[s][r][c] = sum
+// over the columns t of split s (chunk columns each) of y[r][t] y[c][t], for
+// r, c < kp (rows >= k count as zero); both triangles are written.
+struct SymGramItem {
+    const float *y;
+    float *part;          // [nsplit][kp][kp]
+    int k, kp, len, ldy, chunk, nsplit;
+};
+struct SymGramBatch { SymGramItem it[kMaxBatch]; int n; };
+constexpr int kSymGramMaxK = 192;
+hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStream_t s);
+
 // out[i] = sum_s part[s * stride + i], i < count (fixed order); optional double trace
 struct ReduceItem {
     const float *part;
