@@ -239,7 +239,7 @@ static jolt_status build_wt_all(jolt_handle h, const jolt_item *items, int n, co
         PayloadLayout p = payload_layout(it, alloc[i].rt, alloc[i].rf, alloc[i].bits);
         const int rtp = round_up(p.rt, 16);
         wt_ptr[i] = ws + off;
-        off += align_up((size_t)it.L * it.H * it.d * rtp * elem_bytes(dtype), 256);
+        off += align_up((size_t)it.L * it.H * it.d * rtp * 4, 256);      // fp32, or bf16 hi + lo
         if (p.rt == 0) continue;
         const uint8_t *pay = static_cast<const uint8_t *>(payload[i]);
         WtItem &w = b.it[b.n++];

@@ -22,7 +22,7 @@ struct CodecItem {
     const void *x;          // encode input  X[LH][T][D]
     void *out;              // decode output X~[LH][T][D]
     const void *ut;         // payload U~_t [T][rt]
-    const void *wt;         // [LH][D][rtp]
+    const void *wt;         // [LH][D][rtp] (bf16: hi plane, then the lo plane)
     uint16_t *scales;       // payload scales, (LH T D / 64) bf16
     uint8_t *codes;         // payload codes, (LH T D / 64) * 8 bits bytes
     int T, LH, rt, rtp;
@@ -37,7 +37,7 @@ struct CodecBatch {
 struct WtItem {
     const void *uf;         // payload U~_f [D][rf]
     const void *core;       // payload C~ [LH][rt][rf]
-    void *wt;               // out [LH][D][rtp]
+    void *wt;               // out [LH][D][rtp] (bf16: hi plane, then the lo plane)
     int LH, rt, rf, rtp;
     uint32_t sign_bits[4];
 };

@@ -10,7 +10,9 @@
 // of 64 rotated values gets a bf16 absmax scale and b-bit symmetric codes,
 // packed as one little-endian bit stream per group (element j in bits
 // [b j, b j + b)).  The residual is taken against the reconstruction the
-// decoder forms from the stored parameters: X^_lh = U~_t W~_lh.
+// decoder forms from the stored parameters: X^_lh = U~_t W~_lh, W~_lh =
+// C~_lh U~_f^T kept to fp32 precision (for bf16 caches as a hi + lo pair of
+// bf16 planes, each of them an MFMA operand).
 //
 // Register layout of the fused kernels.  A wave owns 32 tokens of one (layer,
 // head).  X^ is an MFMA product D[f][t] = sum_k W~t[f][k] U~_t[t][k]
@@ -22,6 +24,8 @@
 // top feature bit, which leaves each lane holding one whole 64-group
 // (d = 128) or half of it (d = 64).  Group absmax and packing are then
 // in-lane, and each lane stores its group's codes contiguously.
+#include <algorithm>
+
 #include "dev_common.h"
 #include "jolt_internal.h"
 #include "ktimer.h"
@@ -173,9 +177,10 @@ __device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t *sign_bits, int 
 }
 
 // ------------------------------------------------------------------ X^ via MFMA
-// acc[mf] += sum_k wt[f][k] * ut[t][k], f = 32 mf + row, t = token of the lane
+// acc[mf] += sum_k wt[f][k] * ut[t][k], f = 32 mf + row, t = token of the lane;
+// for bf16, wt is the hi plane and wlo (same layout) the lo plane of W~
 template <typename T, int NMF>
-__device__ __forceinline__ void xhat_mfma(const T *wt, int rtp, const T *ut, int rt, int tok, bool tv,
+__device__ __forceinline__ void xhat_mfma(const T *wt, const T *wlo, int rtp, const T *ut, int rt, int tok, bool tv,
                                           int lane, f32x16 *acc) {
     const int ln = lane & 31, h = lane >> 5;
     const bool vec = (rt & 7) == 0;        // rows of U~_t are 16-byte aligned
@@ -188,8 +193,47 @@ __device__ __forceinline__ void xhat_mfma(const T *wt, int rtp, const T *ut, int
         for (int mf = 0; mf < NMF; ++mf) {
             typename Elem<T>::Frag a = load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk);
             mfma(a, b, acc[mf]);
+            if constexpr (sizeof(T) == 2) {
+                typename Elem<T>::Frag al = load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk);
+                mfma(al, b, acc[mf]);
+            }
         }
     }
+}
+
+// W~ of one (layer, head) as the X^ MFMA reads it: straight from global memory,
+// or (WL) staged once per workgroup into dynamic LDS as [planes][D][rtp + 16 B],
+// the workgroup's waves all reading that copy.  Every thread of the workgroup
+// must call this (the LDS variant ends with a barrier).
+template <typename T>
+struct WtView {
+    const T *hi, *lo;
+    int pitch;
+};
+template <typename T, int D, int NW, bool WL>
+__device__ __forceinline__ WtView<T> wt_view(const CodecItem &it, int lh) {
+    const T *g = reinterpret_cast<const T *>(it.wt);
+    WtView<T> v;
+    if constexpr (!WL) {
+        v.hi = g + (size_t)lh * D * it.rtp;
+        v.lo = g + ((size_t)it.LH + lh) * D * it.rtp;
+        v.pitch = it.rtp;
+    } else {
+        extern __shared__ __attribute__((aligned(16))) uint8_t wt_lds[];
+        constexpr int PER = 16 / sizeof(T), PLANES = sizeof(T) == 2 ? 2 : 1;
+        T *w = reinterpret_cast<T *>(wt_lds);
+        const int WP = it.rtp + PER, ppr = it.rtp / PER, total = PLANES * D * ppr;
+        for (int p = threadIdx.x; p < total; p += 64 * NW) {
+            const int pl = p / (D * ppr), rem = p - pl * D * ppr, f = rem / ppr, c = (rem - f * ppr) * PER;
+            const uint4 x = *reinterpret_cast<const uint4 *>(g + ((size_t)(pl * it.LH + lh) * D + f) * it.rtp + c);
+            *reinterpret_cast<uint4 *>(w + ((size_t)pl * D + f) * WP + c) = x;
+        }
+        __syncthreads();
+        v.hi = w;
+        v.lo = w + (size_t)D * WP;
+        v.pitch = WP;
+    }
+    return v;
 }
 
 template <typename T, int D>
@@ -202,21 +246,21 @@ struct Tile {
 };
 
 // ------------------------------------------------------------------ fused encoder
-template <typename T, int D, int BITS>
-__global__ __launch_bounds__(256) void k_encode(CodecBatch batch) {
+template <typename T, int D, int BITS, int NWV, bool WL>
+__global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
     typedef Tile<T, D> TL;
     constexpr int NMF = TL::NMF;
     constexpr int HALF = NMF / 2;
     constexpr int NE = 32 * NMF / 2 * 2 / 2;       // values per lane: 64 (d=128) or 32 (d=64)
     static_assert(NE == 16 * NMF, "layout");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * TL::RS];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NWV][32 * TL::RS];
     const Block3 blk = xcd_block();
     const CodecItem &it = batch.it[blk.z];
     const int lh = blk.y;
-    if (lh >= it.LH || blk.x * 128 >= it.T) return;
+    if (lh >= it.LH || blk.x * 32 * NWV >= it.T) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 31, h = lane >> 5;
-    const int t0 = blk.x * 128 + wave * 32;
+    const int t0 = blk.x * 32 * NWV + wave * 32;
     const int tok = t0 + ln;
     const bool tv = tok < it.T;
     uint8_t *buf = lds[wave];
@@ -241,8 +285,8 @@ __global__ __launch_bounds__(256) void k_encode(CodecBatch batch) {
     f32x16 acc[NMF];
 #pragma unroll
     for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
-    xhat_mfma<T, NMF>(reinterpret_cast<const T *>(it.wt) + (size_t)lh * D * it.rtp, it.rtp,
-                      reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+    const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
+    xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
     __syncthreads();
 
     // residual in the MFMA layout
@@ -333,20 +377,20 @@ __global__ __launch_bounds__(256) void k_encode(CodecBatch batch) {
 }
 
 // ------------------------------------------------------------------ fused decoder
-template <typename T, int D, int BITS>
-__global__ __launch_bounds__(256) void k_decode(CodecBatch batch) {
+template <typename T, int D, int BITS, int NWV, bool WL>
+__global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
     typedef Tile<T, D> TL;
     constexpr int NMF = TL::NMF;
     constexpr int HALF = NMF / 2;
     constexpr int NE = 16 * NMF;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * TL::RS];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NWV][32 * TL::RS];
     const Block3 blk = xcd_block();
     const CodecItem &it = batch.it[blk.z];
     const int lh = blk.y;
-    if (lh >= it.LH || blk.x * 128 >= it.T) return;
+    if (lh >= it.LH || blk.x * 32 * NWV >= it.T) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 31, h = lane >> 5;
-    const int t0 = blk.x * 128 + wave * 32;
+    const int t0 = blk.x * 32 * NWV + wave * 32;
     const int tok = t0 + ln;
     const bool tv = tok < it.T;
     uint8_t *buf = lds[wave];
@@ -354,8 +398,8 @@ __global__ __launch_bounds__(256) void k_decode(CodecBatch batch) {
     f32x16 acc[NMF];
 #pragma unroll
     for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
-    xhat_mfma<T, NMF>(reinterpret_cast<const T *>(it.wt) + (size_t)lh * D * it.rtp, it.rtp,
-                      reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+    const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
+    xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
 
     float r[NMF][16];
     if constexpr (BITS > 0) {
@@ -437,7 +481,8 @@ __global__ __launch_bounds__(256) void k_decode(CodecBatch batch) {
 }
 
 // ------------------------------------------------------------------ W~ construction
-// wt[lh][f][k] = s_f * round(sum_j core[lh][k][j] * uf[f][j]) for k < rt, 0 for rt <= k < rtp.
+// wt[lh][f][k] = s_f * sum_j core[lh][k][j] * uf[f][j] for k < rt, 0 for rt <= k < rtp;
+// bf16: hi plane round(v) and, LH D rtp elements further, lo plane round(v - hi).
 // One wave per (32 features, 32 ranks) tile: D[m = f][n = k] with K = j.
 template <typename T>
 __global__ __launch_bounds__(64) void k_build_wt(WtBatch batch, int D) {
@@ -486,8 +531,13 @@ __global__ __launch_bounds__(64) void k_build_wt(WtBatch batch, int D) {
             float v = (kr < it.rt) ? acc[jr] : 0.f;
             if (sizeof(T) == 2) {
                 uint16_t b = f32_to_bf16(v);
-                if (neg) b ^= 0x8000u;
+                uint16_t bl = f32_to_bf16(v - bf16_to_f32(b));
+                if (neg) {
+                    b ^= 0x8000u;
+                    bl ^= 0x8000u;
+                }
                 reinterpret_cast<uint16_t *>(wt)[(size_t)f * it.rtp + kr] = b;
+                reinterpret_cast<uint16_t *>(wt)[((size_t)it.LH * D + f) * it.rtp + kr] = bl;
             } else {
                 reinterpret_cast<float *>(wt)[(size_t)f * it.rtp + kr] = neg ? -v : v;
             }
@@ -577,51 +627,102 @@ __global__ void k_rademacher_fill(uint64_t key, uint32_t stream, uint64_t first,
 }
 
 // ------------------------------------------------------------------ launchers
+// Workgroups of NW waves x 32 tokens of one (layer, head).  bf16: 8 waves; fp32:
+// 4 (its row staging is twice as large).  W~ goes through LDS when it fits
+// beside the row staging.
 template <typename T, int D>
-static hipError_t encode_bits(const CodecBatch &b, int bits, dim3 grid, hipStream_t s) {
-    switch (bits) {
-        case 2: hipLaunchKernelGGL((k_encode<T, D, 2>), grid, dim3(256), 0, s, b); break;
-        case 3: hipLaunchKernelGGL((k_encode<T, D, 3>), grid, dim3(256), 0, s, b); break;
-        case 4: hipLaunchKernelGGL((k_encode<T, D, 4>), grid, dim3(256), 0, s, b); break;
-        case 5: hipLaunchKernelGGL((k_encode<T, D, 5>), grid, dim3(256), 0, s, b); break;
-        case 6: hipLaunchKernelGGL((k_encode<T, D, 6>), grid, dim3(256), 0, s, b); break;
-        case 7: hipLaunchKernelGGL((k_encode<T, D, 7>), grid, dim3(256), 0, s, b); break;
-        case 8: hipLaunchKernelGGL((k_encode<T, D, 8>), grid, dim3(256), 0, s, b); break;
-        default: return hipErrorInvalidValue;
+struct CodecShape {
+    static constexpr int NW = sizeof(T) == 2 ? 8 : 4;
+    static size_t wt_lds(int maxRtp) {
+        return (size_t)(sizeof(T) == 2 ? 2 : 1) * D * (maxRtp + 16 / sizeof(T)) * sizeof(T);
     }
+    static bool wl(int maxRtp) {
+        return (size_t)NW * 32 * Tile<T, D>::RS + wt_lds(maxRtp) <= 160 * 1024;
+    }
+};
+
+template <typename Kern>
+static hipError_t codec_launch(Kern k, dim3 grid, int threads, size_t lds, hipStream_t s, const CodecBatch &b) {
+    if (lds > 64 * 1024) {
+        hipFuncAttributes fa;
+        hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k));
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    160 * 1024 - (int)fa.sharedSizeBytes);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, grid, dim3(threads), lds, s, b);
     return hipGetLastError();
 }
+
+template <typename T, int D, int BITS>
+static hipError_t encode_one(const CodecBatch &b, int maxT, int maxLH, int maxRtp, hipStream_t s) {
+    using CS = CodecShape<T, D>;
+    dim3 grid((maxT + 32 * CS::NW - 1) / (32 * CS::NW), maxLH, b.n);
+    if (CS::wl(maxRtp)) return codec_launch(k_encode<T, D, BITS, CS::NW, true>, grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b);
+    return codec_launch(k_encode<T, D, BITS, CS::NW, false>, grid, 64 * CS::NW, 0, s, b);
+}
+template <typename T, int D, int BITS>
+static hipError_t decode_one(const CodecBatch &b, int maxT, int maxLH, int maxRtp, hipStream_t s) {
+    using CS = CodecShape<T, D>;
+    dim3 grid((maxT + 32 * CS::NW - 1) / (32 * CS::NW), maxLH, b.n);
+    if (CS::wl(maxRtp)) return codec_launch(k_decode<T, D, BITS, CS::NW, true>, grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b);
+    return codec_launch(k_decode<T, D, BITS, CS::NW, false>, grid, 64 * CS::NW, 0, s, b);
+}
+
 template <typename T, int D>
-static hipError_t decode_bits(const CodecBatch &b, int bits, dim3 grid, hipStream_t s) {
+static hipError_t encode_bits(const CodecBatch &b, int bits, int maxT, int maxLH, int maxRtp, hipStream_t s) {
     switch (bits) {
-        case 0: hipLaunchKernelGGL((k_decode<T, D, 0>), grid, dim3(256), 0, s, b); break;
-        case 2: hipLaunchKernelGGL((k_decode<T, D, 2>), grid, dim3(256), 0, s, b); break;
-        case 3: hipLaunchKernelGGL((k_decode<T, D, 3>), grid, dim3(256), 0, s, b); break;
-        case 4: hipLaunchKernelGGL((k_decode<T, D, 4>), grid, dim3(256), 0, s, b); break;
-        case 5: hipLaunchKernelGGL((k_decode<T, D, 5>), grid, dim3(256), 0, s, b); break;
-        case 6: hipLaunchKernelGGL((k_decode<T, D, 6>), grid, dim3(256), 0, s, b); break;
-        case 7: hipLaunchKernelGGL((k_decode<T, D, 7>), grid, dim3(256), 0, s, b); break;
-        case 8: hipLaunchKernelGGL((k_decode<T, D, 8>), grid, dim3(256), 0, s, b); break;
+        case 2: return encode_one<T, D, 2>(b, maxT, maxLH, maxRtp, s);
+        case 3: return encode_one<T, D, 3>(b, maxT, maxLH, maxRtp, s);
+        case 4: return encode_one<T, D, 4>(b, maxT, maxLH, maxRtp, s);
+        case 5: return encode_one<T, D, 5>(b, maxT, maxLH, maxRtp, s);
+        case 6: return encode_one<T, D, 6>(b, maxT, maxLH, maxRtp, s);
+        case 7: return encode_one<T, D, 7>(b, maxT, maxLH, maxRtp, s);
+        case 8: return encode_one<T, D, 8>(b, maxT, maxLH, maxRtp, s);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+}
+template <typename T, int D>
+static hipError_t decode_bits(const CodecBatch &b, int bits, int maxT, int maxLH, int maxRtp, hipStream_t s) {
+    switch (bits) {
+        case 0: return decode_one<T, D, 0>(b, maxT, maxLH, maxRtp, s);
+        case 2: return decode_one<T, D, 2>(b, maxT, maxLH, maxRtp, s);
+        case 3: return decode_one<T, D, 3>(b, maxT, maxLH, maxRtp, s);
+        case 4: return decode_one<T, D, 4>(b, maxT, maxLH, maxRtp, s);
+        case 5: return decode_one<T, D, 5>(b, maxT, maxLH, maxRtp, s);
+        case 6: return decode_one<T, D, 6>(b, maxT, maxLH, maxRtp, s);
+        case 7: return decode_one<T, D, 7>(b, maxT, maxLH, maxRtp, s);
+        case 8: return decode_one<T, D, 8>(b, maxT, maxLH, maxRtp, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+static int max_rtp(const CodecBatch &b) {
+    int m = 0;
+    for (int i = 0; i < b.n; ++i) m = std::max(m, b.it[i].rtp);
+    return m;
 }
 
 hipError_t launch_encode(const CodecBatch &b, int dtype, int D, int bits, int maxT, int maxLH, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     KTimeScope kts("k_encode", s);
-    dim3 grid((maxT + 127) / 128, maxLH, b.n);
-    if (dtype == JOLT_BF16) return D == 128 ? encode_bits<uint16_t, 128>(b, bits, grid, s)
-                                            : encode_bits<uint16_t, 64>(b, bits, grid, s);
-    return D == 128 ? encode_bits<float, 128>(b, bits, grid, s) : encode_bits<float, 64>(b, bits, grid, s);
+    const int r = max_rtp(b);
+    if (dtype == JOLT_BF16)
+        return D == 128 ? encode_bits<uint16_t, 128>(b, bits, maxT, maxLH, r, s)
+                        : encode_bits<uint16_t, 64>(b, bits, maxT, maxLH, r, s);
+    return D == 128 ? encode_bits<float, 128>(b, bits, maxT, maxLH, r, s)
+                    : encode_bits<float, 64>(b, bits, maxT, maxLH, r, s);
 }
 hipError_t launch_decode(const CodecBatch &b, int dtype, int D, int bits, int maxT, int maxLH, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     KTimeScope kts("k_decode", s);
-    dim3 grid((maxT + 127) / 128, maxLH, b.n);
-    if (dtype == JOLT_BF16) return D == 128 ? decode_bits<uint16_t, 128>(b, bits, grid, s)
-                                            : decode_bits<uint16_t, 64>(b, bits, grid, s);
-    return D == 128 ? decode_bits<float, 128>(b, bits, grid, s) : decode_bits<float, 64>(b, bits, grid, s);
+    const int r = max_rtp(b);
+    if (dtype == JOLT_BF16)
+        return D == 128 ? decode_bits<uint16_t, 128>(b, bits, maxT, maxLH, r, s)
+                        : decode_bits<uint16_t, 64>(b, bits, maxT, maxLH, r, s);
+    return D == 128 ? decode_bits<float, 128>(b, bits, maxT, maxLH, r, s)
+                    : decode_bits<float, 64>(b, bits, maxT, maxLH, r, s);
 }
 hipError_t launch_build_wt(const WtBatch &b, int dtype, int D, int maxLH, int maxRtp, hipStream_t s) {
     if (b.n <= 0 || maxRtp <= 0) return hipSuccess;

@@ -65,7 +65,7 @@ size_t codec_ws_bytes_for(const jolt_item *items, int n, const int *rt) {
     size_t s = 0;
     for (int i = 0; i < n; ++i) {
         const int rtp = round_up(rt[i], 16);
-        s += align_up((size_t)items[i].L * items[i].H * items[i].d * rtp * elem_bytes(items[i].dtype), 256);
+        s += align_up((size_t)items[i].L * items[i].H * items[i].d * rtp * 4, 256);   // fp32, or bf16 hi + lo
     }
     return s;
 }

@@ -1,16 +1,22 @@
 """ORACLE (test infrastructure only): stored parameters, residual codec, decode.
 
 Pages: the truncation residual is captured by a rotated low-bit quantizer
-(landing page abstract); the rotation is a Johnson-Lindenstrauss rotation
-(vendor page; author page abstract: "restores the energy that truncation
-discards with a JL rotated low-bit residual").  Errors are reported on the
+(landing page abstract); the rotation is a Johnson-Lindenstrauss rotation,
+and the quantized, rotated residual gives back energy that the truncation
+dropped (vendor page; author page abstract).  Errors are reported on the
 reconstructed cache (relative Frobenius error, author page abstract).
 
 Readings:
   * stored Tucker parameters are the leading blocks U_t[:, :r_t], U_f[:, :r_f],
     C[:, :, :r_t, :r_f], rounded (RNE) to the parameter dtype (bf16; fp32 for
     fp32 caches);
-  * the decoder forms W_lh = round(C_lh U_f^T) (r_t x d) and X^_lh = U_t W_lh;
+  * the decoder forms X^_lh = U_t W_lh from the stored parameters, with the
+    inner product W_lh = C_lh U_f^T (r_t x d) held to fp32 precision: rounded to
+    fp32 for fp32 caches, and for bf16 caches as the bf16 pair hi = round(W),
+    lo = round(W - hi) (W to about 2^-17).  The pages fix no intermediate
+    precision; a single bf16 rounding of W would let the two sides' W differ by
+    a bf16 step wherever their accumulations straddle a rounding boundary,
+    while a hi + lo pair that straddles one changes by a lo step only;
   * the residual is closed-loop: R = X - X^ with X^ exactly as the decoder
     will rebuild it from the stored, rounded parameters;
   * output is rounded (RNE) to the cache dtype.
@@ -58,12 +64,17 @@ def stored_params(U_t, U_f, C_full, rt: int, rf: int, dtype: str) -> StoredParam
 
 
 def low_rank(p: StoredParams, L: int, H: int, T: int, d: int, dtype: str) -> np.ndarray:
-    """X^ as the decoder rebuilds it: X^_lh = U_t round(C_lh U_f^T)."""
+    """X^ as the decoder rebuilds it: X^_lh = U_t W_lh, W_lh = C_lh U_f^T at fp32
+    precision (bf16 caches: hi + lo bf16 pair)."""
     rt = p.Ut.shape[1]
     if rt == 0:
         return np.zeros((L, H, T, d))
-    rnd = param_round(dtype)
-    W = rnd(np.matmul(p.C, p.Uf.T[None, None]))          # L x H x rt x d
+    W = np.matmul(p.C, p.Uf.T[None, None])               # L x H x rt x d
+    if dtype == "f32":
+        W = quant.round_f32(W)
+    else:
+        hi = quant.round_bf16(W)
+        W = hi + quant.round_bf16(W - hi)
     return np.matmul(p.Ut[None, None], W)
 
 

@@ -5,8 +5,11 @@ input (rotation signs, sketch signs, quantized codes, scales, packing); within
 fp32 rounding for the rotation; and for the fused encoder / decoder:
   * fed the oracle's stored parameters, the fused encoder's codes may differ
     from the oracle's only where its fp32 residual sits on a rounding boundary
-    (fraction <= 1e-4 of codes), and the reconstruction differs from the
-    oracle's by <= 1e-3 relative Frobenius;
+    (<= 1e-4 of codes and 1e-3 of scales, or at most 8 codes and 2 scales); the
+    fused decoder's output of
+    those codes is the oracle's decode of the same codes to 1e-3 relative
+    Frobenius (and, with no residual, the oracle's reconstruction itself); the
+    reconstruction error is at most 1.05 x the oracle's + 1e-4;
   * decoding the oracle's own payload matches the oracle's decode to 1e-3.
 Both sides' outputs are compared after the same final rounding to the cache dtype.
 """
@@ -120,7 +123,7 @@ def test_fused_codec_parity(env, case):
     al = jb.jolt_alloc(rt, rf, bits, 0, 0, 0.0)
     off, total = jb.jolt_payload_layout(jit, al)
     xdev = to_device(it, torch)
-    codec_bytes = max(256, L * H * d * ((rt + 15) // 16 * 16) * (4 if dtype == "f32" else 2) + 256)
+    codec_bytes = max(256, L * H * d * ((rt + 15) // 16 * 16) * 4 + 256)     # W~: fp32, or bf16 hi + lo
     ws = torch.empty(codec_bytes, dtype=torch.uint8, device="cuda")
     # (a) GPU encode of the oracle's stored parameters
     pay = to_dev_bytes(payload_bytes(jb, jit, al, sp, dtype), torch)
@@ -137,12 +140,20 @@ def test_fused_codec_parity(env, case):
         wd = np.frombuffer(section(host, off, total, 4)[:8 * bits * G], dtype="<u8").reshape(G, bits)
         u_gpu = oquant.unpack_codes(wd, bits)
         u_ref = oquant.unpack_codes(enc.words, bits)
-        code_mismatch = np.mean(u_gpu != u_ref)
-        scale_mismatch = np.mean(sc != enc.scale_bits)
-        assert code_mismatch <= 1e-4, code_mismatch
-        assert scale_mismatch <= 1e-3, scale_mismatch
+        # boundary cases: a fraction of the values, with a small absolute
+        # allowance for small tensors
+        assert np.sum(u_gpu != u_ref) <= max(1e-4 * u_ref.size, 8), np.mean(u_gpu != u_ref)
+        assert np.sum(sc != enc.scale_bits) <= max(1e-3 * G, 2), np.mean(sc != enc.scale_bits)
     got = out_values(out, dtype)
-    assert rel(got, ref) <= 1e-3
+    if bits:
+        # the decode of the GPU's own codes and scales is the oracle's decode of them
+        # (a residual value at a rounding boundary may take the neighbouring code
+        # on either side: the encoders form it in fp32 and fp64 respectively;
+        # those cases are bounded by the fractions above)
+        own = ocodec.Encoded(rt, rf, bits, sp, wd, sc, None)
+        assert rel(got, ocodec.decode(own, L, H, T, d, it.seed, it.item_id, dtype)) <= 1e-3
+    else:
+        assert rel(got, ref) <= 1e-3
     # the reconstruction error is the oracle's, up to the same tolerance
     err_gpu, err_ref = rel(got, X), rel(ref, X)
     assert err_gpu <= 1.05 * err_ref + 1e-4

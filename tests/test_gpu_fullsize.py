@@ -1,0 +1,204 @@
+"""GPU checks of the whole path at the workloads' full item sizes, where the fp64
+oracle cannot process whole items: properties that hold at any size, and the
+oracle run on sampled blocks of rows from the GPU's own stored parameters.
+
+Per item:
+  * U_t and U_f orthonormal, eigenvalues descending and non-negative;
+  * ||X||^2 (the trace of the fp32 feature Gram, summed in fp64) against an fp64
+    sum on the host (rel 1e-5);
+  * the feature eigenvalues sum to ||X||^2 (they are the eigenvalues of the
+    feature Gram, whose trace is ||X||^2);
+  * row i of the energy table sums to the token eigenvalue lambda_i: the row is
+    u_i^T A A^T u_i split over the d features (A the token unfolding), and the
+    table's total is at most ||X||^2;
+  * the allocation fits the budget and reports the bytes jolt_item_bytes gives;
+  * codec on sampled row blocks: the oracle encodes the block (token rows of one
+    (layer, head)) from the GPU's stored U_t, U_f and core; codes and scales
+    agree to the codec parity test's fractions, the GPU's decoded block is the
+    oracle's decode of the GPU's codes (rel 1e-3), and its error is at most
+    1.05 x the oracle's + 1e-4;
+  * the reconstruction error is at most the plain truncation error
+    sqrt(||X||^2 - S(r_t, r_f)) / ||X|| (quantizing the residual only removes
+    energy), up to bf16 rounding of the stored values and of the output;
+  * a second plan gives bit-identical factors and the same allocation.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codec as ocodec
+from oracle import quant as oquant
+from tests.gpu_util import jolt_binding, rel, section, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+_HIP = None
+
+
+def _hip():
+    global _HIP
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _HIP.hipMemcpy.restype = ctypes.c_int
+    return _HIP
+
+
+def _fetch(torch, ptr, count, dtype=np.float32):
+    torch.cuda.synchronize()
+    out = np.empty(count, dtype=dtype)
+    assert _hip().hipMemcpy(out.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(ptr), out.nbytes, 2) == 0
+    return out
+
+
+def _bf16_to_f64(u16):
+    return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _delta():
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    return json.load(open(os.path.join(root, "tests", "golden", "delta_b.json")))["delta"]
+
+
+def _items(cfg, picks):
+    specs = synth.item_specs(cfg)
+    return [synth.make_item(cfg, specs[i]) for i in picks]
+
+
+def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=None):
+    torch = torch_cuda()
+    jb = jolt_binding()
+    items = _items(cfg, picks)
+    L, H, T, d = cfg.L, cfg.H, cfg.T, cfg.d
+    budget = synth.budget_for_ratio(cfg, ratio, n_items=len(items))
+    jitems = [jb.make_item(it.L, it.H, it.T, it.d, cfg.dtype, it.item_id, it.seed) for it in items]
+    jcfg = jb.make_config(mode, rt_max=cfg.rt_max, oversample=cfg.oversample, power_iters=cfg.power_iters,
+                          rank_step=cfg.rank_step, bits=cfg.bits, budget=budget, delta=_delta())
+    J = jb.Jolt(jcfg, jitems)
+    xs = [torch.from_numpy(it.raw.view(np.int16).copy()).cuda() for it in items]
+    print("full size", cfg.name, len(items), "items", (L, H, T, d), mode, "ratio", ratio, flush=True)
+    allocs, lam = J.plan(xs)
+    assert J.status == jb.JOLT_OK, J.status
+    assert sum(a.bytes for a in allocs) <= budget
+    rt_max = cfg.rt_max
+    check = range(len(items)) if check_items is None else check_items
+    factors = {}
+    for i in check:
+        it, a = items[i], allocs[i]
+        assert a.bytes == jb.jolt_item_bytes(jitems[i], a.rt, a.rf, a.bits)
+        v = J.factors(i)
+        Ut = _fetch(torch, v.ut, rt_max * T).reshape(rt_max, T)
+        Uf = _fetch(torch, v.uf, d * d).reshape(d, d)
+        lam_t = _fetch(torch, v.lam_t, rt_max).astype(np.float64)
+        lam_f = _fetch(torch, v.lam_f, d).astype(np.float64)
+        nx2 = _fetch(torch, v.normx2, 1, np.float64)[0]
+        E = _fetch(torch, v.energy, rt_max * d).reshape(rt_max, d).astype(np.float64)
+        factors[i] = (Ut, Uf, lam_t, lam_f, E)
+        ref_nx2 = float(np.sum(it.x * it.x))
+        assert abs(nx2 / ref_nx2 - 1) < 1e-5, (nx2, ref_nx2)
+        Ut64 = Ut.astype(np.float64)
+        assert np.max(np.abs(Ut64 @ Ut64.T - np.eye(rt_max))) < 1e-3
+        assert np.max(np.abs(Uf.T.astype(np.float64) @ Uf - np.eye(d))) < 1e-4
+        assert np.all(np.diff(lam_t) <= 1e-6 * lam_t[0]) and np.all(np.diff(lam_f) <= 1e-6 * lam_f[0])
+        assert lam_t[-1] >= -1e-5 * lam_t[0] and lam_f[-1] >= -1e-5 * lam_f[0]
+        assert abs(lam_f.sum() / ref_nx2 - 1) < 1e-4
+        assert np.all(np.abs(E.sum(axis=1) - lam_t) <= 1e-4 * lam_t[0] + 1e-4 * np.abs(lam_t))
+        assert E.min() >= -1e-6 * E.max() and E.sum() <= ref_nx2 * (1 + 1e-5)
+    pays = J.alloc_payloads(allocs)
+    J.compress(xs, pays, allocs)
+    outs = [torch.empty_like(x) for x in xs]
+    J.decompress(pays, outs, allocs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1234)
+    for i in check:
+        it, a, jit = items[i], allocs[i], jitems[i]
+        Ut, Uf, lam_t, lam_f, E = factors[i]
+        # whole-item error against the truncation bound
+        x_dev = xs[i]
+        xf = (x_dev.to(torch.int32) << 16).view(torch.float32).double()
+        of = (outs[i].to(torch.int32) << 16).view(torch.float32).double()
+        err = float(torch.linalg.vector_norm(of - xf) / torch.linalg.vector_norm(xf))
+        S = E[:a.rt, :a.rf].sum() if a.rt and a.rf else 0.0
+        nx2 = float(torch.sum(xf * xf))
+        trunc = np.sqrt(max(nx2 - S, 0.0) / nx2)
+        print("item", it.item_id, "alloc", (a.rt, a.rf, a.bits), "error", err, "truncation", trunc, flush=True)
+        assert err <= 1.05 * trunc + 6e-3
+        # sampled row blocks through the oracle's codec, from the GPU's stored parameters
+        off, total = jb.jolt_payload_layout(jit, a)
+        ends = list(off[1:]) + [total]
+        pay = pays[i]
+
+        def sec(k, nbytes):
+            return pay[off[k]:off[k] + nbytes].cpu().numpy()
+        rt, rf = (a.rt, a.rf) if a.rt and a.rf else (0, 0)
+        Ut_s = _bf16_to_f64(sec(0, 2 * T * rt).view("<u2")).reshape(T, rt) if rt else np.zeros((T, 0))
+        Uf_s = _bf16_to_f64(sec(1, 2 * d * rf).view("<u2")).reshape(d, rf) if rf else np.zeros((d, 0))
+        C_s = _bf16_to_f64(sec(2, 2 * L * H * rt * rf).view("<u2")).reshape(L, H, rt, rf)
+        assert ends[-1] == total
+        ns = min(T, 2048)
+        for _ in range(blocks_per_item):
+            l, h = int(rng.integers(L)), int(rng.integers(H))
+            t0 = int(rng.integers(0, T - ns + 1)) // 64 * 64
+            Xb = it.x[l:l + 1, h:h + 1, t0:t0 + ns]
+            sp = ocodec.StoredParams(Ut=Ut_s[t0:t0 + ns], Uf=Uf_s, C=C_s[l:l + 1, h:h + 1])
+            enc = ocodec.encode(Xb, sp, a.bits, it.seed, it.item_id, cfg.dtype)
+            ref = ocodec.decode(enc, 1, 1, ns, d, it.seed, it.item_id, cfg.dtype)
+            got_u16 = outs[i][l, h, t0:t0 + ns].cpu().numpy().view(np.uint16)
+            got = _bf16_to_f64(got_u16).reshape(1, 1, ns, d)
+            assert rel(got, Xb) <= 1.05 * rel(ref, Xb) + 1e-4
+            own = ref
+            if a.bits:
+                G0 = ((l * H + h) * T + t0) * (d // 64)
+                Gb = ns * d // 64
+                sc = np.frombuffer(pay[off[3] + 2 * G0:off[3] + 2 * (G0 + Gb)].cpu().numpy().tobytes(), dtype="<u2")
+                wd = np.frombuffer(pay[off[4] + 8 * a.bits * G0:off[4] + 8 * a.bits * (G0 + Gb)].cpu().numpy()
+                                   .tobytes(), dtype="<u8").reshape(Gb, a.bits)
+                u_gpu, u_ref = oquant.unpack_codes(wd, a.bits), oquant.unpack_codes(enc.words, a.bits)
+                assert np.sum(u_gpu != u_ref) <= max(1e-4 * u_ref.size, 8), np.mean(u_gpu != u_ref)
+                assert np.sum(sc != enc.scale_bits) <= max(1e-3 * Gb, 2), np.mean(sc != enc.scale_bits)
+                own = ocodec.decode(ocodec.Encoded(rt, rf, a.bits, sp, wd, sc, None), 1, 1, ns, d, it.seed,
+                                    it.item_id, cfg.dtype)
+            assert rel(got, own) <= 1e-3, dict(block=(l, h, t0), gpu_vs_oracle=rel(got, ref))
+    # a second plan: bit-identical factors, the same allocation
+    allocs2, lam2 = J.plan(xs)
+    assert [(a.rt, a.rf, a.bits) for a in allocs2] == [(a.rt, a.rf, a.bits) for a in allocs] and lam2 == lam
+    for i in check:
+        v = J.factors(i)
+        assert np.array_equal(_fetch(torch, v.ut, rt_max * T).reshape(rt_max, T), factors[i][0])
+        assert np.array_equal(_fetch(torch, v.uf, d * d).reshape(d, d), factors[i][1])
+    J.close()
+    return allocs
+
+
+@pytest.mark.timeout(600)
+def test_fullsize_mistral_c2_all_items():
+    """The bench workload itself: 16 items of 4 x 8 x 1024 x 128, randomized, 2x."""
+    cfg = synth.config("mistral7b_gqa_1k")
+    _run(cfg, list(range(cfg.n_items)), 2.0, blocks_per_item=1, check_items=[0, 1, 7, 15])
+
+
+@pytest.mark.timeout(600)
+def test_fullsize_llama2_13b_c3_item():
+    """One 4 x 40 x 4096 x 128 item (k = 266), 3x."""
+    cfg = synth.config("llama2_13b_mha_4k")
+    _run(cfg, [0], 3.0)
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_llama31_8b_c4_item():
+    """One 4 x 8 x 65536 x 128 item (537 MB), 2x."""
+    cfg = synth.config("llama31_8b_gqa_64k")
+    _run(cfg, [0], 2.0)
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_moe_c5_items_shared_dual():
+    """18 items of 4 x 8 x 8192 x 128 from two sequences (different planted
+    token ranks) under one dual: crosses the 16-item launch batch."""
+    cfg = synth.config("moe_gqa_batch16_8k")
+    picks = list(range(0, 9)) + list(range(cfg.items_per_sequence, cfg.items_per_sequence + 9))
+    _run(cfg, picks, 2.5, blocks_per_item=1, check_items=[0, 8, 9, 17])
