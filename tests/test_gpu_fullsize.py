@@ -202,3 +202,10 @@ def test_fullsize_moe_c5_items_shared_dual():
     cfg = synth.config("moe_gqa_batch16_8k")
     picks = list(range(0, 9)) + list(range(cfg.items_per_sequence, cfg.items_per_sequence + 9))
     _run(cfg, picks, 2.5, blocks_per_item=1, check_items=[0, 8, 9, 17])
+
+
+@pytest.mark.timeout(600)
+def test_fullsize_mistral_c2_exact_items():
+    """Exact token mode (the T x T token Gram's eigenvectors) on two full c2 items."""
+    cfg = synth.config("mistral7b_gqa_1k")
+    _run(cfg, [0, 1], 2.0, mode="exact")
