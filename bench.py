@@ -121,7 +121,7 @@ def pmc_traffic(kernel, workload):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (items shard across GPUs "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (items shard across GPUs "
               "with one table all-gather; not built)", file=sys.stderr)
         return 2
     if args.profile:

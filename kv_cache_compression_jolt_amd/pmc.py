@@ -29,7 +29,7 @@ import sys
 COPY_BYTES = 512 * 1024 * 1024
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = {"k_eig_tridiag": "k_eig.hip", "k_chol_inv": "k_orth.hip", "k_apply_linv": "k_orth.hip",
-           "k_gemm": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
+           "k_gemm": "k_gemm.hip", "k_sym_gram": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
            "k_encode": "k_codec.hip", "k_decode": "k_codec.hip", "k_build_wt": "k_codec.hip"}
 
 
@@ -44,14 +44,19 @@ def copy_kernel():
     print("copied %d bytes x 3" % COPY_BYTES)
 
 
-def _rows(d):
-    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+def _newest(d, suffix):
+    """Most recent rocprofv3 output file of one kind under d (an output
+    folder reused by several runs holds one file per run)."""
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
     if not files:
-        raise SystemExit("no counter_collection.csv under %s" % d)
+        raise SystemExit("no %s under %s" % (suffix, d))
+    return max(files, key=os.path.getmtime)
+
+
+def _rows(d):
     out = []
-    for f in files:
-        with open(f, newline="") as fh:
-            out.extend(csv.DictReader(fh))
+    with open(_newest(d, "counter_collection.csv"), newline="") as fh:
+        out.extend(csv.DictReader(fh))
     return out
 
 
@@ -100,11 +105,8 @@ def summarize(d, kernel, workload, commands):
 
 
 def trace_summary(d, out, title, command):
-    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    if not files:
-        raise SystemExit("no kernel_stats.csv under %s" % d)
     rows = []
-    with open(files[0], newline="") as fh:
+    with open(_newest(d, "kernel_stats.csv"), newline="") as fh:
         for r in csv.DictReader(fh):
             rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3,
                          float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
