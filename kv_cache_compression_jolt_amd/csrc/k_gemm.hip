@@ -166,17 +166,25 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
                 acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(ra[k0], rb[k0], acc[u], 0, 0, 0);
         }
     }
+    // each tile in place, and off-diagonal tiles mirrored through a 32 x 33
+    // LDS transpose per wave, so both stores run along rows of the partial
     float *out = it.part + (size_t)sp * it.kp * it.kp;
+    __syncthreads();                            // every wave is done with the staged chunk
+    float *tr = ysg + wid * (32 * 33);
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         if (!tv[u]) continue;
-        const int col = 32 * tnv[u] + m32;
+        const int r0 = 32 * tmv[u], c0 = 32 * tnv[u];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int row = 32 * tmv[u] + frag_row(lane, q);
-            out[(size_t)row * it.kp + col] = acc[u][q];
-            if (tmv[u] != tnv[u]) out[(size_t)col * it.kp + row] = acc[u][q];
-        }
+        for (int q = 0; q < 16; ++q) out[(size_t)(r0 + frag_row(lane, q)) * it.kp + c0 + m32] = acc[u][q];
+        if (r0 == c0) continue;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) tr[frag_row(lane, q) * 33 + m32] = acc[u][q];
+        wave_lds_sync();
+#pragma unroll
+        for (int b = 0; b < 32; b += 2)             // mirror row c0 + b + kh: tile column b + kh
+            out[(size_t)(c0 + b + kh) * it.kp + r0 + m32] = tr[m32 * 33 + b + kh];
+        wave_lds_sync();
     }
 }
 
@@ -188,7 +196,8 @@ hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStr
         if (it.len % 4 || it.ldy % 4 || it.chunk % kSgKC || it.kp < 32 * ((it.k + 31) / 32)) return hipErrorInvalidValue;
     }
     KTimeScope kts("k_sym_gram", s);
-    const size_t lds = (size_t)32 * ((maxK + 31) / 32) * kSgPitch * sizeof(float);
+    // the staged chunk, or 8 waves' 32 x 33 transpose tiles, whichever is larger
+    const size_t lds = std::max<size_t>((size_t)32 * ((maxK + 31) / 32) * kSgPitch, 8 * 32 * 33) * sizeof(float);
     hipLaunchKernelGGL(k_sym_gram, dim3(maxSplit, b.n), dim3(512), lds, s, b);
     return hipGetLastError();
 }

@@ -407,13 +407,33 @@ __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
 }
 
 // ====================================================================== split reduction
+// Sums of split partials in split order (the same order every run): four
+// consecutive entries per thread, with float4 accesses when the item's
+// pointers and stride allow them.
 __global__ void k_reduce(ReduceBatch batch) {
     const ReduceItem &it = batch.it[blockIdx.y];
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
     if (i >= it.count) return;
-    float s = 0.f;
-    for (int p = 0; p < it.nsplit; ++p) s += it.part[(int64_t)p * it.stride + i];
-    it.out[i] = s;
+    const bool vec = i + 4 <= it.count && it.stride % 4 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(it.part) | reinterpret_cast<uintptr_t>(it.out)) & 15) == 0;
+    if (vec) {
+        float4 s = *reinterpret_cast<const float4 *>(it.part + i);
+#pragma unroll 4
+        for (int p = 1; p < it.nsplit; ++p) {
+            const float4 v = *reinterpret_cast<const float4 *>(it.part + (int64_t)p * it.stride + i);
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
+        }
+        *reinterpret_cast<float4 *>(it.out + i) = s;
+    } else {
+        for (int64_t e = i; e < i + 4 && e < it.count; ++e) {
+            float s = 0.f;
+            for (int p = 0; p < it.nsplit; ++p) s += it.part[(int64_t)p * it.stride + e];
+            it.out[e] = s;
+        }
+    }
 }
 
 // ====================================================================== Cholesky
@@ -1032,7 +1052,7 @@ hipError_t launch_gram_rows(const GramBatch &b, int dtype, int d, int maxP, hipS
 hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s) {
     if (b.n <= 0 || maxCount <= 0) return hipSuccess;
     KTimeScope kts("k_reduce", s);
-    dim3 g((unsigned)((maxCount + 255) / 256), b.n);
+    dim3 g((unsigned)((maxCount + 1023) / 1024), b.n);        // 4 entries per thread
     hipLaunchKernelGGL(k_reduce, g, dim3(256), 0, s, b);
     return hipGetLastError();
 }
