@@ -21,7 +21,11 @@
  *     workspace sizes come from jolt_workspace_size().
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *     stream-ordered and asynchronous, except jolt_plan(), which synchronises
- *     `stream` once to read the energy tables back.
+ *     `stream` once to read the energy tables back.  jolt_plan() also forks
+ *     the feature Gram onto a second stream owned by the handle (created on
+ *     the first plan, default priority) and joins it back to `stream` before
+ *     the work that reads it; everything it launched has finished when it
+ *     returns.
  *   - Arguments are validated before any launch; an error leaves no partial
  *     work.  Device errors return JOLT_E_DEVICE with the HIP message in
  *     jolt_last_error().  No C++ exception crosses this interface.
@@ -106,7 +110,8 @@ typedef struct {
 typedef struct jolt_handle_s *jolt_handle;
 
 /* ---- lifetime and errors ------------------------------------------------- */
-/* Binds the calling thread's HIP device `hip_device`; no device memory is taken. */
+/* Binds the calling thread's HIP device `hip_device`; no device memory is taken.
+ * jolt_destroy() waits for and releases the handle's second stream, if any. */
 jolt_status jolt_create(int hip_device, jolt_handle *out);
 void jolt_destroy(jolt_handle h);
 const char *jolt_status_str(jolt_status s);

@@ -22,6 +22,8 @@ using namespace jolt;
 struct jolt_handle_s {
     int device = 0;
     std::string err;
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace jolt {
@@ -44,6 +46,29 @@ jolt_status hip_fail(jolt_handle h, hipError_t e, const char *where) {
 
 void clear_err(jolt_handle h) {
     if (h) h->err.clear();
+}
+
+hipError_t side_stream(jolt_handle h, hipStream_t *st, hipEvent_t *fork, hipEvent_t *join) {
+    if (!h->side) {
+        hipStream_t s = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            if (j) (void)hipEventDestroy(j);
+            if (f) (void)hipEventDestroy(f);
+            if (s) (void)hipStreamDestroy(s);
+            return e;
+        }
+        h->side = s;
+        h->fork = f;
+        h->join = j;
+    }
+    *st = h->side;
+    *fork = h->fork;
+    *join = h->join;
+    return hipSuccess;
 }
 
 void sign_bits_for(uint64_t seed, uint32_t item_id, int d, uint32_t out[4]) {
@@ -99,7 +124,17 @@ extern "C" jolt_status jolt_create(int hip_device, jolt_handle *out) {
     return JOLT_OK;
 }
 
-extern "C" void jolt_destroy(jolt_handle h) { delete h; }
+extern "C" void jolt_destroy(jolt_handle h) {
+    if (!h) return;
+    if (h->side) {
+        (void)hipSetDevice(h->device);
+        (void)hipStreamSynchronize(h->side);
+        (void)hipEventDestroy(h->join);
+        (void)hipEventDestroy(h->fork);
+        (void)hipStreamDestroy(h->side);
+    }
+    delete h;
+}
 
 extern "C" const char *jolt_status_str(jolt_status s) {
     switch (s) {

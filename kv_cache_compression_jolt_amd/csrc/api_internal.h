@@ -13,6 +13,10 @@ namespace jolt {
 jolt_status fail(jolt_handle h, jolt_status s, const char *fmt, ...);
 jolt_status hip_fail(jolt_handle h, hipError_t e, const char *where);
 void clear_err(jolt_handle h);
+// A second stream on the handle's device (default priority, created on first
+// use and destroyed with the handle) and two events, for work forked off the
+// caller's stream and joined back to it within one call.
+hipError_t side_stream(jolt_handle h, hipStream_t *st, hipEvent_t *fork, hipEvent_t *join);
 jolt_status check_item(jolt_handle h, const jolt_item &it);
 jolt_status check_alloc(jolt_handle h, const jolt_item &it, const jolt_alloc &a);
 jolt_status check_items_uniform(jolt_handle h, const jolt_item *items, int n);

@@ -504,8 +504,22 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         maxLH = std::max(maxLH, D[i].LH);
     }
 
-    // ---- feature Gram, ||X||^2
-    {
+    // the feature eigenproblems run on the side stream too, next to the token ones
+    std::vector<EigReq> feigs, eigs;
+    for (int i = 0; i < nb; ++i)
+        feigs.push_back(EigReq{F(S[i].gf), d, d, reinterpret_cast<float *>(ws + pl.item[i0 + i].uf), d,
+                               reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_f),
+                               reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps), &S[i]});
+    // ---- feature Gram, ||X||^2 and the feature eigenproblems, on the side
+    // stream: forked when the token eigenproblems start (one workgroup per
+    // matrix leaves most CUs and HBM idle for this), joined before the core,
+    // their first consumer.
+    hipStream_t side;
+    hipEvent_t fork, join;
+    HIPCHK(side_stream(c.h, &side, &fork, &join), "side stream");
+    auto feature_gram = [&]() -> jolt_status {
+        HIPCHK(hipEventRecord(fork, c.st), "fork");
+        HIPCHK(hipStreamWaitEvent(side, fork, 0), "fork");
         GramBatch gb{};
         ReduceBatch rb{};
         int maxP = 0;
@@ -518,21 +532,19 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             r.part = F(S[i].gfpart); r.out = F(S[i].gf); r.stride = (int64_t)d * d; r.count = (int64_t)d * d;
             r.nsplit = D[i].gf_P;
         }
-        HIPCHK(launch_gram_rows(gb, dt, d, maxP, c.st), "feature gram");
-        HIPCHK(launch_reduce(rb, (int64_t)d * d, c.st), "feature gram reduce");
+        HIPCHK(launch_gram_rows(gb, dt, d, maxP, side), "feature gram");
+        HIPCHK(launch_reduce(rb, (int64_t)d * d, side), "feature gram reduce");
         SmallBatch tb{};
         for (int i = 0; i < nb; ++i) {
             SmallItem &t = tb.it[tb.n++];
             t.in = F(S[i].gf); t.out64 = reinterpret_cast<double *>(W(i, pl.item[i0 + i].normx2)); t.a = d;
         }
-        HIPCHK(launch_trace_batch(tb, c.st), "trace");
-    }
-    // feature eigenproblems join the token eigenproblems in one launch
-    std::vector<EigReq> eigs;
-    for (int i = 0; i < nb; ++i)
-        eigs.push_back(EigReq{F(S[i].gf), d, d, reinterpret_cast<float *>(ws + pl.item[i0 + i].uf), d,
-                              reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_f),
-                              reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps), &S[i]});
+        HIPCHK(launch_trace_batch(tb, side), "trace");
+        const Ctx cs{c.h, side, c.dtype, c.d};
+        if (jolt_status es = eig_all(cs, feigs, scr, max_sweeps, noconv)) return es;
+        HIPCHK(hipEventRecord(join, side), "join");
+        return JOLT_OK;
+    };
 
     if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
         std::vector<float *> yv(nb), zv(nb), gram(nb), gpart(nb), lmat(nb);
@@ -662,6 +674,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
                 eigs.push_back(EigReq{F(S[i].wmat), D[i].kp, D[i].k, F(S[i].vmat), D[i].kp,
                                       reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),
                                       reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i]});
+            if ((s = feature_gram())) return s;
             jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
             if (es) return es;
         }
@@ -702,6 +715,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             eigs.push_back(EigReq{F(S[i].gt), D[i].T, D[i].T, F(S[i].vt), D[i].T,
                                   reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),
                                   reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i]});
+        if (jolt_status fs = feature_gram()) return fs;
         jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
         if (es) return es;
         // U_t^T rows = leading eigenvectors; P = U_t^T A (hi + lo split for bf16 caches)
@@ -745,6 +759,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
     }
 
     // core[lh] = P[:, lh d : lh d + d] U_f, energy
+    HIPCHK(hipStreamWaitEvent(c.st, join, 0), "join");
     if (pl.rt_max > 0) {
         GemmBatch gb{};
         int maxNb = 0;

@@ -74,6 +74,7 @@ ItemHull build_hull(int nc, const int *order, const double *D, const int64_t *B)
     // staircase: per byte count the point of least D (ties: the earliest in
     // order, i.e. smaller rt, rf, bits), kept only where D strictly falls
     std::vector<int> stair;
+    stair.reserve(nc);
     for (int p = 0; p < nc;) {
         int best = order[p], q = p + 1;
         for (; q < nc && B[order[q]] == B[best]; ++q)
@@ -83,6 +84,8 @@ ItemHull build_hull(int nc, const int *order, const double *D, const int64_t *B)
         stair.push_back(best);
     }
     ItemHull h;
+    h.v.reserve(stair.size());
+    h.s.reserve(stair.size());
     for (int i : stair) {
         while (h.v.size() >= 2) {
             const int o = h.v[h.v.size() - 2], a = h.v.back();
@@ -128,24 +131,33 @@ jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, cons
         if (lambda_out) *lambda_out = INFINITY;
         return JOLT_E_INFEASIBLE;
     }
-    auto total = [&](double lam) {
-        int64_t t = 0;
-        for (int i = 0; i < n; ++i) t += B[i][vertex_at(hulls[i], lam)];
-        return t;
-    };
+    // lambda* is 0 when taking every hull edge fits; else the least hull slope
+    // sigma whose allocation (every edge of slope > sigma taken) fits.  The
+    // distinct slopes are walked from the largest down by merging the items'
+    // hulls (each in decreasing slope order): total(sigma_1) is the minimum,
+    // and total(sigma_{k+1}) adds the edges of slope exactly sigma_k.
     double lam = 0.0;
-    if (total(0.0) > budget) {
-        std::vector<double> sl;
-        for (auto &h : hulls) sl.insert(sl.end(), h.s.begin(), h.s.end());
-        std::sort(sl.begin(), sl.end());
-        sl.erase(std::unique(sl.begin(), sl.end()), sl.end());
-        size_t lo = 0, hi = sl.size() - 1;   // total(sl.back()) == min_total <= budget
-        while (lo < hi) {
-            const size_t mid = (lo + hi) / 2;
-            if (total(sl[mid]) <= budget) hi = mid;
-            else lo = mid + 1;
+    {
+        std::vector<size_t> next(n, 0);
+        auto next_slope = [&]() {
+            double m = -1.0;                            // slopes are positive
+            for (int i = 0; i < n; ++i)
+                if (next[i] < hulls[i].s.size()) m = std::max(m, hulls[i].s[next[i]]);
+            return m;
+        };
+        int64_t tot = min_total;                        // total(sg)
+        double fit = 0.0;
+        double sg = next_slope();
+        while (sg > 0.0 && tot <= budget) {
+            fit = sg;
+            for (int i = 0; i < n; ++i) {
+                const ItemHull &h = hulls[i];
+                for (; next[i] < h.s.size() && h.s[next[i]] == sg; ++next[i])
+                    tot += B[i][h.v[next[i] + 1]] - B[i][h.v[next[i]]];
+            }
+            sg = next_slope();
         }
-        lam = sl[lo];
+        lam = (sg <= 0.0 && tot <= budget) ? 0.0 : fit;
     }
     for (int i = 0; i < n; ++i) choice[i] = vertex_at(hulls[i], lam);
     if (lambda_out) *lambda_out = lam;
