@@ -96,11 +96,16 @@ def work_per_step(cfg, jitems, allocs):
 
 
 def source_hash(kernel):
+    """Hash of the kernel's source and of plan.cpp (which sizes and groups its
+    launches), as recorded with the counters in profiles/."""
     f = KERNEL_SOURCE.get(kernel)
     if not f:
         return None
-    with open(os.path.join(ROOT, "kv_cache_compression_jolt_amd", "csrc", f), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in (f, "plan.cpp"):
+        with open(os.path.join(ROOT, "kv_cache_compression_jolt_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def pmc_traffic(kernel, workload):

@@ -72,8 +72,14 @@ def _per_dispatch(d, counter, match):
 
 
 def source_hash(kernel):
-    with open(os.path.join(ROOT, "kv_cache_compression_jolt_amd", "csrc", SOURCES[kernel]), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of the kernel's source and of the plan orchestration that sizes
+    and groups its launches: counters taken before a change to either no
+    longer describe a launch."""
+    h = hashlib.sha256()
+    for f in (SOURCES[kernel], "plan.cpp"):
+        with open(os.path.join(ROOT, "kv_cache_compression_jolt_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def summarize(d, kernel, workload, commands):
@@ -100,7 +106,7 @@ def summarize(d, kernel, workload, commands):
         fh.write("fetch bytes per launch (scaled): %.6g\n" % fetch)
         fh.write("write bytes per launch (scaled): %.6g\n" % write)
         fh.write("hbm bytes per launch: %.6g\n" % (fetch + write))
-        fh.write("source sha256[:16]: %s (%s)\n" % (source_hash(kernel), SOURCES[kernel]))
+        fh.write("source sha256[:16]: %s (%s + plan.cpp)\n" % (source_hash(kernel), SOURCES[kernel]))
     print("wrote", path)
 
 
