@@ -176,26 +176,110 @@ __device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t *sign_bits, int 
     return make_uint4(m[0], m[1], m[2], m[3]);
 }
 
+// Features f0 .. f0 + 3 (f0 a multiple of 4) of one row (bytes), with the
+// rotation signs applied, as floats.
+template <typename T>
+__device__ __forceinline__ void get4_signed(const uint8_t *row, const uint32_t *sign_bits, int f0, float *o);
+template <>
+__device__ __forceinline__ void get4_signed<uint16_t>(const uint8_t *row, const uint32_t *sign_bits, int f0, float *o) {
+    uint2 v = *reinterpret_cast<const uint2 *>(row + 2 * f0);
+    const uint32_t n = (sign_bits[f0 >> 5] >> (f0 & 31)) & 0xFu;
+    v.x ^= ((n & 1u) << 15) | ((n & 2u) << 30);
+    v.y ^= ((n & 4u) << 13) | ((n & 8u) << 28);
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+}
+template <>
+__device__ __forceinline__ void get4_signed<float>(const uint8_t *row, const uint32_t *sign_bits, int f0, float *o) {
+    uint4 v = *reinterpret_cast<const uint4 *>(row + 4 * f0);
+    const uint32_t n = (sign_bits[f0 >> 5] >> (f0 & 31)) & 0xFu;
+    v.x ^= (n & 1u) << 31;
+    v.y ^= (n & 2u) << 30;
+    v.z ^= (n & 4u) << 29;
+    v.w ^= (n & 8u) << 28;
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+}
+
+// Stores a, b, c, d as features f0 .. f0 + 3 of one row (bytes), in the
+// storage type (bf16 by RNE), with the rotation signs applied.
+template <typename T>
+__device__ __forceinline__ void put4_signed(uint8_t *row, const uint32_t *sign_bits, int f0, float a, float b,
+                                            float c, float d);
+template <>
+__device__ __forceinline__ void put4_signed<uint16_t>(uint8_t *row, const uint32_t *sign_bits, int f0, float a,
+                                                      float b, float c, float d) {
+    const uint32_t n = (sign_bits[f0 >> 5] >> (f0 & 31)) & 0xFu;
+    uint2 v;
+    v.x = ((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16)) ^ (((n & 1u) << 15) | ((n & 2u) << 30));
+    v.y = ((uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16)) ^ (((n & 4u) << 13) | ((n & 8u) << 28));
+    *reinterpret_cast<uint2 *>(row + 2 * f0) = v;
+}
+template <>
+__device__ __forceinline__ void put4_signed<float>(uint8_t *row, const uint32_t *sign_bits, int f0, float a, float b,
+                                                   float c, float d) {
+    const uint32_t n = (sign_bits[f0 >> 5] >> (f0 & 31)) & 0xFu;
+    uint4 v = make_uint4(__float_as_uint(a) ^ ((n & 1u) << 31), __float_as_uint(b) ^ ((n & 2u) << 30),
+                         __float_as_uint(c) ^ ((n & 4u) << 29), __float_as_uint(d) ^ ((n & 8u) << 28));
+    *reinterpret_cast<uint4 *>(row + 4 * f0) = v;
+}
+
 // ------------------------------------------------------------------ X^ via MFMA
 // acc[mf] += sum_k wt[f][k] * ut[t][k], f = 32 mf + row, t = token of the lane;
-// for bf16, wt is the hi plane and wlo (same layout) the lo plane of W~
+// for bf16, wt is the hi plane and wlo (same layout) the lo plane of W~.  The
+// lane's fragments of its U~_t row (global memory) are loaded KB at a time, all
+// in flight before the MFMAs that use them.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag frag_or_zero(const T *p, bool ok);
+template <>
+__device__ __forceinline__ FragBF16 frag_or_zero<uint16_t>(const uint16_t *p, bool ok) {
+    uint4 raw = *reinterpret_cast<const uint4 *>(p);
+    if (!ok) raw = make_uint4(0, 0, 0, 0);
+    FragBF16 f;
+    f.v = __builtin_bit_cast(bf16x8, raw);
+    return f;
+}
+template <>
+__device__ __forceinline__ FragF32 frag_or_zero<float>(const float *p, bool ok) {
+    FragF32 f = load_frag(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = ok ? f.v[i] : 0.f;
+    return f;
+}
+
 template <typename T, int NMF>
 __device__ __forceinline__ void xhat_mfma(const T *wt, const T *wlo, int rtp, const T *ut, int rt, int tok, bool tv,
                                           int lane, f32x16 *acc) {
     const int ln = lane & 31, h = lane >> 5;
     const bool vec = (rt & 7) == 0;        // rows of U~_t are 16-byte aligned
-    for (int k0 = 0; k0 < rt; k0 += 16) {
-        const int kk = k0 + 8 * h;
-        typename Elem<T>::Frag b = !(tv && kk < rt) ? zero_frag(ut)
-                                   : vec ? load_frag(ut + (size_t)tok * rt + kk)
-                                         : load_frag_n(ut + (size_t)tok * rt + kk, rt - kk);
+    constexpr int KB = sizeof(T) == 2 ? 8 : 4;
+    const T *urow = ut + (size_t)(tv ? tok : 0) * rt;
+    for (int k0b = 0; k0b < rt; k0b += 16 * KB) {
+        typename Elem<T>::Frag b[KB];
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf) {
-            typename Elem<T>::Frag a = load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk);
-            mfma(a, b, acc[mf]);
-            if constexpr (sizeof(T) == 2) {
-                typename Elem<T>::Frag al = load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk);
-                mfma(al, b, acc[mf]);
+        for (int q = 0; q < KB; ++q) {
+            const int kk = k0b + 16 * q + 8 * h;
+            const bool ok = tv && kk < rt;
+            // in-bounds address (rt >= 8 whenever vec and the loop runs), zero where !ok
+            b[q] = vec ? frag_or_zero(urow + min(kk, rt - 8), ok)
+                       : (ok ? load_frag_n(urow + kk, rt - kk) : zero_frag(ut));
+        }
+#pragma unroll
+        for (int q = 0; q < KB; ++q) {
+            const int kk = k0b + 16 * q + 8 * h;
+            if (k0b + 16 * q >= rt) break;
+#pragma unroll
+            for (int mf = 0; mf < NMF; ++mf) {
+                typename Elem<T>::Frag a = load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk);
+                mfma(a, b[q], acc[mf]);
+                if constexpr (sizeof(T) == 2) {
+                    typename Elem<T>::Frag al = load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk);
+                    mfma(al, b[q], acc[mf]);
+                }
             }
         }
     }
@@ -223,10 +307,24 @@ __device__ __forceinline__ WtView<T> wt_view(const CodecItem &it, int lh) {
         constexpr int PER = 16 / sizeof(T), PLANES = sizeof(T) == 2 ? 2 : 1;
         T *w = reinterpret_cast<T *>(wt_lds);
         const int WP = it.rtp + PER, ppr = it.rtp / PER, total = PLANES * D * ppr;
-        for (int p = threadIdx.x; p < total; p += 64 * NW) {
-            const int pl = p / (D * ppr), rem = p - pl * D * ppr, f = rem / ppr, c = (rem - f * ppr) * PER;
-            const uint4 x = *reinterpret_cast<const uint4 *>(g + ((size_t)(pl * it.LH + lh) * D + f) * it.rtp + c);
-            *reinterpret_cast<uint4 *>(w + ((size_t)pl * D + f) * WP + c) = x;
+        // batches of KB 16-byte pieces per thread, all loads of a batch in flight
+        // before its stores (pieces past the end load piece 0 and are not stored)
+        constexpr int KB = 8;
+        for (int p0 = threadIdx.x; p0 < total; p0 += 64 * NW * KB) {
+            uint4 x[KB];
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                const int p = p0 + 64 * NW * b, q = p < total ? p : 0;
+                const int pl = q / (D * ppr), rem = q - pl * D * ppr, f = rem / ppr, c = (rem - f * ppr) * PER;
+                x[b] = *reinterpret_cast<const uint4 *>(g + ((size_t)(pl * it.LH + lh) * D + f) * it.rtp + c);
+            }
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                const int p = p0 + 64 * NW * b;
+                if (p >= total) break;
+                const int pl = p / (D * ppr), rem = p - pl * D * ppr, f = rem / ppr, c = (rem - f * ppr) * PER;
+                *reinterpret_cast<uint4 *>(w + ((size_t)pl * D + f) * WP + c) = x[b];
+            }
         }
         __syncthreads();
         v.hi = w;
@@ -253,7 +351,6 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
     constexpr int HALF = NMF / 2;
     constexpr int NE = 32 * NMF / 2 * 2 / 2;       // values per lane: 64 (d=128) or 32 (d=64)
     static_assert(NE == 16 * NMF, "layout");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[NWV][32 * TL::RS];
     const Block3 blk = xcd_block();
     const CodecItem &it = batch.it[blk.z];
     const int lh = blk.y;
@@ -263,23 +360,6 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
     const int t0 = blk.x * 32 * NWV + wave * 32;
     const int tok = t0 + ln;
     const bool tv = tok < it.T;
-    uint8_t *buf = lds[wave];
-
-    // stage the wave's 32 rows of X into LDS with the rotation signs applied
-    {
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T) * TL::RB;
-        const uint4 sm = chunk_sign_mask<T>(it.sign_bits, lane % TL::CPR);
-#pragma unroll
-        for (int i = 0; i < 32 * TL::CPR / 64; ++i) {
-            const int c = i * 64 + lane, row = c / TL::CPR, ch = c % TL::CPR;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (t0 + row < it.T) v = *reinterpret_cast<const uint4 *>(src + (size_t)(t0 + row) * TL::RB + ch * 16);
-            v.x ^= sm.x; v.y ^= sm.y; v.z ^= sm.z; v.w ^= sm.w;
-            uint2 *d = reinterpret_cast<uint2 *>(buf + row * TL::RS + ch * 16);
-            d[0] = make_uint2(v.x, v.y);
-            d[1] = make_uint2(v.z, v.w);
-        }
-    }
 
     // s o X^ (signs are folded into wt)
     f32x16 acc[NMF];
@@ -287,16 +367,18 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
     for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
     const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
     xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
-    __syncthreads();
 
-    // residual in the MFMA layout
+    // residual in the MFMA layout: the lane's own features of its token
+    // (32 mf + 8 jb + 4 h + c) straight from global memory with the signs
+    // applied; an invalid token reads row 0 and stores nothing
+    const uint8_t *xrow = reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T + (tv ? tok : 0)) * TL::RB;
     float r[NMF][16];
 #pragma unroll
     for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             float xv[4];
-            Store<T>::get4(buf + ln * TL::RS + (32 * mf + 8 * jb + 4 * h) * (int)sizeof(T), xv);
+            get4_signed<T>(xrow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, xv);
 #pragma unroll
             for (int c = 0; c < 4; ++c) r[mf][4 * jb + c] = xv[c] - acc[mf][4 * jb + c];
         }
@@ -383,7 +465,6 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
     constexpr int NMF = TL::NMF;
     constexpr int HALF = NMF / 2;
     constexpr int NE = 16 * NMF;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[NWV][32 * TL::RS];
     const Block3 blk = xcd_block();
     const CodecItem &it = batch.it[blk.z];
     const int lh = blk.y;
@@ -393,7 +474,28 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
     const int t0 = blk.x * 32 * NWV + wave * 32;
     const int tok = t0 + ln;
     const bool tv = tok < it.T;
-    uint8_t *buf = lds[wave];
+
+    // the lane's codes and scale first, so that their loads overlap the W~
+    // staging and the X^ products
+    constexpr int NCW = BITS > 0 ? BITS * NE / 32 : 1;
+    uint32_t w[NCW];
+    uint16_t sbits = 0;
+    if constexpr (BITS > 0) {
+        const size_t row = (size_t)lh * it.T + (tv ? tok : 0);
+        const size_t grp = row * (D / 64) + (D == 128 ? h : 0);
+        const uint8_t *src = it.codes + grp * 8 * BITS + (D == 64 ? h * 4 * BITS : 0);
+        if constexpr (NCW % 2 == 0) {
+#pragma unroll
+            for (int k = 0; k < NCW; k += 2) {
+                uint2 v = *reinterpret_cast<const uint2 *>(src + 4 * k);
+                w[k] = v.x; w[k + 1] = v.y;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NCW; ++k) w[k] = *reinterpret_cast<const uint32_t *>(src + 4 * k);
+        }
+        sbits = it.scales[grp];
+    }
 
     f32x16 acc[NMF];
 #pragma unroll
@@ -404,23 +506,8 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
     float r[NMF][16];
     if constexpr (BITS > 0) {
         // codes of the lane's group (or half group) -> scaled values
-        const size_t row = (size_t)lh * it.T + (tv ? tok : 0);
-        const size_t grp = row * (D / 64) + (D == 128 ? h : 0);
-        constexpr int NW = BITS * NE / 32;
-        uint32_t w[NW];
-        const uint8_t *src = it.codes + grp * 8 * BITS + (D == 64 ? h * 4 * BITS : 0);
-        if constexpr (NW % 2 == 0) {
-#pragma unroll
-            for (int k = 0; k < NW; k += 2) {
-                uint2 v = *reinterpret_cast<const uint2 *>(src + 4 * k);
-                w[k] = v.x; w[k + 1] = v.y;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < NW; ++k) w[k] = *reinterpret_cast<const uint32_t *>(src + 4 * k);
-        }
         const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
-        const float sc = bf16_to_f32(it.scales[grp]) * isd;
+        const float sc = bf16_to_f32(sbits) * isd;
         const float off = (float)(1 << (BITS - 1));
         float y[NE];
         unpack_codes<BITS, NE>(w, y);
@@ -455,28 +542,19 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
             for (int j = 0; j < 16; ++j) r[mf][j] = 0.f;
     }
 
-    // s o X~ = s o X^ + rotated-back residual; stage rows in LDS, store with signs
+    // s o X~ = s o X^ + rotated-back residual, stored from the MFMA layout (the
+    // lane's features 32 mf + 8 jb + 4 h + c of its token) with the signs
+    if (tv) {
+        uint8_t *orow = reinterpret_cast<uint8_t *>(it.out) + ((size_t)lh * it.T + tok) * TL::RB;
 #pragma unroll
-    for (int mf = 0; mf < NMF; ++mf)
+        for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            const int j = 4 * jb;
-            Store<T>::put4(buf + ln * TL::RS + (32 * mf + 8 * jb + 4 * h) * (int)sizeof(T),
-                           r[mf][j] + acc[mf][j], r[mf][j + 1] + acc[mf][j + 1],
-                           r[mf][j + 2] + acc[mf][j + 2], r[mf][j + 3] + acc[mf][j + 3]);
-        }
-    __syncthreads();
-    {
-        uint8_t *dst = reinterpret_cast<uint8_t *>(it.out) + ((size_t)lh * it.T) * TL::RB;
-        const uint4 sm = chunk_sign_mask<T>(it.sign_bits, lane % TL::CPR);
-#pragma unroll
-        for (int i = 0; i < 32 * TL::CPR / 64; ++i) {
-            const int c = i * 64 + lane, row = c / TL::CPR, ch = c % TL::CPR;
-            const uint2 *s = reinterpret_cast<const uint2 *>(buf + row * TL::RS + ch * 16);
-            uint2 a = s[0], b = s[1];
-            uint4 v = make_uint4(a.x ^ sm.x, a.y ^ sm.y, b.x ^ sm.z, b.y ^ sm.w);
-            if (t0 + row < it.T) *reinterpret_cast<uint4 *>(dst + (size_t)(t0 + row) * TL::RB + ch * 16) = v;
-        }
+            for (int jb = 0; jb < 4; ++jb) {
+                const int j = 4 * jb;
+                put4_signed<T>(orow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, r[mf][j] + acc[mf][j],
+                               r[mf][j + 1] + acc[mf][j + 1], r[mf][j + 2] + acc[mf][j + 2],
+                               r[mf][j + 3] + acc[mf][j + 3]);
+            }
     }
 }
 
@@ -636,20 +714,25 @@ struct CodecShape {
     static size_t wt_lds(int maxRtp) {
         return (size_t)(sizeof(T) == 2 ? 2 : 1) * D * (maxRtp + 16 / sizeof(T)) * sizeof(T);
     }
-    static bool wl(int maxRtp) {
-        return (size_t)NW * 32 * Tile<T, D>::RS + wt_lds(maxRtp) <= 160 * 1024;
-    }
+    // W~ staged in LDS when it fits (the kernels use no other LDS)
+    static bool wl(int maxRtp) { return wt_lds(maxRtp) <= 160 * 1024; }
 };
 
-template <typename Kern>
-static hipError_t codec_launch(Kern k, dim3 grid, int threads, size_t lds, hipStream_t s, const CodecBatch &b) {
+template <void (*K)(CodecBatch)>
+static hipError_t codec_launch(dim3 grid, int threads, size_t lds, hipStream_t s, const CodecBatch &b) {
+    const auto k = K;
     if (lds > 64 * 1024) {
-        hipFuncAttributes fa;
-        hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k));
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    160 * 1024 - (int)fa.sharedSizeBytes);
-        if (e != hipSuccess) return e;
+        // raised once per kernel (one instantiation, and so one static, per kernel)
+        static hipError_t state = hipErrorNotReady;
+        if (state == hipErrorNotReady) {
+            hipFuncAttributes fa;
+            hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k));
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        160 * 1024 - (int)fa.sharedSizeBytes);
+            state = e;
+        }
+        if (state != hipSuccess) return state;
     }
     hipLaunchKernelGGL(k, grid, dim3(threads), lds, s, b);
     return hipGetLastError();
@@ -659,15 +742,15 @@ template <typename T, int D, int BITS>
 static hipError_t encode_one(const CodecBatch &b, int maxT, int maxLH, int maxRtp, hipStream_t s) {
     using CS = CodecShape<T, D>;
     dim3 grid((maxT + 32 * CS::NW - 1) / (32 * CS::NW), maxLH, b.n);
-    if (CS::wl(maxRtp)) return codec_launch(k_encode<T, D, BITS, CS::NW, true>, grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b);
-    return codec_launch(k_encode<T, D, BITS, CS::NW, false>, grid, 64 * CS::NW, 0, s, b);
+    if (CS::wl(maxRtp)) return codec_launch<k_encode<T, D, BITS, CS::NW, true>>(grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b);
+    return codec_launch<k_encode<T, D, BITS, CS::NW, false>>(grid, 64 * CS::NW, 0, s, b);
 }
 template <typename T, int D, int BITS>
 static hipError_t decode_one(const CodecBatch &b, int maxT, int maxLH, int maxRtp, hipStream_t s) {
     using CS = CodecShape<T, D>;
     dim3 grid((maxT + 32 * CS::NW - 1) / (32 * CS::NW), maxLH, b.n);
-    if (CS::wl(maxRtp)) return codec_launch(k_decode<T, D, BITS, CS::NW, true>, grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b);
-    return codec_launch(k_decode<T, D, BITS, CS::NW, false>, grid, 64 * CS::NW, 0, s, b);
+    if (CS::wl(maxRtp)) return codec_launch<k_decode<T, D, BITS, CS::NW, true>>(grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b);
+    return codec_launch<k_decode<T, D, BITS, CS::NW, false>>(grid, 64 * CS::NW, 0, s, b);
 }
 
 template <typename T, int D>
