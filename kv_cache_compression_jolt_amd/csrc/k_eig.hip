@@ -15,8 +15,8 @@
 //   4. V = Q Z with the reflectors applied 32 at a time in compact WY form
 //      (Schreiber & Van Loan 1989) on fp32 MFMA;
 //   5. Newton-Schulz polar steps V <- V (3 I - V^T V) / 2 (at most 3, until
-//      V^T V is within 4e-6 of I), which restore the orthogonality that vectors
-//      of close eigenvalues lose.
+//      V^T V is within 4e-6 of I, or one step after it was within 1e-3),
+//      which restore the orthogonality that vectors of close eigenvalues lose.
 // When V^T V is far from I (numerically repeated eigenvalues: the twisted
 // vectors coincide) the matrix is flagged in sweeps_out and the Jacobi kernel,
 // launched right after in retry mode, solves it instead.
@@ -54,12 +54,20 @@ __device__ __forceinline__ f32x16 mfma_tile(const float *a, int lda_k, int lda_m
     const int m = tm * 32 + (lane & 31), col = tn * 32 + (lane & 31), kh = lane >> 5;
     const bool mv = m < n, cv = col < n;
     const int mc = min(m, n - 1), cc = min(col, n - 1);
-    for (int k0 = 0; k0 < n; k0 += 2) {
-        const int kk = k0 + kh, kc = min(kk, n - 1);
-        const bool kv = kk < n;
-        const float av = ld_or_zero(a, kc * lda_k + mc * lda_m, mv && kv);
-        const float bv = ld_or_zero(b, kc * ld + cc, cv && kv);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    // four K steps per iteration over a multiple of 8 (the masks zero the
+    // padding), so that a batch of loads is in flight before its MFMAs: the
+    // compiler does not unroll loops with a runtime count around MFMAs
+    for (int k0 = 0; k0 < n; k0 += 8) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kk = k0 + 2 * u + kh, kc = min(kk, n - 1);
+            const bool kv = kk < n;
+            av[u] = ld_or_zero(a, kc * lda_k + mc * lda_m, mv && kv);
+            bv[u] = ld_or_zero(b, kc * ld + cc, cv && kv);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u], acc, 0, 0, 0);
     }
     return acc;
 }
@@ -149,7 +157,8 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     __shared__ int s_fail;
     const JacItem &it = batch.it[blockIdx.x];
     const int n = it.n;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // the wave index as a scalar: loops and branches on it stay uniform
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     float *A = sm;          // A[r * ld + c]; reflectors in its rows after phase 1; later M
     float *B1 = sm + boff;  // panel vectors in phase 1; then Z, transformed in place into V
     float *sep = soff >= 0 ? sm + soff : nullptr;
@@ -509,9 +518,12 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
         for (int b = wid; b < nblk; b += kWaves) {
             const int b0 = 32 * b, nbk = min(32, mref - b0);
             f32x16 g = {};
-            for (int k0 = b0; k0 < n; k0 += 2) {
-                const float y = Y(b0, nbk, k0 + kh, m32);
-                g = __builtin_amdgcn_mfma_f32_32x32x2f32(y, y, g, 0, 0, 0);
+            for (int k0 = b0; k0 < n; k0 += 8) {          // Y is zero past row n - 1
+                float y[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) y[u] = Y(b0, nbk, k0 + 2 * u + kh, m32);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) g = __builtin_amdgcn_mfma_f32_32x32x2f32(y[u], y[u], g, 0, 0, 0);
             }
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
@@ -551,10 +563,16 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
                 float *tM = scratch_tile(A, ld, sep, wid, &tsm);
                 const int col = 32 * wid + m32, colc = min(col, n - 1);
                 f32x16 acc = {};
-                for (int k0 = b0; k0 < n; k0 += 2) {
-                    const int k = k0 + kh;
-                    const float bz = ld_or_zero(Z, min(k, n - 1) * ld + colc, k < n && col < n);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Y(b0, nbk, k, m32), bz, acc, 0, 0, 0);
+                for (int k0 = b0; k0 < n; k0 += 8) {      // both operands are zero past row n - 1
+                    float ya[4], bz[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int k = k0 + 2 * u + kh;
+                        bz[u] = ld_or_zero(Z, min(k, n - 1) * ld + colc, k < n && col < n);
+                        ya[u] = Y(b0, nbk, k, m32);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ya[u], bz[u], acc, 0, 0, 0);
                 }
 #pragma unroll
                 for (int q = 0; q < 16; ++q) tM[frag_row(lane, q) * tsm + m32] = acc[q];
@@ -651,6 +669,10 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
         __syncthreads();
         store_tiles(V, acc0, acc1, ld, n, nt, ntiles, wid, lane);
         __syncthreads();
+        // a polar step maps a deviation d of V^T V from I to at most
+        // 3 d^2 / 4 + d^3 / 4: from d <= 1e-3 that is below 1e-6 (plus fp32
+        // rounding of the step), so the result is taken without another check
+        if (devmax <= 1e-3f) break;
     }
     const float *W = V;
 

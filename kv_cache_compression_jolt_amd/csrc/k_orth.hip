@@ -138,7 +138,8 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
     const CholItem &it = batch.it[blockIdx.x];
     if (!it.inverse) return;
     const int k = it.k, nb = (k + 31) >> 5, P = nb * 32;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // the wave index as a scalar: loops and branches on it stay uniform
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int NW = 8;
     float shift = 0.f;                          // used by wave 0 only
     JOLT_PROBE(0);
@@ -412,9 +413,10 @@ hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream
     const size_t ylds = (size_t)P * kApplyYS * sizeof(float);
     const size_t xlds = (size_t)P * ldx * sizeof(float);
     const bool xin = ylds + xlds <= 150 * 1024;
-    // about two workgroups per CU over the batch; each walks its column blocks
+    // about one workgroup per CU over the batch; each walks its column blocks (L^-1 is
+    // staged once per workgroup, so fewer, longer workgroups read less of it)
     const int ncb = (maxLen + 63) / 64;
-    const int gx = std::max(1, std::min(ncb, (512 + b.n - 1) / b.n));
+    const int gx = std::max(1, std::min(ncb, (256 + b.n - 1) / b.n));
     if (xin) hipLaunchKernelGGL(k_apply_linv<true>, dim3(gx, b.n), dim3(64 * ntm), ylds + xlds, s, b, ldx);
     else hipLaunchKernelGGL(k_apply_linv<false>, dim3(gx, b.n), dim3(64 * ntm), ylds, s, b, ldx);
     return hipGetLastError();
