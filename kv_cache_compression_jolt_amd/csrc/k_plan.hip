@@ -353,27 +353,76 @@ __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit
 }
 
 // ====================================================================== feature Gram
+// Partial Grams of 64-row chunks (rows of the (l, h, t) x d unfolding; plans
+// keep T, and so every chunk, a multiple of 64).  Per chunk the rows go to LDS
+// transposed, xs[f][r] (bf16 row pairs packed in 32-bit words); the next
+// chunk's rows are in flight in registers while the MFMAs run on the current
+// one, and each fragment is one 16-byte LDS read.
 template <typename T>
 __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
-    constexpr int XP = 64 + 16 / sizeof(T);
+    constexpr int PER = 16 / sizeof(T);            // features per 16-byte piece
+    constexpr int XP = 64 + PER;                   // pitch (elements) of a feature's row in xs
     __shared__ __attribute__((aligned(16))) T xs[128 * XP];
     const GramItem &it = batch.it[blockIdx.z];
     const int p = blockIdx.x;
     if (p >= it.P) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
-    const int nmf = d / 32;                    // 4 or 2 fragments per side
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, h = lane >> 5;
+    const int nmf = d / 32;                        // 4 or 2 fragments per side
     const T *x = reinterpret_cast<const T *>(it.x);
     const int64_t rb = (int64_t)p * it.chunk;
     const int64_t re = min(it.rows, rb + it.chunk);
+    // staging tasks: row pair rp (32 per chunk) x 16-byte piece fc of the row
+    const int nfc = d / PER, ntask = 32 * nfc / 256;   // 1, 2 or 4 per thread
+    uint4 lo[4], hi[4];
+    auto load = [&](int64_t r0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < ntask) {
+                const int t = tid + 256 * j, rp = t / nfc, fc = t - rp * nfc;
+                const T *src = x + (r0 + 2 * rp) * d + fc * PER;
+                lo[j] = *reinterpret_cast<const uint4 *>(src);
+                hi[j] = *reinterpret_cast<const uint4 *>(src + d);
+            }
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < ntask) {
+                const int t = tid + 256 * j, rp = t / nfc, fc = t - rp * nfc;
+                if constexpr (sizeof(T) == 2) {
+                    uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
+                    const uint32_t a[4] = {lo[j].x, lo[j].y, lo[j].z, lo[j].w}, b[4] = {hi[j].x, hi[j].y, hi[j].z, hi[j].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xw[(fc * PER + 2 * i) * (XP / 2) + rp] = (a[i] & 0xFFFFu) | (b[i] << 16);
+                        xw[(fc * PER + 2 * i + 1) * (XP / 2) + rp] = (a[i] >> 16) | (b[i] & 0xFFFF0000u);
+                    }
+                } else {
+                    const float a[4] = {__uint_as_float(lo[j].x), __uint_as_float(lo[j].y), __uint_as_float(lo[j].z),
+                                        __uint_as_float(lo[j].w)};
+                    const float b[4] = {__uint_as_float(hi[j].x), __uint_as_float(hi[j].y), __uint_as_float(hi[j].z),
+                                        __uint_as_float(hi[j].w)};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        reinterpret_cast<float *>(xs)[(fc * PER + i) * XP + 2 * rp] = a[i];
+                        reinterpret_cast<float *>(xs)[(fc * PER + i) * XP + 2 * rp + 1] = b[i];
+                    }
+                }
+            }
+        }
+    };
     // fragment pairs owned by this wave: (mf, nf) = q / nmf, q % nmf, q = wave + 4 i
     f32x16 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
     const int nq = nmf * nmf;
+    if (rb < re) load(rb);
     for (int64_t r0 = rb; r0 < re; r0 += 64) {
+        __syncthreads();                           // the previous chunk's reads of xs are done
+        store();
         __syncthreads();
-        stage_transposed<T>(x + r0 * d, d, xs, XP);
-        __syncthreads();
+        if (r0 + 64 < re) load(r0 + 64);
 #pragma unroll
         for (int kk = 0; kk < 64; kk += 16) {
 #pragma unroll
@@ -381,14 +430,8 @@ __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
                 const int q = wave + 4 * i;
                 if (q < nq) {
                     const int mf = q / nmf, nf = q % nmf;
-                    typename Elem<T>::Frag a, b;
-                    const T *pa = xs + (32 * mf + ln) * XP + kk + 8 * h;
-                    const T *pb = xs + (32 * nf + ln) * XP + kk + 8 * h;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        reinterpret_cast<T *>(&a)[e] = pa[e];
-                        reinterpret_cast<T *>(&b)[e] = pb[e];
-                    }
+                    const typename Elem<T>::Frag a = load_frag(xs + (32 * mf + ln) * XP + kk + 8 * h);
+                    const typename Elem<T>::Frag b = load_frag(xs + (32 * nf + ln) * XP + kk + 8 * h);
                     mfma(a, b, acc[i]);
                 }
             }
