@@ -24,6 +24,7 @@ struct jolt_handle_s {
     std::string err;
     hipStream_t side = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
+    jolt::DualTables dual;
 };
 
 namespace jolt {
@@ -47,6 +48,8 @@ jolt_status hip_fail(jolt_handle h, hipError_t e, const char *where) {
 void clear_err(jolt_handle h) {
     if (h) h->err.clear();
 }
+
+DualTables &dual_tables(jolt_handle h) { return h->dual; }
 
 hipError_t side_stream(jolt_handle h, hipStream_t *st, hipEvent_t *fork, hipEvent_t *join) {
     if (!h->side) {

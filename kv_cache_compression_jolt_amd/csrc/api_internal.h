@@ -5,6 +5,9 @@
 #include "../../include/libjolt.h"
 #include "dev_common.h"
 #include "payload.h"
+#include "planner.h"
+
+#include <vector>
 
 struct jolt_handle_s;
 
@@ -13,6 +16,23 @@ namespace jolt {
 jolt_status fail(jolt_handle h, jolt_status s, const char *fmt, ...);
 jolt_status hip_fail(jolt_handle h, hipError_t e, const char *where);
 void clear_err(jolt_handle h);
+// The dual's candidate grid and per-shape byte tables depend only on the
+// configuration and the item shapes; a handle keeps the last ones (and the
+// buffer for the items' distortion tables) from one plan to the next.
+struct DualTables {
+    int rt_max = -1, rf_max = -1, step = -1, grid_nf = -1, dtype = -1, d = -1;
+    uint32_t bits_mask = 0;
+    std::vector<Cand> cand;
+    std::vector<int> cell;          // each candidate's energy-grid cell (-1 for rank 0)
+    struct Shape {
+        int L, H, T;
+        std::vector<int64_t> B;     // bytes per candidate
+        std::vector<int> order;     // candidates by (bytes, rt, rf, bits)
+    };
+    std::vector<Shape> shapes;
+    std::vector<double> D;          // n x candidates distortion tables
+};
+DualTables &dual_tables(jolt_handle h);
 // A second stream on the handle's device (default priority, created on first
 // use and destroyed with the handle) and two events, for work forked off the
 // caller's stream and joined back to it within one call.

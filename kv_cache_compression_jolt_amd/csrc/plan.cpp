@@ -856,6 +856,7 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     bool noconv = false;
     // JOLT_TIMING=1: host-side phase times of this call on stderr
     static const bool timing = getenv("JOLT_TIMING") != nullptr;
+    static const bool debug = getenv("JOLT_DEBUG") != nullptr;
     const auto t_start = std::chrono::steady_clock::now();
     for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
         const int nb = std::min(kMaxBatch, n - c0);
@@ -890,7 +891,7 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
         int sw[2];
         std::memcpy(sw, rb.data() + (pl.item[i].sweeps - pl.readback), 8);
         if (sw[0] < 0 || sw[1] < 0) noconv = true;
-        if (getenv("JOLT_DEBUG")) fprintf(stderr, "libjolt: item %d eig sweeps feature %d token %d\n", i, sw[0], sw[1]);
+        if (debug) fprintf(stderr, "libjolt: item %d eig sweeps feature %d token %d\n", i, sw[0], sw[1]);
     }
 
     const int rf_max = pl.rf_max;
@@ -907,42 +908,49 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
         report();
         return noconv ? fail(h, JOLT_E_NOCONV, "eigensolver hit its sweep cap") : JOLT_OK;
     }
-    std::vector<Cand> cand = candidate_grid(rt_max, rf_max, cfg->rank_step, cfg->bits_mask);
+    DualTables &dt = dual_tables(h);
+    if (dt.rt_max != rt_max || dt.rf_max != rf_max || dt.step != pl.step || dt.grid_nf != pl.grid_nf ||
+        dt.bits_mask != cfg->bits_mask || dt.dtype != items[0].dtype || dt.d != items[0].d ||
+        pl.step != cfg->rank_step) {
+        dt = DualTables{};
+        dt.rt_max = rt_max; dt.rf_max = rf_max; dt.step = pl.step; dt.grid_nf = pl.grid_nf;
+        dt.bits_mask = cfg->bits_mask; dt.dtype = items[0].dtype; dt.d = items[0].d;
+        dt.cand = candidate_grid(rt_max, rf_max, cfg->rank_step, cfg->bits_mask);
+        dt.cell.resize(dt.cand.size());
+        for (size_t j = 0; j < dt.cand.size(); ++j)
+            dt.cell[j] = (dt.cand[j].rt == 0 || dt.cand[j].rf == 0)
+                             ? -1 : (dt.cand[j].rt / pl.step - 1) * pl.grid_nf + (dt.cand[j].rf / pl.step - 1);
+    }
+    const std::vector<Cand> &cand = dt.cand;
     const int nc = (int)cand.size();
-    // each candidate's energy-grid cell (-1 for rank 0)
-    std::vector<int> cell(nc);
-    for (int j = 0; j < nc; ++j)
-        cell[j] = (cand[j].rt == 0 || cand[j].rf == 0)
-                      ? -1 : (cand[j].rt / pl.step - 1) * pl.grid_nf + (cand[j].rf / pl.step - 1);
     // byte tables and their order, shared by the items of one shape (dtype and d
     // are common to the call; L, H, T may differ)
-    struct Shape { int L, H, T; std::vector<int64_t> B; std::vector<int> order; };
-    std::vector<Shape> shapes;
     std::vector<int> shape_of(n);
     for (int i = 0; i < n; ++i) {
         int k = 0;
-        while (k < (int)shapes.size() &&
-               !(shapes[k].L == items[i].L && shapes[k].H == items[i].H && shapes[k].T == items[i].T))
+        while (k < (int)dt.shapes.size() &&
+               !(dt.shapes[k].L == items[i].L && dt.shapes[k].H == items[i].H && dt.shapes[k].T == items[i].T))
             ++k;
-        if (k == (int)shapes.size()) {
-            Shape sh{items[i].L, items[i].H, items[i].T, std::vector<int64_t>(nc), {}};
+        if (k == (int)dt.shapes.size()) {
+            DualTables::Shape sh{items[i].L, items[i].H, items[i].T, std::vector<int64_t>(nc), {}};
             for (int j = 0; j < nc; ++j) sh.B[j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
             sh.order = byte_order(nc, cand.data(), sh.B.data());
-            shapes.push_back(std::move(sh));
+            dt.shapes.push_back(std::move(sh));
         }
         shape_of[i] = k;
     }
-    std::vector<std::vector<double>> Dt(n, std::vector<double>(nc));
-    for (int i = 0; i < n; ++i) distortion_table_cells(grid[i], cell.data(), nx2[i], cfg->delta_b, cand, Dt[i].data());
+    dt.D.resize((size_t)n * nc);
+    for (int i = 0; i < n; ++i)
+        distortion_table_cells(grid[i], dt.cell.data(), nx2[i], cfg->delta_b, cand, dt.D.data() + (size_t)i * nc);
     std::vector<int32_t> ncand(n, nc);
     std::vector<const Cand *> cp(n, cand.data());
     std::vector<const double *> dp(n);
     std::vector<const int64_t *> bp(n);
     std::vector<const int *> op(n);
     for (int i = 0; i < n; ++i) {
-        dp[i] = Dt[i].data();
-        bp[i] = shapes[shape_of[i]].B.data();
-        op[i] = shapes[shape_of[i]].order.data();
+        dp[i] = dt.D.data() + (size_t)i * nc;
+        bp[i] = dt.shapes[shape_of[i]].B.data();
+        op[i] = dt.shapes[shape_of[i]].order.data();
     }
     std::vector<int> choice(n);
     double lam = 0.0;
@@ -951,7 +959,7 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
         const Cand &cc = cand[choice[i]];
         alloc_host[i].rt = cc.rt; alloc_host[i].rf = cc.rf; alloc_host[i].bits = cc.bits; alloc_host[i].reserved = 0;
         alloc_host[i].bytes = bp[i][choice[i]];
-        alloc_host[i].distortion = Dt[i][choice[i]];
+        alloc_host[i].distortion = dp[i][choice[i]];
     }
     if (lambda_out) *lambda_out = lam;
     report();
