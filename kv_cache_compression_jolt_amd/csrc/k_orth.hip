@@ -367,6 +367,18 @@ __global__ __launch_bounds__(64 * kCholInverseMaxK / 32) void k_apply_linv(TrsmB
                 if (c0 + m32 < it.len) it.q[(size_t)row * it.ldy + c0 + m32] = acc0[jj];
                 if (c0 + 32 + m32 < it.len) it.q[(size_t)row * it.ldy + c0 + 32 + m32] = acc1[jj];
             }
+            if (it.qh) {
+                // bf16 copies for the next sketch pass, every row (rows k .. P - 1 are zero)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int col = c0 + 32 * u + m32;
+                    if (col >= it.len) continue;
+                    const float v = u ? acc1[jj] : acc0[jj];
+                    const uint16_t hv = f32_to_bf16(v);
+                    it.qh[(size_t)row * it.ldy + col] = hv;
+                    if (it.ql) it.ql[(size_t)row * it.ldy + col] = f32_to_bf16(v - bf16_to_f32(hv));
+                }
+            }
         }
         if (next >= ncb) break;
         cb = next;

@@ -446,8 +446,13 @@ hipError_t panel_grams(const SymGramBatch &gb, int maxK, int maxS, hipStream_t s
     return launch_gemm(g, maxK, maxK, maxS, 1, st);
 }
 
+// Orthonormalizes the rows of each y in place (passes of shifted CholeskyQR).
+// With hi (and lo) given, the last pass also writes bf16 copies of the result
+// when the L^-1 apply runs (k <= kCholInverseMaxK); *bf reports whether it did.
 jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, const int *k,
-                      const int *kp, const int *len, const int *split, const int *chunk, int passes) {
+                      const int *kp, const int *len, const int *split, const int *chunk, int passes,
+                      uint16_t *const *hi = nullptr, uint16_t *const *lo = nullptr, bool *bf = nullptr) {
+    if (bf) *bf = false;
     for (int pass = 0; pass < passes; ++pass) {
         SymGramBatch gb{};
         ReduceBatch rb{};
@@ -466,6 +471,10 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
             ch.inverse = k[i] <= kCholInverseMaxK;
             TrsmItem &t = tb.it[tb.n++];
             t.l = lmat[i]; t.y = y[i]; t.q = y[i]; t.k = k[i]; t.ld = kp[i]; t.len = len[i]; t.ldy = len[i];
+            if (hi && pass + 1 == passes) {
+                t.qh = hi[i];
+                t.ql = lo ? lo[i] : nullptr;
+            }
             maxK = std::max(maxK, k[i]);
             maxLen = std::max(maxLen, len[i]);
             maxS = std::max(maxS, split[i]);
@@ -475,8 +484,12 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
         for (int i = 0; i < nb; ++i) maxCount = std::max<int64_t>(maxCount, (int64_t)kp[i] * kp[i]);
         HIPCHK(launch_reduce(rb, maxCount, c.st), "orth reduce");
         HIPCHK(launch_cholesky(cb, maxK, c.st), "orth cholesky");
-        if (maxK <= kCholInverseMaxK) HIPCHK(launch_apply_linv(tb, maxK, maxLen, c.st), "orth L^-1 Y");
-        else HIPCHK(launch_trsm(tb, maxK, maxLen, c.st), "orth trsm");
+        if (maxK <= kCholInverseMaxK) {
+            HIPCHK(launch_apply_linv(tb, maxK, maxLen, c.st), "orth L^-1 Y");
+            if (bf && hi && pass + 1 == passes) *bf = true;
+        } else {
+            HIPCHK(launch_trsm(tb, maxK, maxLen, c.st), "orth trsm");
+        }
     }
     return JOLT_OK;
 }
@@ -634,23 +647,36 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             return JOLT_OK;
         };
         jolt_status s;
+        // bf16 copies for the sketch passes come from the last L^-1 apply of each
+        // orthonormalization when it can write them (conv), else from to_bf
+        std::vector<uint16_t *> qhv(nb), qlv(nb), zbv(nb);
+        for (int i = 0; i < nb; ++i) {
+            qhv[i] = bf ? reinterpret_cast<uint16_t *>(P(S[i].qh)) : nullptr;
+            qlv[i] = bf ? reinterpret_cast<uint16_t *>(P(S[i].ql)) : nullptr;
+            zbv[i] = bf ? reinterpret_cast<uint16_t *>(P(S[i].zb)) : nullptr;
+        }
+        uint16_t *const *qh_out = bf ? qhv.data() : nullptr;
+        bool conv = false;
         if ((s = xm(true))) return s;                                                        // Y = A Omega
         if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
-                           lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2)))
+                           lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2, qh_out,
+                           (bf && cfg.power_iters == 0) ? qlv.data() : nullptr, &conv)))
             return s;
         for (int q = 0; q < cfg.power_iters; ++q) {
-            if ((s = to_bf(true, false))) return s;
+            if (!conv && (s = to_bf(true, false))) return s;
             if ((s = xtq(false))) return s;                                                 // Z = A^T Q
             if ((s = orth_rows(c, nb, zv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
-                               lenN.data(), sN.data(), cN.data(), 1)))
+                               lenN.data(), sN.data(), cN.data(), 1, bf ? zbv.data() : nullptr, nullptr, &conv)))
                 return s;
-            if ((s = to_bf(false, false))) return s;
+            if (!conv && (s = to_bf(false, false))) return s;
             if ((s = xm(false))) return s;                                                  // Y = A Z
+            const bool last = q + 1 == cfg.power_iters;
             if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
-                               lenT.data(), sT.data(), cT.data(), q + 1 == cfg.power_iters ? 2 : 1)))
+                               lenT.data(), sT.data(), cT.data(), last ? 2 : 1, qh_out,
+                               (bf && last) ? qlv.data() : nullptr, &conv)))
                 return s;
         }
-        if ((s = to_bf(true, true))) return s;
+        if (!conv && (s = to_bf(true, true))) return s;
         if ((s = xtq(true))) return s;                                                      // B = Q^T A (hi + lo)
         // W = B B^T, eig
         {

@@ -94,6 +94,7 @@ struct TrsmItem {
     const float *y;
     float *q;
     int k, ld, len, ldy;
+    uint16_t *qh, *ql;   // optional bf16 copies of q (hi, and lo = q - hi), all kp rows (apply only)
 };
 struct TrsmBatch { TrsmItem it[kMaxBatch]; int n; };
 hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
