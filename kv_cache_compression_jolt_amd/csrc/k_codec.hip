@@ -337,10 +337,7 @@ __device__ __forceinline__ WtView<T> wt_view(const CodecItem &it, int lh) {
 template <typename T, int D>
 struct Tile {
     static constexpr int RB = D * (int)sizeof(T);   // row bytes
-    static constexpr int RS = RB + 8;              // LDS row stride (8-byte aligned rows)
-    static constexpr int CPR = RB / 16;            // 16-byte chunks per row
     static constexpr int NMF = D / 32;
-    static constexpr int NE = 16 * NMF / 2 * 2 / (D == 128 ? 1 : 1);  // values per lane
 };
 
 // ------------------------------------------------------------------ fused encoder
@@ -706,8 +703,8 @@ __global__ void k_rademacher_fill(uint64_t key, uint32_t stream, uint64_t first,
 
 // ------------------------------------------------------------------ launchers
 // Workgroups of NW waves x 32 tokens of one (layer, head).  bf16: 8 waves; fp32:
-// 4 (its row staging is twice as large).  W~ goes through LDS when it fits
-// beside the row staging.
+// 4.  W~ goes through LDS when it fits: 68 KiB for d = 128, r_tp = 128
+// bf16 (hi + lo planes), so two workgroups share a CU.
 template <typename T, int D>
 struct CodecShape {
     static constexpr int NW = sizeof(T) == 2 ? 8 : 4;

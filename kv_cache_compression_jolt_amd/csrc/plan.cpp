@@ -950,7 +950,9 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     const std::vector<Cand> &cand = dt.cand;
     const int nc = (int)cand.size();
     // byte tables and their order, shared by the items of one shape (dtype and d
-    // are common to the call; L, H, T may differ)
+    // are common to the call; L, H, T may differ).  Kept for at most 64 shapes
+    // between calls, so callers whose T changes every call do not grow the cache.
+    if (dt.shapes.size() > 64) dt.shapes.clear();
     std::vector<int> shape_of(n);
     for (int i = 0; i < n; ++i) {
         int k = 0;
