@@ -358,18 +358,12 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
     const int tok = t0 + ln;
     const bool tv = tok < it.T;
 
-    // s o X^ (signs are folded into wt)
-    f32x16 acc[NMF];
-#pragma unroll
-    for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
-    const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
-    xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
-
-    // residual in the MFMA layout: the lane's own features of its token
-    // (32 mf + 8 jb + 4 h + c) straight from global memory with the signs
-    // applied; an invalid token reads row 0 and stores nothing
+    // -(s o x) in the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
+    // of its token), loaded before the W~ staging so that the load latency
+    // overlaps it; an invalid token reads row 0 and stores nothing.  The X^
+    // products (signs folded into wt) accumulate onto it, leaving -(s o r).
     const uint8_t *xrow = reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T + (tv ? tok : 0)) * TL::RB;
-    float r[NMF][16];
+    f32x16 acc[NMF];
 #pragma unroll
     for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
@@ -377,8 +371,15 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
             float xv[4];
             get4_signed<T>(xrow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, xv);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) r[mf][4 * jb + c] = xv[c] - acc[mf][4 * jb + c];
+            for (int c = 0; c < 4; ++c) acc[mf][4 * jb + c] = -xv[c];
         }
+    const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
+    xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+    float r[NMF][16];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) r[mf][j] = acc[mf][j];
 
     // in-register Hadamard stages: feature bits 0, 1, 3, 4 (j bits) and the mf bits
 #pragma unroll
@@ -405,8 +406,10 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
                 }
 
     // feature bit 2 across lane halves; afterwards the lane half is the top
-    // feature bit and y[e] holds in-group element e (+ 32 h for d = 64)
-    const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
+    // feature bit and y[e] holds in-group element e (+ 32 h for d = 64).  The
+    // butterflies so far ran on -r; the negative 1/sqrt(d) restores the sign
+    // exactly (negation commutes with every rounding here).
+    const float isd = (D == 128) ? -0.08838834764831845f : -0.125f;
     float y[NE];
 #pragma unroll
     for (int mp = 0; mp < HALF; ++mp)
@@ -494,13 +497,12 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
         sbits = it.scales[grp];
     }
 
-    f32x16 acc[NMF];
-#pragma unroll
-    for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
     const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
-    xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
 
-    float r[NMF][16];
+    // rotated-back residual first, straight into the accumulators of the X^
+    // products (the MFMA layout), so that it and the products are never live
+    // at the same time
+    f32x16 acc[NMF];
     if constexpr (BITS > 0) {
         // codes of the lane's group (or half group) -> scaled values
         const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
@@ -529,18 +531,18 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
                 const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
                 float u = y[e], v = y[e + 4];
                 swap_halves(u, v);
-                r[mp][j] = u + v;
-                r[mp + HALF][j] = u - v;
+                acc[mp][j] = u + v;
+                acc[mp + HALF][j] = u - v;
             }
     } else {
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) r[mf][j] = 0.f;
+        for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
     }
+    // s o X~ = rotated-back residual + s o X^
+    xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
 
-    // s o X~ = s o X^ + rotated-back residual, stored from the MFMA layout (the
-    // lane's features 32 mf + 8 jb + 4 h + c of its token) with the signs
+    // stored from the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
+    // of its token) with the signs
     if (tv) {
         uint8_t *orow = reinterpret_cast<uint8_t *>(it.out) + ((size_t)lh * it.T + tok) * TL::RB;
 #pragma unroll
@@ -548,9 +550,8 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
                 const int j = 4 * jb;
-                put4_signed<T>(orow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, r[mf][j] + acc[mf][j],
-                               r[mf][j + 1] + acc[mf][j + 1], r[mf][j + 2] + acc[mf][j + 2],
-                               r[mf][j + 3] + acc[mf][j + 3]);
+                put4_signed<T>(orow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, acc[mf][j], acc[mf][j + 1],
+                               acc[mf][j + 2], acc[mf][j + 3]);
             }
     }
 }
