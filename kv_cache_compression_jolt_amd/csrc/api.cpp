@@ -459,10 +459,19 @@ extern "C" jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const 
     if (count > 0 && (!a || !vec || !lam || !info)) return fail(h, JOLT_E_INVALID, "eigh: null pointer");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool tri = !force_jacobi && n <= kTriMaxN;
-    for (int i0 = 0; i0 < count; i0 += 64) {
+    // the tridiagonal solver's hand-over workspace, stream-ordered: one region
+    // per matrix of a batch of up to 64, freed on the stream after the last batch
+    const size_t wsb = tri ? eig_tri_ws_bytes(n) : 0;
+    uint8_t *tws = nullptr;
+    if (tri && count > 0)
+        if (hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&tws), wsb * std::min(count, 64), st);
+            e != hipSuccess)
+            return hip_fail(h, e, "eigh workspace");
+    hipError_t e = hipSuccess;
+    for (int i0 = 0; i0 < count && e == hipSuccess; i0 += 64) {
         JacBatch b{};
         for (int i = i0; i < count && b.n < 64; ++i) {
-            JacItem &j = b.it[b.n++];
+            JacItem &j = b.it[b.n];
             j.a = a + (size_t)i * mat_stride;
             j.lda = lda;
             j.vec = vec + (size_t)i * n * n;
@@ -471,12 +480,17 @@ extern "C" jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const 
             j.n = n;
             j.raw = 0;
             j.sweeps_out = info + i;
+            j.tw = tri ? reinterpret_cast<float *>(tws + (size_t)b.n * wsb) : nullptr;
+            ++b.n;
         }
-        hipError_t e = tri ? launch_eig_tridiag(b, n, st) : launch_jacobi_lds(b, n, 30, st);
+        e = tri ? launch_eig_tridiag(b, n, st) : launch_jacobi_lds(b, n, 30, st);
         if (e == hipSuccess && tri) e = launch_jacobi_lds(b, n, 30, st, 1);
-        if (e != hipSuccess) return hip_fail(h, e, "eigh");
     }
-    return JOLT_OK;
+    if (tws) {
+        const hipError_t ef = hipFreeAsync(tws, st);
+        if (e == hipSuccess) e = ef;
+    }
+    return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "eigh");
 }
 
 extern "C" jolt_status jolt_kernel_timer(jolt_handle h, const char *kernel, int32_t enable) {

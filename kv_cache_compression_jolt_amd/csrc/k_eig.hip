@@ -1,5 +1,8 @@
-// Symmetric eigensolver for small dense matrices (n <= kTriMaxN), one
-// workgroup of 1024 threads per matrix, all of it resident in LDS.
+// Symmetric eigensolver for small dense matrices (n <= kTriMaxN) in three
+// launches: k_eig_tridiag (step 1) and k_eig_backtr (steps 4, 5) run one
+// workgroup of 1024 threads per matrix with the matrix resident in LDS;
+// k_eig_trivec (steps 2, 3) runs one wave per eigenvalue over the whole chip.
+// They hand over through a per-matrix workspace (tri_ws).
 //
 //   1. Householder tridiagonalization Q^T A Q = T (Golub & Van Loan, Matrix
 //      Computations, sec. 8.3.1) in panels of 32 columns: within a panel the
@@ -41,6 +44,27 @@ constexpr int kWaves = kThreads / 64;
 // row stride of the panel's V and W: with an even stride every per-step
 // access pattern over them meets each LDS bank at most twice per wave
 constexpr int kPanelStride = 34;
+
+// Per-matrix workspace between the three launches (floats; eig_tri_ws_bytes
+// gives its size): A after the reduction (n x n, row-major, reflector j in row
+// j), Z^T (row k = the eigenvector of the k-th smallest eigenvalue of T), d,
+// e (e_{n-1} = 0), tau, the eigenvalues of T ascending, and a fail flag.
+struct TriWs {
+    float *a, *zt, *d, *e, *tau, *lam;
+    int *flag;
+};
+__device__ __forceinline__ TriWs tri_ws(float *base, int n) {
+    const size_t nn = (size_t)n * n;
+    TriWs w;
+    w.a = base;
+    w.zt = base + nn;
+    w.d = w.zt + nn;
+    w.e = w.d + n;
+    w.tau = w.e + n;
+    w.lam = w.tau + n;
+    w.flag = reinterpret_cast<int *>(w.lam + n);
+    return w;
+}
 
 
 // C (n x n) tile (tm, tn) of sum_k A(m, k) B(k, n) on v_mfma_f32_32x32x2f32, with
@@ -148,25 +172,20 @@ __device__ __forceinline__ void wblock_t_full(float *D, int ld, const float *tau
             if (i <= c) D[c * ld + i] = x[i];
 }
 
-__global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld, int boff, int poff, int soff) {
+__global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld, int boff, int poff) {
     extern __shared__ float sm[];
-    __shared__ float sd[kTriMaxN], se[kTriMaxN], slam[kTriMaxN], stau[kTriMaxN];
+    __shared__ float sd[kTriMaxN], se[kTriMaxN], stau[kTriMaxN];
     __shared__ float sx0[kTriMaxN], sx1[kTriMaxN], sp[kTriMaxN], sy[64];
-    __shared__ float2 sde[kTriMaxN];
-    __shared__ float sred[2 * kWaves];
-    __shared__ int s_fail;
     const JacItem &it = batch.it[blockIdx.x];
     const int n = it.n;
     // the wave index as a scalar: loops and branches on it stay uniform
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    float *A = sm;          // A[r * ld + c]; reflectors in its rows after phase 1; later M
-    float *B1 = sm + boff;  // panel vectors in phase 1; then Z, transformed in place into V
-    float *sep = soff >= 0 ? sm + soff : nullptr;
+    float *A = sm;          // A[r * ld + c]; the reflectors in its rows after the reduction
+    float *B1 = sm + boff;  // the panel's V and W
     constexpr int PS = kPanelStride;
     float *Vp = B1, *Wp = B1 + poff;
 
     JOLT_PROBE(0);
-    if (tid == 0) s_fail = 0;
     for (int e = tid; e < n * n; e += kThreads) {
         const int r = e / n, c = e - r * n;
         A[r * ld + c] = 0.5f * (it.a[(size_t)r * it.lda + c] + it.a[(size_t)c * it.lda + r]);
@@ -376,8 +395,60 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     }
     __syncthreads();
 
-    // ---------------------------------------------------------------- 2. eigenvalues
-    JOLT_PROBE(2);
+    // hand over to k_eig_trivec and k_eig_backtr: A (reflectors in its rows),
+    // T = (d, e) and tau; the fail flag starts clear
+    const TriWs w = tri_ws(it.tw, n);
+    for (int e = tid; e < n * n; e += kThreads) {
+        const int r = e / n, c = e - r * n;
+        w.a[e] = A[r * ld + c];
+    }
+    for (int i = tid; i < n; i += kThreads) {
+        w.d[i] = sd[i];
+        w.e[i] = i + 1 < n ? se[i] : 0.f;
+        w.tau[i] = i + 2 < n ? stau[i] : 0.f;
+    }
+    if (tid == 0) *w.flag = 0;
+}
+
+// ---------------------------------------------------------------- 2 + 3. eigenpairs of T
+// One wave per eigenvalue k (the k-th smallest) of the tridiagonal T = (d, e)
+// that k_eig_tridiag left in the workspace, so that a batch spreads over the
+// chip instead of one CU per matrix:
+//   2. multisection on Sturm counts (Golub & Van Loan sec. 8.4.1): the 64
+//      lanes count at the 64 inner points of 65 equal sections of the
+//      interval [a, b) that holds it (count(a) <= k < count(b), count(x) =
+//      #{i : q_i(x) < 0}); the interval shrinks to the section that starts
+//      below the first point whose count exceeds k, to a relative width of
+//      2 eps (floored at eps ||T|| / 1024: vectors of close eigenvalues stay
+//      near orthogonal only with accurate shifts);
+//   3. the eigenvector from a twisted factorization of T - lambda I (Dhillon &
+//      Parlett, Orthogonal eigenvectors and relative gaps, 2004): lanes 0 and 1
+//      run the forward and backward LDL^T pivots side by side, lane 0 takes
+//      the twist index r where |gamma| is smallest (the first such index),
+//      lanes 0 and 1 run the one-sided recurrences up and down from z_r = 1,
+//      and the wave normalises.
+// Writes lambda_k and row k of Z^T; sets the fail flag when a vector overflows.
+constexpr int kVecWaves = 4;
+__global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch) {
+    __shared__ float sd[kTriMaxN], se[kTriMaxN];
+    __shared__ float2 sde[kTriMaxN];                  // {d_i, e_{i-1}^2}
+    __shared__ float piv[kVecWaves][2][kTriMaxN];     // forward / backward pivots
+    __shared__ float zc[kVecWaves][kTriMaxN];
+    const JacItem &it = batch.it[blockIdx.y];
+    const int n = it.n;
+    if ((int)blockIdx.x * kVecWaves >= n) return;
+    const TriWs w = tri_ws(it.tw, n);
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int i = tid; i < n; i += 64 * kVecWaves) {
+        const float di = w.d[i], em = i > 0 ? w.e[i - 1] : 0.f;
+        sd[i] = di;
+        se[i] = w.e[i];
+        sde[i] = make_float2(di, em * em);
+    }
+    __syncthreads();
+    const int k = blockIdx.x * kVecWaves + wid;
+    if (k >= n) return;
+
     float glo = FLT_MAX, ghi = -FLT_MAX;
     for (int i = lane; i < n; i += 64) {
         const float rad = (i > 0 ? fabsf(se[i - 1]) : 0.f) + (i + 1 < n ? fabsf(se[i]) : 0.f);
@@ -389,108 +460,111 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     const float eps = FLT_EPSILON;
     const float tnorm = fmaxf(fmaxf(fabsf(glo), fabsf(ghi)), FLT_MIN);
     const float pivmin = fmaxf(FLT_MIN, tnorm * eps * eps);
-    const float lo = glo - (4.f * eps * tnorm + pivmin), hi = ghi + (4.f * eps * tnorm + pivmin);
-    // relative width 2 eps |lambda|, floored at eps ||T|| / 1024 (vectors of
-    // close eigenvalues stay near orthogonal only with accurate shifts)
     const float floor_tol = eps * tnorm * (1.f / 1024.f);
-    // sde[i] = {d_i, e_{i-1}^2}
-    for (int i = tid; i < n; i += kThreads) sde[i] = make_float2(sd[i], i > 0 ? se[i - 1] * se[i - 1] : 0.f);
-    __syncthreads();
-    // multisection: the 4 lanes of quad k hold the k-th smallest eigenvalue's
-    // interval [a, b) (count(a) <= k < count(b), count(x) = #{i : q_i(x) < 0})
-    // and each round count it at the 4 points a + (b - a) (q + 1) / 5; the
-    // interval shrinks to the fifth that starts below the first point whose
-    // count exceeds k.  All four lanes compute the same points from the same
-    // a and b, so they stay in step.
-    {
-        const int k = tid >> 2, q = tid & 3;
-        if (k < n) {
-            float a = lo, b = hi;
-            for (int round = 0; round < 28 && b - a > 2.f * eps * fmaxf(fabsf(a), fabsf(b)) + floor_tol; ++round) {
-                const float w = (b - a) * 0.2f;
-                const float x = a + w * (float)(q + 1);
-                int cnt = 0;
-                float qv = 1.f;
-                for (int i = 0; i < n; ++i) {
-                    const float2 de = sde[i];
-                    qv = (de.x - x) - de.y * __builtin_amdgcn_rcpf(qv);
-                    if (fabsf(qv) < pivmin) qv = -pivmin;
-                    cnt += qv < 0.f;
-                }
-                // first point of the quad past the k-th eigenvalue (4 if none)
-                float first = cnt > k ? (float)q : 4.f;
-                first = fminf(first, dpp_move<kDppXor1>(first));
-                first = fminf(first, dpp_move<kDppXor2>(first));
-                const int m = (int)first;
-                const float na = m > 0 ? a + w * (float)m : a;
-                const float nb = m < 4 ? a + w * (float)(m + 1) : b;
-                a = na;
-                b = nb;
-            }
-            if (q == 0) slam[k] = 0.5f * (a + b);
+    float a = glo - (4.f * eps * tnorm + pivmin), b = ghi + (4.f * eps * tnorm + pivmin);
+    // a and b are the same in every lane; lane q counts at a + (q + 1) (b - a) / 65
+    for (int round = 0; round < 16 && b - a > 2.f * eps * fmaxf(fabsf(a), fabsf(b)) + floor_tol; ++round) {
+        const float wd = (b - a) * (1.f / 65.f);
+        const float x = a + wd * (float)(lane + 1);
+        int cnt = 0;
+        float qv = 1.f;
+        for (int i = 0; i < n; ++i) {
+            const float2 de = sde[i];
+            qv = (de.x - x) - de.y * __builtin_amdgcn_rcpf(qv);
+            if (fabsf(qv) < pivmin) qv = -pivmin;
+            cnt += qv < 0.f;
+        }
+        // first point past the k-th eigenvalue (64 if none)
+        const unsigned long long past = __ballot(cnt > k);
+        const int m = past ? __ffsll((long long)past) - 1 : 64;
+        const float na = m > 0 ? a + wd * (float)m : a;
+        const float nb = m < 64 ? a + wd * (float)(m + 1) : b;
+        a = na;
+        b = nb;
+    }
+    const float lam = 0.5f * (a + b);
+
+    // pivots of T - lam I = L+ D+ L+^T (lane 0, i upwards) = U- D- U-^T (lane 1, i downwards)
+    float *P = &piv[wid][0][0];
+    float *z = zc[wid];
+    if (lane < 2) {
+        const bool fw = lane == 0;
+        float p = 1.f;
+        for (int s = 0; s < n; ++s) {
+            const int i = fw ? s : n - 1 - s;
+            const float e2 = s == 0 ? 0.f : (fw ? sde[i].y : sde[i + 1].y);
+            p = (sd[i] - lam) - e2 * __builtin_amdgcn_rcpf(p);
+            if (fabsf(p) < pivmin) p = -pivmin;
+            P[lane * kTriMaxN + i] = p;
         }
     }
-    __syncthreads();
-
-    // ---------------------------------------------------------------- 3. vectors of T
-    JOLT_PROBE(3);
-    float *Z = B1;     // Z[i * ld + k]: column k belongs to the k-th smallest eigenvalue
-    if (tid < n) {
-        const int k = tid;
-        const float lam = slam[k];
-        float dp = sd[0] - lam;
-        if (fabsf(dp) < pivmin) dp = -pivmin;
-        Z[k] = dp;
-        for (int i = 1; i < n; ++i) {
-            dp = (sd[i] - lam) - sde[i].y * __builtin_amdgcn_rcpf(dp);
-            if (fabsf(dp) < pivmin) dp = -pivmin;
-            Z[i * ld + k] = dp;
-        }
-        float dm = sd[n - 1] - lam;
-        if (fabsf(dm) < pivmin) dm = -pivmin;
-        float best = fabsf(Z[(n - 1) * ld + k]);
-        int r = n - 1;
+    wave_lds_sync();
+    // twist index: gamma_i = D+_i + D-_i - (d_i - lam), gamma_{n-1} = D+_{n-1}
+    int r = n - 1;
+    if (lane == 0) {
+        float best = fabsf(P[n - 1]);
         for (int i = n - 2; i >= 0; --i) {
-            dm = (sd[i] - lam) - sde[i + 1].y * __builtin_amdgcn_rcpf(dm);
-            if (fabsf(dm) < pivmin) dm = -pivmin;
-            const float g = fabsf(Z[i * ld + k] + dm - (sd[i] - lam));
+            const float g = fabsf(P[i] + P[kTriMaxN + i] - (sd[i] - lam));
             if (g <= best) {
                 best = g;
                 r = i;
             }
         }
-        // z_r = 1; z_i = -(e_i / D+_i) z_{i+1} above r; z_{i+1} = -(e_i / D-_{i+1}) z_i below
-        float nrm = 1.f, z = 1.f;
-        for (int i = r - 1; i >= 0; --i) {
-            z = -(se[i] * __builtin_amdgcn_rcpf(Z[i * ld + k])) * z;
-            Z[i * ld + k] = z;
-            nrm += z * z;
-        }
-        dm = sd[n - 1] - lam;
-        if (fabsf(dm) < pivmin) dm = -pivmin;
-        if (r < n - 1) Z[(n - 1) * ld + k] = dm;
-        for (int i = n - 2; i > r; --i) {
-            dm = (sd[i] - lam) - sde[i + 1].y * __builtin_amdgcn_rcpf(dm);
-            if (fabsf(dm) < pivmin) dm = -pivmin;
-            Z[i * ld + k] = dm;
-        }
-        Z[r * ld + k] = 1.f;
-        z = 1.f;
-        for (int i = r; i + 1 < n; ++i) {
-            z = -(se[i] * __builtin_amdgcn_rcpf(Z[(i + 1) * ld + k])) * z;
-            Z[(i + 1) * ld + k] = z;
-            nrm += z * z;
-        }
-        if (!(nrm < FLT_MAX)) s_fail = 1;
-        const float inv = 1.f / sqrtf(nrm);
-        for (int i = 0; i < n; ++i) Z[i * ld + k] *= inv;
     }
-    __syncthreads();
+    r = __builtin_amdgcn_readfirstlane(r);
+    // z_r = 1; z_i = -(e_i / D+_i) z_{i+1} above r (lane 0), z_i = -(e_{i-1} / D-_i) z_{i-1} below (lane 1)
+    if (lane < 2) {
+        const bool up = lane == 0;
+        const int len = up ? r : n - 1 - r;
+        if (up) z[r] = 1.f;
+        float zz = 1.f;
+        for (int s = 0; s < len; ++s) {
+            const int i = up ? r - 1 - s : r + 1 + s;
+            const float ev = up ? se[i] : se[i - 1];
+            const float pv = P[lane * kTriMaxN + i];
+            zz = -(ev * __builtin_amdgcn_rcpf(pv)) * zz;
+            z[i] = zz;
+        }
+    }
+    wave_lds_sync();
+    float ss = 0.f;
+    for (int i = lane; i < n; i += 64) ss += z[i] * z[i];
+    const float nrm = wave_sum(ss);
+    if (!(nrm < FLT_MAX) && lane == 0) *w.flag = 1;
+    const float inv = 1.f / sqrtf(nrm);
+    for (int i = lane; i < n; i += 64) w.zt[(size_t)k * n + i] = z[i] * inv;
+    if (lane == 0) w.lam[k] = lam;
+}
 
-    if (s_fail) {
+// ---------------------------------------------------------------- 4 + 5 and output
+// Back-transform, Newton-Schulz polish and the output of one matrix per
+// workgroup, from what k_eig_tridiag and k_eig_trivec left in the workspace.
+__global__ __launch_bounds__(kThreads) void k_eig_backtr(JacBatch batch, int ld, int boff, int soff) {
+    extern __shared__ float sm[];
+    __shared__ float slam[kTriMaxN], stau[kTriMaxN];
+    __shared__ float sred[2 * kWaves];
+    const JacItem &it = batch.it[blockIdx.x];
+    const int n = it.n;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float *A = sm;          // reflectors in its rows; later M
+    float *B1 = sm + boff;  // Z, transformed in place into V
+    float *sep = soff >= 0 ? sm + soff : nullptr;
+    const TriWs w = tri_ws(it.tw, n);
+    if (*w.flag) {
         if (tid == 0) *it.sweeps_out = kEigRetry;
         return;
     }
+    for (int e = tid; e < n * n; e += kThreads) {
+        const int r = e / n, c = e - r * n;
+        A[r * ld + c] = w.a[e];
+        B1[c * ld + r] = w.zt[e];     // Z(c, r) = row r of Z^T
+    }
+    for (int i = tid; i < n; i += kThreads) {
+        stau[i] = w.tau[i];
+        slam[i] = w.lam[i];
+    }
+    __syncthreads();
+    float *Z = B1;     // Z[i * ld + k]: column k belongs to the k-th smallest eigenvalue
 
     // ---------------------------------------------------------------- 4. V = Q Z
     // Q = H_0 H_1 ... H_{n-3} is applied to Z a block of 32 reflectors at a time,
@@ -696,15 +770,18 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     if (tid == 0) *it.sweeps_out = 0;
 }
 
+static hipError_t allow_lds(const void *fn) {
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, fn);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - (int)fa.sharedSizeBytes);
+    return e;
+}
 static hipError_t allow_lds_tri() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
-        const void *fn = reinterpret_cast<const void *>(k_eig_tridiag);
-        hipFuncAttributes fa;
-        hipError_t e = hipFuncGetAttributes(&fa, fn);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    160 * 1024 - (int)fa.sharedSizeBytes);
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_eig_tridiag));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_backtr));
         state = e;
     }
     return state;
@@ -728,11 +805,21 @@ hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     if (maxN > kTriMaxN) return hipErrorInvalidValue;
     for (int i = 0; i < b.n; ++i)
-        if (!b.it[i].sweeps_out || b.it[i].n > maxN) return hipErrorInvalidValue;
+        if (!b.it[i].sweeps_out || !b.it[i].tw || b.it[i].n > maxN) return hipErrorInvalidValue;
     if (hipError_t e = allow_lds_tri(); e != hipSuccess) return e;
-    KTimeScope kts("k_eig_tridiag", s);
     const TriLayout L = tri_layout(maxN);
-    hipLaunchKernelGGL(k_eig_tridiag, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff, L.poff, L.soff);
+    {
+        KTimeScope kts("k_eig_tridiag", s);
+        hipLaunchKernelGGL(k_eig_tridiag, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff, L.poff);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    {
+        KTimeScope kts("k_eig_trivec", s);
+        hipLaunchKernelGGL(k_eig_trivec, dim3((maxN + kVecWaves - 1) / kVecWaves, b.n), dim3(64 * kVecWaves), 0, s, b);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    KTimeScope kts("k_eig_backtr", s);
+    hipLaunchKernelGGL(k_eig_backtr, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff, L.soff);
     return hipGetLastError();
 }
 

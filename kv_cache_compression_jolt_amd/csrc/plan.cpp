@@ -17,6 +17,7 @@
 #include <chrono>
 #include <cmath>
 #include <cstdio>
+#include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -55,6 +56,7 @@ struct Scratch {
     size_t omt, yt, ypart, qh, ql, zt, zb, xpart, gpart, gram, lmat, wmat, vmat, lamk, sweeps;
     size_t gfpart, gf, pmat, gt, vt, lamT, uh, ul;
     size_t eA, eT, eV, eVT, eR, eRlam, eNorm, eSw;     // block Jacobi (n > 142)
+    size_t etri, ftri;      // tridiagonal solver workspaces (token, feature); SIZE_MAX if unused
     int eN;                                             // padded size, 0 if unused
 };
 
@@ -132,6 +134,9 @@ void reserve_scratch(const jolt_config &cfg, const Dims &D, Bump &b, Scratch &s)
     }
     s.sweeps = b.take(16);
     const int ne = token_eig_n(cfg, D);
+    // the token and feature eigenproblems run at the same time on two streams
+    s.etri = ne <= kTriMaxN ? b.take(eig_tri_ws_bytes(ne)) : SIZE_MAX;
+    s.ftri = D.d <= kTriMaxN ? b.take(eig_tri_ws_bytes(D.d)) : SIZE_MAX;
     s.eN = 0;
     if (ne > kJacobiMaxN) {
         const size_t N = (size_t)round_up(ne, 128), P = N / 128;
@@ -271,6 +276,7 @@ struct EigReq {
     float *lam;
     int *sw;
     const Scratch *S;
+    float *tw;       // tridiagonal solver workspace (n <= kTriMaxN)
 };
 
 int rr_pos_host(int i, int round, int m) {
@@ -394,10 +400,11 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
         return JOLT_OK;
     };
     for (const EigReq &r : reqs) {
-        if (r.n <= kTriMaxN && r.sw) {
+        if (r.n <= kTriMaxN && r.sw && r.tw) {
             JacItem &j = tb.it[tb.n++];
             j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
             j.raw = 0;
+            j.tw = r.tw;
             maxT = std::max(maxT, r.n);
             if (tb.n == 64)
                 if (jolt_status s = flush_tri()) return s;
@@ -522,7 +529,8 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
     for (int i = 0; i < nb; ++i)
         feigs.push_back(EigReq{F(S[i].gf), d, d, reinterpret_cast<float *>(ws + pl.item[i0 + i].uf), d,
                                reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_f),
-                               reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps), &S[i]});
+                               reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps), &S[i],
+                               S[i].ftri != SIZE_MAX ? F(S[i].ftri) : nullptr});
     // ---- feature Gram, ||X||^2 and the feature eigenproblems, on the side
     // stream: forked when the token eigenproblems start (one workgroup per
     // matrix leaves most CUs and HBM idle for this), joined before the core,
@@ -699,7 +707,8 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
             for (int i = 0; i < nb; ++i)
                 eigs.push_back(EigReq{F(S[i].wmat), D[i].kp, D[i].k, F(S[i].vmat), D[i].kp,
                                       reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),
-                                      reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i]});
+                                      reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i],
+                                      S[i].etri != SIZE_MAX ? F(S[i].etri) : nullptr});
             if ((s = feature_gram())) return s;
             jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
             if (es) return es;
@@ -740,7 +749,8 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         for (int i = 0; i < nb; ++i)
             eigs.push_back(EigReq{F(S[i].gt), D[i].T, D[i].T, F(S[i].vt), D[i].T,
                                   reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),
-                                  reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i]});
+                                  reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i],
+                                  S[i].etri != SIZE_MAX ? F(S[i].etri) : nullptr});
         if (jolt_status fs = feature_gram()) return fs;
         jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
         if (es) return es;

@@ -113,6 +113,7 @@ struct JacItem {
     int n, lda, ldv;
     int raw;             // 1: eigenpairs in Jacobi order (no sort / sign change)
     int *sweeps_out;     // sweeps used, or -1 if the cap was hit
+    float *tw;           // tridiagonal solver only: eig_tri_ws_bytes(n) of device workspace
 };
 struct JacBatch { JacItem it[64]; int n; };
 constexpr int kJacobiMaxN = 142;
@@ -121,9 +122,11 @@ hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStr
 
 // Householder tridiagonal eigensolver for n <= kTriMaxN (same outputs as the
 // Jacobi kernel; sweeps_out is required and receives 0, or kEigRetry when the
-// matrix must be handed to the Jacobi kernel)
+// matrix must be handed to the Jacobi kernel; every item needs its own tw of
+// eig_tri_ws_bytes(n), 16-byte aligned, which the three launches share)
 constexpr int kTriMaxN = 140;
 constexpr int kEigRetry = -2;
+inline size_t eig_tri_ws_bytes(int n) { return (((size_t)2 * n * n + 4 * (size_t)n + 1) * 4 + 255) / 256 * 256; }
 hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s);
 
 // block Jacobi state of one large symmetric matrix (N = padded size, multiple of 128)
