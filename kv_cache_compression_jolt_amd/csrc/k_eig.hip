@@ -411,11 +411,11 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
 }
 
 // ---------------------------------------------------------------- 2 + 3. eigenpairs of T
-// One wave per eigenvalue k (the k-th smallest) of the tridiagonal T = (d, e)
-// that k_eig_tridiag left in the workspace, so that a batch spreads over the
-// chip instead of one CU per matrix:
-//   2. multisection on Sturm counts (Golub & Van Loan sec. 8.4.1): the 64
-//      lanes count at the 64 inner points of 65 equal sections of the
+// Every eigenpair of the tridiagonal T = (d, e) that k_eig_tridiag left in the
+// workspace, a group of 16 lanes per eigenvalue k (the k-th smallest), four
+// groups per wave, so that a batch spreads over the chip:
+//   2. multisection on Sturm counts (Golub & Van Loan sec. 8.4.1): the group's
+//      16 lanes count at the 16 inner points of 17 equal sections of the
 //      interval [a, b) that holds it (count(a) <= k < count(b), count(x) =
 //      #{i : q_i(x) < 0}); the interval shrinks to the section that starts
 //      below the first point whose count exceeds k, to a relative width of
@@ -423,31 +423,47 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
 //      near orthogonal only with accurate shifts);
 //   3. the eigenvector from a twisted factorization of T - lambda I (Dhillon &
 //      Parlett, Orthogonal eigenvectors and relative gaps, 2004): lanes 0 and 1
-//      run the forward and backward LDL^T pivots side by side, lane 0 takes
-//      the twist index r where |gamma| is smallest (the first such index),
-//      lanes 0 and 1 run the one-sided recurrences up and down from z_r = 1,
-//      and the wave normalises.
-// Writes lambda_k and row k of Z^T; sets the fail flag when a vector overflows.
-constexpr int kVecWaves = 4;
+//      of the group run the forward and backward LDL^T pivots side by side,
+//      the group finds the twist index r where |gamma| is smallest (the first
+//      such index) and the factors of the one-sided recurrences, lanes 0 and 1
+//      run their products up and down from z_r = 1, and the group normalises.
+// The sequential recurrences read LDS in batches of 8.  Writes lambda_k and
+// row k of Z^T; sets the fail flag when a vector overflows.
+constexpr int kVecWaves = 1;                          // one-wave workgroups spread evenly
+constexpr int kVecGroup = 16;                           // lanes per eigenvalue
+constexpr int kVecPerWave = 64 / kVecGroup;
+constexpr int kVecPad = kTriMaxN + 24;                  // room for the batch reads past the end
 __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch) {
-    __shared__ float sd[kTriMaxN], se[kTriMaxN];
-    __shared__ float2 sde[kTriMaxN];                  // {d_i, e_{i-1}^2}
-    __shared__ float piv[kVecWaves][2][kTriMaxN];     // forward / backward pivots
-    __shared__ float zc[kVecWaves][kTriMaxN];
+    __shared__ float sd[kVecPad], se[kVecPad];
+    __shared__ float2 sde[kVecPad];                     // {d_i, e_{i-1}^2}
+    __shared__ float tx[2][kTriMaxN], te[2][kTriMaxN];  // d, e^2 in step order: [0] up, [1] down
+    __shared__ float piv[kVecWaves][kVecPerWave][2][kTriMaxN];   // forward / backward pivots
+    __shared__ float zc[kVecWaves][kVecPerWave][kTriMaxN];
     const JacItem &it = batch.it[blockIdx.y];
     const int n = it.n;
-    if ((int)blockIdx.x * kVecWaves >= n) return;
+    constexpr int kPerBlock = kVecWaves * kVecPerWave;
+    if ((int)blockIdx.x * kPerBlock >= n) return;
     const TriWs w = tri_ws(it.tw, n);
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    for (int i = tid; i < n; i += 64 * kVecWaves) {
-        const float di = w.d[i], em = i > 0 ? w.e[i - 1] : 0.f;
+    for (int i = tid; i < kVecPad; i += 64 * kVecWaves) {
+        const float di = i < n ? w.d[i] : 0.f, em = i > 0 && i <= n ? w.e[i - 1] : 0.f;
         sd[i] = di;
-        se[i] = w.e[i];
+        se[i] = i < n ? w.e[i] : 0.f;
         sde[i] = make_float2(di, em * em);
+        if (i < n) {
+            const float er = i > 0 ? w.e[n - 1 - i] : 0.f;     // e_{n-1-i}, none at step 0
+            tx[0][i] = di;
+            te[0][i] = em * em;
+            tx[1][i] = w.d[n - 1 - i];
+            te[1][i] = er * er;
+        }
     }
     __syncthreads();
-    const int k = blockIdx.x * kVecWaves + wid;
-    if (k >= n) return;
+    const int g = lane / kVecGroup, q = lane % kVecGroup;
+    const int kw = blockIdx.x * kPerBlock + wid * kVecPerWave;     // the wave's first eigenvalue
+    if (kw >= n) return;
+    const int k = kw + g;
+    const bool kv = k < n;
 
     float glo = FLT_MAX, ghi = -FLT_MAX;
     for (int i = lane; i < n; i += 64) {
@@ -461,79 +477,159 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch) {
     const float tnorm = fmaxf(fmaxf(fabsf(glo), fabsf(ghi)), FLT_MIN);
     const float pivmin = fmaxf(FLT_MIN, tnorm * eps * eps);
     const float floor_tol = eps * tnorm * (1.f / 1024.f);
+    // a and b are the same in the lanes of a group; lane q counts at a + (q + 1) (b - a) / 17
     float a = glo - (4.f * eps * tnorm + pivmin), b = ghi + (4.f * eps * tnorm + pivmin);
-    // a and b are the same in every lane; lane q counts at a + (q + 1) (b - a) / 65
-    for (int round = 0; round < 16 && b - a > 2.f * eps * fmaxf(fabsf(a), fabsf(b)) + floor_tol; ++round) {
-        const float wd = (b - a) * (1.f / 65.f);
-        const float x = a + wd * (float)(lane + 1);
+    const unsigned long long gmask = 0xFFFFull << (kVecGroup * g);
+    for (int round = 0; round < 24; ++round) {
+        const bool open = kv && b - a > 2.f * eps * fmaxf(fabsf(a), fabsf(b)) + floor_tol;
+        if (!__ballot(open)) break;
+        const float wd = (b - a) * (1.f / (kVecGroup + 1));
+        const float x = a + wd * (float)(q + 1);
+        // q_i = (d_i - x) - e_{i-1}^2 / q_{i-1}; a |q_i| below pivmin counts as -pivmin
         int cnt = 0;
         float qv = 1.f;
-        for (int i = 0; i < n; ++i) {
-            const float2 de = sde[i];
-            qv = (de.x - x) - de.y * __builtin_amdgcn_rcpf(qv);
+        auto step = [&](float2 de) {
+            qv = fmaf(-de.y, __builtin_amdgcn_rcpf(qv), de.x - x);
             if (fabsf(qv) < pivmin) qv = -pivmin;
-            cnt += qv < 0.f;
+            cnt += (int)(__float_as_uint(qv) >> 31);
+        };
+        // batches of 8 from LDS, alternating between two register sets so that
+        // one is read while the other is used (reads past n hit the padding)
+        float2 ba[8], bb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ba[u] = sde[u];
+        int i0 = 0;
+        for (; i0 + 16 <= n; i0 += 16) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) bb[u] = sde[i0 + 8 + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) step(ba[u]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ba[u] = sde[i0 + 16 + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) step(bb[u]);
         }
-        // first point past the k-th eigenvalue (64 if none)
-        const unsigned long long past = __ballot(cnt > k);
-        const int m = past ? __ffsll((long long)past) - 1 : 64;
-        const float na = m > 0 ? a + wd * (float)m : a;
-        const float nb = m < 64 ? a + wd * (float)(m + 1) : b;
-        a = na;
-        b = nb;
+        if (i0 + 8 <= n) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) bb[u] = sde[i0 + 8 + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) step(ba[u]);
+#pragma unroll
+            for (int u = 0; u < 7; ++u)
+                if (i0 + 8 + u < n) step(bb[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 7; ++u)
+                if (i0 + u < n) step(ba[u]);
+        }
+        // first point of the group past the k-th eigenvalue (kVecGroup if none)
+        const unsigned long long past = (__ballot(cnt > k) & gmask) >> (kVecGroup * g);
+        const int m = past ? __ffsll((long long)past) - 1 : kVecGroup;
+        if (open) {
+            const float na = m > 0 ? a + wd * (float)m : a;
+            const float nb = m < kVecGroup ? a + wd * (float)(m + 1) : b;
+            a = na;
+            b = nb;
+        }
     }
     const float lam = 0.5f * (a + b);
 
-    // pivots of T - lam I = L+ D+ L+^T (lane 0, i upwards) = U- D- U-^T (lane 1, i downwards)
-    float *P = &piv[wid][0][0];
-    float *z = zc[wid];
-    if (lane < 2) {
-        const bool fw = lane == 0;
-        float p = 1.f;
-        for (int s = 0; s < n; ++s) {
-            const int i = fw ? s : n - 1 - s;
-            const float e2 = s == 0 ? 0.f : (fw ? sde[i].y : sde[i + 1].y);
-            p = (sd[i] - lam) - e2 * __builtin_amdgcn_rcpf(p);
+    // pivots of T - lam I = L+ D+ L+^T (lane 0 of the group, i upwards) and
+    // U- D- U-^T (lane 1, i downwards), both in step order s: lane 1 reads
+    // the reversed copies of d and e^2, and P[1][s] = D-_{n-1-s}
+    float *P = &piv[wid][g][0][0];
+    float *z = zc[wid][g];
+    if (kv && q < 2) {
+        const float *xs = tx[q], *es = te[q];
+        float *ps = P + q * kTriMaxN;
+        float p = 1.f;     // step 0 has e^2 = 0: p = d - lam
+        auto step = [&](float xv, float ev) {
+            p = fmaf(-ev, __builtin_amdgcn_rcpf(p), xv - lam);
             if (fabsf(p) < pivmin) p = -pivmin;
-            P[lane * kTriMaxN + i] = p;
+            return p;
+        };
+        int s0 = 0;
+        for (; s0 + 8 <= n; s0 += 8) {
+            float xv[8], ev[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                xv[u] = xs[s0 + u];
+                ev[u] = es[s0 + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ps[s0 + u] = step(xv[u], ev[u]);
         }
+        for (; s0 < n; ++s0) ps[s0] = step(xs[s0], es[s0]);
     }
     wave_lds_sync();
-    // twist index: gamma_i = D+_i + D-_i - (d_i - lam), gamma_{n-1} = D+_{n-1}
+    // twist index r: the first i where |gamma_i| is smallest, gamma_i =
+    // D+_i + D-_i - (d_i - lam) for i < n - 1 and gamma_{n-1} = D+_{n-1}; each
+    // lane of the group takes i = q mod 16, then the group reduces (value,
+    // index) pairs
+    float best = FLT_MAX;
     int r = n - 1;
-    if (lane == 0) {
-        float best = fabsf(P[n - 1]);
-        for (int i = n - 2; i >= 0; --i) {
-            const float g = fabsf(P[i] + P[kTriMaxN + i] - (sd[i] - lam));
-            if (g <= best) {
-                best = g;
+    if (kv) {
+        for (int i = q; i < n; i += kVecGroup) {
+            const float gv = i == n - 1 ? fabsf(P[i]) : fabsf(P[i] + P[kTriMaxN + n - 1 - i] - (sd[i] - lam));
+            if (gv < best || (gv == best && i < r)) {
+                best = gv;
                 r = i;
             }
         }
     }
-    r = __builtin_amdgcn_readfirstlane(r);
-    // z_r = 1; z_i = -(e_i / D+_i) z_{i+1} above r (lane 0), z_i = -(e_{i-1} / D-_i) z_{i-1} below (lane 1)
-    if (lane < 2) {
-        const bool up = lane == 0;
-        const int len = up ? r : n - 1 - r;
-        if (up) z[r] = 1.f;
+#pragma unroll
+    for (int off = 1; off < kVecGroup; off <<= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int orr = __shfl_xor(r, off);
+        if (ob < best || (ob == best && orr < r)) {
+            best = ob;
+            r = orr;
+        }
+    }
+    // z_r = 1; z_i = f_i z_{i+1} above r with f_i = -(e_i / D+_i), z_i = f_i z_{i-1}
+    // below with f_i = -(e_{i-1} / D-_i): the factors by the whole group, the
+    // running products by lanes 0 (up) and 1 (down)
+    if (kv) {
+        for (int i = q; i < n; i += kVecGroup) {
+            float f = 1.f;
+            if (i < r) f = -(se[i] * __builtin_amdgcn_rcpf(P[i]));
+            else if (i > r) f = -(se[i - 1] * __builtin_amdgcn_rcpf(P[kTriMaxN + n - 1 - i]));
+            z[i] = f;
+        }
+    }
+    wave_lds_sync();
+    if (kv && q < 2) {
+        const bool up = q == 0;
+        const int len = up ? r : n - 1 - r, di = up ? -1 : 1;
         float zz = 1.f;
-        for (int s = 0; s < len; ++s) {
-            const int i = up ? r - 1 - s : r + 1 + s;
-            const float ev = up ? se[i] : se[i - 1];
-            const float pv = P[lane * kTriMaxN + i];
-            zz = -(ev * __builtin_amdgcn_rcpf(pv)) * zz;
+        int i = r + di;
+        int s0 = 0;
+        for (; s0 + 8 <= len; s0 += 8) {
+            float fv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) fv[u] = z[i + di * u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                zz = fv[u] * zz;
+                z[i + di * u] = zz;
+            }
+            i += 8 * di;
+        }
+        for (; s0 < len; ++s0, i += di) {
+            zz = z[i] * zz;
             z[i] = zz;
         }
     }
     wave_lds_sync();
     float ss = 0.f;
-    for (int i = lane; i < n; i += 64) ss += z[i] * z[i];
-    const float nrm = wave_sum(ss);
-    if (!(nrm < FLT_MAX) && lane == 0) *w.flag = 1;
+    if (kv)
+        for (int i = q; i < n; i += kVecGroup) ss += z[i] * z[i];
+    const float nrm = group16_sum(ss);
+    if (!kv) return;
+    if (!(nrm < FLT_MAX) && q == 0) *w.flag = 1;
     const float inv = 1.f / sqrtf(nrm);
-    for (int i = lane; i < n; i += 64) w.zt[(size_t)k * n + i] = z[i] * inv;
-    if (lane == 0) w.lam[k] = lam;
+    for (int i = q; i < n; i += kVecGroup) w.zt[(size_t)k * n + i] = z[i] * inv;
+    if (q == 0) w.lam[k] = lam;
 }
 
 // ---------------------------------------------------------------- 4 + 5 and output
@@ -815,7 +911,8 @@ hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
     }
     {
         KTimeScope kts("k_eig_trivec", s);
-        hipLaunchKernelGGL(k_eig_trivec, dim3((maxN + kVecWaves - 1) / kVecWaves, b.n), dim3(64 * kVecWaves), 0, s, b);
+        constexpr int per = kVecWaves * kVecPerWave;
+        hipLaunchKernelGGL(k_eig_trivec, dim3((maxN + per - 1) / per, b.n), dim3(64 * kVecWaves), 0, s, b);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     KTimeScope kts("k_eig_backtr", s);
