@@ -36,9 +36,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
-KERNELS = ["k_eig_tridiag", "k_eig_trivec", "k_eig_backtr", "k_chol_inv", "k_apply_linv", "k_sym_gram", "k_gemm", "k_reduce", "k_xm", "k_xtq",
+KERNELS = ["k_eig_tridiag", "k_eig_trivec", "k_eig_backtr", "k_eig_polish", "k_chol_inv", "k_apply_linv", "k_sym_gram", "k_gemm", "k_reduce", "k_xm", "k_xtq",
            "k_gram_rows", "k_build_wt", "k_encode", "k_decode", "k_jacobi_lds"]
-KERNEL_SOURCE = {"k_eig_tridiag": "k_eig.hip", "k_eig_trivec": "k_eig.hip", "k_eig_backtr": "k_eig.hip", "k_chol_inv": "k_orth.hip", "k_apply_linv": "k_orth.hip",
+KERNEL_SOURCE = {"k_eig_tridiag": "k_eig.hip", "k_eig_trivec": "k_eig.hip", "k_eig_backtr": "k_eig.hip", "k_eig_polish": "k_eig.hip", "k_chol_inv": "k_orth.hip", "k_apply_linv": "k_orth.hip",
                  "k_gemm": "k_gemm.hip", "k_sym_gram": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
                  "k_encode": "k_codec.hip", "k_decode": "k_codec.hip", "k_build_wt": "k_codec.hip"}
 
@@ -70,11 +70,12 @@ def work_per_step(cfg, jitems, allocs):
                                                 for n, it in zip(n_lhd, jitems)))
     out["k_gram_rows"] = ("bytes", xb + sum(4 * it.d * it.d for it in jitems))
     # dense symmetric eigendecompositions (token k x k and feature d x d per item):
-    # Householder tridiagonalization 4/3 n^3; back-transform Q Z 2 n^3 plus the
-    # polish's check V^T V, n^3 on its upper tiles (the tridiagonal eigenpairs
-    # in between are O(n^2) per multisection round)
+    # Householder tridiagonalization 4/3 n^3; back-transform Q Z 2 n^3; polish:
+    # the check V^T V on its upper tiles n^3 and one update V E 2 n^3 (the
+    # tridiagonal eigenpairs in between are O(n^2) per multisection round)
     out["k_eig_tridiag"] = ("flops", sum(4.0 / 3 * (k ** 3 + it.d ** 3) for it in jitems))
-    out["k_eig_backtr"] = ("flops", sum(3.0 * (k ** 3 + it.d ** 3) for it in jitems))
+    out["k_eig_backtr"] = ("flops", sum(2.0 * (k ** 3 + it.d ** 3) for it in jitems))
+    out["k_eig_polish"] = ("flops", sum(3.0 * (k ** 3 + it.d ** 3) for it in jitems))
     # CholeskyQR inverse factor: n^3 / 3 (factor) + n^3 / 3 (inverse), 2 q + 2 factorizations
     out["k_chol_inv"] = ("flops", sum((2 * q + 2) * (2.0 / 3) * k ** 3 for _ in jitems))
     # CholeskyQR Grams and B B^T (symmetric: k (k + 1) len flops each) and the L^-1

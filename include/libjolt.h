@@ -233,7 +233,7 @@ jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const float *a, i
 /* ---- measurement hooks -------------------------------------------------- */
 /* Launch timing of one of the library's kernels, named as in its source
  * ("k_decode", "k_encode", "k_xm", "k_xtq", "k_eig_tridiag", "k_eig_trivec",
- * "k_eig_backtr", "k_chol_inv",
+ * "k_eig_backtr", "k_eig_polish", "k_chol_inv",
  * "k_apply_linv", "k_gemm", "k_gram_rows", "k_reduce", "k_build_wt",
  * "k_jacobi_lds").  While a kernel's timer is on, each of its launches is
  * bracketed by a HIP event pair on its launch stream.  enable != 0 turns the

@@ -1,8 +1,10 @@
-// Symmetric eigensolver for small dense matrices (n <= kTriMaxN) in three
-// launches: k_eig_tridiag (step 1) and k_eig_backtr (steps 4, 5) run one
-// workgroup of 1024 threads per matrix with the matrix resident in LDS;
-// k_eig_trivec (steps 2, 3) runs one wave per eigenvalue over the whole chip.
-// They hand over through a per-matrix workspace (tri_ws).
+// Symmetric eigensolver for small dense matrices (n <= kTriMaxN) in four
+// launches that hand over through a per-matrix workspace (tri_ws):
+// k_eig_tridiag (step 1) and k_eig_polish (step 5, output) run one workgroup
+// of 1024 threads per matrix with the matrix resident in LDS; k_eig_trivec
+// (steps 2, 3, and the compact-WY T of each reflector block) runs a group of
+// 16 lanes per eigenvalue over the whole chip; k_eig_backtr (step 4) runs a
+// workgroup per 32 columns of each matrix.
 //
 //   1. Householder tridiagonalization Q^T A Q = T (Golub & Van Loan, Matrix
 //      Computations, sec. 8.3.1) in panels of 32 columns: within a panel the
@@ -10,7 +12,7 @@
 //      panel's V and W (the latrd form), then updated once on fp32 MFMA;
 //      the reflectors stay in the rows of A;
 //   2. every eigenvalue of T by multisection on Sturm counts (sec. 8.4.1),
-//      four lanes per eigenvalue, to a relative width of 2 eps;
+//      16 lanes per eigenvalue, to a relative width of 2 eps;
 //   3. every eigenvector of T from a twisted factorization of T - lambda I
 //      (Dhillon & Parlett, Orthogonal eigenvectors and relative gaps, 2004):
 //      forward and backward LDL^T pivots, the twist index where |gamma| is
@@ -45,25 +47,57 @@ constexpr int kWaves = kThreads / 64;
 // access pattern over them meets each LDS bank at most twice per wave
 constexpr int kPanelStride = 34;
 
-// Per-matrix workspace between the three launches (floats; eig_tri_ws_bytes
-// gives its size): A after the reduction (n x n, row-major, reflector j in row
-// j), Z^T (row k = the eigenvector of the k-th smallest eigenvalue of T), d,
-// e (e_{n-1} = 0), tau, the eigenvalues of T ascending, and a fail flag.
+// Per-matrix workspace between the launches (floats; eig_tri_ws_bytes gives
+// its size): A after the reduction (n x n, row-major, reflector j in row j),
+// Z^T (row k = the eigenvector of the k-th smallest eigenvalue of T, later
+// the back-transformed V^T), both with rows of np = n rounded up to 4 floats
+// (16-byte aligned), the compact-WY T of each block of 32 reflectors (32 x 32
+// row-major, zero below the diagonal), d, e (e_{n-1} = 0), tau, the
+// eigenvalues of T ascending, and a fail flag.
 struct TriWs {
-    float *a, *zt, *d, *e, *tau, *lam;
+    float *a, *zt, *tb, *d, *e, *tau, *lam;
     int *flag;
+    int np;
 };
+__device__ __forceinline__ int tri_blocks(int n) { return (max(n - 2, 0) + 31) >> 5; }
 __device__ __forceinline__ TriWs tri_ws(float *base, int n) {
-    const size_t nn = (size_t)n * n;
     TriWs w;
+    w.np = (n + 3) & ~3;
+    const size_t nn = (size_t)n * w.np;
     w.a = base;
     w.zt = base + nn;
-    w.d = w.zt + nn;
+    w.tb = w.zt + nn;
+    w.d = w.tb + 1024 * tri_blocks(n);
     w.e = w.d + n;
     w.tau = w.e + n;
     w.lam = w.tau + n;
     w.flag = reinterpret_cast<int *>(w.lam + n);
     return w;
+}
+
+// Reads rows [0, rows) of float4 columns [0, c4) of a global matrix (row
+// stride gs floats, rows 16-byte aligned) with B loads of each thread in
+// flight before their LDS stores: st(r, c, v) stores the float4 of row r at
+// columns 4c .. 4c + 3.  NT threads take part.
+template <int NT, int B, typename St>
+__device__ __forceinline__ void load_rows4(const float *g, int gs, int rows, int c4, int tid, St st) {
+    const int total = rows * c4;
+    for (int e0 = tid; e0 < total; e0 += NT * B) {
+        float4 v[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int e = min(e0 + NT * u, total - 1), r = e / c4, c = e - r * c4;
+            v[u] = *reinterpret_cast<const float4 *>(g + (size_t)r * gs + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int e = e0 + NT * u;
+            if (e < total) {
+                const int r = e / c4, c = e - r * c4;
+                st(r, c, v[u]);
+            }
+        }
+    }
 }
 
 
@@ -129,20 +163,6 @@ __device__ __forceinline__ void store_tiles(float *dst, const f32x16 &a0, const 
 
 }  // namespace
 
-// Scratch tile q (q < 5, 32 x 32, row stride *ts) for the back-transform:
-// in the free lower triangle of the A buffer when it has 128 rows or more
-// (off-diagonal blocks (2,0) (3,0) (3,1) (1,0) (2,1)), else in a separate
-// region.
-__device__ __forceinline__ float *scratch_tile(float *A, int ld, float *sep, int q, int *ts) {
-    if (!sep) {
-        const int R[5] = {2, 3, 3, 1, 2}, C[5] = {0, 0, 1, 0, 1};
-        *ts = ld;
-        return A + 32 * R[q] * ld + 32 * C[q];
-    }
-    *ts = 33;
-    return sep + q * 32 * 33;
-}
-
 // Column c = lane % 32 of T for a full block of 32 reflectors, in registers:
 // solves (diag(1 / tau) + strict_upper(G)) t = e_c from the last row up and
 // stores T(i, c), i <= c, at D[c * ld + i].  On entry G(i, r), i < r, is at
@@ -186,9 +206,23 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     float *Vp = B1, *Wp = B1 + poff;
 
     JOLT_PROBE(0);
-    for (int e = tid; e < n * n; e += kThreads) {
-        const int r = e / n, c = e - r * n;
-        A[r * ld + c] = 0.5f * (it.a[(size_t)r * it.lda + c] + it.a[(size_t)c * it.lda + r]);
+    // (A + A^T) / 2, eight entries of each thread in flight
+    for (int e0 = tid; e0 < n * n; e0 += 8 * kThreads) {
+        float x[8], y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = min(e0 + u * kThreads, n * n - 1), r = e / n, c = e - r * n;
+            x[u] = it.a[(size_t)r * it.lda + c];
+            y[u] = it.a[(size_t)c * it.lda + r];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * kThreads;
+            if (e < n * n) {
+                const int r = e / n, c = e - r * n;
+                A[r * ld + c] = 0.5f * (x[u] + y[u]);
+            }
+        }
     }
 
     // ---------------------------------------------------------------- 1. tridiagonalize
@@ -398,9 +432,9 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     // hand over to k_eig_trivec and k_eig_backtr: A (reflectors in its rows),
     // T = (d, e) and tau; the fail flag starts clear
     const TriWs w = tri_ws(it.tw, n);
-    for (int e = tid; e < n * n; e += kThreads) {
-        const int r = e / n, c = e - r * n;
-        w.a[e] = A[r * ld + c];
+    for (int e = tid; e < n * w.np; e += kThreads) {
+        const int r = e / w.np, c = e - r * w.np;
+        w.a[e] = c < n ? A[r * ld + c] : 0.f;
     }
     for (int i = tid; i < n; i += kThreads) {
         w.d[i] = sd[i];
@@ -433,18 +467,72 @@ constexpr int kVecWaves = 1;                          // one-wave workgroups spr
 constexpr int kVecGroup = 16;                           // lanes per eigenvalue
 constexpr int kVecPerWave = 64 / kVecGroup;
 constexpr int kVecPad = kTriMaxN + 24;                  // room for the batch reads past the end
-__global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch) {
-    __shared__ float sd[kVecPad], se[kVecPad];
-    __shared__ float2 sde[kVecPad];                     // {d_i, e_{i-1}^2}
-    __shared__ float tx[2][kTriMaxN], te[2][kTriMaxN];  // d, e^2 in step order: [0] up, [1] down
-    __shared__ float piv[kVecWaves][kVecPerWave][2][kTriMaxN];   // forward / backward pivots
-    __shared__ float zc[kVecWaves][kVecPerWave][kTriMaxN];
+constexpr int kYPitch = kTriMaxN + 1;                   // odd: lanes reading a column meet distinct banks
+// LDS of one k_eig_trivec workgroup in floats: the eigenpair role's arrays, or
+// the T role's reflector block and G / T buffer
+constexpr int kVecLdsEig = 4 * kVecPad + 4 * kTriMaxN + kVecPerWave * 3 * kTriMaxN;
+constexpr int kVecLdsWy = 32 * kYPitch + 32 * 33 + 32;
+constexpr int kVecLds = kVecLdsEig > kVecLdsWy ? kVecLdsEig : kVecLdsWy;
+
+// T of reflector block b for k_eig_backtr, one wave (the T role of
+// k_eig_trivec): G = Y^T Y of the block's 32 reflectors (Y(r, i) = v_{b0+i}(r),
+// zero for r <= b0 + i), then (diag(1 / tau) + strict_upper(G)) T = I column
+// by column (wblock_t_full).  A partial last block is padded with zero
+// reflectors of tau = 0, whose rows and columns of T come out zero.
+__device__ void wy_block(const TriWs &w, int n, int b, float *lds, int lane) {
+    const int mref = max(n - 2, 0), b0 = 32 * b, nbk = min(32, mref - b0);
+    float *Ys = lds;                    // Ys[i * kYPitch + r] = Y(r, i)
+    float *D = Ys + 32 * kYPitch;       // G(i, c), i < c, then T(i, c), i <= c, at D[c * 33 + i]
+    float *taus = D + 32 * 33;
+    for (int e = lane; e < 32 * kYPitch; e += 64) {
+        const int i = e / kYPitch, r = e - i * kYPitch;
+        Ys[e] = i < nbk && r > b0 + i && r < n ? w.a[(size_t)(b0 + i) * w.np + r] : 0.f;
+    }
+    if (lane < 32) taus[lane] = lane < nbk ? w.tau[b0 + lane] : 0.f;
+    wave_lds_sync();
+    const int m32 = lane & 31, kh = lane >> 5;
+    f32x16 g = {};
+    for (int k0 = b0; k0 < n; k0 += 8) {
+        float y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) y[u] = Ys[m32 * kYPitch + min(k0 + 2 * u + kh, kYPitch - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) g = __builtin_amdgcn_mfma_f32_32x32x2f32(y[u], y[u], g, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int r = frag_row(lane, q);
+        if (r < m32) D[m32 * 33 + r] = g[q];
+    }
+    wave_lds_sync();
+    wblock_t_full(D, 33, taus, m32, lane);
+    wave_lds_sync();
+    float *tb = w.tb + 1024 * b;
+    for (int e = lane; e < 1024; e += 64) {
+        const int i = e >> 5, c = e & 31;
+        tb[e] = i <= c ? D[c * 33 + i] : 0.f;
+    }
+}
+
+__global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch, int eig_blocks) {
+    __shared__ __attribute__((aligned(16))) float lds[kVecLds];
     const JacItem &it = batch.it[blockIdx.y];
     const int n = it.n;
-    constexpr int kPerBlock = kVecWaves * kVecPerWave;
-    if ((int)blockIdx.x * kPerBlock >= n) return;
     const TriWs w = tri_ws(it.tw, n);
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if ((int)blockIdx.x >= eig_blocks) {
+        const int b = blockIdx.x - eig_blocks;
+        if (b < tri_blocks(n)) wy_block(w, n, b, lds, lane);
+        return;
+    }
+    constexpr int kPerBlock = kVecWaves * kVecPerWave;
+    if ((int)blockIdx.x * kPerBlock >= n) return;
+    float *sd = lds, *se = sd + kVecPad;
+    float2 *sde = reinterpret_cast<float2 *>(se + kVecPad);      // {d_i, e_{i-1}^2}
+    float *tx = reinterpret_cast<float *>(sde + kVecPad);         // d, e^2 in step order: [0] up, [1] down
+    float *te = tx + 2 * kTriMaxN;
+    float *piv = te + 2 * kTriMaxN;                                // [wave][group][2][kTriMaxN] pivots
+    float *zc = piv + kVecWaves * kVecPerWave * 2 * kTriMaxN;      // [wave][group][kTriMaxN]
     for (int i = tid; i < kVecPad; i += 64 * kVecWaves) {
         const float di = i < n ? w.d[i] : 0.f, em = i > 0 && i <= n ? w.e[i - 1] : 0.f;
         sd[i] = di;
@@ -452,10 +540,10 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch) {
         sde[i] = make_float2(di, em * em);
         if (i < n) {
             const float er = i > 0 ? w.e[n - 1 - i] : 0.f;     // e_{n-1-i}, none at step 0
-            tx[0][i] = di;
-            te[0][i] = em * em;
-            tx[1][i] = w.d[n - 1 - i];
-            te[1][i] = er * er;
+            tx[i] = di;
+            te[i] = em * em;
+            tx[kTriMaxN + i] = w.d[n - 1 - i];
+            te[kTriMaxN + i] = er * er;
         }
     }
     __syncthreads();
@@ -537,10 +625,10 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch) {
     // pivots of T - lam I = L+ D+ L+^T (lane 0 of the group, i upwards) and
     // U- D- U-^T (lane 1, i downwards), both in step order s: lane 1 reads
     // the reversed copies of d and e^2, and P[1][s] = D-_{n-1-s}
-    float *P = &piv[wid][g][0][0];
-    float *z = zc[wid][g];
+    float *P = piv + (wid * kVecPerWave + g) * 2 * kTriMaxN;
+    float *z = zc + (wid * kVecPerWave + g) * kTriMaxN;
     if (kv && q < 2) {
-        const float *xs = tx[q], *es = te[q];
+        const float *xs = tx + q * kTriMaxN, *es = te + q * kTriMaxN;
         float *ps = P + q * kTriMaxN;
         float p = 1.f;     // step 0 has e^2 = 0: p = d - lam
         auto step = [&](float xv, float ev) {
@@ -628,166 +716,168 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch) {
     if (!kv) return;
     if (!(nrm < FLT_MAX) && q == 0) *w.flag = 1;
     const float inv = 1.f / sqrtf(nrm);
-    for (int i = q; i < n; i += kVecGroup) w.zt[(size_t)k * n + i] = z[i] * inv;
+    for (int i = q; i < w.np; i += kVecGroup) w.zt[(size_t)k * w.np + i] = i < n ? z[i] * inv : 0.f;
     if (q == 0) w.lam[k] = lam;
 }
 
-// ---------------------------------------------------------------- 4 + 5 and output
-// Back-transform, Newton-Schulz polish and the output of one matrix per
-// workgroup, from what k_eig_tridiag and k_eig_trivec left in the workspace.
-__global__ __launch_bounds__(kThreads) void k_eig_backtr(JacBatch batch, int ld, int boff, int soff) {
+// ---------------------------------------------------------------- 4. V = Q Z
+// Q = H_0 H_1 ... H_{n-3} applied to Z a block of 32 reflectors at a time,
+// last block first, in compact WY form: H_b0 ... H_b0+31 = I - Y T Y^T
+// (Schreiber & Van Loan's storage-efficient WY, T from the T role of
+// k_eig_trivec), Z <- Z - Y (T (Y^T Z)).  Columns of Z are independent, so one
+// workgroup takes a chunk of 32 columns of one matrix: per block, its waves
+// split the rows of S = Y^T Z_c, wave 0 forms M = T S, and the waves update
+// the row tiles Z_c -= Y M.  V_c goes back over Z_c^T in the workspace.
+constexpr int kBtWaves = 4;
+constexpr int kTile = 32 * 33;                          // a 32 x 32 LDS tile, row pitch 33
+__global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr(JacBatch batch, int ldy) {
     extern __shared__ float sm[];
-    __shared__ float slam[kTriMaxN], stau[kTriMaxN];
+    const JacItem &it = batch.it[blockIdx.y];
+    const int n = it.n, c0 = 32 * blockIdx.x;
+    if (c0 >= n) return;
+    const TriWs w = tri_ws(it.tw, n);
+    if (*w.flag) return;                                // k_eig_polish reports it
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m32 = lane & 31, kh = lane >> 5;
+    const int mref = max(n - 2, 0), nblk = tri_blocks(n), nt = (n + 31) >> 5;
+    float *Ys = sm;                      // Ys[j * ldy + r] = v_j(r) for r > j (row j of A)
+    float *Ts = Ys + mref * ldy;         // T_b(i, k) at Ts[b * kTile + i * 33 + k]
+    float *Zc = Ts + nblk * kTile;       // Z(r, c0 + m) at Zc[r * 33 + m]
+    float *Pt = Zc + n * 33;             // partial S of wave w: S(i, m) at Pt[w * kTile + i * 33 + m]
+    float *Mt = Pt + kBtWaves * kTile;   // M(k, m) at Mt[k * 33 + m]
+    constexpr int NT = 64 * kBtWaves;
+    const int c4 = w.np >> 2, ncol = min(32, n - c0);
+    load_rows4<NT, 8>(w.a, w.np, mref, c4, tid, [&](int r, int c, float4 v) {
+        float *d = Ys + r * ldy + 4 * c;
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    });
+    load_rows4<NT, 8>(w.tb, 32, 32 * nblk, 8, tid, [&](int r, int c, float4 v) {
+        float *d = Ts + (r >> 5) * kTile + (r & 31) * 33 + 4 * c;
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    });
+    // Z(r, c0 + m) = Z^T(c0 + m, r); columns past n read as zero
+    for (int e = tid; e < (32 - ncol) * n; e += NT) {
+        const int m = ncol + e / n, r = e - (e / n) * n;
+        Zc[r * 33 + m] = 0.f;
+    }
+    load_rows4<NT, 8>(w.zt + (size_t)c0 * w.np, w.np, ncol, c4, tid, [&](int m, int c, float4 v) {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * c + i < n) Zc[(4 * c + i) * 33 + m] = vv[i];
+    });
+    __syncthreads();
+    // Y(r, b0 + i): reflector b0 + i at row r, zero unless b0 + i < mref and b0 + i < r < n
+    auto Y = [&](int b0, int r, int i) {
+        const int j = b0 + i;
+        return ld_or_zero(Ys, min(j, mref - 1) * ldy + min(r, n - 1), j < mref && r > j && r < n);
+    };
+    for (int b = nblk - 1; b >= 0; --b) {
+        const int b0 = 32 * b;
+        // S = Y_b^T Z_c over rows b0 + 1 .. n - 1, split in runs of 8 rows over the waves
+        {
+            const int rows = n - 1 - b0, per = ((rows + 8 * kBtWaves - 1) / (8 * kBtWaves)) * 8;
+            const int r0 = b0 + 1 + wid * per, r1 = min(n, r0 + per);
+            f32x16 acc = {};
+            for (int k0 = r0; k0 < r1; k0 += 8) {
+                float ya[4], zb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = k0 + 2 * u + kh;
+                    const bool ok = r < r1;
+                    ya[u] = ok ? Y(b0, r, m32) : 0.f;
+                    zb[u] = ld_or_zero(Zc, min(r, n - 1) * 33 + m32, ok);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ya[u], zb[u], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) Pt[wid * kTile + frag_row(lane, q) * 33 + m32] = acc[q];
+        }
+        __syncthreads();
+        if (wid == 0) {
+            // M = T_b S, S the sum of the partials (T_b is upper triangular)
+            const float *T = Ts + b * kTile;
+            f32x16 acc = {};
+#pragma unroll
+            for (int k0 = 0; k0 < 32; k0 += 8) {
+                float ta[4], sb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int k = k0 + 2 * u + kh;
+                    ta[u] = T[m32 * 33 + k];
+                    float sv = 0.f;
+#pragma unroll
+                    for (int v = 0; v < kBtWaves; ++v) sv += Pt[v * kTile + k * 33 + m32];
+                    sb[u] = sv;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ta[u], sb[u], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) Mt[frag_row(lane, q) * 33 + m32] = acc[q];
+        }
+        __syncthreads();
+        // Z_c -= Y_b M on the row tiles that Y_b touches (rows > b0)
+        for (int rt = b + wid; rt < nt; rt += kBtWaves) {
+            f32x16 acc;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * rt + frag_row(lane, q);
+                acc[q] = ld_or_zero(Zc, min(row, n - 1) * 33 + m32, row < n);
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < 32; k0 += 8) {
+                float ya[4], mb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int k = k0 + 2 * u + kh;
+                    ya[u] = -Y(b0, 32 * rt + m32, k);
+                    mb[u] = Mt[k * 33 + m32];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ya[u], mb[u], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * rt + frag_row(lane, q);
+                if (row < n) Zc[row * 33 + m32] = acc[q];
+            }
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < ncol * n; e += NT) {
+        const int m = e / n, r = e - m * n;
+        w.zt[(size_t)(c0 + m) * w.np + r] = Zc[r * 33 + m];
+    }
+}
+
+// ---------------------------------------------------------------- 5 and output
+// Newton-Schulz polish and the output of one matrix per workgroup, V loaded
+// from the workspace.
+__global__ __launch_bounds__(kThreads) void k_eig_polish(JacBatch batch, int ld, int boff) {
+    extern __shared__ float sm[];
+    __shared__ float slam[kTriMaxN];
     __shared__ float sred[2 * kWaves];
     const JacItem &it = batch.it[blockIdx.x];
     const int n = it.n;
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    float *A = sm;          // reflectors in its rows; later M
-    float *B1 = sm + boff;  // Z, transformed in place into V
-    float *sep = soff >= 0 ? sm + soff : nullptr;
+    float *A = sm;          // E of the polish steps
+    float *V = sm + boff;   // V[r * ld + c]
     const TriWs w = tri_ws(it.tw, n);
     if (*w.flag) {
         if (tid == 0) *it.sweeps_out = kEigRetry;
         return;
     }
-    for (int e = tid; e < n * n; e += kThreads) {
-        const int r = e / n, c = e - r * n;
-        A[r * ld + c] = w.a[e];
-        B1[c * ld + r] = w.zt[e];     // Z(c, r) = row r of Z^T
-    }
-    for (int i = tid; i < n; i += kThreads) {
-        stau[i] = w.tau[i];
-        slam[i] = w.lam[i];
-    }
+    load_rows4<kThreads, 4>(w.zt, w.np, n, w.np >> 2, tid, [&](int k, int c, float4 v) {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * c + i < n) V[(4 * c + i) * ld + k] = vv[i];
+    });
+    for (int i = tid; i < n; i += kThreads) slam[i] = w.lam[i];
     __syncthreads();
-    float *Z = B1;     // Z[i * ld + k]: column k belongs to the k-th smallest eigenvalue
-
-    // ---------------------------------------------------------------- 4. V = Q Z
-    // Q = H_0 H_1 ... H_{n-3} is applied to Z a block of 32 reflectors at a time,
-    // last block first, in compact WY form: H_b0 ... H_b0+31 = I - Y T Y^T with
-    // T upper triangular and T^-1 = diag(1 / tau) + strict_upper(Y^T Y)
-    // (Schreiber & Van Loan's storage-efficient WY; the inverse form follows
-    // from the column recurrence of T), and Z <- Z - Y (T (Y^T Z)).
-    JOLT_PROBE(4);
     const int nt = (n + 31) >> 5, ntiles = nt * nt;
-    float *V = B1;     // V[r * ld + c]
-    {
-        const int mref = n > 2 ? n - 2 : 0, nblk = (mref + 31) >> 5;
-        const int m32 = lane & 31, kh = lane >> 5;
-        // Y(r, i) = v_{b0+i}(r): reflector b0 + i, nonzero for r > b0 + i
-        auto Y = [&](int b0, int nbk, int r, int i) {
-            return ld_or_zero(A, (b0 + min(i, nbk - 1)) * ld + min(r, n - 1), i < nbk && r > b0 + i && r < n);
-        };
-        // T_b for every block, one wave each.  G = Y^T Y goes first to the free
-        // strict lower triangle of diagonal block b (G(i, c), i < c, at
-        // A[(b0 + c) * ld + b0 + i]; the reflectors sit above the diagonal); lane c
-        // then solves (diag(1 / tau) + strict_upper(G)) t = e_c by substitution
-        // from the last row up (no division: t_r = tau_r x_r) and stores column c
-        // of T, T(i, c) for i <= c, over G's column at the same places.  Rows and
-        // columns past the block's nbk reflectors are never read.
-        for (int b = wid; b < nblk; b += kWaves) {
-            const int b0 = 32 * b, nbk = min(32, mref - b0);
-            f32x16 g = {};
-            for (int k0 = b0; k0 < n; k0 += 8) {          // Y is zero past row n - 1
-                float y[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) y[u] = Y(b0, nbk, k0 + 2 * u + kh, m32);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) g = __builtin_amdgcn_mfma_f32_32x32x2f32(y[u], y[u], g, 0, 0, 0);
-            }
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int r = frag_row(lane, q);
-                if (r < m32 && m32 < nbk) A[(b0 + m32) * ld + b0 + r] = g[q];
-            }
-            wave_lds_sync();
-            if (nbk == 32) {
-                wblock_t_full(A + b0 * ld + b0, ld, stau + b0, m32, lane);
-            } else {
-                // the last, partial block: the solve runs in scratch tile b,
-                // X(i, c) at tX[i * tsx + c]
-                int tsx = 0;
-                float *tX = scratch_tile(A, ld, sep, b, &tsx);
-                if (lane < 32)
-                    for (int i = 0; i < nbk; ++i) tX[i * tsx + m32] = i == m32 ? 1.f : 0.f;
-                wave_lds_sync();
-                for (int r = nbk - 1; r >= 0; --r) {
-                    const float xr = stau[b0 + r] * tX[r * tsx + m32];
-                    const float *Gc = A + (b0 + r) * ld + b0;
-                    if (lane < 32) {
-                        tX[r * tsx + m32] = xr;
-                        for (int i = 0; i < r; ++i) tX[i * tsx + m32] = fmaf(-Gc[i], xr, tX[i * tsx + m32]);
-                    }
-                    wave_lds_sync();
-                }
-                if (lane < 32 && m32 < nbk)
-                    for (int i = 0; i <= m32; ++i) A[(b0 + m32) * ld + b0 + i] = tX[i * tsx + m32];
-            }
-        }
-        __syncthreads();
-        for (int b = nblk - 1; b >= 0; --b) {
-            const int b0 = 32 * b, nbk = min(32, mref - b0);
-            if (wid < nt) {
-                // M = T (Y^T Z) for column chunk wid
-                int tsm = 0;
-                float *tM = scratch_tile(A, ld, sep, wid, &tsm);
-                const int col = 32 * wid + m32, colc = min(col, n - 1);
-                f32x16 acc = {};
-                for (int k0 = b0; k0 < n; k0 += 8) {      // both operands are zero past row n - 1
-                    float ya[4], bz[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int k = k0 + 2 * u + kh;
-                        bz[u] = ld_or_zero(Z, min(k, n - 1) * ld + colc, k < n && col < n);
-                        ya[u] = Y(b0, nbk, k, m32);
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ya[u], bz[u], acc, 0, 0, 0);
-                }
-#pragma unroll
-                for (int q = 0; q < 16; ++q) tM[frag_row(lane, q) * tsm + m32] = acc[q];
-                wave_lds_sync();
-                f32x16 acc2 = {};
-#pragma unroll
-                for (int k0 = 0; k0 < 32; k0 += 2) {
-                    const int k = k0 + kh;
-                    // T(m32, k) at A[(b0 + k) * ld + b0 + m32], k >= m32
-                    const float t = ld_or_zero(A, (b0 + min(k, nbk - 1)) * ld + b0 + m32, k >= m32 && k < nbk);
-                    acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(t, tM[k * tsm + m32], acc2, 0, 0, 0);
-                }
-                wave_lds_sync();
-#pragma unroll
-                for (int q = 0; q < 16; ++q) tM[frag_row(lane, q) * tsm + m32] = acc2[q];
-            }
-            __syncthreads();
-            // Z -= Y M on the row blocks that Y touches (rows > b0)
-            const int nrt = nt - b;
-            for (int t = wid; t < nrt * nt; t += kWaves) {
-                const int rt = b + t / nt, c = t % nt;
-                int tsm = 0;
-                const float *tM = scratch_tile(A, ld, sep, c, &tsm);
-                const int col = 32 * c + m32, colc = min(col, n - 1);
-                f32x16 acc;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = 32 * rt + frag_row(lane, q);
-                    acc[q] = ld_or_zero(Z, min(row, n - 1) * ld + colc, row < n && col < n);
-                }
-#pragma unroll
-                for (int k0 = 0; k0 < 32; k0 += 2) {
-                    const int k = k0 + kh;
-                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(-Y(b0, nbk, 32 * rt + m32, k), tM[k * tsm + m32], acc,
-                                                               0, 0, 0);
-                }
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = 32 * rt + frag_row(lane, q);
-                    if (row < n && col < n) Z[row * ld + col] = acc[q];
-                }
-            }
-            __syncthreads();
-        }
-    }
 
     // ---------------------------------------------------------------- 5. Newton-Schulz steps
     // V <- V (3 I - V^T V) / 2 = V + V E with E = (I - V^T V) / 2.  V^T V is
@@ -878,22 +968,22 @@ static hipError_t allow_lds_tri() {
     if (state == hipErrorNotReady) {
         hipError_t e = allow_lds(reinterpret_cast<const void *>(k_eig_tridiag));
         if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_backtr));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_polish));
         state = e;
     }
     return state;
 }
 
-// dynamic LDS layout for a batch of order <= maxN (floats):
-// [A: maxN x ld | B1: max(maxN x ld, 2 maxN x kPanelStride) | scratch tiles (maxN < 128 only)]
-struct TriLayout { int ld, boff, poff, soff; size_t bytes; };
+// dynamic LDS layout of k_eig_tridiag and k_eig_polish for a batch of order
+// <= maxN (floats): [A: maxN x ld | B1: max(maxN x ld, 2 maxN x kPanelStride)]
+struct TriLayout { int ld, boff, poff; size_t bytes; };
 static TriLayout tri_layout(int maxN) {
     TriLayout L;
     L.ld = maxN | 1;
     L.boff = maxN * L.ld;
     L.poff = maxN * kPanelStride;
     const int b1 = std::max(maxN * L.ld, 2 * maxN * kPanelStride);
-    L.soff = maxN >= 128 ? -1 : L.boff + b1;
-    L.bytes = (size_t)(L.boff + b1 + (L.soff >= 0 ? 5 * 32 * 33 : 0)) * sizeof(float);
+    L.bytes = (size_t)(L.boff + b1) * sizeof(float);
     return L;
 }
 
@@ -909,14 +999,24 @@ hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
         hipLaunchKernelGGL(k_eig_tridiag, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff, L.poff);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
+    const int nblk = (std::max(maxN - 2, 0) + 31) / 32;
     {
         KTimeScope kts("k_eig_trivec", s);
         constexpr int per = kVecWaves * kVecPerWave;
-        hipLaunchKernelGGL(k_eig_trivec, dim3((maxN + per - 1) / per, b.n), dim3(64 * kVecWaves), 0, s, b);
+        const int eig_blocks = (maxN + per - 1) / per;
+        hipLaunchKernelGGL(k_eig_trivec, dim3(eig_blocks + nblk, b.n), dim3(64 * kVecWaves), 0, s, b, eig_blocks);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
-    KTimeScope kts("k_eig_backtr", s);
-    hipLaunchKernelGGL(k_eig_backtr, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff, L.soff);
+    {
+        KTimeScope kts("k_eig_backtr", s);
+        const int ldy = ((maxN + 3) & ~3) | 1;         // odd, and room for the padded rows
+        const size_t lds = ((size_t)std::max(maxN - 2, 0) * ldy + (size_t)nblk * kTile + (size_t)maxN * 33 +
+                            (size_t)(kBtWaves + 1) * kTile) * sizeof(float);
+        hipLaunchKernelGGL(k_eig_backtr, dim3((maxN + 31) / 32, b.n), dim3(64 * kBtWaves), lds, s, b, ldy);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    KTimeScope kts("k_eig_polish", s);
+    hipLaunchKernelGGL(k_eig_polish, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff);
     return hipGetLastError();
 }
 

@@ -126,7 +126,11 @@ hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStr
 // eig_tri_ws_bytes(n), 16-byte aligned, which the three launches share)
 constexpr int kTriMaxN = 140;
 constexpr int kEigRetry = -2;
-inline size_t eig_tri_ws_bytes(int n) { return (((size_t)2 * n * n + 4 * (size_t)n + 1) * 4 + 255) / 256 * 256; }
+inline size_t eig_tri_ws_bytes(int n) {
+    const size_t blocks = ((n > 2 ? n - 2 : 0) + 31) / 32;
+    const size_t np = ((size_t)n + 3) / 4 * 4;
+    return (((size_t)2 * n * np + 1024 * blocks + 4 * (size_t)n + 1) * 4 + 255) / 256 * 256;
+}
 hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s);
 
 // block Jacobi state of one large symmetric matrix (N = padded size, multiple of 128)
