@@ -16,9 +16,9 @@ namespace jolt {
 jolt_status fail(jolt_handle h, jolt_status s, const char *fmt, ...);
 jolt_status hip_fail(jolt_handle h, hipError_t e, const char *where);
 void clear_err(jolt_handle h);
-// The dual's candidate grid and per-shape byte tables depend only on the
-// configuration and the item shapes; a handle keeps the last ones (and the
-// buffer for the items' distortion tables) from one plan to the next.
+// The dual's candidate grid and per-shape byte-ordered candidates depend only
+// on the configuration and the item shapes; a handle keeps the last ones from
+// one plan to the next.
 struct DualTables {
     int rt_max = -1, rf_max = -1, step = -1, grid_nf = -1, dtype = -1, d = -1;
     uint32_t bits_mask = 0;
@@ -26,11 +26,9 @@ struct DualTables {
     std::vector<int> cell;          // each candidate's energy-grid cell (-1 for rank 0)
     struct Shape {
         int L, H, T;
-        std::vector<int64_t> B;     // bytes per candidate
-        std::vector<int> order;     // candidates by (bytes, rt, rf, bits)
+        SortedCands sc;             // the candidates in byte order, with their bytes
     };
     std::vector<Shape> shapes;
-    std::vector<double> D;          // n x candidates distortion tables
 };
 DualTables &dual_tables(jolt_handle h);
 // A second stream on the handle's device (default priority, created on first

@@ -970,34 +970,24 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
                !(dt.shapes[k].L == items[i].L && dt.shapes[k].H == items[i].H && dt.shapes[k].T == items[i].T))
             ++k;
         if (k == (int)dt.shapes.size()) {
-            DualTables::Shape sh{items[i].L, items[i].H, items[i].T, std::vector<int64_t>(nc), {}};
-            for (int j = 0; j < nc; ++j) sh.B[j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
-            sh.order = byte_order(nc, cand.data(), sh.B.data());
-            dt.shapes.push_back(std::move(sh));
+            std::vector<int64_t> B(nc);
+            for (int j = 0; j < nc; ++j) B[j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
+            dt.shapes.push_back(DualTables::Shape{items[i].L, items[i].H, items[i].T, sorted_cands(cand, dt.cell.data(), B.data())});
         }
         shape_of[i] = k;
     }
-    dt.D.resize((size_t)n * nc);
-    for (int i = 0; i < n; ++i)
-        distortion_table_cells(grid[i], dt.cell.data(), nx2[i], cfg->delta_b, cand, dt.D.data() + (size_t)i * nc);
-    std::vector<int32_t> ncand(n, nc);
-    std::vector<const Cand *> cp(n, cand.data());
-    std::vector<const double *> dp(n);
-    std::vector<const int64_t *> bp(n);
-    std::vector<const int *> op(n);
-    for (int i = 0; i < n; ++i) {
-        dp[i] = dt.D.data() + (size_t)i * nc;
-        bp[i] = dt.shapes[shape_of[i]].B.data();
-        op[i] = dt.shapes[shape_of[i]].order.data();
-    }
+    std::vector<const SortedCands *> scp(n);
+    for (int i = 0; i < n; ++i) scp[i] = &dt.shapes[shape_of[i]].sc;
     std::vector<int> choice(n);
+    std::vector<double> dist(n);
     double lam = 0.0;
-    s = allocate(n, ncand.data(), cp.data(), dp.data(), bp.data(), cfg->budget_bytes, choice.data(), &lam, op.data());
+    s = allocate_sorted(n, scp.data(), grid.data(), nx2.data(), cfg->delta_b, cfg->budget_bytes, choice.data(),
+                        dist.data(), &lam);
     for (int i = 0; i < n; ++i) {
         const Cand &cc = cand[choice[i]];
         alloc_host[i].rt = cc.rt; alloc_host[i].rf = cc.rf; alloc_host[i].bits = cc.bits; alloc_host[i].reserved = 0;
-        alloc_host[i].bytes = bp[i][choice[i]];
-        alloc_host[i].distortion = dp[i][choice[i]];
+        alloc_host[i].bytes = jolt_item_bytes(&items[i], cc.rt, cc.rf, cc.bits);
+        alloc_host[i].distortion = dist[i];
     }
     if (lambda_out) *lambda_out = lam;
     report();

@@ -59,47 +59,58 @@ std::vector<int> byte_order(int nc, const Cand *cand, const int64_t *B) {
 namespace {
 
 struct ItemHull {
-    std::vector<int> v;        // candidate indices, bytes ascending
+    std::vector<int> v;        // positions in byte order, bytes ascending
+    std::vector<double> d;     // distortion at v[j]
     std::vector<double> s;     // slope between v[j] and v[j+1] (decreasing)
 };
 
-struct Pt {
-    int64_t B;
-    double D;
-    int rt, rf, bits, idx;
-};
-
-// `order`: candidate indices by (bytes, rt, rf, bits)
-ItemHull build_hull(int nc, const int *order, const double *D, const int64_t *B) {
-    // staircase: per byte count the point of least D (ties: the earliest in
-    // order, i.e. smaller rt, rf, bits), kept only where D strictly falls
-    std::vector<int> stair;
-    stair.reserve(nc);
-    for (int p = 0; p < nc;) {
-        int best = order[p], q = p + 1;
-        for (; q < nc && B[order[q]] == B[best]; ++q)
-            if (D[order[q]] < D[best]) best = order[q];
-        p = q;
-        if (!stair.empty() && !(D[best] < D[stair.back()])) continue;
-        stair.push_back(best);
-    }
-    ItemHull h;
-    h.v.reserve(stair.size());
-    h.s.reserve(stair.size());
-    for (int i : stair) {
+// Lower convex hull of the (bytes, distortion) points of one item, given in
+// byte order (equal bytes in the order (rt, rf, bits)): B[p] and D(p) at
+// position p.  The points that matter form a staircase: of each run of equal
+// bytes the point of least D (ties: the earliest), kept only where D falls
+// strictly below every point kept so far.  Each staircase point goes onto the
+// monotone chain as it is found; a later point of the same bytes and lower D
+// first takes the earlier one off the end of the chain (it pops at least what
+// that one popped, so the chain is the one over the final staircase).  h is
+// reused: its vectors keep their capacity from call to call.
+template <typename DF>
+void build_hull(int nc, const int64_t *B, DF D, ItemHull &h) {
+    h.v.clear();
+    h.d.clear();
+    h.s.clear();
+    double run = 0.0;
+    for (int p = 0; p < nc; ++p) {
+        const double di = D(p);
+        if (!h.v.empty()) {
+            if (!(di < run)) continue;
+            if (B[h.v.back()] == B[p]) {
+                h.v.pop_back();
+                h.d.pop_back();
+            }
+        }
+        run = di;
         while (h.v.size() >= 2) {
             const int o = h.v[h.v.size() - 2], a = h.v.back();
-            const double cross = (double)(B[a] - B[o]) * (D[i] - D[o]) - (D[a] - D[o]) * (double)(B[i] - B[o]);
-            if (cross <= 0.0) h.v.pop_back();
-            else break;
+            const double dO = h.d[h.d.size() - 2], dA = h.d.back();
+            const double cross = (double)(B[a] - B[o]) * (di - dO) - (dA - dO) * (double)(B[p] - B[o]);
+            if (cross <= 0.0) {
+                h.v.pop_back();
+                h.d.pop_back();
+            } else {
+                break;
+            }
         }
-        h.v.push_back(i);
+        h.v.push_back(p);
+        h.d.push_back(di);
     }
-    for (size_t j = 0; j + 1 < h.v.size(); ++j) {
-        const int a = h.v[j], b = h.v[j + 1];
-        h.s.push_back((D[a] - D[b]) / (double)(B[b] - B[a]));
-    }
-    return h;
+    for (size_t j = 0; j + 1 < h.v.size(); ++j) h.s.push_back((h.d[j] - h.d[j + 1]) / (double)(B[h.v[j + 1]] - B[h.v[j]]));
+}
+
+// per-thread hulls, kept between calls for their capacity
+std::vector<ItemHull> &hull_scratch(int n) {
+    thread_local std::vector<ItemHull> hulls;
+    if ((int)hulls.size() < n) hulls.resize(n);
+    return hulls;
 }
 
 // vertex chosen at lambda: v[J], J = #{j : s_j > lambda}
@@ -109,25 +120,14 @@ int vertex_at(const ItemHull &h, double lam) {
     return h.v[J];
 }
 
-}  // namespace
-
-jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, const double *const *D,
-                     const int64_t *const *B, int64_t budget, int *choice, double *lambda_out,
-                     const int *const *order) {
-    std::vector<ItemHull> hulls(n);
+// the single dual over the items' hulls (B_i: item i's bytes in byte order):
+// lambda* and each item's chosen position
+jolt_status dual(int n, const std::vector<ItemHull> &hulls, const int64_t *const *B, int64_t budget, int *pos,
+                 double *lambda_out) {
     int64_t min_total = 0;
-    for (int i = 0; i < n; ++i) {
-        if (n_cand[i] <= 0) return JOLT_E_INVALID;
-        if (order && order[i]) {
-            hulls[i] = build_hull(n_cand[i], order[i], D[i], B[i]);
-        } else {
-            const std::vector<int> o = byte_order(n_cand[i], cand[i], B[i]);
-            hulls[i] = build_hull(n_cand[i], o.data(), D[i], B[i]);
-        }
-        min_total += B[i][hulls[i].v[0]];
-    }
+    for (int i = 0; i < n; ++i) min_total += B[i][hulls[i].v[0]];
     if (min_total > budget) {
-        for (int i = 0; i < n; ++i) choice[i] = hulls[i].v[0];
+        for (int i = 0; i < n; ++i) pos[i] = hulls[i].v[0];
         if (lambda_out) *lambda_out = INFINITY;
         return JOLT_E_INFEASIBLE;
     }
@@ -159,9 +159,88 @@ jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, cons
         }
         lam = (sg <= 0.0 && tot <= budget) ? 0.0 : fit;
     }
-    for (int i = 0; i < n; ++i) choice[i] = vertex_at(hulls[i], lam);
+    for (int i = 0; i < n; ++i) pos[i] = vertex_at(hulls[i], lam);
     if (lambda_out) *lambda_out = lam;
     return JOLT_OK;
+}
+
+}  // namespace
+
+jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, const double *const *D,
+                     const int64_t *const *B, int64_t budget, int *choice, double *lambda_out,
+                     const int *const *order) {
+    std::vector<ItemHull> &hulls = hull_scratch(n);
+    std::vector<std::vector<int>> own(n);
+    std::vector<std::vector<int64_t>> Bs(n);
+    std::vector<const int64_t *> bp(n);
+    std::vector<const int *> op(n);
+    for (int i = 0; i < n; ++i) {
+        if (n_cand[i] <= 0) return JOLT_E_INVALID;
+        if (order && order[i]) {
+            op[i] = order[i];
+        } else {
+            own[i] = byte_order(n_cand[i], cand[i], B[i]);
+            op[i] = own[i].data();
+        }
+        Bs[i].resize(n_cand[i]);
+        for (int p = 0; p < n_cand[i]; ++p) Bs[i][p] = B[i][op[i][p]];
+        bp[i] = Bs[i].data();
+        const double *Di = D[i];
+        const int *oi = op[i];
+        build_hull(n_cand[i], bp[i], [&](int p) { return Di[oi[p]]; }, hulls[i]);
+    }
+    std::vector<int> pos(n);
+    const jolt_status s = dual(n, hulls, bp.data(), budget, pos.data(), lambda_out);
+    for (int i = 0; i < n; ++i) choice[i] = op[i][pos[i]];
+    return s;
+}
+
+jolt_status allocate_sorted(int n, const SortedCands *const *sc, const double *const *grid, const double *normx2,
+                            const double *delta, int64_t budget, int *choice, double *distortion,
+                            double *lambda_out) {
+    std::vector<ItemHull> &hulls = hull_scratch(n);
+    std::vector<const int64_t *> bp(n);
+    for (int i = 0; i < n; ++i) {
+        const SortedCands &c = *sc[i];
+        if (c.B.empty()) return JOLT_E_INVALID;
+        bp[i] = c.B.data();
+        const double *g = grid[i], nx2 = normx2[i];
+        const int *cell = c.cell.data();
+        const uint8_t *bits = c.bits.data();
+        // the distortion of distortion_table_cells, position by position
+        build_hull((int)c.B.size(), bp[i], [&](int p) {
+            const double S = cell[p] < 0 ? 0.0 : g[cell[p]];
+            return delta[bits[p]] * std::max(0.0, nx2 - S);
+        }, hulls[i]);
+    }
+    std::vector<int> pos(n);
+    const jolt_status s = dual(n, hulls, bp.data(), budget, pos.data(), lambda_out);
+    for (int i = 0; i < n; ++i) {
+        const SortedCands &c = *sc[i];
+        const int p = pos[i];
+        choice[i] = c.cand[p];
+        const double S = c.cell[p] < 0 ? 0.0 : grid[i][c.cell[p]];
+        distortion[i] = delta[c.bits[p]] * std::max(0.0, normx2[i] - S);
+    }
+    return s;
+}
+
+SortedCands sorted_cands(const std::vector<Cand> &cand, const int *cell, const int64_t *B) {
+    SortedCands s;
+    const std::vector<int> order = byte_order((int)cand.size(), cand.data(), B);
+    const size_t nc = cand.size();
+    s.B.resize(nc);
+    s.cell.resize(nc);
+    s.bits.resize(nc);
+    s.cand.resize(nc);
+    for (size_t p = 0; p < nc; ++p) {
+        const int j = order[p];
+        s.B[p] = B[j];
+        s.cell[p] = cell[j];
+        s.bits[p] = (uint8_t)cand[j].bits;
+        s.cand[p] = j;
+    }
+    return s;
 }
 
 void distortion_table(const double *grid /* captured energy S at (rt, rf) = (step (i+1), step (j+1)) */, int nf,

@@ -21,6 +21,21 @@ std::vector<int> byte_order(int nc, const Cand *cand, const int64_t *B);
 jolt_status allocate(int n, const int32_t *n_cand, const Cand *const *cand, const double *const *D,
                      const int64_t *const *B, int64_t budget, int *choice, double *lambda_out,
                      const int *const *order = nullptr);
+// One item shape's candidates in byte order (as byte_order): bytes, grid cell
+// (-1: rank 0), bits and candidate index at each position.
+struct SortedCands {
+    std::vector<int64_t> B;
+    std::vector<int> cell;
+    std::vector<uint8_t> bits;
+    std::vector<int> cand;
+};
+SortedCands sorted_cands(const std::vector<Cand> &cand, const int *cell, const int64_t *B);
+// allocate() with each item's distortions formed from its captured-energy grid
+// as distortion_table_cells does, position by position in byte order (no
+// table): choice[i] is a candidate index, distortion[i] its distortion
+jolt_status allocate_sorted(int n, const SortedCands *const *sc, const double *const *grid, const double *normx2,
+                            const double *delta, int64_t budget, int *choice, double *distortion,
+                            double *lambda_out);
 void distortion_table(const double *grid, int nf, int step, double normx2, const double *delta,
                       const std::vector<Cand> &cand, double *D);
 // the same with each candidate's grid cell precomputed (-1: rank 0, S = 0)
