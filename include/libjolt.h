@@ -18,7 +18,9 @@
  * Conventions (all entry points):
  *   - Device pointers are caller-owned device memory; host pointers are
  *     caller-owned host memory.  libjolt never allocates device memory; the
- *     workspace sizes come from jolt_workspace_size().
+ *     workspace sizes come from jolt_workspace_size() (jolt_eigh_workspace_size
+ *     for jolt_eigh).  A handle holds one small pinned host buffer (at least
+ *     64 KiB, grown as the plan's readback needs) from its first plan on.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *     stream-ordered and asynchronous, except jolt_plan(), which synchronises
  *     `stream` once to read the energy tables back.  jolt_plan() also forks
@@ -111,7 +113,8 @@ typedef struct jolt_handle_s *jolt_handle;
 
 /* ---- lifetime and errors ------------------------------------------------- */
 /* Binds the calling thread's HIP device `hip_device`; no device memory is taken.
- * jolt_destroy() waits for and releases the handle's second stream, if any. */
+ * jolt_destroy() waits for and releases the handle's second stream and its
+ * pinned readback buffer, if any. */
 jolt_status jolt_create(int hip_device, jolt_handle *out);
 void jolt_destroy(jolt_handle h);
 const char *jolt_status_str(jolt_status s);
@@ -226,9 +229,17 @@ jolt_status jolt_rademacher(jolt_handle h, uint64_t seed, uint32_t item_id, uint
  * magnitude (first such row) positive.  info (count int32, device) receives
  * 0 when the Householder-tridiagonal solver (n <= 140) produced the result,
  * the sweep count when the Jacobi solver did (n > 140, force_jacobi != 0, or
- * numerically repeated eigenvalues), -1 when Jacobi hit its sweep cap. */
+ * numerically repeated eigenvalues), -1 when Jacobi hit its sweep cap.
+ * workspace (device, 16-byte aligned) of at least
+ * jolt_eigh_workspace_size(n, count, force_jacobi) bytes carries the
+ * tridiagonal solver's intermediates from launch to launch; calls that
+ * overlap on one workspace race. */
 jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const float *a, int32_t lda, int64_t mat_stride,
-                      float *vec, float *lam, int32_t *info, int32_t force_jacobi, void *stream);
+                      float *vec, float *lam, int32_t *info, int32_t force_jacobi, void *workspace,
+                      size_t workspace_bytes, void *stream);
+/* Bytes of workspace that jolt_eigh needs for these arguments (0 when the
+ * Jacobi solver does all of it). */
+size_t jolt_eigh_workspace_size(int32_t n, int32_t count, int32_t force_jacobi);
 
 /* ---- measurement hooks -------------------------------------------------- */
 /* Launch timing of one of the library's kernels, named as in its source

@@ -55,7 +55,8 @@ EXPORTED = [
     "jolt_item_bytes", "jolt_payload_size", "jolt_payload_layout", "jolt_payload_header",
     "jolt_payload_validate", "jolt_plan", "jolt_compress", "jolt_encode_residual", "jolt_decompress",
     "jolt_plan_factors", "jolt_plan_from_tables", "jolt_rotate", "jolt_quantize_pack",
-    "jolt_unpack_dequant", "jolt_rademacher", "jolt_eigh", "jolt_kernel_timer", "jolt_kernel_time",
+    "jolt_unpack_dequant", "jolt_rademacher", "jolt_eigh", "jolt_eigh_workspace_size", "jolt_kernel_timer",
+    "jolt_kernel_time",
 ]
 
 _lib = None
@@ -99,7 +100,8 @@ def lib():
             "jolt_quantize_pack": (I32, [P, P, I64, I32, I32, P, P, P]),
             "jolt_unpack_dequant": (I32, [P, P, P, I64, I32, I32, P, P]),
             "jolt_rademacher": (I32, [P, U64, U32, U32, U64, I64, P, P]),
-            "jolt_eigh": (I32, [P, I32, I32, P, I32, I64, P, P, P, I32, P]),
+            "jolt_eigh": (I32, [P, I32, I32, P, I32, I64, P, P, P, I32, P, SZ, P]),
+            "jolt_eigh_workspace_size": (SZ, [I32, I32, I32]),
             "jolt_kernel_timer": (I32, [P, C.c_char_p, I32]),
             "jolt_kernel_time": (I32, [P, C.c_char_p, C.POINTER(D), C.POINTER(I64)]),
         }
@@ -247,9 +249,15 @@ def jolt_rademacher(h, seed, item_id, stream_id, first, count, out_ptr, stream):
                                  C.c_void_p(stream)), h)
 
 
-def jolt_eigh(h, n, count, a_ptr, lda, mat_stride, vec_ptr, lam_ptr, info_ptr, force_jacobi, stream):
+def jolt_eigh_workspace_size(n, count, force_jacobi=False) -> int:
+    return int(lib().jolt_eigh_workspace_size(n, count, int(bool(force_jacobi))))
+
+
+def jolt_eigh(h, n, count, a_ptr, lda, mat_stride, vec_ptr, lam_ptr, info_ptr, force_jacobi, ws_ptr, ws_bytes,
+              stream):
     _check(lib().jolt_eigh(h, n, count, C.c_void_p(a_ptr), lda, mat_stride, C.c_void_p(vec_ptr),
-                           C.c_void_p(lam_ptr), C.c_void_p(info_ptr), int(force_jacobi), C.c_void_p(stream)), h)
+                           C.c_void_p(lam_ptr), C.c_void_p(info_ptr), int(force_jacobi), C.c_void_p(ws_ptr),
+                           ws_bytes, C.c_void_p(stream)), h)
 
 
 def jolt_kernel_timer(h, kernel: str, enable: bool):

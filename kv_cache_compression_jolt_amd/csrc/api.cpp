@@ -25,6 +25,8 @@ struct jolt_handle_s {
     hipStream_t side = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
     jolt::DualTables dual;
+    uint8_t *readback = nullptr;    // pinned host memory for the plan's one readback
+    size_t readback_cap = 0;
 };
 
 namespace jolt {
@@ -50,6 +52,23 @@ void clear_err(jolt_handle h) {
 }
 
 DualTables &dual_tables(jolt_handle h) { return h->dual; }
+
+hipError_t readback_buffer(jolt_handle h, size_t bytes, uint8_t **buf) {
+    if (bytes > h->readback_cap) {
+        // every earlier use ended with its stream synchronised, so the old
+        // buffer is idle
+        if (h->readback) (void)hipHostFree(h->readback);
+        h->readback = nullptr;
+        h->readback_cap = 0;
+        const size_t cap = std::max<size_t>(bytes, 64 * 1024);
+        if (hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&h->readback), cap, hipHostMallocDefault);
+            e != hipSuccess)
+            return e;
+        h->readback_cap = cap;
+    }
+    *buf = h->readback;
+    return hipSuccess;
+}
 
 hipError_t side_stream(jolt_handle h, hipStream_t *st, hipEvent_t *fork, hipEvent_t *join) {
     if (!h->side) {
@@ -136,6 +155,7 @@ extern "C" void jolt_destroy(jolt_handle h) {
         (void)hipEventDestroy(h->fork);
         (void)hipStreamDestroy(h->side);
     }
+    if (h->readback) (void)hipHostFree(h->readback);
     delete h;
 }
 
@@ -449,26 +469,30 @@ extern "C" jolt_status jolt_rademacher(jolt_handle h, uint64_t seed, uint32_t it
     return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "rademacher");
 }
 
+extern "C" size_t jolt_eigh_workspace_size(int32_t n, int32_t count, int32_t force_jacobi) {
+    if (n < 1 || n > kTriMaxN || count < 1 || force_jacobi) return 0;
+    return eig_tri_ws_bytes(n) * (size_t)std::min(count, 64);
+}
+
 extern "C" jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const float *a, int32_t lda,
                                  int64_t mat_stride, float *vec, float *lam, int32_t *info, int32_t force_jacobi,
-                                 void *stream) {
+                                 void *workspace, size_t workspace_bytes, void *stream) {
     if (!h) return JOLT_E_INVALID;
     clear_err(h);
     if (n < 1 || n > kJacobiMaxN || count < 0 || lda < n || mat_stride < (int64_t)(n - 1) * lda + n)
         return fail(h, JOLT_E_INVALID, "eigh: bad sizes (n=%d count=%d lda=%d)", n, count, lda);
     if (count > 0 && (!a || !vec || !lam || !info)) return fail(h, JOLT_E_INVALID, "eigh: null pointer");
+    const size_t need = jolt_eigh_workspace_size(n, count, force_jacobi);
+    if (workspace_bytes < need || (need && (!workspace || reinterpret_cast<uintptr_t>(workspace) % 16)))
+        return fail(h, JOLT_E_WORKSPACE, "eigh workspace: need %zu bytes (16-byte aligned), have %zu", need,
+                    workspace_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool tri = !force_jacobi && n <= kTriMaxN;
-    // the tridiagonal solver's hand-over workspace, stream-ordered: one region
-    // per matrix of a batch of up to 64, freed on the stream after the last batch
+    const bool tri = need > 0;
+    // one workspace region per matrix of a batch of up to 64; batches run in
+    // stream order, so they reuse the regions
     const size_t wsb = tri ? eig_tri_ws_bytes(n) : 0;
-    uint8_t *tws = nullptr;
-    if (tri && count > 0)
-        if (hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&tws), wsb * std::min(count, 64), st);
-            e != hipSuccess)
-            return hip_fail(h, e, "eigh workspace");
-    hipError_t e = hipSuccess;
-    for (int i0 = 0; i0 < count && e == hipSuccess; i0 += 64) {
+    uint8_t *tws = static_cast<uint8_t *>(workspace);
+    for (int i0 = 0; i0 < count; i0 += 64) {
         JacBatch b{};
         for (int i = i0; i < count && b.n < 64; ++i) {
             JacItem &j = b.it[b.n];
@@ -483,14 +507,11 @@ extern "C" jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const 
             j.tw = tri ? reinterpret_cast<float *>(tws + (size_t)b.n * wsb) : nullptr;
             ++b.n;
         }
-        e = tri ? launch_eig_tridiag(b, n, st) : launch_jacobi_lds(b, n, 30, st);
+        hipError_t e = tri ? launch_eig_tridiag(b, n, st) : launch_jacobi_lds(b, n, 30, st);
         if (e == hipSuccess && tri) e = launch_jacobi_lds(b, n, 30, st, 1);
+        if (e != hipSuccess) return hip_fail(h, e, "eigh");
     }
-    if (tws) {
-        const hipError_t ef = hipFreeAsync(tws, st);
-        if (e == hipSuccess) e = ef;
-    }
-    return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "eigh");
+    return JOLT_OK;
 }
 
 extern "C" jolt_status jolt_kernel_timer(jolt_handle h, const char *kernel, int32_t enable) {

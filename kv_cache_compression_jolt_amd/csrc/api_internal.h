@@ -31,6 +31,9 @@ struct DualTables {
     std::vector<Shape> shapes;
 };
 DualTables &dual_tables(jolt_handle h);
+// The handle's pinned host buffer of at least `bytes` (grown on demand) for a
+// device-to-host copy that the caller synchronises before it returns.
+hipError_t readback_buffer(jolt_handle h, size_t bytes, uint8_t **buf);
 // A second stream on the handle's device (default priority, created on first
 // use and destroyed with the handle) and two events, for work forked off the
 // caller's stream and joined back to it within one call.

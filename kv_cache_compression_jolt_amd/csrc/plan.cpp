@@ -901,8 +901,10 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     }
     // energy tables, ||X||^2 and sweep counters back to the host (the one synchronisation)
     const int rt_max = pl.rt_max;
-    std::vector<uint8_t> rb(pl.readback_stride * n);
-    hipError_t e = hipMemcpyAsync(rb.data(), ws + pl.readback, rb.size(), hipMemcpyDeviceToHost, st);
+    const size_t rb_bytes = pl.readback_stride * n;
+    uint8_t *rb = nullptr;
+    hipError_t e = readback_buffer(h, rb_bytes, &rb);
+    if (e == hipSuccess) e = hipMemcpyAsync(rb, ws + pl.readback, rb_bytes, hipMemcpyDeviceToHost, st);
     const auto t_launched = std::chrono::steady_clock::now();
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(h, e, "plan");
@@ -920,12 +922,12 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     std::vector<const double *> grid(n);
     std::vector<double> nx2(n), sfix(n);
     for (int i = 0; i < n; ++i) {
-        grid[i] = reinterpret_cast<const double *>(rb.data() + (pl.item[i].grid - pl.readback));
+        grid[i] = reinterpret_cast<const double *>(rb + (pl.item[i].grid - pl.readback));
         (void)cells;
-        std::memcpy(&sfix[i], rb.data() + (pl.item[i].sfixed - pl.readback), 8);
-        std::memcpy(&nx2[i], rb.data() + (pl.item[i].normx2 - pl.readback), 8);
+        std::memcpy(&sfix[i], rb + (pl.item[i].sfixed - pl.readback), 8);
+        std::memcpy(&nx2[i], rb + (pl.item[i].normx2 - pl.readback), 8);
         int sw[2];
-        std::memcpy(sw, rb.data() + (pl.item[i].sweeps - pl.readback), 8);
+        std::memcpy(sw, rb + (pl.item[i].sweeps - pl.readback), 8);
         if (sw[0] < 0 || sw[1] < 0) noconv = true;
         if (debug) fprintf(stderr, "libjolt: item %d eig sweeps feature %d token %d\n", i, sw[0], sw[1]);
     }

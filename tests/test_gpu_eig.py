@@ -35,10 +35,12 @@ def _run(mats, force_jacobi=False):
     vec = torch.empty((count, n, n), dtype=torch.float32, device="cuda")
     lam = torch.empty((count, n), dtype=torch.float32, device="cuda")
     info = torch.full((count,), 99, dtype=torch.int32, device="cuda")
+    wsb = jb.jolt_eigh_workspace_size(n, count, force_jacobi)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
     h = jb.jolt_create()
     try:
         jb.jolt_eigh(h, n, count, a.data_ptr(), n, n * n, vec.data_ptr(), lam.data_ptr(), info.data_ptr(),
-                     force_jacobi, torch.cuda.current_stream().cuda_stream)
+                     force_jacobi, ws.data_ptr(), wsb, torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
     finally:
         jb.jolt_destroy(h)
