@@ -884,16 +884,30 @@ __global__ void k_to_bf16_batch(SmallBatch batch) {
     }
 }
 
+// omt[c][r] = Omega[r][c] (+-1, counter r k + c of stream 1), zero rows c >= k;
+// each thread takes 8 consecutive r of one row c (n is a multiple of 8), one
+// 16-byte store of bf16 or two of fp32
 __global__ void k_gen_omega_batch(SmallBatch batch) {
     const SmallItem &it = batch.it[blockIdx.y];
     const int k = it.a, kp = it.b;
-    const int64_t n = it.count / kp;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < it.count; e += (int64_t)gridDim.x * blockDim.x) {
-        const int c = (int)(e / n);
-        const int64_t r = e % n;
-        const float v = (c < k) ? rademacher(it.key, 1, (uint64_t)r * k + c) : 0.f;
-        if (it.hi) it.hi[e] = f32_to_bf16(v);
-        if (it.out32) it.out32[e] = v;
+    const uint32_t n8 = (uint32_t)(it.count / kp / 8), total = (uint32_t)kp * n8;
+    for (uint32_t g = blockIdx.x * blockDim.x + threadIdx.x; g < total; g += gridDim.x * blockDim.x) {
+        const int c = (int)(g / n8);
+        const uint64_t r0 = (uint64_t)(g - (uint32_t)c * n8) * 8;
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (c < k) ? rademacher(it.key, 1, (r0 + u) * (uint64_t)k + c) : 0.f;
+        const size_t e = (size_t)c * n8 * 8 + r0;
+        if (it.hi) {
+            uint32_t w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[u] = (uint32_t)f32_to_bf16(v[2 * u]) | ((uint32_t)f32_to_bf16(v[2 * u + 1]) << 16);
+            *reinterpret_cast<uint4 *>(it.hi + e) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        if (it.out32) {
+            *reinterpret_cast<float4 *>(it.out32 + e) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4 *>(it.out32 + e + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
     }
 }
 
@@ -1181,7 +1195,12 @@ hipError_t launch_to_bf16_batch(const SmallBatch &b, int64_t maxCount, hipStream
 }
 hipError_t launch_gen_omega_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s) {
     if (b.n <= 0 || maxCount <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gen_omega_batch, dim3((unsigned)std::min<int64_t>(2048, (maxCount + 255) / 256), b.n),
+    for (int i = 0; i < b.n; ++i) {
+        const SmallItem &it = b.it[i];
+        const int64_t n = it.b > 0 ? it.count / it.b : 0;
+        if (it.b <= 0 || it.count % it.b || n % 8 || it.count / 8 > 0xFFFFFFFFll) return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(k_gen_omega_batch, dim3((unsigned)std::min<int64_t>(2048, (maxCount / 8 + 255) / 256), b.n),
                        dim3(256), 0, s, b);
     return hipGetLastError();
 }
