@@ -841,24 +841,36 @@ __global__ void k_energy_batch(SmallBatch batch) {
 }
 
 // One workgroup per item: step x step block sums, then prefix sums along the
-// rows and down the columns of the grid (in place, fp64), then the fixed-rank sum.
-__global__ __launch_bounds__(256) void k_energy_grid(GridBatch batch) {
+// rows and down the columns of the grid (fp64), then the fixed-rank sum.  The
+// grid lives in LDS while it is built when it has at most lds_cells cells
+// (the prefix sums are chains of dependent read-modify-writes), else in place
+// in global memory; either way the same additions in the same order.
+__global__ __launch_bounds__(256) void k_energy_grid(GridBatch batch, int lds_cells) {
+    extern __shared__ double sgrid[];
     __shared__ double red[4];
     const GridItem &it = batch.it[blockIdx.x];
     const int tid = threadIdx.x, nr = it.nr, nf = it.nf, st = it.step, d = it.d;
+    const bool in_lds = nr * nf <= lds_cells;
+    double *S = in_lds ? sgrid : it.S;
     for (int c = tid; c < nr * nf; c += 256) {
         const int bi = c / nf, bj = c - bi * nf;
         double s = 0.0;
-        for (int r = bi * st; r < (bi + 1) * st; ++r)
-            for (int f = bj * st; f < (bj + 1) * st; ++f) s += (double)it.E[(size_t)r * d + f];
-        it.S[c] = s;
+        for (int r = bi * st; r < (bi + 1) * st; ++r) {
+            const float *row = it.E + (size_t)r * d + bj * st;
+#pragma unroll 8
+            for (int f = 0; f < st; ++f) s += (double)row[f];
+        }
+        S[c] = s;
     }
     __syncthreads();
     for (int bi = tid; bi < nr; bi += 256)
-        for (int bj = 1; bj < nf; ++bj) it.S[bi * nf + bj] += it.S[bi * nf + bj - 1];
+        for (int bj = 1; bj < nf; ++bj) S[bi * nf + bj] += S[bi * nf + bj - 1];
     __syncthreads();
     for (int bj = tid; bj < nf; bj += 256)
-        for (int bi = 1; bi < nr; ++bi) it.S[bi * nf + bj] += it.S[(bi - 1) * nf + bj];
+        for (int bi = 1; bi < nr; ++bi) S[bi * nf + bj] += S[(bi - 1) * nf + bj];
+    __syncthreads();
+    if (in_lds)
+        for (int c = tid; c < nr * nf; c += 256) it.S[c] = S[c];
     if (it.frt > 0 && it.frf > 0) {
         double s = 0.0;
         for (int e = tid; e < it.frt * it.frf; e += 256) {
@@ -1184,7 +1196,10 @@ hipError_t launch_energy_batch(const SmallBatch &b, int64_t maxCount, hipStream_
 }
 hipError_t launch_energy_grid(const GridBatch &b, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_energy_grid, dim3(b.n), dim3(256), 0, s, b);
+    int cells = 0;
+    for (int i = 0; i < b.n; ++i) cells = std::max(cells, b.it[i].nr * b.it[i].nf);
+    const int lds_cells = cells <= 8000 ? cells : 0;        // within the default 64 KiB of LDS
+    hipLaunchKernelGGL(k_energy_grid, dim3(b.n), dim3(256), (size_t)lds_cells * sizeof(double), s, b, lds_cells);
     return hipGetLastError();
 }
 hipError_t launch_to_bf16_batch(const SmallBatch &b, int64_t maxCount, hipStream_t s) {
