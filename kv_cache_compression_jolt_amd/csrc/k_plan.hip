@@ -933,36 +933,6 @@ __global__ void k_to_bf16(const float *in, uint16_t *hi, uint16_t *lo, int64_t c
     if (lo) lo[i] = f32_to_bf16(v - bf16_to_f32(h));
 }
 
-// omt[c][r] = Omega[r][c] (+-1, counter r * k + c of stream 1), zero rows c >= k
-__global__ void k_gen_omega(uint16_t *omt, float *omt32, uint64_t key, int k, int kp, int64_t n) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= (int64_t)kp * n) return;
-    const int c = (int)(e / n);
-    const int64_t r = e % n;
-    const float v = (c < k) ? rademacher(key, 1, (uint64_t)r * k + c) : 0.f;
-    if (omt) omt[e] = f32_to_bf16(v);
-    if (omt32) omt32[e] = v;
-}
-
-__global__ void k_energy(const float *core, float *energy, int LH, int rt_max, int d) {
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= rt_max * d) return;
-    float s = 0.f;
-    for (int lh = 0; lh < LH; ++lh) {
-        const float v = core[(size_t)lh * rt_max * d + e];
-        s = fmaf(v, v, s);
-    }
-    energy[e] = s;
-}
-
-__global__ void k_trace(const float *g, int d, double *out) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        double s = 0.0;
-        for (int i = 0; i < d; ++i) s += (double)g[(size_t)i * d + i];
-        *out = s;
-    }
-}
-
 __global__ void k_transpose(const float *in, float *out, int rows, int cols, int ldi, int ldo) {
     __shared__ float tile[32][33];
     const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
@@ -1223,25 +1193,6 @@ hipError_t launch_gen_omega_batch(const SmallBatch &b, int64_t maxCount, hipStre
 hipError_t launch_to_bf16(const float *in, uint16_t *hi, uint16_t *lo, int64_t count, hipStream_t s) {
     if (count <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_to_bf16, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, in, hi, lo, count);
-    return hipGetLastError();
-}
-
-hipError_t launch_gen_omega(uint16_t *omt, float *omt32, uint64_t key, int k, int kp, int64_t n, hipStream_t s) {
-    const int64_t cnt = (int64_t)kp * n;
-    if (cnt <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gen_omega, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s, omt, omt32, key, k, kp, n);
-    return hipGetLastError();
-}
-
-hipError_t launch_energy(const float *core, float *energy, int LH, int rt_max, int d, hipStream_t s) {
-    const int cnt = rt_max * d;
-    if (cnt <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_energy, dim3((cnt + 255) / 256), dim3(256), 0, s, core, energy, LH, rt_max, d);
-    return hipGetLastError();
-}
-
-hipError_t launch_trace(const float *g, int d, double *out, hipStream_t s) {
-    hipLaunchKernelGGL(k_trace, dim3(1), dim3(64), 0, s, g, d, out);
     return hipGetLastError();
 }
 

@@ -178,9 +178,6 @@ hipError_t launch_gen_omega_batch(const SmallBatch &b, int64_t maxCount, hipStre
 
 // elementwise conversions
 hipError_t launch_to_bf16(const float *in, uint16_t *hi, uint16_t *lo, int64_t count, hipStream_t s);
-hipError_t launch_gen_omega(uint16_t *omt, float *omt32, uint64_t key, int k, int kp, int64_t n, hipStream_t s);
-hipError_t launch_energy(const float *core, float *energy, int LH, int rt_max, int d, hipStream_t s);
-hipError_t launch_trace(const float *g, int d, double *out, hipStream_t s);
 hipError_t launch_transpose(const float *in, float *out, int rows, int cols, int ldi, int ldo, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 

@@ -207,7 +207,7 @@ jolt_status allocate_sorted(int n, const SortedCands *const *sc, const double *c
         const double *g = grid[i], nx2 = normx2[i];
         const int *cell = c.cell.data();
         const uint8_t *bits = c.bits.data();
-        // the distortion of distortion_table_cells, position by position
+        // D = delta_b max(0, ||X||^2 - S), S the captured energy of the cell (0 at rank 0)
         build_hull((int)c.B.size(), bp[i], [&](int p) {
             const double S = cell[p] < 0 ? 0.0 : g[cell[p]];
             return delta[bits[p]] * std::max(0.0, nx2 - S);
@@ -241,23 +241,6 @@ SortedCands sorted_cands(const std::vector<Cand> &cand, const int *cell, const i
         s.cand[p] = j;
     }
     return s;
-}
-
-void distortion_table(const double *grid /* captured energy S at (rt, rf) = (step (i+1), step (j+1)) */, int nf,
-                      int step, double normx2, const double *delta, const std::vector<Cand> &cand, double *D) {
-    for (size_t i = 0; i < cand.size(); ++i) {
-        const Cand &c = cand[i];
-        const double S = (c.rt == 0 || c.rf == 0) ? 0.0 : grid[(size_t)(c.rt / step - 1) * nf + (c.rf / step - 1)];
-        D[i] = delta[c.bits] * std::max(0.0, normx2 - S);
-    }
-}
-
-void distortion_table_cells(const double *grid, const int *cell, double normx2, const double *delta,
-                            const std::vector<Cand> &cand, double *D) {
-    for (size_t i = 0; i < cand.size(); ++i) {
-        const double S = cell[i] < 0 ? 0.0 : grid[cell[i]];
-        D[i] = delta[cand[i].bits] * std::max(0.0, normx2 - S);
-    }
 }
 
 }  // namespace jolt

@@ -31,15 +31,11 @@ struct SortedCands {
 };
 SortedCands sorted_cands(const std::vector<Cand> &cand, const int *cell, const int64_t *B);
 // allocate() with each item's distortions formed from its captured-energy grid
-// as distortion_table_cells does, position by position in byte order (no
-// table): choice[i] is a candidate index, distortion[i] its distortion
+// position by position in byte order, D = delta_b max(0, ||X||^2 - S(cell))
+// with S = 0 at rank 0 (no table): choice[i] is a candidate index,
+// distortion[i] its distortion
 jolt_status allocate_sorted(int n, const SortedCands *const *sc, const double *const *grid, const double *normx2,
                             const double *delta, int64_t budget, int *choice, double *distortion,
                             double *lambda_out);
-void distortion_table(const double *grid, int nf, int step, double normx2, const double *delta,
-                      const std::vector<Cand> &cand, double *D);
-// the same with each candidate's grid cell precomputed (-1: rank 0, S = 0)
-void distortion_table_cells(const double *grid, const int *cell, double normx2, const double *delta,
-                            const std::vector<Cand> &cand, double *D);
 
 }  // namespace jolt
