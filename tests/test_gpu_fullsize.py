@@ -69,6 +69,38 @@ def _items(cfg, picks):
     return [synth.make_item(cfg, specs[i]) for i in picks]
 
 
+def _check_dual(torch, jb, J, cfg, items, allocs, budget):
+    """The allocation is the oracle's exact-rational single dual (oracle/alloc.py)
+    on the GPU's own energy tables and norms: the same (r_t, r_f, b) for every
+    item, except where the two candidates' Lagrangian values at the oracle's
+    lambda* tie to 1e-9 (the oracle sums the captured energies in its own fp64
+    order)."""
+    from oracle import alloc as oalloc
+    bits = [b for b in range(9) if (int(J.cfg.bits_mask) >> b) & 1]
+    delta = _delta()
+    tables = []
+    for i, it in enumerate(items):
+        v = J.factors(i)
+        E = _fetch(torch, v.energy, v.rt_max * it.d).reshape(v.rt_max, it.d).astype(np.float64)
+        nx2 = float(_fetch(torch, v.normx2, 1, np.float64)[0])
+        cand = oalloc.candidate_grid(v.rt_max, v.rf_max, cfg.rank_step, bits)
+        e = 2 if cfg.dtype == "bf16" else 4
+        tables.append({"cand": cand, "D": oalloc.distortion_table(E, nx2, delta, cand),
+                       "B": oalloc.bytes_table(it.L, it.H, it.T, it.d, e, cand)})
+    choice, lam, ok = oalloc.lagrangian_allocate(tables, budget)
+    assert ok
+    lamf = float(lam)
+    for i, (t, a) in enumerate(zip(tables, allocs)):
+        ref = tuple(int(x) for x in t["cand"][choice[i]])
+        got = (a.rt, a.rf, a.bits)
+        if got == ref:
+            continue
+        j = [tuple(int(x) for x in c) for c in t["cand"]].index(got)
+        lo = t["D"][choice[i]] + lamf * float(t["B"][choice[i]])
+        lg = t["D"][j] + lamf * float(t["B"][j])
+        assert abs(lg - lo) <= 1e-9 * (abs(lo) + 1.0), ("allocation differs from the oracle's dual", i, got, ref)
+
+
 def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=None):
     torch = torch_cuda()
     jb = jolt_binding()
@@ -84,6 +116,7 @@ def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=No
     allocs, lam = J.plan(xs)
     assert J.status == jb.JOLT_OK, J.status
     assert sum(a.bytes for a in allocs) <= budget
+    _check_dual(torch, jb, J, cfg, items, allocs, budget)
     rt_max = cfg.rt_max
     check = range(len(items)) if check_items is None else check_items
     factors = {}
