@@ -959,25 +959,44 @@ __device__ __forceinline__ void put_param(uint8_t *base, size_t idx, float v) {
     else reinterpret_cast<float *>(base)[idx] = v;
 }
 
+// Workgroups [0, tiles) transpose U~_t ([rt_max][T] in the plan, [T][rt]
+// in the payload) through a 64 x 65 LDS tile, so that both the reads and the
+// writes run along rows; the rest write U~_f, C~ and the header element by
+// element (32-bit index math: the launcher checks the sizes).
 template <typename T>
-__global__ void k_store(StoreBatch batch) {
+__global__ __launch_bounds__(256) void k_store(StoreBatch batch, int tiles) {
+    __shared__ float tile[64][65];
     const StoreItem &it = batch.it[blockIdx.y];
-    const size_t n_ut = (size_t)it.T * it.rt, n_uf = (size_t)it.d * it.rf, n_c = (size_t)it.LH * it.rt * it.rf;
-    const size_t total = n_ut + n_uf + n_c + 16;
-    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
-        if (e < n_ut) {
-            const size_t t = e / it.rt, r = e % it.rt;
-            put_param<T>(it.pay + it.off_ut, e, it.ut[r * it.T + t]);
-        } else if (e < n_ut + n_uf) {
-            const size_t q = e - n_ut, f = q / it.rf, j = q % it.rf;
-            put_param<T>(it.pay + it.off_uf, q, it.uf[f * it.d + j]);
-        } else if (e < n_ut + n_uf + n_c) {
-            const size_t q = e - n_ut - n_uf;
-            const size_t lh = q / ((size_t)it.rt * it.rf), rem = q % ((size_t)it.rt * it.rf);
-            const size_t r = rem / it.rf, j = rem % it.rf;
-            put_param<T>(it.pay + it.off_core, q, it.core[(lh * it.rt_max + r) * it.d + j]);
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < tiles) {
+        const int ntt = (it.T + 63) / 64, ntr = (it.rt + 63) / 64;
+        for (int tb = blockIdx.x; tb < ntt * ntr; tb += tiles) {
+            const int t0 = 64 * (tb % ntt), r0 = 64 * (tb / ntt);
+            __syncthreads();
+            for (int e = tid; e < 64 * 64; e += 256) {
+                const int r = e >> 6, t = e & 63;
+                if (r0 + r < it.rt && t0 + t < it.T) tile[r][t] = it.ut[(size_t)(r0 + r) * it.T + t0 + t];
+            }
+            __syncthreads();
+            for (int e = tid; e < 64 * 64; e += 256) {
+                const int t = e >> 6, r = e & 63;
+                if (r0 + r < it.rt && t0 + t < it.T)
+                    put_param<T>(it.pay + it.off_ut, (size_t)(t0 + t) * it.rt + r0 + r, tile[r][t]);
+            }
+        }
+        return;
+    }
+    const uint32_t n_uf = (uint32_t)it.d * it.rf, rr = (uint32_t)it.rt * it.rf, n_c = (uint32_t)it.LH * rr;
+    const uint32_t total = n_uf + n_c + 16;
+    for (uint32_t e = (blockIdx.x - tiles) * 256 + tid; e < total; e += (gridDim.x - tiles) * 256) {
+        if (e < n_uf) {
+            const uint32_t f = e / it.rf, j = e - f * it.rf;
+            put_param<T>(it.pay + it.off_uf, e, it.uf[(size_t)f * it.d + j]);
+        } else if (e < n_uf + n_c) {
+            const uint32_t q = e - n_uf, lh = q / rr, rem = q - lh * rr, r = rem / it.rf, j = rem - r * it.rf;
+            put_param<T>(it.pay + it.off_core, q, it.core[((size_t)lh * it.rt_max + r) * it.d + j]);
         } else {
-            const size_t w = e - n_ut - n_uf - n_c;
+            const uint32_t w = e - n_uf - n_c;
             reinterpret_cast<uint32_t *>(it.pay)[w] = it.header[w];
         }
     }
@@ -1212,9 +1231,18 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
 
 hipError_t launch_store(const StoreBatch &b, int dtype, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    dim3 g(512, b.n);
-    if (dtype == JOLT_BF16) hipLaunchKernelGGL(k_store<uint16_t>, g, dim3(256), 0, s, b);
-    else hipLaunchKernelGGL(k_store<float>, g, dim3(256), 0, s, b);
+    uint64_t maxElem = 0;
+    int tiles = 1;
+    for (int i = 0; i < b.n; ++i) {
+        const StoreItem &it = b.it[i];
+        const uint64_t e = (uint64_t)it.d * it.rf + (uint64_t)it.LH * it.rt * it.rf + 16;
+        if (e > 0xFFFFFFFFull) return hipErrorInvalidValue;
+        maxElem = std::max(maxElem, e);
+        tiles = std::max(tiles, std::min(512, ((it.T + 63) / 64) * ((it.rt + 63) / 64)));
+    }
+    dim3 g(tiles + (unsigned)std::min<uint64_t>(512, (maxElem + 255) / 256), b.n);
+    if (dtype == JOLT_BF16) hipLaunchKernelGGL(k_store<uint16_t>, g, dim3(256), 0, s, b, tiles);
+    else hipLaunchKernelGGL(k_store<float>, g, dim3(256), 0, s, b, tiles);
     return hipGetLastError();
 }
 
