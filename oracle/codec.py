@@ -10,15 +10,12 @@ Readings:
   * stored Tucker parameters are the leading blocks U_t[:, :r_t], U_f[:, :r_f],
     C[:, :, :r_t, :r_f], rounded (RNE) to the parameter dtype (bf16; fp32 for
     fp32 caches);
-  * the decoder forms X^_lh = U_t W_lh from the stored parameters, with the
-    inner product W_lh = C_lh U_f^T (r_t x d) held to fp32 precision: rounded to
-    fp32 for fp32 caches, and for bf16 caches as the bf16 pair hi = round(W),
-    lo = round(W - hi) (W to about 2^-17).  The pages fix no intermediate
-    precision; a single bf16 rounding of W would let the two sides' W differ by
-    a bf16 step wherever their accumulations straddle a rounding boundary,
-    while a hi + lo pair that straddles one changes by a lo step only;
-  * the residual is closed-loop: R = X - X^ with X^ exactly as the decoder
-    will rebuild it from the stored, rounded parameters;
+  * the low-rank part is the Tucker product of the stored parameters,
+    X^_lh = U_t (C_lh U_f^T), formed here in fp64 with no intermediate
+    rounding (the pages fix no intermediate precision; a decoder that holds
+    C_lh U_f^T to a finite precision differs from this by that precision);
+  * the residual is closed-loop: R = X - X^ with X^ the reconstruction from the
+    stored, rounded parameters;
   * output is rounded (RNE) to the cache dtype.
 """
 from __future__ import annotations
@@ -64,17 +61,11 @@ def stored_params(U_t, U_f, C_full, rt: int, rf: int, dtype: str) -> StoredParam
 
 
 def low_rank(p: StoredParams, L: int, H: int, T: int, d: int, dtype: str) -> np.ndarray:
-    """X^ as the decoder rebuilds it: X^_lh = U_t W_lh, W_lh = C_lh U_f^T at fp32
-    precision (bf16 caches: hi + lo bf16 pair)."""
+    """X^_lh = U_t (C_lh U_f^T) from the stored parameters, in fp64."""
     rt = p.Ut.shape[1]
     if rt == 0:
         return np.zeros((L, H, T, d))
     W = np.matmul(p.C, p.Uf.T[None, None])               # L x H x rt x d
-    if dtype == "f32":
-        W = quant.round_f32(W)
-    else:
-        hi = quant.round_bf16(W)
-        W = hi + quant.round_bf16(W - hi)
     return np.matmul(p.Ut[None, None], W)
 
 

@@ -14,7 +14,8 @@ Per item:
   * the allocation fits the budget and reports the bytes jolt_item_bytes gives;
   * codec on sampled row blocks: the oracle encodes the block (token rows of one
     (layer, head)) from the GPU's stored U_t, U_f and core; codes and scales
-    agree to the codec parity test's fractions, the GPU's decoded block is the
+    agree except at rounding boundaries within the bound on the two
+    residuals' difference (tests/parity_util.py), the GPU's decoded block is the
     oracle's decode of the GPU's codes (rel 1e-3), and its error is at most
     1.05 x the oracle's + 1e-4;
   * the reconstruction error is at most the plain truncation error
@@ -31,6 +32,7 @@ import synth
 from oracle import codec as ocodec
 from oracle import quant as oquant
 from tests.gpu_util import jolt_binding, rel, section, torch_cuda
+from tests.parity_util import check_codes, row_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -191,8 +193,9 @@ def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=No
                 wd = np.frombuffer(pay[off[4] + 8 * a.bits * G0:off[4] + 8 * a.bits * (G0 + Gb)].cpu().numpy()
                                    .tobytes(), dtype="<u8").reshape(Gb, a.bits)
                 u_gpu, u_ref = oquant.unpack_codes(wd, a.bits), oquant.unpack_codes(enc.words, a.bits)
-                assert np.sum(u_gpu != u_ref) <= max(1e-4 * u_ref.size, 8), np.mean(u_gpu != u_ref)
-                assert np.sum(sc != enc.scale_bits) <= max(1e-3 * Gb, 2), np.mean(sc != enc.scale_bits)
+                Rb = Xb - ocodec.low_rank(sp, 1, 1, ns, d, cfg.dtype)
+                check_codes(u_gpu, u_ref, sc, enc.scale_bits, enc.rotated, row_tolerance(sp.Ut, sp.Uf, sp.C, Rb),
+                            a.bits, d)
                 own = ocodec.decode(ocodec.Encoded(rt, rf, a.bits, sp, wd, sc, None), 1, 1, ns, d, it.seed,
                                     it.item_id, cfg.dtype)
             assert rel(got, own) <= 1e-3, dict(block=(l, h, t0), gpu_vs_oracle=rel(got, ref))
