@@ -4,6 +4,7 @@ import os
 
 import numpy as np
 import pytest
+from scipy import special
 
 from oracle import quant
 from oracle.calibrate import measure
@@ -67,3 +68,58 @@ def test_delta_b_constants(golden_dir):
     for b in range(3, 9):
         assert delta[b] < delta[b - 1]
     assert 3.0 < delta[7] / delta[8] < 5.0
+
+
+def _half_normal_moment(a, b, c):
+    """Integral over [a, b] (0 <= a <= b) of (x - c)^2 times the half-normal
+    density 2 phi(x), from the Gaussian partial moments:
+    int phi = Phi(b) - Phi(a), int x phi = phi(a) - phi(b),
+    int x^2 phi = Phi(b) - Phi(a) + a phi(a) - b phi(b)."""
+    Phi = lambda x: 0.5 * (1.0 + special.erf(x / np.sqrt(2.0)))
+    phi = lambda x: np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+    m0 = Phi(b) - Phi(a)
+    m1 = phi(a) - phi(b)
+    m2 = m0 + a * phi(a) - b * phi(b)
+    return 2.0 * (m2 - 2.0 * c * m1 + c * c * m0)
+
+
+def _delta_exact(bits, n=200001, hi=9.0):
+    """Expected relative squared error of the b-bit group quantizer on iid N(0,1)
+    groups of 64, by quadrature over the group's absmax M (order statistics),
+    not by sampling.  Given M, the scale is s = bf16(M / qmax); the other 63
+    magnitudes are iid half-normal conditioned below M and each is rounded to
+    the nearest multiple k s (k <= qmax, larger values clamped to qmax s); the
+    absmax element itself is rounded the same way.  The per-element energy is 1,
+    so delta_b = E[group squared error] / 64."""
+    qm = (1 << (bits - 1)) - 1
+    M = np.linspace(1e-3, hi, n)
+    s = quant.bf16_bits_to_f32(quant.f32_to_bf16_bits((M / qm).astype(np.float32))).astype(np.float64)
+    F = special.erf(M / np.sqrt(2.0))                      # P(|x| < M)
+    k = np.arange(qm + 1)[:, None]
+    a = np.clip((k - 0.5) * s, 0.0, M)
+    b = np.clip((k + 0.5) * s, 0.0, M)
+    b[-1] = M                                              # everything above (qmax - 1/2) s -> qmax s
+    inner = _half_normal_moment(a, b, k * s).sum(axis=0) / F
+    top = M - np.minimum(np.rint(M / s), qm) * s
+    dens = 64.0 * F ** 63 * 2.0 * np.exp(-0.5 * M * M) / np.sqrt(2.0 * np.pi)     # density of M
+    g = 63.0 * inner + top * top
+    return float(np.trapezoid(g * dens, M) / 64.0), float(np.trapezoid(dens, M))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_delta_b_matches_exact_quadrature(golden_dir, bits):
+    """The frozen delta_b (a 2^20-group Monte-Carlo run of the oracle's
+    quantizer) against its expectation computed independently in closed form:
+    Monte-Carlo error at 2^20 groups is about 3e-4 relative, so 1e-3 pins the
+    definition (relative MSE against the input energy), the scale rule and the
+    rounding; the high-resolution limit (63/64) E[M^2] / (12 qmax^2) is the
+    b -> infinity check of the same expression."""
+    delta = json.load(open(os.path.join(golden_dir, "delta_b.json")))["delta"]
+    exact, mass = _delta_exact(bits)
+    assert abs(mass - 1.0) < 1e-9
+    assert abs(delta[bits] / exact - 1.0) < 1e-3, (bits, delta[bits], exact)
+    if bits >= 6:
+        f = lambda m: m * m * 64 * special.erf(m / np.sqrt(2)) ** 63 * 2 * np.exp(-m * m / 2) / np.sqrt(2 * np.pi)
+        em2 = float(np.trapezoid(f(np.linspace(0, 12, 400001)), np.linspace(0, 12, 400001)))
+        qm = (1 << (bits - 1)) - 1
+        assert abs(exact / ((63 / 64) * em2 / (12 * qm * qm)) - 1) < 0.02
