@@ -208,11 +208,14 @@ jolt_status jolt_plan_from_tables(int32_t n, const int32_t *n_cand, const int32_
  * or, with inverse != 0, out = s o ((1/sqrt d) H in). */
 jolt_status jolt_rotate(jolt_handle h, const float *in, float *out, int64_t rows, int32_t d,
                         uint64_t seed, uint32_t item_id, int32_t inverse, void *stream);
-/* Quantize and pack fp32 rotated rows (device; rows x d, d a multiple of 64):
- * codes = (rows d / 64) groups x bits uint64 words, scales = bf16 per group. */
+/* Quantize and pack fp32 rotated rows (device; rows x d, d = 64 or 128):
+ * codes = (rows d / 64) groups x bits uint64 words, scales = bf16 per group.
+ * Runs the fused encoder's own quantize / pack / store code on rows read from
+ * memory, so its output is the encoder's for the same rotated residual. */
 jolt_status jolt_quantize_pack(jolt_handle h, const float *rot, int64_t rows, int32_t d, int32_t bits,
                                uint64_t *codes, uint16_t *scales, void *stream);
-/* Inverse of jolt_quantize_pack: q * scale per element (fp32, device). */
+/* Inverse of jolt_quantize_pack: q * scale per element (fp32, device), with
+ * the fused decoder's own code loading and unpacking. */
 jolt_status jolt_unpack_dequant(jolt_handle h, const uint64_t *codes, const uint16_t *scales,
                                 int64_t rows, int32_t d, int32_t bits, float *out, void *stream);
 /* +-1 values of the counter stream (device, fp32): out[i] for counters

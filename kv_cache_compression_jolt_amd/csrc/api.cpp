@@ -441,8 +441,9 @@ extern "C" jolt_status jolt_quantize_pack(jolt_handle h, const float *rot, int64
                                           uint64_t *codes, uint16_t *scales, void *stream) {
     if (!h) return JOLT_E_INVALID;
     clear_err(h);
-    if (rows < 0 || d <= 0 || d % 64 || bits < 2 || bits > 8 || (rows > 0 && (!rot || !codes || !scales)))
+    if (rows < 0 || bits < 2 || bits > 8 || (rows > 0 && (!rot || !codes || !scales)))
         return fail(h, JOLT_E_INVALID, "quantize_pack: bad arguments");
+    if (d != 64 && d != 128) return fail(h, JOLT_E_UNSUPPORTED, "quantize_pack: d must be 64 or 128");
     hipError_t e = launch_quantize_pack(rot, rows, d, bits, reinterpret_cast<uint8_t *>(codes), scales,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "quantize_pack");
@@ -452,8 +453,9 @@ extern "C" jolt_status jolt_unpack_dequant(jolt_handle h, const uint64_t *codes,
                                            int64_t rows, int32_t d, int32_t bits, float *out, void *stream) {
     if (!h) return JOLT_E_INVALID;
     clear_err(h);
-    if (rows < 0 || d <= 0 || d % 64 || bits < 2 || bits > 8 || (rows > 0 && (!out || !codes || !scales)))
+    if (rows < 0 || bits < 2 || bits > 8 || (rows > 0 && (!out || !codes || !scales)))
         return fail(h, JOLT_E_INVALID, "unpack_dequant: bad arguments");
+    if (d != 64 && d != 128) return fail(h, JOLT_E_UNSUPPORTED, "unpack_dequant: d must be 64 or 128");
     hipError_t e = launch_unpack_dequant(reinterpret_cast<const uint8_t *>(codes), scales, rows, d, bits, out,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "unpack_dequant");

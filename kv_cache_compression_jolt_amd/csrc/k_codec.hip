@@ -340,6 +340,74 @@ struct Tile {
     static constexpr int NMF = D / 32;
 };
 
+// ------------------------------------------------------------------ quantize, pack, store
+// One lane's share of a 64-group of rotated residual values y: the whole group
+// (d = 128, group h of the row) or half of it (d = 64: elements 32 h ..
+// 32 h + 31, the two lane halves sharing one scale).  Group absmax, scale =
+// bf16(absmax / qmax), inv = 1 / scale (0 for a zero scale), codes clamped to
+// [-qmax, qmax] and rounded half to even by the fp32 add of 1.5 * 2^23 + 2^(b-1)
+// (ulp 1 there, so the sum's low bits are the code u = q + 2^(b-1)), packed as
+// the group's little-endian bit stream and stored with the scale when tv.
+// Every lane of the wave must call it (d = 64 combines the halves' absmax).
+template <int D, int BITS>
+__device__ __forceinline__ void quantize_store(const float *y, int h, bool tv, size_t row, uint8_t *codes,
+                                               uint16_t *scales) {
+    constexpr int NE = D / 2;
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) amax = fmaxf(amax, fabsf(y[e]));
+    if (D == 64) amax = fmaxf(amax, __shfl_xor(amax, 32));
+    constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+    const float s32 = amax / qmax;
+    const uint16_t sbits = f32_to_bf16(s32);
+    const float scale = bf16_to_f32(sbits);
+    const float inv = (scale == 0.f) ? 0.f : 1.0f / scale;
+    constexpr float magic = 12582912.0f + (float)(1 << (BITS - 1));
+    uint32_t tq[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        float v = y[e] * inv;
+        v = fminf(fmaxf(v, -qmax), qmax);
+        tq[e] = __float_as_uint(v + magic);
+    }
+    constexpr int NW = BITS * NE / 32;
+    uint32_t w[NW];
+    pack_codes<BITS, NE>(tq, w);
+    if (tv) {
+        const size_t grp = row * (D / 64) + (D == 128 ? h : 0);
+        uint8_t *dst = codes + grp * 8 * BITS + (D == 64 ? h * 4 * BITS : 0);
+        if constexpr (NW % 2 == 0) {
+#pragma unroll
+            for (int k = 0; k < NW; k += 2) *reinterpret_cast<uint2 *>(dst + 4 * k) = make_uint2(w[k], w[k + 1]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NW; ++k) *reinterpret_cast<uint32_t *>(dst + 4 * k) = w[k];
+        }
+        if (D == 128 || h == 0) scales[grp] = sbits;
+    }
+}
+
+// The code words and scale of one lane's share of a group (the layout above);
+// `row` must be a valid row.
+template <int D, int BITS>
+__device__ __forceinline__ void load_codes(const uint8_t *codes, const uint16_t *scales, size_t row, int h,
+                                           uint32_t *w, uint16_t &sbits) {
+    constexpr int NCW = BITS * (D / 2) / 32;
+    const size_t grp = row * (D / 64) + (D == 128 ? h : 0);
+    const uint8_t *src = codes + grp * 8 * BITS + (D == 64 ? h * 4 * BITS : 0);
+    if constexpr (NCW % 2 == 0) {
+#pragma unroll
+        for (int k = 0; k < NCW; k += 2) {
+            uint2 v = *reinterpret_cast<const uint2 *>(src + 4 * k);
+            w[k] = v.x; w[k + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NCW; ++k) w[k] = *reinterpret_cast<const uint32_t *>(src + 4 * k);
+    }
+    sbits = scales[grp];
+}
+
 // ------------------------------------------------------------------ fused encoder
 template <typename T, int D, int BITS, int NWV, bool WL>
 __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
@@ -422,40 +490,7 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
             y[e + 4] = (u - w) * isd;
         }
 
-    // group absmax, bf16 scale, codes
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) amax = fmaxf(amax, fabsf(y[e]));
-    if (D == 64) amax = fmaxf(amax, __shfl_xor(amax, 32));
-    constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
-    const float s32 = amax / qmax;
-    const uint16_t sbits = f32_to_bf16(s32);
-    const float scale = bf16_to_f32(sbits);
-    const float inv = (scale == 0.f) ? 0.f : 1.0f / scale;
-    constexpr float magic = 12582912.0f + (float)(1 << (BITS - 1));
-    uint32_t tq[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        float v = y[e] * inv;
-        v = fminf(fmaxf(v, -qmax), qmax);
-        tq[e] = __float_as_uint(v + magic);
-    }
-    constexpr int NW = BITS * NE / 32;
-    uint32_t w[NW];
-    pack_codes<BITS, NE>(tq, w);
-    if (tv) {
-        const size_t row = (size_t)lh * it.T + tok;
-        const size_t grp = row * (D / 64) + (D == 128 ? h : 0);
-        uint8_t *dst = it.codes + grp * 8 * BITS + (D == 64 ? h * 4 * BITS : 0);
-        if constexpr (NW % 2 == 0) {
-#pragma unroll
-            for (int k = 0; k < NW; k += 2) *reinterpret_cast<uint2 *>(dst + 4 * k) = make_uint2(w[k], w[k + 1]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < NW; ++k) *reinterpret_cast<uint32_t *>(dst + 4 * k) = w[k];
-        }
-        if (D == 128 || h == 0) it.scales[grp] = sbits;
-    }
+    quantize_store<D, BITS>(y, h, tv, (size_t)lh * it.T + tok, it.codes, it.scales);
 }
 
 // ------------------------------------------------------------------ fused decoder
@@ -480,22 +515,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
     constexpr int NCW = BITS > 0 ? BITS * NE / 32 : 1;
     uint32_t w[NCW];
     uint16_t sbits = 0;
-    if constexpr (BITS > 0) {
-        const size_t row = (size_t)lh * it.T + (tv ? tok : 0);
-        const size_t grp = row * (D / 64) + (D == 128 ? h : 0);
-        const uint8_t *src = it.codes + grp * 8 * BITS + (D == 64 ? h * 4 * BITS : 0);
-        if constexpr (NCW % 2 == 0) {
-#pragma unroll
-            for (int k = 0; k < NCW; k += 2) {
-                uint2 v = *reinterpret_cast<const uint2 *>(src + 4 * k);
-                w[k] = v.x; w[k + 1] = v.y;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < NCW; ++k) w[k] = *reinterpret_cast<const uint32_t *>(src + 4 * k);
-        }
-        sbits = it.scales[grp];
-    }
+    if constexpr (BITS > 0) load_codes<D, BITS>(it.codes, it.scales, (size_t)lh * it.T + (tv ? tok : 0), h, w, sbits);
 
     const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
 
@@ -649,51 +669,43 @@ __global__ void k_rotate_rows(const float *in, float *out, int64_t rows, int d, 
     }
 }
 
-// One thread per 64-group: the quantizer definition step by step.
-__global__ void k_quant_pack_groups(const float *x, int64_t groups, int bits, uint8_t *codes, uint16_t *scales) {
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= groups) return;
-    const float *p = x + g * 64;
-    float amax = 0.f;
-    for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(p[j]));
-    const float qmax = (float)((1 << (bits - 1)) - 1);
-    const float s32 = amax / qmax;
-    const uint16_t sb = f32_to_bf16(s32);
-    const float scale = bf16_to_f32(sb);
-    const float inv = 1.0f / scale;
-    uint64_t st[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < 64; ++j) {
-        float q = 0.f;
-        if (scale != 0.f) {
-            const float yv = p[j] * inv;
-            q = fminf(fmaxf(rintf(yv), -qmax), qmax);
-        }
-        const uint64_t u = (uint64_t)((int)q + (1 << (bits - 1)));
-        const int pos = bits * j;
-        st[pos >> 6] |= u << (pos & 63);
-        if ((pos & 63) + bits > 64) st[(pos >> 6) + 1] |= u >> (64 - (pos & 63));
+// The fused encoder's quantize / pack / store on rotated rows read from memory:
+// a wave per 32 rows, lane (t, h) holding row t's share of a group exactly as
+// k_encode holds it after its rotation.
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void k_quant_rows(const float *rot, int64_t rows, uint8_t *codes,
+                                                    uint16_t *scales) {
+    constexpr int NE = D / 2;
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 32 + (lane & 31);
+    const bool tv = r < rows;
+    const float *src = rot + (size_t)(tv ? r : 0) * D + h * NE;
+    float y[NE];
+#pragma unroll
+    for (int e = 0; e < NE; e += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(src + e);
+        y[e] = v.x; y[e + 1] = v.y; y[e + 2] = v.z; y[e + 3] = v.w;
     }
-    uint64_t *dst = reinterpret_cast<uint64_t *>(codes + g * 8 * bits);
-    for (int k = 0; k < bits; ++k) dst[k] = st[k];
-    scales[g] = sb;
+    quantize_store<D, BITS>(y, h, tv, (size_t)r, codes, scales);
 }
 
-__global__ void k_unpack_dequant_groups(const uint8_t *codes, const uint16_t *scales, int64_t groups, int bits,
-                                        float *out) {
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= groups) return;
-    const uint64_t *src = reinterpret_cast<const uint64_t *>(codes + g * 8 * bits);
-    uint64_t st[9];
-    for (int k = 0; k < bits; ++k) st[k] = src[k];
-    st[bits] = 0;
-    const float scale = bf16_to_f32(scales[g]);
-    for (int j = 0; j < 64; ++j) {
-        const int pos = bits * j;
-        uint64_t v = st[pos >> 6] >> (pos & 63);
-        if ((pos & 63) + bits > 64) v |= st[(pos >> 6) + 1] << (64 - (pos & 63));
-        const int u = (int)(v & ((1u << bits) - 1u));
-        out[g * 64 + j] = (float)(u - (1 << (bits - 1))) * scale;
-    }
+// The fused decoder's code loading and unpacking, then q * scale (exact in fp32).
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void k_dequant_rows(const uint8_t *codes, const uint16_t *scales, int64_t rows,
+                                                      float *out) {
+    constexpr int NE = D / 2;
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 32 + (lane & 31);
+    if (r >= rows) return;
+    uint32_t w[BITS * NE / 32];
+    uint16_t sbits;
+    load_codes<D, BITS>(codes, scales, (size_t)r, h, w, sbits);
+    float u[NE];
+    unpack_codes<BITS, NE>(w, u);
+    const float scale = bf16_to_f32(sbits), off = (float)(1 << (BITS - 1));
+    float *dst = out + (size_t)r * D + h * NE;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) dst[e] = (u[e] - off) * scale;
 }
 
 __global__ void k_rademacher_fill(uint64_t key, uint32_t stream, uint64_t first, int64_t count, float *out) {
@@ -820,21 +832,49 @@ hipError_t launch_rotate(const float *in, float *out, int64_t rows, int d, const
                        sb[0], sb[1], sb[2], sb[3], inverse);
     return hipGetLastError();
 }
+template <int D>
+static hipError_t quant_rows_d(const float *rot, int64_t rows, int bits, uint8_t *codes, uint16_t *scales,
+                               hipStream_t s) {
+    const dim3 grid((unsigned)((rows + 127) / 128));
+    switch (bits) {
+        case 2: hipLaunchKernelGGL((k_quant_rows<D, 2>), grid, dim3(256), 0, s, rot, rows, codes, scales); break;
+        case 3: hipLaunchKernelGGL((k_quant_rows<D, 3>), grid, dim3(256), 0, s, rot, rows, codes, scales); break;
+        case 4: hipLaunchKernelGGL((k_quant_rows<D, 4>), grid, dim3(256), 0, s, rot, rows, codes, scales); break;
+        case 5: hipLaunchKernelGGL((k_quant_rows<D, 5>), grid, dim3(256), 0, s, rot, rows, codes, scales); break;
+        case 6: hipLaunchKernelGGL((k_quant_rows<D, 6>), grid, dim3(256), 0, s, rot, rows, codes, scales); break;
+        case 7: hipLaunchKernelGGL((k_quant_rows<D, 7>), grid, dim3(256), 0, s, rot, rows, codes, scales); break;
+        case 8: hipLaunchKernelGGL((k_quant_rows<D, 8>), grid, dim3(256), 0, s, rot, rows, codes, scales); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+template <int D>
+static hipError_t dequant_rows_d(const uint8_t *codes, const uint16_t *scales, int64_t rows, int bits, float *out,
+                                 hipStream_t s) {
+    const dim3 grid((unsigned)((rows + 127) / 128));
+    switch (bits) {
+        case 2: hipLaunchKernelGGL((k_dequant_rows<D, 2>), grid, dim3(256), 0, s, codes, scales, rows, out); break;
+        case 3: hipLaunchKernelGGL((k_dequant_rows<D, 3>), grid, dim3(256), 0, s, codes, scales, rows, out); break;
+        case 4: hipLaunchKernelGGL((k_dequant_rows<D, 4>), grid, dim3(256), 0, s, codes, scales, rows, out); break;
+        case 5: hipLaunchKernelGGL((k_dequant_rows<D, 5>), grid, dim3(256), 0, s, codes, scales, rows, out); break;
+        case 6: hipLaunchKernelGGL((k_dequant_rows<D, 6>), grid, dim3(256), 0, s, codes, scales, rows, out); break;
+        case 7: hipLaunchKernelGGL((k_dequant_rows<D, 7>), grid, dim3(256), 0, s, codes, scales, rows, out); break;
+        case 8: hipLaunchKernelGGL((k_dequant_rows<D, 8>), grid, dim3(256), 0, s, codes, scales, rows, out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 hipError_t launch_quantize_pack(const float *rot, int64_t rows, int d, int bits, uint8_t *codes, uint16_t *scales,
                                 hipStream_t s) {
-    const int64_t groups = rows * d / 64;
-    if (groups <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_quant_pack_groups, dim3((unsigned)((groups + 127) / 128)), dim3(128), 0, s, rot, groups,
-                       bits, codes, scales);
-    return hipGetLastError();
+    if (rows <= 0) return hipSuccess;
+    return d == 128 ? quant_rows_d<128>(rot, rows, bits, codes, scales, s)
+                    : quant_rows_d<64>(rot, rows, bits, codes, scales, s);
 }
 hipError_t launch_unpack_dequant(const uint8_t *codes, const uint16_t *scales, int64_t rows, int d, int bits,
                                  float *out, hipStream_t s) {
-    const int64_t groups = rows * d / 64;
-    if (groups <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_unpack_dequant_groups, dim3((unsigned)((groups + 127) / 128)), dim3(128), 0, s, codes,
-                       scales, groups, bits, out);
-    return hipGetLastError();
+    if (rows <= 0) return hipSuccess;
+    return d == 128 ? dequant_rows_d<128>(codes, scales, rows, bits, out, s)
+                    : dequant_rows_d<64>(codes, scales, rows, bits, out, s);
 }
 hipError_t launch_rademacher(uint64_t key, uint32_t stream, uint64_t first, int64_t count, float *out,
                              hipStream_t s) {
