@@ -16,4 +16,5 @@ from .caches import (  # noqa: F401
     budget_for_ratio,
     bf16_bits_to_f64,
     f64_to_bf16_bits,
+    iter_raw_parallel,
 )

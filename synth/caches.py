@@ -27,8 +27,9 @@ import numpy as np
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp64 -> fp32 (RNE) -> bf16 (RNE); returns the uint16 bit patterns."""
     f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = f.view(np.uint32)
+    # finite values stay below 2^32 after the rounding increment
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -192,8 +193,9 @@ def item_specs(cfg: CacheConfig, n_items: Optional[int] = None) -> List[Item]:
 
 
 def make_item(cfg: CacheConfig, spec: Item, sigma: Optional[float] = None,
-              keep_planted: bool = False) -> Item:
-    """Fill ``spec`` with its seeded tensor."""
+              keep_planted: bool = False, keep_x: bool = True) -> Item:
+    """Fill ``spec`` with its seeded tensor (``keep_x=False``: the stored bits
+    only, without the fp64 copy)."""
     L, H, T, d = spec.L, spec.H, spec.T, spec.d
     rt, rf = spec.rank_t, spec.rank_f
     sig = cfg.sigma if sigma is None else sigma
@@ -214,12 +216,12 @@ def make_item(cfg: CacheConfig, spec: Item, sigma: Optional[float] = None,
                 X[l, h][:, ch] *= 8.0
     if spec.dtype == "f32":
         raw = X.astype(np.float32)
-        xv = raw.astype(np.float64)
+        xv = raw.astype(np.float64) if keep_x else None
     else:
         raw = f64_to_bf16_bits(X)
-        xv = bf16_bits_to_f64(raw)
+        xv = bf16_bits_to_f64(raw) if keep_x else None
     del X
-    spec.x = xv
+    spec.x = xv if keep_x else None
     spec.raw = raw
     if keep_planted:
         spec.planted = {"U": U, "V": V, "C": C}
@@ -228,6 +230,35 @@ def make_item(cfg: CacheConfig, spec: Item, sigma: Optional[float] = None,
 
 def make_items(cfg: CacheConfig, n_items: Optional[int] = None, **kw) -> List[Item]:
     return [make_item(cfg, s, **kw) for s in item_specs(cfg, n_items)]
+
+
+def _raw_worker(args):
+    cfg, spec = args
+    try:
+        import threadpoolctl
+        with threadpoolctl.threadpool_limits(1):
+            return make_item(cfg, spec, keep_x=False).raw
+    except ImportError:
+        return make_item(cfg, spec, keep_x=False).raw
+
+
+def iter_raw_parallel(cfg: CacheConfig, specs: List[Item], workers: int = 0):
+    """Yield (index, stored bits) of every spec, in order, generated by a pool
+    of forked worker processes (the same values as make_item).  Call it before
+    anything initialises a GPU in this process: the workers are forked."""
+    import multiprocessing as mp
+    import os
+    if workers <= 0:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    workers = min(workers, max(1, len(specs)))
+    if workers == 1:
+        for i, s in enumerate(specs):
+            yield i, make_item(cfg, s, keep_x=False).raw
+        return
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        for i, raw in enumerate(pool.imap(_raw_worker, [(cfg, s) for s in specs], chunksize=1)):
+            yield i, raw
 
 
 def gaussian_groups(n_groups: int, group: int = 64, seed: int = 0) -> np.ndarray:
