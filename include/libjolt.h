@@ -23,7 +23,12 @@
  *     64 KiB, grown as the plan's readback needs) from its first plan on.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *     stream-ordered and asynchronous, except jolt_plan(), which synchronises
- *     `stream` once to read the energy tables back.  jolt_plan() also forks
+ *     `stream` once to read the energy tables back.  Two cases add
+ *     synchronisations: exact token mode with T > 272, whose T x T
+ *     eigenproblem runs block Jacobi with one convergence readback per sweep,
+ *     and a sketch whose order 141..272 eigenproblem has numerically repeated
+ *     eigenvalues, whose group of up to 16 items is then planned again with
+ *     block Jacobi before a second readback.  jolt_plan() also forks
  *     the feature Gram onto a second stream owned by the handle (created on
  *     the first plan, default priority) and joins it back to `stream` before
  *     the work that reads it; everything it launched has finished when it
@@ -225,14 +230,16 @@ jolt_status jolt_rademacher(jolt_handle h, uint64_t seed, uint32_t item_id, uint
                             uint64_t first, int64_t count, float *out, void *stream);
 
 /* The plan's symmetric eigensolver on caller matrices (device).  count
- * matrices of order n <= 142: matrix i starts at a + i * mat_stride, row
+ * matrices of order n <= 272: matrix i starts at a + i * mat_stride, row
  * stride lda, and only its symmetric part (A + A^T) / 2 is used.  Matrix i's
  * eigenvalues go to lam + i n in descending order and its eigenvectors to the
  * columns of vec + i n n (row stride n), each column's entry of largest
  * magnitude (first such row) positive.  info (count int32, device) receives
- * 0 when the Householder-tridiagonal solver (n <= 140) produced the result,
- * the sweep count when the Jacobi solver did (n > 140, force_jacobi != 0, or
- * numerically repeated eigenvalues), -1 when Jacobi hit its sweep cap.
+ * 0 when the Householder-tridiagonal solver produced the result, the sweep
+ * count when the Jacobi solver did (force_jacobi != 0, for n <= 142, or
+ * numerically repeated eigenvalues at n <= 140), -1 when Jacobi
+ * hit its sweep cap, -3 when, for n > 140, the tridiagonal solver could not
+ * make the eigenvectors orthonormal (results written as they stand).
  * workspace (device, 16-byte aligned) of at least
  * jolt_eigh_workspace_size(n, count, force_jacobi) bytes carries the
  * tridiagonal solver's intermediates from launch to launch; calls that

@@ -27,6 +27,7 @@ struct jolt_handle_s {
     jolt::DualTables dual;
     uint8_t *readback = nullptr;    // pinned host memory for the plan's one readback
     size_t readback_cap = 0;
+    float *sweep = nullptr;         // pinned host memory for block Jacobi's per-sweep norms
 };
 
 namespace jolt {
@@ -67,6 +68,18 @@ hipError_t readback_buffer(jolt_handle h, size_t bytes, uint8_t **buf) {
         h->readback_cap = cap;
     }
     *buf = h->readback;
+    return hipSuccess;
+}
+
+hipError_t sweep_buffer(jolt_handle h, float **buf) {
+    if (!h->sweep)
+        if (hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&h->sweep), 2 * kMaxBatch * sizeof(float),
+                                         hipHostMallocDefault);
+            e != hipSuccess) {
+            h->sweep = nullptr;
+            return e;
+        }
+    *buf = h->sweep;
     return hipSuccess;
 }
 
@@ -156,6 +169,7 @@ extern "C" void jolt_destroy(jolt_handle h) {
         (void)hipStreamDestroy(h->side);
     }
     if (h->readback) (void)hipHostFree(h->readback);
+    if (h->sweep) (void)hipHostFree(h->sweep);
     delete h;
 }
 
@@ -472,7 +486,7 @@ extern "C" jolt_status jolt_rademacher(jolt_handle h, uint64_t seed, uint32_t it
 }
 
 extern "C" size_t jolt_eigh_workspace_size(int32_t n, int32_t count, int32_t force_jacobi) {
-    if (n < 1 || n > kTriMaxN || count < 1 || force_jacobi) return 0;
+    if (n < 1 || n > kWideMaxN || count < 1 || (force_jacobi && n <= kJacobiMaxN)) return 0;
     return eig_tri_ws_bytes(n) * (size_t)std::min(count, 64);
 }
 
@@ -481,8 +495,9 @@ extern "C" jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const 
                                  void *workspace, size_t workspace_bytes, void *stream) {
     if (!h) return JOLT_E_INVALID;
     clear_err(h);
-    if (n < 1 || n > kJacobiMaxN || count < 0 || lda < n || mat_stride < (int64_t)(n - 1) * lda + n)
+    if (n < 1 || n > kWideMaxN || count < 0 || lda < n || mat_stride < (int64_t)(n - 1) * lda + n)
         return fail(h, JOLT_E_INVALID, "eigh: bad sizes (n=%d count=%d lda=%d)", n, count, lda);
+    if (force_jacobi && n > kJacobiMaxN) return fail(h, JOLT_E_INVALID, "eigh: the Jacobi solver takes n <= 142");
     if (count > 0 && (!a || !vec || !lam || !info)) return fail(h, JOLT_E_INVALID, "eigh: null pointer");
     const size_t need = jolt_eigh_workspace_size(n, count, force_jacobi);
     if (workspace_bytes < need || (need && (!workspace || reinterpret_cast<uintptr_t>(workspace) % 16)))
@@ -510,7 +525,7 @@ extern "C" jolt_status jolt_eigh(jolt_handle h, int32_t n, int32_t count, const 
             ++b.n;
         }
         hipError_t e = tri ? launch_eig_tridiag(b, n, st) : launch_jacobi_lds(b, n, 30, st);
-        if (e == hipSuccess && tri) e = launch_jacobi_lds(b, n, 30, st, 1);
+        if (e == hipSuccess && tri && n <= kTriMaxN) e = launch_jacobi_lds(b, n, 30, st, 1);
         if (e != hipSuccess) return hip_fail(h, e, "eigh");
     }
     return JOLT_OK;

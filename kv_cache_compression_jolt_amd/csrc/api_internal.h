@@ -34,6 +34,9 @@ DualTables &dual_tables(jolt_handle h);
 // The handle's pinned host buffer of at least `bytes` (grown on demand) for a
 // device-to-host copy that the caller synchronises before it returns.
 hipError_t readback_buffer(jolt_handle h, size_t bytes, uint8_t **buf);
+// The handle's small pinned host buffer (2 kMaxBatch floats) for the block
+// Jacobi convergence norms, read once per sweep.
+hipError_t sweep_buffer(jolt_handle h, float **buf);
 // A second stream on the handle's device (default priority, created on first
 // use and destroyed with the handle) and two events, for work forked off the
 // caller's stream and joined back to it within one call.

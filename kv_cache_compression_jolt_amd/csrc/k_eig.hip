@@ -57,12 +57,13 @@ constexpr int kPanelStride = 34;
 struct TriWs {
     float *a, *zt, *tb, *d, *e, *tau, *lam;
     int *flag;
+    float *ex;          // wide solver only: E of the polish steps (n x np)
     int np;
 };
 __device__ __forceinline__ int tri_blocks(int n) { return (max(n - 2, 0) + 31) >> 5; }
 __device__ __forceinline__ TriWs tri_ws(float *base, int n) {
     TriWs w;
-    w.np = (n + 3) & ~3;
+    w.np = n > kTriMaxN ? (n + 15) & ~15 : (n + 3) & ~3;
     const size_t nn = (size_t)n * w.np;
     w.a = base;
     w.zt = base + nn;
@@ -72,6 +73,7 @@ __device__ __forceinline__ TriWs tri_ws(float *base, int n) {
     w.tau = w.e + n;
     w.lam = w.tau + n;
     w.flag = reinterpret_cast<int *>(w.lam + n);
+    w.ex = w.lam + n + 4;
     return w;
 }
 
@@ -444,6 +446,228 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     if (tid == 0) *w.flag = 0;
 }
 
+// ---------------------------------------------------------------- 1 (wide). tridiagonalize, 140 < n <= 272
+// The same blocked reduction for matrices too large for LDS: the whole matrix
+// stays in the registers of a 512-thread workgroup (two waves per SIMD, so up
+// to 256 registers per lane) for the entire reduction.  Lane l32 of half h of
+// wave w (hw = 2 w + h) holds A(R_p, C_u), R_p = hw + 16 p (p < 17), C_u =
+// l32 + 32 u (u < 9).  Per panel the 32 panel columns go to LDS (Xp), the
+// steps run as in k_eig_tridiag with the matrix-vector products from the
+// registers, and the panel's rank-64 update A22 -= V W^T + W V^T is applied in
+// the registers.  Reflectors go straight to the workspace rows.
+constexpr int kWThreads = 512;
+constexpr int kWRows = 17;
+constexpr int kWCols = 9;
+constexpr int kXpPitch = 33;
+constexpr size_t kWTriLds = ((size_t)kWideMaxN * (kXpPitch + 2 * kPanelStride) + 6 * kWideMaxN + 64) * 4;
+
+__global__ __launch_bounds__(kWThreads) void k_eig_tridiag_w(JacBatch batch) {
+    extern __shared__ float sm[];
+    const JacItem &it = batch.it[blockIdx.x];
+    const int n = it.n;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hw = 2 * wid + (lane >> 5);
+    constexpr int PS = kPanelStride;
+    float *Xp = sm;                              // panel columns: Xp[r * 33 + m] = A(r, p0 + m)
+    float *Vp = Xp + kWideMaxN * kXpPitch;       // the panel's V and W
+    float *Wp = Vp + kWideMaxN * PS;
+    float *sx0 = Wp + kWideMaxN * PS, *sx1 = sx0 + kWideMaxN, *sp = sx1 + kWideMaxN;
+    float *sd = sp + kWideMaxN, *se = sd + kWideMaxN, *stau = se + kWideMaxN, *sy = stau + kWideMaxN;
+    const TriWs w = tri_ws(it.tw, n);
+
+    // (A + A^T) / 2 into the registers
+    float areg[kWRows][kWCols];
+#pragma unroll
+    for (int pp = 0; pp < kWRows; ++pp)
+#pragma unroll
+        for (int u = 0; u < kWCols; ++u) {
+            const int R = hw + 16 * pp, C = l32 + 32 * u;
+            const bool ok = R < n && C < n;
+            const int Rc = min(R, n - 1), Cc = min(C, n - 1);
+            const float x = it.a[(size_t)Rc * it.lda + Cc], y = it.a[(size_t)Cc * it.lda + Rc];
+            areg[pp][u] = ok ? 0.5f * (x + y) : 0.f;
+        }
+
+    float *sxa = sx0, *sxb = sx1;
+    for (int p0 = 0; p0 + 2 < n; p0 += 32) {
+        const int nb = min(32, n - 2 - p0);
+        const int up = p0 >> 5;
+        __syncthreads();
+        // the panel's columns from the registers (column block up of every lane)
+#pragma unroll
+        for (int pp = 0; pp < kWRows; ++pp) {
+            const int R = hw + 16 * pp;
+            float v = 0.f;
+#pragma unroll
+            for (int u = 0; u < kWCols; ++u) v = u == up ? areg[pp][u] : v;
+            if (R < n && R >= p0) Xp[R * kXpPitch + l32] = v;
+        }
+        for (int e = tid; e < (n - p0) * 32; e += kWThreads) {
+            const int r = p0 + (e >> 5), m = e & 31;
+            Vp[r * PS + m] = 0.f;
+            Wp[r * PS + m] = 0.f;
+        }
+        if (tid < 64) sy[tid] = 0.f;
+        __syncthreads();
+        for (int r = p0 + tid; r < n; r += kWThreads) sxa[r] = Xp[r * kXpPitch];
+        __syncthreads();
+        for (int jj = 0; jj < nb; ++jj) {
+            const int j = p0 + jj, s = n - j - 1;
+            float part = 0.f;
+#pragma unroll
+            for (int t = 0; t < 5; ++t) {
+                const int c = 1 + lane + 64 * t;
+                const float x = ld_or_zero(sxa, j + 1 + min(c, s - 1), c < s);
+                part = fmaf(x, x, part);
+            }
+            const float xn2 = wave_sum(part);
+            const float x0 = sxa[j + 1];
+            float beta = x0, v0 = 0.f, tau = 0.f;
+            if (xn2 > 0.f) {
+                const float alpha = sqrtf(x0 * x0 + xn2);
+                beta = x0 >= 0.f ? -alpha : alpha;
+                v0 = x0 - beta;
+                tau = 2.f * __builtin_amdgcn_rcpf(v0 * v0 + xn2);
+            }
+            if (tid == 0) {
+                sd[j] = sxa[j];
+                se[j] = beta;
+                stau[j] = tau;
+            }
+            for (int c = tid; c < s; c += kWThreads) {
+                const float vc = c == 0 ? v0 : sxa[j + 1 + c];
+                Vp[(j + 1 + c) * PS + jj] = vc;
+                w.a[(size_t)j * w.np + j + 1 + c] = vc;
+            }
+            float vr[kWCols];
+#pragma unroll
+            for (int u = 0; u < kWCols; ++u) {
+                const int C = l32 + 32 * u;
+                vr[u] = C == j + 1 ? v0 : ld_or_zero(sxa, min(C, n - 1), C > j + 1 && C < n);
+            }
+            // sp = A22 v from the registers: 9 products per row, then the sum over
+            // the 32 lanes of the half (rows of 16 by DPP, the lower row's total
+            // from its lane 15 into the upper row)
+#pragma unroll
+            for (int pp = 0; pp < kWRows; ++pp) {
+                float t = 0.f;
+#pragma unroll
+                for (int u = 0; u < kWCols; ++u) t = fmaf(areg[pp][u], vr[u], t);
+                t = group16_sum(t);
+                t += dpp_move<kDppRowBcast15>(t);
+                const int R = hw + 16 * pp;
+                if (l32 == 16 && R > j && R < n) sp[R - j - 1] = t;
+            }
+            // sy[m] = (W^T v)_m, sy[32 + m] = (V^T v)_m: half-wave hw takes outputs
+            // hw + 16 oo of the 2 jj
+#pragma unroll
+            for (int oo = 0; oo < 4; ++oo) {
+                const int o = hw + 16 * oo;
+                if (o < 2 * jj) {
+                    const float *vec = o < jj ? Wp + o : Vp + (o - jj);
+                    float acc = 0.f;
+#pragma unroll
+                    for (int u = 0; u < kWCols; ++u) {
+                        const int C = l32 + 32 * u;
+                        acc = fmaf(ld_or_zero(vec, min(C, n - 1) * PS, C > j && C < n), vr[u], acc);
+                    }
+                    acc = group16_sum(acc);
+                    acc += dpp_move<kDppRowBcast15>(acc);
+                    if (l32 == 16) sy[o < jj ? o : 32 + (o - jj)] = acc;
+                }
+            }
+            __syncthreads();
+            float kp = 0.f;
+#pragma unroll
+            for (int t = 0; t < 5; ++t) {
+                const int c = lane + 64 * t, cc = min(c, s - 1);
+                const float vc = c == 0 ? v0 : sxa[j + 1 + cc];
+                kp = fmaf(ld_or_zero(sp, cc, c < s), vc, kp);
+            }
+            kp = wave_sum(kp);
+            const bool next = jj + 1 < nb;
+            // w and the next column, 4 lanes per row, 128 rows per pass
+            for (int cb = 0; cb < s; cb += kWThreads / 4) {
+                if (cb + 16 * wid >= s) break;
+                const int l4 = tid & 3, c = cb + (tid >> 2), r = j + 1 + c, rc = min(r, n - 1);
+                const bool live = c < s;
+                float cw = 0.f, cx = 0.f, cw1 = 0.f, yy = 0.f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int m = l4 + 4 * t;
+                    const bool on = m < jj;
+                    const float y1 = sy[m], y2 = sy[32 + m];
+                    const float bv = ld_or_zero(Vp, (j + 1) * PS + m, on);
+                    const float bw = ld_or_zero(Wp, (j + 1) * PS + m, on);
+                    const float rv = Vp[rc * PS + m], rw = Wp[rc * PS + m];
+                    yy = fmaf(y1, y2, yy);
+                    cw1 = fmaf(bv, y1, fmaf(bw, y2, cw1));
+                    cw = fmaf(rv, y1, fmaf(rw, y2, cw));
+                    cx = fmaf(rv, bw, fmaf(rw, bv, cx));
+                }
+                cw = group4_sum(cw);
+                cx = group4_sum(cx);
+                cw1 = group4_sum(cw1);
+                yy = group4_sum(yy);
+                const float hk = 0.5f * tau * (tau * (kp - 2.f * yy));
+                if (live && l4 == 0) {
+                    const float vc = c == 0 ? v0 : sxa[r];
+                    const float wv = tau * (sp[c] - cw) - hk * vc;
+                    Wp[r * PS + jj] = wv;
+                    if (next) {
+                        const float w0 = tau * (sp[0] - cw1) - hk * v0;
+                        sxb[r] = Xp[r * kXpPitch + jj + 1] - cx - fmaf(vc, w0, wv * v0);
+                    }
+                }
+            }
+            float *t = sxa;
+            sxa = sxb;
+            sxb = t;
+            __syncthreads();
+        }
+        // A22 -= V W^T + W V^T in the registers, rows and columns >= q0
+        const int q0 = p0 + nb;
+        for (int m = 0; m < nb; ++m) {
+            float cv[kWCols], cwv[kWCols];
+#pragma unroll
+            for (int u = 0; u < kWCols; ++u) {
+                const int C = l32 + 32 * u;
+                const bool ok = C >= q0 && C < n;
+                cv[u] = ld_or_zero(Vp, min(C, n - 1) * PS + m, ok);
+                cwv[u] = ld_or_zero(Wp, min(C, n - 1) * PS + m, ok);
+            }
+#pragma unroll
+            for (int pp = 0; pp < kWRows; ++pp) {
+                if (16 * pp + 15 < q0) continue;
+                const int R = hw + 16 * pp;
+                const bool ok = R >= q0 && R < n;
+                const float rv = ld_or_zero(Vp, min(R, n - 1) * PS + m, ok);
+                const float rw = ld_or_zero(Wp, min(R, n - 1) * PS + m, ok);
+#pragma unroll
+                for (int u = 0; u < kWCols; ++u) areg[pp][u] = fmaf(-rv, cwv[u], fmaf(-rw, cv[u], areg[pp][u]));
+            }
+        }
+    }
+    __syncthreads();
+    // the trailing 2 x 2 block from the registers
+#pragma unroll
+    for (int pp = 0; pp < kWRows; ++pp)
+#pragma unroll
+        for (int u = 0; u < kWCols; ++u) {
+            const int R = hw + 16 * pp, C = l32 + 32 * u;
+            if (R == n - 2 && C == n - 2) sd[n - 2] = areg[pp][u];
+            if (R == n - 2 && C == n - 1) se[n - 2] = areg[pp][u];
+            if (R == n - 1 && C == n - 1) sd[n - 1] = areg[pp][u];
+        }
+    __syncthreads();
+    for (int i = tid; i < n; i += kWThreads) {
+        w.d[i] = sd[i];
+        w.e[i] = i + 1 < n ? se[i] : 0.f;
+        w.tau[i] = i + 2 < n ? stau[i] : 0.f;
+    }
+    if (tid == 0) *w.flag = 0;
+}
+
 // ---------------------------------------------------------------- 2 + 3. eigenpairs of T
 // Every eigenpair of the tridiagonal T = (d, e) that k_eig_tridiag left in the
 // workspace, a group of 16 lanes per eigenvalue k (the k-th smallest), four
@@ -466,20 +690,26 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
 constexpr int kVecWaves = 1;                          // one-wave workgroups spread evenly
 constexpr int kVecGroup = 16;                           // lanes per eigenvalue
 constexpr int kVecPerWave = 64 / kVecGroup;
-constexpr int kVecPad = kTriMaxN + 24;                  // room for the batch reads past the end
-constexpr int kYPitch = kTriMaxN + 1;                   // odd: lanes reading a column meet distinct banks
-// LDS of one k_eig_trivec workgroup in floats: the eigenpair role's arrays, or
-// the T role's reflector block and G / T buffer
-constexpr int kVecLdsEig = 4 * kVecPad + 4 * kTriMaxN + kVecPerWave * 3 * kTriMaxN;
-constexpr int kVecLdsWy = 32 * kYPitch + 32 * 33 + 32;
-constexpr int kVecLds = kVecLdsEig > kVecLdsWy ? kVecLdsEig : kVecLdsWy;
+// sizes for matrices of order <= NMAX (kTriMaxN or kWideMaxN)
+template <int NMAX>
+struct VecDims {
+    static constexpr int kVecPad = NMAX + 24;           // room for the batch reads past the end
+    static constexpr int kYPitch = NMAX + 1;            // odd: lanes reading a column meet distinct banks
+    // LDS of one k_eig_trivec workgroup in floats: the eigenpair role's arrays,
+    // or the T role's reflector block and G / T buffer
+    static constexpr int kLdsEig = 4 * kVecPad + 4 * NMAX + kVecPerWave * 3 * NMAX;
+    static constexpr int kLdsWy = 32 * kYPitch + 32 * 33 + 32;
+    static constexpr int kLds = kLdsEig > kLdsWy ? kLdsEig : kLdsWy;
+};
 
 // T of reflector block b for k_eig_backtr, one wave (the T role of
 // k_eig_trivec): G = Y^T Y of the block's 32 reflectors (Y(r, i) = v_{b0+i}(r),
 // zero for r <= b0 + i), then (diag(1 / tau) + strict_upper(G)) T = I column
 // by column (wblock_t_full).  A partial last block is padded with zero
 // reflectors of tau = 0, whose rows and columns of T come out zero.
+template <int NMAX>
 __device__ void wy_block(const TriWs &w, int n, int b, float *lds, int lane) {
+    constexpr int kYPitch = VecDims<NMAX>::kYPitch;
     const int mref = max(n - 2, 0), b0 = 32 * b, nbk = min(32, mref - b0);
     float *Ys = lds;                    // Ys[i * kYPitch + r] = Y(r, i)
     float *D = Ys + 32 * kYPitch;       // G(i, c), i < c, then T(i, c), i <= c, at D[c * 33 + i]
@@ -514,15 +744,17 @@ __device__ void wy_block(const TriWs &w, int n, int b, float *lds, int lane) {
     }
 }
 
+template <int NMAX>
 __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch, int eig_blocks) {
-    __shared__ __attribute__((aligned(16))) float lds[kVecLds];
+    constexpr int kTriMaxN = NMAX, kVecPad = VecDims<NMAX>::kVecPad;
+    __shared__ __attribute__((aligned(16))) float lds[VecDims<NMAX>::kLds];
     const JacItem &it = batch.it[blockIdx.y];
     const int n = it.n;
     const TriWs w = tri_ws(it.tw, n);
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     if ((int)blockIdx.x >= eig_blocks) {
         const int b = blockIdx.x - eig_blocks;
-        if (b < tri_blocks(n)) wy_block(w, n, b, lds, lane);
+        if (b < tri_blocks(n)) wy_block<NMAX>(w, n, b, lds, lane);
         return;
     }
     constexpr int kPerBlock = kVecWaves * kVecPerWave;
@@ -852,6 +1084,264 @@ __global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr(JacBatch batch, in
     }
 }
 
+// The back-transform for the wide solver: the reflectors of one block at a
+// time go through LDS (all of them would not fit), with the block's T.
+__global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr_w(JacBatch batch, int ldy) {
+    extern __shared__ float sm[];
+    const JacItem &it = batch.it[blockIdx.y];
+    const int n = it.n, c0 = 32 * blockIdx.x;
+    if (c0 >= n) return;
+    const TriWs w = tri_ws(it.tw, n);
+    if (*w.flag) return;                                // k_eig_polish_w reports it
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m32 = lane & 31, kh = lane >> 5;
+    const int mref = max(n - 2, 0), nblk = tri_blocks(n), nt = (n + 31) >> 5;
+    float *Ys = sm;                      // Ys[i * ldy + r] = v_{b0 + i}(r), block b only
+    float *Ts = Ys + 32 * ldy;           // T_b(i, k) at Ts[i * 33 + k]
+    float *Zc = Ts + kTile;              // Z(r, c0 + m) at Zc[r * 33 + m]
+    float *Pt = Zc + n * 33;             // partial S of wave w
+    float *Mt = Pt + kBtWaves * kTile;   // M(k, m) at Mt[k * 33 + m]
+    constexpr int NT = 64 * kBtWaves;
+    const int c4 = w.np >> 2, ncol = min(32, n - c0);
+    for (int e = tid; e < (32 - ncol) * n; e += NT) {
+        const int m = ncol + e / n, r = e - (e / n) * n;
+        Zc[r * 33 + m] = 0.f;
+    }
+    load_rows4<NT, 8>(w.zt + (size_t)c0 * w.np, w.np, ncol, c4, tid, [&](int m, int c, float4 v) {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * c + i < n) Zc[(4 * c + i) * 33 + m] = vv[i];
+    });
+    for (int b = nblk - 1; b >= 0; --b) {
+        const int b0 = 32 * b, nbk = min(32, mref - b0);
+        __syncthreads();
+        load_rows4<NT, 8>(w.a + (size_t)b0 * w.np, w.np, nbk, c4, tid, [&](int r, int c, float4 v) {
+            float *d = Ys + r * ldy + 4 * c;
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        });
+        load_rows4<NT, 8>(w.tb + 1024 * b, 32, 32, 8, tid, [&](int r, int c, float4 v) {
+            float *d = Ts + r * 33 + 4 * c;
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        });
+        __syncthreads();
+        // Y(r, i): reflector b0 + i at row r, zero unless i < nbk and b0 + i < r < n
+        auto Y = [&](int r, int i) {
+            return ld_or_zero(Ys, min(i, nbk - 1) * ldy + min(r, n - 1), i < nbk && r > b0 + i && r < n);
+        };
+        {
+            const int rows = n - 1 - b0, per = ((rows + 8 * kBtWaves - 1) / (8 * kBtWaves)) * 8;
+            const int r0 = b0 + 1 + wid * per, r1 = min(n, r0 + per);
+            f32x16 acc = {};
+            for (int k0 = r0; k0 < r1; k0 += 8) {
+                float ya[4], zb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = k0 + 2 * u + kh;
+                    const bool ok = r < r1;
+                    ya[u] = ok ? Y(r, m32) : 0.f;
+                    zb[u] = ld_or_zero(Zc, min(r, n - 1) * 33 + m32, ok);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ya[u], zb[u], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) Pt[wid * kTile + frag_row(lane, q) * 33 + m32] = acc[q];
+        }
+        __syncthreads();
+        if (wid == 0) {
+            f32x16 acc = {};
+#pragma unroll
+            for (int k0 = 0; k0 < 32; k0 += 8) {
+                float ta[4], sb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int k = k0 + 2 * u + kh;
+                    ta[u] = Ts[m32 * 33 + k];
+                    float sv = 0.f;
+#pragma unroll
+                    for (int v = 0; v < kBtWaves; ++v) sv += Pt[v * kTile + k * 33 + m32];
+                    sb[u] = sv;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ta[u], sb[u], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) Mt[frag_row(lane, q) * 33 + m32] = acc[q];
+        }
+        __syncthreads();
+        for (int rt = b + wid; rt < nt; rt += kBtWaves) {
+            f32x16 acc;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * rt + frag_row(lane, q);
+                acc[q] = ld_or_zero(Zc, min(row, n - 1) * 33 + m32, row < n);
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < 32; k0 += 8) {
+                float ya[4], mb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int k = k0 + 2 * u + kh;
+                    ya[u] = -Y(32 * rt + m32, k);
+                    mb[u] = Mt[k * 33 + m32];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ya[u], mb[u], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * rt + frag_row(lane, q);
+                if (row < n) Zc[row * 33 + m32] = acc[q];
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < ncol * n; e += NT) {
+        const int m = e / n, r = e - m * n;
+        w.zt[(size_t)(c0 + m) * w.np + r] = Zc[r * 33 + m];
+    }
+}
+
+// C(m, c) = sum_k a[m lda + k] b[c ldb + k] for tile (tm, tn), both operands
+// rows in k padded with zeros to a multiple of 8 past n, 16-byte aligned rows:
+// four K steps per pair of float4 loads (lane half kh takes k0 + 4 kh + u on
+// both operands, so the hardware's K pairing cancels)
+__device__ __forceinline__ f32x16 mfma_tile_rr(const float *a, int lda, const float *b, int ldb, int n, int tm,
+                                               int tn, int lane) {
+    f32x16 acc = {};
+    const int kh = lane >> 5;
+    const int mc = min(tm * 32 + (lane & 31), n - 1), cc = min(tn * 32 + (lane & 31), n - 1);
+    const float *ap = a + (size_t)mc * lda + 4 * kh, *bp = b + (size_t)cc * ldb + 4 * kh;
+    for (int k0 = 0; k0 < n; k0 += 8) {
+        const float4 av = *reinterpret_cast<const float4 *>(ap + k0);
+        const float4 bv = *reinterpret_cast<const float4 *>(bp + k0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Newton-Schulz polish and output for the wide solver, one workgroup per
+// matrix, on the workspace: Z^T (rows = vectors) in zt, E = (I - Z^T Z) / 2 in
+// ex (both triangles, zero padded), the next Z^T in the reflector rows (no
+// longer needed), the two swapping roles every step.  The same step rule as
+// k_eig_polish; a matrix it cannot make orthonormal reports kEigWideFail in
+// sweeps_out (its output is written as it stands).
+__global__ __launch_bounds__(kThreads) void k_eig_polish_w(JacBatch batch) {
+    __shared__ float sred[kWaves];
+    const JacItem &it = batch.it[blockIdx.x];
+    const int n = it.n;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const TriWs w = tri_ws(it.tw, n);
+    if (*w.flag) {
+        if (tid == 0) *it.sweeps_out = kEigWideFail;
+        return;
+    }
+    const int np = w.np, nt = (n + 31) >> 5, ntiles = nt * nt, ntri = nt * (nt + 1) / 2;
+    float *Z = w.zt, *Z2 = w.a, *E = w.ex;
+    for (int e = tid; e < n * (np - n); e += kThreads) {
+        const int r = e / (np - n), c = n + e - r * (np - n);
+        E[(size_t)r * np + c] = 0.f;
+        Z2[(size_t)r * np + c] = 0.f;
+    }
+    bool failed = false;
+    for (int step = 0;; ++step) {
+        float dev = 0.f;
+        for (int t = wid; t < ntri; t += kWaves) {
+            int tt = t, tm = 0;
+            while (tt >= nt - tm) {
+                tt -= nt - tm;
+                ++tm;
+            }
+            const int tn = tm + tt, col = tn * 32 + (lane & 31);
+            const f32x16 g = mfma_tile_rr(Z, np, Z, np, n, tm, tn, lane);
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const int row = tm * 32 + frag_row(lane, jj);
+                if (row < n && col < n) {
+                    const float id = row == col ? 1.f : 0.f;
+                    const float gv = g[jj];
+                    dev = fmaxf(dev, fabsf(gv - id));
+                    if (!(gv == gv)) dev = FLT_MAX;
+                    const float ev = 0.5f * (id - gv);
+                    E[(size_t)row * np + col] = ev;
+                    E[(size_t)col * np + row] = ev;
+                }
+            }
+        }
+        dev = wave_max(dev);
+        if (lane == 0) sred[wid] = dev;
+        __syncthreads();
+        float devmax = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) devmax = fmaxf(devmax, sred[v]);
+        __syncthreads();
+        if (devmax <= 4e-6f) break;
+        if (step == 3 || !(devmax <= 0.3f)) {
+            failed = !(devmax <= 1e-4f);
+            break;
+        }
+        // Z2 = Z + E Z (E symmetric: the rows of Z^T (I + E))
+        for (int t = wid; t < ntiles; t += kWaves) {
+            const int tm = t / nt, tn = t % nt;
+            const int kh = lane >> 5, cc = min(tn * 32 + (lane & 31), n - 1), col = tn * 32 + (lane & 31);
+            const int mc = min(tm * 32 + (lane & 31), n - 1);
+            f32x16 acc;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = tm * 32 + frag_row(lane, q);
+                acc[q] = ld_or_zero(Z, min(row, n - 1) * np + cc, row < n && col < n);
+            }
+            const float *ap = E + (size_t)mc * np + 4 * kh;
+            for (int k0 = 0; k0 < n; k0 += 8) {
+                const float4 av = *reinterpret_cast<const float4 *>(ap + k0);
+                float bv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int k = k0 + 4 * kh + u;
+                    bv[u] = ld_or_zero(Z, min(k, n - 1) * np + cc, k < n);
+                }
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv[0], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv[1], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv[2], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv[3], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = tm * 32 + frag_row(lane, q);
+                if (row < n && col < n) Z2[(size_t)row * np + col] = acc[q];
+            }
+        }
+        __syncthreads();
+        float *t = Z;
+        Z = Z2;
+        Z2 = t;
+        if (devmax <= 1e-3f) break;
+    }
+    // output: eigenvalue k (ascending) -> column n - 1 - k, sign so that the
+    // entry of largest magnitude (first such row) is positive
+    for (int k = tid; k < n; k += kThreads) {
+        const float *zr = Z + (size_t)k * np;
+        int best = 0;
+        float bm = -1.f;
+        for (int r = 0; r < n; ++r) {
+            const float v = fabsf(zr[r]);
+            if (v > bm) {
+                bm = v;
+                best = r;
+            }
+        }
+        const float sg = zr[best] < 0.f ? -1.f : 1.f;
+        const int col = n - 1 - k;
+        it.lam[col] = w.lam[k];
+        for (int r = 0; r < n; ++r) it.vec[(size_t)r * it.ldv + col] = sg * zr[r];
+    }
+    if (tid == 0) *it.sweeps_out = failed ? kEigWideFail : 0;
+}
+
 // ---------------------------------------------------------------- 5 and output
 // Newton-Schulz polish and the output of one matrix per workgroup, V loaded
 // from the workspace.
@@ -987,9 +1477,50 @@ static TriLayout tri_layout(int maxN) {
     return L;
 }
 
+static hipError_t launch_eig_wide(const JacBatch &b, int maxN, hipStream_t s) {
+    static hipError_t state = hipErrorNotReady;
+    if (state == hipErrorNotReady) {
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_eig_tridiag_w));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_backtr_w));
+        state = e;
+    }
+    if (state != hipSuccess) return state;
+    {
+        KTimeScope kts("k_eig_tridiag", s);
+        hipLaunchKernelGGL(k_eig_tridiag_w, dim3(b.n), dim3(kWThreads), kWTriLds, s, b);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    const int nblk = (std::max(maxN - 2, 0) + 31) / 32;
+    {
+        KTimeScope kts("k_eig_trivec", s);
+        constexpr int per = kVecWaves * kVecPerWave;
+        const int eig_blocks = (maxN + per - 1) / per;
+        hipLaunchKernelGGL(k_eig_trivec<kWideMaxN>, dim3(eig_blocks + nblk, b.n), dim3(64 * kVecWaves), 0, s, b,
+                           eig_blocks);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    {
+        KTimeScope kts("k_eig_backtr", s);
+        const int ldy = eig_tri_np(maxN) + 1;
+        const size_t lds = ((size_t)32 * ldy + kTile + (size_t)maxN * 33 + (size_t)(kBtWaves + 1) * kTile) *
+                           sizeof(float);
+        hipLaunchKernelGGL(k_eig_backtr_w, dim3((maxN + 31) / 32, b.n), dim3(64 * kBtWaves), lds, s, b, ldy);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    KTimeScope kts("k_eig_polish", s);
+    hipLaunchKernelGGL(k_eig_polish_w, dim3(b.n), dim3(kThreads), 0, s, b);
+    return hipGetLastError();
+}
+
 hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    if (maxN > kTriMaxN) return hipErrorInvalidValue;
+    if (maxN > kWideMaxN) return hipErrorInvalidValue;
+    if (maxN > kTriMaxN) {
+        for (int i = 0; i < b.n; ++i)
+            if (!b.it[i].sweeps_out || !b.it[i].tw || b.it[i].n > maxN || b.it[i].n <= kTriMaxN)
+                return hipErrorInvalidValue;
+        return launch_eig_wide(b, maxN, s);
+    }
     for (int i = 0; i < b.n; ++i)
         if (!b.it[i].sweeps_out || !b.it[i].tw || b.it[i].n > maxN) return hipErrorInvalidValue;
     if (hipError_t e = allow_lds_tri(); e != hipSuccess) return e;
@@ -1004,7 +1535,8 @@ hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
         KTimeScope kts("k_eig_trivec", s);
         constexpr int per = kVecWaves * kVecPerWave;
         const int eig_blocks = (maxN + per - 1) / per;
-        hipLaunchKernelGGL(k_eig_trivec, dim3(eig_blocks + nblk, b.n), dim3(64 * kVecWaves), 0, s, b, eig_blocks);
+        hipLaunchKernelGGL(k_eig_trivec<kTriMaxN>, dim3(eig_blocks + nblk, b.n), dim3(64 * kVecWaves), 0, s, b,
+                           eig_blocks);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     {

@@ -135,10 +135,10 @@ void reserve_scratch(const jolt_config &cfg, const Dims &D, Bump &b, Scratch &s)
     s.sweeps = b.take(16);
     const int ne = token_eig_n(cfg, D);
     // the token and feature eigenproblems run at the same time on two streams
-    s.etri = ne <= kTriMaxN ? b.take(eig_tri_ws_bytes(ne)) : SIZE_MAX;
-    s.ftri = D.d <= kTriMaxN ? b.take(eig_tri_ws_bytes(D.d)) : SIZE_MAX;
+    s.etri = ne <= kWideMaxN ? b.take(eig_tri_ws_bytes(ne)) : SIZE_MAX;
+    s.ftri = D.d <= kWideMaxN ? b.take(eig_tri_ws_bytes(D.d)) : SIZE_MAX;
     s.eN = 0;
-    if (ne > kJacobiMaxN) {
+    if (ne > kJacobiMaxN) {     // block Jacobi: above kWideMaxN, and the wide solver's fallback
         const size_t N = (size_t)round_up(ne, 128), P = N / 128;
         s.eN = (int)N;
         s.eA = b.take(N * N * 4);
@@ -263,8 +263,9 @@ namespace {
 
 // ------------------------------------------------------------------ eigensolvers
 // Symmetric eigen-decompositions (descending, sign-normalised eigenvectors).
-// n <= 142: one workgroup per matrix, Jacobi in LDS (k_jacobi_lds).
-// n > 142: block Jacobi over 64-wide blocks (see k_plan.hip): every round the
+// n <= 272: the Householder-tridiagonal solver (k_eig.hip), n <= 140 with the
+// Jacobi kernel for the matrices it hands back.
+// n > 272: block Jacobi over 64-wide blocks (see k_plan.hip): every round the
 // pair sub-matrices (128 x 128) are diagonalised in LDS and the rotations are
 // applied to the whole matrix and to V with the fp32 GEMM; sweeps repeat until
 // off(A) <= 4e-6 ||A||_F (checked on the host once per sweep).
@@ -364,13 +365,17 @@ jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint
         }
         HIPCHK(launch_offnorm(eb, c.st), "eig offnorm");
         // stop at the tolerance, or once the off-diagonal norm stops falling
-        // (quadratic convergence has reached the fp32 rounding floor)
+        // (quadratic convergence has reached the fp32 rounding floor); every
+        // item's two norms come back in one synchronisation per sweep
+        float *nr = nullptr;
+        HIPCHK(sweep_buffer(c.h, &nr), "eig norms");
+        for (int i = 0; i < eb.n; ++i)
+            HIPCHK(hipMemcpyAsync(nr + 2 * i, eb.it[i].norms, 2 * sizeof(float), hipMemcpyDeviceToHost, c.st),
+                   "eig norms");
+        HIPCHK(hipStreamSynchronize(c.st), "eig norms");
         float worst = 0.f;
         for (int i = 0; i < eb.n; ++i) {
-            float nr[2];
-            HIPCHK(hipMemcpyAsync(nr, eb.it[i].norms, sizeof nr, hipMemcpyDeviceToHost, c.st), "eig norms");
-            HIPCHK(hipStreamSynchronize(c.st), "eig norms");
-            const float rel2 = nr[1] > 0.f ? nr[0] / nr[1] : 0.f;
+            const float rel2 = nr[2 * i + 1] > 0.f ? nr[2 * i] / nr[2 * i + 1] : 0.f;
             worst = std::max(worst, rel2);
         }
         if (getenv("JOLT_DEBUG")) fprintf(stderr, "libjolt: block Jacobi N=%d sweep %d off %.3e\n", N, sweep, sqrtf(worst));
@@ -386,12 +391,14 @@ jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint
     return JOLT_OK;
 }
 
-jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr, int max_sweeps, bool *noconv) {
-    JacBatch jb{}, tb{};
-    int maxN = 0, maxT = 0;
+jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr, int max_sweeps, bool *noconv,
+                    bool wide_ok) {
+    JacBatch jb{}, tb{}, wb{};
+    int maxN = 0, maxT = 0, maxW = 0;
     std::vector<std::vector<EigReq>> large;
     std::vector<int> largeN;
-    // tridiagonal solver first, Jacobi for what it hands back
+    // tridiagonal solver first, Jacobi for what it hands back (n <= kTriMaxN);
+    // the wide tridiagonal solver for kTriMaxN < n <= kWideMaxN
     auto flush_tri = [&]() -> jolt_status {
         HIPCHK(launch_eig_tridiag(tb, maxT, c.st), "eig (tridiagonal)");
         HIPCHK(launch_jacobi_lds(tb, maxT, max_sweeps, c.st, 1), "eig (Jacobi retry)");
@@ -399,8 +406,22 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
         maxT = 0;
         return JOLT_OK;
     };
+    auto flush_wide = [&]() -> jolt_status {
+        HIPCHK(launch_eig_tridiag(wb, maxW, c.st), "eig (wide tridiagonal)");
+        wb.n = 0;
+        maxW = 0;
+        return JOLT_OK;
+    };
     for (const EigReq &r : reqs) {
-        if (r.n <= kTriMaxN && r.sw && r.tw) {
+        if (wide_ok && r.n <= kWideMaxN && r.n > kTriMaxN && r.sw && r.tw) {
+            JacItem &j = wb.it[wb.n++];
+            j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
+            j.raw = 0;
+            j.tw = r.tw;
+            maxW = std::max(maxW, r.n);
+            if (wb.n == 64)
+                if (jolt_status s = flush_wide()) return s;
+        } else if (r.n <= kTriMaxN && r.sw && r.tw) {
             JacItem &j = tb.it[tb.n++];
             j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
             j.raw = 0;
@@ -429,6 +450,8 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
     HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
     if (tb.n)
         if (jolt_status s = flush_tri()) return s;
+    if (wb.n)
+        if (jolt_status s = flush_wide()) return s;
     for (size_t g = 0; g < large.size(); ++g) {
         jolt_status s = eig_block(c, large[g], largeN[g], scr, max_sweeps, noconv);
         if (s) return s;
@@ -501,8 +524,9 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
     return JOLT_OK;
 }
 
-jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items, int i0,
-                      int nb, const void *const *x_dev, uint8_t *ws, bool *noconv) {
+jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items,
+                           int i0, int nb, const void *const *x_dev, uint8_t *ws, bool *noconv, bool wide_ok,
+                           hipStream_t *forked) {
     const int max_sweeps = cfg.max_sweeps > 0 ? cfg.max_sweeps : 30;
     const int d = c.d, dt = c.dtype;
     const bool bf = dt == JOLT_BF16;
@@ -514,7 +538,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         reserve_scratch(cfg, D[i], sb, S[i]);
     }
     uint8_t *scr = ws + pl.scratch;
-    if (i0 == 0) HIPCHK(launch_zero(ws + pl.readback, pl.readback_stride * pl.item.size(), c.st), "zero readback");
+    HIPCHK(launch_zero(ws + pl.item[i0].grid, pl.readback_stride * nb, c.st), "zero readback");
     auto P = [&](size_t off) { return scr + off; };
     auto F = [&](size_t off) { return reinterpret_cast<float *>(scr + off); };
     auto W = [&](int i, size_t off) { return ws + off; };
@@ -541,6 +565,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
     auto feature_gram = [&]() -> jolt_status {
         HIPCHK(hipEventRecord(fork, c.st), "fork");
         HIPCHK(hipStreamWaitEvent(side, fork, 0), "fork");
+        *forked = side;
         GramBatch gb{};
         ReduceBatch rb{};
         int maxP = 0;
@@ -562,7 +587,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
         }
         HIPCHK(launch_trace_batch(tb, side), "trace");
         const Ctx cs{c.h, side, c.dtype, c.d};
-        if (jolt_status es = eig_all(cs, feigs, scr, max_sweeps, noconv)) return es;
+        if (jolt_status es = eig_all(cs, feigs, scr, max_sweeps, noconv, wide_ok)) return es;
         HIPCHK(hipEventRecord(join, side), "join");
         return JOLT_OK;
     };
@@ -710,7 +735,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
                                       reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i],
                                       S[i].etri != SIZE_MAX ? F(S[i].etri) : nullptr});
             if ((s = feature_gram())) return s;
-            jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
+            jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv, wide_ok);
             if (es) return es;
         }
         // U_t^T = U~^T Q, P = U~^T B, lambda_t
@@ -752,7 +777,7 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
                                   reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i],
                                   S[i].etri != SIZE_MAX ? F(S[i].etri) : nullptr});
         if (jolt_status fs = feature_gram()) return fs;
-        jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv);
+        jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv, wide_ok);
         if (es) return es;
         // U_t^T rows = leading eigenvectors; P = U_t^T A (hi + lo split for bf16 caches)
         XtqBatch qb{};
@@ -832,6 +857,17 @@ jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl
     return JOLT_OK;
 }
 
+// One chunk of the plan.  Work forked onto the side stream reads the inputs and
+// writes the workspace, so an error after the fork waits for that stream
+// before returning: everything launched has finished when jolt_plan returns.
+jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items, int i0,
+                      int nb, const void *const *x_dev, uint8_t *ws, bool *noconv, bool wide_ok) {
+    hipStream_t forked = nullptr;
+    jolt_status s = run_chunk_body(c, cfg, pl, items, i0, nb, x_dev, ws, noconv, wide_ok, &forked);
+    if (s != JOLT_OK && forked) (void)hipStreamSynchronize(forked);
+    return s;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ parameter store (jolt_compress)
@@ -896,7 +932,7 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     const auto t_start = std::chrono::steady_clock::now();
     for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
         const int nb = std::min(kMaxBatch, n - c0);
-        s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv);
+        s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv, true);
         if (s) return s;
     }
     // energy tables, ||X||^2 and sweep counters back to the host (the one synchronisation)
@@ -908,6 +944,31 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     const auto t_launched = std::chrono::steady_clock::now();
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(h, e, "plan");
+    // a chunk whose wide eigensolves did not all finish (numerically repeated
+    // eigenvalues) is planned again with block Jacobi for them, then read back
+    // again: the only case with more than one synchronisation
+    {
+        bool again = false;
+        for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
+            const int nb = std::min(kMaxBatch, n - c0);
+            bool redo = false;
+            for (int i = c0; i < c0 + nb; ++i) {
+                int sw[2];
+                std::memcpy(sw, rb + (pl.item[i].sweeps - pl.readback), 8);
+                redo |= sw[0] == kEigWideFail || sw[1] == kEigWideFail;
+            }
+            if (!redo) continue;
+            if (debug) fprintf(stderr, "libjolt: items %d..%d planned again with block Jacobi\n", c0, c0 + nb - 1);
+            s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv, false);
+            if (s) return s;
+            again = true;
+        }
+        if (again) {
+            e = hipMemcpyAsync(rb, ws + pl.readback, rb_bytes, hipMemcpyDeviceToHost, st);
+            if (e == hipSuccess) e = hipStreamSynchronize(st);
+            if (e != hipSuccess) return hip_fail(h, e, "plan (block Jacobi fallback)");
+        }
+    }
     const auto t_synced = std::chrono::steady_clock::now();
     auto report = [&]() {
         if (!timing) return;

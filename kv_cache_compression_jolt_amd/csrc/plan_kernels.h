@@ -125,11 +125,20 @@ hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStr
 // matrix must be handed to the Jacobi kernel; every item needs its own tw of
 // eig_tri_ws_bytes(n), 16-byte aligned, which the three launches share)
 constexpr int kTriMaxN = 140;
+// the wide variant of the same four-launch solver (140 < n <= kWideMaxN): the
+// reduction keeps the matrix in registers and the polish works in the
+// workspace; it has no Jacobi hand-back (a matrix it cannot make orthonormal
+// reports -1 in sweeps_out, results written)
+constexpr int kWideMaxN = 272;
 constexpr int kEigRetry = -2;
+constexpr int kEigWideFail = -3;    // the wide solver's sweeps_out when it could not finish
+// row pitch (floats) of the solver's n x n workspace matrices
+inline int eig_tri_np(int n) { return n > kTriMaxN ? (n + 15) / 16 * 16 : (n + 3) / 4 * 4; }
 inline size_t eig_tri_ws_bytes(int n) {
     const size_t blocks = ((n > 2 ? n - 2 : 0) + 31) / 32;
-    const size_t np = ((size_t)n + 3) / 4 * 4;
-    return (((size_t)2 * n * np + 1024 * blocks + 4 * (size_t)n + 1) * 4 + 255) / 256 * 256;
+    const size_t np = (size_t)eig_tri_np(n);
+    const size_t ex = n > kTriMaxN ? (size_t)n * np : 0;      // the wide polish's E
+    return (((size_t)2 * n * np + 1024 * blocks + 4 * (size_t)n + 4 + ex) * 4 + 255) / 256 * 256;
 }
 hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s);
 

@@ -2,9 +2,10 @@
 oracle's fp64 Jacobi eigensolver.
 
 Both solvers the library carries are covered: the Householder-tridiagonal one
-(bisection + twisted-factorization vectors + one Newton-Schulz step) and the
-two-sided Jacobi one (forced, for n = 141..142, and as the hand-back for
-numerically repeated eigenvalues).  Matrices: the token Gram W = B B^T of the
+(bisection + twisted-factorization vectors + Newton-Schulz steps), for
+n <= 140 with the matrix in LDS and for 140 < n <= 272 with it in registers,
+and the two-sided Jacobi one (forced, up to n = 142, and as the hand-back for
+numerically repeated eigenvalues at n <= 140).  Matrices: the token Gram W = B B^T of the
 FlashJoLT sketch and the feature Gram of Mistral-7B-shaped synthetic items,
 random symmetric, rank-deficient, clustered and degenerate ones.
 
@@ -112,12 +113,17 @@ def test_random_symmetric_sizes(n):
 
 @pytest.mark.parametrize("n", [141, 142])
 def test_jacobi_sizes(n):
+    """The largest orders the Jacobi solver takes (forced), and the wide
+    tridiagonal solver on the same matrices."""
     rng = np.random.default_rng(n)
     B = rng.standard_normal((n, 2 * n))
     M = B @ B.T
-    V, lam, info = _run([M])
+    V, lam, info = _run([M], force_jacobi=True)
     assert info[0] > 0
-    _check(M, V[0], lam[0], "n=%d" % n)
+    _check(M, V[0], lam[0], "jacobi n=%d" % n)
+    V, lam, info = _run([M])
+    assert info[0] == 0
+    _check(M, V[0], lam[0], "wide n=%d" % n)
 
 
 def test_rank_deficient_and_graded():
@@ -142,3 +148,62 @@ def test_repeated_eigenvalues_fall_back_to_jacobi():
     assert np.all(info != -1), info
     for i, M in enumerate(mats):
         _check(M, V[i], lam[i], "repeated %d" % i)
+
+
+# ---------------------------------------------------------------- the wide solver (140 < n <= 272)
+@pytest.mark.parametrize("n", [143, 160, 200, 266, 272])
+def test_wide_random_sizes(n):
+    rng = np.random.default_rng(2000 + n)
+    mats = []
+    for _ in range(3):
+        B = rng.standard_normal((n, n))
+        mats.append(0.5 * (B + B.T))
+    V, lam, info = _run(mats)
+    assert np.all(info == 0), info
+    for i, M in enumerate(mats):
+        _check(M, V[i], lam[i], "wide random n=%d #%d" % (n, i))
+
+
+def test_wide_sketch_gram_k266():
+    """Token Gram W = B B^T of a k = 266 sketch (rank limit 256 + 10)."""
+    cfg = synth.config("moe_gqa_batch16_8k", L=2, H=4, T=1024, rank_t=150)
+    W, G = _sketch_grams(cfg, 2)
+    assert W[0].shape == (266, 266)
+    V, lam, info = _run(W)
+    assert np.all(info == 0), info
+    for i, M in enumerate(W):
+        _check(M, V[i], lam[i], "wide token W %d" % i)
+
+
+def test_wide_structured():
+    rng = np.random.default_rng(17)
+    n = 266
+    mats = []
+    G = rng.standard_normal((n, 5))
+    mats.append(G @ G.T)                                          # rank 5
+    U = np.linalg.qr(rng.standard_normal((n, n)))[0]
+    mats.append(U @ np.diag(0.9 ** np.arange(n)) @ U.T)          # graded spectrum
+    mats.append(U @ np.diag(np.r_[np.linspace(100, 10, 40), 1 + 1e-3 * rng.standard_normal(n - 40)]) @ U.T)
+    V, lam, info = _run(mats)
+    # the rank-deficient matrix (261 zero eigenvalues) and the tight cluster are
+    # flagged (jolt_plan re-plans such items with block Jacobi); the rest pass
+    assert info[1] == 0 and np.all((info == 0) | (info == -3)), info
+    for i, M in enumerate(mats):
+        if info[i] == 0:
+            _check(M, V[i], lam[i], "wide structured %d" % i)
+
+
+def test_wide_repeated_eigenvalues_flagged_or_exact():
+    """Exactly repeated eigenvalues: the wide solver has no Jacobi hand-back, so
+    each matrix is either solved to the usual tolerances (info 0) or reported
+    with info -3."""
+    rng = np.random.default_rng(5)
+    n = 200
+    U = np.linalg.qr(rng.standard_normal((n, n)))[0]
+    ev = np.r_[[10.0] * 5, [1.0] * 10, np.linspace(0.5, 0.1, n - 15)]
+    mats = [U @ np.diag(ev) @ U.T, np.eye(n), np.diag(np.r_[[3.0] * 100, [1.0] * 100])]
+    V, lam, info = _run(mats)
+    assert np.all((info == 0) | (info == -3)), info
+    for i, M in enumerate(mats):
+        if info[i] == 0:
+            _check(M, V[i], lam[i], "wide repeated %d" % i)
