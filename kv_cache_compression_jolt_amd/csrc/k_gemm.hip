@@ -100,7 +100,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmBatch batch, int maxSplit) {
 // the 32 x 32 tile grid, whose MFMA operands are both rows of the staged chunk.
 constexpr int kSgKC = 64, kSgPitch = kSgKC + 1;
 
+// KMAX: the largest order of the launch (192, or kSymGramWideK: then up to 6
+// tiles per wave).
+template <int KMAX>
 __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
+    constexpr int TPW = ((KMAX / 32) * (KMAX / 32 + 1) / 2 + 7) / 8;     // tiles per wave
     extern __shared__ float ysg[];          // [P][kSgPitch]
     const SymGramItem &it = batch.it[blockIdx.y];
     const int sp = blockIdx.x;
@@ -108,10 +112,10 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
     const int k = it.k, ntm = (k + 31) >> 5, P = 32 * ntm, ntiles = ntm * (ntm + 1) / 2;
     const int tb = sp * it.chunk, te = min(it.len, tb + it.chunk);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, m32 = lane & 31, kh = lane >> 5;
-    int tmv[3], tnv[3];
-    bool tv[3];
+    int tmv[TPW], tnv[TPW];
+    bool tv[TPW];
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+    for (int u = 0; u < TPW; ++u) {
         int t = wid + 8 * u, tm = 0;
         tv[u] = t < ntiles;
         if (!tv[u]) t = 0;
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
         tmv[u] = tm;
         tnv[u] = tm + t;
     }
-    constexpr int kPieces = (kSymGramMaxK * kSgKC / 4 + 511) / 512;     // float4 per thread
+    constexpr int kPieces = (KMAX * kSgKC / 4 + 511) / 512;     // float4 per thread
     float4 stg[kPieces];
     auto load = [&](int t0) {
 #pragma unroll
@@ -147,9 +151,9 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
             }
         }
     };
-    f32x16 acc[3];
+    f32x16 acc[TPW];
 #pragma unroll
-    for (int u = 0; u < 3; ++u) acc[u] = f32x16{};
+    for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
     if (tb < te) load(tb);
     for (int t0 = tb; t0 < te; t0 += kSgKC) {
         __syncthreads();
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
         __syncthreads();
         if (t0 + kSgKC < te) load(t0 + kSgKC);
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
+        for (int u = 0; u < TPW; ++u) {
             if (!tv[u]) continue;
             const float *ra = ysg + (32 * tmv[u] + m32) * kSgPitch + kh;
             const float *rb = ysg + (32 * tnv[u] + m32) * kSgPitch + kh;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
     __syncthreads();                            // every wave is done with the staged chunk
     float *tr = ysg + wid * (32 * 33);
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+    for (int u = 0; u < TPW; ++u) {
         if (!tv[u]) continue;
         const int r0 = 32 * tmv[u], c0 = 32 * tnv[u];
 #pragma unroll
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
 
 hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    if (maxK > kSymGramMaxK) return hipErrorInvalidValue;
+    if (maxK > kSymGramWideK) return hipErrorInvalidValue;
     for (int i = 0; i < b.n; ++i) {
         const SymGramItem &it = b.it[i];
         if (it.len % 4 || it.ldy % 4 || it.chunk % kSgKC || it.kp < 32 * ((it.k + 31) / 32)) return hipErrorInvalidValue;
@@ -198,7 +202,21 @@ hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStr
     KTimeScope kts("k_sym_gram", s);
     // the staged chunk, or 8 waves' 32 x 33 transpose tiles, whichever is larger
     const size_t lds = std::max<size_t>((size_t)32 * ((maxK + 31) / 32) * kSgPitch, 8 * 32 * 33) * sizeof(float);
-    hipLaunchKernelGGL(k_sym_gram, dim3(maxSplit, b.n), dim3(512), lds, s, b);
+    if (maxK > kSymGramMaxK) {
+        static hipError_t state = hipErrorNotReady;
+        if (state == hipErrorNotReady) {
+            hipFuncAttributes fa;
+            state = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k_sym_gram<kSymGramWideK>));
+            if (state == hipSuccess)
+                state = hipFuncSetAttribute(reinterpret_cast<const void *>(k_sym_gram<kSymGramWideK>),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            160 * 1024 - (int)fa.sharedSizeBytes);
+        }
+        if (state != hipSuccess) return state;
+        hipLaunchKernelGGL(k_sym_gram<kSymGramWideK>, dim3(maxSplit, b.n), dim3(512), lds, s, b);
+    } else {
+        hipLaunchKernelGGL(k_sym_gram<kSymGramMaxK>, dim3(maxSplit, b.n), dim3(512), lds, s, b);
+    }
     return hipGetLastError();
 }
 

@@ -132,11 +132,28 @@ __device__ __forceinline__ void tile_kblock(f32x16 &acc, int lane, FA a, FB b) {
 //      (the slot of X_IK^T); meanwhile wave 0 updates block (J+1, J+1) first
 //      and factors it, so the next step's diagonal block is ready at the
 //      barrier.
+//
+// GS: the working square lives in the item's work buffer in device memory
+// (orders up to kCholWideMaxK, whose square does not fit LDS) instead of LDS;
+// the arithmetic and its order are the same.
+template <bool GS>
 __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
-    extern __shared__ float S[];
+    extern __shared__ float S_lds[];
     __shared__ float cb[32 * 64];
     const CholItem &it = batch.it[blockIdx.x];
     if (!it.inverse) return;
+    float *S = GS ? it.work : S_lds;
+    // a wave's stores to S before its lanes read each other's values: LDS
+    // ordering, or (GS) the stores' completion in device memory
+    auto sync_s = []() {
+        if constexpr (GS) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        } else {
+            wave_lds_sync();
+        }
+    };
     const int k = it.k, nb = (k + 31) >> 5, P = nb * 32;
     // the wave index as a scalar: loops and branches on it stay uniform
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,8 +175,17 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
             const float g = it.g[ok ? (size_t)i * it.ld + c : 0];
             S[i * ld + c] = ok ? g : (i == c ? 1.f : 0.f);        // both half-waves write the same value
         }
-        wave_lds_sync();
+        sync_s();
         diag_block(S, ld, cb, shift, k, lane);
+    } else if constexpr (GS) {
+        // the rest of G, with the identity in the padding rows and columns
+        for (int e = tid - 64; e < P * P; e += 64 * (NW - 1)) {
+            const int r = e / P, c = e - r * P;
+            if (r < 32 && c < 32) continue;
+            const bool ok = r < k && c < k;
+            const float g = it.g[ok ? (size_t)r * it.ld + c : 0];
+            S[(size_t)r * ld + c] = ok ? g : (r == c ? 1.f : 0.f);
+        }
     } else {
         // the rest of G, with the identity in the padding rows and columns
         // (float4 loads: rows of G are 16-byte aligned, it.ld is a multiple of 4)
@@ -199,7 +225,7 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
                 const int I0 = 32 * (J + 1 + t);
                 tile_kblock(acc, lane, [&](int m, int kk) { return LDSv(I0 + m, J0 + kk); },
                             [&](int kk, int n) { return x_diag(S, ld, J0, n, kk); });
-                wave_lds_sync();
+                sync_s();
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) S[(I0 + frag_row(lane, jj)) * ld + J0 + (lane & 31)] = acc[jj];
             } else {
@@ -207,7 +233,7 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
                 const int K0 = 32 * (t - npanel);
                 tile_kblock(acc, lane, [&](int m, int kk) { return -x_diag(S, ld, J0, m, kk); },
                             [&](int kk, int n) { return LDSv(K0 + n, J0 + kk); });
-                wave_lds_sync();
+                sync_s();
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) S[(K0 + (lane & 31)) * ld + J0 + frag_row(lane, jj)] = acc[jj];
             }
@@ -225,7 +251,7 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
                         [&](int kk, int n) { return LDSv(J1 + n, J0 + kk); });
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) S[(J1 + frag_row(lane, jj)) * ld + J1 + (lane & 31)] = acc[jj];
-            wave_lds_sync();
+            sync_s();
             diag_block(S + J1 * ld + J1, ld, cb, shift, k - J1, lane);
         } else {
             const int ntrail = npanel * (npanel + 1) / 2 - 1, nacc = npanel * (J + 1);
@@ -263,13 +289,15 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
     JOLT_PROBE(21);
     // L^{-1}: X(i, c) = S[c][i] on and below the diagonal; four rows per wave
     // in flight (in-bounds loads, then selects)
+    __syncthreads();
+    constexpr int NU = ((GS ? kCholWideMaxK : kCholInverseMaxK) + 63) / 64;
     for (int i0 = wid; i0 < k; i0 += 4 * NW) {
-        float val[4][3];
+        float val[4][NU];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int i = min(i0 + q * NW, P - 1);
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
+            for (int u = 0; u < NU; ++u) {
                 const int c = min(lane + 64 * u, P - 1);
                 const float x = S[c * ld + i];
                 val[q][u] = c <= i ? x : 0.f;
@@ -279,7 +307,7 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
         for (int q = 0; q < 4; ++q) {
             const int i = i0 + q * NW;
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
+            for (int u = 0; u < NU; ++u) {
                 const int c = lane + 64 * u;
                 if (i < k && c < k) it.l[(size_t)i * it.ld + c] = val[q][u];
             }
@@ -296,8 +324,8 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
 // registers while the current one is multiplied.
 constexpr int kApplyYS = 68;                // row stride of a staged Y block
 
-template <bool XLDS>
-__global__ __launch_bounds__(64 * kCholInverseMaxK / 32) void k_apply_linv(TrsmBatch batch, int ldx) {
+template <bool XLDS, int KMAX>
+__global__ __launch_bounds__(64 * KMAX / 32) void k_apply_linv(TrsmBatch batch, int ldx) {
     extern __shared__ float sh[];
     const TrsmItem &it = batch.it[blockIdx.y];
     const int k = it.k, ntm = (k + 31) >> 5, P = 32 * ntm, nthr = 64 * ntm;
@@ -394,9 +422,10 @@ static hipError_t allow_lds(const void *fn) {
 static hipError_t orth_lds_attrs() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_chol_inv));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<true>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<false>));
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_chol_inv<false>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<true, kCholInverseMaxK>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<false, kCholInverseMaxK>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<false, kCholWideMaxK>));
         state = e;
     }
     return state;
@@ -404,19 +433,23 @@ static hipError_t orth_lds_attrs() {
 
 hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    if (maxK > kCholInverseMaxK) return hipErrorInvalidValue;
-    for (int i = 0; i < b.n; ++i)
+    if (maxK > kCholWideMaxK) return hipErrorInvalidValue;
+    const bool gs = maxK > kCholInverseMaxK;
+    for (int i = 0; i < b.n; ++i) {
         if (b.it[i].ld % 4 || b.it[i].ld < b.it[i].k) return hipErrorInvalidValue;    // float4 rows of G
+        if (gs && !b.it[i].work) return hipErrorInvalidValue;
+    }
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
     KTimeScope kts("k_chol_inv", s);
-    const int P = (maxK + 31) / 32 * 32, ld = P + 1;
-    hipLaunchKernelGGL(k_chol_inv, dim3(b.n), dim3(512), (size_t)P * ld * sizeof(float), s, b, ld);
+    const int P = (maxK + 31) / 32 * 32;
+    if (gs) hipLaunchKernelGGL(k_chol_inv<true>, dim3(b.n), dim3(512), 0, s, b, P);
+    else hipLaunchKernelGGL(k_chol_inv<false>, dim3(b.n), dim3(512), (size_t)P * (P + 1) * sizeof(float), s, b, P + 1);
     return hipGetLastError();
 }
 
 hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
-    if (maxK > kCholInverseMaxK) return hipErrorInvalidValue;
+    if (maxK > kCholWideMaxK) return hipErrorInvalidValue;
     for (int i = 0; i < b.n; ++i)
         if (b.it[i].len % 4 || b.it[i].ldy % 4 || b.it[i].ld % 4) return hipErrorInvalidValue;
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
@@ -429,8 +462,13 @@ hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream
     // staged once per workgroup, so fewer, longer workgroups read less of it)
     const int ncb = (maxLen + 63) / 64;
     const int gx = std::max(1, std::min(ncb, (256 + b.n - 1) / b.n));
-    if (xin) hipLaunchKernelGGL(k_apply_linv<true>, dim3(gx, b.n), dim3(64 * ntm), ylds + xlds, s, b, ldx);
-    else hipLaunchKernelGGL(k_apply_linv<false>, dim3(gx, b.n), dim3(64 * ntm), ylds, s, b, ldx);
+    if (maxK > kCholInverseMaxK)
+        hipLaunchKernelGGL((k_apply_linv<false, kCholWideMaxK>), dim3(gx, b.n), dim3(64 * ntm), ylds, s, b, ldx);
+    else if (xin)
+        hipLaunchKernelGGL((k_apply_linv<true, kCholInverseMaxK>), dim3(gx, b.n), dim3(64 * ntm), ylds + xlds, s, b,
+                           ldx);
+    else
+        hipLaunchKernelGGL((k_apply_linv<false, kCholInverseMaxK>), dim3(gx, b.n), dim3(64 * ntm), ylds, s, b, ldx);
     return hipGetLastError();
 }
 

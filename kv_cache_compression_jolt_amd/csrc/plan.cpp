@@ -53,7 +53,7 @@ struct Dims {
 };
 
 struct Scratch {
-    size_t omt, yt, ypart, qh, ql, zt, zb, xpart, gpart, gram, lmat, wmat, vmat, lamk, sweeps;
+    size_t omt, yt, ypart, qh, ql, zt, zb, xpart, gpart, gram, lmat, csq, wmat, vmat, lamk, sweeps;
     size_t gfpart, gf, pmat, gt, vt, lamT, uh, ul;
     size_t eA, eT, eV, eVT, eR, eRlam, eNorm, eSw;     // block Jacobi (n > 142)
     size_t etri, ftri;      // tridiagonal solver workspaces (token, feature); SIZE_MAX if unused
@@ -119,6 +119,7 @@ void reserve_scratch(const jolt_config &cfg, const Dims &D, Bump &b, Scratch &s)
         s.gpart = b.take((size_t)std::max(D.gT_split, D.gN_split) * kp * kp * 4);
         s.gram = b.take(kp * kp * 4);
         s.lmat = b.take(kp * kp * 4);
+        s.csq = D.k > kCholInverseMaxK ? b.take(kp * kp * 4) : 0;     // the inverse factor's working square
         s.wmat = b.take(kp * kp * 4);
         s.vmat = b.take(kp * kp * 4);
         s.lamk = b.take(kp * 4);
@@ -462,7 +463,7 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
 // Grams of k-row panels (part[s] = partial sums of split s): the symmetric
 // kernel up to kSymGramMaxK rows, the generic GEMM beyond
 hipError_t panel_grams(const SymGramBatch &gb, int maxK, int maxS, hipStream_t st) {
-    if (maxK <= kSymGramMaxK) return launch_sym_gram(gb, maxK, maxS, st);
+    if (maxK <= kSymGramWideK) return launch_sym_gram(gb, maxK, maxS, st);
     GemmBatch g{};
     for (int i = 0; i < gb.n; ++i) {
         const SymGramItem &s = gb.it[i];
@@ -479,8 +480,8 @@ hipError_t panel_grams(const SymGramBatch &gb, int maxK, int maxS, hipStream_t s
 // Orthonormalizes the rows of each y in place (passes of shifted CholeskyQR).
 // With hi (and lo) given, the last pass also writes bf16 copies of the result
 // when the L^-1 apply runs (k <= kCholInverseMaxK); *bf reports whether it did.
-jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, const int *k,
-                      const int *kp, const int *len, const int *split, const int *chunk, int passes,
+jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, float **csq,
+                      const int *k, const int *kp, const int *len, const int *split, const int *chunk, int passes,
                       uint16_t *const *hi = nullptr, uint16_t *const *lo = nullptr, bool *bf = nullptr) {
     if (bf) *bf = false;
     for (int pass = 0; pass < passes; ++pass) {
@@ -498,7 +499,8 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
             r.nsplit = split[i];
             CholItem &ch = cb.it[cb.n++];
             ch.g = gram[i]; ch.l = lmat[i]; ch.k = k[i]; ch.ld = kp[i]; ch.rel_shift = 1.0f / 1048576.0f;
-            ch.inverse = k[i] <= kCholInverseMaxK;
+            ch.inverse = k[i] <= kCholWideMaxK;
+            ch.work = csq[i];
             TrsmItem &t = tb.it[tb.n++];
             t.l = lmat[i]; t.y = y[i]; t.q = y[i]; t.k = k[i]; t.ld = kp[i]; t.len = len[i]; t.ldy = len[i];
             if (hi && pass + 1 == passes) {
@@ -514,7 +516,7 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
         for (int i = 0; i < nb; ++i) maxCount = std::max<int64_t>(maxCount, (int64_t)kp[i] * kp[i]);
         HIPCHK(launch_reduce(rb, maxCount, c.st), "orth reduce");
         HIPCHK(launch_cholesky(cb, maxK, c.st), "orth cholesky");
-        if (maxK <= kCholInverseMaxK) {
+        if (maxK <= kCholWideMaxK) {
             HIPCHK(launch_apply_linv(tb, maxK, maxLen, c.st), "orth L^-1 Y");
             if (bf && hi && pass + 1 == passes) *bf = true;
         } else {
@@ -593,7 +595,7 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     };
 
     if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
-        std::vector<float *> yv(nb), zv(nb), gram(nb), gpart(nb), lmat(nb);
+        std::vector<float *> yv(nb), zv(nb), gram(nb), gpart(nb), lmat(nb), csq(nb);
         std::vector<int> kk(nb), kpp(nb), lenT(nb), lenN(nb), sT(nb), cT(nb), sN(nb), cN(nb);
         SmallBatch ob{};
         int64_t maxOm = 0;
@@ -609,6 +611,7 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
         for (int i = 0; i < nb; ++i) {
             yv[i] = F(S[i].yt); zv[i] = F(S[i].zt); gram[i] = F(S[i].gram); gpart[i] = F(S[i].gpart);
             lmat[i] = F(S[i].lmat);
+            csq[i] = S[i].csq ? F(S[i].csq) : nullptr;
             kk[i] = D[i].k; kpp[i] = D[i].kp; lenT[i] = D[i].T; lenN[i] = D[i].n;
             sT[i] = D[i].gT_split; cT[i] = D[i].gT_chunk; sN[i] = D[i].gN_split; cN[i] = D[i].gN_chunk;
         }
@@ -691,20 +694,20 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
         uint16_t *const *qh_out = bf ? qhv.data() : nullptr;
         bool conv = false;
         if ((s = xm(true))) return s;                                                        // Y = A Omega
-        if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
+        if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(), kpp.data(),
                            lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2, qh_out,
                            (bf && cfg.power_iters == 0) ? qlv.data() : nullptr, &conv)))
             return s;
         for (int q = 0; q < cfg.power_iters; ++q) {
             if (!conv && (s = to_bf(true, false))) return s;
             if ((s = xtq(false))) return s;                                                 // Z = A^T Q
-            if ((s = orth_rows(c, nb, zv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
+            if ((s = orth_rows(c, nb, zv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(), kpp.data(),
                                lenN.data(), sN.data(), cN.data(), 1, bf ? zbv.data() : nullptr, nullptr, &conv)))
                 return s;
             if (!conv && (s = to_bf(false, false))) return s;
             if ((s = xm(false))) return s;                                                  // Y = A Z
             const bool last = q + 1 == cfg.power_iters;
-            if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), kk.data(), kpp.data(),
+            if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(), kpp.data(),
                                lenT.data(), sT.data(), cT.data(), last ? 2 : 1, qh_out,
                                (bf && last) ? qlv.data() : nullptr, &conv)))
                 return s;

@@ -65,6 +65,7 @@ struct SymGramItem {
 };
 struct SymGramBatch { SymGramItem it[kMaxBatch]; int n; };
 constexpr int kSymGramMaxK = 192;
+constexpr int kSymGramWideK = 288;
 hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStream_t s);
 
 // out[i] = sum_s part[s * stride + i], i < count (fixed order); optional double trace
@@ -80,10 +81,11 @@ hipError_t launch_reduce(const ReduceBatch &b, int64_t maxCount, hipStream_t s);
 // Cholesky of G + shift I (k x k, ld) -> lower L written to l (k x k, ld), zeros above
 struct CholItem {
     const float *g;
-    float *l;            // L, or L^{-1} when inverse != 0 (k <= kCholInverseMaxK)
+    float *l;            // L, or L^{-1} when inverse != 0 (k <= kCholWideMaxK)
     int k, ld;
     float rel_shift;     // shift = rel_shift * trace(G) / k
     int inverse;
+    float *work;         // k > kCholInverseMaxK: P x P device scratch (P = k rounded up to 32)
 };
 struct CholBatch { CholItem it[kMaxBatch]; int n; };
 hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s);
@@ -100,7 +102,8 @@ struct TrsmBatch { TrsmItem it[kMaxBatch]; int n; };
 hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
 // y <- X y with X = L^{-1} lower triangular (in place; k <= 600)
 hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
-constexpr int kCholInverseMaxK = 192;
+constexpr int kCholInverseMaxK = 192;     // the inverse factor's working square in LDS
+constexpr int kCholWideMaxK = 288;        // ... or in the item's work buffer
 // the fused elimination behind launch_cholesky for the inverse != 0 items
 hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s);
 
