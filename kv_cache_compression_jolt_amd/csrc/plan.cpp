@@ -243,9 +243,9 @@ jolt_status plan_layout(const jolt_config &cfg, const jolt_item *items, int n, P
     }
     pl.scratch = b.off;
     size_t worst = 0;
-    for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
+    for (int c0 = 0; c0 < n; c0 += kPlanGroup) {
         Bump sb;
-        for (int i = c0; i < std::min(n, c0 + kMaxBatch); ++i) {
+        for (int i = c0; i < std::min(n, c0 + kPlanGroup); ++i) {
             Dims D = dims_for(cfg, items[i], pl.rt_max, pl.rf_max);
             Scratch S;
             reserve_scratch(cfg, D, sb, S);
@@ -333,7 +333,7 @@ jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint
                     j.n = 128;
                     j.raw = 1;
                     j.sweeps_out = reinterpret_cast<int *>(scr + reqs[i].S->eSw) + p;
-                    if (jb.n == 64) {
+                    if (jb.n == kSolverBatch) {
                         HIPCHK(launch_jacobi_lds(jb, 128, inner_sweeps, c.st), "eig pairs");
                         jb.n = 0;
                     }
@@ -420,7 +420,7 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
             j.raw = 0;
             j.tw = r.tw;
             maxW = std::max(maxW, r.n);
-            if (wb.n == 64)
+            if (wb.n == kSolverBatch)
                 if (jolt_status s = flush_wide()) return s;
         } else if (r.n <= kTriMaxN && r.sw && r.tw) {
             JacItem &j = tb.it[tb.n++];
@@ -428,14 +428,14 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
             j.raw = 0;
             j.tw = r.tw;
             maxT = std::max(maxT, r.n);
-            if (tb.n == 64)
+            if (tb.n == kSolverBatch)
                 if (jolt_status s = flush_tri()) return s;
         } else if (r.n <= kJacobiMaxN) {
             JacItem &j = jb.it[jb.n++];
             j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
             j.raw = 0;
             maxN = std::max(maxN, r.n);
-            if (jb.n == 64) {
+            if (jb.n == kSolverBatch) {
                 HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
                 jb.n = 0;
                 maxN = 0;
@@ -453,10 +453,13 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
         if (jolt_status s = flush_tri()) return s;
     if (wb.n)
         if (jolt_status s = flush_wide()) return s;
-    for (size_t g = 0; g < large.size(); ++g) {
-        jolt_status s = eig_block(c, large[g], largeN[g], scr, max_sweeps, noconv);
-        if (s) return s;
-    }
+    for (size_t g = 0; g < large.size(); ++g)
+        for (size_t s0 = 0; s0 < large[g].size(); s0 += kMaxBatch) {
+            const std::vector<EigReq> part(large[g].begin() + s0,
+                                           large[g].begin() + std::min(large[g].size(), s0 + kMaxBatch));
+            jolt_status s = eig_block(c, part, largeN[g], scr, max_sweeps, noconv);
+            if (s) return s;
+        }
     return JOLT_OK;
 }
 
@@ -477,56 +480,91 @@ hipError_t panel_grams(const SymGramBatch &gb, int maxK, int maxS, hipStream_t s
     return launch_gemm(g, maxK, maxK, maxS, 1, st);
 }
 
+// Launches in slices of at most CAP items: fill(batch, i) appends item i (or
+// nothing), go(batch) launches a non-empty batch.
+template <class Batch, int CAP, class Fill, class Go>
+hipError_t sliced(int n, Fill &&fill, Go &&go) {
+    for (int s0 = 0; s0 < n; s0 += CAP) {
+        Batch b{};
+        b.n = 0;
+        for (int i = s0; i < std::min(n, s0 + CAP); ++i) fill(b, i);
+        if (b.n == 0) continue;
+        if (hipError_t e = go(b); e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Orthonormalizes the rows of each y in place (passes of shifted CholeskyQR).
 // With hi (and lo) given, the last pass also writes bf16 copies of the result
-// when the L^-1 apply runs (k <= kCholInverseMaxK); *bf reports whether it did.
+// when the L^-1 apply runs (k <= kCholWideMaxK); *bf reports whether it did.
 jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, float **csq,
                       const int *k, const int *kp, const int *len, const int *split, const int *chunk, int passes,
                       uint16_t *const *hi = nullptr, uint16_t *const *lo = nullptr, bool *bf = nullptr) {
     if (bf) *bf = false;
+    int maxK = 0, maxLen = 0, maxS = 0;
+    int64_t maxCount = 0;
+    for (int i = 0; i < nb; ++i) {
+        maxK = std::max(maxK, k[i]);
+        maxLen = std::max(maxLen, len[i]);
+        maxS = std::max(maxS, split[i]);
+        maxCount = std::max<int64_t>(maxCount, (int64_t)kp[i] * kp[i]);
+    }
     for (int pass = 0; pass < passes; ++pass) {
-        SymGramBatch gb{};
-        ReduceBatch rb{};
-        CholBatch cb{};
-        TrsmBatch tb{};
-        int maxK = 0, maxLen = 0, maxS = 0;
-        for (int i = 0; i < nb; ++i) {
-            SymGramItem &g = gb.it[gb.n++];
-            g.y = y[i]; g.part = gpart[i]; g.k = k[i]; g.kp = kp[i]; g.len = len[i]; g.ldy = len[i];
-            g.chunk = chunk[i]; g.nsplit = split[i];
-            ReduceItem &r = rb.it[rb.n++];
-            r.part = gpart[i]; r.out = gram[i]; r.stride = (int64_t)kp[i] * kp[i]; r.count = (int64_t)kp[i] * kp[i];
-            r.nsplit = split[i];
-            CholItem &ch = cb.it[cb.n++];
-            ch.g = gram[i]; ch.l = lmat[i]; ch.k = k[i]; ch.ld = kp[i]; ch.rel_shift = 1.0f / 1048576.0f;
-            ch.inverse = k[i] <= kCholWideMaxK;
-            ch.work = csq[i];
-            TrsmItem &t = tb.it[tb.n++];
-            t.l = lmat[i]; t.y = y[i]; t.q = y[i]; t.k = k[i]; t.ld = kp[i]; t.len = len[i]; t.ldy = len[i];
-            if (hi && pass + 1 == passes) {
-                t.qh = hi[i];
-                t.ql = lo ? lo[i] : nullptr;
-            }
-            maxK = std::max(maxK, k[i]);
-            maxLen = std::max(maxLen, len[i]);
-            maxS = std::max(maxS, split[i]);
-        }
-        HIPCHK(panel_grams(gb, maxK, maxS, c.st), "orth gram");
-        int64_t maxCount = 0;
-        for (int i = 0; i < nb; ++i) maxCount = std::max<int64_t>(maxCount, (int64_t)kp[i] * kp[i]);
-        HIPCHK(launch_reduce(rb, maxCount, c.st), "orth reduce");
-        HIPCHK(launch_cholesky(cb, maxK, c.st), "orth cholesky");
-        if (maxK <= kCholWideMaxK) {
-            HIPCHK(launch_apply_linv(tb, maxK, maxLen, c.st), "orth L^-1 Y");
-            if (bf && hi && pass + 1 == passes) *bf = true;
-        } else {
-            HIPCHK(launch_trsm(tb, maxK, maxLen, c.st), "orth trsm");
-        }
+        const bool last = pass + 1 == passes;
+        HIPCHK((sliced<SymGramBatch, kMaxBatch>(
+                   nb,
+                   [&](SymGramBatch &b, int i) {
+                       SymGramItem &g = b.it[b.n++];
+                       g.y = y[i]; g.part = gpart[i]; g.k = k[i]; g.kp = kp[i]; g.len = len[i]; g.ldy = len[i];
+                       g.chunk = chunk[i]; g.nsplit = split[i];
+                   },
+                   [&](const SymGramBatch &b) { return panel_grams(b, maxK, maxS, c.st); })),
+               "orth gram");
+        HIPCHK((sliced<ReduceBatch, kMaxBatch>(
+                   nb,
+                   [&](ReduceBatch &b, int i) {
+                       ReduceItem &r = b.it[b.n++];
+                       r.part = gpart[i]; r.out = gram[i]; r.stride = (int64_t)kp[i] * kp[i];
+                       r.count = (int64_t)kp[i] * kp[i]; r.nsplit = split[i];
+                   },
+                   [&](const ReduceBatch &b) { return launch_reduce(b, maxCount, c.st); })),
+               "orth reduce");
+        HIPCHK((sliced<CholBatch, kSolverBatch>(
+                   nb,
+                   [&](CholBatch &b, int i) {
+                       CholItem &ch = b.it[b.n++];
+                       ch.g = gram[i]; ch.l = lmat[i]; ch.k = k[i]; ch.ld = kp[i]; ch.rel_shift = 1.0f / 1048576.0f;
+                       ch.inverse = k[i] <= kCholWideMaxK;
+                       ch.work = csq[i];
+                   },
+                   [&](const CholBatch &b) { return launch_cholesky(b, maxK, c.st); })),
+               "orth cholesky");
+        HIPCHK((sliced<TrsmBatch, kMaxBatch>(
+                   nb,
+                   [&](TrsmBatch &b, int i) {
+                       TrsmItem &t = b.it[b.n++];
+                       t.l = lmat[i]; t.y = y[i]; t.q = y[i]; t.k = k[i]; t.ld = kp[i]; t.len = len[i];
+                       t.ldy = len[i];
+                       if (hi && last) {
+                           t.qh = hi[i];
+                           t.ql = lo ? lo[i] : nullptr;
+                       }
+                   },
+                   [&](const TrsmBatch &b) {
+                       return maxK <= kCholWideMaxK ? launch_apply_linv(b, maxK, maxLen, c.st)
+                                                    : launch_trsm(b, maxK, maxLen, c.st);
+                   })),
+               "orth L^-1 Y");
+        if (bf && hi && last && maxK <= kCholWideMaxK) *bf = true;
     }
     return JOLT_OK;
 }
 
-jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items,
+// One group of up to kPlanGroup items: every stage runs for all of them
+// before the next, with launches of kMaxBatch items for the streaming kernels
+// and kSolverBatch items for the one-workgroup-per-matrix solvers, whose
+// launches would otherwise leave most CUs idle.
+jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items,
                            int i0, int nb, const void *const *x_dev, uint8_t *ws, bool *noconv, bool wide_ok,
                            hipStream_t *forked) {
     const int max_sweeps = cfg.max_sweeps > 0 ? cfg.max_sweeps : 30;
@@ -543,7 +581,8 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     HIPCHK(launch_zero(ws + pl.item[i0].grid, pl.readback_stride * nb, c.st), "zero readback");
     auto P = [&](size_t off) { return scr + off; };
     auto F = [&](size_t off) { return reinterpret_cast<float *>(scr + off); };
-    auto W = [&](int i, size_t off) { return ws + off; };
+    auto W = [&](size_t off) { return ws + off; };
+    const FactorOffsets *fo = pl.item.data() + i0;
     int maxT = 0, maxLH = 0;
     for (int i = 0; i < nb; ++i) {
         maxT = std::max(maxT, D[i].T);
@@ -553,10 +592,9 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     // the feature eigenproblems run on the side stream too, next to the token ones
     std::vector<EigReq> feigs, eigs;
     for (int i = 0; i < nb; ++i)
-        feigs.push_back(EigReq{F(S[i].gf), d, d, reinterpret_cast<float *>(ws + pl.item[i0 + i].uf), d,
-                               reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_f),
-                               reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps), &S[i],
-                               S[i].ftri != SIZE_MAX ? F(S[i].ftri) : nullptr});
+        feigs.push_back(EigReq{F(S[i].gf), d, d, reinterpret_cast<float *>(W(fo[i].uf)), d,
+                               reinterpret_cast<float *>(W(fo[i].lam_f)), reinterpret_cast<int *>(W(fo[i].sweeps)),
+                               &S[i], S[i].ftri != SIZE_MAX ? F(S[i].ftri) : nullptr});
     // ---- feature Gram, ||X||^2 and the feature eigenproblems, on the side
     // stream: forked when the token eigenproblems start (one workgroup per
     // matrix leaves most CUs and HBM idle for this), joined before the core,
@@ -568,26 +606,34 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
         HIPCHK(hipEventRecord(fork, c.st), "fork");
         HIPCHK(hipStreamWaitEvent(side, fork, 0), "fork");
         *forked = side;
-        GramBatch gb{};
-        ReduceBatch rb{};
         int maxP = 0;
-        for (int i = 0; i < nb; ++i) {
-            GramItem &g = gb.it[gb.n++];
-            g.x = x_dev[i0 + i]; g.out = F(S[i].gfpart);
-            g.rows = (int64_t)D[i].LH * D[i].T; g.chunk = D[i].gf_chunk; g.P = D[i].gf_P;
-            maxP = std::max(maxP, g.P);
-            ReduceItem &r = rb.it[rb.n++];
-            r.part = F(S[i].gfpart); r.out = F(S[i].gf); r.stride = (int64_t)d * d; r.count = (int64_t)d * d;
-            r.nsplit = D[i].gf_P;
-        }
-        HIPCHK(launch_gram_rows(gb, dt, d, maxP, side), "feature gram");
-        HIPCHK(launch_reduce(rb, (int64_t)d * d, side), "feature gram reduce");
-        SmallBatch tb{};
-        for (int i = 0; i < nb; ++i) {
-            SmallItem &t = tb.it[tb.n++];
-            t.in = F(S[i].gf); t.out64 = reinterpret_cast<double *>(W(i, pl.item[i0 + i].normx2)); t.a = d;
-        }
-        HIPCHK(launch_trace_batch(tb, side), "trace");
+        for (int i = 0; i < nb; ++i) maxP = std::max(maxP, D[i].gf_P);
+        HIPCHK((sliced<GramBatch, kMaxBatch>(
+                   nb,
+                   [&](GramBatch &b, int i) {
+                       GramItem &g = b.it[b.n++];
+                       g.x = x_dev[i0 + i]; g.out = F(S[i].gfpart);
+                       g.rows = (int64_t)D[i].LH * D[i].T; g.chunk = D[i].gf_chunk; g.P = D[i].gf_P;
+                   },
+                   [&](const GramBatch &b) { return launch_gram_rows(b, dt, d, maxP, side); })),
+               "feature gram");
+        HIPCHK((sliced<ReduceBatch, kMaxBatch>(
+                   nb,
+                   [&](ReduceBatch &b, int i) {
+                       ReduceItem &r = b.it[b.n++];
+                       r.part = F(S[i].gfpart); r.out = F(S[i].gf); r.stride = (int64_t)d * d;
+                       r.count = (int64_t)d * d; r.nsplit = D[i].gf_P;
+                   },
+                   [&](const ReduceBatch &b) { return launch_reduce(b, (int64_t)d * d, side); })),
+               "feature gram reduce");
+        HIPCHK((sliced<SmallBatch, kMaxBatch>(
+                   nb,
+                   [&](SmallBatch &b, int i) {
+                       SmallItem &t = b.it[b.n++];
+                       t.in = F(S[i].gf); t.out64 = reinterpret_cast<double *>(W(fo[i].normx2)); t.a = d;
+                   },
+                   [&](const SmallBatch &b) { return launch_trace_batch(b, side); })),
+               "trace");
         const Ctx cs{c.h, side, c.dtype, c.d};
         if (jolt_status es = eig_all(cs, feigs, scr, max_sweeps, noconv, wide_ok)) return es;
         HIPCHK(hipEventRecord(join, side), "join");
@@ -597,17 +643,20 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     if (cfg.mode == JOLT_TOKEN_RANDOMIZED) {
         std::vector<float *> yv(nb), zv(nb), gram(nb), gpart(nb), lmat(nb), csq(nb);
         std::vector<int> kk(nb), kpp(nb), lenT(nb), lenN(nb), sT(nb), cT(nb), sN(nb), cN(nb);
-        SmallBatch ob{};
         int64_t maxOm = 0;
-        for (int i = 0; i < nb; ++i) {
-            const jolt_item &it = items[i0 + i];
-            SmallItem &o = ob.it[ob.n++];
-            o.hi = bf ? reinterpret_cast<uint16_t *>(P(S[i].omt)) : nullptr;
-            o.out32 = bf ? nullptr : F(S[i].omt);
-            o.key = item_key(it.seed, it.item_id); o.a = D[i].k; o.b = D[i].kp; o.count = (int64_t)D[i].kp * D[i].n;
-            maxOm = std::max(maxOm, o.count);
-        }
-        HIPCHK(launch_gen_omega_batch(ob, maxOm, c.st), "omega");
+        for (int i = 0; i < nb; ++i) maxOm = std::max<int64_t>(maxOm, (int64_t)D[i].kp * D[i].n);
+        HIPCHK((sliced<SmallBatch, kMaxBatch>(
+                   nb,
+                   [&](SmallBatch &b, int i) {
+                       const jolt_item &it = items[i0 + i];
+                       SmallItem &o = b.it[b.n++];
+                       o.hi = bf ? reinterpret_cast<uint16_t *>(P(S[i].omt)) : nullptr;
+                       o.out32 = bf ? nullptr : F(S[i].omt);
+                       o.key = item_key(it.seed, it.item_id); o.a = D[i].k; o.b = D[i].kp;
+                       o.count = (int64_t)D[i].kp * D[i].n;
+                   },
+                   [&](const SmallBatch &b) { return launch_gen_omega_batch(b, maxOm, c.st); })),
+               "omega");
         for (int i = 0; i < nb; ++i) {
             yv[i] = F(S[i].yt); zv[i] = F(S[i].zt); gram[i] = F(S[i].gram); gpart[i] = F(S[i].gpart);
             lmat[i] = F(S[i].lmat);
@@ -616,70 +665,88 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
             sT[i] = D[i].gT_split; cT[i] = D[i].gT_chunk; sN[i] = D[i].gN_split; cN[i] = D[i].gN_chunk;
         }
         auto xm = [&](bool first) -> jolt_status {
-            XmBatch xb{};
-            ReduceBatch rb{};
             int maxC = 0, maxS = 0;
             int64_t maxCount = 0;
             for (int i = 0; i < nb; ++i) {
-                XmItem &x = xb.it[xb.n++];
-                x.x = x_dev[i0 + i];
-                x.m = first ? (const void *)P(S[i].omt) : (bf ? (const void *)P(S[i].zb) : (const void *)P(S[i].zt));
-                x.m_c = D[i].n; x.m_blk = d;
-                x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].kp; x.ldo = D[i].T;
-                x.lh_split = D[i].xm_lh; x.nsplit = D[i].xm_split;
-                x.out = x.nsplit > 1 ? F(S[i].ypart) : F(S[i].yt);
-                maxC = std::max(maxC, x.ncols);
-                maxS = std::max(maxS, x.nsplit);
-                if (x.nsplit > 1) {
-                    ReduceItem &r = rb.it[rb.n++];
-                    r.part = F(S[i].ypart); r.out = F(S[i].yt);
-                    r.stride = (int64_t)D[i].kp * D[i].T; r.count = r.stride; r.nsplit = x.nsplit;
-                    maxCount = std::max(maxCount, r.count);
-                }
+                maxC = std::max(maxC, D[i].kp);
+                maxS = std::max(maxS, D[i].xm_split);
+                maxCount = std::max<int64_t>(maxCount, (int64_t)D[i].kp * D[i].T);
             }
-            HIPCHK(launch_xm(xb, dt, d, maxT, maxC, maxS, c.st), "sketch A M");
-            HIPCHK(launch_reduce(rb, maxCount, c.st), "sketch reduce");
+            HIPCHK((sliced<XmBatch, kMaxBatch>(
+                       nb,
+                       [&](XmBatch &b, int i) {
+                           XmItem &x = b.it[b.n++];
+                           x.x = x_dev[i0 + i];
+                           x.m = first ? (const void *)P(S[i].omt)
+                                       : (bf ? (const void *)P(S[i].zb) : (const void *)P(S[i].zt));
+                           x.m_c = D[i].n; x.m_blk = d;
+                           x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].kp; x.ldo = D[i].T;
+                           x.lh_split = D[i].xm_lh; x.nsplit = D[i].xm_split;
+                           x.out = x.nsplit > 1 ? F(S[i].ypart) : F(S[i].yt);
+                       },
+                       [&](const XmBatch &b) { return launch_xm(b, dt, d, maxT, maxC, maxS, c.st); })),
+                   "sketch A M");
+            HIPCHK((sliced<ReduceBatch, kMaxBatch>(
+                       nb,
+                       [&](ReduceBatch &b, int i) {
+                           if (D[i].xm_split <= 1) return;
+                           ReduceItem &r = b.it[b.n++];
+                           r.part = F(S[i].ypart); r.out = F(S[i].yt);
+                           r.stride = (int64_t)D[i].kp * D[i].T; r.count = r.stride; r.nsplit = D[i].xm_split;
+                       },
+                       [&](const ReduceBatch &b) { return launch_reduce(b, maxCount, c.st); })),
+                   "sketch reduce");
             return JOLT_OK;
         };
         auto xtq = [&](bool hilo) -> jolt_status {
-            XtqBatch xb{};
-            ReduceBatch rb{};
             int maxS = 0, maxC = 0;
             int64_t maxCount = 0;
             for (int i = 0; i < nb; ++i) {
-                XtqItem &x = xb.it[xb.n++];
-                x.x = x_dev[i0 + i];
-                x.qh = bf ? (const void *)P(S[i].qh) : (const void *)P(S[i].yt);
-                x.ql = (bf && hilo) ? (const void *)P(S[i].ql) : nullptr;
-                x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].kp; x.ldq = D[i].T;
-                x.tsplit = D[i].xs_tsplit; x.nsplit = D[i].xs_split;
-                x.out = x.nsplit == 1 ? F(S[i].zt) : F(S[i].xpart);
-                maxS = std::max(maxS, x.nsplit);
-                maxC = std::max(maxC, x.ncols);
-                if (x.nsplit > 1) {
-                    ReduceItem &r = rb.it[rb.n++];
-                    r.part = F(S[i].xpart); r.out = F(S[i].zt);
-                    r.stride = (int64_t)D[i].kp * D[i].n; r.count = r.stride; r.nsplit = x.nsplit;
-                    maxCount = std::max(maxCount, r.count);
-                }
+                maxS = std::max(maxS, D[i].xs_split);
+                maxC = std::max(maxC, D[i].kp);
+                maxCount = std::max<int64_t>(maxCount, (int64_t)D[i].kp * D[i].n);
             }
-            HIPCHK(launch_xtq(xb, dt, d, maxLH, maxS, maxC, c.st), "sketch Q^T A");
-            HIPCHK(launch_reduce(rb, maxCount, c.st), "sketch reduce");
+            HIPCHK((sliced<XtqBatch, kMaxBatch>(
+                       nb,
+                       [&](XtqBatch &b, int i) {
+                           XtqItem &x = b.it[b.n++];
+                           x.x = x_dev[i0 + i];
+                           x.qh = bf ? (const void *)P(S[i].qh) : (const void *)P(S[i].yt);
+                           x.ql = (bf && hilo) ? (const void *)P(S[i].ql) : nullptr;
+                           x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].kp; x.ldq = D[i].T;
+                           x.tsplit = D[i].xs_tsplit; x.nsplit = D[i].xs_split;
+                           x.out = x.nsplit == 1 ? F(S[i].zt) : F(S[i].xpart);
+                       },
+                       [&](const XtqBatch &b) { return launch_xtq(b, dt, d, maxLH, maxS, maxC, c.st); })),
+                   "sketch Q^T A");
+            HIPCHK((sliced<ReduceBatch, kMaxBatch>(
+                       nb,
+                       [&](ReduceBatch &b, int i) {
+                           if (D[i].xs_split <= 1) return;
+                           ReduceItem &r = b.it[b.n++];
+                           r.part = F(S[i].xpart); r.out = F(S[i].zt);
+                           r.stride = (int64_t)D[i].kp * D[i].n; r.count = r.stride; r.nsplit = D[i].xs_split;
+                       },
+                       [&](const ReduceBatch &b) { return launch_reduce(b, maxCount, c.st); })),
+                   "sketch reduce");
             return JOLT_OK;
         };
         auto to_bf = [&](bool from_y, bool lo) -> jolt_status {
             if (!bf) return JOLT_OK;
-            SmallBatch cb{};
             int64_t maxC = 0;
-            for (int i = 0; i < nb; ++i) {
-                SmallItem &t = cb.it[cb.n++];
-                t.in = from_y ? F(S[i].yt) : F(S[i].zt);
-                t.hi = reinterpret_cast<uint16_t *>(from_y ? P(S[i].qh) : P(S[i].zb));
-                t.lo = (from_y && lo) ? reinterpret_cast<uint16_t *>(P(S[i].ql)) : nullptr;
-                t.count = (int64_t)D[i].kp * (from_y ? D[i].T : D[i].n);
-                maxC = std::max(maxC, t.count);
-            }
-            HIPCHK(launch_to_bf16_batch(cb, maxC, c.st), "to bf16");
+            for (int i = 0; i < nb; ++i)
+                maxC = std::max<int64_t>(maxC, (int64_t)D[i].kp * (from_y ? D[i].T : D[i].n));
+            HIPCHK((sliced<SmallBatch, kMaxBatch>(
+                       nb,
+                       [&](SmallBatch &b, int i) {
+                           SmallItem &t = b.it[b.n++];
+                           t.in = from_y ? F(S[i].yt) : F(S[i].zt);
+                           t.hi = reinterpret_cast<uint16_t *>(from_y ? P(S[i].qh) : P(S[i].zb));
+                           t.lo = (from_y && lo) ? reinterpret_cast<uint16_t *>(P(S[i].ql)) : nullptr;
+                           t.count = (int64_t)D[i].kp * (from_y ? D[i].T : D[i].n);
+                       },
+                       [&](const SmallBatch &b) { return launch_to_bf16_batch(b, maxC, c.st); })),
+                   "to bf16");
             return JOLT_OK;
         };
         jolt_status s;
@@ -694,21 +761,22 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
         uint16_t *const *qh_out = bf ? qhv.data() : nullptr;
         bool conv = false;
         if ((s = xm(true))) return s;                                                        // Y = A Omega
-        if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(), kpp.data(),
-                           lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2, qh_out,
+        if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
+                           kpp.data(), lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2, qh_out,
                            (bf && cfg.power_iters == 0) ? qlv.data() : nullptr, &conv)))
             return s;
         for (int q = 0; q < cfg.power_iters; ++q) {
             if (!conv && (s = to_bf(true, false))) return s;
             if ((s = xtq(false))) return s;                                                 // Z = A^T Q
-            if ((s = orth_rows(c, nb, zv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(), kpp.data(),
-                               lenN.data(), sN.data(), cN.data(), 1, bf ? zbv.data() : nullptr, nullptr, &conv)))
+            if ((s = orth_rows(c, nb, zv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
+                               kpp.data(), lenN.data(), sN.data(), cN.data(), 1, bf ? zbv.data() : nullptr, nullptr,
+                               &conv)))
                 return s;
             if (!conv && (s = to_bf(false, false))) return s;
             if ((s = xm(false))) return s;                                                  // Y = A Z
             const bool last = q + 1 == cfg.power_iters;
-            if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(), kpp.data(),
-                               lenT.data(), sT.data(), cT.data(), last ? 2 : 1, qh_out,
+            if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
+                               kpp.data(), lenT.data(), sT.data(), cT.data(), last ? 2 : 1, qh_out,
                                (bf && last) ? qlv.data() : nullptr, &conv)))
                 return s;
         }
@@ -716,79 +784,98 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
         if ((s = xtq(true))) return s;                                                      // B = Q^T A (hi + lo)
         // W = B B^T, eig
         {
-            SymGramBatch gb{};
-            ReduceBatch rb{};
             int maxK = 0, maxS = 0;
             int64_t maxCount = 0;
             for (int i = 0; i < nb; ++i) {
-                SymGramItem &g = gb.it[gb.n++];
-                g.y = zv[i]; g.part = gpart[i]; g.k = D[i].k; g.kp = D[i].kp; g.len = D[i].n; g.ldy = D[i].n;
-                g.chunk = D[i].gN_chunk; g.nsplit = D[i].gN_split;
-                ReduceItem &r = rb.it[rb.n++];
-                r.part = gpart[i]; r.out = F(S[i].wmat); r.stride = (int64_t)D[i].kp * D[i].kp;
-                r.count = r.stride; r.nsplit = g.nsplit;
-                maxK = std::max(maxK, D[i].k); maxS = std::max(maxS, g.nsplit);
-                maxCount = std::max(maxCount, r.count);
+                maxK = std::max(maxK, D[i].k);
+                maxS = std::max(maxS, D[i].gN_split);
+                maxCount = std::max<int64_t>(maxCount, (int64_t)D[i].kp * D[i].kp);
             }
-            HIPCHK(panel_grams(gb, maxK, maxS, c.st), "B B^T");
-            HIPCHK(launch_reduce(rb, maxCount, c.st), "B B^T reduce");
+            HIPCHK((sliced<SymGramBatch, kMaxBatch>(
+                       nb,
+                       [&](SymGramBatch &b, int i) {
+                           SymGramItem &g = b.it[b.n++];
+                           g.y = zv[i]; g.part = gpart[i]; g.k = D[i].k; g.kp = D[i].kp; g.len = D[i].n;
+                           g.ldy = D[i].n; g.chunk = D[i].gN_chunk; g.nsplit = D[i].gN_split;
+                       },
+                       [&](const SymGramBatch &b) { return panel_grams(b, maxK, maxS, c.st); })),
+                   "B B^T");
+            HIPCHK((sliced<ReduceBatch, kMaxBatch>(
+                       nb,
+                       [&](ReduceBatch &b, int i) {
+                           ReduceItem &r = b.it[b.n++];
+                           r.part = gpart[i]; r.out = F(S[i].wmat); r.stride = (int64_t)D[i].kp * D[i].kp;
+                           r.count = r.stride; r.nsplit = D[i].gN_split;
+                       },
+                       [&](const ReduceBatch &b) { return launch_reduce(b, maxCount, c.st); })),
+                   "B B^T reduce");
             for (int i = 0; i < nb; ++i)
                 eigs.push_back(EigReq{F(S[i].wmat), D[i].kp, D[i].k, F(S[i].vmat), D[i].kp,
-                                      reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),
-                                      reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i],
+                                      reinterpret_cast<float *>(W(fo[i].lam_t)),
+                                      reinterpret_cast<int *>(W(fo[i].sweeps)) + 1, &S[i],
                                       S[i].etri != SIZE_MAX ? F(S[i].etri) : nullptr});
             if ((s = feature_gram())) return s;
             jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv, wide_ok);
             if (es) return es;
         }
         // U_t^T = U~^T Q, P = U~^T B, lambda_t
-        {
-            GemmBatch gu{}, gp{};
+        if (pl.rt_max > 0) {
             int maxN = 0, maxNn = 0;
             for (int i = 0; i < nb; ++i) {
-                GemmItem &g = gu.it[gu.n++];
-                g.a = F(S[i].vmat); g.b = yv[i]; g.c = reinterpret_cast<float *>(ws + pl.item[i0 + i].ut);
-                g.a_i = 1; g.a_k = D[i].kp; g.b_k = D[i].T; g.b_j = 1; g.c_i = D[i].T; g.c_j = 1; g.c_split = 0;
-                g.M = pl.rt_max; g.N = D[i].T; g.K = D[i].k; g.kchunk = D[i].k; g.nsplit = 1; g.nb = 1;
-                GemmItem &q = gp.it[gp.n++];
-                q.a = F(S[i].vmat); q.b = zv[i]; q.c = F(S[i].pmat);
-                q.a_i = 1; q.a_k = D[i].kp; q.b_k = D[i].n; q.b_j = 1; q.c_i = D[i].n; q.c_j = 1; q.c_split = 0;
-                q.M = pl.rt_max; q.N = D[i].n; q.K = D[i].k; q.kchunk = D[i].k; q.nsplit = 1; q.nb = 1;
-                maxN = std::max(maxN, D[i].T); maxNn = std::max(maxNn, D[i].n);
+                maxN = std::max(maxN, D[i].T);
+                maxNn = std::max(maxNn, D[i].n);
             }
-            if (pl.rt_max > 0) {
-                HIPCHK(launch_gemm(gu, pl.rt_max, maxN, 1, 1, c.st), "U_t");
-                HIPCHK(launch_gemm(gp, pl.rt_max, maxNn, 1, 1, c.st), "P");
-            }
+            HIPCHK((sliced<GemmBatch, kMaxBatch>(
+                       nb,
+                       [&](GemmBatch &b, int i) {
+                           GemmItem &g = b.it[b.n++];
+                           g.a = F(S[i].vmat); g.b = yv[i]; g.c = reinterpret_cast<float *>(W(fo[i].ut));
+                           g.a_i = 1; g.a_k = D[i].kp; g.b_k = D[i].T; g.b_j = 1; g.c_i = D[i].T; g.c_j = 1;
+                           g.c_split = 0; g.a_z = g.b_z = g.c_z = 0;
+                           g.M = pl.rt_max; g.N = D[i].T; g.K = D[i].k; g.kchunk = D[i].k; g.nsplit = 1; g.nb = 1;
+                       },
+                       [&](const GemmBatch &b) { return launch_gemm(b, pl.rt_max, maxN, 1, 1, c.st); })),
+                   "U_t");
+            HIPCHK((sliced<GemmBatch, kMaxBatch>(
+                       nb,
+                       [&](GemmBatch &b, int i) {
+                           GemmItem &q = b.it[b.n++];
+                           q.a = F(S[i].vmat); q.b = zv[i]; q.c = F(S[i].pmat);
+                           q.a_i = 1; q.a_k = D[i].kp; q.b_k = D[i].n; q.b_j = 1; q.c_i = D[i].n; q.c_j = 1;
+                           q.c_split = 0; q.a_z = q.b_z = q.c_z = 0;
+                           q.M = pl.rt_max; q.N = D[i].n; q.K = D[i].k; q.kchunk = D[i].k; q.nsplit = 1; q.nb = 1;
+                       },
+                       [&](const GemmBatch &b) { return launch_gemm(b, pl.rt_max, maxNn, 1, 1, c.st); })),
+                   "P");
         }
     } else {
         // exact token factor: eigenvectors of G_t = A A^T (T x T)
-        XmBatch xb{};
         int maxC = 0;
-        for (int i = 0; i < nb; ++i) {
-            XmItem &x = xb.it[xb.n++];
-            x.x = x_dev[i0 + i]; x.m = x_dev[i0 + i]; x.out = F(S[i].gt);
-            x.m_c = d; x.m_blk = (int64_t)D[i].T * d;
-            x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].T; x.ldo = D[i].T;
-            x.lh_split = D[i].LH; x.nsplit = 1;
-            maxC = std::max(maxC, x.ncols);
-        }
-        HIPCHK(launch_xm(xb, dt, d, maxT, maxC, 1, c.st), "token Gram");
+        for (int i = 0; i < nb; ++i) maxC = std::max(maxC, D[i].T);
+        HIPCHK((sliced<XmBatch, kMaxBatch>(
+                   nb,
+                   [&](XmBatch &b, int i) {
+                       XmItem &x = b.it[b.n++];
+                       x.x = x_dev[i0 + i]; x.m = x_dev[i0 + i]; x.out = F(S[i].gt);
+                       x.m_c = d; x.m_blk = (int64_t)D[i].T * d;
+                       x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].T; x.ldo = D[i].T;
+                       x.lh_split = D[i].LH; x.nsplit = 1;
+                   },
+                   [&](const XmBatch &b) { return launch_xm(b, dt, d, maxT, maxC, 1, c.st); })),
+               "token Gram");
         for (int i = 0; i < nb; ++i)
             eigs.push_back(EigReq{F(S[i].gt), D[i].T, D[i].T, F(S[i].vt), D[i].T,
-                                  reinterpret_cast<float *>(ws + pl.item[i0 + i].lam_t),
-                                  reinterpret_cast<int *>(ws + pl.item[i0 + i].sweeps) + 1, &S[i],
+                                  reinterpret_cast<float *>(W(fo[i].lam_t)),
+                                  reinterpret_cast<int *>(W(fo[i].sweeps)) + 1, &S[i],
                                   S[i].etri != SIZE_MAX ? F(S[i].etri) : nullptr});
         if (jolt_status fs = feature_gram()) return fs;
         jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv, wide_ok);
         if (es) return es;
         // U_t^T rows = leading eigenvectors; P = U_t^T A (hi + lo split for bf16 caches)
-        XtqBatch qb{};
-        ReduceBatch rb{};
         int maxS = 0, maxCols = 0;
         int64_t maxCount = 0;
         for (int i = 0; i < nb; ++i) {
-            float *ut = reinterpret_cast<float *>(ws + pl.item[i0 + i].ut);
+            float *ut = reinterpret_cast<float *>(W(fo[i].ut));
             HIPCHK(launch_transpose(F(S[i].vt), ut, D[i].T, pl.rt_max, D[i].T, D[i].T, c.st), "U_t");
             const int64_t rows_pad = (int64_t)D[i].rtp32 * D[i].T;
             if (bf) {
@@ -802,71 +889,86 @@ jolt_status run_chunk_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                 HIPCHK(hipMemcpyAsync(P(S[i].uh), ut, (size_t)pl.rt_max * D[i].T * 4, hipMemcpyDeviceToDevice, c.st),
                        "U_t copy");
             }
-            XtqItem &x = qb.it[qb.n++];
-            x.x = x_dev[i0 + i]; x.qh = P(S[i].uh); x.ql = bf ? (const void *)P(S[i].ul) : nullptr;
-            x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].rtp32; x.ldq = D[i].T;
-            x.tsplit = D[i].xs_tsplit; x.nsplit = D[i].xs_split;
-            x.out = x.nsplit == 1 ? F(S[i].pmat) : F(S[i].xpart);
-            maxS = std::max(maxS, x.nsplit);
-            maxCols = std::max(maxCols, x.ncols);
-            if (x.nsplit > 1) {
-                ReduceItem &r = rb.it[rb.n++];
-                r.part = F(S[i].xpart); r.out = F(S[i].pmat);
-                r.stride = (int64_t)D[i].rtp32 * D[i].n; r.count = r.stride; r.nsplit = x.nsplit;
-                maxCount = std::max(maxCount, r.count);
-            }
+            maxS = std::max(maxS, D[i].xs_split);
+            maxCols = std::max(maxCols, D[i].rtp32);
+            maxCount = std::max<int64_t>(maxCount, (int64_t)D[i].rtp32 * D[i].n);
         }
         if (pl.rt_max > 0) {
-            HIPCHK(launch_xtq(qb, dt, d, maxLH, maxS, maxCols, c.st), "U_t^T A");
-            HIPCHK(launch_reduce(rb, maxCount, c.st), "U_t^T A reduce");
+            HIPCHK((sliced<XtqBatch, kMaxBatch>(
+                       nb,
+                       [&](XtqBatch &b, int i) {
+                           XtqItem &x = b.it[b.n++];
+                           x.x = x_dev[i0 + i]; x.qh = P(S[i].uh); x.ql = bf ? (const void *)P(S[i].ul) : nullptr;
+                           x.T = D[i].T; x.LH = D[i].LH; x.ncols = D[i].rtp32; x.ldq = D[i].T;
+                           x.tsplit = D[i].xs_tsplit; x.nsplit = D[i].xs_split;
+                           x.out = x.nsplit == 1 ? F(S[i].pmat) : F(S[i].xpart);
+                       },
+                       [&](const XtqBatch &b) { return launch_xtq(b, dt, d, maxLH, maxS, maxCols, c.st); })),
+                   "U_t^T A");
+            HIPCHK((sliced<ReduceBatch, kMaxBatch>(
+                       nb,
+                       [&](ReduceBatch &b, int i) {
+                           if (D[i].xs_split <= 1) return;
+                           ReduceItem &r = b.it[b.n++];
+                           r.part = F(S[i].xpart); r.out = F(S[i].pmat);
+                           r.stride = (int64_t)D[i].rtp32 * D[i].n; r.count = r.stride; r.nsplit = D[i].xs_split;
+                       },
+                       [&](const ReduceBatch &b) { return launch_reduce(b, maxCount, c.st); })),
+                   "U_t^T A reduce");
         }
     }
 
     // core[lh] = P[:, lh d : lh d + d] U_f, energy
     HIPCHK(hipStreamWaitEvent(c.st, join, 0), "join");
     if (pl.rt_max > 0) {
-        GemmBatch gb{};
         int maxNb = 0;
-        for (int i = 0; i < nb; ++i) {
-            GemmItem &g = gb.it[gb.n++];
-            g.a = F(S[i].pmat); g.b = reinterpret_cast<const float *>(ws + pl.item[i0 + i].uf);
-            g.c = reinterpret_cast<float *>(ws + pl.item[i0 + i].core);
-            g.a_i = D[i].n; g.a_k = 1; g.b_k = d; g.b_j = 1; g.c_i = d; g.c_j = 1; g.c_split = 0;
-            g.a_z = d; g.b_z = 0; g.c_z = (int64_t)pl.rt_max * d;
-            g.M = pl.rt_max; g.N = d; g.K = d; g.kchunk = d; g.nsplit = 1; g.nb = D[i].LH;
-            maxNb = std::max(maxNb, g.nb);
-        }
-        HIPCHK(launch_gemm(gb, pl.rt_max, d, 1, maxNb, c.st), "core");
-        SmallBatch eb{};
-        for (int i = 0; i < nb; ++i) {
-            SmallItem &t = eb.it[eb.n++];
-            t.in = reinterpret_cast<const float *>(ws + pl.item[i0 + i].core);
-            t.out32 = reinterpret_cast<float *>(ws + pl.item[i0 + i].energy);
-            t.a = D[i].LH; t.b = pl.rt_max; t.c = d;
-        }
-        HIPCHK(launch_energy_batch(eb, (int64_t)pl.rt_max * d, c.st), "energy");
-        GridBatch gbt{};
-        for (int i = 0; i < nb; ++i) {
-            GridItem &g = gbt.it[gbt.n++];
-            g.E = reinterpret_cast<const float *>(ws + pl.item[i0 + i].energy);
-            g.S = reinterpret_cast<double *>(ws + pl.item[i0 + i].grid);
-            g.s_fixed = reinterpret_cast<double *>(ws + pl.item[i0 + i].sfixed);
-            g.d = d; g.step = pl.step; g.nr = pl.grid_nr; g.nf = pl.grid_nf;
-            g.frt = cfg.budget_bytes < 0 ? std::min(cfg.fixed_rt, pl.rt_max) : 0;
-            g.frf = cfg.budget_bytes < 0 ? std::min(cfg.fixed_rf, d) : 0;
-        }
-        HIPCHK(launch_energy_grid(gbt, c.st), "energy grid");
+        for (int i = 0; i < nb; ++i) maxNb = std::max(maxNb, D[i].LH);
+        HIPCHK((sliced<GemmBatch, kMaxBatch>(
+                   nb,
+                   [&](GemmBatch &b, int i) {
+                       GemmItem &g = b.it[b.n++];
+                       g.a = F(S[i].pmat); g.b = reinterpret_cast<const float *>(W(fo[i].uf));
+                       g.c = reinterpret_cast<float *>(W(fo[i].core));
+                       g.a_i = D[i].n; g.a_k = 1; g.b_k = d; g.b_j = 1; g.c_i = d; g.c_j = 1; g.c_split = 0;
+                       g.a_z = d; g.b_z = 0; g.c_z = (int64_t)pl.rt_max * d;
+                       g.M = pl.rt_max; g.N = d; g.K = d; g.kchunk = d; g.nsplit = 1; g.nb = D[i].LH;
+                   },
+                   [&](const GemmBatch &b) { return launch_gemm(b, pl.rt_max, d, 1, maxNb, c.st); })),
+               "core");
+        HIPCHK((sliced<SmallBatch, kMaxBatch>(
+                   nb,
+                   [&](SmallBatch &b, int i) {
+                       SmallItem &t = b.it[b.n++];
+                       t.in = reinterpret_cast<const float *>(W(fo[i].core));
+                       t.out32 = reinterpret_cast<float *>(W(fo[i].energy));
+                       t.a = D[i].LH; t.b = pl.rt_max; t.c = d;
+                   },
+                   [&](const SmallBatch &b) { return launch_energy_batch(b, (int64_t)pl.rt_max * d, c.st); })),
+               "energy");
+        HIPCHK((sliced<GridBatch, kMaxBatch>(
+                   nb,
+                   [&](GridBatch &b, int i) {
+                       GridItem &g = b.it[b.n++];
+                       g.E = reinterpret_cast<const float *>(W(fo[i].energy));
+                       g.S = reinterpret_cast<double *>(W(fo[i].grid));
+                       g.s_fixed = reinterpret_cast<double *>(W(fo[i].sfixed));
+                       g.d = d; g.step = pl.step; g.nr = pl.grid_nr; g.nf = pl.grid_nf;
+                       g.frt = cfg.budget_bytes < 0 ? std::min(cfg.fixed_rt, pl.rt_max) : 0;
+                       g.frf = cfg.budget_bytes < 0 ? std::min(cfg.fixed_rf, d) : 0;
+                   },
+                   [&](const GridBatch &b) { return launch_energy_grid(b, c.st); })),
+               "energy grid");
     }
     return JOLT_OK;
 }
 
-// One chunk of the plan.  Work forked onto the side stream reads the inputs and
+// One group of the plan.  Work forked onto the side stream reads the inputs and
 // writes the workspace, so an error after the fork waits for that stream
 // before returning: everything launched has finished when jolt_plan returns.
-jolt_status run_chunk(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items, int i0,
+jolt_status run_group(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items, int i0,
                       int nb, const void *const *x_dev, uint8_t *ws, bool *noconv, bool wide_ok) {
     hipStream_t forked = nullptr;
-    jolt_status s = run_chunk_body(c, cfg, pl, items, i0, nb, x_dev, ws, noconv, wide_ok, &forked);
+    jolt_status s = run_group_body(c, cfg, pl, items, i0, nb, x_dev, ws, noconv, wide_ok, &forked);
     if (s != JOLT_OK && forked) (void)hipStreamSynchronize(forked);
     return s;
 }
@@ -933,9 +1035,9 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     static const bool timing = getenv("JOLT_TIMING") != nullptr;
     static const bool debug = getenv("JOLT_DEBUG") != nullptr;
     const auto t_start = std::chrono::steady_clock::now();
-    for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
-        const int nb = std::min(kMaxBatch, n - c0);
-        s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv, true);
+    for (int c0 = 0; c0 < n; c0 += kPlanGroup) {
+        const int nb = std::min(kPlanGroup, n - c0);
+        s = run_group(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv, true);
         if (s) return s;
     }
     // energy tables, ||X||^2 and sweep counters back to the host (the one synchronisation)
@@ -952,8 +1054,8 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
     // again: the only case with more than one synchronisation
     {
         bool again = false;
-        for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
-            const int nb = std::min(kMaxBatch, n - c0);
+        for (int c0 = 0; c0 < n; c0 += kPlanGroup) {
+            const int nb = std::min(kPlanGroup, n - c0);
             bool redo = false;
             for (int i = c0; i < c0 + nb; ++i) {
                 int sw[2];
@@ -962,7 +1064,7 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
             }
             if (!redo) continue;
             if (debug) fprintf(stderr, "libjolt: items %d..%d planned again with block Jacobi\n", c0, c0 + nb - 1);
-            s = run_chunk(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv, false);
+            s = run_group(c, *cfg, pl, items, c0, nb, x_dev, ws, &noconv, false);
             if (s) return s;
             again = true;
         }

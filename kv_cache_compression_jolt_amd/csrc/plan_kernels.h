@@ -87,7 +87,7 @@ struct CholItem {
     int inverse;
     float *work;         // k > kCholInverseMaxK: P x P device scratch (P = k rounded up to 32)
 };
-struct CholBatch { CholItem it[kMaxBatch]; int n; };
+struct CholBatch { CholItem it[kSolverBatch]; int n; };
 hipError_t launch_cholesky(const CholBatch &b, int maxK, hipStream_t s);
 
 // rows 0..k-1 of y[k][len] <- L^{-1} y   (forward substitution, in place allowed)
@@ -118,7 +118,7 @@ struct JacItem {
     int *sweeps_out;     // sweeps used, or -1 if the cap was hit
     float *tw;           // tridiagonal solver only: eig_tri_ws_bytes(n) of device workspace
 };
-struct JacBatch { JacItem it[64]; int n; };
+struct JacBatch { JacItem it[kSolverBatch]; int n; };
 constexpr int kJacobiMaxN = 142;
 // retry_only: solve only the items whose sweeps_out holds kEigRetry
 hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s, int retry_only = 0);
