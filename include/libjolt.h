@@ -159,6 +159,20 @@ jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jolt_item *it
                       const void *const *x_dev, void *plan_ws, size_t plan_ws_bytes,
                       void *stream, jolt_alloc *alloc_host, double *lambda_out);
 
+/* The allocation alone, under a new budget: reads back the energy tables that
+ * jolt_plan left in plan_ws for the same items (one device-to-host copy;
+ * synchronises `stream` once) and runs the single dual again.  The method
+ * picks ranks and residual bits per item under one byte budget from per-item
+ * distortion tables ("A JoLT for the KV cache", landing page abstract), so a
+ * new budget needs no new factorization.  cfg must be the configuration
+ * jolt_plan ran with, except budget_bytes (>= 0 here) and delta_b; the
+ * factors in plan_ws stay valid for jolt_compress with the new allocation.
+ * Errors as jolt_plan (JOLT_E_INFEASIBLE: alloc_host holds the minimum-byte
+ * choices; JOLT_E_NOCONV: the plan's eigensolver status). */
+jolt_status jolt_replan(jolt_handle h, const jolt_config *cfg, const jolt_item *items, int32_t n,
+                        const void *plan_ws, size_t plan_ws_bytes, void *stream, jolt_alloc *alloc_host,
+                        double *lambda_out);
+
 /* Write each item's payload: header, stored Tucker parameters (rounded to the
  * item dtype) and the quantized rotated residual against the reconstruction
  * the decoder will form from those stored parameters.  plan_ws must hold the

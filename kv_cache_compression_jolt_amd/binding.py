@@ -53,7 +53,8 @@ class jolt_factor_view(C.Structure):
 EXPORTED = [
     "jolt_create", "jolt_destroy", "jolt_status_str", "jolt_last_error", "jolt_workspace_size",
     "jolt_item_bytes", "jolt_payload_size", "jolt_payload_layout", "jolt_payload_header",
-    "jolt_payload_validate", "jolt_plan", "jolt_compress", "jolt_encode_residual", "jolt_decompress",
+    "jolt_payload_validate", "jolt_plan", "jolt_replan", "jolt_compress", "jolt_encode_residual",
+    "jolt_decompress",
     "jolt_plan_factors", "jolt_plan_from_tables", "jolt_rotate", "jolt_quantize_pack",
     "jolt_unpack_dequant", "jolt_rademacher", "jolt_eigh", "jolt_eigh_workspace_size", "jolt_kernel_timer",
     "jolt_kernel_time",
@@ -85,6 +86,8 @@ def lib():
             "jolt_payload_validate": (I32, [P, C.POINTER(jolt_item), C.POINTER(jolt_alloc)]),
             "jolt_plan": (I32, [P, C.POINTER(jolt_config), C.POINTER(jolt_item), I32, C.POINTER(P), P, SZ, P,
                                 C.POINTER(jolt_alloc), C.POINTER(D)]),
+            "jolt_replan": (I32, [P, C.POINTER(jolt_config), C.POINTER(jolt_item), I32, P, SZ, P,
+                                  C.POINTER(jolt_alloc), C.POINTER(D)]),
             "jolt_compress": (I32, [P, C.POINTER(jolt_config), C.POINTER(jolt_item), I32, C.POINTER(P),
                                     C.POINTER(jolt_alloc), P, SZ, P, SZ, C.POINTER(P), P]),
             "jolt_encode_residual": (I32, [P, C.POINTER(jolt_item), I32, C.POINTER(P), C.POINTER(jolt_alloc),
@@ -181,6 +184,15 @@ def jolt_plan(h, cfg, items, x_ptrs, ws_ptr, ws_bytes, stream):
     lam = C.c_double()
     st = lib().jolt_plan(h, C.byref(cfg), _items(items), n, _ptrs(x_ptrs), C.c_void_p(ws_ptr), ws_bytes,
                          C.c_void_p(stream), allocs, C.byref(lam))
+    return st, [allocs[i] for i in range(n)], lam.value
+
+
+def jolt_replan(h, cfg, items, ws_ptr, ws_bytes, stream):
+    n = len(items)
+    allocs = (jolt_alloc * max(1, n))()
+    lam = C.c_double()
+    st = lib().jolt_replan(h, C.byref(cfg), _items(items), n, C.c_void_p(ws_ptr), ws_bytes, C.c_void_p(stream),
+                           allocs, C.byref(lam))
     return st, [allocs[i] for i in range(n)], lam.value
 
 
@@ -320,6 +332,16 @@ class Jolt:
     def plan(self, xs):
         st, allocs, lam = jolt_plan(self.h, self.cfg, self.items, [x.data_ptr() for x in xs],
                                     self.plan_ws.data_ptr(), self.plan_ws.numel(), stream_ptr())
+        if st not in (JOLT_OK, JOLT_E_INFEASIBLE, JOLT_E_NOCONV):
+            _check(st, self.h)
+        self.status, self.allocs, self.lam = st, allocs, lam
+        return allocs, lam
+
+    def replan(self, budget):
+        """The dual alone under a new budget, on this object's last plan."""
+        self.cfg.budget_bytes = int(budget)
+        st, allocs, lam = jolt_replan(self.h, self.cfg, self.items, self.plan_ws.data_ptr(), self.plan_ws.numel(),
+                                      stream_ptr())
         if st not in (JOLT_OK, JOLT_E_INFEASIBLE, JOLT_E_NOCONV):
             _check(st, self.h)
         self.status, self.allocs, self.lam = st, allocs, lam

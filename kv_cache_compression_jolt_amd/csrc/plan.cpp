@@ -1009,6 +1009,91 @@ jolt_status store_params(jolt_handle h, const PlanLayout &pl, const jolt_item *i
 
 using namespace jolt;
 
+// The allocation from a plan's host copy of its readback block (energy grids,
+// ||X||^2, eigensolver status): fixed ranks, or the single dual under
+// cfg.budget_bytes.  Shared by jolt_plan and jolt_replan.
+static jolt_status allocate_from_readback(jolt_handle h, const jolt_config &cfg, const jolt_item *items, int n,
+                                          const PlanLayout &pl, const uint8_t *rb, jolt_alloc *alloc_host,
+                                          double *lambda_out, bool *noconv) {
+    static const bool debug = getenv("JOLT_DEBUG") != nullptr;
+    const int rt_max = pl.rt_max;
+    const size_t cells = (size_t)std::max(pl.grid_nr * pl.grid_nf, 1);
+    std::vector<const double *> grid(n);
+    std::vector<double> nx2(n), sfix(n);
+    for (int i = 0; i < n; ++i) {
+        grid[i] = reinterpret_cast<const double *>(rb + (pl.item[i].grid - pl.readback));
+        (void)cells;
+        std::memcpy(&sfix[i], rb + (pl.item[i].sfixed - pl.readback), 8);
+        std::memcpy(&nx2[i], rb + (pl.item[i].normx2 - pl.readback), 8);
+        int sw[2];
+        std::memcpy(sw, rb + (pl.item[i].sweeps - pl.readback), 8);
+        if (sw[0] < 0 || sw[1] < 0) *noconv = true;
+        if (debug) fprintf(stderr, "libjolt: item %d eig sweeps feature %d token %d\n", i, sw[0], sw[1]);
+    }
+
+    const int rf_max = pl.rf_max;
+    if (cfg.budget_bytes < 0) {
+        for (int i = 0; i < n; ++i) {
+            jolt_alloc &a = alloc_host[i];
+            a.rt = cfg.fixed_rt; a.rf = cfg.fixed_rf; a.bits = cfg.fixed_bits; a.reserved = 0;
+            if (a.rt == 0 || a.rf == 0) a.rt = a.rf = 0;
+            a.bytes = jolt_item_bytes(&items[i], a.rt, a.rf, a.bits);
+            const double S = (a.rt == 0 || a.rf == 0) ? 0.0 : sfix[i];
+            a.distortion = std::max(0.0, nx2[i] - S);
+        }
+        if (lambda_out) *lambda_out = -1.0;
+        return JOLT_OK;
+    }
+    DualTables &dt = dual_tables(h);
+    if (dt.rt_max != rt_max || dt.rf_max != rf_max || dt.step != pl.step || dt.grid_nf != pl.grid_nf ||
+        dt.bits_mask != cfg.bits_mask || dt.dtype != items[0].dtype || dt.d != items[0].d ||
+        pl.step != cfg.rank_step) {
+        dt = DualTables{};
+        dt.rt_max = rt_max; dt.rf_max = rf_max; dt.step = pl.step; dt.grid_nf = pl.grid_nf;
+        dt.bits_mask = cfg.bits_mask; dt.dtype = items[0].dtype; dt.d = items[0].d;
+        dt.cand = candidate_grid(rt_max, rf_max, cfg.rank_step, cfg.bits_mask);
+        dt.cell.resize(dt.cand.size());
+        for (size_t j = 0; j < dt.cand.size(); ++j)
+            dt.cell[j] = (dt.cand[j].rt == 0 || dt.cand[j].rf == 0)
+                             ? -1 : (dt.cand[j].rt / pl.step - 1) * pl.grid_nf + (dt.cand[j].rf / pl.step - 1);
+    }
+    const std::vector<Cand> &cand = dt.cand;
+    const int nc = (int)cand.size();
+    // byte tables and their order, shared by the items of one shape (dtype and d
+    // are common to the call; L, H, T may differ).  Kept for at most 64 shapes
+    // between calls, so callers whose T changes every call do not grow the cache.
+    if (dt.shapes.size() > 64) dt.shapes.clear();
+    std::vector<int> shape_of(n);
+    for (int i = 0; i < n; ++i) {
+        int k = 0;
+        while (k < (int)dt.shapes.size() &&
+               !(dt.shapes[k].L == items[i].L && dt.shapes[k].H == items[i].H && dt.shapes[k].T == items[i].T))
+            ++k;
+        if (k == (int)dt.shapes.size()) {
+            std::vector<int64_t> B(nc);
+            for (int j = 0; j < nc; ++j) B[j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
+            dt.shapes.push_back(DualTables::Shape{items[i].L, items[i].H, items[i].T, sorted_cands(cand, dt.cell.data(), B.data())});
+        }
+        shape_of[i] = k;
+    }
+    std::vector<const SortedCands *> scp(n);
+    for (int i = 0; i < n; ++i) scp[i] = &dt.shapes[shape_of[i]].sc;
+    std::vector<int> choice(n);
+    std::vector<double> dist(n);
+    double lam = 0.0;
+    jolt_status s = allocate_sorted(n, scp.data(), grid.data(), nx2.data(), cfg.delta_b, cfg.budget_bytes, choice.data(),
+                        dist.data(), &lam);
+    for (int i = 0; i < n; ++i) {
+        const Cand &cc = cand[choice[i]];
+        alloc_host[i].rt = cc.rt; alloc_host[i].rf = cc.rf; alloc_host[i].bits = cc.bits; alloc_host[i].reserved = 0;
+        alloc_host[i].bytes = jolt_item_bytes(&items[i], cc.rt, cc.rf, cc.bits);
+        alloc_host[i].distortion = dist[i];
+    }
+    if (lambda_out) *lambda_out = lam;
+    if (s == JOLT_E_INFEASIBLE) return fail(h, s, "budget below the sum of minimum item bytes");
+    return JOLT_OK;
+}
+
 extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jolt_item *items, int32_t n,
                                  const void *const *x_dev, void *plan_ws, size_t plan_ws_bytes, void *stream,
                                  jolt_alloc *alloc_host, double *lambda_out) {
@@ -1084,82 +1169,42 @@ extern "C" jolt_status jolt_plan(jolt_handle h, const jolt_config *cfg, const jo
         fprintf(stderr, "libjolt plan: launch %.1f us, wait for device %.1f us, tables + dual %.1f us\n",
                 us(t_start, t_launched), us(t_launched, t_synced), us(t_synced, t_end));
     };
-    const size_t cells = (size_t)std::max(pl.grid_nr * pl.grid_nf, 1);
-    std::vector<const double *> grid(n);
-    std::vector<double> nx2(n), sfix(n);
-    for (int i = 0; i < n; ++i) {
-        grid[i] = reinterpret_cast<const double *>(rb + (pl.item[i].grid - pl.readback));
-        (void)cells;
-        std::memcpy(&sfix[i], rb + (pl.item[i].sfixed - pl.readback), 8);
-        std::memcpy(&nx2[i], rb + (pl.item[i].normx2 - pl.readback), 8);
-        int sw[2];
-        std::memcpy(sw, rb + (pl.item[i].sweeps - pl.readback), 8);
-        if (sw[0] < 0 || sw[1] < 0) noconv = true;
-        if (debug) fprintf(stderr, "libjolt: item %d eig sweeps feature %d token %d\n", i, sw[0], sw[1]);
-    }
-
-    const int rf_max = pl.rf_max;
-    if (cfg->budget_bytes < 0) {
-        for (int i = 0; i < n; ++i) {
-            jolt_alloc &a = alloc_host[i];
-            a.rt = cfg->fixed_rt; a.rf = cfg->fixed_rf; a.bits = cfg->fixed_bits; a.reserved = 0;
-            if (a.rt == 0 || a.rf == 0) a.rt = a.rf = 0;
-            a.bytes = jolt_item_bytes(&items[i], a.rt, a.rf, a.bits);
-            const double S = (a.rt == 0 || a.rf == 0) ? 0.0 : sfix[i];
-            a.distortion = std::max(0.0, nx2[i] - S);
-        }
-        if (lambda_out) *lambda_out = -1.0;
-        report();
-        return noconv ? fail(h, JOLT_E_NOCONV, "eigensolver hit its sweep cap") : JOLT_OK;
-    }
-    DualTables &dt = dual_tables(h);
-    if (dt.rt_max != rt_max || dt.rf_max != rf_max || dt.step != pl.step || dt.grid_nf != pl.grid_nf ||
-        dt.bits_mask != cfg->bits_mask || dt.dtype != items[0].dtype || dt.d != items[0].d ||
-        pl.step != cfg->rank_step) {
-        dt = DualTables{};
-        dt.rt_max = rt_max; dt.rf_max = rf_max; dt.step = pl.step; dt.grid_nf = pl.grid_nf;
-        dt.bits_mask = cfg->bits_mask; dt.dtype = items[0].dtype; dt.d = items[0].d;
-        dt.cand = candidate_grid(rt_max, rf_max, cfg->rank_step, cfg->bits_mask);
-        dt.cell.resize(dt.cand.size());
-        for (size_t j = 0; j < dt.cand.size(); ++j)
-            dt.cell[j] = (dt.cand[j].rt == 0 || dt.cand[j].rf == 0)
-                             ? -1 : (dt.cand[j].rt / pl.step - 1) * pl.grid_nf + (dt.cand[j].rf / pl.step - 1);
-    }
-    const std::vector<Cand> &cand = dt.cand;
-    const int nc = (int)cand.size();
-    // byte tables and their order, shared by the items of one shape (dtype and d
-    // are common to the call; L, H, T may differ).  Kept for at most 64 shapes
-    // between calls, so callers whose T changes every call do not grow the cache.
-    if (dt.shapes.size() > 64) dt.shapes.clear();
-    std::vector<int> shape_of(n);
-    for (int i = 0; i < n; ++i) {
-        int k = 0;
-        while (k < (int)dt.shapes.size() &&
-               !(dt.shapes[k].L == items[i].L && dt.shapes[k].H == items[i].H && dt.shapes[k].T == items[i].T))
-            ++k;
-        if (k == (int)dt.shapes.size()) {
-            std::vector<int64_t> B(nc);
-            for (int j = 0; j < nc; ++j) B[j] = jolt_item_bytes(&items[i], cand[j].rt, cand[j].rf, cand[j].bits);
-            dt.shapes.push_back(DualTables::Shape{items[i].L, items[i].H, items[i].T, sorted_cands(cand, dt.cell.data(), B.data())});
-        }
-        shape_of[i] = k;
-    }
-    std::vector<const SortedCands *> scp(n);
-    for (int i = 0; i < n; ++i) scp[i] = &dt.shapes[shape_of[i]].sc;
-    std::vector<int> choice(n);
-    std::vector<double> dist(n);
-    double lam = 0.0;
-    s = allocate_sorted(n, scp.data(), grid.data(), nx2.data(), cfg->delta_b, cfg->budget_bytes, choice.data(),
-                        dist.data(), &lam);
-    for (int i = 0; i < n; ++i) {
-        const Cand &cc = cand[choice[i]];
-        alloc_host[i].rt = cc.rt; alloc_host[i].rf = cc.rf; alloc_host[i].bits = cc.bits; alloc_host[i].reserved = 0;
-        alloc_host[i].bytes = jolt_item_bytes(&items[i], cc.rt, cc.rf, cc.bits);
-        alloc_host[i].distortion = dist[i];
-    }
-    if (lambda_out) *lambda_out = lam;
+    jolt_status ds = allocate_from_readback(h, *cfg, items, n, pl, rb, alloc_host, lambda_out, &noconv);
     report();
-    if (s == JOLT_E_INFEASIBLE) return fail(h, s, "budget below the sum of minimum item bytes");
+    if (ds) return ds;
+    if (noconv) return fail(h, JOLT_E_NOCONV, "eigensolver hit its sweep cap");
+    return JOLT_OK;
+}
+
+extern "C" jolt_status jolt_replan(jolt_handle h, const jolt_config *cfg, const jolt_item *items, int32_t n,
+                                   const void *plan_ws, size_t plan_ws_bytes, void *stream, jolt_alloc *alloc_host,
+                                   double *lambda_out) {
+    if (!h || !cfg) return JOLT_E_INVALID;
+    clear_err(h);
+    jolt_status s = check_items_uniform(h, items, n);
+    if (s) return s;
+    if (n == 0) return JOLT_OK;
+    if (!plan_ws || !alloc_host) return fail(h, JOLT_E_INVALID, "NULL array");
+    if (cfg->budget_bytes < 0) return fail(h, JOLT_E_INVALID, "replan: budget_bytes must be >= 0");
+    s = check_config(h, *cfg, items, n);
+    if (s) return s;
+    PlanLayout pl;
+    s = plan_layout(*cfg, items, n, &pl);
+    if (s) return fail(h, s, "layout");
+    if (plan_ws_bytes < pl.total)
+        return fail(h, JOLT_E_WORKSPACE, "plan workspace: need %zu bytes, have %zu", pl.total, plan_ws_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t rb_bytes = pl.readback_stride * n;
+    uint8_t *rb = nullptr;
+    hipError_t e = readback_buffer(h, rb_bytes, &rb);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(rb, static_cast<const uint8_t *>(plan_ws) + pl.readback, rb_bytes, hipMemcpyDeviceToHost,
+                           st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(h, e, "replan");
+    bool noconv = false;
+    s = allocate_from_readback(h, *cfg, items, n, pl, rb, alloc_host, lambda_out, &noconv);
+    if (s) return s;
     if (noconv) return fail(h, JOLT_E_NOCONV, "eigensolver hit its sweep cap");
     return JOLT_OK;
 }

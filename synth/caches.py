@@ -242,10 +242,11 @@ def _raw_worker(args):
         return make_item(cfg, spec, keep_x=False).raw
 
 
-def iter_raw_parallel(cfg: CacheConfig, specs: List[Item], workers: int = 0):
+def iter_raw_parallel(cfg: CacheConfig, specs: List[Item], workers: int = 0, start: str = "fork"):
     """Yield (index, stored bits) of every spec, in order, generated by a pool
-    of forked worker processes (the same values as make_item).  Call it before
-    anything initialises a GPU in this process: the workers are forked."""
+    of worker processes (the same values as make_item).  With start="fork"
+    call it before anything initialises a GPU in this process; "spawn" starts
+    fresh interpreters and is safe afterwards."""
     import multiprocessing as mp
     import os
     if workers <= 0:
@@ -255,7 +256,7 @@ def iter_raw_parallel(cfg: CacheConfig, specs: List[Item], workers: int = 0):
         for i, s in enumerate(specs):
             yield i, make_item(cfg, s, keep_x=False).raw
         return
-    ctx = mp.get_context("fork")
+    ctx = mp.get_context(start)
     with ctx.Pool(workers) as pool:
         for i, raw in enumerate(pool.imap(_raw_worker, [(cfg, s) for s in specs], chunksize=1)):
             yield i, raw

@@ -66,9 +66,33 @@ def _delta():
     return json.load(open(os.path.join(root, "tests", "golden", "delta_b.json")))["delta"]
 
 
+class _Lazy:
+    """An item whose fp64 values are formed from its stored bits on demand (the
+    largest workloads do not fit in host memory as fp64)."""
+
+    def __init__(self, spec, raw):
+        self.spec, self.raw = spec, raw
+        for k in ("item_id", "seed", "L", "H", "T", "d", "dtype"):
+            setattr(self, k, getattr(spec, k))
+
+    @property
+    def x(self):
+        return synth.bf16_bits_to_f64(self.raw)
+
+    def block(self, l, h, t0, t1):
+        return synth.bf16_bits_to_f64(self.raw[l:l + 1, h:h + 1, t0:t1])
+
+
 def _items(cfg, picks):
     specs = synth.item_specs(cfg)
-    return [synth.make_item(cfg, specs[i]) for i in picks]
+    sel = [specs[i] for i in picks]
+    if len(sel) <= 2:
+        return [synth.make_item(cfg, s) for s in sel]
+    print("generating", len(sel), "items", flush=True)
+    out = [None] * len(sel)
+    for i, raw in synth.iter_raw_parallel(cfg, sel, start="spawn"):
+        out[i] = _Lazy(sel[i], raw)
+    return out
 
 
 def _check_dual(torch, jb, J, cfg, items, allocs, budget):
@@ -103,7 +127,8 @@ def _check_dual(torch, jb, J, cfg, items, allocs, budget):
         assert abs(lg - lo) <= 1e-9 * (abs(lo) + 1.0), ("allocation differs from the oracle's dual", i, got, ref)
 
 
-def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=None):
+def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=None, replan_ratios=(),
+         binding_ratios=()):
     torch = torch_cuda()
     jb = jolt_binding()
     items = _items(cfg, picks)
@@ -119,6 +144,20 @@ def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=No
     assert J.status == jb.JOLT_OK, J.status
     assert sum(a.bytes for a in allocs) <= budget
     _check_dual(torch, jb, J, cfg, items, allocs, budget)
+    if ratio in binding_ratios:
+        assert lam > 0, ("the budget should bind", ratio)
+    # other budgets from the same factorization: the dual alone (jolt_replan)
+    for r2 in replan_ratios:
+        b2 = synth.budget_for_ratio(cfg, r2, n_items=len(items))
+        a2, lam2 = J.replan(b2)
+        assert J.status == jb.JOLT_OK, J.status
+        assert sum(a.bytes for a in a2) <= b2
+        print("replan", r2, "lambda", lam2, sorted(set((a.rt, a.rf, a.bits) for a in a2)), flush=True)
+        _check_dual(torch, jb, J, cfg, items, a2, b2)
+        if r2 in binding_ratios:
+            assert lam2 > 0, ("the budget should bind", r2)
+    if replan_ratios:
+        allocs, lam = J.replan(synth.budget_for_ratio(cfg, replan_ratios[-1], n_items=len(items)))
     rt_max = cfg.rt_max
     check = range(len(items)) if check_items is None else check_items
     factors = {}
@@ -133,7 +172,9 @@ def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=No
         nx2 = _fetch(torch, v.normx2, 1, np.float64)[0]
         E = _fetch(torch, v.energy, rt_max * d).reshape(rt_max, d).astype(np.float64)
         factors[i] = (Ut, Uf, lam_t, lam_f, E)
-        ref_nx2 = float(np.sum(it.x * it.x))
+        xi = it.x
+        ref_nx2 = float(np.sum(xi * xi))
+        del xi
         assert abs(nx2 / ref_nx2 - 1) < 1e-5, (nx2, ref_nx2)
         Ut64 = Ut.astype(np.float64)
         assert np.max(np.abs(Ut64 @ Ut64.T - np.eye(rt_max))) < 1e-3
@@ -178,7 +219,7 @@ def _run(cfg, picks, ratio, mode="randomized", blocks_per_item=2, check_items=No
         for _ in range(blocks_per_item):
             l, h = int(rng.integers(L)), int(rng.integers(H))
             t0 = int(rng.integers(0, T - ns + 1)) // 64 * 64
-            Xb = it.x[l:l + 1, h:h + 1, t0:t0 + ns]
+            Xb = it.block(l, h, t0, t0 + ns) if isinstance(it, _Lazy) else it.x[l:l + 1, h:h + 1, t0:t0 + ns]
             sp = ocodec.StoredParams(Ut=Ut_s[t0:t0 + ns], Uf=Uf_s, C=C_s[l:l + 1, h:h + 1])
             enc = ocodec.encode(Xb, sp, a.bits, it.seed, it.item_id, cfg.dtype)
             ref = ocodec.decode(enc, 1, 1, ns, d, it.seed, it.item_id, cfg.dtype)
@@ -224,20 +265,23 @@ def test_fullsize_llama2_13b_c3_item():
     _run(cfg, [0], 3.0)
 
 
-@pytest.mark.timeout(900)
-def test_fullsize_llama31_8b_c4_item():
-    """One 4 x 8 x 65536 x 128 item (537 MB), 2x."""
+@pytest.mark.timeout(1200)
+def test_fullsize_llama31_8b_c4_budget_sweep():
+    """All 16 items of 4 x 8 x 65536 x 128 (8.6 GB): one factorization, the
+    dual at 2x (jolt_plan) and again at 3x, 4x and 5x (jolt_replan), each equal
+    to the oracle's dual on the GPU's tables; the budget binds at 4x and 5x,
+    and the 5x allocation is compressed, decompressed and checked."""
     cfg = synth.config("llama31_8b_gqa_64k")
-    _run(cfg, [0], 2.0)
+    _run(cfg, list(range(cfg.n_items)), 2.0, blocks_per_item=1, check_items=[0, 15],
+         replan_ratios=(3.0, 4.0, 5.0), binding_ratios=(4.0, 5.0))
 
 
-@pytest.mark.timeout(900)
-def test_fullsize_moe_c5_items_shared_dual():
-    """18 items of 4 x 8 x 8192 x 128 from two sequences (different planted
-    token ranks) under one dual: crosses the 16-item launch batch."""
+@pytest.mark.timeout(1200)
+def test_fullsize_moe_c5_all_items_one_dual():
+    """All 256 items of 4 x 8 x 8192 x 128 (16 sequences with their own planted
+    token ranks, 17.2 GB) under one 2.5x dual, as the benchmark runs them."""
     cfg = synth.config("moe_gqa_batch16_8k")
-    picks = list(range(0, 9)) + list(range(cfg.items_per_sequence, cfg.items_per_sequence + 9))
-    _run(cfg, picks, 2.5, blocks_per_item=1, check_items=[0, 8, 9, 17])
+    _run(cfg, list(range(cfg.n_items)), 2.5, blocks_per_item=1, check_items=[0, 17, 130, 255])
 
 
 @pytest.mark.timeout(600)
