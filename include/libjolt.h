@@ -198,6 +198,20 @@ jolt_status jolt_decompress(jolt_handle h, const jolt_item *items, int32_t n, co
                             const void *const *payload_dev, void *codec_ws, size_t codec_ws_bytes,
                             void *const *out_dev, void *stream);
 
+/* jolt_decompress without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The W~ workspace is a fixed scratch
+ * array of 64 MiB that the library holds on every GPU it runs on until the
+ * process ends; this call allocates nothing.  The items of one call may need
+ * at most 64 MiB of it (L H d r_t' 4 bytes per item, r_t' = r_t rounded up to
+ * 16; 4 MiB for a 4 x 8 x T x 128 item at r_t = 256), else JOLT_E_WORKSPACE
+ * before any launch.  Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (different streams, or different host threads) race.
+ * Nothing in the array needs to start zeroed (each call writes all of what it
+ * reads).  Results are those of jolt_decompress. */
+jolt_status jolt_decompress_noalloc(jolt_handle h, const jolt_item *items, int32_t n, const jolt_alloc *alloc,
+                                    const void *const *payload_dev, void *const *out_dev, void *stream);
+
 /* ---- factor export (device pointers into plan_ws) ------------------------ */
 /* After jolt_plan: where item i's factors live in plan_ws (fp32, device):
  *   ut    rt_max x T   row r = token-factor column r (descending eigenvalue)

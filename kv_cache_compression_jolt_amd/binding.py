@@ -54,7 +54,7 @@ EXPORTED = [
     "jolt_create", "jolt_destroy", "jolt_status_str", "jolt_last_error", "jolt_workspace_size",
     "jolt_item_bytes", "jolt_payload_size", "jolt_payload_layout", "jolt_payload_header",
     "jolt_payload_validate", "jolt_plan", "jolt_replan", "jolt_compress", "jolt_encode_residual",
-    "jolt_decompress",
+    "jolt_decompress", "jolt_decompress_noalloc",
     "jolt_plan_factors", "jolt_plan_from_tables", "jolt_rotate", "jolt_quantize_pack",
     "jolt_unpack_dequant", "jolt_rademacher", "jolt_eigh", "jolt_eigh_workspace_size", "jolt_kernel_timer",
     "jolt_kernel_time",
@@ -94,6 +94,8 @@ def lib():
                                            P, SZ, C.POINTER(P), P]),
             "jolt_decompress": (I32, [P, C.POINTER(jolt_item), I32, C.POINTER(jolt_alloc), C.POINTER(P), P, SZ,
                                       C.POINTER(P), P]),
+            "jolt_decompress_noalloc": (I32, [P, C.POINTER(jolt_item), I32, C.POINTER(jolt_alloc), C.POINTER(P),
+                                              C.POINTER(P), P]),
             "jolt_plan_factors": (I32, [C.POINTER(jolt_config), C.POINTER(jolt_item), I32, P, I32,
                                         C.POINTER(jolt_factor_view)]),
             "jolt_plan_from_tables": (I32, [I32, C.POINTER(I32), C.POINTER(C.POINTER(I32)),
@@ -216,6 +218,13 @@ def jolt_decompress(h, items, allocs, pay_ptrs, codec_ptr, codec_bytes, out_ptrs
     arr = (jolt_alloc * max(1, n))(*allocs)
     _check(lib().jolt_decompress(h, _items(items), n, arr, _ptrs(pay_ptrs), C.c_void_p(codec_ptr), codec_bytes,
                                  _ptrs(out_ptrs), C.c_void_p(stream)), h)
+
+
+def jolt_decompress_noalloc(h, items, allocs, pay_ptrs, out_ptrs, stream):
+    n = len(items)
+    arr = (jolt_alloc * max(1, n))(*allocs)
+    _check(lib().jolt_decompress_noalloc(h, _items(items), n, arr, _ptrs(pay_ptrs), _ptrs(out_ptrs),
+                                         C.c_void_p(stream)), h)
 
 
 def jolt_plan_factors(cfg, items, plan_ptr, i) -> jolt_factor_view:

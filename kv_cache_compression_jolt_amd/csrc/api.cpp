@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -28,9 +29,34 @@ struct jolt_handle_s {
     uint8_t *readback = nullptr;    // pinned host memory for the plan's one readback
     size_t readback_cap = 0;
     float *sweep = nullptr;         // pinned host memory for block Jacobi's per-sweep norms
+    void *scratch = nullptr;        // this device's address of the fixed scratch array
 };
 
 namespace jolt {
+
+// ---------------------------------------------------------------- fixed device scratch
+// The W~ workspace of jolt_decompress_noalloc: a file-scope device array, one
+// copy per GPU for the life of the process.  Host code never uses the array's
+// name as an address: jolt_create takes each device's address of it once, with
+// that device current, and kernels get that address.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];
+
+static hipError_t scratch_address(int device, void **out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = p;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
 
 jolt_status fail(jolt_handle h, jolt_status s, const char *fmt, ...) {
     if (h) {
@@ -153,8 +179,12 @@ extern "C" jolt_status jolt_create(int hip_device, jolt_handle *out) {
     if (e != hipSuccess || hip_device < 0 || hip_device >= count) return JOLT_E_DEVICE;
     e = hipSetDevice(hip_device);
     if (e != hipSuccess) return JOLT_E_DEVICE;
+    void *sp = nullptr;
+    e = scratch_address(hip_device, &sp);      // the fixed scratch's address on this device
+    if (e != hipSuccess) return JOLT_E_DEVICE;
     jolt_handle h = new jolt_handle_s();
     h->device = hip_device;
+    h->scratch = sp;
     *out = h;
     return JOLT_OK;
 }
@@ -409,6 +439,30 @@ extern "C" jolt_status jolt_decompress(jolt_handle h, const jolt_item *items, in
     if (!h) return JOLT_E_INVALID;
     clear_err(h);
     return run_codec(h, false, items, n, nullptr, alloc, codec_ws, codec_ws_bytes,
+                     const_cast<void *const *>(payload_dev), out_dev, static_cast<hipStream_t>(stream));
+}
+
+extern "C" jolt_status jolt_decompress_noalloc(jolt_handle h, const jolt_item *items, int32_t n,
+                                               const jolt_alloc *alloc, const void *const *payload_dev,
+                                               void *const *out_dev, void *stream) {
+    if (!h) return JOLT_E_INVALID;
+    clear_err(h);
+    jolt_status s = check_items_uniform(h, items, n);
+    if (s) return s;
+    if (n == 0) return JOLT_OK;
+    if (!alloc) return fail(h, JOLT_E_INVALID, "NULL array");
+    std::vector<int> rts(n);
+    for (int i = 0; i < n; ++i) {
+        s = check_alloc(h, items[i], alloc[i]);
+        if (s) return s;
+        rts[i] = (alloc[i].rt == 0 || alloc[i].rf == 0) ? 0 : alloc[i].rt;
+    }
+    const size_t need = codec_ws_bytes_for(items, n, rts.data());
+    if (need > kNoAllocScratchBytes)
+        return fail(h, JOLT_E_WORKSPACE,
+                    "decompress_noalloc: these items need %zu bytes of scratch, above the fixed %zu (split the call "
+                    "or use jolt_decompress)", need, kNoAllocScratchBytes);
+    return run_codec(h, false, items, n, nullptr, alloc, h->scratch, kNoAllocScratchBytes,
                      const_cast<void *const *>(payload_dev), out_dev, static_cast<hipStream_t>(stream));
 }
 
