@@ -58,7 +58,7 @@ def _hip():
 
 
 def _plan_parity(cfg, n_items, mode, rt_max, ratio=None, fixed=None, oversample=10, sub_tol=1e-2,
-                 item_offset=0):
+                 item_offset=0, codec=True):
     torch = torch_cuda()
     jb = jolt_binding()
     specs = synth.item_specs(cfg)[item_offset:item_offset + n_items]
@@ -67,6 +67,7 @@ def _plan_parity(cfg, n_items, mode, rt_max, ratio=None, fixed=None, oversample=
     budget = synth.budget_for_ratio(cfg, ratio, n_items=n_items) if ratio else None
     p = opipe.Params(mode=mode, rt_max=rt_max, oversample=oversample, budget=budget, fixed=fixed, delta=DELTA,
                      bits=cfg.bits)
+    print("oracle plan", cfg.name, (cfg.L, cfg.H, cfg.T, cfg.d), mode, n_items, "items", flush=True)
     ref = opipe.plan([i.x for i in items], [i.seed for i in items], [i.item_id for i in items], cfg.dtype, p)
     jitems = [jb.make_item(L, H, T, d, cfg.dtype, i.item_id, i.seed) for i in items]
     jcfg = jb.make_config(mode, rt_max=rt_max, oversample=oversample, bits=cfg.bits,
@@ -97,6 +98,9 @@ def _plan_parity(cfg, n_items, mode, rt_max, ratio=None, fixed=None, oversample=
         for r in _gap_blocks(f.lam_t):
             assert _sine(Ut[:, :r], f.U_t[:, :r]) <= sub_tol, ("token", r)
         assert np.max(np.abs(E - f.E)) <= 1e-3 * f.E.max()
+    if not codec:
+        J.close()
+        return allocs, ref
     pays = J.alloc_payloads(allocs)
     J.compress(xs, pays, allocs)
     outs = [torch.empty_like(x) for x in xs]
@@ -138,3 +142,27 @@ def test_randomized_wide_sketch():
     """k = 256 + 10 > 142: the small SVD goes through block Jacobi."""
     cfg = synth.config("llama2_13b_mha_4k", L=2, H=4, T=1024)
     _plan_parity(cfg, 2, "randomized", 256, ratio=3.0)
+
+
+# ---------------------------------------------------------------- full item sizes, free running
+@pytest.mark.timeout(900)
+def test_fullsize_free_running_llama2_13b_item():
+    """One whole 4 x 40 x 4096 x 128 item (k = 266), each side with its own
+    factors: eigenvalues, energy table, subspaces where the gap allows, and the
+    reconstruction error."""
+    _plan_parity(synth.config("llama2_13b_mha_4k"), 1, "randomized", 256, ratio=3.0)
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_free_running_mistral_exact_items():
+    """Two whole 4 x 8 x 1024 x 128 items in exact token mode (1024 x 1024 token
+    Gram): the oracle's fp64 Jacobi against the GPU's block Jacobi."""
+    _plan_parity(synth.config("mistral7b_gqa_1k"), 2, "exact", 128, ratio=2.0)
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_free_running_llama31_8b_item():
+    """One whole 4 x 8 x 65536 x 128 item (537 MB): factors, eigenvalues and the
+    energy table against the oracle's own (the codec on this shape is covered
+    by the full-size sampled-block tests)."""
+    _plan_parity(synth.config("llama31_8b_gqa_64k"), 1, "randomized", 256, ratio=2.0, codec=False)
