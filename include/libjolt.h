@@ -147,10 +147,15 @@ jolt_status jolt_payload_header(const jolt_item *item, const jolt_alloc *a, void
 jolt_status jolt_payload_validate(const void *header64, const jolt_item *item, const jolt_alloc *a);
 
 /* ---- the three calls ----------------------------------------------------- */
-/* Factor every item (feature Gram + eigensolve; exact or randomized token
- * factor; core and energy table), synchronise once, build the distortion and
- * byte tables and run the single-dual allocation (bisection over the
- * breakpoints of lambda).  x_dev[i] points to item i's X.  On return
+/* Factor every item and allocate.  The method factors a grouped prefill cache
+ * by a partial Tucker decomposition along the token and feature modes, the
+ * token factor by an exact SVD or by FlashJoLT's randomized approximation, and
+ * picks Tucker ranks and residual bits with a single Lagrangian dual per layer
+ * group, K and V separately, under one global byte budget ("A JoLT for the KV
+ * cache", paper landing page, abstract; author page, abstract).  Here: feature
+ * Gram + eigensolve; exact or randomized token factor; core and energy table;
+ * one synchronisation; the distortion and byte tables and the single-dual
+ * allocation (the breakpoints of lambda).  x_dev[i] points to item i's X.  On return
  * alloc_host[i] holds item i's allocation and *lambda_out the dual (0 when the
  * unconstrained optimum fits, -1 in fixed-rank mode).  The factors stay in
  * plan_ws for jolt_compress.  JOLT_E_INFEASIBLE: alloc_host holds the
@@ -175,7 +180,10 @@ jolt_status jolt_replan(jolt_handle h, const jolt_config *cfg, const jolt_item *
 
 /* Write each item's payload: header, stored Tucker parameters (rounded to the
  * item dtype) and the quantized rotated residual against the reconstruction
- * the decoder will form from those stored parameters.  plan_ws must hold the
+ * the decoder will form from those stored parameters.  The method captures
+ * the truncation residual with a rotated low-bit quantizer, the rotation a
+ * Johnson-Lindenstrauss one (paper landing page, abstract; author page,
+ * abstract).  plan_ws must hold the
  * jolt_plan results for the same (cfg, items).  payload_dev[i] must have
  * jolt_payload_size() bytes. */
 jolt_status jolt_compress(jolt_handle h, const jolt_config *cfg, const jolt_item *items, int32_t n,
@@ -191,8 +199,11 @@ jolt_status jolt_encode_residual(jolt_handle h, const jolt_item *items, int32_t 
                                  void *codec_ws, size_t codec_ws_bytes, void *const *payload_dev,
                                  void *stream);
 
-/* Rebuild every item's dense X~ = U_t round(C U_f^T) + rotate^T(dequant(codes))
- * into out_dev[i] (item dtype, [L][H][T][d]).  Reads only the payloads; the
+/* Rebuild every item's dense X~ = U_t (C U_f^T) + rotate^T(dequant(codes))
+ * into out_dev[i] (item dtype, [L][H][T][d]); the method's errors are those of
+ * this reconstruction (author page, abstract: relative Frobenius error).
+ * C U_f^T is held as a bf16 hi + lo pair (about 2^-16 relative) for bf16
+ * items, in fp32 for fp32 items.  Reads only the payloads; the
  * device header is not read (validate a host copy with jolt_payload_validate). */
 jolt_status jolt_decompress(jolt_handle h, const jolt_item *items, int32_t n, const jolt_alloc *alloc,
                             const void *const *payload_dev, void *codec_ws, size_t codec_ws_bytes,

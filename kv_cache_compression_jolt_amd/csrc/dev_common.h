@@ -3,12 +3,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Phase timestamps for one workgroup of a kernel: a no-op unless a
-// measurement build defines JOLT_PROBE(slot) to record the cycle counter.
-#ifndef JOLT_PROBE
-#define JOLT_PROBE(slot) ((void)0)
-#endif
-
 namespace jolt {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

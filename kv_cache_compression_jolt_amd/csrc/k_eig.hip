@@ -207,7 +207,6 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     constexpr int PS = kPanelStride;
     float *Vp = B1, *Wp = B1 + poff;
 
-    JOLT_PROBE(0);
     // (A + A^T) / 2, eight entries of each thread in flight
     for (int e0 = tid; e0 < n * n; e0 += 8 * kThreads) {
         float x[8], y[8];
@@ -237,7 +236,6 @@ __global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld
     //   w = p - (tau p^T v / 2) v,  p = tau (A22 - V W^T - W V^T) v
     // to W, with p^T v = tau (v^T A22 v - 2 (W^T v) . (V^T v)).  At the end of
     // the panel A22 -= V W^T + W V^T on MFMA.  Reflector j is kept in row j.
-    JOLT_PROBE(1);
     float *sxa = sx0, *sxb = sx1;
     // Within a panel A22 is read-only, so each lane keeps its share in
     // registers for the panel's steps: lane l32 of half h of wave w holds
@@ -1373,7 +1371,6 @@ __global__ __launch_bounds__(kThreads) void k_eig_polish(JacBatch batch, int ld,
     // V <- V (3 I - V^T V) / 2 = V + V E with E = (I - V^T V) / 2.  V^T V is
     // symmetric: its upper tiles are formed and E goes to both triangles of
     // the A buffer; V + V E is formed with V E as the small term.
-    JOLT_PROBE(5);
     const int ntri = nt * (nt + 1) / 2;     // <= kWaves for n <= 160
     for (int step = 0;; ++step) {
         float dev = 0.f;
@@ -1427,7 +1424,6 @@ __global__ __launch_bounds__(kThreads) void k_eig_polish(JacBatch batch, int ld,
     const float *W = V;
 
     // ---------------------------------------------------------------- output
-    JOLT_PROBE(6);
     if (tid < n) {
         const int k = tid, col = n - 1 - k;
         int best = 0;

@@ -159,7 +159,6 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int NW = 8;
     float shift = 0.f;                          // used by wave 0 only
-    JOLT_PROBE(0);
     if (wid == 0) {
         // wave 0: shift = rel_shift * trace(G) / k, then block (0, 0) straight
         // from G (identity in the padding), while the other waves fill LDS
@@ -216,7 +215,6 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
     for (int J = 0; J < nb; ++J) {
         const int J0 = 32 * J;
         __syncthreads();                        // diagonal block J factored, R_JK complete
-        JOLT_PROBE(1 + 2 * J);
         const int npanel = nb - 1 - J;
         for (int t = wid; t < npanel + J; t += NW) {
             f32x16 acc = {};
@@ -239,7 +237,6 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
             }
         }
         __syncthreads();
-        JOLT_PROBE(2 + 2 * J);
         if (npanel == 0) break;
         const int J1 = J0 + 32;
         if (wid == 0) {
@@ -286,7 +283,6 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
             }
         }
     }
-    JOLT_PROBE(21);
     // L^{-1}: X(i, c) = S[c][i] on and below the diagonal; four rows per wave
     // in flight (in-bounds loads, then selects)
     __syncthreads();
@@ -313,7 +309,6 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
             }
         }
     }
-    JOLT_PROBE(22);
 }
 
 // One wave per 32-row block tm of Q (K = 32 (tm + 1): X is lower triangular).
