@@ -16,4 +16,4 @@ model's fidelity on real residuals (delta_b is pinned on Gaussian groups only),
 and the pages' own quality numbers (0.009 / 0.006 relative error at 2x), which
 need trained weights.
 """
-from . import alloc, codec, linalg, pipeline, quant, rng, tucker, wht  # noqa: F401
+from . import alloc, attention, codec, linalg, pipeline, quant, rng, tucker, wht  # noqa: F401
