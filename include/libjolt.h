@@ -223,6 +223,36 @@ jolt_status jolt_decompress(jolt_handle h, const jolt_item *items, int32_t n, co
 jolt_status jolt_decompress_noalloc(jolt_handle h, const jolt_item *items, int32_t n, const jolt_alloc *alloc,
                                     const void *const *payload_dev, void *const *out_dev, void *stream);
 
+/* ---- decode attention over the stored factors --------------------------- */
+/* The method's decode kernel evaluates attention directly over the stored
+ * factors, without materializing dense K and V ("A JoLT for the KV cache",
+ * paper landing page, abstract).  For one decode step, every query head j of
+ * layer l (q_heads per layer, grouped-query: KV head j / (q_heads / H))
+ * attends to the cached tokens of its layer group:
+ *   out = sum_t p_t v_t,  p = softmax(scale * q . k_t),  lse = log sum_t exp(scale * q . k_t)
+ * where k_t, v_t are the rows the K and V payloads represent (Tucker part plus
+ * rotated residual, unrounded).  Scores come from U_t and the K codes with a
+ * per-head z = scale C (U_f^T q) and rotated query; values are summed in the
+ * factor and rotated domains and mapped to features once per head.  lse lets
+ * a caller merge attention over tokens kept outside the payloads.
+ *   k_item / v_item   the group's K and V items (same L, H, T, d, dtype)
+ *   k_alloc / v_alloc their allocations; k_payload / v_payload (device)
+ *   q    device fp32 [L][q_heads][d];  out device fp32 [L][q_heads][d];
+ *   lse  device fp32 [L][q_heads]
+ * All groups of a call share dtype, d and H; q_heads / H must be 1, 2, 4 or
+ * 8; workspace (device) of jolt_attention_workspace_size() bytes. */
+typedef struct {
+    jolt_item k_item, v_item;
+    jolt_alloc k_alloc, v_alloc;
+    const void *k_payload, *v_payload;
+    const float *q;
+    float *out;
+    float *lse;
+} jolt_attn_group;
+jolt_status jolt_attention_workspace_size(const jolt_attn_group *groups, int32_t n, int32_t q_heads, size_t *bytes);
+jolt_status jolt_decode_attention(jolt_handle h, const jolt_attn_group *groups, int32_t n, int32_t q_heads,
+                                  float scale, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- factor export (device pointers into plan_ws) ------------------------ */
 /* After jolt_plan: where item i's factors live in plan_ws (fp32, device):
  *   ut    rt_max x T   row r = token-factor column r (descending eigenvalue)

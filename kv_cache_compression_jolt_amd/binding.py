@@ -44,6 +44,12 @@ class jolt_alloc(C.Structure):
                 ("bytes", C.c_int64), ("distortion", C.c_double)]
 
 
+class jolt_attn_group(C.Structure):
+    _fields_ = [("k_item", jolt_item), ("v_item", jolt_item), ("k_alloc", jolt_alloc), ("v_alloc", jolt_alloc),
+                ("k_payload", C.c_void_p), ("v_payload", C.c_void_p), ("q", C.c_void_p), ("out", C.c_void_p),
+                ("lse", C.c_void_p)]
+
+
 class jolt_factor_view(C.Structure):
     _fields_ = [("ut", C.c_void_p), ("uf", C.c_void_p), ("lam_t", C.c_void_p), ("lam_f", C.c_void_p),
                 ("core", C.c_void_p), ("energy", C.c_void_p), ("normx2", C.c_void_p),
@@ -54,7 +60,7 @@ EXPORTED = [
     "jolt_create", "jolt_destroy", "jolt_status_str", "jolt_last_error", "jolt_workspace_size",
     "jolt_item_bytes", "jolt_payload_size", "jolt_payload_layout", "jolt_payload_header",
     "jolt_payload_validate", "jolt_plan", "jolt_replan", "jolt_compress", "jolt_encode_residual",
-    "jolt_decompress", "jolt_decompress_noalloc",
+    "jolt_decompress", "jolt_decompress_noalloc", "jolt_attention_workspace_size", "jolt_decode_attention",
     "jolt_plan_factors", "jolt_plan_from_tables", "jolt_rotate", "jolt_quantize_pack",
     "jolt_unpack_dequant", "jolt_rademacher", "jolt_eigh", "jolt_eigh_workspace_size", "jolt_kernel_timer",
     "jolt_kernel_time",
@@ -96,6 +102,8 @@ def lib():
                                       C.POINTER(P), P]),
             "jolt_decompress_noalloc": (I32, [P, C.POINTER(jolt_item), I32, C.POINTER(jolt_alloc), C.POINTER(P),
                                               C.POINTER(P), P]),
+            "jolt_attention_workspace_size": (I32, [C.POINTER(jolt_attn_group), I32, I32, C.POINTER(SZ)]),
+            "jolt_decode_attention": (I32, [P, C.POINTER(jolt_attn_group), I32, I32, C.c_float, P, SZ, P]),
             "jolt_plan_factors": (I32, [C.POINTER(jolt_config), C.POINTER(jolt_item), I32, P, I32,
                                         C.POINTER(jolt_factor_view)]),
             "jolt_plan_from_tables": (I32, [I32, C.POINTER(I32), C.POINTER(C.POINTER(I32)),
@@ -225,6 +233,19 @@ def jolt_decompress_noalloc(h, items, allocs, pay_ptrs, out_ptrs, stream):
     arr = (jolt_alloc * max(1, n))(*allocs)
     _check(lib().jolt_decompress_noalloc(h, _items(items), n, arr, _ptrs(pay_ptrs), _ptrs(out_ptrs),
                                          C.c_void_p(stream)), h)
+
+
+def jolt_attention_workspace_size(groups: Sequence[jolt_attn_group], q_heads: int) -> int:
+    arr = (jolt_attn_group * max(1, len(groups)))(*groups)
+    b = C.c_size_t()
+    _check(lib().jolt_attention_workspace_size(arr, len(groups), q_heads, C.byref(b)))
+    return b.value
+
+
+def jolt_decode_attention(h, groups: Sequence[jolt_attn_group], q_heads: int, scale: float, ws_ptr, ws_bytes, stream):
+    arr = (jolt_attn_group * max(1, len(groups)))(*groups)
+    _check(lib().jolt_decode_attention(h, arr, len(groups), q_heads, C.c_float(scale), C.c_void_p(ws_ptr), ws_bytes,
+                                       C.c_void_p(stream)), h)
 
 
 def jolt_plan_factors(cfg, items, plan_ptr, i) -> jolt_factor_view:

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "api_internal.h"
+#include "attn.h"
 #include "jolt_internal.h"
 #include "payload.h"
 #include "ktimer.h"
@@ -599,4 +600,128 @@ extern "C" jolt_status jolt_kernel_time(jolt_handle h, const char *kernel, doubl
     if (!kernel || !total_ms || !launches) return fail(h, JOLT_E_INVALID, "kernel_time: null argument");
     hipError_t e = ktimer_read(kernel, total_ms, launches);
     return e == hipSuccess ? JOLT_OK : hip_fail(h, e, "kernel_time");
+}
+
+// --------------------------------------------------------------------------- decode attention
+namespace jolt {
+
+// Token ranges of one group: about two workgroups per CU over the call, ranges
+// a multiple of 256 tokens, none empty.
+static void attn_splits(int T, int LH, int n, int *splits, int *per) {
+    const int chunks = (T + 255) / 256;
+    const int want = std::max(1, std::min(chunks, (512 + LH * n - 1) / std::max(1, LH * n)));
+    *per = 256 * ((chunks + want - 1) / want);
+    *splits = (T + *per - 1) / *per;
+}
+
+static jolt_status attn_check(jolt_handle h, const jolt_attn_group *g, int32_t n, int32_t q_heads) {
+    if (n < 0 || (n > 0 && !g)) return fail(h, JOLT_E_INVALID, "attention: bad group array");
+    for (int i = 0; i < n; ++i) {
+        const jolt_item &k = g[i].k_item, &v = g[i].v_item;
+        jolt_status s = check_item(h, k);
+        if (s) return s;
+        if ((s = check_item(h, v))) return s;
+        if (k.L != v.L || k.H != v.H || k.T != v.T || k.d != v.d || k.dtype != v.dtype)
+            return fail(h, JOLT_E_INVALID, "attention: K and V items of group %d differ in shape or dtype", i);
+        if (k.dtype != g[0].k_item.dtype || k.d != g[0].k_item.d || k.H != g[0].k_item.H)
+            return fail(h, JOLT_E_UNSUPPORTED, "attention: all groups of one call must share dtype, d and H");
+        if ((s = check_alloc(h, k, g[i].k_alloc))) return s;
+        if ((s = check_alloc(h, v, g[i].v_alloc))) return s;
+        if (!g[i].k_payload || !g[i].v_payload || !g[i].q || !g[i].out || !g[i].lse)
+            return fail(h, JOLT_E_INVALID, "attention: NULL pointer in group %d", i);
+    }
+    if (n > 0) {
+        const int H = g[0].k_item.H;
+        if (q_heads < H || q_heads % H) return fail(h, JOLT_E_INVALID, "attention: q_heads must be a multiple of H");
+        const int G = q_heads / H;
+        if (G != 1 && G != 2 && G != 4 && G != 8)
+            return fail(h, JOLT_E_UNSUPPORTED, "attention: q_heads / H must be 1, 2, 4 or 8");
+    }
+    return JOLT_OK;
+}
+
+static size_t attn_ws_for(const jolt_attn_group &g, int q_heads, size_t *prep, size_t *part) {
+    const jolt_item &k = g.k_item;
+    const int rtk = (g.k_alloc.rt == 0 || g.k_alloc.rf == 0) ? 0 : g.k_alloc.rt;
+    const int rtv = (g.v_alloc.rt == 0 || g.v_alloc.rf == 0) ? 0 : g.v_alloc.rt;
+    int splits, per;
+    attn_splits(k.T, k.L * k.H, 1, &splits, &per);
+    *prep = align_up((size_t)k.L * q_heads * (round_up(rtk, 16) + k.d) * 4, 256);
+    *part = align_up((size_t)splits * k.L * q_heads * (2 + round_up(rtv, 16) + k.d) * 4, 256);
+    return *prep + *part;
+}
+
+}  // namespace jolt
+
+extern "C" jolt_status jolt_attention_workspace_size(const jolt_attn_group *groups, int32_t n, int32_t q_heads,
+                                                     size_t *bytes) {
+    if (!bytes) return JOLT_E_INVALID;
+    jolt_status s = attn_check(nullptr, groups, n, q_heads);
+    if (s) return s;
+    size_t tot = 0;
+    for (int i = 0; i < n; ++i) {
+        size_t a, b;
+        tot += attn_ws_for(groups[i], q_heads, &a, &b);
+    }
+    *bytes = std::max<size_t>(tot, 256);
+    return JOLT_OK;
+}
+
+extern "C" jolt_status jolt_decode_attention(jolt_handle h, const jolt_attn_group *groups, int32_t n,
+                                             int32_t q_heads, float scale, void *workspace, size_t workspace_bytes,
+                                             void *stream) {
+    if (!h) return JOLT_E_INVALID;
+    clear_err(h);
+    jolt_status s = attn_check(h, groups, n, q_heads);
+    if (s) return s;
+    if (n == 0) return JOLT_OK;
+    size_t need = 0;
+    for (int i = 0; i < n; ++i) {
+        size_t a, b;
+        need += attn_ws_for(groups[i], q_heads, &a, &b);
+    }
+    if (!workspace || workspace_bytes < need)
+        return fail(h, JOLT_E_WORKSPACE, "attention workspace: need %zu bytes, have %zu", need, workspace_bytes);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(h, JOLT_E_INVALID, "attention: scale must be > 0");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const int nall = n;
+    int cursor = 0;
+    size_t off = 0;
+    while (cursor < nall) {
+        AttnBatch b{};
+        b.n = 0;
+        b.hq = q_heads;
+        b.scale = scale;
+        const int nb = std::min(kMaxBatch, nall - cursor);
+        for (int i = cursor; i < cursor + nb; ++i) {
+            const jolt_attn_group &g = groups[i];
+            const jolt_item &k = g.k_item, &v = g.v_item;
+            AttnGroup &a = b.it[b.n++];
+            a.L = k.L; a.H = k.H; a.T = k.T; a.d = k.d;
+            PayloadLayout pk = payload_layout(k, g.k_alloc.rt, g.k_alloc.rf, g.k_alloc.bits);
+            PayloadLayout pv = payload_layout(v, g.v_alloc.rt, g.v_alloc.rf, g.v_alloc.bits);
+            a.rtk = pk.rt; a.rfk = pk.rf; a.bk = g.k_alloc.bits; a.rtpk = round_up(pk.rt, 16);
+            a.rtv = pv.rt; a.rfv = pv.rf; a.bv = g.v_alloc.bits; a.rtpv = round_up(pv.rt, 16);
+            attn_splits(k.T, k.L * k.H, nb, &a.splits, &a.per_split);
+            sign_bits_for(k.seed, k.item_id, k.d, a.sk);
+            sign_bits_for(v.seed, v.item_id, v.d, a.sv);
+            a.isd = 1.0f / std::sqrt((float)k.d);
+            const uint8_t *kp = static_cast<const uint8_t *>(g.k_payload), *vp = static_cast<const uint8_t *>(g.v_payload);
+            a.ut_k = kp + pk.ut; a.uf_k = kp + pk.uf; a.core_k = kp + pk.core;
+            a.scales_k = reinterpret_cast<const uint16_t *>(kp + pk.scales); a.codes_k = kp + pk.codes;
+            a.ut_v = vp + pv.ut; a.uf_v = vp + pv.uf; a.core_v = vp + pv.core;
+            a.scales_v = reinterpret_cast<const uint16_t *>(vp + pv.scales); a.codes_v = vp + pv.codes;
+            a.q = g.q; a.out = g.out; a.lse = g.lse;
+            const size_t prep = align_up((size_t)k.L * q_heads * (a.rtpk + k.d) * 4, 256);
+            const size_t part = align_up((size_t)a.splits * k.L * q_heads * (2 + a.rtpv + k.d) * 4, 256);
+            a.ws_prep = reinterpret_cast<float *>(ws + off);
+            a.ws_part = reinterpret_cast<float *>(ws + off + prep);
+            off += prep + part;
+        }
+        hipError_t e = launch_attention(b, groups[0].k_item.dtype, st);
+        if (e != hipSuccess) return hip_fail(h, e, "attention");
+        cursor += nb;
+    }
+    return JOLT_OK;
 }
