@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-items", type=int, default=1, help="items in the oracle's timed sample")
     ap.add_argument("--no-mode-ratio", action="store_true")
+    ap.add_argument("--no-studies", action="store_true", help="skip the comparators and allocator variants")
     ap.add_argument("--profile", action="store_true", help="few steps, no extras (for rocprofv3)")
     return ap.parse_args()
 
@@ -184,6 +185,7 @@ def main():
         return 2
     if args.profile:
         args.steps, args.warmup, args.no_cpu_baseline, args.no_mode_ratio = min(args.steps, 2), 1, True, True
+        args.no_studies = True
 
     import synth
     cfg = synth.config(args.config)
@@ -334,6 +336,8 @@ def main():
 
     if not args.no_mode_ratio:
         out["exact_vs_randomized"] = mode_ratio(torch, jb, dev, delta)
+    if not args.no_studies:
+        out["studies"] = run_studies(torch, jb, dev, delta)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, specs, sample_raw, budget, n_items, delta, layer_group_tokens)
 
@@ -374,6 +378,25 @@ def mode_ratio(torch, jb, dev, delta, steps=3):
         J.close()
     res["ratio"] = round(res["exact_ms"] / res["randomized_ms"], 3)
     res["workload"] = "mistral7b_gqa_1k (16 items of 4x8x1024x128 bf16, 2x budget), plan + compress"
+    return res
+
+
+def run_studies(torch, jb, dev, delta):
+    """Comparators (4-bit, cross-layer SVD) and allocator variants (budget split
+    between K and V in advance; measured residual distortion) on the
+    Mistral-7B-shaped 1024-token cache."""
+    import synth
+    from kv_cache_compression_jolt_amd import studies
+    cfg = synth.config("mistral7b_gqa_1k")
+    specs = synth.item_specs(cfg)
+    xs = [upload(torch, synth.make_item(cfg, s, keep_x=False).raw, dev) for s in specs]
+    jitems = [jb.make_item(s.L, s.H, s.T, s.d, s.dtype, s.item_id, s.seed) for s in specs]
+    kv = [s.kv for s in specs]
+    res = {"workload": "mistral7b_gqa_1k (16 items of 4x8x1024x128 bf16)"}
+    res["comparators"] = [studies.comparators(torch, cfg, jitems, xs, kv, delta, r) for r in (2.0, 3.76)]
+    res["allocator_presplit"] = [studies.presplit(torch, cfg, jitems, xs, kv, delta, r) for r in (3.0, 4.0)]
+    res["distortion_model"] = studies.measured_delta(torch, cfg, jitems, xs, delta, cfg.rt_max, cfg.d)
+    print("bench: studies done", file=sys.stderr, flush=True)
     return res
 
 
