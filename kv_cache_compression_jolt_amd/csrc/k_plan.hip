@@ -28,11 +28,13 @@ namespace jolt {
 // out[s][c][t] = sum over the split's features k of x[t][k] m[k][c] (x the token
 // unfolding, m the sketch operand stored as m[c][k]).
 //
-// WG: 4 waves x 64 tokens (two 32-token row fragments per wave) and NF column
-// fragments of 32.  The K range (lh_split whole (layer, head) blocks) runs in
-// chunks of 64 features.  A chunk of m (NF*32 columns x 64) is staged once per
-// WG in LDS, double buffered, and read by all four waves; x fragments come
-// straight from global memory, each element once, one chunk ahead.
+// WG: 256 tokens, as NWV waves of R 32-token row fragments (4 x 2, or 8 x 1
+// for the widest column tiles, whose NF accumulators per row fragment leave no
+// registers for a second one), and NF column fragments of 32.  The K range
+// (lh_split whole (layer, head) blocks) runs in chunks of 64 features.  A chunk
+// of m (NF*32 columns x 64) is staged once per WG in LDS, double buffered, and
+// read by all the waves; x fragments come straight from global memory, each
+// element once, one chunk ahead.
 template <typename T, int KC_>
 struct XmTile {
     static constexpr int PER = 16 / sizeof(T);     // elements per 16-byte piece
@@ -41,24 +43,26 @@ struct XmTile {
     static constexpr int U = KC / 16;              // MFMA K steps per chunk
 };
 
-template <typename T, int NF, int KC_>
-__global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles) {
+template <typename T, int NF, int KC_, int R, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_xm(XmBatch batch, int d, int ncol_tiles) {
+    static_assert(32 * R * NWV == 256, "256 tokens per workgroup");
+    constexpr int NT = 64 * NWV;
     using Frag = typename Elem<T>::Frag;
     using Tile = XmTile<T, KC_>;
     constexpr int PER = Tile::PER, KC = Tile::KC, KP = Tile::KP, U = Tile::U;
     constexpr int ROWS = 32 * NF;
     constexpr int PIECES = ROWS * KC / PER;                 // 16-byte pieces per m chunk
-    constexpr int PPT = (PIECES + 255) / 256;               // per thread
+    constexpr int PPT = (PIECES + NT - 1) / NT;             // per thread
     extern __shared__ __attribute__((aligned(16))) unsigned char xm_lds[];
     T *ms = reinterpret_cast<T *>(xm_lds);                  // [2][ROWS][KP]
     const Block3 blk = xcd_block();
     const XmItem &it = batch.it[blk.z];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
-    const int tw = blk.x * 256 + wave * 64;                 // this wave's first token
+    const int tw = blk.x * 256 + wave * 32 * R;             // this wave's first token
     const int c0 = (blk.y % ncol_tiles) * ROWS;
     const int sp = blk.y / ncol_tiles;
     if (blk.x * 256 >= it.T || c0 >= it.ncols || sp >= it.nsplit) return;
-    const bool wv = tw < it.T;                              // T is a multiple of 64
+    const bool wv = tw < it.T;                              // T is a multiple of 64 (of 32 R)
     const T *x = reinterpret_cast<const T *>(it.x);
     const T *m = reinterpret_cast<const T *>(it.m);
     const int n = it.LH * d;
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles
         const int lh = k0 / d, fb = k0 - lh * d;
 #pragma unroll
         for (int q = 0; q < PPT; ++q) {
-            const int p = threadIdx.x + 256 * q;
+            const int p = threadIdx.x + NT * q;
             const int r = p / (KC / PER), kk = (p % (KC / PER)) * PER;
             const int c = c0 + r;
             const bool ok = p < PIECES && c < it.ncols;
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles
     auto store_m = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < PPT; ++q) {
-            const int p = threadIdx.x + 256 * q;
+            const int p = threadIdx.x + NT * q;
             if (p < PIECES) {
                 const int r = p / (KC / PER), kk = (p % (KC / PER)) * PER;
                 *reinterpret_cast<uint4 *>(ms + ((size_t)buf * ROWS + r) * KP + kk) = stg[q];
@@ -91,11 +95,11 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles
         }
     };
     // x fragments of a chunk: rows tw + 32 r + ln, K = 16 u + 8 h + (0..7)
-    Frag an[2][U], a[2][U];
+    Frag an[R][U], a[R][U];
     auto load_x = [&](int k0) {
         const int lh = k0 / d, fb = k0 - lh * d;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < R; ++r) {
             const int tok = wv ? tw + 32 * r + ln : 0;
             const T *xa = x + ((size_t)lh * it.T + tok) * d + fb + 8 * h;
 #pragma unroll
@@ -103,9 +107,9 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles
         }
     };
 
-    f32x16 acc[2][NF];
+    f32x16 acc[R][NF];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int f = 0; f < NF; ++f) acc[r][f] = f32x16{};
     if (nck > 0) {
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles
     for (int ci = 0; ci < nck; ++ci) {
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int u = 0; u < U; ++u) a[r][u] = an[r][u];
         const bool more = ci + 1 < nck;
@@ -131,8 +135,8 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles
 #pragma unroll
                 for (int f = 0; f < NF; ++f) {
                     const Frag b = load_frag(mb + (32 * f + ln) * KP + 16 * u + 8 * h);
-                    mfma(a[0][u], b, acc[0][f]);
-                    mfma(a[1][u], b, acc[1][f]);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) mfma(a[r][u], b, acc[r][f]);
                 }
         }
         if (more) store_m((ci + 1) & 1);
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void k_xm(XmBatch batch, int d, int ncol_tiles
         if (c < it.ncols) {
             float *o = it.out + (size_t)sp * it.ncols * it.ldo + (size_t)c * it.ldo + tw;
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
+            for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int row = 32 * r + 8 * q + 4 * h;
@@ -174,13 +178,13 @@ __device__ __forceinline__ void stage_transposed(const T *src, int d, T *xs, int
 // out[s][c][F] = sum over the split's tokens t of q[c][t] x[t][F], F = lh d + f
 // the global feature index (the token unfolding's column).
 //
-// WG: a tile of 256 features (4 waves x 2 row fragments of 32) and NF column
-// fragments of 32.  Per chunk of 64 tokens the WG stages, once, x's tile
+// WG: a tile of 256 features (NWV waves x R row fragments of 32: 4 x 2, or
+// 8 x 1 for the widest column tiles) and NF column fragments of 32.  Per chunk of 64 tokens the WG stages, once, x's tile
 // transposed to xs[F][t] (token pairs packed in 32-bit words for bf16) and the
 // chunk of q (hi and lo parts when LO) as qs[c][t]; the next chunk is loaded
 // into registers meanwhile.  Each wave then reads 2 x fragments and NF (2 NF)
 // q fragments per 16 tokens from LDS.
-template <typename T, int NF, bool LO>
+template <typename T, int NF, bool LO, int NT>
 struct XtqTile {
     static constexpr int PER = 16 / sizeof(T);
     static constexpr int FT = 256;                       // features per WG
@@ -188,15 +192,17 @@ struct XtqTile {
     static constexpr int XP = TC + PER;                  // LDS pitch of xs and qs rows
     static constexpr int QR = 32 * NF * (LO ? 2 : 1);    // q rows staged (hi rows, then lo rows)
     static constexpr int XPIECES = FT * TC / PER / (sizeof(T) == 2 ? 2 : 1);  // loads of x per chunk
-    static constexpr int XPT = XPIECES / 256;
+    static constexpr int XPT = XPIECES / NT;
     static constexpr int QPIECES = QR * TC / PER;
-    static constexpr int QPT = (QPIECES + 255) / 256;
+    static constexpr int QPT = (QPIECES + NT - 1) / NT;
     static constexpr size_t lds_bytes = (size_t)(FT + QR) * XP * sizeof(T);
 };
 
-template <typename T, int NF, bool LO>
-__global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit) {
-    using Tile = XtqTile<T, NF, LO>;
+template <typename T, int NF, bool LO, int R, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int maxSplit) {
+    static_assert(32 * R * NWV == 256, "256 features per workgroup");
+    constexpr int NT = 64 * NWV;
+    using Tile = XtqTile<T, NF, LO, NT>;
     using Frag = typename Elem<T>::Frag;
     constexpr int PER = Tile::PER, FT = Tile::FT, TC = Tile::TC, XP = Tile::XP, QR = Tile::QR;
     constexpr int XPT = Tile::XPT, QPT = Tile::QPT, QPIECES = Tile::QPIECES;
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit
     auto load_x = [&](int t0) {
 #pragma unroll
         for (int q = 0; q < XPT; ++q) {
-            const int pass = wave + 4 * q;                // 0 .. 4 XPT - 1
+            const int pass = wave + NWV * q;              // 0 .. NWV XPT - 1
             const int tl = lane % TPL, fg = lane / TPL;
             const int tpass = pass % (TC / (BF ? 2 : 1) / TPL), fpass = pass / (TC / (BF ? 2 : 1) / TPL);
             const int t = t0 + (tpass * TPL + tl) * (BF ? 2 : 1);
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit
     auto store_x = [&]() {
 #pragma unroll
         for (int q = 0; q < XPT; ++q) {
-            const int pass = wave + 4 * q;
+            const int pass = wave + NWV * q;
             const int tl = lane % TPL, fg = lane / TPL;
             const int tpass = pass % (TC / (BF ? 2 : 1) / TPL), fpass = pass / (TC / (BF ? 2 : 1) / TPL);
             const int tt = (tpass * TPL + tl) * (BF ? 2 : 1);
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit
     auto load_q = [&](int t0) {
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
-            const int p = threadIdx.x + 256 * q;
+            const int p = threadIdx.x + NT * q;
             const int r = p / (TC / PER), tt = (p % (TC / PER)) * PER;
             const int c = c0 + (r < 32 * NF ? r : r - 32 * NF);
             const bool ok = p < QPIECES && c < it.ncols;
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit
     auto store_q = [&]() {
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
-            const int p = threadIdx.x + 256 * q;
+            const int p = threadIdx.x + NT * q;
             if (p < QPIECES) {
                 const int r = p / (TC / PER), tt = (p % (TC / PER)) * PER;
                 *reinterpret_cast<uint4 *>(qs + r * XP + tt) = qr[q];
@@ -293,12 +299,12 @@ __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit
         }
     };
 
-    f32x16 acc[2][NF];
+    f32x16 acc[R][NF];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int f = 0; f < NF; ++f) acc[r][f] = f32x16{};
-    const int fw = 64 * wave;                             // this wave's first feature in the tile
+    const int fw = 32 * R * wave;                         // this wave's first feature in the tile
     if (nck > 0) {
         load_x(tb);
         load_q(tb);
@@ -314,18 +320,18 @@ __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit
         }
 #pragma unroll
         for (int kk = 0; kk < TC; kk += 16) {
-            Frag a[2];
+            Frag a[R];
 #pragma unroll
-            for (int r = 0; r < 2; ++r) a[r] = load_frag(xs + (fw + 32 * r + ln) * XP + kk + 8 * h);
+            for (int r = 0; r < R; ++r) a[r] = load_frag(xs + (fw + 32 * r + ln) * XP + kk + 8 * h);
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
                 const Frag b = load_frag(qs + (32 * f + ln) * XP + kk + 8 * h);
-                mfma(a[0], b, acc[0][f]);
-                mfma(a[1], b, acc[1][f]);
+#pragma unroll
+                for (int r = 0; r < R; ++r) mfma(a[r], b, acc[r][f]);
                 if constexpr (LO) {
                     const Frag bl = load_frag(qs + (32 * NF + 32 * f + ln) * XP + kk + 8 * h);
-                    mfma(a[0], bl, acc[0][f]);
-                    mfma(a[1], bl, acc[1][f]);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) mfma(a[r], bl, acc[r][f]);
                 }
             }
         }
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(256) void k_xtq(XtqBatch batch, int d, int maxSplit
         const int c = c0 + 32 * f + ln;
         if (c < it.ncols) {
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
+            for (int r = 0; r < R; ++r) {
                 const int Fr = F0 + fw + 32 * r;
                 if (Fr < n) {
                     float *o = out + (size_t)c * n + Fr;
@@ -1023,13 +1029,14 @@ static hipError_t ensure_lds_attrs() {
     return state;
 }
 
-template <typename T, int NF, int KC>
+template <typename T, int NF, int KC, int R = 2, int NWV = 4>
 static hipError_t xm_launch(const XmBatch &b, int d, dim3 g, int tiles, hipStream_t s) {
     const size_t lds = (size_t)2 * 32 * NF * XmTile<T, KC>::KP * sizeof(T);
+    const auto k = k_xm<T, NF, KC, R, NWV>;
     static hipError_t attr = hipErrorNotReady;
-    if (attr == hipErrorNotReady) attr = allow_dynamic_lds(reinterpret_cast<const void *>(k_xm<T, NF, KC>));
+    if (attr == hipErrorNotReady) attr = allow_dynamic_lds(reinterpret_cast<const void *>(k));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((k_xm<T, NF, KC>), g, dim3(256), lds, s, b, d, tiles);
+    hipLaunchKernelGGL(k, g, dim3(64 * NWV), lds, s, b, d, tiles);
     return hipGetLastError();
 }
 
@@ -1046,6 +1053,7 @@ static hipError_t xm_nf(const XmBatch &b, int d, dim3 g, int nf, int tiles, hipS
     if constexpr (sizeof(T) == 2) {      // wider tiles fit the registers in bf16 only
         if (nf == 5) return xm_launch<T, 5, 64>(b, d, g, tiles, s);
         if (nf == 6) return xm_launch<T, 6, 64>(b, d, g, tiles, s);
+        if (nf == 9) return xm_launch<T, 9, 64, 1, 8>(b, d, g, tiles, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1056,18 +1064,22 @@ hipError_t launch_xm(const XmBatch &b, int dtype, int d, int maxT, int maxCols, 
     KTimeScope kts("k_xm", s);
     int nf = (maxCols + 31) / 32;
     int tiles = 1;
-    if (nf > (dtype == JOLT_BF16 ? 6 : 4)) { tiles = (nf + 3) / 4; nf = 4; }
+    // bf16: up to 6 fragments in one tile, and 7 to 9 as one tile of 9 (the
+    // whole sketch of an r_t = 256 plan in one pass over x); otherwise tiles of 4
+    if (dtype == JOLT_BF16 && nf >= 7 && nf <= 9) nf = 9;
+    else if (nf > (dtype == JOLT_BF16 ? 6 : 4)) { tiles = (nf + 3) / 4; nf = 4; }
     dim3 g((maxT + 255) / 256, tiles * maxSplit, b.n);
     return dtype == JOLT_BF16 ? xm_nf<uint16_t>(b, d, g, nf, tiles, s) : xm_nf<float>(b, d, g, nf, tiles, s);
 }
 
-template <typename T, int NF, bool LO>
+template <typename T, int NF, bool LO, int R = 2, int NWV = 4>
 static hipError_t xtq_launch(const XtqBatch &b, int d, dim3 g, int maxSplit, hipStream_t s) {
+    const auto k = k_xtq<T, NF, LO, R, NWV>;
     static hipError_t attr = hipErrorNotReady;
-    if (attr == hipErrorNotReady) attr = allow_dynamic_lds(reinterpret_cast<const void *>(k_xtq<T, NF, LO>));
+    if (attr == hipErrorNotReady) attr = allow_dynamic_lds(reinterpret_cast<const void *>(k));
     if (attr != hipSuccess) return attr;
-    const size_t lds = XtqTile<T, NF, LO>::lds_bytes;
-    hipLaunchKernelGGL((k_xtq<T, NF, LO>), g, dim3(256), lds, s, b, d, maxSplit);
+    const size_t lds = XtqTile<T, NF, LO, 64 * NWV>::lds_bytes;
+    hipLaunchKernelGGL(k, g, dim3(64 * NWV), lds, s, b, d, maxSplit);
     return hipGetLastError();
 }
 
@@ -1079,8 +1091,11 @@ static hipError_t xtq_nf(const XtqBatch &b, int d, dim3 g, int nf, int maxSplit,
         case 3: return xtq_launch<T, 3, LO>(b, d, g, maxSplit, s);
         case 4: return xtq_launch<T, 4, LO>(b, d, g, maxSplit, s);
         case 5: return xtq_launch<T, 5, LO>(b, d, g, maxSplit, s);
-        default: return hipErrorInvalidValue;
+        default: break;
     }
+    if constexpr (sizeof(T) == 2)
+        if (nf == 9) return xtq_launch<T, 9, LO, 1, 8>(b, d, g, maxSplit, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_xtq(const XtqBatch &b, int dtype, int d, int maxLH, int maxSplit, int maxCols, hipStream_t s) {
@@ -1089,8 +1104,11 @@ hipError_t launch_xtq(const XtqBatch &b, int dtype, int d, int maxLH, int maxSpl
     for (int i = 0; i < b.n; ++i)
         if (b.it[i].T % 64 || b.it[i].tsplit % 64) return hipErrorInvalidValue;
     KTimeScope kts("k_xtq", s);
-    // column tiles of at most 5 fragments (160 columns)
-    const int frags = (maxCols + 31) / 32, ctiles = (frags + 4) / 5, nf = (frags + ctiles - 1) / ctiles;
+    // column tiles of at most 5 fragments (160 columns); bf16 sketches of 7 to 9
+    // fragments as one tile of 9 (x read once)
+    const int frags = (maxCols + 31) / 32;
+    int ctiles = (frags + 4) / 5, nf = (frags + ctiles - 1) / ctiles;
+    if (dtype == JOLT_BF16 && frags >= 7 && frags <= 9) { ctiles = 1; nf = 9; }
     dim3 g(maxSplit * ctiles, (maxLH * d + 255) / 256, b.n);
     const bool lo = b.it[0].ql != nullptr;
     if (dtype == JOLT_BF16)
