@@ -256,7 +256,7 @@ __device__ __forceinline__ void xhat_mfma(const T *wt, const T *wlo, int rtp, co
                                           int lane, f32x16 *acc) {
     const int ln = lane & 31, h = lane >> 5;
     const bool vec = (rt & 7) == 0;        // rows of U~_t are 16-byte aligned
-    constexpr int KB = sizeof(T) == 2 ? 8 : 4;
+    constexpr int KB = 4;                  // fragments in flight (registers: 4 waves per SIMD)
     const T *urow = ut + (size_t)(tv ? tok : 0) * rt;
     for (int k0b = 0; k0b < rt; k0b += 16 * KB) {
         typename Elem<T>::Frag b[KB];
@@ -409,170 +409,186 @@ __device__ __forceinline__ void load_codes(const uint8_t *codes, const uint16_t 
 }
 
 // ------------------------------------------------------------------ fused encoder
+// A workgroup takes one (layer, head) and a range of tpw tokens: it stages W~
+// once, then its NWV waves walk the range's 32-token tiles (wave w: tiles w,
+// w + NWV, ...).  The staging is paid once per range, and the waves, each at
+// its own point of the tile loop, overlap one wave's MFMAs with another's
+// butterflies and packing.
 template <typename T, int D, int BITS, int NWV, bool WL>
-__global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch) {
+__global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch, int tpw) {
     typedef Tile<T, D> TL;
     constexpr int NMF = TL::NMF;
     constexpr int HALF = NMF / 2;
-    constexpr int NE = 32 * NMF / 2 * 2 / 2;       // values per lane: 64 (d=128) or 32 (d=64)
-    static_assert(NE == 16 * NMF, "layout");
+    constexpr int NE = 16 * NMF;                   // values per lane: 64 (d=128) or 32 (d=64)
     const Block3 blk = xcd_block();
     const CodecItem &it = batch.it[blk.z];
-    const int lh = blk.y;
-    if (lh >= it.LH || blk.x * 32 * NWV >= it.T) return;
+    const int lh = blk.y, tb = blk.x * tpw;
+    if (lh >= it.LH || tb >= it.T) return;
+    const int te = min(it.T, tb + tpw);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 31, h = lane >> 5;
-    const int t0 = blk.x * 32 * NWV + wave * 32;
-    const int tok = t0 + ln;
-    const bool tv = tok < it.T;
-
-    // -(s o x) in the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
-    // of its token), loaded before the W~ staging so that the load latency
-    // overlaps it; an invalid token reads row 0 and stores nothing.  The X^
-    // products (signs folded into wt) accumulate onto it, leaving -(s o r).
-    const uint8_t *xrow = reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T + (tv ? tok : 0)) * TL::RB;
-    f32x16 acc[NMF];
-#pragma unroll
-    for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            float xv[4];
-            get4_signed<T>(xrow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, xv);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[mf][4 * jb + c] = -xv[c];
-        }
     const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
-    xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
-    float r[NMF][16];
-#pragma unroll
-    for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) r[mf][j] = acc[mf][j];
 
-    // in-register Hadamard stages: feature bits 0, 1, 3, 4 (j bits) and the mf bits
-#pragma unroll
-    for (int jbit = 1; jbit < 16; jbit <<= 1)
+    for (int t0 = tb + 32 * wave; t0 < te; t0 += 32 * NWV) {
+        const int tok = t0 + ln;
+        const bool tv = tok < te;
+        // -(s o x) in the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
+        // of its token); an invalid token reads row 0 and stores nothing.  The
+        // X^ products (signs folded into wt) accumulate onto it, leaving -(s o r).
+        const uint8_t *xrow =
+            reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T + (tv ? tok : 0)) * TL::RB;
+        f32x16 acc[NMF];
 #pragma unroll
         for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (!(j & jbit)) {
-                    const float a = r[mf][j], b = r[mf][j | jbit];
-                    r[mf][j] = a + b;
-                    r[mf][j | jbit] = a - b;
-                }
+            for (int jb = 0; jb < 4; ++jb) {
+                float xv[4];
+                get4_signed<T>(xrow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, xv);
 #pragma unroll
-    for (int mbit = 1; mbit < NMF; mbit <<= 1)
+                for (int c = 0; c < 4; ++c) acc[mf][4 * jb + c] = -xv[c];
+            }
+        xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+        float r[NMF][16];
 #pragma unroll
         for (int mf = 0; mf < NMF; ++mf)
-            if (!(mf & mbit))
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float a = r[mf][j], b = r[mf | mbit][j];
-                    r[mf][j] = a + b;
-                    r[mf | mbit][j] = a - b;
-                }
+            for (int j = 0; j < 16; ++j) r[mf][j] = acc[mf][j];
 
-    // feature bit 2 across lane halves; afterwards the lane half is the top
-    // feature bit and y[e] holds in-group element e (+ 32 h for d = 64).  The
-    // butterflies so far ran on -r; the negative 1/sqrt(d) restores the sign
-    // exactly (negation commutes with every rounding here).
-    const float isd = (D == 128) ? -0.08838834764831845f : -0.125f;
-    float y[NE];
+        // in-register Hadamard stages: feature bits 0, 1, 3, 4 (j bits) and the mf bits
 #pragma unroll
-    for (int mp = 0; mp < HALF; ++mp)
+        for (int jbit = 1; jbit < 16; jbit <<= 1)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            float u = r[mp][j], w = r[mp + HALF][j];
-            swap_halves(u, w);
-            const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
-            y[e] = (u + w) * isd;
-            y[e + 4] = (u - w) * isd;
-        }
+            for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (!(j & jbit)) {
+                        const float a = r[mf][j], b = r[mf][j | jbit];
+                        r[mf][j] = a + b;
+                        r[mf][j | jbit] = a - b;
+                    }
+#pragma unroll
+        for (int mbit = 1; mbit < NMF; mbit <<= 1)
+#pragma unroll
+            for (int mf = 0; mf < NMF; ++mf)
+                if (!(mf & mbit))
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const float a = r[mf][j], b = r[mf | mbit][j];
+                        r[mf][j] = a + b;
+                        r[mf | mbit][j] = a - b;
+                    }
 
-    quantize_store<D, BITS>(y, h, tv, (size_t)lh * it.T + tok, it.codes, it.scales);
+        // feature bit 2 across lane halves; afterwards the lane half is the top
+        // feature bit and y[e] holds in-group element e (+ 32 h for d = 64).  The
+        // butterflies so far ran on -r; the negative 1/sqrt(d) restores the sign
+        // exactly (negation commutes with every rounding here).
+        const float isd = (D == 128) ? -0.08838834764831845f : -0.125f;
+        float y[NE];
+#pragma unroll
+        for (int mp = 0; mp < HALF; ++mp)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                float u = r[mp][j], w = r[mp + HALF][j];
+                swap_halves(u, w);
+                const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
+                y[e] = (u + w) * isd;
+                y[e + 4] = (u - w) * isd;
+            }
+
+        quantize_store<D, BITS>(y, h, tv, (size_t)lh * it.T + tok, it.codes, it.scales);
+    }
 }
 
 // ------------------------------------------------------------------ fused decoder
+// The encoder's workgroup shape and tile loop.  A lane's codes for its next
+// tile are loaded while the current tile's products run.
 template <typename T, int D, int BITS, int NWV, bool WL>
-__global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch) {
+__global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch, int tpw) {
     typedef Tile<T, D> TL;
     constexpr int NMF = TL::NMF;
     constexpr int HALF = NMF / 2;
     constexpr int NE = 16 * NMF;
     const Block3 blk = xcd_block();
     const CodecItem &it = batch.it[blk.z];
-    const int lh = blk.y;
-    if (lh >= it.LH || blk.x * 32 * NWV >= it.T) return;
+    const int lh = blk.y, tb = blk.x * tpw;
+    if (lh >= it.LH || tb >= it.T) return;
+    const int te = min(it.T, tb + tpw);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 31, h = lane >> 5;
-    const int t0 = blk.x * 32 * NWV + wave * 32;
-    const int tok = t0 + ln;
-    const bool tv = tok < it.T;
 
-    // the lane's codes and scale first, so that their loads overlap the W~
-    // staging and the X^ products
+    // codes and scale of the lane's token in its first tile; their loads
+    // overlap the W~ staging
     constexpr int NCW = BITS > 0 ? BITS * NE / 32 : 1;
     uint32_t w[NCW];
     uint16_t sbits = 0;
-    if constexpr (BITS > 0) load_codes<D, BITS>(it.codes, it.scales, (size_t)lh * it.T + (tv ? tok : 0), h, w, sbits);
+    auto codes_of = [&](int t0) {
+        const int tok = t0 + ln;
+        if constexpr (BITS > 0)
+            load_codes<D, BITS>(it.codes, it.scales, (size_t)lh * it.T + (tok < te ? tok : tb), h, w, sbits);
+    };
+    if (tb + 32 * wave < te) codes_of(tb + 32 * wave);
 
     const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
 
-    // rotated-back residual first, straight into the accumulators of the X^
-    // products (the MFMA layout), so that it and the products are never live
-    // at the same time
-    f32x16 acc[NMF];
-    if constexpr (BITS > 0) {
-        // codes of the lane's group (or half group) -> scaled values
-        const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
-        const float sc = bf16_to_f32(sbits) * isd;
-        const float off = (float)(1 << (BITS - 1));
-        float y[NE];
-        unpack_codes<BITS, NE>(w, y);
+    for (int t0 = tb + 32 * wave; t0 < te; t0 += 32 * NWV) {
+        const int tok = t0 + ln;
+        const bool tv = tok < te;
+        // rotated-back residual first, straight into the accumulators of the X^
+        // products (the MFMA layout), so that it and the products are never live
+        // at the same time
+        f32x16 acc[NMF];
+        if constexpr (BITS > 0) {
+            // codes of the lane's group (or half group) -> scaled values
+            const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
+            const float sc = bf16_to_f32(sbits) * isd;
+            const float off = (float)(1 << (BITS - 1));
+            float y[NE];
+            unpack_codes<BITS, NE>(w, y);
+            if (t0 + 32 * NWV < te) codes_of(t0 + 32 * NWV);     // the next tile's, in flight meanwhile
 #pragma unroll
-        for (int e = 0; e < NE; ++e) y[e] = fmaf(y[e], sc, -off * sc);
-        // back to the register pairs of the swap stage: y[e], e = (j&3) + 4 sd + 8 (j>>2) + 32 mp
-        // in-register stages over the in-group bits (incl. feature bit 2 = sd)
+            for (int e = 0; e < NE; ++e) y[e] = fmaf(y[e], sc, -off * sc);
+            // back to the register pairs of the swap stage: y[e], e = (j&3) + 4 sd + 8 (j>>2) + 32 mp
+            // in-register stages over the in-group bits (incl. feature bit 2 = sd)
 #pragma unroll
-        for (int bit = 1; bit < NE; bit <<= 1)
+            for (int bit = 1; bit < NE; bit <<= 1)
 #pragma unroll
-            for (int e = 0; e < NE; ++e)
-                if (!(e & bit)) {
-                    const float a = y[e], b = y[e | bit];
-                    y[e] = a + b;
-                    y[e | bit] = a - b;
+                for (int e = 0; e < NE; ++e)
+                    if (!(e & bit)) {
+                        const float a = y[e], b = y[e | bit];
+                        y[e] = a + b;
+                        y[e | bit] = a - b;
+                    }
+            // top feature bit across lane halves; lane half becomes feature bit 2 again
+#pragma unroll
+            for (int mp = 0; mp < HALF; ++mp)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
+                    float u = y[e], v = y[e + 4];
+                    swap_halves(u, v);
+                    acc[mp][j] = u + v;
+                    acc[mp + HALF][j] = u - v;
                 }
-        // top feature bit across lane halves; lane half becomes feature bit 2 again
+        } else {
 #pragma unroll
-        for (int mp = 0; mp < HALF; ++mp)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
-                float u = y[e], v = y[e + 4];
-                swap_halves(u, v);
-                acc[mp][j] = u + v;
-                acc[mp + HALF][j] = u - v;
-            }
-    } else {
-#pragma unroll
-        for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
-    }
-    // s o X~ = rotated-back residual + s o X^
-    xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+            for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
+        }
+        // s o X~ = rotated-back residual + s o X^
+        xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
 
-    // stored from the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
-    // of its token) with the signs
-    if (tv) {
-        uint8_t *orow = reinterpret_cast<uint8_t *>(it.out) + ((size_t)lh * it.T + tok) * TL::RB;
+        // stored from the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
+        // of its token) with the signs
+        if (tv) {
+            uint8_t *orow = reinterpret_cast<uint8_t *>(it.out) + ((size_t)lh * it.T + tok) * TL::RB;
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf)
+            for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                const int j = 4 * jb;
-                put4_signed<T>(orow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, acc[mf][j], acc[mf][j + 1],
-                               acc[mf][j + 2], acc[mf][j + 3]);
-            }
+                for (int jb = 0; jb < 4; ++jb) {
+                    const int j = 4 * jb;
+                    put4_signed<T>(orow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, acc[mf][j], acc[mf][j + 1],
+                                   acc[mf][j + 2], acc[mf][j + 3]);
+                }
+        }
     }
 }
 
@@ -715,12 +731,14 @@ __global__ void k_rademacher_fill(uint64_t key, uint32_t stream, uint64_t first,
 }
 
 // ------------------------------------------------------------------ launchers
-// Workgroups of NW waves x 32 tokens of one (layer, head).  bf16: 8 waves; fp32:
-// 4.  W~ goes through LDS when it fits: 68 KiB for d = 128, r_tp = 128
-// bf16 (hi + lo planes), so two workgroups share a CU.
+// Workgroups of NW waves (16 for bf16, 8 for fp32) over one (layer, head) and
+// a range of tokens.  W~ goes through LDS when it fits (135 KiB for bf16
+// d = 128, r_tp = 256: one workgroup per CU).  The ranges are whole tiles,
+// as many per (layer, head) as give about 1024 workgroups per launch, but no
+// fewer tiles per range than waves.
 template <typename T, int D>
 struct CodecShape {
-    static constexpr int NW = sizeof(T) == 2 ? 8 : 4;
+    static constexpr int NW = 8;
     static size_t wt_lds(int maxRtp) {
         return (size_t)(sizeof(T) == 2 ? 2 : 1) * D * (maxRtp + 16 / sizeof(T)) * sizeof(T);
     }
@@ -728,8 +746,16 @@ struct CodecShape {
     static bool wl(int maxRtp) { return wt_lds(maxRtp) <= 160 * 1024; }
 };
 
-template <void (*K)(CodecBatch)>
-static hipError_t codec_launch(dim3 grid, int threads, size_t lds, hipStream_t s, const CodecBatch &b) {
+static dim3 codec_grid(const CodecBatch &b, int maxT, int maxLH, int nw, int &tpw) {
+    const int tiles = (maxT + 31) / 32;
+    const int pairs = std::max(1, maxLH * b.n);
+    const int split = std::max(1, std::min((1024 + pairs - 1) / pairs, tiles / nw));
+    tpw = 32 * ((tiles + split - 1) / split);
+    return dim3((maxT + tpw - 1) / tpw, maxLH, b.n);
+}
+
+template <void (*K)(CodecBatch, int)>
+static hipError_t codec_launch(dim3 grid, int threads, size_t lds, hipStream_t s, const CodecBatch &b, int tpw) {
     const auto k = K;
     if (lds > 64 * 1024) {
         // raised once per kernel (one instantiation, and so one static, per kernel)
@@ -744,23 +770,27 @@ static hipError_t codec_launch(dim3 grid, int threads, size_t lds, hipStream_t s
         }
         if (state != hipSuccess) return state;
     }
-    hipLaunchKernelGGL(k, grid, dim3(threads), lds, s, b);
+    hipLaunchKernelGGL(k, grid, dim3(threads), lds, s, b, tpw);
     return hipGetLastError();
 }
 
 template <typename T, int D, int BITS>
 static hipError_t encode_one(const CodecBatch &b, int maxT, int maxLH, int maxRtp, hipStream_t s) {
     using CS = CodecShape<T, D>;
-    dim3 grid((maxT + 32 * CS::NW - 1) / (32 * CS::NW), maxLH, b.n);
-    if (CS::wl(maxRtp)) return codec_launch<k_encode<T, D, BITS, CS::NW, true>>(grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b);
-    return codec_launch<k_encode<T, D, BITS, CS::NW, false>>(grid, 64 * CS::NW, 0, s, b);
+    int tpw = 0;
+    const dim3 grid = codec_grid(b, maxT, maxLH, CS::NW, tpw);
+    if (CS::wl(maxRtp))
+        return codec_launch<k_encode<T, D, BITS, CS::NW, true>>(grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b, tpw);
+    return codec_launch<k_encode<T, D, BITS, CS::NW, false>>(grid, 64 * CS::NW, 0, s, b, tpw);
 }
 template <typename T, int D, int BITS>
 static hipError_t decode_one(const CodecBatch &b, int maxT, int maxLH, int maxRtp, hipStream_t s) {
     using CS = CodecShape<T, D>;
-    dim3 grid((maxT + 32 * CS::NW - 1) / (32 * CS::NW), maxLH, b.n);
-    if (CS::wl(maxRtp)) return codec_launch<k_decode<T, D, BITS, CS::NW, true>>(grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b);
-    return codec_launch<k_decode<T, D, BITS, CS::NW, false>>(grid, 64 * CS::NW, 0, s, b);
+    int tpw = 0;
+    const dim3 grid = codec_grid(b, maxT, maxLH, CS::NW, tpw);
+    if (CS::wl(maxRtp))
+        return codec_launch<k_decode<T, D, BITS, CS::NW, true>>(grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b, tpw);
+    return codec_launch<k_decode<T, D, BITS, CS::NW, false>>(grid, 64 * CS::NW, 0, s, b, tpw);
 }
 
 template <typename T, int D>
