@@ -10,7 +10,7 @@ namespace jolt {
 
 constexpr int kMaxBatch = 16;      // items per launch (kernel-argument tables)
 constexpr int kSolverBatch = 64;   // items per launch of the one-workgroup-per-matrix solvers
-constexpr int kPlanGroup = 64;     // items a plan takes through its stages together
+constexpr int kPlanGroup = 256;    // items a plan takes through its stages together
 constexpr int kGroup = 64;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

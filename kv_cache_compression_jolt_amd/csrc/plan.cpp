@@ -165,6 +165,52 @@ struct Ctx {
         if (e_ != hipSuccess) return hip_fail(c.h, e_, where); \
     } while (0)
 
+// The slices of one solver stage spread over the calling stream and the
+// handle's solver streams: slice j on stream j % (kSolverStreams + 1), 0 being
+// the calling stream.  The solver streams wait for the calling stream's work
+// up to the first slice; join() makes the calling stream wait for them.
+class Fan {
+  public:
+    explicit Fan(const Ctx &c, bool on = true) : c_(c), on_(on) {}
+    hipError_t next(hipStream_t *st) {
+        if (!on_) {
+            *st = c_.st;
+            return hipSuccess;
+        }
+        if (n_ == 0) {
+            if (!ss_)
+                if (hipError_t e = solver_streams(c_.h, &ss_); e != hipSuccess) return e;
+            if (hipError_t e = hipEventRecord(ss_->fork, c_.st); e != hipSuccess) return e;
+        }
+        const int j = n_ % (kSolverStreams + 1);
+        ++n_;
+        if (j == 0) {
+            *st = c_.st;
+            return hipSuccess;
+        }
+        if (j > used_) {
+            if (hipError_t e = hipStreamWaitEvent(ss_->st[j - 1], ss_->fork, 0); e != hipSuccess) return e;
+            used_ = j;
+        }
+        *st = ss_->st[j - 1];
+        return hipSuccess;
+    }
+    hipError_t join() {
+        for (int j = 0; j < used_; ++j) {
+            if (hipError_t e = hipEventRecord(ss_->join[j], ss_->st[j]); e != hipSuccess) return e;
+            if (hipError_t e = hipStreamWaitEvent(c_.st, ss_->join[j], 0); e != hipSuccess) return e;
+        }
+        n_ = used_ = 0;
+        return hipSuccess;
+    }
+
+  private:
+    const Ctx &c_;
+    const bool on_;
+    const SolverStreams *ss_ = nullptr;
+    int n_ = 0, used_ = 0;
+};
+
 }  // namespace
 
 // ------------------------------------------------------------------ config and layout
@@ -392,23 +438,29 @@ jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint
     return JOLT_OK;
 }
 
+// fan: spread the slices over the solver streams (else all on c.st)
 jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr, int max_sweeps, bool *noconv,
-                    bool wide_ok) {
+                    bool wide_ok, bool fan_out = true) {
     JacBatch jb{}, tb{}, wb{};
     int maxN = 0, maxT = 0, maxW = 0;
     std::vector<std::vector<EigReq>> large;
     std::vector<int> largeN;
+    // slices of kSolverBatch matrices, spread over the solver streams
+    Fan fan(c, fan_out);
+    hipStream_t fs = nullptr;
     // tridiagonal solver first, Jacobi for what it hands back (n <= kTriMaxN);
     // the wide tridiagonal solver for kTriMaxN < n <= kWideMaxN
     auto flush_tri = [&]() -> jolt_status {
-        HIPCHK(launch_eig_tridiag(tb, maxT, c.st), "eig (tridiagonal)");
-        HIPCHK(launch_jacobi_lds(tb, maxT, max_sweeps, c.st, 1), "eig (Jacobi retry)");
+        HIPCHK(fan.next(&fs), "solver stream");
+        HIPCHK(launch_eig_tridiag(tb, maxT, fs), "eig (tridiagonal)");
+        HIPCHK(launch_jacobi_lds(tb, maxT, max_sweeps, fs, 1), "eig (Jacobi retry)");
         tb.n = 0;
         maxT = 0;
         return JOLT_OK;
     };
     auto flush_wide = [&]() -> jolt_status {
-        HIPCHK(launch_eig_tridiag(wb, maxW, c.st), "eig (wide tridiagonal)");
+        HIPCHK(fan.next(&fs), "solver stream");
+        HIPCHK(launch_eig_tridiag(wb, maxW, fs), "eig (wide tridiagonal)");
         wb.n = 0;
         maxW = 0;
         return JOLT_OK;
@@ -436,7 +488,8 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
             j.raw = 0;
             maxN = std::max(maxN, r.n);
             if (jb.n == kSolverBatch) {
-                HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
+                HIPCHK(fan.next(&fs), "solver stream");
+                HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, fs), "eig");
                 jb.n = 0;
                 maxN = 0;
             }
@@ -448,11 +501,15 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
             large[g].push_back(r);
         }
     }
-    HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
+    if (jb.n) {
+        HIPCHK(fan.next(&fs), "solver stream");
+        HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, fs), "eig");
+    }
     if (tb.n)
         if (jolt_status s = flush_tri()) return s;
     if (wb.n)
         if (jolt_status s = flush_wide()) return s;
+    HIPCHK(fan.join(), "solver join");
     for (size_t g = 0; g < large.size(); ++g)
         for (size_t s0 = 0; s0 < large[g].size(); s0 += kMaxBatch) {
             const std::vector<EigReq> part(large[g].begin() + s0,
@@ -529,6 +586,7 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
                    },
                    [&](const ReduceBatch &b) { return launch_reduce(b, maxCount, c.st); })),
                "orth reduce");
+        Fan fan(c);
         HIPCHK((sliced<CholBatch, kSolverBatch>(
                    nb,
                    [&](CholBatch &b, int i) {
@@ -537,8 +595,13 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
                        ch.inverse = k[i] <= kCholWideMaxK;
                        ch.work = csq[i];
                    },
-                   [&](const CholBatch &b) { return launch_cholesky(b, maxK, c.st); })),
+                   [&](const CholBatch &b) {
+                       hipStream_t fs = nullptr;
+                       if (hipError_t e = fan.next(&fs); e != hipSuccess) return e;
+                       return launch_cholesky(b, maxK, fs);
+                   })),
                "orth cholesky");
+        HIPCHK(fan.join(), "solver join");
         HIPCHK((sliced<TrsmBatch, kMaxBatch>(
                    nb,
                    [&](TrsmBatch &b, int i) {
@@ -562,8 +625,9 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
 
 // One group of up to kPlanGroup items: every stage runs for all of them
 // before the next, with launches of kMaxBatch items for the streaming kernels
-// and kSolverBatch items for the one-workgroup-per-matrix solvers, whose
-// launches would otherwise leave most CUs idle.
+// and kSolverBatch items for the one-workgroup-per-matrix solvers, those
+// slices spread over the solver streams so that they run at once (one slice
+// alone would leave most CUs idle).
 jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items,
                            int i0, int nb, const void *const *x_dev, uint8_t *ws, bool *noconv, bool wide_ok,
                            hipStream_t *forked) {
@@ -635,7 +699,8 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                    [&](const SmallBatch &b) { return launch_trace_batch(b, side); })),
                "trace");
         const Ctx cs{c.h, side, c.dtype, c.d};
-        if (jolt_status es = eig_all(cs, feigs, scr, max_sweeps, noconv, wide_ok)) return es;
+        // kept on the side stream: the solver streams are the token eigenproblems'
+        if (jolt_status es = eig_all(cs, feigs, scr, max_sweeps, noconv, wide_ok, false)) return es;
         HIPCHK(hipEventRecord(join, side), "join");
         return JOLT_OK;
     };
@@ -962,14 +1027,14 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     return JOLT_OK;
 }
 
-// One group of the plan.  Work forked onto the side stream reads the inputs and
-// writes the workspace, so an error after the fork waits for that stream
+// One group of the plan.  Work forked onto the side and solver streams reads
+// the inputs and writes the workspace, so an error waits for those streams
 // before returning: everything launched has finished when jolt_plan returns.
 jolt_status run_group(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items, int i0,
                       int nb, const void *const *x_dev, uint8_t *ws, bool *noconv, bool wide_ok) {
     hipStream_t forked = nullptr;
     jolt_status s = run_group_body(c, cfg, pl, items, i0, nb, x_dev, ws, noconv, wide_ok, &forked);
-    if (s != JOLT_OK && forked) (void)hipStreamSynchronize(forked);
+    if (s != JOLT_OK) drain_streams(c.h);
     return s;
 }
 
