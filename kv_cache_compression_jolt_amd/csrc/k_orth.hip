@@ -311,99 +311,169 @@ __global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
     }
 }
 
-// One wave per 32-row block tm of Q (K = 32 (tm + 1): X is lower triangular).
-// X is staged in LDS once per workgroup (zero outside the k x k triangle; read
-// from global memory when it does not fit), and the workgroup walks column
-// blocks of 64 (cb = blockIdx.x, + gridDim.x, ...): each block of Y (all P
-// rows, zero past k and len) goes through LDS, the next one is loaded into
-// registers while the current one is multiplied.
-constexpr int kApplyYS = 68;                // row stride of a staged Y block
-
-template <bool XLDS, int KMAX>
-__global__ __launch_bounds__(64 * KMAX / 32) void k_apply_linv(TrsmBatch batch, int ldx) {
-    extern __shared__ float sh[];
-    const TrsmItem &it = batch.it[blockIdx.y];
-    const int k = it.k, ntm = (k + 31) >> 5, P = 32 * ntm, nthr = 64 * ntm;
-    const int ncb = (it.len + 63) >> 6;
-    if ((int)blockIdx.x >= ncb || (int)threadIdx.x >= nthr) return;      // whole waves leave together
-    const int tid = threadIdx.x, lane = tid & 63, tm = tid >> 6;
-    const int m32 = lane & 31, kh = lane >> 5, m = 32 * tm + m32, mc = min(m, k - 1);
-    float *ys = sh;                             // [P][kApplyYS]
-    float *xs = sh + P * kApplyYS;              // [P][ldx] when XLDS
-    if constexpr (XLDS) {
-        for (int e = tid; e < P * P / 4; e += nthr) {
-            const int r = e / (P / 4), c = 4 * (e % (P / 4));
-            const bool ok = r < k && c < k;
-            float4 v = *reinterpret_cast<const float4 *>(it.l + (size_t)(ok ? r : 0) * it.ld + (ok ? c : 0));
-            if (!ok) v = make_float4(0.f, 0.f, 0.f, 0.f);
-            float *d = xs + r * ldx + c;
-            d[0] = c < k ? v.x : 0.f;
-            d[1] = c + 1 < k ? v.y : 0.f;
-            d[2] = c + 2 < k ? v.z : 0.f;
-            d[3] = c + 3 < k ? v.w : 0.f;
+// One workgroup of 4 waves (one per SIMD) per item slice.  The triangle's
+// 32-row blocks (block tm needs K = 32 (tm + 1) columns of X) are dealt to the
+// waves largest first, each to the least loaded wave, so that the waves' MFMA
+// counts differ by at most a block's.  Each wave keeps its blocks' rows of X in
+// registers for the whole kernel (the A fragments of v_mfma_f32_32x32x2f32:
+// lane l holds X[32 tm + l % 32][2 i + l / 32], i = 0 .. 16 (tm + 1) - 1), and
+// the workgroup walks 32-column blocks of Y (cb = blockIdx.x, + gridDim.x, ...)
+// through double-buffered LDS: all P rows of the block as ys[r][c] (row pitch
+// 32: a B fragment is one wave-wide read of 64 consecutive floats), the next
+// block loaded into registers while the current one is multiplied.
+template <int NTM>
+struct ApplyDeal {
+    int cnt[4] = {0, 0, 0, 0};
+    int tm[4][3] = {{0, 0, 0}, {0, 0, 0}, {0, 0, 0}, {0, 0, 0}};
+    int load[4] = {0, 0, 0, 0};
+    constexpr ApplyDeal() {
+        for (int b = NTM - 1; b >= 0; --b) {
+            int w = 0;
+            for (int i = 1; i < 4; ++i)
+                if (load[i] < load[w]) w = i;
+            tm[w][cnt[w]++] = b;
+            load[w] += b + 1;
         }
     }
-    // staging of a Y block: P rows x 16 float4 = exactly 8 pieces per thread
-    constexpr int kPer = 8;
-    float4 stg[kPer];
-    auto load_y = [&](int cb) {
-        const int c0 = cb * 64;
+    constexpr int regs(int w) const { return 16 * load[w]; }
+    constexpr int max_regs() const {
+        int m = 0;
+        for (int w = 0; w < 4; ++w) m = regs(w) > m ? regs(w) : m;
+        return m;
+    }
+    constexpr int max_cnt() const {
+        int m = 0;
+        for (int w = 0; w < 4; ++w) m = cnt[w] > m ? cnt[w] : m;
+        return m;
+    }
+};
+
+constexpr int kApplyCols = 32;                      // columns of Y per block
+
+// wave W's rows of X into xr (block r of the wave at offset 16 sum_{r' < r} (tm_r' + 1))
+template <int NTM, int W>
+__device__ __forceinline__ void apply_load_x(const TrsmItem &it, int lane, float *xr) {
+    constexpr ApplyDeal<NTM> D{};
+    const int m32 = lane & 31, kh = lane >> 5;
+    int off = 0;
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int p = tid + nthr * q;
-            const int r = p >> 4, c = c0 + 4 * (p & 15);
-            const bool ok = r < k && c < it.len;     // len is a multiple of 4
+    for (int r = 0; r < D.cnt[W]; ++r) {
+        const int tm = D.tm[W][r];
+        const int row = 32 * tm + m32;
+        const bool rok = row < it.k;
+        const float *xrow = it.l + (size_t)(rok ? row : 0) * it.ld;
+#pragma unroll
+        for (int i = 0; i < 16 * (tm + 1); ++i) {
+            const int col = 2 * i + kh;
+            xr[off + i] = ld_or_zero(xrow, col < it.k ? col : 0, rok && col < it.k);
+        }
+        off += 16 * (tm + 1);
+    }
+}
+
+// acc[r] = (rows of wave W's block r) x (the staged block ys)
+template <int NTM, int W, int MC>
+__device__ __forceinline__ void apply_mul(const float *xr, const float *ys, int lane, f32x16 *acc) {
+    constexpr ApplyDeal<NTM> D{};
+    const int m32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < MC; ++r) acc[r] = f32x16{};
+    if constexpr (D.cnt[W] > 0) {
+        constexpr int IMAX = 16 * (D.tm[W][0] + 1);         // the wave's largest block comes first
+#pragma unroll
+        for (int i = 0; i < IMAX; ++i) {
+            const float b = ys[(2 * i + kh) * kApplyCols + m32];
+            int off = 0;
+#pragma unroll
+            for (int r = 0; r < D.cnt[W]; ++r) {
+                const int n = 16 * (D.tm[W][r] + 1);
+                if (i < n) acc[r] = __builtin_amdgcn_mfma_f32_32x32x2f32(xr[off + i], b, acc[r], 0, 0, 0);
+                off += n;
+            }
+        }
+    }
+}
+
+template <int NTM, int W, int MC>
+__device__ __forceinline__ void apply_store(const TrsmItem &it, int lane, int c0, const f32x16 *acc) {
+    constexpr ApplyDeal<NTM> D{};
+    const int m32 = lane & 31;
+    const int col = c0 + m32;
+    if (col >= it.len) return;
+#pragma unroll
+    for (int r = 0; r < D.cnt[W]; ++r) {
+        const int tm = D.tm[W][r];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int row = 32 * tm + frag_row(lane, j);
+            const float v = acc[r][j];
+            if (row < it.k) it.q[(size_t)row * it.ldy + col] = v;
+            if (it.qh) {
+                // bf16 copies for the next sketch pass, every row (rows k .. P - 1 are zero)
+                const uint16_t hv = f32_to_bf16(v);
+                it.qh[(size_t)row * it.ldy + col] = hv;
+                if (it.ql) it.ql[(size_t)row * it.ldy + col] = f32_to_bf16(v - bf16_to_f32(hv));
+            }
+        }
+    }
+}
+
+template <int NTM>
+__global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch) {
+    constexpr ApplyDeal<NTM> D{};
+    constexpr int P = 32 * NTM, XR = D.max_regs(), MC = D.max_cnt();
+    constexpr int PIECES = P * kApplyCols / 4, PPT = (PIECES + 255) / 256;   // float4 pieces of a block
+    extern __shared__ float sh[];
+    const TrsmItem &it = batch.it[blockIdx.y];
+    const int ncb = (it.len + kApplyCols - 1) / kApplyCols;
+    if ((int)blockIdx.x >= ncb || it.k > P) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    float xr[XR];
+    switch (wave) {
+        case 0: apply_load_x<NTM, 0>(it, lane, xr); break;
+        case 1: apply_load_x<NTM, 1>(it, lane, xr); break;
+        case 2: apply_load_x<NTM, 2>(it, lane, xr); break;
+        default: apply_load_x<NTM, 3>(it, lane, xr); break;
+    }
+    float4 stg[PPT];
+    auto load_y = [&](int cb) {
+        const int c0 = cb * kApplyCols;
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) {
+            const int p = tid + 256 * q;
+            const int r = p / (kApplyCols / 4), c = c0 + 4 * (p % (kApplyCols / 4));
+            const bool ok = p < PIECES && r < it.k && c < it.len;     // len is a multiple of 4
             const float4 v = *reinterpret_cast<const float4 *>(it.y + (size_t)(ok ? r : 0) * it.ldy + (ok ? c : 0));
             stg[q] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
-    auto store_y = [&]() {
+    auto store_y = [&](float *ys) {
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int p = tid + nthr * q;
-            *reinterpret_cast<float4 *>(ys + (p >> 4) * kApplyYS + 4 * (p & 15)) = stg[q];
+        for (int q = 0; q < PPT; ++q) {
+            const int p = tid + 256 * q;
+            if (p < PIECES) *reinterpret_cast<float4 *>(ys + 4 * p) = stg[q];
         }
     };
-    const int kend = 32 * (tm + 1);
-    const float *xrow = XLDS ? xs + m * ldx : it.l + (size_t)mc * it.ld;
-    int cb = blockIdx.x;
+    int cb = blockIdx.x, buf = 0;
     load_y(cb);
+    store_y(sh);
+    __syncthreads();
     for (;;) {
-        __syncthreads();                        // the previous block's reads of ys are done
-        store_y();
-        __syncthreads();
         const int next = cb + gridDim.x;
         if (next < ncb) load_y(next);
-        f32x16 acc0 = {}, acc1 = {};
-#pragma unroll 8
-        for (int k0 = 0; k0 < kend; k0 += 2) {
-            const int kk = k0 + kh;
-            const float a = XLDS ? xrow[kk] : ld_or_zero(xrow, min(kk, k - 1), m < k && kk < k);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, ys[kk * kApplyYS + m32], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, ys[kk * kApplyYS + 32 + m32], acc1, 0, 0, 0);
-        }
-        const int c0 = cb * 64;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int row = 32 * tm + frag_row(lane, jj);
-            if (row < k) {
-                if (c0 + m32 < it.len) it.q[(size_t)row * it.ldy + c0 + m32] = acc0[jj];
-                if (c0 + 32 + m32 < it.len) it.q[(size_t)row * it.ldy + c0 + 32 + m32] = acc1[jj];
-            }
-            if (it.qh) {
-                // bf16 copies for the next sketch pass, every row (rows k .. P - 1 are zero)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int col = c0 + 32 * u + m32;
-                    if (col >= it.len) continue;
-                    const float v = u ? acc1[jj] : acc0[jj];
-                    const uint16_t hv = f32_to_bf16(v);
-                    it.qh[(size_t)row * it.ldy + col] = hv;
-                    if (it.ql) it.ql[(size_t)row * it.ldy + col] = f32_to_bf16(v - bf16_to_f32(hv));
-                }
-            }
+        const float *ys = sh + buf * P * kApplyCols;
+        f32x16 acc[MC];
+        const int c0 = cb * kApplyCols;
+        switch (wave) {
+            case 0: apply_mul<NTM, 0, MC>(xr, ys, lane, acc); apply_store<NTM, 0, MC>(it, lane, c0, acc); break;
+            case 1: apply_mul<NTM, 1, MC>(xr, ys, lane, acc); apply_store<NTM, 1, MC>(it, lane, c0, acc); break;
+            case 2: apply_mul<NTM, 2, MC>(xr, ys, lane, acc); apply_store<NTM, 2, MC>(it, lane, c0, acc); break;
+            default: apply_mul<NTM, 3, MC>(xr, ys, lane, acc); apply_store<NTM, 3, MC>(it, lane, c0, acc); break;
         }
         if (next >= ncb) break;
+        store_y(sh + (buf ^ 1) * P * kApplyCols);
+        __syncthreads();
+        buf ^= 1;
         cb = next;
     }
 }
@@ -418,9 +488,9 @@ static hipError_t orth_lds_attrs() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
         hipError_t e = allow_lds(reinterpret_cast<const void *>(k_chol_inv<false>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<true, kCholInverseMaxK>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<false, kCholInverseMaxK>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<false, kCholWideMaxK>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<7>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<8>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<9>));
         state = e;
     }
     return state;
@@ -442,28 +512,35 @@ hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int NTM>
+static void apply_launch(const TrsmBatch &b, int gx, hipStream_t s) {
+    const size_t lds = (size_t)2 * 32 * NTM * kApplyCols * sizeof(float);
+    hipLaunchKernelGGL(k_apply_linv<NTM>, dim3(gx, b.n), dim3(256), lds, s, b);
+}
+
 hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     if (maxK > kCholWideMaxK) return hipErrorInvalidValue;
     for (int i = 0; i < b.n; ++i)
-        if (b.it[i].len % 4 || b.it[i].ldy % 4 || b.it[i].ld % 4) return hipErrorInvalidValue;
+        if (b.it[i].len % 4 || b.it[i].ldy % 4 || b.it[i].k > maxK) return hipErrorInvalidValue;
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
     KTimeScope kts("k_apply_linv", s);
-    const int ntm = (maxK + 31) / 32, P = 32 * ntm, ldx = P + 1;
-    const size_t ylds = (size_t)P * kApplyYS * sizeof(float);
-    const size_t xlds = (size_t)P * ldx * sizeof(float);
-    const bool xin = ylds + xlds <= 150 * 1024;
-    // about one workgroup per CU over the batch; each walks its column blocks (L^-1 is
-    // staged once per workgroup, so fewer, longer workgroups read less of it)
-    const int ncb = (maxLen + 63) / 64;
+    const int ntm = std::max(1, (maxK + 31) / 32);
+    // about one workgroup per CU over the batch; each walks its column blocks
+    // (X is loaded once per workgroup, so fewer, longer workgroups read less of it)
+    const int ncb = (maxLen + kApplyCols - 1) / kApplyCols;
     const int gx = std::max(1, std::min(ncb, (256 + b.n - 1) / b.n));
-    if (maxK > kCholInverseMaxK)
-        hipLaunchKernelGGL((k_apply_linv<false, kCholWideMaxK>), dim3(gx, b.n), dim3(64 * ntm), ylds, s, b, ldx);
-    else if (xin)
-        hipLaunchKernelGGL((k_apply_linv<true, kCholInverseMaxK>), dim3(gx, b.n), dim3(64 * ntm), ylds + xlds, s, b,
-                           ldx);
-    else
-        hipLaunchKernelGGL((k_apply_linv<false, kCholInverseMaxK>), dim3(gx, b.n), dim3(64 * ntm), ylds, s, b, ldx);
+    switch (ntm) {
+        case 1: apply_launch<1>(b, gx, s); break;
+        case 2: apply_launch<2>(b, gx, s); break;
+        case 3: apply_launch<3>(b, gx, s); break;
+        case 4: apply_launch<4>(b, gx, s); break;
+        case 5: apply_launch<5>(b, gx, s); break;
+        case 6: apply_launch<6>(b, gx, s); break;
+        case 7: apply_launch<7>(b, gx, s); break;
+        case 8: apply_launch<8>(b, gx, s); break;
+        default: apply_launch<9>(b, gx, s); break;
+    }
     return hipGetLastError();
 }
 
