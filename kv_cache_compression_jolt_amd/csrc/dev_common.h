@@ -106,6 +106,22 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Scheduling hint for an unrolled run of N LDS fragment reads, each feeding M
+// MFMAs: the reads are issued AHEAD in front of the MFMAs, then one read per
+// M MFMAs, so that AHEAD reads are in flight while the MFMAs run (without it
+// the scheduler puts each read right before its MFMA and waits for it there).
+template <int N, int M, int AHEAD>
+__device__ __forceinline__ void sched_reads_ahead() {
+    constexpr int A = AHEAD < N ? AHEAD : N;
+    __builtin_amdgcn_sched_group_barrier(0x100, A, 0);          // DS reads
+#pragma unroll
+    for (int i = 0; i < N - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, M * A, 0);
+}
+
 // ---------------------------------------------------------------- wave reductions
 // Sums within aligned lane groups of 4, 8 and 16 use DPP lane moves inside a
 // row of 16 lanes (quad permutes, then the half-row and row mirrors), which

@@ -268,17 +268,35 @@ __device__ __forceinline__ void xhat_mfma(const T *wt, const T *wlo, int rtp, co
             b[q] = vec ? frag_or_zero(urow + min(kk, rt - 8), ok)
                        : (ok ? load_frag_n(urow + kk, rt - kk) : zero_frag(ut));
         }
+        if (k0b + 16 * KB <= rt) {
+            // a whole batch, one straight run: per K step the hi products of
+            // every feature block, then the lo ones (no MFMA waits on the one
+            // before it), with the W~ fragment reads kept ahead of them
 #pragma unroll
-        for (int q = 0; q < KB; ++q) {
-            const int kk = k0b + 16 * q + 8 * h;
-            if (k0b + 16 * q >= rt) break;
+            for (int q = 0; q < KB; ++q) {
+                const int kk = k0b + 16 * q + 8 * h;
 #pragma unroll
-            for (int mf = 0; mf < NMF; ++mf) {
-                typename Elem<T>::Frag a = load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk);
-                mfma(a, b[q], acc[mf]);
-                if constexpr (sizeof(T) == 2) {
-                    typename Elem<T>::Frag al = load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk);
-                    mfma(al, b[q], acc[mf]);
+                for (int mf = 0; mf < NMF; ++mf)
+                    mfma(load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk), b[q], acc[mf]);
+                if constexpr (sizeof(T) == 2)
+#pragma unroll
+                    for (int mf = 0; mf < NMF; ++mf)
+                        mfma(load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk), b[q], acc[mf]);
+            }
+            if constexpr (sizeof(T) == 2) sched_reads_ahead<KB * NMF * 2, 1, 4>();
+        } else {
+#pragma unroll
+            for (int q = 0; q < KB; ++q) {
+                const int kk = k0b + 16 * q + 8 * h;
+                if (k0b + 16 * q >= rt) break;
+#pragma unroll
+                for (int mf = 0; mf < NMF; ++mf) {
+                    typename Elem<T>::Frag a = load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk);
+                    mfma(a, b[q], acc[mf]);
+                    if constexpr (sizeof(T) == 2) {
+                        typename Elem<T>::Frag al = load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk);
+                        mfma(al, b[q], acc[mf]);
+                    }
                 }
             }
         }

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64 * NWV) void k_xm(XmBatch batch, int d, int ncol_
     extern __shared__ __attribute__((aligned(16))) unsigned char xm_lds[];
     T *ms = reinterpret_cast<T *>(xm_lds);                  // [2][ROWS][KP]
     const Block3 blk = xcd_block();
-    const XmItem &it = batch.it[blk.z];
+    const XmItem it = batch.it[blk.z];      // a copy: its fields stay in registers
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln = lane & 31, h = lane >> 5;
     const int tw = blk.x * 256 + wave * 32 * R;             // this wave's first token
     const int c0 = (blk.y % ncol_tiles) * ROWS;
@@ -138,6 +138,8 @@ __global__ __launch_bounds__(64 * NWV) void k_xm(XmBatch batch, int d, int ncol_
 #pragma unroll
                     for (int r = 0; r < R; ++r) mfma(a[r][u], b, acc[r][f]);
                 }
+            // LDS reads kept 4 ahead of the MFMAs that use them
+            sched_reads_ahead<U * NF, R, 4>();
         }
         if (more) store_m((ci + 1) & 1);
     }
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
     T *xs = reinterpret_cast<T *>(xtq_lds);               // [FT][XP]
     T *qs = xs + FT * XP;                                 // [QR][XP]
     const Block3 blk = xcd_block();
-    const XtqItem &it = batch.it[blk.z];
+    const XtqItem it = batch.it[blk.z];     // a copy: its fields stay in registers
     const int n = it.LH * d;
     const int F0 = blk.y * FT, sp = blk.x % maxSplit, c0 = (blk.x / maxSplit) * 32 * NF;
     if (F0 >= n || sp >= it.nsplit || c0 >= it.ncols) return;
@@ -335,6 +337,9 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
                 }
             }
         }
+        // LDS reads kept ahead of the MFMAs (per 16 tokens: R x fragments, then
+        // one q fragment per R MFMAs)
+        if constexpr (BF) sched_reads_ahead<(TC / 16) * (R + NF * (LO ? 2 : 1)), R, 4>();
     }
     float *out = it.out + (size_t)sp * it.ncols * n;
 #pragma unroll
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
     constexpr int PER = 16 / sizeof(T);            // features per 16-byte piece
     constexpr int XP = 64 + PER;                   // pitch (elements) of a feature's row in xs
     __shared__ __attribute__((aligned(16))) T xs[128 * XP];
-    const GramItem &it = batch.it[blockIdx.z];
+    const GramItem it = batch.it[blockIdx.z];   // a copy: its fields stay in registers
     const int p = blockIdx.x;
     if (p >= it.P) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, h = lane >> 5;

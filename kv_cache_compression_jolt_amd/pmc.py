@@ -17,6 +17,12 @@ Kernel-time table from a `rocprofv3 --kernel-trace --stats --output-format csv`
 run:
 
   python3 -m kv_cache_compression_jolt_amd.pmc trace-summary D OUT "TITLE" "COMMAND"
+
+Per-kernel means per dispatch of every counter in the counter runs under D
+(one subfolder per pass; derived metrics such as MfmaUtil, LdsUtil,
+LdsBankConflict and OccupancyPercent are computed by rocprofv3 itself):
+
+  python3 -m kv_cache_compression_jolt_amd.pmc counters D OUT "TITLE" "COMMANDS" KERNEL [KERNEL ...]
 """
 from __future__ import annotations
 
@@ -125,6 +131,45 @@ def trace_summary(d, out, title, command):
     print("wrote", out)
 
 
+def _all_rows(d):
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                r["_file"] = f
+                out.append(r)
+    return out
+
+
+def counters(d, out, title, commands, kernels):
+    rows = _all_rows(d)
+    table = {}
+    for k in kernels:
+        is_k = lambda name, k=k: ("::%s(" % k) in name or ("::%s<" % k) in name or name.startswith(k)
+        per = {}
+        for r in rows:
+            if not is_k(r.get("Kernel_Name", "")):
+                continue
+            key = (r["_file"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            name = r.get("Counter_Name", "").strip()
+            per.setdefault(name, {}).setdefault(key, 0.0)
+            per[name][key] += float(r["Counter_Value"])
+        table[k] = {n: (sum(v.values()) / len(v), len(v)) for n, v in per.items()}
+    names = sorted({n for t in table.values() for n in t})
+    with open(out, "w") as fh:
+        fh.write("%s\ncommands:\n%s\n\n" % (title, commands))
+        fh.write("mean per dispatch (dispatches in brackets)\n")
+        for k in kernels:
+            fh.write("\n%s\n" % k)
+            for n in names:
+                if n in table[k]:
+                    v, c = table[k][n]
+                    fh.write("  %-28s %16.6g  [%d]\n" % (n, v, c))
+        fh.write("\nsource sha256[:16]: %s\n" % ", ".join(
+            "%s %s" % (k, source_hash(k)) for k in kernels if k in SOURCES))
+    print("wrote", out)
+
+
 if __name__ == "__main__":
     cmd = sys.argv[1] if len(sys.argv) > 1 else ""
     if cmd == "copy":
@@ -133,5 +178,7 @@ if __name__ == "__main__":
         summarize(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     elif cmd == "trace-summary":
         trace_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    elif cmd == "counters":
+        counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6:])
     else:
         raise SystemExit(__doc__)
