@@ -135,13 +135,14 @@ def roof(bytes_, flops, unit, ms):
 
 
 def source_hash(kernel):
-    """Hash of the kernel's source and of plan.cpp and api.cpp (which size and
-    group its launches), as recorded with the counters in profiles/."""
+    """Hash of the kernel's source, of the shared device helpers and of
+    plan.cpp and api.cpp (which size and group its launches), as recorded with
+    the counters in profiles/."""
     f = KERNEL_SOURCE.get(kernel)
     if not f:
         return None
     h = hashlib.sha256()
-    for name in (f, "plan.cpp", "api.cpp"):
+    for name in (f, "dev_common.h", "plan.cpp", "api.cpp"):
         with open(os.path.join(ROOT, "kv_cache_compression_jolt_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -34,7 +34,8 @@ import sys
 
 COPY_BYTES = 512 * 1024 * 1024
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCES = {"k_eig_tridiag": "k_eig.hip", "k_eig_trivec": "k_eig.hip", "k_eig_backtr": "k_eig.hip", "k_eig_polish": "k_eig.hip", "k_chol_inv": "k_orth.hip", "k_apply_linv": "k_orth.hip",
+SOURCES = {"k_eig_tridiag": "k_eig.hip", "k_eig_trivec": "k_eig.hip", "k_eig_backtr": "k_eig.hip", "k_eig_polish": "k_eig.hip",
+           "k_eig_tridiag_w": "k_eig.hip", "k_eig_backtr_w": "k_eig.hip", "k_eig_polish_w": "k_eig.hip", "k_chol_inv": "k_orth.hip", "k_apply_linv": "k_orth.hip",
            "k_gemm": "k_gemm.hip", "k_sym_gram": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
            "k_encode": "k_codec.hip", "k_decode": "k_codec.hip", "k_build_wt": "k_codec.hip"}
 
@@ -78,11 +79,12 @@ def _per_dispatch(d, counter, match):
 
 
 def source_hash(kernel):
-    """Hash of the kernel's source and of the plan orchestration that sizes
-    and groups its launches: counters taken before a change to either no
-    longer describe a launch."""
+    """Hash of the kernel's source, of the shared device helpers and of the
+    host code that sizes and groups its launches (plan.cpp, api.cpp): counters
+    taken before a change to any of them no longer describe a launch.  The
+    same files as bench.py's source_hash."""
     h = hashlib.sha256()
-    for f in (SOURCES[kernel], "plan.cpp"):
+    for f in (SOURCES[kernel], "dev_common.h", "plan.cpp", "api.cpp"):
         with open(os.path.join(ROOT, "kv_cache_compression_jolt_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -94,7 +96,7 @@ def summarize(d, kernel, workload, commands):
     cw = max(_per_dispatch(os.path.join(d, "copy_write"), "WRITE_SIZE", is_copy))
     f_fetch = COPY_BYTES / (cf * 1024.0)
     f_write = COPY_BYTES / (cw * 1024.0)
-    is_k = lambda name: ("::%s" % kernel) in name or name.startswith(kernel)
+    is_k = lambda name: ("::%s(" % kernel) in name or ("::%s<" % kernel) in name or name.startswith(kernel + "(")
     kf = _per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", is_k)
     kw = _per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", is_k)
     if not kf or not kw:
@@ -112,7 +114,7 @@ def summarize(d, kernel, workload, commands):
         fh.write("fetch bytes per launch (scaled): %.6g\n" % fetch)
         fh.write("write bytes per launch (scaled): %.6g\n" % write)
         fh.write("hbm bytes per launch: %.6g\n" % (fetch + write))
-        fh.write("source sha256[:16]: %s (%s + plan.cpp)\n" % (source_hash(kernel), SOURCES[kernel]))
+        fh.write("source sha256[:16]: %s (%s + dev_common.h + plan.cpp + api.cpp)\n" % (source_hash(kernel), SOURCES[kernel]))
     print("wrote", path)
 
 
