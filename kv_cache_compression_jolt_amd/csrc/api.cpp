@@ -26,7 +26,6 @@ struct jolt_handle_s {
     std::string err;
     hipStream_t side = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
-    jolt::SolverStreams solver{};   // created on first use (solver.fork set)
     jolt::DualTables dual;
     uint8_t *readback = nullptr;    // pinned host memory for the plan's one readback
     size_t readback_cap = 0;
@@ -134,32 +133,8 @@ hipError_t side_stream(jolt_handle h, hipStream_t *st, hipEvent_t *fork, hipEven
     return hipSuccess;
 }
 
-hipError_t solver_streams(jolt_handle h, const SolverStreams **out) {
-    if (!h->solver.fork) {
-        SolverStreams s{};
-        hipError_t e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming);
-        for (int i = 0; i < kSolverStreams && e == hipSuccess; ++i) {
-            e = hipStreamCreateWithFlags(&s.st[i], hipStreamNonBlocking);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&s.join[i], hipEventDisableTiming);
-        }
-        if (e != hipSuccess) {
-            for (int i = 0; i < kSolverStreams; ++i) {
-                if (s.join[i]) (void)hipEventDestroy(s.join[i]);
-                if (s.st[i]) (void)hipStreamDestroy(s.st[i]);
-            }
-            if (s.fork) (void)hipEventDestroy(s.fork);
-            return e;
-        }
-        h->solver = s;
-    }
-    *out = &h->solver;
-    return hipSuccess;
-}
-
 void drain_streams(jolt_handle h) {
     if (h->side) (void)hipStreamSynchronize(h->side);
-    if (h->solver.fork)
-        for (int i = 0; i < kSolverStreams; ++i) (void)hipStreamSynchronize(h->solver.st[i]);
 }
 
 void sign_bits_for(uint64_t seed, uint32_t item_id, int d, uint32_t out[4]) {
@@ -221,20 +196,12 @@ extern "C" jolt_status jolt_create(int hip_device, jolt_handle *out) {
 
 extern "C" void jolt_destroy(jolt_handle h) {
     if (!h) return;
-    if (h->side || h->solver.fork) (void)hipSetDevice(h->device);
     if (h->side) {
+        (void)hipSetDevice(h->device);
         (void)hipStreamSynchronize(h->side);
         (void)hipEventDestroy(h->join);
         (void)hipEventDestroy(h->fork);
         (void)hipStreamDestroy(h->side);
-    }
-    if (h->solver.fork) {
-        for (int i = 0; i < kSolverStreams; ++i) {
-            (void)hipStreamSynchronize(h->solver.st[i]);
-            (void)hipEventDestroy(h->solver.join[i]);
-            (void)hipStreamDestroy(h->solver.st[i]);
-        }
-        (void)hipEventDestroy(h->solver.fork);
     }
     if (h->readback) (void)hipHostFree(h->readback);
     if (h->sweep) (void)hipHostFree(h->sweep);

@@ -41,21 +41,8 @@ hipError_t sweep_buffer(jolt_handle h, float **buf);
 // use and destroyed with the handle) and two events, for work forked off the
 // caller's stream and joined back to it within one call.
 hipError_t side_stream(jolt_handle h, hipStream_t *st, hipEvent_t *fork, hipEvent_t *join);
-// kSolverStreams more streams on the handle's device (default priority, created
-// on first use, destroyed with the handle), a fork event and one join event per
-// stream: slices of the one-workgroup-per-matrix solver launches spread over
-// them and the caller's stream and run at once.  Two: with the caller's and
-// the side stream that makes four, the hardware queues HIP gives a process by
-// default (streams beyond those share a queue and run one after the other).
-constexpr int kSolverStreams = 2;
-struct SolverStreams {
-    hipStream_t st[kSolverStreams];
-    hipEvent_t fork;
-    hipEvent_t join[kSolverStreams];
-};
-hipError_t solver_streams(jolt_handle h, const SolverStreams **out);
-// Waits for the handle's own streams (side and solver streams, those that
-// exist): an error path's guarantee that nothing it launched still runs.
+// Waits for the handle's side stream (if it exists): an error path's
+// guarantee that nothing it launched still runs.
 void drain_streams(jolt_handle h);
 jolt_status check_item(jolt_handle h, const jolt_item &it);
 jolt_status check_alloc(jolt_handle h, const jolt_item &it, const jolt_alloc &a);

@@ -194,7 +194,8 @@ __device__ __forceinline__ void wblock_t_full(float *D, int ld, const float *tau
             if (i <= c) D[c * ld + i] = x[i];
 }
 
-__global__ __launch_bounds__(kThreads) void k_eig_tridiag(JacBatch batch, int ld, int boff, int poff) {
+template <class B>
+__global__ __launch_bounds__(kThreads) void k_eig_tridiag(B batch, int ld, int boff, int poff) {
     extern __shared__ float sm[];
     __shared__ float sd[kTriMaxN], se[kTriMaxN], stau[kTriMaxN];
     __shared__ float sx0[kTriMaxN], sx1[kTriMaxN], sp[kTriMaxN], sy[64];
@@ -459,7 +460,8 @@ constexpr int kWCols = 9;
 constexpr int kXpPitch = 33;
 constexpr size_t kWTriLds = ((size_t)kWideMaxN * (kXpPitch + 2 * kPanelStride) + 6 * kWideMaxN + 64) * 4;
 
-__global__ __launch_bounds__(kWThreads) void k_eig_tridiag_w(JacBatch batch) {
+template <class B>
+__global__ __launch_bounds__(kWThreads) void k_eig_tridiag_w(B batch) {
     extern __shared__ float sm[];
     const JacItem &it = batch.it[blockIdx.x];
     const int n = it.n;
@@ -742,8 +744,8 @@ __device__ void wy_block(const TriWs &w, int n, int b, float *lds, int lane) {
     }
 }
 
-template <int NMAX>
-__global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch, int eig_blocks) {
+template <int NMAX, class B>
+__global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(B batch, int eig_blocks) {
     constexpr int kTriMaxN = NMAX, kVecPad = VecDims<NMAX>::kVecPad;
     __shared__ __attribute__((aligned(16))) float lds[VecDims<NMAX>::kLds];
     const JacItem &it = batch.it[blockIdx.y];
@@ -960,7 +962,8 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(JacBatch batch, i
 // the row tiles Z_c -= Y M.  V_c goes back over Z_c^T in the workspace.
 constexpr int kBtWaves = 4;
 constexpr int kTile = 32 * 33;                          // a 32 x 32 LDS tile, row pitch 33
-__global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr(JacBatch batch, int ldy) {
+template <class B>
+__global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr(B batch, int ldy) {
     extern __shared__ float sm[];
     const JacItem &it = batch.it[blockIdx.y];
     const int n = it.n, c0 = 32 * blockIdx.x;
@@ -1084,7 +1087,8 @@ __global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr(JacBatch batch, in
 
 // The back-transform for the wide solver: the reflectors of one block at a
 // time go through LDS (all of them would not fit), with the block's T.
-__global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr_w(JacBatch batch, int ldy) {
+template <class B>
+__global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr_w(B batch, int ldy) {
     extern __shared__ float sm[];
     const JacItem &it = batch.it[blockIdx.y];
     const int n = it.n, c0 = 32 * blockIdx.x;
@@ -1228,7 +1232,8 @@ __device__ __forceinline__ f32x16 mfma_tile_rr(const float *a, int lda, const fl
 // longer needed), the two swapping roles every step.  The same step rule as
 // k_eig_polish; a matrix it cannot make orthonormal reports kEigWideFail in
 // sweeps_out (its output is written as it stands).
-__global__ __launch_bounds__(kThreads) void k_eig_polish_w(JacBatch batch) {
+template <class B>
+__global__ __launch_bounds__(kThreads) void k_eig_polish_w(B batch) {
     __shared__ float sred[kWaves];
     const JacItem &it = batch.it[blockIdx.x];
     const int n = it.n;
@@ -1343,7 +1348,8 @@ __global__ __launch_bounds__(kThreads) void k_eig_polish_w(JacBatch batch) {
 // ---------------------------------------------------------------- 5 and output
 // Newton-Schulz polish and the output of one matrix per workgroup, V loaded
 // from the workspace.
-__global__ __launch_bounds__(kThreads) void k_eig_polish(JacBatch batch, int ld, int boff) {
+template <class B>
+__global__ __launch_bounds__(kThreads) void k_eig_polish(B batch, int ld, int boff) {
     extern __shared__ float sm[];
     __shared__ float slam[kTriMaxN];
     __shared__ float sred[2 * kWaves];
@@ -1449,12 +1455,13 @@ static hipError_t allow_lds(const void *fn) {
         e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - (int)fa.sharedSizeBytes);
     return e;
 }
+template <class B>
 static hipError_t allow_lds_tri() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_eig_tridiag));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_backtr));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_polish));
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_eig_tridiag<B>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_backtr<B>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_polish<B>));
         state = e;
     }
     return state;
@@ -1473,17 +1480,18 @@ static TriLayout tri_layout(int maxN) {
     return L;
 }
 
-static hipError_t launch_eig_wide(const JacBatch &b, int maxN, hipStream_t s) {
+template <class B>
+static hipError_t launch_eig_wide(const B &b, int count, int maxN, hipStream_t s) {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_eig_tridiag_w));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_backtr_w));
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_eig_tridiag_w<B>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_eig_backtr_w<B>));
         state = e;
     }
     if (state != hipSuccess) return state;
     {
         KTimeScope kts("k_eig_tridiag", s);
-        hipLaunchKernelGGL(k_eig_tridiag_w, dim3(b.n), dim3(kWThreads), kWTriLds, s, b);
+        hipLaunchKernelGGL(k_eig_tridiag_w<B>, dim3(count), dim3(kWThreads), kWTriLds, s, b);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     const int nblk = (std::max(maxN - 2, 0) + 31) / 32;
@@ -1491,7 +1499,7 @@ static hipError_t launch_eig_wide(const JacBatch &b, int maxN, hipStream_t s) {
         KTimeScope kts("k_eig_trivec", s);
         constexpr int per = kVecWaves * kVecPerWave;
         const int eig_blocks = (maxN + per - 1) / per;
-        hipLaunchKernelGGL(k_eig_trivec<kWideMaxN>, dim3(eig_blocks + nblk, b.n), dim3(64 * kVecWaves), 0, s, b,
+        hipLaunchKernelGGL((k_eig_trivec<kWideMaxN, B>), dim3(eig_blocks + nblk, count), dim3(64 * kVecWaves), 0, s, b,
                            eig_blocks);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
@@ -1500,30 +1508,31 @@ static hipError_t launch_eig_wide(const JacBatch &b, int maxN, hipStream_t s) {
         const int ldy = eig_tri_np(maxN) + 1;
         const size_t lds = ((size_t)32 * ldy + kTile + (size_t)maxN * 33 + (size_t)(kBtWaves + 1) * kTile) *
                            sizeof(float);
-        hipLaunchKernelGGL(k_eig_backtr_w, dim3((maxN + 31) / 32, b.n), dim3(64 * kBtWaves), lds, s, b, ldy);
+        hipLaunchKernelGGL(k_eig_backtr_w<B>, dim3((maxN + 31) / 32, count), dim3(64 * kBtWaves), lds, s, b, ldy);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     KTimeScope kts("k_eig_polish", s);
-    hipLaunchKernelGGL(k_eig_polish_w, dim3(b.n), dim3(kThreads), 0, s, b);
+    hipLaunchKernelGGL(k_eig_polish_w<B>, dim3(count), dim3(kThreads), 0, s, b);
     return hipGetLastError();
 }
 
-hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
-    if (b.n <= 0) return hipSuccess;
+template <class B>
+static hipError_t eig_tri(const JacItem *items, int count, const B &b, int maxN, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
     if (maxN > kWideMaxN) return hipErrorInvalidValue;
     if (maxN > kTriMaxN) {
-        for (int i = 0; i < b.n; ++i)
-            if (!b.it[i].sweeps_out || !b.it[i].tw || b.it[i].n > maxN || b.it[i].n <= kTriMaxN)
+        for (int i = 0; i < count; ++i)
+            if (!items[i].sweeps_out || !items[i].tw || items[i].n > maxN || items[i].n <= kTriMaxN)
                 return hipErrorInvalidValue;
-        return launch_eig_wide(b, maxN, s);
+        return launch_eig_wide(b, count, maxN, s);
     }
-    for (int i = 0; i < b.n; ++i)
-        if (!b.it[i].sweeps_out || !b.it[i].tw || b.it[i].n > maxN) return hipErrorInvalidValue;
-    if (hipError_t e = allow_lds_tri(); e != hipSuccess) return e;
+    for (int i = 0; i < count; ++i)
+        if (!items[i].sweeps_out || !items[i].tw || items[i].n > maxN) return hipErrorInvalidValue;
+    if (hipError_t e = allow_lds_tri<B>(); e != hipSuccess) return e;
     const TriLayout L = tri_layout(maxN);
     {
         KTimeScope kts("k_eig_tridiag", s);
-        hipLaunchKernelGGL(k_eig_tridiag, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff, L.poff);
+        hipLaunchKernelGGL(k_eig_tridiag<B>, dim3(count), dim3(kThreads), L.bytes, s, b, L.ld, L.boff, L.poff);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     const int nblk = (std::max(maxN - 2, 0) + 31) / 32;
@@ -1531,7 +1540,7 @@ hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
         KTimeScope kts("k_eig_trivec", s);
         constexpr int per = kVecWaves * kVecPerWave;
         const int eig_blocks = (maxN + per - 1) / per;
-        hipLaunchKernelGGL(k_eig_trivec<kTriMaxN>, dim3(eig_blocks + nblk, b.n), dim3(64 * kVecWaves), 0, s, b,
+        hipLaunchKernelGGL((k_eig_trivec<kTriMaxN, B>), dim3(eig_blocks + nblk, count), dim3(64 * kVecWaves), 0, s, b,
                            eig_blocks);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
@@ -1540,12 +1549,18 @@ hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
         const int ldy = ((maxN + 3) & ~3) | 1;         // odd, and room for the padded rows
         const size_t lds = ((size_t)std::max(maxN - 2, 0) * ldy + (size_t)nblk * kTile + (size_t)maxN * 33 +
                             (size_t)(kBtWaves + 1) * kTile) * sizeof(float);
-        hipLaunchKernelGGL(k_eig_backtr, dim3((maxN + 31) / 32, b.n), dim3(64 * kBtWaves), lds, s, b, ldy);
+        hipLaunchKernelGGL(k_eig_backtr<B>, dim3((maxN + 31) / 32, count), dim3(64 * kBtWaves), lds, s, b, ldy);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     KTimeScope kts("k_eig_polish", s);
-    hipLaunchKernelGGL(k_eig_polish, dim3(b.n), dim3(kThreads), L.bytes, s, b, L.ld, L.boff);
+    hipLaunchKernelGGL(k_eig_polish<B>, dim3(count), dim3(kThreads), L.bytes, s, b, L.ld, L.boff);
     return hipGetLastError();
+}
+hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s) {
+    return eig_tri(b.it, b.n, b, maxN, s);
+}
+hipError_t launch_eig_tridiag(const JacItem *host, const JacTable &dev, int maxN, hipStream_t s) {
+    return eig_tri(host, dev.n, dev, maxN, s);
 }
 
 }  // namespace jolt

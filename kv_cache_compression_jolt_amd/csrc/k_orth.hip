@@ -136,8 +136,8 @@ __device__ __forceinline__ void tile_kblock(f32x16 &acc, int lane, FA a, FB b) {
 // GS: the working square lives in the item's work buffer in device memory
 // (orders up to kCholWideMaxK, whose square does not fit LDS) instead of LDS;
 // the arithmetic and its order are the same.
-template <bool GS>
-__global__ __launch_bounds__(512) void k_chol_inv(CholBatch batch, int ld) {
+template <bool GS, class B>
+__global__ __launch_bounds__(512) void k_chol_inv(B batch, int ld) {
     extern __shared__ float S_lds[];
     __shared__ float cb[32 * 64];
     const CholItem &it = batch.it[blockIdx.x];
@@ -487,7 +487,8 @@ static hipError_t allow_lds(const void *fn) {
 static hipError_t orth_lds_attrs() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_chol_inv<false>));
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(k_chol_inv<false, CholBatch>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_chol_inv<false, CholTable>));
         if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<7>));
         if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<8>));
         if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<9>));
@@ -496,20 +497,27 @@ static hipError_t orth_lds_attrs() {
     return state;
 }
 
-hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s) {
-    if (b.n <= 0) return hipSuccess;
+template <class B>
+static hipError_t chol_inv(const CholItem *items, int count, const B &b, int maxK, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
     if (maxK > kCholWideMaxK) return hipErrorInvalidValue;
     const bool gs = maxK > kCholInverseMaxK;
-    for (int i = 0; i < b.n; ++i) {
-        if (b.it[i].ld % 4 || b.it[i].ld < b.it[i].k) return hipErrorInvalidValue;    // float4 rows of G
-        if (gs && !b.it[i].work) return hipErrorInvalidValue;
+    for (int i = 0; i < count; ++i) {
+        if (items[i].ld % 4 || items[i].ld < items[i].k) return hipErrorInvalidValue;    // float4 rows of G
+        if (gs && !items[i].work) return hipErrorInvalidValue;
     }
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
     KTimeScope kts("k_chol_inv", s);
     const int P = (maxK + 31) / 32 * 32;
-    if (gs) hipLaunchKernelGGL(k_chol_inv<true>, dim3(b.n), dim3(512), 0, s, b, P);
-    else hipLaunchKernelGGL(k_chol_inv<false>, dim3(b.n), dim3(512), (size_t)P * (P + 1) * sizeof(float), s, b, P + 1);
+    if (gs) hipLaunchKernelGGL((k_chol_inv<true, B>), dim3(count), dim3(512), 0, s, b, P);
+    else hipLaunchKernelGGL((k_chol_inv<false, B>), dim3(count), dim3(512), (size_t)P * (P + 1) * sizeof(float), s, b, P + 1);
     return hipGetLastError();
+}
+hipError_t launch_chol_inv(const CholBatch &b, int maxK, hipStream_t s) {
+    return chol_inv(b.it, b.n, b, maxK, s);
+}
+hipError_t launch_chol_inv(const CholItem *host, const CholTable &dev, int maxK, hipStream_t s) {
+    return chol_inv(host, dev.n, dev, maxK, s);
 }
 
 template <int NTM>

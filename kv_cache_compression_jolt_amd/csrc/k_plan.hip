@@ -17,6 +17,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <cstring>
 
 #include "dev_common.h"
 #include "plan_kernels.h"
@@ -602,8 +603,8 @@ __device__ __forceinline__ int rr_pos(int i, int round, int m) {
     return 1 + ((i - 1 - round) % (m - 1) + (m - 1)) % (m - 1);
 }
 
-template <int NT>
-__global__ __launch_bounds__(NT) void k_jacobi_lds(JacBatch batch, int max_sweeps, int retry_only) {
+template <int NT, class B>
+__global__ __launch_bounds__(NT) void k_jacobi_lds(B batch, int max_sweeps, int retry_only) {
     extern __shared__ float sm[];
     __shared__ int sP[kJacobiMaxN / 2 + 1], sQ[kJacobiMaxN / 2 + 1];
     __shared__ float sC[kJacobiMaxN / 2 + 1], sS[kJacobiMaxN / 2 + 1];
@@ -1026,7 +1027,8 @@ static hipError_t allow_dynamic_lds(const void *fn) {
 static hipError_t ensure_lds_attrs() {
     static hipError_t state = hipErrorNotReady;
     if (state == hipErrorNotReady) {
-        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<1024>));
+        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<1024, JacBatch>));
+        if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_jacobi_lds<1024, JacTable>));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_cholesky));
         if (e == hipSuccess) e = allow_dynamic_lds(reinterpret_cast<const void *>(k_trsm));
         state = e;
@@ -1165,14 +1167,49 @@ hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) 
     return hipGetLastError();
 }
 
-hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s, int retry_only) {
-    if (b.n <= 0) return hipSuccess;
+template <class B>
+static hipError_t jacobi_lds(int count, const B &b, int maxN, int max_sweeps, hipStream_t s, int retry_only) {
+    if (count <= 0) return hipSuccess;
     if (hipError_t e = ensure_lds_attrs(); e != hipSuccess) return e;
     KTimeScope kts("k_jacobi_lds", s);
     const int m = maxN + (maxN & 1);
     const size_t lds = (size_t)2 * m * m * sizeof(float);
-    hipLaunchKernelGGL(k_jacobi_lds<1024>, dim3(b.n), dim3(1024), lds, s, b, max_sweeps, retry_only);
+    hipLaunchKernelGGL((k_jacobi_lds<1024, B>), dim3(count), dim3(1024), lds, s, b, max_sweeps, retry_only);
     return hipGetLastError();
+}
+hipError_t launch_jacobi_lds(const JacBatch &b, int maxN, int max_sweeps, hipStream_t s, int retry_only) {
+    return jacobi_lds(b.n, b, maxN, max_sweeps, s, retry_only);
+}
+hipError_t launch_jacobi_lds(const JacItem *, const JacTable &dev, int maxN, int max_sweeps, hipStream_t s,
+                             int retry_only) {
+    return jacobi_lds(dev.n, dev, maxN, max_sweeps, s, retry_only);
+}
+
+// ---------------------------------------------------------------- item tables
+// A table chunk travels as the kernel's argument (under the 4 KB argument
+// limit) and is written to device memory by one workgroup.
+constexpr int kTableWords = 992;
+struct TableChunk {
+    uint32_t w[kTableWords];
+    uint32_t *dst;
+    int n;
+};
+__global__ __launch_bounds__(256) void k_put_table(TableChunk c) {
+    for (int i = threadIdx.x; i < c.n; i += 256) c.dst[i] = c.w[i];
+}
+hipError_t launch_put_table(const void *host, size_t bytes, void *dev, hipStream_t s) {
+    if (bytes % 4 || reinterpret_cast<uintptr_t>(dev) % 4) return hipErrorInvalidValue;
+    const uint32_t *src = static_cast<const uint32_t *>(host);
+    uint32_t *dst = static_cast<uint32_t *>(dev);
+    for (size_t w0 = 0; w0 < bytes / 4; w0 += kTableWords) {
+        TableChunk c;
+        c.n = (int)std::min<size_t>(kTableWords, bytes / 4 - w0);
+        c.dst = dst + w0;
+        std::memcpy(c.w, src + w0, (size_t)c.n * 4);
+        hipLaunchKernelGGL(k_put_table, dim3(1), dim3(256), 0, s, c);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_eig_init(const EigBatch &b, int maxN, hipStream_t s) {

@@ -40,6 +40,21 @@ struct Bump {
     }
 };
 
+// Device item tables of a plan group's solver launches (feature eigensolver,
+// token eigensolver, CholeskyQR), in the group scratch after the items'.
+constexpr int kTableItems = kPlanGroup;
+struct Tables {
+    size_t feat, tok, chol;
+};
+inline Tables reserve_tables(Bump &b) {
+    const size_t bytes = (size_t)kTableItems * std::max(sizeof(JacItem), sizeof(CholItem));
+    Tables t;
+    t.feat = b.take(bytes);
+    t.tok = b.take(bytes);
+    t.chol = b.take(bytes);
+    return t;
+}
+
 struct Dims {
     int L, H, T, d, LH, n;       // n = L H d
     int e;                        // element bytes of the item dtype
@@ -165,52 +180,6 @@ struct Ctx {
         if (e_ != hipSuccess) return hip_fail(c.h, e_, where); \
     } while (0)
 
-// The slices of one solver stage spread over the calling stream and the
-// handle's solver streams: slice j on stream j % (kSolverStreams + 1), 0 being
-// the calling stream.  The solver streams wait for the calling stream's work
-// up to the first slice; join() makes the calling stream wait for them.
-class Fan {
-  public:
-    explicit Fan(const Ctx &c, bool on = true) : c_(c), on_(on) {}
-    hipError_t next(hipStream_t *st) {
-        if (!on_) {
-            *st = c_.st;
-            return hipSuccess;
-        }
-        if (n_ == 0) {
-            if (!ss_)
-                if (hipError_t e = solver_streams(c_.h, &ss_); e != hipSuccess) return e;
-            if (hipError_t e = hipEventRecord(ss_->fork, c_.st); e != hipSuccess) return e;
-        }
-        const int j = n_ % (kSolverStreams + 1);
-        ++n_;
-        if (j == 0) {
-            *st = c_.st;
-            return hipSuccess;
-        }
-        if (j > used_) {
-            if (hipError_t e = hipStreamWaitEvent(ss_->st[j - 1], ss_->fork, 0); e != hipSuccess) return e;
-            used_ = j;
-        }
-        *st = ss_->st[j - 1];
-        return hipSuccess;
-    }
-    hipError_t join() {
-        for (int j = 0; j < used_; ++j) {
-            if (hipError_t e = hipEventRecord(ss_->join[j], ss_->st[j]); e != hipSuccess) return e;
-            if (hipError_t e = hipStreamWaitEvent(c_.st, ss_->join[j], 0); e != hipSuccess) return e;
-        }
-        n_ = used_ = 0;
-        return hipSuccess;
-    }
-
-  private:
-    const Ctx &c_;
-    const bool on_;
-    const SolverStreams *ss_ = nullptr;
-    int n_ = 0, used_ = 0;
-};
-
 }  // namespace
 
 // ------------------------------------------------------------------ config and layout
@@ -296,6 +265,7 @@ jolt_status plan_layout(const jolt_config &cfg, const jolt_item *items, int n, P
             Scratch S;
             reserve_scratch(cfg, D, sb, S);
         }
+        reserve_tables(sb);
         worst = std::max(worst, sb.off);
     }
     pl.scratch_bytes = worst;
@@ -438,58 +408,35 @@ jolt_status eig_block(const Ctx &c, const std::vector<EigReq> &reqs, int N, uint
     return JOLT_OK;
 }
 
-// fan: spread the slices over the solver streams (else all on c.st)
+// table: device memory for the item tables of this call's tridiagonal
+// solves (one launch each for all the n <= kTriMaxN matrices and all the wide
+// ones; kTableItems items in all), else slices of kSolverBatch by value
 jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr, int max_sweeps, bool *noconv,
-                    bool wide_ok, bool fan_out = true) {
-    JacBatch jb{}, tb{}, wb{};
+                    bool wide_ok, JacItem *table) {
+    JacBatch jb{};
     int maxN = 0, maxT = 0, maxW = 0;
+    std::vector<JacItem> tri, wide;
     std::vector<std::vector<EigReq>> large;
     std::vector<int> largeN;
-    // slices of kSolverBatch matrices, spread over the solver streams
-    Fan fan(c, fan_out);
-    hipStream_t fs = nullptr;
-    // tridiagonal solver first, Jacobi for what it hands back (n <= kTriMaxN);
-    // the wide tridiagonal solver for kTriMaxN < n <= kWideMaxN
-    auto flush_tri = [&]() -> jolt_status {
-        HIPCHK(fan.next(&fs), "solver stream");
-        HIPCHK(launch_eig_tridiag(tb, maxT, fs), "eig (tridiagonal)");
-        HIPCHK(launch_jacobi_lds(tb, maxT, max_sweeps, fs, 1), "eig (Jacobi retry)");
-        tb.n = 0;
-        maxT = 0;
-        return JOLT_OK;
-    };
-    auto flush_wide = [&]() -> jolt_status {
-        HIPCHK(fan.next(&fs), "solver stream");
-        HIPCHK(launch_eig_tridiag(wb, maxW, fs), "eig (wide tridiagonal)");
-        wb.n = 0;
-        maxW = 0;
-        return JOLT_OK;
-    };
     for (const EigReq &r : reqs) {
+        JacItem j{};
+        j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
+        j.raw = 0;
         if (wide_ok && r.n <= kWideMaxN && r.n > kTriMaxN && r.sw && r.tw) {
-            JacItem &j = wb.it[wb.n++];
-            j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
-            j.raw = 0;
+            // the wide tridiagonal solver for kTriMaxN < n <= kWideMaxN
             j.tw = r.tw;
+            wide.push_back(j);
             maxW = std::max(maxW, r.n);
-            if (wb.n == kSolverBatch)
-                if (jolt_status s = flush_wide()) return s;
         } else if (r.n <= kTriMaxN && r.sw && r.tw) {
-            JacItem &j = tb.it[tb.n++];
-            j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
-            j.raw = 0;
+            // tridiagonal solver first, Jacobi for what it hands back
             j.tw = r.tw;
+            tri.push_back(j);
             maxT = std::max(maxT, r.n);
-            if (tb.n == kSolverBatch)
-                if (jolt_status s = flush_tri()) return s;
         } else if (r.n <= kJacobiMaxN) {
-            JacItem &j = jb.it[jb.n++];
-            j.a = r.g; j.lda = r.ldg; j.vec = r.vec; j.ldv = r.ldv; j.lam = r.lam; j.n = r.n; j.sweeps_out = r.sw;
-            j.raw = 0;
+            jb.it[jb.n++] = j;
             maxN = std::max(maxN, r.n);
             if (jb.n == kSolverBatch) {
-                HIPCHK(fan.next(&fs), "solver stream");
-                HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, fs), "eig");
+                HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
                 jb.n = 0;
                 maxN = 0;
             }
@@ -501,15 +448,26 @@ jolt_status eig_all(const Ctx &c, const std::vector<EigReq> &reqs, uint8_t *scr,
             large[g].push_back(r);
         }
     }
-    if (jb.n) {
-        HIPCHK(fan.next(&fs), "solver stream");
-        HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, fs), "eig");
-    }
-    if (tb.n)
-        if (jolt_status s = flush_tri()) return s;
-    if (wb.n)
-        if (jolt_status s = flush_wide()) return s;
-    HIPCHK(fan.join(), "solver join");
+    HIPCHK(launch_jacobi_lds(jb, maxN, max_sweeps, c.st), "eig");
+    auto solve = [&](const std::vector<JacItem> &v, JacItem *dev, int maxn, bool retry) -> jolt_status {
+        if (v.empty()) return JOLT_OK;
+        if (table && dev + v.size() <= table + kTableItems) {
+            HIPCHK(launch_put_table(v.data(), v.size() * sizeof(JacItem), dev, c.st), "eig table");
+            const JacTable t{dev, (int)v.size()};
+            HIPCHK(launch_eig_tridiag(v.data(), t, maxn, c.st), "eig (tridiagonal)");
+            if (retry) HIPCHK(launch_jacobi_lds(v.data(), t, maxn, max_sweeps, c.st, 1), "eig (Jacobi retry)");
+            return JOLT_OK;
+        }
+        for (size_t s0 = 0; s0 < v.size(); s0 += kSolverBatch) {
+            JacBatch b{};
+            for (size_t i = s0; i < std::min(v.size(), s0 + kSolverBatch); ++i) b.it[b.n++] = v[i];
+            HIPCHK(launch_eig_tridiag(b, maxn, c.st), "eig (tridiagonal)");
+            if (retry) HIPCHK(launch_jacobi_lds(b, maxn, max_sweeps, c.st, 1), "eig (Jacobi retry)");
+        }
+        return JOLT_OK;
+    };
+    if (jolt_status s = solve(tri, table, maxT, true)) return s;
+    if (jolt_status s = solve(wide, table ? table + tri.size() : nullptr, maxW, false)) return s;
     for (size_t g = 0; g < large.size(); ++g)
         for (size_t s0 = 0; s0 < large[g].size(); s0 += kMaxBatch) {
             const std::vector<EigReq> part(large[g].begin() + s0,
@@ -554,10 +512,13 @@ hipError_t sliced(int n, Fill &&fill, Go &&go) {
 // Orthonormalizes the rows of each y in place (passes of shifted CholeskyQR).
 // With hi (and lo) given, the last pass also writes bf16 copies of the result
 // when the L^-1 apply runs (k <= kCholWideMaxK); *bf reports whether it did.
+// table: device memory for the Cholesky item table (kTableItems items).
 jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, float **csq,
                       const int *k, const int *kp, const int *len, const int *split, const int *chunk, int passes,
-                      uint16_t *const *hi = nullptr, uint16_t *const *lo = nullptr, bool *bf = nullptr) {
+                      CholItem *table, uint16_t *const *hi = nullptr, uint16_t *const *lo = nullptr,
+                      bool *bf = nullptr) {
     if (bf) *bf = false;
+    std::vector<CholItem> chol;
     int maxK = 0, maxLen = 0, maxS = 0;
     int64_t maxCount = 0;
     for (int i = 0; i < nb; ++i) {
@@ -586,22 +547,33 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
                    },
                    [&](const ReduceBatch &b) { return launch_reduce(b, maxCount, c.st); })),
                "orth reduce");
-        Fan fan(c);
-        HIPCHK((sliced<CholBatch, kSolverBatch>(
-                   nb,
-                   [&](CholBatch &b, int i) {
-                       CholItem &ch = b.it[b.n++];
-                       ch.g = gram[i]; ch.l = lmat[i]; ch.k = k[i]; ch.ld = kp[i]; ch.rel_shift = 1.0f / 1048576.0f;
-                       ch.inverse = k[i] <= kCholWideMaxK;
-                       ch.work = csq[i];
-                   },
-                   [&](const CholBatch &b) {
-                       hipStream_t fs = nullptr;
-                       if (hipError_t e = fan.next(&fs); e != hipSuccess) return e;
-                       return launch_cholesky(b, maxK, fs);
-                   })),
-               "orth cholesky");
-        HIPCHK(fan.join(), "solver join");
+        if (maxK <= kCholWideMaxK && table && nb <= kTableItems) {
+            // every matrix in one launch, from a device table written once per call
+            if (pass == 0) {
+                chol.resize(nb);
+                for (int i = 0; i < nb; ++i) {
+                    CholItem &ch = chol[i];
+                    ch = CholItem{};
+                    ch.g = gram[i]; ch.l = lmat[i]; ch.k = k[i]; ch.ld = kp[i]; ch.rel_shift = 1.0f / 1048576.0f;
+                    ch.inverse = 1;
+                    ch.work = csq[i];
+                }
+                HIPCHK(launch_put_table(chol.data(), nb * sizeof(CholItem), table, c.st), "cholesky table");
+            }
+            HIPCHK(launch_chol_inv(chol.data(), CholTable{table, nb}, maxK, c.st), "orth cholesky");
+        } else {
+            HIPCHK((sliced<CholBatch, kSolverBatch>(
+                       nb,
+                       [&](CholBatch &b, int i) {
+                           CholItem &ch = b.it[b.n++];
+                           ch.g = gram[i]; ch.l = lmat[i]; ch.k = k[i]; ch.ld = kp[i];
+                           ch.rel_shift = 1.0f / 1048576.0f;
+                           ch.inverse = k[i] <= kCholWideMaxK;
+                           ch.work = csq[i];
+                       },
+                       [&](const CholBatch &b) { return launch_cholesky(b, maxK, c.st); })),
+                   "orth cholesky");
+        }
         HIPCHK((sliced<TrsmBatch, kMaxBatch>(
                    nb,
                    [&](TrsmBatch &b, int i) {
@@ -625,9 +597,9 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
 
 // One group of up to kPlanGroup items: every stage runs for all of them
 // before the next, with launches of kMaxBatch items for the streaming kernels
-// and kSolverBatch items for the one-workgroup-per-matrix solvers, those
-// slices spread over the solver streams so that they run at once (one slice
-// alone would leave most CUs idle).
+// (item tables as kernel arguments) and one launch for all the group's
+// matrices of each one-workgroup-per-matrix solver (item tables in device
+// memory), whose launches of a few matrices would leave most CUs idle.
 jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items,
                            int i0, int nb, const void *const *x_dev, uint8_t *ws, bool *noconv, bool wide_ok,
                            hipStream_t *forked) {
@@ -641,7 +613,11 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
         D[i] = dims_for(cfg, items[i0 + i], pl.rt_max, pl.rf_max);
         reserve_scratch(cfg, D[i], sb, S[i]);
     }
+    const Tables tabs = reserve_tables(sb);
     uint8_t *scr = ws + pl.scratch;
+    JacItem *tab_feat = reinterpret_cast<JacItem *>(scr + tabs.feat);
+    JacItem *tab_tok = reinterpret_cast<JacItem *>(scr + tabs.tok);
+    CholItem *tab_chol = reinterpret_cast<CholItem *>(scr + tabs.chol);
     HIPCHK(launch_zero(ws + pl.item[i0].grid, pl.readback_stride * nb, c.st), "zero readback");
     auto P = [&](size_t off) { return scr + off; };
     auto F = [&](size_t off) { return reinterpret_cast<float *>(scr + off); };
@@ -662,7 +638,8 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     // ---- feature Gram, ||X||^2 and the feature eigenproblems, on the side
     // stream: forked when the token eigenproblems start (one workgroup per
     // matrix leaves most CUs and HBM idle for this), joined before the core,
-    // their first consumer.
+    // their first consumer.  (Forked at the start instead, the Gram pass and
+    // the first sketch pass took turns on HBM and the CUs: no faster.)
     hipStream_t side;
     hipEvent_t fork, join;
     HIPCHK(side_stream(c.h, &side, &fork, &join), "side stream");
@@ -700,7 +677,7 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                "trace");
         const Ctx cs{c.h, side, c.dtype, c.d};
         // kept on the side stream: the solver streams are the token eigenproblems'
-        if (jolt_status es = eig_all(cs, feigs, scr, max_sweeps, noconv, wide_ok, false)) return es;
+        if (jolt_status es = eig_all(cs, feigs, scr, max_sweeps, noconv, wide_ok, tab_feat)) return es;
         HIPCHK(hipEventRecord(join, side), "join");
         return JOLT_OK;
     };
@@ -827,21 +804,21 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
         bool conv = false;
         if ((s = xm(true))) return s;                                                        // Y = A Omega
         if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
-                           kpp.data(), lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2, qh_out,
+                           kpp.data(), lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2, tab_chol, qh_out,
                            (bf && cfg.power_iters == 0) ? qlv.data() : nullptr, &conv)))
             return s;
         for (int q = 0; q < cfg.power_iters; ++q) {
             if (!conv && (s = to_bf(true, false))) return s;
             if ((s = xtq(false))) return s;                                                 // Z = A^T Q
             if ((s = orth_rows(c, nb, zv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
-                               kpp.data(), lenN.data(), sN.data(), cN.data(), 1, bf ? zbv.data() : nullptr, nullptr,
+                               kpp.data(), lenN.data(), sN.data(), cN.data(), 1, tab_chol, bf ? zbv.data() : nullptr, nullptr,
                                &conv)))
                 return s;
             if (!conv && (s = to_bf(false, false))) return s;
             if ((s = xm(false))) return s;                                                  // Y = A Z
             const bool last = q + 1 == cfg.power_iters;
             if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
-                               kpp.data(), lenT.data(), sT.data(), cT.data(), last ? 2 : 1, qh_out,
+                               kpp.data(), lenT.data(), sT.data(), cT.data(), last ? 2 : 1, tab_chol, qh_out,
                                (bf && last) ? qlv.data() : nullptr, &conv)))
                 return s;
         }
@@ -880,7 +857,7 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                                       reinterpret_cast<int *>(W(fo[i].sweeps)) + 1, &S[i],
                                       S[i].etri != SIZE_MAX ? F(S[i].etri) : nullptr});
             if ((s = feature_gram())) return s;
-            jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv, wide_ok);
+            jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv, wide_ok, tab_tok);
             if (es) return es;
         }
         // U_t^T = U~^T Q, P = U~^T B, lambda_t
@@ -934,7 +911,7 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                                   reinterpret_cast<int *>(W(fo[i].sweeps)) + 1, &S[i],
                                   S[i].etri != SIZE_MAX ? F(S[i].etri) : nullptr});
         if (jolt_status fs = feature_gram()) return fs;
-        jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv, wide_ok);
+        jolt_status es = eig_all(c, eigs, scr, max_sweeps, noconv, wide_ok, tab_tok);
         if (es) return es;
         // U_t^T rows = leading eigenvectors; P = U_t^T A (hi + lo split for bf16 caches)
         int maxS = 0, maxCols = 0;
@@ -1027,9 +1004,9 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     return JOLT_OK;
 }
 
-// One group of the plan.  Work forked onto the side and solver streams reads
-// the inputs and writes the workspace, so an error waits for those streams
-// before returning: everything launched has finished when jolt_plan returns.
+// One group of the plan.  Work forked onto the side stream reads the inputs
+// and writes the workspace, so an error waits for that stream before
+// returning: everything launched has finished when jolt_plan returns.
 jolt_status run_group(const Ctx &c, const jolt_config &cfg, const PlanLayout &pl, const jolt_item *items, int i0,
                       int nb, const void *const *x_dev, uint8_t *ws, bool *noconv, bool wide_ok) {
     hipStream_t forked = nullptr;

@@ -145,6 +145,25 @@ inline size_t eig_tri_ws_bytes(int n) {
 }
 hipError_t launch_eig_tridiag(const JacBatch &b, int maxN, hipStream_t s);
 
+// A solver batch whose item table is in device memory, for any number of
+// items in one launch (a by-value batch is limited by the kernel-argument
+// size): the kernels read it.it[blockIdx] exactly as from a by-value batch.
+// The launchers take the host copy of the items too, for their checks and
+// sizes; launch_put_table copies a table to device memory in stream order.
+template <typename Item> struct DevTable {
+    const Item *it;
+    int n;
+};
+typedef DevTable<JacItem> JacTable;
+typedef DevTable<CholItem> CholTable;
+hipError_t launch_eig_tridiag(const JacItem *host, const JacTable &dev, int maxN, hipStream_t s);
+hipError_t launch_jacobi_lds(const JacItem *host, const JacTable &dev, int maxN, int max_sweeps, hipStream_t s,
+                             int retry_only = 0);
+hipError_t launch_chol_inv(const CholItem *host, const CholTable &dev, int maxK, hipStream_t s);
+// bytes (a multiple of 4) from host memory to dev (4-byte aligned), through
+// kernel arguments: the host memory may be reused as soon as this returns
+hipError_t launch_put_table(const void *host, size_t bytes, void *dev, hipStream_t s);
+
 // block Jacobi state of one large symmetric matrix (N = padded size, multiple of 128)
 struct EigItem {
     const float *g;      // input n x n (ld ldg)
