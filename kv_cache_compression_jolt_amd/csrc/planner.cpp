@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstring>
 #include <numeric>
+#include <thread>
 #include <vector>
 
 #include "planner.h"
@@ -131,33 +132,48 @@ jolt_status dual(int n, const std::vector<ItemHull> &hulls, const int64_t *const
         if (lambda_out) *lambda_out = INFINITY;
         return JOLT_E_INFEASIBLE;
     }
-    // lambda* is 0 when taking every hull edge fits; else the least hull slope
-    // sigma whose allocation (every edge of slope > sigma taken) fits.  The
-    // distinct slopes are walked from the largest down by merging the items'
-    // hulls (each in decreasing slope order): total(sigma_1) is the minimum,
-    // and total(sigma_{k+1}) adds the edges of slope exactly sigma_k.
+    // lambda* is 0 when taking every hull edge fits.  Otherwise it is the
+    // largest hull slope sigma at which the minimum bytes plus the bytes of
+    // every edge of slope >= sigma exceed the budget: walking the distinct
+    // slopes from the largest down, the first whose edges no longer fit.  The
+    // allocation at sigma takes the edges of slope > sigma only, and those fit.
+    // sigma is found by a weighted selection over all the items' edges:
+    // partition the range around a pivot slope into (> p, == p, < p) and keep
+    // the part that holds the crossing; every edge of one slope stays together.
+    struct Edge {
+        double s;
+        int64_t w;
+    };
+    thread_local std::vector<Edge> E;
+    E.clear();
+    for (int i = 0; i < n; ++i) {
+        const ItemHull &h = hulls[i];
+        for (size_t j = 0; j < h.s.size(); ++j) E.push_back(Edge{h.s[j], B[i][h.v[j + 1]] - B[i][h.v[j]]});
+    }
     double lam = 0.0;
-    {
-        std::vector<size_t> next(n, 0);
-        auto next_slope = [&]() {
-            double m = -1.0;                            // slopes are positive
-            for (int i = 0; i < n; ++i)
-                if (next[i] < hulls[i].s.size()) m = std::max(m, hulls[i].s[next[i]]);
-            return m;
-        };
-        int64_t tot = min_total;                        // total(sg)
-        double fit = 0.0;
-        double sg = next_slope();
-        while (sg > 0.0 && tot <= budget) {
-            fit = sg;
-            for (int i = 0; i < n; ++i) {
-                const ItemHull &h = hulls[i];
-                for (; next[i] < h.s.size() && h.s[next[i]] == sg; ++next[i])
-                    tot += B[i][h.v[next[i] + 1]] - B[i][h.v[next[i]]];
-            }
-            sg = next_slope();
+    int64_t base = min_total;                           // bytes of the edges above the range, plus the minimum
+    size_t lo = 0, hi = E.size();
+    while (lo < hi) {
+        const double a = E[lo].s, b = E[lo + (hi - lo) / 2].s, c = E[hi - 1].s;
+        const double p = std::max(std::min(a, b), std::min(std::max(a, b), c));   // median of three
+        size_t m1 = lo, k = lo, m2 = hi;
+        while (k < m2) {
+            if (E[k].s > p) std::swap(E[k++], E[m1++]);
+            else if (E[k].s < p) std::swap(E[k], E[--m2]);
+            else ++k;
         }
-        lam = (sg <= 0.0 && tot <= budget) ? 0.0 : fit;
+        int64_t w_gt = 0, w_eq = 0;
+        for (size_t q = lo; q < m1; ++q) w_gt += E[q].w;
+        for (size_t q = m1; q < m2; ++q) w_eq += E[q].w;
+        if (base + w_gt > budget) {
+            hi = m1;                                    // the crossing lies among the slopes > p
+        } else if (base + w_gt + w_eq > budget) {
+            lam = p;
+            break;
+        } else {
+            base += w_gt + w_eq;
+            lo = m2;
+        }
     }
     for (int i = 0; i < n; ++i) pos[i] = vertex_at(hulls[i], lam);
     if (lambda_out) *lambda_out = lam;
@@ -201,9 +217,11 @@ jolt_status allocate_sorted(int n, const SortedCands *const *sc, const double *c
     std::vector<ItemHull> &hulls = hull_scratch(n);
     std::vector<const int64_t *> bp(n);
     for (int i = 0; i < n; ++i) {
+        if (sc[i]->B.empty()) return JOLT_E_INVALID;
+        bp[i] = sc[i]->B.data();
+    }
+    auto hull_of = [&](int i) {
         const SortedCands &c = *sc[i];
-        if (c.B.empty()) return JOLT_E_INVALID;
-        bp[i] = c.B.data();
         const double *g = grid[i], nx2 = normx2[i];
         const int *cell = c.cell.data();
         const uint8_t *bits = c.bits.data();
@@ -212,6 +230,22 @@ jolt_status allocate_sorted(int n, const SortedCands *const *sc, const double *c
             const double S = cell[p] < 0 ? 0.0 : g[cell[p]];
             return delta[bits[p]] * std::max(0.0, nx2 - S);
         }, hulls[i]);
+    };
+    // The hulls are independent: a large call builds them on a few threads,
+    // each over a contiguous run of items (the result does not depend on it).
+    const int workers = std::min({(int)std::max(1u, std::thread::hardware_concurrency()), 8, (n + 31) / 32});
+    if (workers <= 1) {
+        for (int i = 0; i < n; ++i) hull_of(i);
+    } else {
+        std::vector<std::thread> pool;
+        pool.reserve(workers - 1);
+        const int per = (n + workers - 1) / workers;
+        for (int w = 1; w < workers; ++w)
+            pool.emplace_back([&, w]() {
+                for (int i = w * per; i < std::min(n, (w + 1) * per); ++i) hull_of(i);
+            });
+        for (int i = 0; i < std::min(n, per); ++i) hull_of(i);
+        for (std::thread &t : pool) t.join();
     }
     std::vector<int> pos(n);
     const jolt_status s = dual(n, hulls, bp.data(), budget, pos.data(), lambda_out);
