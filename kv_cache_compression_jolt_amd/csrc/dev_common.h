@@ -110,9 +110,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // MFMAs: the reads are issued AHEAD in front of the MFMAs, then one read per
 // M MFMAs, so that AHEAD reads are in flight while the MFMAs run (without it
 // the scheduler puts each read right before its MFMA and waits for it there).
-template <int N, int M, int AHEAD>
+// VM > 0: VM global loads of the same region are issued first of all, so that
+// they are in flight together.
+template <int N, int M, int AHEAD, int VM = 0>
 __device__ __forceinline__ void sched_reads_ahead() {
     constexpr int A = AHEAD < N ? AHEAD : N;
+    if constexpr (VM > 0) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);   // VMEM reads
     __builtin_amdgcn_sched_group_barrier(0x100, A, 0);          // DS reads
 #pragma unroll
     for (int i = 0; i < N - A; ++i) {

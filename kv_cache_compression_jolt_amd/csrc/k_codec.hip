@@ -251,27 +251,25 @@ __device__ __forceinline__ FragF32 frag_or_zero<float>(const float *p, bool ok) 
     return f;
 }
 
-template <typename T, int NMF>
-__device__ __forceinline__ void xhat_mfma(const T *wt, const T *wlo, int rtp, const T *ut, int rt, int tok, bool tv,
-                                          int lane, f32x16 *acc) {
+// VEC: rows of U~_t are 16-byte aligned (rt a multiple of 8).  Then the whole
+// batches of KB K steps run first as straight code: KB plain 16-byte loads all
+// in flight together (an invalid token's lanes read row 0; their results are
+// never stored, and a token's column of the product depends on its own lanes
+// only), then per K step the hi products of every feature block and the lo
+// ones, with the W~ fragment reads kept ahead of them.  What is left (all of
+// it when !VEC) runs with its fragments checked against the row end.
+template <typename T, int NMF, bool VEC>
+__device__ __forceinline__ void xhat_mfma_rows(const T *wt, const T *wlo, int rtp, const T *ut, int rt, int tok,
+                                               bool tv, int lane, f32x16 *acc) {
     const int ln = lane & 31, h = lane >> 5;
-    const bool vec = (rt & 7) == 0;        // rows of U~_t are 16-byte aligned
-    constexpr int KB = 4;                  // fragments in flight (registers: 4 waves per SIMD)
+    constexpr int KB = 4;                  // fragments in flight
     const T *urow = ut + (size_t)(tv ? tok : 0) * rt;
-    for (int k0b = 0; k0b < rt; k0b += 16 * KB) {
-        typename Elem<T>::Frag b[KB];
+    int k0b = 0;
+    if constexpr (VEC) {
+        for (; k0b + 16 * KB <= rt; k0b += 16 * KB) {
+            typename Elem<T>::Frag b[KB];
 #pragma unroll
-        for (int q = 0; q < KB; ++q) {
-            const int kk = k0b + 16 * q + 8 * h;
-            const bool ok = tv && kk < rt;
-            // in-bounds address (rt >= 8 whenever vec and the loop runs), zero where !ok
-            b[q] = vec ? frag_or_zero(urow + min(kk, rt - 8), ok)
-                       : (ok ? load_frag_n(urow + kk, rt - kk) : zero_frag(ut));
-        }
-        if (k0b + 16 * KB <= rt) {
-            // a whole batch, one straight run: per K step the hi products of
-            // every feature block, then the lo ones (no MFMA waits on the one
-            // before it), with the W~ fragment reads kept ahead of them
+            for (int q = 0; q < KB; ++q) b[q] = load_frag(urow + k0b + 16 * q + 8 * h);
 #pragma unroll
             for (int q = 0; q < KB; ++q) {
                 const int kk = k0b + 16 * q + 8 * h;
@@ -283,24 +281,41 @@ __device__ __forceinline__ void xhat_mfma(const T *wt, const T *wlo, int rtp, co
                     for (int mf = 0; mf < NMF; ++mf)
                         mfma(load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk), b[q], acc[mf]);
             }
-            if constexpr (sizeof(T) == 2) sched_reads_ahead<KB * NMF * 2, 1, 4>();
-        } else {
+            if constexpr (sizeof(T) == 2) sched_reads_ahead<KB * NMF * 2, 1, 4, KB>();
+        }
+    }
+    for (; k0b < rt; k0b += 16 * KB) {
+        typename Elem<T>::Frag b[KB];
 #pragma unroll
-            for (int q = 0; q < KB; ++q) {
-                const int kk = k0b + 16 * q + 8 * h;
-                if (k0b + 16 * q >= rt) break;
+        for (int q = 0; q < KB; ++q) {
+            const int kk = k0b + 16 * q + 8 * h;
+            const bool ok = tv && kk < rt;
+            // in-bounds address (rt >= 8 whenever VEC and the loop runs), zero where !ok
+            if constexpr (VEC) b[q] = frag_or_zero(urow + min(kk, rt - 8), ok);
+            else b[q] = ok ? load_frag_n(urow + kk, rt - kk) : zero_frag(ut);
+        }
 #pragma unroll
-                for (int mf = 0; mf < NMF; ++mf) {
-                    typename Elem<T>::Frag a = load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk);
-                    mfma(a, b[q], acc[mf]);
-                    if constexpr (sizeof(T) == 2) {
-                        typename Elem<T>::Frag al = load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk);
-                        mfma(al, b[q], acc[mf]);
-                    }
+        for (int q = 0; q < KB; ++q) {
+            const int kk = k0b + 16 * q + 8 * h;
+            if (k0b + 16 * q >= rt) break;
+#pragma unroll
+            for (int mf = 0; mf < NMF; ++mf) {
+                typename Elem<T>::Frag a = load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk);
+                mfma(a, b[q], acc[mf]);
+                if constexpr (sizeof(T) == 2) {
+                    typename Elem<T>::Frag al = load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk);
+                    mfma(al, b[q], acc[mf]);
                 }
             }
         }
     }
+}
+
+template <typename T, int NMF>
+__device__ __forceinline__ void xhat_mfma(const T *wt, const T *wlo, int rtp, const T *ut, int rt, int tok, bool tv,
+                                          int lane, f32x16 *acc) {
+    if ((rt & 7) == 0) xhat_mfma_rows<T, NMF, true>(wt, wlo, rtp, ut, rt, tok, tv, lane, acc);
+    else xhat_mfma_rows<T, NMF, false>(wt, wlo, rtp, ut, rt, tok, tv, lane, acc);
 }
 
 // W~ of one (layer, head) as the X^ MFMA reads it: straight from global memory,
