@@ -283,20 +283,23 @@ __global__ __launch_bounds__(512) void k_chol_inv(B batch, int ld) {
             }
         }
     }
-    // L^{-1}: X(i, c) = S[c][i] on and below the diagonal; four rows per wave
-    // in flight (in-bounds loads, then selects)
+    // L^{-1}: X(i, c) = S[c][i] on and below the diagonal, zero above it and in
+    // the padding rows and columns k .. kq - 1 (kq = k rounded up to 32, the
+    // square k_apply_linv reads without masks); four rows per wave in flight
+    // (in-bounds loads, then selects)
     __syncthreads();
     constexpr int NU = ((GS ? kCholWideMaxK : kCholInverseMaxK) + 63) / 64;
-    for (int i0 = wid; i0 < k; i0 += 4 * NW) {
+    const int kq = (k + 31) / 32 * 32;
+    for (int i0 = wid; i0 < kq; i0 += 4 * NW) {
         float val[4][NU];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int i = min(i0 + q * NW, P - 1);
+            const int iu = i0 + q * NW, i = min(iu, P - 1);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                const int c = min(lane + 64 * u, P - 1);
+                const int cu = lane + 64 * u, c = min(cu, P - 1);
                 const float x = S[c * ld + i];
-                val[q][u] = c <= i ? x : 0.f;
+                val[q][u] = cu <= iu && iu < k && cu < k ? x : 0.f;
             }
         }
 #pragma unroll
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(512) void k_chol_inv(B batch, int ld) {
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 const int c = lane + 64 * u;
-                if (i < k && c < k) it.l[(size_t)i * it.ld + c] = val[q][u];
+                if (i < kq && c < kq) it.l[(size_t)i * it.ld + c] = val[q][u];
             }
         }
     }
@@ -350,23 +353,27 @@ struct ApplyDeal {
 
 constexpr int kApplyCols = 32;                      // columns of Y per block
 
-// wave W's rows of X into xr (block r of the wave at offset 16 sum_{r' < r} (tm_r' + 1))
+// wave W's rows of X into xr (block r of the wave at offset 16 sum_{r' < r} (tm_r' + 1)).
+// X is stored zero-padded to kq = k rounded up to 32 (rows and columns), so a
+// row below kq is read without masks (its columns < 32 (tm + 1) <= kq); a block
+// of rows at or past kq is zero.  All of a block's loads go out before the
+// selects.
 template <int NTM, int W>
 __device__ __forceinline__ void apply_load_x(const TrsmItem &it, int lane, float *xr) {
     constexpr ApplyDeal<NTM> D{};
     const int m32 = lane & 31, kh = lane >> 5;
+    const int kq = (it.k + 31) / 32 * 32;
     int off = 0;
 #pragma unroll
     for (int r = 0; r < D.cnt[W]; ++r) {
         const int tm = D.tm[W][r];
         const int row = 32 * tm + m32;
-        const bool rok = row < it.k;
-        const float *xrow = it.l + (size_t)(rok ? row : 0) * it.ld;
+        const bool rok = 32 * tm < kq;
+        const float *xrow = it.l + (size_t)(rok ? row : 0) * it.ld + kh;
 #pragma unroll
-        for (int i = 0; i < 16 * (tm + 1); ++i) {
-            const int col = 2 * i + kh;
-            xr[off + i] = ld_or_zero(xrow, col < it.k ? col : 0, rok && col < it.k);
-        }
+        for (int i = 0; i < 16 * (tm + 1); ++i) xr[off + i] = xrow[2 * i];
+#pragma unroll
+        for (int i = 0; i < 16 * (tm + 1); ++i) xr[off + i] = rok ? xr[off + i] : 0.f;
         off += 16 * (tm + 1);
     }
 }
@@ -503,7 +510,8 @@ static hipError_t chol_inv(const CholItem *items, int count, const B &b, int max
     if (maxK > kCholWideMaxK) return hipErrorInvalidValue;
     const bool gs = maxK > kCholInverseMaxK;
     for (int i = 0; i < count; ++i) {
-        if (items[i].ld % 4 || items[i].ld < items[i].k) return hipErrorInvalidValue;    // float4 rows of G
+        // float4 rows of G; X is written zero-padded to k rounded up to 32
+        if (items[i].ld % 4 || items[i].ld < (items[i].k + 31) / 32 * 32) return hipErrorInvalidValue;
         if (gs && !items[i].work) return hipErrorInvalidValue;
     }
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
@@ -530,7 +538,8 @@ hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream
     if (b.n <= 0) return hipSuccess;
     if (maxK > kCholWideMaxK) return hipErrorInvalidValue;
     for (int i = 0; i < b.n; ++i)
-        if (b.it[i].len % 4 || b.it[i].ldy % 4 || b.it[i].k > maxK) return hipErrorInvalidValue;
+        if (b.it[i].len % 4 || b.it[i].ldy % 4 || b.it[i].k > maxK || b.it[i].ld < (b.it[i].k + 31) / 32 * 32)
+            return hipErrorInvalidValue;
     if (hipError_t e = orth_lds_attrs(); e != hipSuccess) return e;
     KTimeScope kts("k_apply_linv", s);
     const int ntm = std::max(1, (maxK + 31) / 32);
