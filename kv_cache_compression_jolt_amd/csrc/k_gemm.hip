@@ -3,7 +3,7 @@
 // rows of a panel (CholeskyQR Grams, B B^T).
 //
 // One workgroup computes a 64 x 64 tile of C (4 waves, 2 x 2 tiles of 32 x 32 on
-// v_mfma_f32_32x32x2f32).  K is staged through LDS 32 deep; the next slice is
+// v_mfma_f32_32x32x2f32), or a 128 x 128 tile when both M and N exceed 64.  K is staged through LDS 32 deep; the next slice is
 // loaded into registers while the current one is multiplied.  Operands are
 // addressed by element strides, so transposed views need no copies; loads are
 // coalesced along whichever index has stride 1.
@@ -91,6 +91,112 @@ __global__ __launch_bounds__(256) void k_gemm(GemmBatch batch, int maxSplit) {
             const int gi = i0 + wm * 32 + frag_row(lane, jj);
             if (gi < it.M) c[(int64_t)gi * it.c_i + (int64_t)gj * it.c_j] = acc[jj];
         }
+}
+
+// ---------------------------------------------------------------- 128 x 128 tiles
+// The same product for launches whose M and N both exceed 64: a workgroup of 4
+// waves computes a 128 x 128 tile of C, each wave a 64 x 64 quarter as 2 x 2
+// MFMA tiles, so that every 32-deep K slice staged in LDS feeds 64 MFMAs per
+// wave between two barriers (16 for the 64 x 64 tiles), and every operand
+// element staged serves twice as many products.
+constexpr int kBT = 128, kBPad = 132;
+
+// A thread's 16 elements of each operand's slice, walked with a fixed step so
+// that one base pointer and one stride cover them: element q of operand A is
+// (i, k) = (i0 + r + q dr, k0 + c + q dc) with (r, c, dr, dc) = (tid / 32,
+// tid % 32, 8, 0) when k has unit stride (threads run along k), else (tid %
+// 128, tid / 128, 0, 2) (threads run along i); B's (j, k) likewise.
+struct Walk {
+    int r, c, dr, dc;         // first (row, column) in the slice and the step per element
+};
+__device__ __forceinline__ Walk walk128(bool cfast, int tid) {
+    return cfast ? Walk{tid >> 5, tid & 31, 8, 0} : Walk{tid & 127, tid >> 7, 0, 2};
+}
+
+__global__ __launch_bounds__(256) void k_gemm128(GemmBatch batch, int maxSplit) {
+    __shared__ float As[kKS][kBPad];    // As[k][i]
+    __shared__ float Bs[kKS][kBPad];    // Bs[k][j]
+    const int z = blockIdx.z;
+    const GemmItem &it0 = batch.it[z % batch.n];
+    const int sp = (z / batch.n) % maxSplit, bi = (z / batch.n) / maxSplit;
+    const int i0 = blockIdx.y * kBT, j0 = blockIdx.x * kBT;
+    if (sp >= it0.nsplit || bi >= it0.nb || i0 >= it0.M || j0 >= it0.N) return;
+    const float *A = it0.a + bi * it0.a_z;
+    const float *B = it0.b + bi * it0.b_z;
+    float *C = it0.c + bi * it0.c_z + (int64_t)sp * it0.c_split;
+    const int M = it0.M, N = it0.N;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid >> 1, wn = wid & 1, kh = lane >> 5, l32 = lane & 31;
+    const int kb = sp * it0.kchunk, ke = min(it0.K, kb + it0.kchunk);
+    // A walks (r, c) = (i, k) and B walks (r, c) = (j, k); threads run along
+    // whichever index has unit stride
+    const Walk wa = walk128(it0.a_k == 1, tid), vb = walk128(it0.b_j != 1, tid);
+    const int64_t a_step = (int64_t)wa.dr * it0.a_i + (int64_t)wa.dc * it0.a_k;
+    const int64_t b_step = (int64_t)vb.dr * it0.b_j + (int64_t)vb.dc * it0.b_k;
+    float va[16], vbv[16];
+    auto load = [&](int k0) {
+        const float *pa = A + (int64_t)(i0 + wa.r) * it0.a_i + (int64_t)(k0 + wa.c) * it0.a_k;
+        const float *pb = B + (int64_t)(j0 + vb.r) * it0.b_j + (int64_t)(k0 + vb.c) * it0.b_k;
+        if (i0 + kBT <= M && j0 + kBT <= N && k0 + kKS <= ke) {      // an interior slice: no masks
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                va[q] = pa[q * a_step];
+                vbv[q] = pb[q * b_step];
+            }
+            return;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const bool oka = i0 + wa.r + q * wa.dr < M && k0 + wa.c + q * wa.dc < ke;
+            const bool okb = j0 + vb.r + q * vb.dr < N && k0 + vb.c + q * vb.dc < ke;
+            const float x = *(oka ? pa + q * a_step : A);
+            const float y = *(okb ? pb + q * b_step : B);
+            va[q] = oka ? x : 0.f;
+            vbv[q] = okb ? y : 0.f;
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn) acc[tm][tn] = f32x16{};
+    load(kb);
+    for (int k0 = kb; k0 < ke; k0 += kKS) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            As[wa.c + q * wa.dc][wa.r + q * wa.dr] = va[q];
+            Bs[vb.c + q * vb.dc][vb.r + q * vb.dr] = vbv[q];
+        }
+        __syncthreads();
+        if (k0 + kKS < ke) load(k0 + kKS);
+#pragma unroll
+        for (int s = 0; s < kKS / 2; ++s) {
+            float a[2], b[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                a[t] = As[2 * s + kh][64 * wm + 32 * t + l32];
+                b[t] = Bs[2 * s + kh][64 * wn + 32 * t + l32];
+            }
+#pragma unroll
+            for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+        const int gj = j0 + 64 * wn + 32 * tn + l32;
+        if (gj >= N) continue;
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const int gi = i0 + 64 * wm + 32 * tm + frag_row(lane, jj);
+                if (gi < M) C[(int64_t)gi * it0.c_i + (int64_t)gj * it0.c_j] = acc[tm][tn][jj];
+            }
+    }
 }
 
 // ---------------------------------------------------------------- symmetric Gram
@@ -223,8 +329,13 @@ hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStr
 hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     KTimeScope kts("k_gemm", s);
-    dim3 g((maxN + 63) / 64, (maxM + 63) / 64, b.n * maxSplit * maxNb);
-    hipLaunchKernelGGL(k_gemm, g, dim3(256), 0, s, b, maxSplit);
+    if (maxM > 64 && maxN > 64) {
+        dim3 g((maxN + kBT - 1) / kBT, (maxM + kBT - 1) / kBT, b.n * maxSplit * maxNb);
+        hipLaunchKernelGGL(k_gemm128, g, dim3(256), 0, s, b, maxSplit);
+    } else {
+        dim3 g((maxN + 63) / 64, (maxM + 63) / 64, b.n * maxSplit * maxNb);
+        hipLaunchKernelGGL(k_gemm, g, dim3(256), 0, s, b, maxSplit);
+    }
     return hipGetLastError();
 }
 
