@@ -20,6 +20,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+// two fp32 -> two bf16 (a in the low half) in one conversion instruction; round
+// to nearest even, the same bits as f32_to_bf16 for finite values
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 
 // ---------------------------------------------------------------- counter RNG
 // SplitMix64 output function (Steele, Lea & Flood 2014), used as a counter hash.

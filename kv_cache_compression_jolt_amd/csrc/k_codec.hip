@@ -25,6 +25,7 @@
 // (d = 128) or half of it (d = 64).  Group absmax and packing are then
 // in-lane, and each lane stores its group's codes contiguously.
 #include <algorithm>
+#include <type_traits>
 
 #include "dev_common.h"
 #include "jolt_internal.h"
@@ -177,32 +178,32 @@ __device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t *sign_bits, int 
 }
 
 // Features f0 .. f0 + 3 (f0 a multiple of 4) of one row (bytes), with the
-// rotation signs applied, as floats.
-template <typename T>
-__device__ __forceinline__ void get4_signed(const uint8_t *row, const uint32_t *sign_bits, int f0, float *o);
-template <>
-__device__ __forceinline__ void get4_signed<uint16_t>(const uint8_t *row, const uint32_t *sign_bits, int f0, float *o) {
-    uint2 v = *reinterpret_cast<const uint2 *>(row + 2 * f0);
+// rotation signs applied and then negated (NEG), as floats.  Both are sign
+// flips, taken together as one XOR on the stored bits.
+template <typename T, bool NEG = false>
+__device__ __forceinline__ void get4_signed(const uint8_t *row, const uint32_t *sign_bits, int f0, float *o) {
     const uint32_t n = (sign_bits[f0 >> 5] >> (f0 & 31)) & 0xFu;
-    v.x ^= ((n & 1u) << 15) | ((n & 2u) << 30);
-    v.y ^= ((n & 4u) << 13) | ((n & 8u) << 28);
-    o[0] = __uint_as_float(v.x << 16);
-    o[1] = __uint_as_float(v.x & 0xFFFF0000u);
-    o[2] = __uint_as_float(v.y << 16);
-    o[3] = __uint_as_float(v.y & 0xFFFF0000u);
-}
-template <>
-__device__ __forceinline__ void get4_signed<float>(const uint8_t *row, const uint32_t *sign_bits, int f0, float *o) {
-    uint4 v = *reinterpret_cast<const uint4 *>(row + 4 * f0);
-    const uint32_t n = (sign_bits[f0 >> 5] >> (f0 & 31)) & 0xFu;
-    v.x ^= (n & 1u) << 31;
-    v.y ^= (n & 2u) << 30;
-    v.z ^= (n & 4u) << 29;
-    v.w ^= (n & 8u) << 28;
-    o[0] = __uint_as_float(v.x);
-    o[1] = __uint_as_float(v.y);
-    o[2] = __uint_as_float(v.z);
-    o[3] = __uint_as_float(v.w);
+    if constexpr (sizeof(T) == 2) {
+        uint2 v = *reinterpret_cast<const uint2 *>(row + 2 * f0);
+        constexpr uint32_t ng = NEG ? 0x80008000u : 0u;
+        v.x ^= (((n & 1u) << 15) | ((n & 2u) << 30)) ^ ng;
+        v.y ^= (((n & 4u) << 13) | ((n & 8u) << 28)) ^ ng;
+        o[0] = __uint_as_float(v.x << 16);
+        o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        o[2] = __uint_as_float(v.y << 16);
+        o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    } else {
+        uint4 v = *reinterpret_cast<const uint4 *>(row + 4 * f0);
+        constexpr uint32_t ng = NEG ? 0x80000000u : 0u;
+        v.x ^= ((n & 1u) << 31) ^ ng;
+        v.y ^= ((n & 2u) << 30) ^ ng;
+        v.z ^= ((n & 4u) << 29) ^ ng;
+        v.w ^= ((n & 8u) << 28) ^ ng;
+        o[0] = __uint_as_float(v.x);
+        o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z);
+        o[3] = __uint_as_float(v.w);
+    }
 }
 
 // Stores a, b, c, d as features f0 .. f0 + 3 of one row (bytes), in the
@@ -215,8 +216,8 @@ __device__ __forceinline__ void put4_signed<uint16_t>(uint8_t *row, const uint32
                                                       float b, float c, float d) {
     const uint32_t n = (sign_bits[f0 >> 5] >> (f0 & 31)) & 0xFu;
     uint2 v;
-    v.x = ((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16)) ^ (((n & 1u) << 15) | ((n & 2u) << 30));
-    v.y = ((uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16)) ^ (((n & 4u) << 13) | ((n & 8u) << 28));
+    v.x = bf16_pair(a, b) ^ (((n & 1u) << 15) | ((n & 2u) << 30));
+    v.y = bf16_pair(c, d) ^ (((n & 4u) << 13) | ((n & 8u) << 28));
     *reinterpret_cast<uint2 *>(row + 2 * f0) = v;
 }
 template <>
@@ -265,6 +266,26 @@ __device__ __forceinline__ void xhat_mfma_rows(const T *wt, const T *wlo, int rt
     constexpr int KB = 4;                  // fragments in flight
     const T *urow = ut + (size_t)(tv ? tok : 0) * rt;
     int k0b = 0;
+    if constexpr (VEC && sizeof(T) == 2) {
+        // 256-deep batches first: 16 fragments in flight, one wait per batch
+        constexpr int KW = 16;
+        for (; k0b + 16 * KW <= rt; k0b += 16 * KW) {
+            typename Elem<T>::Frag b[KW];
+#pragma unroll
+            for (int q = 0; q < KW; ++q) b[q] = load_frag(urow + k0b + 16 * q + 8 * h);
+#pragma unroll
+            for (int q = 0; q < KW; ++q) {
+                const int kk = k0b + 16 * q + 8 * h;
+#pragma unroll
+                for (int mf = 0; mf < NMF; ++mf)
+                    mfma(load_frag(wt + (size_t)(32 * mf + ln) * rtp + kk), b[q], acc[mf]);
+#pragma unroll
+                for (int mf = 0; mf < NMF; ++mf)
+                    mfma(load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk), b[q], acc[mf]);
+            }
+            sched_reads_ahead<KW * NMF * 2, 1, 4, KW>();
+        }
+    }
     if constexpr (VEC) {
         for (; k0b + 16 * KB <= rt; k0b += 16 * KB) {
             typename Elem<T>::Frag b[KB];
@@ -309,13 +330,6 @@ __device__ __forceinline__ void xhat_mfma_rows(const T *wt, const T *wlo, int rt
             }
         }
     }
-}
-
-template <typename T, int NMF>
-__device__ __forceinline__ void xhat_mfma(const T *wt, const T *wlo, int rtp, const T *ut, int rt, int tok, bool tv,
-                                          int lane, f32x16 *acc) {
-    if ((rt & 7) == 0) xhat_mfma_rows<T, NMF, true>(wt, wlo, rtp, ut, rt, tok, tv, lane, acc);
-    else xhat_mfma_rows<T, NMF, false>(wt, wlo, rtp, ut, rt, tok, tv, lane, acc);
 }
 
 // W~ of one (layer, head) as the X^ MFMA reads it: straight from global memory,
@@ -462,74 +476,81 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch, int tpw) 
     const int ln = lane & 31, h = lane >> 5;
     const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
 
-    for (int t0 = tb + 32 * wave; t0 < te; t0 += 32 * NWV) {
-        const int tok = t0 + ln;
-        const bool tv = tok < te;
-        // -(s o x) in the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
-        // of its token); an invalid token reads row 0 and stores nothing.  The
-        // X^ products (signs folded into wt) accumulate onto it, leaving -(s o r).
-        const uint8_t *xrow =
-            reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T + (tv ? tok : 0)) * TL::RB;
-        f32x16 acc[NMF];
-#pragma unroll
-        for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                float xv[4];
-                get4_signed<T>(xrow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, xv);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[mf][4 * jb + c] = -xv[c];
-            }
-        xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
-        float r[NMF][16];
-#pragma unroll
-        for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) r[mf][j] = acc[mf][j];
-
-        // in-register Hadamard stages: feature bits 0, 1, 3, 4 (j bits) and the mf bits
-#pragma unroll
-        for (int jbit = 1; jbit < 16; jbit <<= 1)
-#pragma unroll
+    // one tile loop for 16-byte aligned rows of U~_t and one for the rest,
+    // chosen once
+    auto tiles = [&](auto vec_tag) {
+        constexpr bool VEC = decltype(vec_tag)::value;
+        for (int t0 = tb + 32 * wave; t0 < te; t0 += 32 * NWV) {
+            const int tok = t0 + ln;
+            const bool tv = tok < te;
+            // -(s o x) in the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
+            // of its token); an invalid token reads row 0 and stores nothing.  The
+            // X^ products (signs folded into wt) accumulate onto it, leaving -(s o r).
+            const uint8_t *xrow =
+                reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T + (tv ? tok : 0)) * TL::RB;
+            f32x16 acc[NMF];
+    #pragma unroll
             for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (!(j & jbit)) {
-                        const float a = r[mf][j], b = r[mf][j | jbit];
-                        r[mf][j] = a + b;
-                        r[mf][j | jbit] = a - b;
-                    }
-#pragma unroll
-        for (int mbit = 1; mbit < NMF; mbit <<= 1)
-#pragma unroll
+    #pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    float xv[4];
+                    get4_signed<T, true>(xrow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, xv);
+    #pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[mf][4 * jb + c] = xv[c];
+                }
+            xhat_mfma_rows<T, NMF, VEC>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+            float r[NMF][16];
+    #pragma unroll
             for (int mf = 0; mf < NMF; ++mf)
-                if (!(mf & mbit))
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const float a = r[mf][j], b = r[mf | mbit][j];
-                        r[mf][j] = a + b;
-                        r[mf | mbit][j] = a - b;
-                    }
+    #pragma unroll
+                for (int j = 0; j < 16; ++j) r[mf][j] = acc[mf][j];
 
-        // feature bit 2 across lane halves; afterwards the lane half is the top
-        // feature bit and y[e] holds in-group element e (+ 32 h for d = 64).  The
-        // butterflies so far ran on -r; the negative 1/sqrt(d) restores the sign
-        // exactly (negation commutes with every rounding here).
-        const float isd = (D == 128) ? -0.08838834764831845f : -0.125f;
-        float y[NE];
-#pragma unroll
-        for (int mp = 0; mp < HALF; ++mp)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float u = r[mp][j], w = r[mp + HALF][j];
-                swap_halves(u, w);
-                const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
-                y[e] = (u + w) * isd;
-                y[e + 4] = (u - w) * isd;
-            }
+            // in-register Hadamard stages: feature bits 0, 1, 3, 4 (j bits) and the mf bits
+    #pragma unroll
+            for (int jbit = 1; jbit < 16; jbit <<= 1)
+    #pragma unroll
+                for (int mf = 0; mf < NMF; ++mf)
+    #pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (!(j & jbit)) {
+                            const float a = r[mf][j], b = r[mf][j | jbit];
+                            r[mf][j] = a + b;
+                            r[mf][j | jbit] = a - b;
+                        }
+    #pragma unroll
+            for (int mbit = 1; mbit < NMF; mbit <<= 1)
+    #pragma unroll
+                for (int mf = 0; mf < NMF; ++mf)
+                    if (!(mf & mbit))
+    #pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const float a = r[mf][j], b = r[mf | mbit][j];
+                            r[mf][j] = a + b;
+                            r[mf | mbit][j] = a - b;
+                        }
 
-        quantize_store<D, BITS>(y, h, tv, (size_t)lh * it.T + tok, it.codes, it.scales);
-    }
+            // feature bit 2 across lane halves; afterwards the lane half is the top
+            // feature bit and y[e] holds in-group element e (+ 32 h for d = 64).  The
+            // butterflies so far ran on -r; the negative 1/sqrt(d) restores the sign
+            // exactly (negation commutes with every rounding here).
+            const float isd = (D == 128) ? -0.08838834764831845f : -0.125f;
+            float y[NE];
+    #pragma unroll
+            for (int mp = 0; mp < HALF; ++mp)
+    #pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    float u = r[mp][j], w = r[mp + HALF][j];
+                    swap_halves(u, w);
+                    const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
+                    y[e] = (u + w) * isd;
+                    y[e + 4] = (u - w) * isd;
+                }
+
+            quantize_store<D, BITS>(y, h, tv, (size_t)lh * it.T + tok, it.codes, it.scales);
+        }
+    };
+    if ((it.rt & 7) == 0) tiles(std::true_type{});
+    else tiles(std::false_type{});
 }
 
 // ------------------------------------------------------------------ fused decoder
@@ -563,66 +584,73 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch, int tpw) 
 
     const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
 
-    for (int t0 = tb + 32 * wave; t0 < te; t0 += 32 * NWV) {
-        const int tok = t0 + ln;
-        const bool tv = tok < te;
-        // rotated-back residual first, straight into the accumulators of the X^
-        // products (the MFMA layout), so that it and the products are never live
-        // at the same time
-        f32x16 acc[NMF];
-        if constexpr (BITS > 0) {
-            // codes of the lane's group (or half group) -> scaled values
-            const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
-            const float sc = bf16_to_f32(sbits) * isd;
-            const float off = (float)(1 << (BITS - 1));
-            float y[NE];
-            unpack_codes<BITS, NE>(w, y);
-            if (t0 + 32 * NWV < te) codes_of(t0 + 32 * NWV);     // the next tile's, in flight meanwhile
-#pragma unroll
-            for (int e = 0; e < NE; ++e) y[e] = fmaf(y[e], sc, -off * sc);
-            // back to the register pairs of the swap stage: y[e], e = (j&3) + 4 sd + 8 (j>>2) + 32 mp
-            // in-register stages over the in-group bits (incl. feature bit 2 = sd)
-#pragma unroll
-            for (int bit = 1; bit < NE; bit <<= 1)
-#pragma unroll
-                for (int e = 0; e < NE; ++e)
-                    if (!(e & bit)) {
-                        const float a = y[e], b = y[e | bit];
-                        y[e] = a + b;
-                        y[e | bit] = a - b;
+    // one tile loop for 16-byte aligned rows of U~_t and one for the rest,
+    // chosen once
+    auto tiles = [&](auto vec_tag) {
+        constexpr bool VEC = decltype(vec_tag)::value;
+        for (int t0 = tb + 32 * wave; t0 < te; t0 += 32 * NWV) {
+            const int tok = t0 + ln;
+            const bool tv = tok < te;
+            // rotated-back residual first, straight into the accumulators of the X^
+            // products (the MFMA layout), so that it and the products are never live
+            // at the same time
+            f32x16 acc[NMF];
+            if constexpr (BITS > 0) {
+                // codes of the lane's group (or half group) -> scaled values
+                const float isd = (D == 128) ? 0.08838834764831845f : 0.125f;
+                const float sc = bf16_to_f32(sbits) * isd;
+                const float off = (float)(1 << (BITS - 1));
+                float y[NE];
+                unpack_codes<BITS, NE>(w, y);
+                if (t0 + 32 * NWV < te) codes_of(t0 + 32 * NWV);     // the next tile's, in flight meanwhile
+    #pragma unroll
+                for (int e = 0; e < NE; ++e) y[e] = fmaf(y[e], sc, -off * sc);
+                // back to the register pairs of the swap stage: y[e], e = (j&3) + 4 sd + 8 (j>>2) + 32 mp
+                // in-register stages over the in-group bits (incl. feature bit 2 = sd)
+    #pragma unroll
+                for (int bit = 1; bit < NE; bit <<= 1)
+    #pragma unroll
+                    for (int e = 0; e < NE; ++e)
+                        if (!(e & bit)) {
+                            const float a = y[e], b = y[e | bit];
+                            y[e] = a + b;
+                            y[e | bit] = a - b;
+                        }
+                // top feature bit across lane halves; lane half becomes feature bit 2 again
+    #pragma unroll
+                for (int mp = 0; mp < HALF; ++mp)
+    #pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
+                        float u = y[e], v = y[e + 4];
+                        swap_halves(u, v);
+                        acc[mp][j] = u + v;
+                        acc[mp + HALF][j] = u - v;
                     }
-            // top feature bit across lane halves; lane half becomes feature bit 2 again
-#pragma unroll
-            for (int mp = 0; mp < HALF; ++mp)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
-                    float u = y[e], v = y[e + 4];
-                    swap_halves(u, v);
-                    acc[mp][j] = u + v;
-                    acc[mp + HALF][j] = u - v;
-                }
-        } else {
-#pragma unroll
-            for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
-        }
-        // s o X~ = rotated-back residual + s o X^
-        xhat_mfma<T, NMF>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+            } else {
+    #pragma unroll
+                for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
+            }
+            // s o X~ = rotated-back residual + s o X^
+            xhat_mfma_rows<T, NMF, VEC>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
 
-        // stored from the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
-        // of its token) with the signs
-        if (tv) {
-            uint8_t *orow = reinterpret_cast<uint8_t *>(it.out) + ((size_t)lh * it.T + tok) * TL::RB;
-#pragma unroll
-            for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    const int j = 4 * jb;
-                    put4_signed<T>(orow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, acc[mf][j], acc[mf][j + 1],
-                                   acc[mf][j + 2], acc[mf][j + 3]);
-                }
+            // stored from the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
+            // of its token) with the signs
+            if (tv) {
+                uint8_t *orow = reinterpret_cast<uint8_t *>(it.out) + ((size_t)lh * it.T + tok) * TL::RB;
+    #pragma unroll
+                for (int mf = 0; mf < NMF; ++mf)
+    #pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) {
+                        const int j = 4 * jb;
+                        put4_signed<T>(orow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, acc[mf][j], acc[mf][j + 1],
+                                       acc[mf][j + 2], acc[mf][j + 3]);
+                    }
+            }
         }
-    }
+    };
+    if ((it.rt & 7) == 0) tiles(std::true_type{});
+    else tiles(std::false_type{});
 }
 
 // ------------------------------------------------------------------ W~ construction
@@ -771,7 +799,8 @@ __global__ void k_rademacher_fill(uint64_t key, uint32_t stream, uint64_t first,
 // fewer tiles per range than waves.
 template <typename T, int D>
 struct CodecShape {
-    static constexpr int NW = 8;
+    static constexpr int NWE = 8;           // encoder waves
+    static constexpr int NW = 8;            // decoder waves
     static size_t wt_lds(int maxRtp) {
         return (size_t)(sizeof(T) == 2 ? 2 : 1) * D * (maxRtp + 16 / sizeof(T)) * sizeof(T);
     }
@@ -811,10 +840,10 @@ template <typename T, int D, int BITS>
 static hipError_t encode_one(const CodecBatch &b, int maxT, int maxLH, int maxRtp, hipStream_t s) {
     using CS = CodecShape<T, D>;
     int tpw = 0;
-    const dim3 grid = codec_grid(b, maxT, maxLH, CS::NW, tpw);
+    const dim3 grid = codec_grid(b, maxT, maxLH, CS::NWE, tpw);
     if (CS::wl(maxRtp))
-        return codec_launch<k_encode<T, D, BITS, CS::NW, true>>(grid, 64 * CS::NW, CS::wt_lds(maxRtp), s, b, tpw);
-    return codec_launch<k_encode<T, D, BITS, CS::NW, false>>(grid, 64 * CS::NW, 0, s, b, tpw);
+        return codec_launch<k_encode<T, D, BITS, CS::NWE, true>>(grid, 64 * CS::NWE, CS::wt_lds(maxRtp), s, b, tpw);
+    return codec_launch<k_encode<T, D, BITS, CS::NWE, false>>(grid, 64 * CS::NWE, 0, s, b, tpw);
 }
 template <typename T, int D, int BITS>
 static hipError_t decode_one(const CodecBatch &b, int maxT, int maxLH, int maxRtp, hipStream_t s) {
