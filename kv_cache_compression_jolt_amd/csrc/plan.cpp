@@ -92,7 +92,9 @@ Dims dims_for(const jolt_config &cfg, const jolt_item &it, int rt_max, int rf_ma
     D.rtp32 = round_up(std::max(rt_max, 1), 32);
     D.k = (cfg.mode == JOLT_TOKEN_RANDOMIZED) ? rt_max + cfg.oversample : 0;
     D.kp = round_up(std::max(D.k, 1), 32);
-    D.xs_split = clampi(D.T / 4096, 1, 16);
+    // Q^T A: about one workgroup per CU, as for A M below (ceil(n / 256) feature
+    // tiles per item, 16 items per launch); a split adds a reduction pass
+    D.xs_split = clampi(256 / std::max(1, ((D.n + 255) / 256) * kMaxBatch), 1, std::max(1, D.T / 64));
     D.xs_tsplit = round_up((D.T + D.xs_split - 1) / D.xs_split, 64);
     D.xs_split = (D.T + D.xs_tsplit - 1) / D.xs_tsplit;
     const int64_t rows = (int64_t)D.LH * D.T;
