@@ -340,7 +340,7 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
         }
         // LDS reads kept ahead of the MFMAs (per 16 tokens: R x fragments, then
         // one q fragment per R MFMAs)
-        if constexpr (BF) sched_reads_ahead<(TC / 16) * (R + NF * (LO ? 2 : 1)), R, 4>();
+        if constexpr (BF) sched_reads_ahead<(TC / 16) * (R + NF * (LO ? 2 : 1)), R, 8>();
     }
     float *out = it.out + (size_t)sp * it.ncols * n;
 #pragma unroll
