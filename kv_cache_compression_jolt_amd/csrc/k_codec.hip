@@ -259,15 +259,17 @@ __device__ __forceinline__ FragF32 frag_or_zero<float>(const float *p, bool ok) 
 // only), then per K step the hi products of every feature block and the lo
 // ones, with the W~ fragment reads kept ahead of them.  What is left (all of
 // it when !VEC) runs with its fragments checked against the row end.
-template <typename T, int NMF, bool VEC>
+template <typename T, int NMF, bool VEC, bool DEEP>
 __device__ __forceinline__ void xhat_mfma_rows(const T *wt, const T *wlo, int rtp, const T *ut, int rt, int tok,
                                                bool tv, int lane, f32x16 *acc) {
     const int ln = lane & 31, h = lane >> 5;
     constexpr int KB = 4;                  // fragments in flight
     const T *urow = ut + (size_t)(tv ? tok : 0) * rt;
     int k0b = 0;
-    if constexpr (VEC && sizeof(T) == 2) {
+    if constexpr (VEC && DEEP && sizeof(T) == 2) {
         // 256-deep batches first: 16 fragments in flight, one wait per batch
+        // (DEEP: W~ in LDS; with W~ read from global memory the 16 fragments
+        // leave too few registers)
         constexpr int KW = 16;
         for (; k0b + 16 * KW <= rt; k0b += 16 * KW) {
             typename Elem<T>::Frag b[KW];
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch, int tpw) 
     #pragma unroll
                     for (int c = 0; c < 4; ++c) acc[mf][4 * jb + c] = xv[c];
                 }
-            xhat_mfma_rows<T, NMF, VEC>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+            xhat_mfma_rows<T, NMF, VEC, WL>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
             float r[NMF][16];
     #pragma unroll
             for (int mf = 0; mf < NMF; ++mf)
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(64 * NWV) void k_decode(CodecBatch batch, int tpw) 
                 for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
             }
             // s o X~ = rotated-back residual + s o X^
-            xhat_mfma_rows<T, NMF, VEC>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
+            xhat_mfma_rows<T, NMF, VEC, WL>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
 
             // stored from the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
             // of its token) with the signs
@@ -792,7 +794,8 @@ __global__ void k_rademacher_fill(uint64_t key, uint32_t stream, uint64_t first,
 }
 
 // ------------------------------------------------------------------ launchers
-// Workgroups of NW waves (16 for bf16, 8 for fp32) over one (layer, head) and
+// Workgroups of 8 waves (two per SIMD: the encoder and decoder each need
+// about 220-250 registers per lane) over one (layer, head) and
 // a range of tokens.  W~ goes through LDS when it fits (135 KiB for bf16
 // d = 128, r_tp = 256: one workgroup per CU).  The ranges are whole tiles,
 // as many per (layer, head) as give about 1024 workgroups per launch, but no
