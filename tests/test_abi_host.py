@@ -143,6 +143,32 @@ def test_plan_from_tables_bit_exact(lib, seed, structured):
             assert a.bytes == int(t["B"][c]) and a.distortion == float(t["D"][c])
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_plan_from_tables_tied_slopes(lib, seed):
+    # Groups of items with identical integer tables share every hull slope
+    # exactly: the selection of lambda* must take all edges of one slope, over
+    # all items, together (the pages' single dual, landing page abstract).
+    grid = oalloc.candidate_grid(16, 16, 8, (0, 2, 3, 4))
+    rg = np.random.default_rng(seed + 7)
+    base = []
+    for _ in range(3):
+        D = rg.integers(0, 40, len(grid)).astype(np.float64)
+        B = (rg.integers(1, 64, len(grid)) * 16).astype(np.int64)
+        base.append((D, B))
+    tabs = [{"cand": grid, "D": base[i % 3][0], "B": base[i % 3][1]} for i in range(12)]
+    Bmin = sum(int(t["B"].min()) for t in tabs)
+    Bmax = sum(int(t["B"].max()) for t in tabs)
+    budgets = sorted(set([Bmin, Bmax] + [int(v) for v in rg.integers(Bmin, Bmax, 40)]))
+    for budget in budgets:
+        ch, lam, ok = oalloc.lagrangian_allocate(tabs, budget)
+        st, al, lam_c = jb.jolt_plan_from_tables([t["cand"] for t in tabs], [t["D"] for t in tabs],
+                                                 [t["B"] for t in tabs], budget)
+        assert ok and st == jb.JOLT_OK
+        assert abs(lam_c - float(lam)) <= 1e-12 * max(1.0, abs(float(lam)))
+        for t, c, a in zip(tabs, ch, al):
+            assert (a.rt, a.rf, a.bits) == tuple(int(v) for v in t["cand"][c])
+
+
 def test_plan_from_tables_full_grid(lib):
     # one c2-sized problem: 16 items x 1028 candidates
     grid = oalloc.candidate_grid(128, 128, 8, (0, 2, 3, 4))
