@@ -1,10 +1,10 @@
-// Symmetric eigensolver for small dense matrices (n <= kTriMaxN) in four
+// Symmetric eigensolver for small dense matrices (n <= kTriMaxN) in five
 // launches that hand over through a per-matrix workspace (tri_ws):
 // k_eig_tridiag (step 1) and k_eig_polish (step 5, output) run one workgroup
-// of 1024 threads per matrix with the matrix resident in LDS; k_eig_trivec
-// (steps 2, 3, and the compact-WY T of each reflector block) runs a group of
-// 16 lanes per eigenvalue over the whole chip; k_eig_backtr (step 4) runs a
-// workgroup per 32 columns of each matrix.
+// of 1024 threads per matrix with the matrix resident in LDS; k_eig_wy forms
+// the compact-WY T of each reflector block (a wave per block); k_eig_trivec
+// (steps 2 and 3) runs a group of 16 lanes per eigenvalue over the whole chip;
+// k_eig_backtr (step 4) runs a workgroup per 32 columns of each matrix.
 //
 //   1. Householder tridiagonalization Q^T A Q = T (Golub & Van Loan, Matrix
 //      Computations, sec. 8.3.1) in panels of 32 columns: within a panel the
@@ -695,11 +695,10 @@ template <int NMAX>
 struct VecDims {
     static constexpr int kVecPad = NMAX + 24;           // room for the batch reads past the end
     static constexpr int kYPitch = NMAX + 1;            // odd: lanes reading a column meet distinct banks
-    // LDS of one k_eig_trivec workgroup in floats: the eigenpair role's arrays,
-    // or the T role's reflector block and G / T buffer
+    // LDS in floats of one k_eig_trivec workgroup (the eigenpair arrays) and of
+    // one k_eig_wy workgroup (a reflector block and its G / T buffer)
     static constexpr int kLdsEig = 4 * kVecPad + 4 * NMAX + kVecPerWave * 3 * NMAX;
     static constexpr int kLdsWy = 32 * kYPitch + 32 * 33 + 32;
-    static constexpr int kLds = kLdsEig > kLdsWy ? kLdsEig : kLdsWy;
 };
 
 // T of reflector block b for k_eig_backtr, one wave (the T role of
@@ -744,19 +743,26 @@ __device__ void wy_block(const TriWs &w, int n, int b, float *lds, int lane) {
     }
 }
 
+// The compact-WY T blocks for k_eig_backtr, one wave per block of 32 reflectors
+// (a launch of its own: its LDS, which the eigenpair workgroups do not need,
+// would otherwise be reserved for every one of them and cut their occupancy).
 template <int NMAX, class B>
-__global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(B batch, int eig_blocks) {
+__global__ __launch_bounds__(64) void k_eig_wy(B batch) {
+    __shared__ __attribute__((aligned(16))) float lds[VecDims<NMAX>::kLdsWy];
+    const JacItem &it = batch.it[blockIdx.y];
+    const int n = it.n;
+    const TriWs w = tri_ws(it.tw, n);
+    if ((int)blockIdx.x < tri_blocks(n)) wy_block<NMAX>(w, n, blockIdx.x, lds, threadIdx.x & 63);
+}
+
+template <int NMAX, class B>
+__global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(B batch) {
     constexpr int kTriMaxN = NMAX, kVecPad = VecDims<NMAX>::kVecPad;
-    __shared__ __attribute__((aligned(16))) float lds[VecDims<NMAX>::kLds];
+    __shared__ __attribute__((aligned(16))) float lds[VecDims<NMAX>::kLdsEig];
     const JacItem &it = batch.it[blockIdx.y];
     const int n = it.n;
     const TriWs w = tri_ws(it.tw, n);
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if ((int)blockIdx.x >= eig_blocks) {
-        const int b = blockIdx.x - eig_blocks;
-        if (b < tri_blocks(n)) wy_block<NMAX>(w, n, b, lds, lane);
-        return;
-    }
     constexpr int kPerBlock = kVecWaves * kVecPerWave;
     if ((int)blockIdx.x * kPerBlock >= n) return;
     float *sd = lds, *se = sd + kVecPad;
@@ -1499,8 +1505,8 @@ static hipError_t launch_eig_wide(const B &b, int count, int maxN, hipStream_t s
         KTimeScope kts("k_eig_trivec", s);
         constexpr int per = kVecWaves * kVecPerWave;
         const int eig_blocks = (maxN + per - 1) / per;
-        hipLaunchKernelGGL((k_eig_trivec<kWideMaxN, B>), dim3(eig_blocks + nblk, count), dim3(64 * kVecWaves), 0, s, b,
-                           eig_blocks);
+        hipLaunchKernelGGL((k_eig_wy<kWideMaxN, B>), dim3(std::max(nblk, 1), count), dim3(64), 0, s, b);
+        hipLaunchKernelGGL((k_eig_trivec<kWideMaxN, B>), dim3(eig_blocks, count), dim3(64 * kVecWaves), 0, s, b);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     {
@@ -1540,8 +1546,8 @@ static hipError_t eig_tri(const JacItem *items, int count, const B &b, int maxN,
         KTimeScope kts("k_eig_trivec", s);
         constexpr int per = kVecWaves * kVecPerWave;
         const int eig_blocks = (maxN + per - 1) / per;
-        hipLaunchKernelGGL((k_eig_trivec<kTriMaxN, B>), dim3(eig_blocks + nblk, count), dim3(64 * kVecWaves), 0, s, b,
-                           eig_blocks);
+        hipLaunchKernelGGL((k_eig_wy<kTriMaxN, B>), dim3(std::max(nblk, 1), count), dim3(64), 0, s, b);
+        hipLaunchKernelGGL((k_eig_trivec<kTriMaxN, B>), dim3(eig_blocks, count), dim3(64 * kVecWaves), 0, s, b);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     {
