@@ -697,7 +697,7 @@ struct VecDims {
     static constexpr int kYPitch = NMAX + 1;            // odd: lanes reading a column meet distinct banks
     // LDS in floats of one k_eig_trivec workgroup (the eigenpair arrays) and of
     // one k_eig_wy workgroup (a reflector block and its G / T buffer)
-    static constexpr int kLdsEig = 4 * kVecPad + 4 * NMAX + kVecPerWave * 3 * NMAX;
+    static constexpr int kLdsEig = 4 * kVecPad + kVecPerWave * 2 * NMAX;
     static constexpr int kLdsWy = 32 * kYPitch + 32 * 33 + 32;
 };
 
@@ -767,22 +767,13 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(B batch) {
     if ((int)blockIdx.x * kPerBlock >= n) return;
     float *sd = lds, *se = sd + kVecPad;
     float2 *sde = reinterpret_cast<float2 *>(se + kVecPad);      // {d_i, e_{i-1}^2}
-    float *tx = reinterpret_cast<float *>(sde + kVecPad);         // d, e^2 in step order: [0] up, [1] down
-    float *te = tx + 2 * kTriMaxN;
-    float *piv = te + 2 * kTriMaxN;                                // [wave][group][2][kTriMaxN] pivots
-    float *zc = piv + kVecWaves * kVecPerWave * 2 * kTriMaxN;      // [wave][group][kTriMaxN]
+    // [wave][group][2][kTriMaxN]: the pivots, then the eigenvector in their place
+    float *piv = reinterpret_cast<float *>(sde + kVecPad);
     for (int i = tid; i < kVecPad; i += 64 * kVecWaves) {
-        const float di = i < n ? w.d[i] : 0.f, em = i > 0 && i <= n ? w.e[i - 1] : 0.f;
+        const float di = i < n ? w.d[i] : 0.f, em = i > 0 && i < n ? w.e[i - 1] : 0.f;
         sd[i] = di;
         se[i] = i < n ? w.e[i] : 0.f;
         sde[i] = make_float2(di, em * em);
-        if (i < n) {
-            const float er = i > 0 ? w.e[n - 1 - i] : 0.f;     // e_{n-1-i}, none at step 0
-            tx[i] = di;
-            te[i] = em * em;
-            tx[kTriMaxN + i] = w.d[n - 1 - i];
-            te[kTriMaxN + i] = er * er;
-        }
     }
     __syncthreads();
     const int g = lane / kVecGroup, q = lane % kVecGroup;
@@ -861,13 +852,15 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(B batch) {
     const float lam = 0.5f * (a + b);
 
     // pivots of T - lam I = L+ D+ L+^T (lane 0 of the group, i upwards) and
-    // U- D- U-^T (lane 1, i downwards), both in step order s: lane 1 reads
-    // the reversed copies of d and e^2, and P[1][s] = D-_{n-1-s}
+    // U- D- U-^T (lane 1, i downwards), both in step order s: step s of lane 1
+    // takes row n-1-s (d from sde[n-1-s], e^2 of the pair below it from
+    // sde[n-s], none at step 0), and P[1][s] = D-_{n-1-s}
     float *P = piv + (wid * kVecPerWave + g) * 2 * kTriMaxN;
-    float *z = zc + (wid * kVecPerWave + g) * kTriMaxN;
     if (kv && q < 2) {
-        const float *xs = tx + q * kTriMaxN, *es = te + q * kTriMaxN;
         float *ps = P + q * kTriMaxN;
+        const float *sdx = reinterpret_cast<const float *>(sde), *sdy = sdx + 1;
+        // float offsets of row x(s) = s or n-1-s and of the e^2 entry e(s) = s or n-s
+        const int x0 = q ? 2 * (n - 1) : 0, e0 = q ? 2 * n : 0, dx = q ? -2 : 2;
         float p = 1.f;     // step 0 has e^2 = 0: p = d - lam
         auto step = [&](float xv, float ev) {
             p = fmaf(-ev, __builtin_amdgcn_rcpf(p), xv - lam);
@@ -879,13 +872,14 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(B batch) {
             float xv[8], ev[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                xv[u] = xs[s0 + u];
-                ev[u] = es[s0 + u];
+                xv[u] = sdx[x0 + dx * (s0 + u)];
+                ev[u] = sdy[e0 + dx * (s0 + u)];
             }
+            if (s0 == 0) ev[0] = 0.f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) ps[s0 + u] = step(xv[u], ev[u]);
         }
-        for (; s0 < n; ++s0) ps[s0] = step(xs[s0], es[s0]);
+        for (; s0 < n; ++s0) ps[s0] = step(sdx[x0 + dx * s0], s0 == 0 ? 0.f : sdy[e0 + dx * s0]);
     }
     wave_lds_sync();
     // twist index r: the first i where |gamma_i| is smallest, gamma_i =
@@ -914,47 +908,57 @@ __global__ __launch_bounds__(64 * kVecWaves) void k_eig_trivec(B batch) {
     }
     // z_r = 1; z_i = f_i z_{i+1} above r with f_i = -(e_i / D+_i), z_i = f_i z_{i-1}
     // below with f_i = -(e_{i-1} / D-_i): the factors by the whole group, the
-    // running products by lanes 0 (up) and 1 (down)
+    // running products by lanes 0 (up) and 1 (down).  Each factor and product
+    // takes the place of the pivot it came from: z_i at P[i] for i <= r and at
+    // P[1][n-1-i] for i > r, so both lanes walk their half downwards.
     if (kv) {
         for (int i = q; i < n; i += kVecGroup) {
-            float f = 1.f;
-            if (i < r) f = -(se[i] * __builtin_amdgcn_rcpf(P[i]));
-            else if (i > r) f = -(se[i - 1] * __builtin_amdgcn_rcpf(P[kTriMaxN + n - 1 - i]));
-            z[i] = f;
+            if (i < r) {
+                P[i] = -(se[i] * __builtin_amdgcn_rcpf(P[i]));
+            } else if (i > r) {
+                float *pb = P + kTriMaxN + n - 1 - i;
+                *pb = -(se[i - 1] * __builtin_amdgcn_rcpf(*pb));
+            } else {
+                P[r] = 1.f;
+            }
         }
     }
     wave_lds_sync();
     if (kv && q < 2) {
-        const bool up = q == 0;
-        const int len = up ? r : n - 1 - r, di = up ? -1 : 1;
+        float *zb = P + q * kTriMaxN;
+        const int len = q == 0 ? r : n - 1 - r;
+        int j = q == 0 ? r - 1 : n - 2 - r;      // the first entry of the walk
         float zz = 1.f;
-        int i = r + di;
         int s0 = 0;
         for (; s0 + 8 <= len; s0 += 8) {
             float fv[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) fv[u] = z[i + di * u];
+            for (int u = 0; u < 8; ++u) fv[u] = zb[j - u];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 zz = fv[u] * zz;
-                z[i + di * u] = zz;
+                zb[j - u] = zz;
             }
-            i += 8 * di;
+            j -= 8;
         }
-        for (; s0 < len; ++s0, i += di) {
-            zz = z[i] * zz;
-            z[i] = zz;
+        for (; s0 < len; ++s0, --j) {
+            zz = zb[j] * zz;
+            zb[j] = zz;
         }
     }
     wave_lds_sync();
+    auto zval = [&](int i) { return i <= r ? P[i] : P[kTriMaxN + n - 1 - i]; };
     float ss = 0.f;
     if (kv)
-        for (int i = q; i < n; i += kVecGroup) ss += z[i] * z[i];
+        for (int i = q; i < n; i += kVecGroup) {
+            const float zi = zval(i);
+            ss += zi * zi;
+        }
     const float nrm = group16_sum(ss);
     if (!kv) return;
     if (!(nrm < FLT_MAX) && q == 0) *w.flag = 1;
     const float inv = 1.f / sqrtf(nrm);
-    for (int i = q; i < w.np; i += kVecGroup) w.zt[(size_t)k * w.np + i] = i < n ? z[i] * inv : 0.f;
+    for (int i = q; i < w.np; i += kVecGroup) w.zt[(size_t)k * w.np + i] = i < n ? zval(i) * inv : 0.f;
     if (q == 0) w.lam[k] = lam;
 }
 
