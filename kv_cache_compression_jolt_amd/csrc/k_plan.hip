@@ -369,7 +369,11 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
 // keep T, and so every chunk, a multiple of 64).  Per chunk the rows go to LDS
 // transposed, xs[f][r] (bf16 row pairs packed in 32-bit words); the next
 // chunk's rows are in flight in registers while the MFMAs run on the current
-// one, and each fragment is one 16-byte LDS read.
+// one, and each fragment is one 16-byte LDS read.  Only the upper fragment
+// pairs (mf <= nf) are formed, dealt to the waves in row order (pair t to wave
+// t mod 4); a lower tile is the transpose of its upper one, whose every entry
+// is the same sum of the same exact products in the same order, and is stored
+// from it.
 template <typename T>
 __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
     constexpr int PER = 16 / sizeof(T);            // features per 16-byte piece
@@ -424,11 +428,23 @@ __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
             }
         }
     };
-    // fragment pairs owned by this wave: (mf, nf) = q / nmf, q % nmf, q = wave + 4 i
-    f32x16 acc[4];
+    // upper fragment pairs owned by this wave: t = wave + 4 i, t -> (mf, nf) in
+    // row order of the upper triangle
+    f32x16 acc[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-    const int nq = nmf * nmf;
+    for (int i = 0; i < 3; ++i) acc[i] = f32x16{};
+    const int nq = nmf * (nmf + 1) / 2;
+    int pm[3], pn[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        int t = wave + 4 * i, mf = 0;
+        while (t >= nmf - mf && mf < nmf - 1) {
+            t -= nmf - mf;
+            ++mf;
+        }
+        pm[i] = mf;
+        pn[i] = mf + t;
+    }
     if (rb < re) load(rb);
     for (int64_t r0 = rb; r0 < re; r0 += 64) {
         __syncthreads();                           // the previous chunk's reads of xs are done
@@ -438,12 +454,10 @@ __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
 #pragma unroll
         for (int kk = 0; kk < 64; kk += 16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = wave + 4 * i;
-                if (q < nq) {
-                    const int mf = q / nmf, nf = q % nmf;
-                    const typename Elem<T>::Frag a = load_frag(xs + (32 * mf + ln) * XP + kk + 8 * h);
-                    const typename Elem<T>::Frag b = load_frag(xs + (32 * nf + ln) * XP + kk + 8 * h);
+            for (int i = 0; i < 3; ++i) {
+                if (wave + 4 * i < nq) {
+                    const typename Elem<T>::Frag a = load_frag(xs + (32 * pm[i] + ln) * XP + kk + 8 * h);
+                    const typename Elem<T>::Frag b = load_frag(xs + (32 * pn[i] + ln) * XP + kk + 8 * h);
                     mfma(a, b, acc[i]);
                 }
             }
@@ -451,12 +465,17 @@ __global__ __launch_bounds__(256) void k_gram_rows(GramBatch batch, int d) {
     }
     float *out = it.out + (size_t)p * d * d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = wave + 4 * i;
-        if (q < nq) {
-            const int mf = q / nmf, nf = q % nmf;
+    for (int i = 0; i < 3; ++i) {
+        if (wave + 4 * i < nq) {
+            const int mf = pm[i], nf = pn[i];
 #pragma unroll
             for (int j = 0; j < 16; ++j) out[(size_t)(32 * mf + frag_row(lane, j)) * d + 32 * nf + ln] = acc[i][j];
+            if (mf != nf)
+                // the mirror: row 32 nf + ln, columns 32 mf + frag_row(lane, 4 c .. 4 c + 3)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<float4 *>(out + (size_t)(32 * nf + ln) * d + 32 * mf + frag_row(lane, 4 * c)) =
+                        make_float4(acc[i][4 * c], acc[i][4 * c + 1], acc[i][4 * c + 2], acc[i][4 * c + 3]);
         }
     }
 }
