@@ -260,6 +260,11 @@ def iter_raw_parallel(cfg: CacheConfig, specs: List[Item], workers: int = 0, sta
     with ctx.Pool(workers) as pool:
         for i, raw in enumerate(pool.imap(_raw_worker, [(cfg, s) for s in specs], chunksize=1)):
             yield i, raw
+        # every task is done: let the workers exit on their own rather than
+        # terminating them with a signal (a profiler preloaded into them
+        # handles that signal and can stall the parent waiting for them)
+        pool.close()
+        pool.join()
 
 
 def gaussian_groups(n_groups: int, group: int = 64, seed: int = 0) -> np.ndarray:
