@@ -694,11 +694,10 @@ constexpr int kVecPerWave = 64 / kVecGroup;
 template <int NMAX>
 struct VecDims {
     static constexpr int kVecPad = NMAX + 24;           // room for the batch reads past the end
-    static constexpr int kYPitch = NMAX + 1;            // odd: lanes reading a column meet distinct banks
     // LDS in floats of one k_eig_trivec workgroup (the eigenpair arrays) and of
-    // one k_eig_wy workgroup (a reflector block and its G / T buffer)
+    // one k_eig_wy workgroup (a block's G / T buffer and its tau)
     static constexpr int kLdsEig = 4 * kVecPad + kVecPerWave * 2 * NMAX;
-    static constexpr int kLdsWy = 32 * kYPitch + 32 * 33 + 32;
+    static constexpr int kLdsWy = 32 * 33 + 32;
 };
 
 // T of reflector block b for k_eig_backtr, one wave (the T role of
@@ -706,27 +705,27 @@ struct VecDims {
 // zero for r <= b0 + i), then (diag(1 / tau) + strict_upper(G)) T = I column
 // by column (wblock_t_full).  A partial last block is padded with zero
 // reflectors of tau = 0, whose rows and columns of T come out zero.
+// The reflectors are read straight from the workspace rows (reflector i of the
+// block is row b0 + i, 16-byte aligned): lane (i, kh) loads 4 consecutive
+// entries of row i and supplies the K index kh of two consecutive MFMA steps.
 template <int NMAX>
 __device__ void wy_block(const TriWs &w, int n, int b, float *lds, int lane) {
-    constexpr int kYPitch = VecDims<NMAX>::kYPitch;
     const int mref = max(n - 2, 0), b0 = 32 * b, nbk = min(32, mref - b0);
-    float *Ys = lds;                    // Ys[i * kYPitch + r] = Y(r, i)
-    float *D = Ys + 32 * kYPitch;       // G(i, c), i < c, then T(i, c), i <= c, at D[c * 33 + i]
+    float *D = lds;                     // G(i, c), i < c, then T(i, c), i <= c, at D[c * 33 + i]
     float *taus = D + 32 * 33;
-    for (int e = lane; e < 32 * kYPitch; e += 64) {
-        const int i = e / kYPitch, r = e - i * kYPitch;
-        Ys[e] = i < nbk && r > b0 + i && r < n ? w.a[(size_t)(b0 + i) * w.np + r] : 0.f;
-    }
     if (lane < 32) taus[lane] = lane < nbk ? w.tau[b0 + lane] : 0.f;
-    wave_lds_sync();
     const int m32 = lane & 31, kh = lane >> 5;
+    const bool iv = m32 < nbk;
+    const float *yrow = w.a + (size_t)(b0 + (iv ? m32 : 0)) * w.np;
     f32x16 g = {};
-    for (int k0 = b0; k0 < n; k0 += 8) {
-        float y[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) y[u] = Ys[m32 * kYPitch + min(k0 + 2 * u + kh, kYPitch - 1)];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) g = __builtin_amdgcn_mfma_f32_32x32x2f32(y[u], y[u], g, 0, 0, 0);
+    for (int k0 = b0; k0 < n; k0 += 4) {            // k0 + 3 < np: rows are n rounded up to 4
+        const float4 v = *reinterpret_cast<const float4 *>(yrow + k0);
+        const float e0 = kh ? v.y : v.x, e1 = kh ? v.w : v.z;
+        const int r0 = k0 + kh, r1 = k0 + 2 + kh;
+        const float y0 = iv && r0 > b0 + m32 && r0 < n ? e0 : 0.f;
+        const float y1 = iv && r1 > b0 + m32 && r1 < n ? e1 : 0.f;
+        g = __builtin_amdgcn_mfma_f32_32x32x2f32(y0, y0, g, 0, 0, 0);
+        g = __builtin_amdgcn_mfma_f32_32x32x2f32(y1, y1, g, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
