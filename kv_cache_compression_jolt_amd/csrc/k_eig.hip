@@ -1094,10 +1094,11 @@ __global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr(B batch, int ldy) 
     }
 }
 
-// The back-transform for the wide solver: the reflectors of one block at a
-// time go through LDS (all of them would not fit), with the block's T.
+// The back-transform for the wide solver: the reflectors are read straight
+// from the workspace rows (L2-resident; all of them would not fit in LDS next to
+// the columns of Z), the block's T through LDS.
 template <class B>
-__global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr_w(B batch, int ldy) {
+__global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr_w(B batch) {
     extern __shared__ float sm[];
     const JacItem &it = batch.it[blockIdx.y];
     const int n = it.n, c0 = 32 * blockIdx.x;
@@ -1107,8 +1108,7 @@ __global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr_w(B batch, int ldy
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m32 = lane & 31, kh = lane >> 5;
     const int mref = max(n - 2, 0), nblk = tri_blocks(n), nt = (n + 31) >> 5;
-    float *Ys = sm;                      // Ys[i * ldy + r] = v_{b0 + i}(r), block b only
-    float *Ts = Ys + 32 * ldy;           // T_b(i, k) at Ts[i * 33 + k]
+    float *Ts = sm;                      // T_b(i, k) at Ts[i * 33 + k]
     float *Zc = Ts + kTile;              // Z(r, c0 + m) at Zc[r * 33 + m]
     float *Pt = Zc + n * 33;             // partial S of wave w
     float *Mt = Pt + kBtWaves * kTile;   // M(k, m) at Mt[k * 33 + m]
@@ -1127,18 +1127,16 @@ __global__ __launch_bounds__(64 * kBtWaves) void k_eig_backtr_w(B batch, int ldy
     for (int b = nblk - 1; b >= 0; --b) {
         const int b0 = 32 * b, nbk = min(32, mref - b0);
         __syncthreads();
-        load_rows4<NT, 8>(w.a + (size_t)b0 * w.np, w.np, nbk, c4, tid, [&](int r, int c, float4 v) {
-            float *d = Ys + r * ldy + 4 * c;
-            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-        });
         load_rows4<NT, 8>(w.tb + 1024 * b, 32, 32, 8, tid, [&](int r, int c, float4 v) {
             float *d = Ts + r * 33 + 4 * c;
             d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
         });
         __syncthreads();
-        // Y(r, i): reflector b0 + i at row r, zero unless i < nbk and b0 + i < r < n
+        // Y(r, i): reflector b0 + i at row r (workspace row b0 + i), zero unless
+        // i < nbk and b0 + i < r < n
+        const float *ya0 = w.a + (size_t)b0 * w.np;
         auto Y = [&](int r, int i) {
-            return ld_or_zero(Ys, min(i, nbk - 1) * ldy + min(r, n - 1), i < nbk && r > b0 + i && r < n);
+            return ld_or_zero(ya0, min(i, nbk - 1) * w.np + min(r, n - 1), i < nbk && r > b0 + i && r < n);
         };
         {
             const int rows = n - 1 - b0, per = ((rows + 8 * kBtWaves - 1) / (8 * kBtWaves)) * 8;
@@ -1514,10 +1512,8 @@ static hipError_t launch_eig_wide(const B &b, int count, int maxN, hipStream_t s
     }
     {
         KTimeScope kts("k_eig_backtr", s);
-        const int ldy = eig_tri_np(maxN) + 1;
-        const size_t lds = ((size_t)32 * ldy + kTile + (size_t)maxN * 33 + (size_t)(kBtWaves + 1) * kTile) *
-                           sizeof(float);
-        hipLaunchKernelGGL(k_eig_backtr_w<B>, dim3((maxN + 31) / 32, count), dim3(64 * kBtWaves), lds, s, b, ldy);
+        const size_t lds = ((size_t)kTile + (size_t)maxN * 33 + (size_t)(kBtWaves + 1) * kTile) * sizeof(float);
+        hipLaunchKernelGGL(k_eig_backtr_w<B>, dim3((maxN + 31) / 32, count), dim3(64 * kBtWaves), lds, s, b);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     KTimeScope kts("k_eig_polish", s);
