@@ -182,23 +182,31 @@ __device__ __forceinline__ void stage_transposed(const T *src, int d, T *xs, int
 // the global feature index (the token unfolding's column).
 //
 // WG: a tile of 256 features (NWV waves x R row fragments of 32: 4 x 2, or
-// 8 x 1 for the widest column tiles) and NF column fragments of 32.  Per chunk of 64 tokens the WG stages, once, x's tile
-// transposed to xs[F][t] (token pairs packed in 32-bit words for bf16) and the
-// chunk of q (hi and lo parts when LO) as qs[c][t]; the next chunk is loaded
-// into registers meanwhile.  Each wave then reads 2 x fragments and NF (2 NF)
-// q fragments per 16 tokens from LDS.
+// 8 x 1 for the widest column tiles) and NF column fragments of 32.  Per chunk
+// of TC tokens the WG stages, once, x's tile transposed to xs[F][t] (token
+// pairs packed in 32-bit words for bf16) and the chunk of q (hi and lo parts
+// when LO) as qs[c][t].  Two LDS buffers: while the waves run the MFMAs of one
+// chunk out of one buffer, the next chunk (already in registers) is stored
+// into the other and the chunk after it is loaded from global memory, with one
+// barrier per chunk.  TC is 64 tokens when two such buffers fit the 160 KB of
+// LDS, else 32.  Each wave reads R x fragments and NF (2 NF) q fragments per
+// 16 tokens from LDS.
 template <typename T, int NF, bool LO, int NT>
 struct XtqTile {
     static constexpr int PER = 16 / sizeof(T);
     static constexpr int FT = 256;                       // features per WG
-    static constexpr int TC = 64;                        // tokens per chunk
-    static constexpr int XP = TC + PER;                  // LDS pitch of xs and qs rows
     static constexpr int QR = 32 * NF * (LO ? 2 : 1);    // q rows staged (hi rows, then lo rows)
+    static constexpr size_t buf_for(int tc) { return (size_t)(FT + QR) * (tc + PER) * sizeof(T); }
+    static constexpr int TC = 2 * buf_for(64) <= 160 * 1024 ? 64 : 32;   // tokens per chunk
+    static constexpr int XP = TC + PER;                  // LDS pitch of xs and qs rows
+    static constexpr int BUF = (FT + QR) * XP;           // elements per buffer
     static constexpr int XPIECES = FT * TC / PER / (sizeof(T) == 2 ? 2 : 1);  // loads of x per chunk
     static constexpr int XPT = XPIECES / NT;
     static constexpr int QPIECES = QR * TC / PER;
     static constexpr int QPT = (QPIECES + NT - 1) / NT;
-    static constexpr size_t lds_bytes = (size_t)(FT + QR) * XP * sizeof(T);
+    static constexpr size_t lds_bytes = 2 * buf_for(TC);
+    static_assert(XPIECES % NT == 0, "x pieces spread evenly over the threads");
+    static_assert(lds_bytes <= 160 * 1024, "two chunk buffers in LDS");
 };
 
 template <typename T, int NF, bool LO, int R, int NWV>
@@ -211,8 +219,7 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
     constexpr int XPT = Tile::XPT, QPT = Tile::QPT, QPIECES = Tile::QPIECES;
     constexpr bool BF = sizeof(T) == 2;
     extern __shared__ __attribute__((aligned(16))) unsigned char xtq_lds[];
-    T *xs = reinterpret_cast<T *>(xtq_lds);               // [FT][XP]
-    T *qs = xs + FT * XP;                                 // [QR][XP]
+    T *const lds = reinterpret_cast<T *>(xtq_lds);       // 2 x ([FT][XP] x rows, then [QR][XP] q rows)
     const Block3 blk = xcd_block();
     const XtqItem it = batch.it[blk.z];     // a copy: its fields stay in registers
     const int n = it.LH * d;
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
     const T *qh = reinterpret_cast<const T *>(it.qh);
     const T *ql = reinterpret_cast<const T *>(it.ql);
     const int tb = sp * it.tsplit, te = min(it.T, tb + it.tsplit);
-    const int nck = (te - tb) / TC;                       // T is a multiple of 64
+    const int nck = (te - tb) / TC;                       // T and the split are multiples of 64
 
     // x staging.  bf16: piece = 2 consecutive tokens x 8 features (two 16-byte
     // loads), lanes: 8 token pairs x 8 feature groups; fp32: piece = 1 token x 4
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
             }
         }
     };
-    auto store_x = [&]() {
+    auto store_x = [&](T *xs) {
 #pragma unroll
         for (int q = 0; q < XPT; ++q) {
             const int pass = wave + NWV * q;
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
             qr[q] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
         }
     };
-    auto store_q = [&]() {
+    auto store_q = [&](T *qs) {
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
             const int p = threadIdx.x + NT * q;
@@ -311,16 +318,17 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
     if (nck > 0) {
         load_x(tb);
         load_q(tb);
-    }
-    for (int ci = 0; ci < nck; ++ci) {
-        __syncthreads();                                  // the previous chunk's reads are done
-        store_x();
-        store_q();
-        __syncthreads();
-        if (ci + 1 < nck) {
-            load_x(tb + (ci + 1) * TC);
-            load_q(tb + (ci + 1) * TC);
+        store_x(lds);
+        store_q(lds + FT * XP);
+        if (nck > 1) {
+            load_x(tb + TC);
+            load_q(tb + TC);
         }
+    }
+    __syncthreads();
+    for (int ci = 0; ci < nck; ++ci) {
+        const T *xs = lds + (ci & 1) * Tile::BUF;
+        const T *qs = xs + FT * XP;
 #pragma unroll
         for (int kk = 0; kk < TC; kk += 16) {
             Frag a[R];
@@ -341,6 +349,17 @@ __global__ __launch_bounds__(64 * NWV) void k_xtq(XtqBatch batch, int d, int max
         // LDS reads kept ahead of the MFMAs (per 16 tokens: R x fragments, then
         // one q fragment per R MFMAs)
         if constexpr (BF) sched_reads_ahead<(TC / 16) * (R + NF * (LO ? 2 : 1)), R, 8>();
+        if (ci + 1 < nck) {
+            // the other buffer was last read before the previous barrier
+            T *nx = lds + ((ci + 1) & 1) * Tile::BUF;
+            store_x(nx);
+            store_q(nx + FT * XP);
+            if (ci + 2 < nck) {
+                load_x(tb + (ci + 2) * TC);
+                load_q(tb + (ci + 2) * TC);
+            }
+        }
+        __syncthreads();
     }
     float *out = it.out + (size_t)sp * it.ncols * n;
 #pragma unroll
