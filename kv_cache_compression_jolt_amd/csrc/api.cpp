@@ -325,10 +325,11 @@ extern "C" jolt_status jolt_plan_from_tables(int32_t n, const int32_t *n_cand, c
 // --------------------------------------------------------------------------- codec orchestration
 namespace jolt {
 
-// W~ for every item from its payload parameters, into codec_ws
+// W~ for every item from its payload parameters, into codec_ws (rot: the
+// encoder's rotated W~ for bf16 caches)
 static jolt_status build_wt_all(jolt_handle h, const jolt_item *items, int n, const jolt_alloc *alloc,
                                 const void *const *payload, uint8_t *ws, std::vector<void *> &wt_ptr,
-                                hipStream_t st) {
+                                bool rot, hipStream_t st) {
     const int D = items[0].d, dtype = items[0].dtype;
     size_t off = 0;
     wt_ptr.assign(n, nullptr);
@@ -336,7 +337,8 @@ static jolt_status build_wt_all(jolt_handle h, const jolt_item *items, int n, co
     b.n = 0;
     int maxLH = 0, maxRtp = 0;
     auto flush = [&]() -> jolt_status {
-        hipError_t e = launch_build_wt(b, dtype, D, maxLH, maxRtp, st);
+        hipError_t e = (rot && dtype == JOLT_BF16) ? launch_build_wt_rot(b, D, maxLH, maxRtp, st)
+                                                  : launch_build_wt(b, dtype, D, maxLH, maxRtp, st);
         if (e != hipSuccess) return hip_fail(h, e, "build_wt");
         b.n = 0; maxLH = 0; maxRtp = 0;
         return JOLT_OK;
@@ -384,7 +386,7 @@ static jolt_status run_codec(jolt_handle h, bool encode, const jolt_item *items,
         return fail(h, JOLT_E_WORKSPACE, "codec workspace: need %zu bytes, have %zu", need, codec_ws_bytes);
     std::vector<void *> wt;
     s = build_wt_all(h, items, n, alloc, reinterpret_cast<const void *const *>(payload_dev),
-                     static_cast<uint8_t *>(codec_ws), wt, st);
+                     static_cast<uint8_t *>(codec_ws), wt, encode, st);
     if (s) return s;
     const int D = items[0].d, dtype = items[0].dtype;
     for (int bits = 0; bits <= 8; ++bits) {

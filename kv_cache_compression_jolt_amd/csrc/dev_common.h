@@ -119,12 +119,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 // M MFMAs, so that AHEAD reads are in flight while the MFMAs run (without it
 // the scheduler puts each read right before its MFMA and waits for it there).
 // VM > 0: VM global loads of the same region are issued first of all, so that
-// they are in flight together.
-template <int N, int M, int AHEAD, int VM = 0>
+// they are in flight together.  PRE > 0: PRE MFMAs of the region that need none
+// of the reads (and of the loads) come next, while the loads are in flight,
+// with the first AHEAD reads issued in front of them.
+template <int N, int M, int AHEAD, int VM = 0, int PRE = 0>
 __device__ __forceinline__ void sched_reads_ahead() {
     constexpr int A = AHEAD < N ? AHEAD : N;
     if constexpr (VM > 0) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);   // VMEM reads
     __builtin_amdgcn_sched_group_barrier(0x100, A, 0);          // DS reads
+    if constexpr (PRE > 0) __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
 #pragma unroll
     for (int i = 0; i < N - A; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, M, 0);      // MFMA

@@ -53,6 +53,8 @@ hipError_t launch_encode(const CodecBatch &b, int dtype, int D, int bits, int ma
 hipError_t launch_decode(const CodecBatch &b, int dtype, int D, int bits, int maxT, int maxLH,
                          hipStream_t s);
 hipError_t launch_build_wt(const WtBatch &b, int dtype, int D, int maxLH, int maxRtp, hipStream_t s);
+// the encoder's W~ of bf16 caches: rotated, in the encoder's row order
+hipError_t launch_build_wt_rot(const WtBatch &b, int D, int maxLH, int maxRtp, hipStream_t s);
 
 // test hooks
 hipError_t launch_rotate(const float *in, float *out, int64_t rows, int d, const uint32_t *sign_bits,

@@ -259,22 +259,32 @@ __device__ __forceinline__ FragF32 frag_or_zero<float>(const float *p, bool ok) 
 // only), then per K step the hi products of every feature block and the lo
 // ones, with the W~ fragment reads kept ahead of them.  What is left (all of
 // it when !VEC) runs with its fragments checked against the row end.
-template <typename T, int NMF, bool VEC, bool DEEP>
+// pre: work on acc that needs none of the products (NPRE MFMAs), run after the
+// loads of the first 256-deep batch are issued when there is one (so that it
+// overlaps them), else before the products.
+struct NoPre {
+    static constexpr int NPRE = 0;
+    __device__ void operator()() const {}
+};
+template <typename T, int NMF, bool VEC, bool DEEP, typename Pre = NoPre>
 __device__ __forceinline__ void xhat_mfma_rows(const T *wt, const T *wlo, int rtp, const T *ut, int rt, int tok,
-                                               bool tv, int lane, f32x16 *acc) {
+                                               bool tv, int lane, f32x16 *acc, const Pre &pre = Pre{}) {
     const int ln = lane & 31, h = lane >> 5;
     constexpr int KB = 4;                  // fragments in flight
     const T *urow = ut + (size_t)(tv ? tok : 0) * rt;
     int k0b = 0;
+    bool pre_done = false;
     if constexpr (VEC && DEEP && sizeof(T) == 2) {
         // 256-deep batches first: 16 fragments in flight, one wait per batch
         // (DEEP: W~ in LDS; with W~ read from global memory the 16 fragments
         // leave too few registers)
         constexpr int KW = 16;
-        for (; k0b + 16 * KW <= rt; k0b += 16 * KW) {
+        auto batch = [&](auto with_pre) {
+            constexpr bool PRE = decltype(with_pre)::value;
             typename Elem<T>::Frag b[KW];
 #pragma unroll
             for (int q = 0; q < KW; ++q) b[q] = load_frag(urow + k0b + 16 * q + 8 * h);
+            if constexpr (PRE) pre();
 #pragma unroll
             for (int q = 0; q < KW; ++q) {
                 const int kk = k0b + 16 * q + 8 * h;
@@ -285,9 +295,16 @@ __device__ __forceinline__ void xhat_mfma_rows(const T *wt, const T *wlo, int rt
                 for (int mf = 0; mf < NMF; ++mf)
                     mfma(load_frag(wlo + (size_t)(32 * mf + ln) * rtp + kk), b[q], acc[mf]);
             }
-            sched_reads_ahead<KW * NMF * 2, 1, 4, KW>();
+            sched_reads_ahead<KW * NMF * 2, 1, 4, KW, PRE ? Pre::NPRE : 0>();
+        };
+        if (k0b + 16 * KW <= rt) {
+            batch(std::true_type{});
+            pre_done = true;
+            k0b += 16 * KW;
         }
+        for (; k0b + 16 * KW <= rt; k0b += 16 * KW) batch(std::false_type{});
     }
+    if (!pre_done) pre();
     if constexpr (VEC) {
         for (; k0b + 16 * KB <= rt; k0b += 16 * KB) {
             typename Elem<T>::Frag b[KB];
@@ -389,6 +406,130 @@ struct Tile {
     static constexpr int NMF = D / 32;
 };
 
+// ------------------------------------------------------------------ in-register Hadamard
+// H_D over the features of a 32-column tile held in the MFMA output layout
+// (lane l: column l % 32, features 32 mf + 8 (j / 4) + 4 (l / 32) + (j % 4)),
+// scaled by sc: the in-register stages over feature bits 0, 1, 3, 4 (j bits)
+// and the mf bits, then the stage over feature bit 2 (the lane half) with
+// v_permlane32_swap on register pairs that differ in the top feature bit.
+// Afterwards lane half h holds outputs (D/2) h + e in y[e], e < D/2.
+template <int NMF>
+__device__ __forceinline__ void hadamard_tile(const f32x16 *acc, float sc, float *y) {
+    constexpr int HALF = NMF / 2;
+    float r[NMF][16];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) r[mf][j] = acc[mf][j];
+#pragma unroll
+    for (int jbit = 1; jbit < 16; jbit <<= 1)
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (!(j & jbit)) {
+                    const float a = r[mf][j], b = r[mf][j | jbit];
+                    r[mf][j] = a + b;
+                    r[mf][j | jbit] = a - b;
+                }
+#pragma unroll
+    for (int mbit = 1; mbit < NMF; mbit <<= 1)
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf)
+            if (!(mf & mbit))
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float a = r[mf][j], b = r[mf | mbit][j];
+                    r[mf][j] = a + b;
+                    r[mf | mbit][j] = a - b;
+                }
+#pragma unroll
+    for (int mp = 0; mp < HALF; ++mp)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            float u = r[mp][j], w = r[mp + HALF][j];
+            swap_halves(u, w);
+            const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
+            y[e] = (u + w) * sc;
+            y[e + 4] = (u - w) * sc;
+        }
+}
+
+// ------------------------------------------------------------------ Hadamard as an MFMA operand
+// The rotated-domain encoder orders the D output rows of its products so that
+// MFMA row R = 32 mf + 8 jb + 4 hr + c is rotated feature
+// phi(R) = (D/2) hr + 16 mf + 4 jb + c: lane half h of the output tile then
+// holds rotated features (D/2) h + 16 mf + j in acc[mf][j], one whole 64-group
+// (d = 128) or its half (d = 64), with no butterflies and no lane swaps.
+//
+// A fragment (mf, ks) of -H in that row order: lane (row ln, half h) holds
+// -H[phi(32 mf + ln)][16 ks + 8 h + i], i < 8.  The Sylvester entry is
+// (-1)^popcount(phi & f); phi's bits are c (0-1), jb (2-3), mf (4 ..) and hr
+// (bit log2(D/2)), f's are i (0-2), h (3) and ks (4 ..), so the sign splits
+// into a per-lane pattern over i and h (bits 0-3), the factor
+// (-1)^popcount(mf & ks) over the mf bits, and (-1)^(hr & top) for the bit of
+// ks that meets hr (top = bit log2(D/2) - 4 of ks).  Every fragment is thus
+// one of four per-lane register sets: +-G0 (top = 0) and +-G1 = +-(-1)^hr G0.
+struct HadFrags {
+    FragBF16 g0, g1, n0, n1;
+};
+__device__ __forceinline__ HadFrags hadamard_frags(int lane) {
+    const int ln = lane & 31, h = lane >> 5;
+    const uint32_t c = ln & 3, jb = ln >> 3, hr = (ln >> 2) & 1;
+    uint32_t w0[4], w1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t i = 2 * q + p;
+            // the leading 1 is the minus of -H
+            const uint32_t neg = 1u ^ (__builtin_popcount(c & i) & 1u) ^ ((jb & 1u) & (i >> 2)) ^ ((jb >> 1) & (uint32_t)h);
+            v0 |= (0x3F80u | (neg << 15)) << (16 * p);
+            v1 |= (0x3F80u | ((neg ^ hr) << 15)) << (16 * p);
+        }
+        w0[q] = v0;
+        w1[q] = v1;
+    }
+    HadFrags f;
+    f.g0.v = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
+    f.g1.v = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+    f.n0.v = __builtin_bit_cast(bf16x8, make_uint4(w0[0] ^ 0x80008000u, w0[1] ^ 0x80008000u, w0[2] ^ 0x80008000u,
+                                                   w0[3] ^ 0x80008000u));
+    f.n1.v = __builtin_bit_cast(bf16x8, make_uint4(w1[0] ^ 0x80008000u, w1[1] ^ 0x80008000u, w1[2] ^ 0x80008000u,
+                                                   w1[3] ^ 0x80008000u));
+    return f;
+}
+template <int D>
+__device__ __forceinline__ const FragBF16 &hadamard_frag(const HadFrags &f, int mf, int ks) {
+    constexpr int TOPSHIFT = (D == 128 ? 6 : 5) - 4;
+    const bool top = (ks >> TOPSHIFT) & 1;
+    const bool neg = __builtin_popcount(mf & ks & (D / 32 - 1)) & 1;
+    return top ? (neg ? f.n1 : f.g1) : (neg ? f.n0 : f.g0);
+}
+// acc[mf] += -H (s o x) over the D / 16 K steps of the raw x fragments bx,
+// the signs applied here as XOR masks xm[ks] (the `pre` step of the
+// encoder's products; applying them at use keeps the loads of x in flight
+// until then)
+template <int D>
+struct HadPre {
+    static constexpr int NPRE = (D / 32) * (D / 16);
+    const HadFrags &hf;
+    const uint4 *bx;
+    const uint4 *xm;
+    f32x16 *acc;
+    __device__ void operator()() const {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const uint4 m = xm[ks];
+            FragBF16 b;
+            b.v = __builtin_bit_cast(bf16x8, make_uint4(bx[ks].x ^ m.x, bx[ks].y ^ m.y, bx[ks].z ^ m.z, bx[ks].w ^ m.w));
+#pragma unroll
+            for (int mf = 0; mf < D / 32; ++mf) mfma(hadamard_frag<D>(hf, mf, ks), b, acc[mf]);
+        }
+    }
+};
+
 // ------------------------------------------------------------------ quantize, pack, store
 // One lane's share of a 64-group of rotated residual values y: the whole group
 // (d = 128, group h of the row) or half of it (d = 64: elements 32 h ..
@@ -462,12 +603,16 @@ __device__ __forceinline__ void load_codes(const uint8_t *codes, const uint16_t 
 // once, then its NWV waves walk the range's 32-token tiles (wave w: tiles w,
 // w + NWV, ...).  The staging is paid once per range, and the waves, each at
 // its own point of the tile loop, overlap one wave's MFMAs with another's
-// butterflies and packing.
+// quantization and packing.  bf16 caches are encoded in the rotated domain:
+// the tile's products are -H (s o x) (the Hadamard as an MFMA operand) plus
+// the products with W~ rotated beforehand (k_build_wt_rot), so the rotation
+// costs D / 16 MFMA steps per feature block instead of log2(D) butterfly
+// stages and a lane-half exchange; fp32 caches take the plain W~ and the
+// in-register butterflies.
 template <typename T, int D, int BITS, int NWV, bool WL>
 __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch, int tpw) {
     typedef Tile<T, D> TL;
     constexpr int NMF = TL::NMF;
-    constexpr int HALF = NMF / 2;
     constexpr int NE = 16 * NMF;                   // values per lane: 64 (d=128) or 32 (d=64)
     const Block3 blk = xcd_block();
     const CodecItem &it = batch.it[blk.z];
@@ -476,78 +621,82 @@ __global__ __launch_bounds__(64 * NWV) void k_encode(CodecBatch batch, int tpw) 
     const int te = min(it.T, tb + tpw);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 31, h = lane >> 5;
+    constexpr bool BF = sizeof(T) == 2;
+    const float isd = (D == 128) ? -0.08838834764831845f : -0.125f;
+    // bf16: the Hadamard operand fragments (registers) and the sign masks of
+    // the x fragments, xmask[hh][ks] for features 16 ks + 8 hh .. + 7 (LDS, read
+    // per tile as a broadcast within each lane half), the same for every tile
+    __shared__ uint4 xmask[BF ? 2 : 1][BF ? D / 16 : 1];
+    HadFrags hf;
+    if constexpr (BF) {
+        hf = hadamard_frags(lane);
+        if (threadIdx.x < D / 8) xmask[threadIdx.x / (D / 16)][threadIdx.x % (D / 16)] =
+            chunk_sign_mask<T>(it.sign_bits, 2 * (threadIdx.x % (D / 16)) + threadIdx.x / (D / 16));
+        __syncthreads();
+    }
     const WtView<T> wv = wt_view<T, D, NWV, WL>(it, lh);
 
     // one tile loop for 16-byte aligned rows of U~_t and one for the rest,
     // chosen once
+    // bf16: the raw x fragments of the lane's token (features 16 ks + 8 h ..
+    // + 7); an invalid token reads row 0 (its results are not stored)
+    uint4 bx[BF ? D / 16 : 1];
+    auto load_x = [&](int t0) {
+        if constexpr (BF) {
+            const int tok = t0 + ln;
+            const uint8_t *xrow =
+                reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T + (tok < te ? tok : 0)) * TL::RB;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) bx[ks] = *reinterpret_cast<const uint4 *>(xrow + (16 * ks + 8 * h) * 2);
+        }
+    };
+    if (tb + 32 * wave < te) load_x(tb + 32 * wave);
+
     auto tiles = [&](auto vec_tag) {
         constexpr bool VEC = decltype(vec_tag)::value;
         for (int t0 = tb + 32 * wave; t0 < te; t0 += 32 * NWV) {
             const int tok = t0 + ln;
             const bool tv = tok < te;
-            // -(s o x) in the MFMA layout (the lane's features 32 mf + 8 jb + 4 h + c
-            // of its token); an invalid token reads row 0 and stores nothing.  The
-            // X^ products (signs folded into wt) accumulate onto it, leaving -(s o r).
+            // an invalid token reads row 0 and stores nothing
             const uint8_t *xrow =
                 reinterpret_cast<const uint8_t *>(it.x) + ((size_t)lh * it.T + (tv ? tok : 0)) * TL::RB;
             f32x16 acc[NMF];
-    #pragma unroll
-            for (int mf = 0; mf < NMF; ++mf)
-    #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    float xv[4];
-                    get4_signed<T, true>(xrow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, xv);
-    #pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[mf][4 * jb + c] = xv[c];
-                }
-            xhat_mfma_rows<T, NMF, VEC, WL>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt, tok, tv, lane, acc);
-            float r[NMF][16];
-    #pragma unroll
-            for (int mf = 0; mf < NMF; ++mf)
-    #pragma unroll
-                for (int j = 0; j < 16; ++j) r[mf][j] = acc[mf][j];
-
-            // in-register Hadamard stages: feature bits 0, 1, 3, 4 (j bits) and the mf bits
-    #pragma unroll
-            for (int jbit = 1; jbit < 16; jbit <<= 1)
-    #pragma unroll
-                for (int mf = 0; mf < NMF; ++mf)
-    #pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (!(j & jbit)) {
-                            const float a = r[mf][j], b = r[mf][j | jbit];
-                            r[mf][j] = a + b;
-                            r[mf][j | jbit] = a - b;
-                        }
-    #pragma unroll
-            for (int mbit = 1; mbit < NMF; mbit <<= 1)
-    #pragma unroll
-                for (int mf = 0; mf < NMF; ++mf)
-                    if (!(mf & mbit))
-    #pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const float a = r[mf][j], b = r[mf | mbit][j];
-                            r[mf][j] = a + b;
-                            r[mf | mbit][j] = a - b;
-                        }
-
-            // feature bit 2 across lane halves; afterwards the lane half is the top
-            // feature bit and y[e] holds in-group element e (+ 32 h for d = 64).  The
-            // butterflies so far ran on -r; the negative 1/sqrt(d) restores the sign
-            // exactly (negation commutes with every rounding here).
-            const float isd = (D == 128) ? -0.08838834764831845f : -0.125f;
             float y[NE];
+            if constexpr (BF) {
+                // -H (s o x) by MFMA (the Hadamard's +-1 and the bf16 cache values are
+                // exact operands; x came in during the previous tile) while the first
+                // U~_t loads are in flight, then the products with the rotated W~
+                // (+H (s o X^)): -H (s o r) in the lane's group order
+#pragma unroll
+                for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
+                xhat_mfma_rows<T, NMF, VEC, WL>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt,
+                                                tok, tv, lane, acc, HadPre<D>{hf, bx, xmask[h], acc});
+#pragma unroll
+                for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) y[16 * mf + j] = acc[mf][j] * isd;
+                // the next tile's x, in flight during the quantization
+                if (t0 + 32 * NWV < te) load_x(t0 + 32 * NWV);
+            } else {
+                // -(s o x) in the MFMA layout (the lane's features 32 mf + 8 jb + 4 h +
+                // c of its token); the X^ products (signs folded into wt) accumulate
+                // onto it, leaving -(s o r), rotated in registers
     #pragma unroll
-            for (int mp = 0; mp < HALF; ++mp)
+                for (int mf = 0; mf < NMF; ++mf)
     #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    float u = r[mp][j], w = r[mp + HALF][j];
-                    swap_halves(u, w);
-                    const int e = (j & 3) + 8 * (j >> 2) + 32 * mp;
-                    y[e] = (u + w) * isd;
-                    y[e + 4] = (u - w) * isd;
-                }
-
+                    for (int jb = 0; jb < 4; ++jb) {
+                        float xv[4];
+                        get4_signed<T, true>(xrow, it.sign_bits, 32 * mf + 8 * jb + 4 * h, xv);
+    #pragma unroll
+                        for (int c = 0; c < 4; ++c) acc[mf][4 * jb + c] = xv[c];
+                    }
+                xhat_mfma_rows<T, NMF, VEC, WL>(wv.hi, wv.lo, wv.pitch, reinterpret_cast<const T *>(it.ut), it.rt,
+                                                tok, tv, lane, acc);
+                hadamard_tile<NMF>(acc, isd, y);
+            }
+            // y[e] is element e (+ 32 h for d = 64) of the lane's group of r' =
+            // (1/sqrt d) H (s o r): the negative 1/sqrt(d) restores the sign of
+            // -H (s o r) exactly (negation commutes with every rounding here)
             quantize_store<D, BITS>(y, h, tv, (size_t)lh * it.T + tok, it.codes, it.scales);
         }
     };
@@ -720,6 +869,68 @@ __global__ __launch_bounds__(64) void k_build_wt(WtBatch batch, int D) {
     }
 }
 
+// The encoder's W~ for bf16 caches, in the rotated domain and the encoder's
+// row order: row R = 32 mf + 8 jb + 4 hr + c of (l, h)'s block holds
+// sum_f H[phi(R)][f] s_f W~[k][f] (phi(R) = (D/2) hr + 16 mf + 4 jb + c), as
+// bf16 hi and lo planes.  One wave per (l, h) and 32 ranks: the D x 32 block
+// s o W~^T as D/32 MFMA tiles (K = r_f), the Hadamard over its features in
+// registers (fp32), then the hi/lo split and the stores in row order.
+template <int D>
+__global__ __launch_bounds__(64) void k_build_wt_rot(WtBatch batch) {
+    constexpr int NMF = D / 32;
+    const Block3 blk = xcd_block();
+    const WtItem &it = batch.it[blk.z];
+    const int lh = blk.y, k0 = blk.x * 32;
+    if (lh >= it.LH || k0 >= it.rtp) return;
+    const int lane = threadIdx.x, ln = lane & 31, h = lane >> 5;
+    const uint16_t *uf = reinterpret_cast<const uint16_t *>(it.uf);
+    const uint16_t *core = reinterpret_cast<const uint16_t *>(it.core) + (size_t)lh * it.rt * it.rf;
+    const int kr = k0 + ln;
+    const bool kv = kr < it.rt;
+    const uint16_t *cb = core + (size_t)(kv ? kr : 0) * it.rf;
+    f32x16 acc[NMF];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf) acc[mf] = f32x16{};
+    const bool whole = (it.rf & 7) == 0;      // rows of whole, 16-byte aligned fragments
+    for (int j0 = 0; j0 < it.rf; j0 += 16) {
+        const int jj = j0 + 8 * h;
+        const bool in = jj < it.rf;
+        FragBF16 b;
+        if (whole) b = (kv && in) ? load_frag(cb + jj) : zero_frag(uf);
+        else b = kv ? load_frag_n(cb + jj, it.rf - jj) : zero_frag(uf);
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf) {
+            const uint16_t *ua = uf + (size_t)(32 * mf + ln) * it.rf + jj;
+            const FragBF16 a = whole ? (in ? load_frag(ua) : zero_frag(uf)) : load_frag_n(ua, it.rf - jj);
+            mfma(a, b, acc[mf]);
+        }
+    }
+    // s o W~^T: acc[mf][j] of lane half h is feature 32 mf + 8 (j / 4) + 4 h + (j % 4)
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int f = 32 * mf + 8 * (j >> 2) + 4 * h + (j & 3);
+            if ((it.sign_bits[f >> 5] >> (f & 31)) & 1u) acc[mf][j] = -acc[mf][j];
+        }
+    float y[D / 2];
+    hadamard_tile<NMF>(acc, 1.0f, y);
+    if (kr < it.rtp) {
+        uint16_t *wt = reinterpret_cast<uint16_t *>(it.wt) + (size_t)lh * D * it.rtp;
+        const size_t lo_off = (size_t)it.LH * D * it.rtp;
+#pragma unroll
+        for (int e = 0; e < D / 2; ++e) {
+            // rotated feature (D/2) h + e sits in row 32 mf + 8 jb + 4 h + c, e = 16 mf + 4 jb + c
+            const int R = 32 * (e >> 4) + 8 * ((e >> 2) & 3) + 4 * h + (e & 3);
+            const float v = y[e];
+            const uint16_t b = f32_to_bf16(v);
+            const uint16_t bl = f32_to_bf16(v - bf16_to_f32(b));
+            wt[(size_t)R * it.rtp + kr] = b;
+            wt[lo_off + (size_t)R * it.rtp + kr] = bl;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ test-hook kernels
 // One thread per row: plain Hadamard butterflies.
 __global__ void k_rotate_rows(const float *in, float *out, int64_t rows, int d, uint32_t s0, uint32_t s1,
@@ -807,8 +1018,8 @@ struct CodecShape {
     static size_t wt_lds(int maxRtp) {
         return (size_t)(sizeof(T) == 2 ? 2 : 1) * D * (maxRtp + 16 / sizeof(T)) * sizeof(T);
     }
-    // W~ staged in LDS when it fits (the kernels use no other LDS)
-    static bool wl(int maxRtp) { return wt_lds(maxRtp) <= 160 * 1024; }
+    // W~ staged in LDS when it fits beside the encoder's static sign masks
+    static bool wl(int maxRtp) { return wt_lds(maxRtp) + 2 * D / 16 * 16 <= 160 * 1024; }
 };
 
 static dim3 codec_grid(const CodecBatch &b, int maxT, int maxLH, int nw, int &tpw) {
@@ -911,6 +1122,15 @@ hipError_t launch_decode(const CodecBatch &b, int dtype, int D, int bits, int ma
                         : decode_bits<uint16_t, 64>(b, bits, maxT, maxLH, r, s);
     return D == 128 ? decode_bits<float, 128>(b, bits, maxT, maxLH, r, s)
                     : decode_bits<float, 64>(b, bits, maxT, maxLH, r, s);
+}
+hipError_t launch_build_wt_rot(const WtBatch &b, int D, int maxLH, int maxRtp, hipStream_t s) {
+    if (b.n <= 0 || maxRtp <= 0) return hipSuccess;
+    if (D != 64 && D != 128) return hipErrorInvalidValue;
+    KTimeScope kts("k_build_wt", s);
+    dim3 grid((maxRtp + 31) / 32, maxLH, b.n);
+    if (D == 128) hipLaunchKernelGGL(k_build_wt_rot<128>, grid, dim3(64), 0, s, b);
+    else hipLaunchKernelGGL(k_build_wt_rot<64>, grid, dim3(64), 0, s, b);
+    return hipGetLastError();
 }
 hipError_t launch_build_wt(const WtBatch &b, int dtype, int D, int maxLH, int maxRtp, hipStream_t s) {
     if (b.n <= 0 || maxRtp <= 0) return hipSuccess;
