@@ -3,7 +3,13 @@
 Free-running comparison (each side computes its own factors and allocation):
   * factor subspaces: largest principal-angle sine <= 1e-2 for every leading
     block whose eigengap exceeds 1e-3 of the top eigenvalue;
-  * ||X||^2 and the energy table agree to fp32 accuracy on the leading block;
+  * ||X||^2 and the energy table agree to fp32 accuracy: a row of the table
+    belongs to one token eigenvector, and inside a cluster of eigenvalues whose
+    gaps are below that same 1e-3 threshold only the cluster's span is
+    determined (any rounding difference rotates the vectors within it and
+    moves energy between their rows), so such rows are compared through the
+    cluster's sum; a row with gaps above the threshold on both sides is
+    compared on its own;
   * the chosen allocation fits the budget;
   * the GPU reconstruction error <= 1.05 x the oracle's error + 1e-4.
 """
@@ -97,7 +103,9 @@ def _plan_parity(cfg, n_items, mode, rt_max, ratio=None, fixed=None, oversample=
             assert _sine(Uf[:, :r], f.U_f[:, :r]) <= sub_tol, ("feature", r)
         for r in _gap_blocks(f.lam_t):
             assert _sine(Ut[:, :r], f.U_t[:, :r]) <= sub_tol, ("token", r)
-        assert np.max(np.abs(E - f.E)) <= 1e-3 * f.E.max()
+        bounds = [0] + _gap_blocks(f.lam_t[:rt_max]) + [rt_max]
+        for lo, hi in zip(bounds[:-1], bounds[1:]):
+            assert np.max(np.abs(E[lo:hi].sum(0) - f.E[lo:hi].sum(0))) <= 1e-3 * f.E.max(), ("energy rows", lo, hi)
     if not codec:
         J.close()
         return allocs, ref
