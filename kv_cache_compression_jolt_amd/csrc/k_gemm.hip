@@ -204,18 +204,29 @@ __global__ __launch_bounds__(256) void k_gemm128(GemmBatch batch, int maxSplit) 
 // chunks of 64 (P rows, zero past k and len; the next chunk is loaded into
 // registers meanwhile); wave w owns upper tiles (tm <= tn) w, w + 8, w + 16 of
 // the 32 x 32 tile grid, whose MFMA operands are both rows of the staged chunk.
-constexpr int kSgKC = 64, kSgPitch = kSgKC + 1;
+//
+// The products run on the bf16 MFMA: each staged value y is split once into
+// hi = bf16(y) and lo = bf16(y - hi) (|y - hi - lo| <= 2^-18 |y|), and a tile
+// accumulates hi_a hi_b + hi_a lo_b + lo_a hi_b (each product exact in fp32;
+// the omitted lo_a lo_b is below 2^-16 of |y_a y_b|), three 32x32x16 MFMAs
+// per 16 columns where fp32 operands take eight 32x32x2 ones at twice the
+// cycles each.  Per product that is about 2^-16 relative, random in sign, so
+// a Gram entry over a few thousand columns is as close to the exact sum as
+// its fp32 accumulation already is.
+constexpr int kSgKC = 64, kSgXP = kSgKC + 8;   // chunk columns; bf16 pitch of a staged row (144 B)
 
 // KMAX: the largest order of the launch (192, or kSymGramWideK: then up to 6
 // tiles per wave).
 template <int KMAX>
 __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
     constexpr int TPW = ((KMAX / 32) * (KMAX / 32 + 1) / 2 + 7) / 8;     // tiles per wave
-    extern __shared__ float ysg[];          // [P][kSgPitch]
+    extern __shared__ __attribute__((aligned(16))) uint8_t sg_lds[];
     const SymGramItem &it = batch.it[blockIdx.y];
     const int sp = blockIdx.x;
     if (sp >= it.nsplit) return;
     const int k = it.k, ntm = (k + 31) >> 5, P = 32 * ntm, ntiles = ntm * (ntm + 1) / 2;
+    uint16_t *yh = reinterpret_cast<uint16_t *>(sg_lds);    // [P][kSgXP] hi planes of the chunk
+    uint16_t *yl = yh + (size_t)P * kSgXP;                  // [P][kSgXP] lo planes
     const int tb = sp * it.chunk, te = min(it.len, tb + it.chunk);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, m32 = lane & 31, kh = lane >> 5;
     int tmv[TPW], tnv[TPW];
@@ -244,16 +255,24 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
             stg[q] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
+    auto split = [](float v, uint32_t &hi, uint32_t &lo) {
+        const uint16_t h = f32_to_bf16(v);
+        hi = h;
+        lo = f32_to_bf16(v - bf16_to_f32(h));
+    };
     auto store = [&]() {
 #pragma unroll
         for (int q = 0; q < kPieces; ++q) {
             const int p = tid + 512 * q;
             if (p < P * (kSgKC / 4)) {
-                float *d = ysg + (p >> 4) * kSgPitch + 4 * (p & 15);
-                d[0] = stg[q].x;
-                d[1] = stg[q].y;
-                d[2] = stg[q].z;
-                d[3] = stg[q].w;
+                uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+                split(stg[q].x, h0, l0);
+                split(stg[q].y, h1, l1);
+                split(stg[q].z, h2, l2);
+                split(stg[q].w, h3, l3);
+                const size_t o = (size_t)(p >> 4) * kSgXP + 4 * (p & 15);
+                *reinterpret_cast<uint2 *>(yh + o) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                *reinterpret_cast<uint2 *>(yl + o) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
             }
         }
     };
@@ -269,18 +288,23 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             if (!tv[u]) continue;
-            const float *ra = ysg + (32 * tmv[u] + m32) * kSgPitch + kh;
-            const float *rb = ysg + (32 * tnv[u] + m32) * kSgPitch + kh;
-#pragma unroll 8
-            for (int k0 = 0; k0 < kSgKC; k0 += 2)
-                acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(ra[k0], rb[k0], acc[u], 0, 0, 0);
+            const size_t ra = (size_t)(32 * tmv[u] + m32) * kSgXP + 8 * kh;
+            const size_t rb = (size_t)(32 * tnv[u] + m32) * kSgXP + 8 * kh;
+#pragma unroll
+            for (int k0 = 0; k0 < kSgKC; k0 += 16) {
+                const FragBF16 ah = load_frag(yh + ra + k0), bh = load_frag(yh + rb + k0);
+                const FragBF16 al = load_frag(yl + ra + k0), bl = load_frag(yl + rb + k0);
+                mfma(ah, bh, acc[u]);
+                mfma(ah, bl, acc[u]);
+                mfma(al, bh, acc[u]);
+            }
         }
     }
     // each tile in place, and off-diagonal tiles mirrored through a 32 x 33
     // LDS transpose per wave, so both stores run along rows of the partial
     float *out = it.part + (size_t)sp * it.kp * it.kp;
     __syncthreads();                            // every wave is done with the staged chunk
-    float *tr = ysg + wid * (32 * 33);
+    float *tr = reinterpret_cast<float *>(sg_lds) + wid * (32 * 33);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         if (!tv[u]) continue;
@@ -306,8 +330,9 @@ hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStr
         if (it.len % 4 || it.ldy % 4 || it.chunk % kSgKC || it.kp < 32 * ((it.k + 31) / 32)) return hipErrorInvalidValue;
     }
     KTimeScope kts("k_sym_gram", s);
-    // the staged chunk, or 8 waves' 32 x 33 transpose tiles, whichever is larger
-    const size_t lds = std::max<size_t>((size_t)32 * ((maxK + 31) / 32) * kSgPitch, 8 * 32 * 33) * sizeof(float);
+    // the staged chunk (hi and lo planes), or 8 waves' 32 x 33 transpose tiles, whichever is larger
+    const size_t lds = std::max<size_t>((size_t)2 * 32 * ((maxK + 31) / 32) * kSgXP * sizeof(uint16_t),
+                                        (size_t)8 * 32 * 33 * sizeof(float));
     if (maxK > kSymGramMaxK) {
         static hipError_t state = hipErrorNotReady;
         if (state == hipErrorNotReady) {
