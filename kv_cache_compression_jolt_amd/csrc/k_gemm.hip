@@ -217,8 +217,8 @@ constexpr int kSgKC = 64, kSgXP = kSgKC + 8;   // chunk columns; bf16 pitch of a
 
 // KMAX: the largest order of the launch (192, or kSymGramWideK: then up to 6
 // tiles per wave).
-template <int KMAX>
-__global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
+template <int KMAX, class B>
+__global__ __launch_bounds__(512) void k_sym_gram(B batch) {
     constexpr int TPW = ((KMAX / 32) * (KMAX / 32 + 1) / 2 + 7) / 8;     // tiles per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t sg_lds[];
     const SymGramItem &it = batch.it[blockIdx.y];
@@ -322,11 +322,14 @@ __global__ __launch_bounds__(512) void k_sym_gram(SymGramBatch batch) {
     }
 }
 
-hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStream_t s) {
-    if (b.n <= 0) return hipSuccess;
+// items: the host copy of the launch's items (checks and sizes); b: what the
+// kernel reads them from (a by-value batch or a device table)
+template <class B>
+static hipError_t sym_gram_go(const SymGramItem *items, int n, const B &b, int maxK, int maxSplit, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
     if (maxK > kSymGramWideK) return hipErrorInvalidValue;
-    for (int i = 0; i < b.n; ++i) {
-        const SymGramItem &it = b.it[i];
+    for (int i = 0; i < n; ++i) {
+        const SymGramItem &it = items[i];
         if (it.len % 4 || it.ldy % 4 || it.chunk % kSgKC || it.kp < 32 * ((it.k + 31) / 32)) return hipErrorInvalidValue;
     }
     KTimeScope kts("k_sym_gram", s);
@@ -334,21 +337,27 @@ hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStr
     const size_t lds = std::max<size_t>((size_t)2 * 32 * ((maxK + 31) / 32) * kSgXP * sizeof(uint16_t),
                                         (size_t)8 * 32 * 33 * sizeof(float));
     if (maxK > kSymGramMaxK) {
-        static hipError_t state = hipErrorNotReady;
+        static hipError_t state = hipErrorNotReady;     // one per instantiation
         if (state == hipErrorNotReady) {
             hipFuncAttributes fa;
-            state = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k_sym_gram<kSymGramWideK>));
+            state = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k_sym_gram<kSymGramWideK, B>));
             if (state == hipSuccess)
-                state = hipFuncSetAttribute(reinterpret_cast<const void *>(k_sym_gram<kSymGramWideK>),
+                state = hipFuncSetAttribute(reinterpret_cast<const void *>(k_sym_gram<kSymGramWideK, B>),
                                             hipFuncAttributeMaxDynamicSharedMemorySize,
                                             160 * 1024 - (int)fa.sharedSizeBytes);
         }
         if (state != hipSuccess) return state;
-        hipLaunchKernelGGL(k_sym_gram<kSymGramWideK>, dim3(maxSplit, b.n), dim3(512), lds, s, b);
+        hipLaunchKernelGGL((k_sym_gram<kSymGramWideK, B>), dim3(maxSplit, n), dim3(512), lds, s, b);
     } else {
-        hipLaunchKernelGGL(k_sym_gram<kSymGramMaxK>, dim3(maxSplit, b.n), dim3(512), lds, s, b);
+        hipLaunchKernelGGL((k_sym_gram<kSymGramMaxK, B>), dim3(maxSplit, n), dim3(512), lds, s, b);
     }
     return hipGetLastError();
+}
+hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStream_t s) {
+    return sym_gram_go(b.it, b.n, b, maxK, maxSplit, s);
+}
+hipError_t launch_sym_gram(const SymGramItem *host, const SymGramTable &dev, int maxK, int maxSplit, hipStream_t s) {
+    return sym_gram_go(host, dev.n, dev, maxK, maxSplit, s);
 }
 
 hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s) {

@@ -44,7 +44,7 @@ struct Bump {
 // token eigensolver, CholeskyQR), in the group scratch after the items'.
 constexpr int kTableItems = kPlanGroup;
 struct Tables {
-    size_t feat, tok, chol;
+    size_t feat, tok, chol, sg;
 };
 inline Tables reserve_tables(Bump &b) {
     const size_t bytes = (size_t)kTableItems * std::max(sizeof(JacItem), sizeof(CholItem));
@@ -52,6 +52,7 @@ inline Tables reserve_tables(Bump &b) {
     t.feat = b.take(bytes);
     t.tok = b.take(bytes);
     t.chol = b.take(bytes);
+    t.sg = b.take((size_t)kTableItems * sizeof(SymGramItem));
     return t;
 }
 
@@ -82,6 +83,16 @@ int token_eig_n(const jolt_config &cfg, const Dims &D) {
 
 int clampi(int v, int lo, int hi) { return std::max(lo, std::min(hi, v)); }
 
+// Splits of the symmetric Grams over whole 64-column chunks, at most cap.
+void set_gram_splits(Dims &D, int cap) {
+    D.gT_split = clampi(D.T / 64, 1, cap);
+    D.gT_chunk = round_up((D.T + D.gT_split - 1) / D.gT_split, 64);
+    D.gT_split = (D.T + D.gT_chunk - 1) / D.gT_chunk;
+    D.gN_split = clampi(D.n / 64, 1, cap);
+    D.gN_chunk = round_up((D.n + D.gN_split - 1) / D.gN_split, 64);
+    D.gN_split = (D.n + D.gN_chunk - 1) / D.gN_chunk;
+}
+
 Dims dims_for(const jolt_config &cfg, const jolt_item &it, int rt_max, int rf_max) {
     Dims D;
     D.L = it.L; D.H = it.H; D.T = it.T; D.d = it.d;
@@ -103,12 +114,7 @@ Dims dims_for(const jolt_config &cfg, const jolt_item &it, int rt_max, int rf_ma
     D.gf_P = (int)((rows + D.gf_chunk - 1) / D.gf_chunk);
     // symmetric Grams of k-row panels: up to 16 splits of whole 64-column chunks
     // (16 items x 16 splits fill the CUs)
-    D.gT_split = clampi(D.T / 64, 1, 16);
-    D.gT_chunk = round_up((D.T + D.gT_split - 1) / D.gT_split, 64);
-    D.gT_split = (D.T + D.gT_chunk - 1) / D.gT_chunk;
-    D.gN_split = clampi(D.n / 64, 1, 16);
-    D.gN_chunk = round_up((D.n + D.gN_split - 1) / D.gN_split, 64);
-    D.gN_split = (D.n + D.gN_chunk - 1) / D.gN_chunk;
+    set_gram_splits(D, 16);
     // about one workgroup per CU: ceil(T / 256) token tiles per item, 16 items per launch
     D.xm_split = clampi(256 / std::max(1, ((D.T + 255) / 256) * kMaxBatch), 1, 8);
     D.xm_split = std::min(D.xm_split, D.LH);
@@ -515,10 +521,33 @@ hipError_t sliced(int n, Fill &&fill, Go &&go) {
 // With hi (and lo) given, the last pass also writes bf16 copies of the result
 // when the L^-1 apply runs (k <= kCholWideMaxK); *bf reports whether it did.
 // table: device memory for the Cholesky item table (kTableItems items).
+// Symmetric Grams of the k-row panels g[i].y: by-value launches of kMaxBatch
+// items, or, given a device table (groups of more items), one launch for all
+// of them (the table written first when put).
+hipError_t sym_grams(const Ctx &c, const std::vector<SymGramItem> &g, SymGramItem *tab, bool put) {
+    int maxK = 0, maxS = 0;
+    for (const SymGramItem &i : g) {
+        maxK = std::max(maxK, i.k);
+        maxS = std::max(maxS, i.nsplit);
+    }
+    const int nb = (int)g.size();
+    if (tab && maxK <= kSymGramWideK) {
+        if (put)
+            if (hipError_t e = launch_put_table(g.data(), g.size() * sizeof(SymGramItem), tab, c.st); e != hipSuccess)
+                return e;
+        return launch_sym_gram(g.data(), SymGramTable{tab, nb}, maxK, maxS, c.st);
+    }
+    return sliced<SymGramBatch, kMaxBatch>(
+        nb, [&](SymGramBatch &b, int i) { b.it[b.n++] = g[i]; },
+        [&](const SymGramBatch &b) { return panel_grams(b, maxK, maxS, c.st); });
+}
+
+// direct: an item whose Gram is a single launch-table split goes straight to
+// gram (no partials, no reduction)
 jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpart, float **lmat, float **csq,
                       const int *k, const int *kp, const int *len, const int *split, const int *chunk, int passes,
                       CholItem *table, uint16_t *const *hi = nullptr, uint16_t *const *lo = nullptr,
-                      bool *bf = nullptr) {
+                      bool *bf = nullptr, SymGramItem *sg_tab = nullptr) {
     if (bf) *bf = false;
     std::vector<CholItem> chol;
     int maxK = 0, maxLen = 0, maxS = 0;
@@ -529,20 +558,21 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
         maxS = std::max(maxS, split[i]);
         maxCount = std::max<int64_t>(maxCount, (int64_t)kp[i] * kp[i]);
     }
+    std::vector<SymGramItem> gi(nb);
+    std::vector<char> direct(nb);
+    for (int i = 0; i < nb; ++i) {
+        direct[i] = sg_tab && split[i] == 1 && maxK <= kSymGramWideK;
+        SymGramItem &g = gi[i];
+        g.y = y[i]; g.part = direct[i] ? gram[i] : gpart[i]; g.k = k[i]; g.kp = kp[i]; g.len = len[i];
+        g.ldy = len[i]; g.chunk = chunk[i]; g.nsplit = split[i];
+    }
     for (int pass = 0; pass < passes; ++pass) {
         const bool last = pass + 1 == passes;
-        HIPCHK((sliced<SymGramBatch, kMaxBatch>(
-                   nb,
-                   [&](SymGramBatch &b, int i) {
-                       SymGramItem &g = b.it[b.n++];
-                       g.y = y[i]; g.part = gpart[i]; g.k = k[i]; g.kp = kp[i]; g.len = len[i]; g.ldy = len[i];
-                       g.chunk = chunk[i]; g.nsplit = split[i];
-                   },
-                   [&](const SymGramBatch &b) { return panel_grams(b, maxK, maxS, c.st); })),
-               "orth gram");
+        HIPCHK(sym_grams(c, gi, sg_tab, pass == 0), "orth gram");
         HIPCHK((sliced<ReduceBatch, kMaxBatch>(
                    nb,
                    [&](ReduceBatch &b, int i) {
+                       if (direct[i]) return;
                        ReduceItem &r = b.it[b.n++];
                        r.part = gpart[i]; r.out = gram[i]; r.stride = (int64_t)kp[i] * kp[i];
                        r.count = (int64_t)kp[i] * kp[i]; r.nsplit = split[i];
@@ -611,8 +641,14 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     std::vector<Dims> D(nb);
     std::vector<Scratch> S(nb);
     Bump sb;
+    // symmetric Grams: a group of more items than one by-value launch holds
+    // launches all of them at once from a device table, split over columns only
+    // as far as needed to fill the CUs (not at all from 256 items on: no
+    // partial Grams and no reduction pass)
+    const bool sg_tab = nb > kMaxBatch;
     for (int i = 0; i < nb; ++i) {
         D[i] = dims_for(cfg, items[i0 + i], pl.rt_max, pl.rf_max);
+        if (sg_tab) set_gram_splits(D[i], clampi((256 + nb - 1) / nb, 1, 16));
         reserve_scratch(cfg, D[i], sb, S[i]);
     }
     const Tables tabs = reserve_tables(sb);
@@ -620,6 +656,7 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
     JacItem *tab_feat = reinterpret_cast<JacItem *>(scr + tabs.feat);
     JacItem *tab_tok = reinterpret_cast<JacItem *>(scr + tabs.tok);
     CholItem *tab_chol = reinterpret_cast<CholItem *>(scr + tabs.chol);
+    SymGramItem *tab_sg = sg_tab ? reinterpret_cast<SymGramItem *>(scr + tabs.sg) : nullptr;
     HIPCHK(launch_zero(ws + pl.item[i0].grid, pl.readback_stride * nb, c.st), "zero readback");
     auto P = [&](size_t off) { return scr + off; };
     auto F = [&](size_t off) { return reinterpret_cast<float *>(scr + off); };
@@ -807,21 +844,21 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
         if ((s = xm(true))) return s;                                                        // Y = A Omega
         if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
                            kpp.data(), lenT.data(), sT.data(), cT.data(), cfg.power_iters > 0 ? 1 : 2, tab_chol, qh_out,
-                           (bf && cfg.power_iters == 0) ? qlv.data() : nullptr, &conv)))
+                           (bf && cfg.power_iters == 0) ? qlv.data() : nullptr, &conv, tab_sg)))
             return s;
         for (int q = 0; q < cfg.power_iters; ++q) {
             if (!conv && (s = to_bf(true, false))) return s;
             if ((s = xtq(false))) return s;                                                 // Z = A^T Q
             if ((s = orth_rows(c, nb, zv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
                                kpp.data(), lenN.data(), sN.data(), cN.data(), 1, tab_chol, bf ? zbv.data() : nullptr, nullptr,
-                               &conv)))
+                               &conv, tab_sg)))
                 return s;
             if (!conv && (s = to_bf(false, false))) return s;
             if ((s = xm(false))) return s;                                                  // Y = A Z
             const bool last = q + 1 == cfg.power_iters;
             if ((s = orth_rows(c, nb, yv.data(), gram.data(), gpart.data(), lmat.data(), csq.data(), kk.data(),
                                kpp.data(), lenT.data(), sT.data(), cT.data(), last ? 2 : 1, tab_chol, qh_out,
-                               (bf && last) ? qlv.data() : nullptr, &conv)))
+                               (bf && last) ? qlv.data() : nullptr, &conv, tab_sg)))
                 return s;
         }
         if (!conv && (s = to_bf(true, true))) return s;
@@ -835,18 +872,19 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                 maxS = std::max(maxS, D[i].gN_split);
                 maxCount = std::max<int64_t>(maxCount, (int64_t)D[i].kp * D[i].kp);
             }
-            HIPCHK((sliced<SymGramBatch, kMaxBatch>(
-                       nb,
-                       [&](SymGramBatch &b, int i) {
-                           SymGramItem &g = b.it[b.n++];
-                           g.y = zv[i]; g.part = gpart[i]; g.k = D[i].k; g.kp = D[i].kp; g.len = D[i].n;
-                           g.ldy = D[i].n; g.chunk = D[i].gN_chunk; g.nsplit = D[i].gN_split;
-                       },
-                       [&](const SymGramBatch &b) { return panel_grams(b, maxK, maxS, c.st); })),
-                   "B B^T");
+            std::vector<SymGramItem> gw(nb);
+            std::vector<char> direct(nb);
+            for (int i = 0; i < nb; ++i) {
+                direct[i] = tab_sg && D[i].gN_split == 1 && maxK <= kSymGramWideK;
+                SymGramItem &g = gw[i];
+                g.y = zv[i]; g.part = direct[i] ? F(S[i].wmat) : gpart[i]; g.k = D[i].k; g.kp = D[i].kp;
+                g.len = D[i].n; g.ldy = D[i].n; g.chunk = D[i].gN_chunk; g.nsplit = D[i].gN_split;
+            }
+            HIPCHK(sym_grams(c, gw, tab_sg, true), "B B^T");
             HIPCHK((sliced<ReduceBatch, kMaxBatch>(
                        nb,
                        [&](ReduceBatch &b, int i) {
+                           if (direct[i]) return;
                            ReduceItem &r = b.it[b.n++];
                            r.part = gpart[i]; r.out = F(S[i].wmat); r.stride = (int64_t)D[i].kp * D[i].kp;
                            r.count = r.stride; r.nsplit = D[i].gN_split;

@@ -156,6 +156,9 @@ template <typename Item> struct DevTable {
 };
 typedef DevTable<JacItem> JacTable;
 typedef DevTable<CholItem> CholTable;
+typedef DevTable<SymGramItem> SymGramTable;
+// every item of a plan group in one launch
+hipError_t launch_sym_gram(const SymGramItem *host, const SymGramTable &dev, int maxK, int maxSplit, hipStream_t s);
 hipError_t launch_eig_tridiag(const JacItem *host, const JacTable &dev, int maxN, hipStream_t s);
 hipError_t launch_jacobi_lds(const JacItem *host, const JacTable &dev, int maxN, int max_sweeps, hipStream_t s,
                              int retry_only = 0);
