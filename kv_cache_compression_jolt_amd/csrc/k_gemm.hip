@@ -199,6 +199,120 @@ __global__ __launch_bounds__(256) void k_gemm128(GemmBatch batch, int maxSplit) 
     }
 }
 
+// ---------------------------------------------------------------- split-operand GEMM
+// C = A B as k_gemm128 (128 x 128 tiles, 4 waves of 2 x 2 MFMA tiles, slices of
+// kKS), on the bf16 MFMA: every operand value v is split into hi = bf16(v) and
+// lo = bf16(v - hi) on its way into LDS, and a tile accumulates hi_a hi_b +
+// hi_a lo_b + lo_a hi_b (exact products, fp32 accumulation; the omitted lo lo
+// and the split are below 2^-16 of |a b|).  Each operand must have unit stride
+// along its row index or along K; a thread then loads two runs of 8
+// consecutive K of one row and writes each plane of a run as one 16-byte row
+// piece of the K-contiguous LDS tile.
+__global__ __launch_bounds__(256) void k_gemm128_bx3(GemmBatch batch, int maxSplit) {
+    constexpr int XP = kKS + 8;                       // bf16 pitch of a tile row (80 B)
+    __shared__ __attribute__((aligned(16))) uint16_t Ah[kBT * XP], Al[kBT * XP], Bh[kBT * XP], Bl[kBT * XP];
+    const int z = blockIdx.z;
+    const GemmItem &it0 = batch.it[z % batch.n];
+    const int sp = (z / batch.n) % maxSplit, bi = (z / batch.n) / maxSplit;
+    const int i0 = blockIdx.y * kBT, j0 = blockIdx.x * kBT;
+    if (sp >= it0.nsplit || bi >= it0.nb || i0 >= it0.M || j0 >= it0.N) return;
+    const float *A = it0.a + bi * it0.a_z;
+    const float *B = it0.b + bi * it0.b_z;
+    float *C = it0.c + bi * it0.c_z + (int64_t)sp * it0.c_split;
+    const int M = it0.M, N = it0.N;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid >> 1, wn = wid & 1, kh = lane >> 5, l32 = lane & 31;
+    const int kb = sp * it0.kchunk, ke = min(it0.K, kb + it0.kchunk);
+    // run u of this thread: row and first K in the slice
+    auto run_of = [&](bool kfast, int u, int &r, int &kk) {
+        if (kfast) { r = (tid >> 2) + 64 * u; kk = 8 * (tid & 3); }      // 4 lanes per 32 K of a row
+        else { r = tid & 127; kk = 16 * (tid >> 7) + 8 * u; }            // lanes along the rows
+    };
+    const bool akf = it0.a_k == 1, bkf = it0.b_k == 1;
+    float va[16], vb[16];
+    auto load_op = [&](const float *X, int64_t s_r, int64_t s_k, bool kf, int r0, int R, int k0, float *v) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            int r, kk;
+            run_of(kf, u, r, kk);
+            const int gr = r0 + r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int gk = k0 + kk + e;
+                const bool ok = gr < R && gk < ke;
+                const float x = *(ok ? X + (int64_t)gr * s_r + (int64_t)gk * s_k : X);
+                v[8 * u + e] = ok ? x : 0.f;
+            }
+        }
+    };
+    auto store_op = [&](const float *v, uint16_t *H, uint16_t *L, bool kf) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            int r, kk;
+            run_of(kf, u, r, kk);
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint16_t h0 = f32_to_bf16(v[8 * u + 2 * p]), h1 = f32_to_bf16(v[8 * u + 2 * p + 1]);
+                const uint16_t l0 = f32_to_bf16(v[8 * u + 2 * p] - bf16_to_f32(h0));
+                const uint16_t l1 = f32_to_bf16(v[8 * u + 2 * p + 1] - bf16_to_f32(h1));
+                h[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                l[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            *reinterpret_cast<uint4 *>(H + r * XP + kk) = make_uint4(h[0], h[1], h[2], h[3]);
+            *reinterpret_cast<uint4 *>(L + r * XP + kk) = make_uint4(l[0], l[1], l[2], l[3]);
+        }
+    };
+    auto load = [&](int k0) {
+        load_op(A, it0.a_i, it0.a_k, akf, i0, M, k0, va);
+        load_op(B, it0.b_j, it0.b_k, bkf, j0, N, k0, vb);
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn) acc[tm][tn] = f32x16{};
+    load(kb);
+    for (int k0 = kb; k0 < ke; k0 += kKS) {
+        __syncthreads();
+        store_op(va, Ah, Al, akf);
+        store_op(vb, Bh, Bl, bkf);
+        __syncthreads();
+        if (k0 + kKS < ke) load(k0 + kKS);
+#pragma unroll
+        for (int ks = 0; ks < kKS / 16; ++ks) {
+            FragBF16 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ra = (64 * wm + 32 * t + l32) * XP + 16 * ks + 8 * kh;
+                const int rb = (64 * wn + 32 * t + l32) * XP + 16 * ks + 8 * kh;
+                ah[t] = load_frag(Ah + ra); al[t] = load_frag(Al + ra);
+                bh[t] = load_frag(Bh + rb); bl[t] = load_frag(Bl + rb);
+            }
+#pragma unroll
+            for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) {
+                    mfma(ah[tm], bh[tn], acc[tm][tn]);
+                    mfma(ah[tm], bl[tn], acc[tm][tn]);
+                    mfma(al[tm], bh[tn], acc[tm][tn]);
+                }
+        }
+    }
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+        const int gj = j0 + 64 * wn + 32 * tn + l32;
+        if (gj >= N) continue;
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const int gi = i0 + 64 * wm + 32 * tm + frag_row(lane, jj);
+                if (gi < M) C[(int64_t)gi * it0.c_i + (int64_t)gj * it0.c_j] = acc[tm][tn][jj];
+            }
+    }
+}
+
 // ---------------------------------------------------------------- symmetric Gram
 // WG (8 waves) per (split, item): the split's columns of Y go through LDS in
 // chunks of 64 (P rows, zero past k and len; the next chunk is loaded into
@@ -358,6 +472,19 @@ hipError_t launch_sym_gram(const SymGramBatch &b, int maxK, int maxSplit, hipStr
 }
 hipError_t launch_sym_gram(const SymGramItem *host, const SymGramTable &dev, int maxK, int maxSplit, hipStream_t s) {
     return sym_gram_go(host, dev.n, dev, maxK, maxSplit, s);
+}
+
+hipError_t launch_gemm_split(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s) {
+    if (b.n <= 0) return hipSuccess;
+    for (int i = 0; i < b.n; ++i) {
+        const GemmItem &g = b.it[i];
+        if ((g.a_i != 1 && g.a_k != 1) || (g.b_j != 1 && g.b_k != 1))
+            return launch_gemm(b, maxM, maxN, maxSplit, maxNb, s);     // operands of other strides: fp32
+    }
+    KTimeScope kts("k_gemm", s);
+    dim3 g((maxN + kBT - 1) / kBT, (maxM + kBT - 1) / kBT, b.n * maxSplit * maxNb);
+    hipLaunchKernelGGL(k_gemm128_bx3, g, dim3(256), 0, s, b, maxSplit);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s) {

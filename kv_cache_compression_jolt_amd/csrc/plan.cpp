@@ -916,7 +916,7 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                            g.c_split = 0; g.a_z = g.b_z = g.c_z = 0;
                            g.M = pl.rt_max; g.N = D[i].T; g.K = D[i].k; g.kchunk = D[i].k; g.nsplit = 1; g.nb = 1;
                        },
-                       [&](const GemmBatch &b) { return launch_gemm(b, pl.rt_max, maxN, 1, 1, c.st); })),
+                       [&](const GemmBatch &b) { return launch_gemm_split(b, pl.rt_max, maxN, 1, 1, c.st); })),
                    "U_t");
             HIPCHK((sliced<GemmBatch, kMaxBatch>(
                        nb,
@@ -927,7 +927,7 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                            q.c_split = 0; q.a_z = q.b_z = q.c_z = 0;
                            q.M = pl.rt_max; q.N = D[i].n; q.K = D[i].k; q.kchunk = D[i].k; q.nsplit = 1; q.nb = 1;
                        },
-                       [&](const GemmBatch &b) { return launch_gemm(b, pl.rt_max, maxNn, 1, 1, c.st); })),
+                       [&](const GemmBatch &b) { return launch_gemm_split(b, pl.rt_max, maxNn, 1, 1, c.st); })),
                    "P");
         }
     } else {
@@ -1015,7 +1015,7 @@ jolt_status run_group_body(const Ctx &c, const jolt_config &cfg, const PlanLayou
                        g.a_z = d; g.b_z = 0; g.c_z = (int64_t)pl.rt_max * d;
                        g.M = pl.rt_max; g.N = d; g.K = d; g.kchunk = d; g.nsplit = 1; g.nb = D[i].LH;
                    },
-                   [&](const GemmBatch &b) { return launch_gemm(b, pl.rt_max, d, 1, maxNb, c.st); })),
+                   [&](const GemmBatch &b) { return launch_gemm_split(b, pl.rt_max, d, 1, maxNb, c.st); })),
                "core");
         HIPCHK((sliced<SmallBatch, kMaxBatch>(
                    nb,

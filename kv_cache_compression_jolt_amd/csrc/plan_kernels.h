@@ -54,6 +54,11 @@ struct GemmItem {
 };
 struct GemmBatch { GemmItem it[kMaxBatch]; int n; };
 hipError_t launch_gemm(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s);
+// The same product on the bf16 MFMA with both operands split into hi + lo
+// planes (about 2^-16 relative per product), for products whose operands are
+// well conditioned; operands need unit stride along their row index or K
+// (others go to launch_gemm).
+hipError_t launch_gemm_split(const GemmBatch &b, int maxM, int maxN, int maxSplit, int maxNb, hipStream_t s);
 
 // Symmetric Gram of the rows of Y (k x len, row stride ldy): part[s][r][c] = sum
 // over the columns t of split s (chunk columns each) of y[r][t] y[c][t], for
