@@ -40,7 +40,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA bf16; fp32 (MFMA and vector)
+# dense MFMA bf16; fp32 (MFMA and vector); "bf16x3": fp32-accurate products formed
+# from three bf16 MFMA products of hi/lo-split operands (hi hi + hi lo + lo hi),
+# whose fp32-equivalent roof is a third of the bf16 peak
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3, "bf16x3": 2500.0 / 3}
 
 KERNELS = ["k_eig_tridiag", "k_eig_trivec", "k_eig_backtr", "k_eig_polish", "k_chol_inv", "k_apply_linv",
            "k_sym_gram", "k_gemm", "k_reduce", "k_xm", "k_xtq", "k_gram_rows", "k_build_wt", "k_encode",
@@ -71,7 +74,8 @@ def parse():
 def work_per_step(cfg, jitems, allocs, mode="randomized"):
     """Algorithmic work of each kernel over one step: {kernel: (bytes, flops,
     flop unit)}; bytes are HBM bytes read + written once, flops those of the
-    kernel's arithmetic unit ("bf16" MFMA or "fp32")."""
+    kernel's arithmetic unit ("bf16" MFMA, "bf16x3" for fp32-accurate products
+    of split operands on the bf16 MFMA, or "fp32")."""
     k = cfg.rt_max + cfg.oversample
     q = cfg.power_iters
     out = {}
@@ -88,12 +92,12 @@ def work_per_step(cfg, jitems, allocs, mode="randomized"):
         # CholeskyQR Grams and B B^T (symmetric: k (k + 1) len flops each) and the
         # L^-1 applies: T-long panels q + 2 times, n-long panels q (+1 for B B^T)
         out["k_sym_gram"] = (0, sum(k * (k + 1) * ((q + 2) * it.T + (q + 1) * n) for n, it in zip(n_lhd, jitems)),
-                             "fp32")
+                             "bf16x3")
         out["k_apply_linv"] = (sum(4 * k * ((q + 2) * it.T + q * n) * 2 for n, it in zip(n_lhd, jitems)),
                                sum(k * (k + 1) * ((q + 2) * it.T + q * n) for n, it in zip(n_lhd, jitems)), "fp32")
         out["k_chol_inv"] = (0, sum((2 * q + 2) * (2.0 / 3) * k ** 3 for _ in jitems), "fp32")
         out["k_gemm"] = (0, sum(2.0 * cfg.rt_max * k * (it.T + n) + 2.0 * cfg.rt_max * n * it.d
-                                for n, it in zip(n_lhd, jitems)), "fp32")
+                                for n, it in zip(n_lhd, jitems)), "bf16x3")
         ne = k
     else:
         ne = jitems[0].T
@@ -129,7 +133,7 @@ def roof(bytes_, flops, unit, ms):
     if t_hbm >= t_fl:
         return {"bound": "hbm", "achieved": bytes_ / s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": t_hbm / s}
-    bound = "mfma" if unit == "bf16" else "alu"
+    bound = "mfma" if unit in ("bf16", "bf16x3") else "alu"
     return {"bound": bound, "achieved": flops / s / 1e12, "peak": PEAK_TFLOPS[unit], "unit": "TFLOP/s",
             "precision": unit, "frac": t_fl / s}
 

@@ -36,7 +36,7 @@ COPY_BYTES = 512 * 1024 * 1024
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = {"k_eig_tridiag": "k_eig.hip", "k_eig_trivec": "k_eig.hip", "k_eig_backtr": "k_eig.hip", "k_eig_polish": "k_eig.hip",
            "k_eig_tridiag_w": "k_eig.hip", "k_eig_backtr_w": "k_eig.hip", "k_eig_polish_w": "k_eig.hip", "k_chol_inv": "k_orth.hip", "k_apply_linv": "k_orth.hip",
-           "k_gemm": "k_gemm.hip", "k_gemm128": "k_gemm.hip", "k_sym_gram": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
+           "k_gemm": "k_gemm.hip", "k_gemm128": "k_gemm.hip", "k_gemm128_bx3": "k_gemm.hip", "k_sym_gram": "k_gemm.hip", "k_xm": "k_plan.hip", "k_xtq": "k_plan.hip", "k_gram_rows": "k_plan.hip",
            "k_encode": "k_codec.hip", "k_decode": "k_codec.hip", "k_build_wt": "k_codec.hip"}
 
 
