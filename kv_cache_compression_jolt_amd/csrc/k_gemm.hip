@@ -199,6 +199,20 @@ __global__ __launch_bounds__(256) void k_gemm128(GemmBatch batch, int maxSplit) 
     }
 }
 
+// ---------------------------------------------------------------- hi/lo split
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two values split into bf16 hi = RNE(v) and lo = RNE(v - hi), packed in pairs
+// (element 0 in the low half): the hardware's paired conversion, which rounds
+// to nearest even as f32_to_bf16 does for finite values.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    const f32x2 f = {a, b};
+    const bf16x2 h = __builtin_convertvector(f, bf16x2);
+    const bf16x2 l = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // ---------------------------------------------------------------- split-operand GEMM
 // C = A B as k_gemm128 (128 x 128 tiles, 4 waves of 2 x 2 MFMA tiles, slices of
 // kKS), on the bf16 MFMA: every operand value v is split into hi = bf16(v) and
@@ -252,13 +266,7 @@ __global__ __launch_bounds__(256) void k_gemm128_bx3(GemmBatch batch, int maxSpl
             run_of(kf, u, r, kk);
             uint32_t h[4], l[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint16_t h0 = f32_to_bf16(v[8 * u + 2 * p]), h1 = f32_to_bf16(v[8 * u + 2 * p + 1]);
-                const uint16_t l0 = f32_to_bf16(v[8 * u + 2 * p] - bf16_to_f32(h0));
-                const uint16_t l1 = f32_to_bf16(v[8 * u + 2 * p + 1] - bf16_to_f32(h1));
-                h[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                l[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-            }
+            for (int p = 0; p < 4; ++p) split_bf16x2(v[8 * u + 2 * p], v[8 * u + 2 * p + 1], h[p], l[p]);
             *reinterpret_cast<uint4 *>(H + r * XP + kk) = make_uint4(h[0], h[1], h[2], h[3]);
             *reinterpret_cast<uint4 *>(L + r * XP + kk) = make_uint4(l[0], l[1], l[2], l[3]);
         }
@@ -369,24 +377,17 @@ __global__ __launch_bounds__(512) void k_sym_gram(B batch) {
             stg[q] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
-    auto split = [](float v, uint32_t &hi, uint32_t &lo) {
-        const uint16_t h = f32_to_bf16(v);
-        hi = h;
-        lo = f32_to_bf16(v - bf16_to_f32(h));
-    };
     auto store = [&]() {
 #pragma unroll
         for (int q = 0; q < kPieces; ++q) {
             const int p = tid + 512 * q;
             if (p < P * (kSgKC / 4)) {
-                uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-                split(stg[q].x, h0, l0);
-                split(stg[q].y, h1, l1);
-                split(stg[q].z, h2, l2);
-                split(stg[q].w, h3, l3);
+                uint32_t h01, h23, l01, l23;
+                split_bf16x2(stg[q].x, stg[q].y, h01, l01);
+                split_bf16x2(stg[q].z, stg[q].w, h23, l23);
                 const size_t o = (size_t)(p >> 4) * kSgXP + 4 * (p & 15);
-                *reinterpret_cast<uint2 *>(yh + o) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-                *reinterpret_cast<uint2 *>(yl + o) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+                *reinterpret_cast<uint2 *>(yh + o) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2 *>(yl + o) = make_uint2(l01, l23);
             }
         }
     };
