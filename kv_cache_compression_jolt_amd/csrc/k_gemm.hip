@@ -219,9 +219,7 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uin
 // lo = bf16(v - hi) on its way into LDS, and a tile accumulates hi_a hi_b +
 // hi_a lo_b + lo_a hi_b (exact products, fp32 accumulation; the omitted lo lo
 // and the split are below 2^-16 of |a b|).  Each operand must have unit stride
-// along its row index or along K; a thread then loads two runs of 8
-// consecutive K of one row and writes each plane of a run as one 16-byte row
-// piece of the K-contiguous LDS tile.
+// along its row index or along K; its values go to K-contiguous LDS rows.
 __global__ __launch_bounds__(256) void k_gemm128_bx3(GemmBatch batch, int maxSplit) {
     constexpr int XP = kKS + 8;                       // bf16 pitch of a tile row (80 B)
     __shared__ __attribute__((aligned(16))) uint16_t Ah[kBT * XP], Al[kBT * XP], Bh[kBT * XP], Bl[kBT * XP];
@@ -237,38 +235,74 @@ __global__ __launch_bounds__(256) void k_gemm128_bx3(GemmBatch batch, int maxSpl
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1, kh = lane >> 5, l32 = lane & 31;
     const int kb = sp * it0.kchunk, ke = min(it0.K, kb + it0.kchunk);
-    // run u of this thread: row and first K in the slice
-    auto run_of = [&](bool kfast, int u, int &r, int &kk) {
-        if (kfast) { r = (tid >> 2) + 64 * u; kk = 8 * (tid & 3); }      // 4 lanes per 32 K of a row
-        else { r = tid & 127; kk = 16 * (tid >> 7) + 8 * u; }            // lanes along the rows
-    };
+    // An operand with unit stride along K: a thread takes two runs of 8
+    // consecutive K of one row (4 lanes per 32 K of a row), each loaded as two
+    // 16-byte loads where whole and aligned.  Unit stride along its rows: a
+    // thread takes 4 consecutive rows x 4 consecutive K (rows 4 (tid % 32) ..,
+    // K 4 (tid / 32) ..), one 16-byte load per K.  Either way the thread
+    // stores 16 values, split into hi and lo, as row pieces of the LDS tiles.
     const bool akf = it0.a_k == 1, bkf = it0.b_k == 1;
     float va[16], vb[16];
     auto load_op = [&](const float *X, int64_t s_r, int64_t s_k, bool kf, int r0, int R, int k0, float *v) {
+        if (kf) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int r, kk;
-            run_of(kf, u, r, kk);
-            const int gr = r0 + r;
+            for (int u = 0; u < 2; ++u) {
+                const int gr = r0 + (tid >> 2) + 64 * u, gk0 = k0 + 8 * (tid & 3);
+                const float *p = X + (int64_t)(gr < R ? gr : 0) * s_r + gk0;
+                if (gr < R && gk0 + 8 <= ke && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+                    const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+                    v[8 * u + 0] = a.x; v[8 * u + 1] = a.y; v[8 * u + 2] = a.z; v[8 * u + 3] = a.w;
+                    v[8 * u + 4] = b.x; v[8 * u + 5] = b.y; v[8 * u + 6] = b.z; v[8 * u + 7] = b.w;
+                } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int gk = k0 + kk + e;
-                const bool ok = gr < R && gk < ke;
-                const float x = *(ok ? X + (int64_t)gr * s_r + (int64_t)gk * s_k : X);
-                v[8 * u + e] = ok ? x : 0.f;
+                    for (int e = 0; e < 8; ++e) {
+                        const bool ok = gr < R && gk0 + e < ke;
+                        const float x = *(ok ? p + e : X);
+                        v[8 * u + e] = ok ? x : 0.f;
+                    }
+                }
+            }
+        } else {
+            const int gr0 = r0 + 4 * (tid & 31), gk0 = k0 + 4 * (tid >> 5);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int gk = gk0 + c;
+                const float *p = X + (int64_t)(gk < ke ? gk : 0) * s_k + gr0;
+                if (gk < ke && gr0 + 4 <= R && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+                    const float4 a = *reinterpret_cast<const float4 *>(p);
+                    v[4 * c + 0] = a.x; v[4 * c + 1] = a.y; v[4 * c + 2] = a.z; v[4 * c + 3] = a.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = gk < ke && gr0 + e < R;
+                        const float x = *(ok ? p + e : X);
+                        v[4 * c + e] = ok ? x : 0.f;
+                    }
+                }
             }
         }
     };
     auto store_op = [&](const float *v, uint16_t *H, uint16_t *L, bool kf) {
+        if (kf) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int r, kk;
-            run_of(kf, u, r, kk);
-            uint32_t h[4], l[4];
+            for (int u = 0; u < 2; ++u) {
+                const int r = (tid >> 2) + 64 * u, kk = 8 * (tid & 3);
+                uint32_t h[4], l[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) split_bf16x2(v[8 * u + 2 * p], v[8 * u + 2 * p + 1], h[p], l[p]);
-            *reinterpret_cast<uint4 *>(H + r * XP + kk) = make_uint4(h[0], h[1], h[2], h[3]);
-            *reinterpret_cast<uint4 *>(L + r * XP + kk) = make_uint4(l[0], l[1], l[2], l[3]);
+                for (int p = 0; p < 4; ++p) split_bf16x2(v[8 * u + 2 * p], v[8 * u + 2 * p + 1], h[p], l[p]);
+                *reinterpret_cast<uint4 *>(H + r * XP + kk) = make_uint4(h[0], h[1], h[2], h[3]);
+                *reinterpret_cast<uint4 *>(L + r * XP + kk) = make_uint4(l[0], l[1], l[2], l[3]);
+            }
+        } else {
+            const int r0l = 4 * (tid & 31), kk = 4 * (tid >> 5);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {             // row r0l + e: K kk .. kk + 3 are v[4 c + e]
+                uint32_t h0, l0, h1, l1;
+                split_bf16x2(v[e], v[4 + e], h0, l0);
+                split_bf16x2(v[8 + e], v[12 + e], h1, l1);
+                *reinterpret_cast<uint2 *>(H + (r0l + e) * XP + kk) = make_uint2(h0, h1);
+                *reinterpret_cast<uint2 *>(L + (r0l + e) * XP + kk) = make_uint2(l0, l1);
+            }
         }
     };
     auto load = [&](int k0) {
