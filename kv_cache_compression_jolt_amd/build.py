@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "plan.cpp", "planner.cpp", "payload.cpp", "ktimer.cpp", "k_codec.hip", "k_plan.hip", "k_eig.hip", "k_orth.hip", "k_gemm.hip",
            "k_attn.hip"]
-HEADERS = ["dev_common.h", "jolt_internal.h", "plan_kernels.h", "planner.h", "payload.h", "api_internal.h", "attn.h"]
+HEADERS = ["bf16_split.h", "dev_common.h", "jolt_internal.h", "plan_kernels.h", "planner.h", "payload.h", "api_internal.h", "attn.h"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

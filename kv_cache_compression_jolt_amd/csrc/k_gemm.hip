@@ -7,6 +7,7 @@
 // loaded into registers while the current one is multiplied.  Operands are
 // addressed by element strides, so transposed views need no copies; loads are
 // coalesced along whichever index has stride 1.
+#include "bf16_split.h"
 #include "dev_common.h"
 #include "plan_kernels.h"
 #include "ktimer.h"
@@ -197,20 +198,6 @@ __global__ __launch_bounds__(256) void k_gemm128(GemmBatch batch, int maxSplit) 
                 if (gi < M) C[(int64_t)gi * it0.c_i + (int64_t)gj * it0.c_j] = acc[tm][tn][jj];
             }
     }
-}
-
-// ---------------------------------------------------------------- hi/lo split
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-// Two values split into bf16 hi = RNE(v) and lo = RNE(v - hi), packed in pairs
-// (element 0 in the low half): the hardware's paired conversion, which rounds
-// to nearest even as f32_to_bf16 does for finite values.
-__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    const f32x2 f = {a, b};
-    const bf16x2 h = __builtin_convertvector(f, bf16x2);
-    const bf16x2 l = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
-    hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // ---------------------------------------------------------------- split-operand GEMM
