@@ -20,7 +20,6 @@
 
 #include <algorithm>
 
-#include "bf16_split.h"
 #include "dev_common.h"
 #include "plan_kernels.h"
 #include "ktimer.h"
@@ -379,66 +378,6 @@ __device__ __forceinline__ void apply_load_x(const TrsmItem &it, int lane, float
     }
 }
 
-// The split form of wave W's rows of X for the bf16 MFMA: the pairs (i, i + 1)
-// of xr (K = 2 i + kh and 2 i + 2 + kh of the lane's row) as bf16 hi and lo
-// words, hi at xw[i / 2] and lo at xw[XR / 2 + i / 2] (bit patterns).
-template <int NTM, int W, int XR>
-__device__ __forceinline__ void apply_split_x(const float *xr, float *xw) {
-    constexpr ApplyDeal<NTM> D{};
-#pragma unroll
-    for (int i = 0; i < D.regs(W); i += 2) {
-        uint32_t h, l;
-        split_bf16x2(xr[i], xr[i + 1], h, l);
-        xw[i / 2] = __uint_as_float(h);
-        xw[XR / 2 + i / 2] = __uint_as_float(l);
-    }
-}
-
-// acc[r] = (rows of wave W's block r) x (the staged block ys) on the bf16 MFMA
-// from split operands (hi hi + hi lo + lo hi).  K step s covers i = 8 s .. 8 s
-// + 7: slot j of a lane holds K = 16 s + 2 j + kh on both operands, the A
-// words from xw and the B values read from ys and split in registers.
-template <int NTM, int W, int MC, int XR>
-__device__ __forceinline__ void apply_mul_split(const float *xw, const float *ys, int lane, f32x16 *acc) {
-    constexpr ApplyDeal<NTM> D{};
-    const int m32 = lane & 31, kh = lane >> 5;
-#pragma unroll
-    for (int r = 0; r < MC; ++r) acc[r] = f32x16{};
-    if constexpr (D.cnt[W] > 0) {
-        constexpr int IMAX = 16 * (D.tm[W][0] + 1);         // the wave's largest block comes first
-#pragma unroll
-        for (int s = 0; s < IMAX / 8; ++s) {
-            uint32_t bh[4], bl[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                split_bf16x2(ys[(16 * s + 4 * q + kh) * kApplyCols + m32], ys[(16 * s + 4 * q + 2 + kh) * kApplyCols + m32],
-                             bh[q], bl[q]);
-            FragBF16 Bh, Bl;
-            Bh.v = __builtin_bit_cast(bf16x8, make_uint4(bh[0], bh[1], bh[2], bh[3]));
-            Bl.v = __builtin_bit_cast(bf16x8, make_uint4(bl[0], bl[1], bl[2], bl[3]));
-            int off = 0;
-#pragma unroll
-            for (int r = 0; r < D.cnt[W]; ++r) {
-                const int n = 16 * (D.tm[W][r] + 1);
-                if (8 * s < n) {
-                    const int a0 = (off + 8 * s) / 2;
-                    FragBF16 Ah, Al;
-                    Ah.v = __builtin_bit_cast(bf16x8, make_uint4(__float_as_uint(xw[a0]), __float_as_uint(xw[a0 + 1]),
-                                                                 __float_as_uint(xw[a0 + 2]), __float_as_uint(xw[a0 + 3])));
-                    Al.v = __builtin_bit_cast(bf16x8, make_uint4(__float_as_uint(xw[XR / 2 + a0]),
-                                                                 __float_as_uint(xw[XR / 2 + a0 + 1]),
-                                                                 __float_as_uint(xw[XR / 2 + a0 + 2]),
-                                                                 __float_as_uint(xw[XR / 2 + a0 + 3])));
-                    mfma(Ah, Bh, acc[r]);
-                    mfma(Ah, Bl, acc[r]);
-                    mfma(Al, Bh, acc[r]);
-                }
-                off += n;
-            }
-        }
-    }
-}
-
 // acc[r] = (rows of wave W's block r) x (the staged block ys)
 template <int NTM, int W, int MC>
 __device__ __forceinline__ void apply_mul(const float *xr, const float *ys, int lane, f32x16 *acc) {
@@ -486,11 +425,7 @@ __device__ __forceinline__ void apply_store(const TrsmItem &it, int lane, int c0
     }
 }
 
-// SPLIT: the products on the bf16 MFMA from split operands (about 2^-16
-// relative per product), for the second pass of CholeskyQR2, whose input is
-// already orthonormal to a few ulp (L^-1 close to the identity: nothing to
-// amplify the split's error).
-template <int NTM, bool SPLIT>
+template <int NTM>
 __global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch) {
     constexpr ApplyDeal<NTM> D{};
     constexpr int P = 32 * NTM, XR = D.max_regs(), MC = D.max_cnt();
@@ -501,12 +436,11 @@ __global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch) {
     if ((int)blockIdx.x >= ncb || it.k > P) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     float xr[XR];
-    float xw[SPLIT ? XR : 1];                  // SPLIT: xr's hi / lo words (xr is dead after the split)
     switch (wave) {
-        case 0: apply_load_x<NTM, 0>(it, lane, xr); if constexpr (SPLIT) apply_split_x<NTM, 0, XR>(xr, xw); break;
-        case 1: apply_load_x<NTM, 1>(it, lane, xr); if constexpr (SPLIT) apply_split_x<NTM, 1, XR>(xr, xw); break;
-        case 2: apply_load_x<NTM, 2>(it, lane, xr); if constexpr (SPLIT) apply_split_x<NTM, 2, XR>(xr, xw); break;
-        default: apply_load_x<NTM, 3>(it, lane, xr); if constexpr (SPLIT) apply_split_x<NTM, 3, XR>(xr, xw); break;
+        case 0: apply_load_x<NTM, 0>(it, lane, xr); break;
+        case 1: apply_load_x<NTM, 1>(it, lane, xr); break;
+        case 2: apply_load_x<NTM, 2>(it, lane, xr); break;
+        default: apply_load_x<NTM, 3>(it, lane, xr); break;
     }
     float4 stg[PPT];
     auto load_y = [&](int cb) {
@@ -538,15 +472,10 @@ __global__ __launch_bounds__(256) void k_apply_linv(TrsmBatch batch) {
         f32x16 acc[MC];
         const int c0 = cb * kApplyCols;
         switch (wave) {
-#define JOLT_APPLY_WAVE(W)                                                   \
-    if constexpr (SPLIT) apply_mul_split<NTM, W, MC, XR>(xw, ys, lane, acc); \
-    else apply_mul<NTM, W, MC>(xr, ys, lane, acc);                           \
-    apply_store<NTM, W, MC>(it, lane, c0, acc);
-            case 0: JOLT_APPLY_WAVE(0) break;
-            case 1: JOLT_APPLY_WAVE(1) break;
-            case 2: JOLT_APPLY_WAVE(2) break;
-            default: JOLT_APPLY_WAVE(3) break;
-#undef JOLT_APPLY_WAVE
+            case 0: apply_mul<NTM, 0, MC>(xr, ys, lane, acc); apply_store<NTM, 0, MC>(it, lane, c0, acc); break;
+            case 1: apply_mul<NTM, 1, MC>(xr, ys, lane, acc); apply_store<NTM, 1, MC>(it, lane, c0, acc); break;
+            case 2: apply_mul<NTM, 2, MC>(xr, ys, lane, acc); apply_store<NTM, 2, MC>(it, lane, c0, acc); break;
+            default: apply_mul<NTM, 3, MC>(xr, ys, lane, acc); apply_store<NTM, 3, MC>(it, lane, c0, acc); break;
         }
         if (next >= ncb) break;
         store_y(sh + (buf ^ 1) * P * kApplyCols);
@@ -567,12 +496,9 @@ static hipError_t orth_lds_attrs() {
     if (state == hipErrorNotReady) {
         hipError_t e = allow_lds(reinterpret_cast<const void *>(k_chol_inv<false, CholBatch>));
         if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_chol_inv<false, CholTable>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<7, false>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<8, false>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<9, false>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<7, true>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<8, true>));
-        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<9, true>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<7>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<8>));
+        if (e == hipSuccess) e = allow_lds(reinterpret_cast<const void *>(k_apply_linv<9>));
         state = e;
     }
     return state;
@@ -603,13 +529,12 @@ hipError_t launch_chol_inv(const CholItem *host, const CholTable &dev, int maxK,
 }
 
 template <int NTM>
-static void apply_launch(const TrsmBatch &b, int gx, bool split, hipStream_t s) {
+static void apply_launch(const TrsmBatch &b, int gx, hipStream_t s) {
     const size_t lds = (size_t)2 * 32 * NTM * kApplyCols * sizeof(float);
-    if (split) hipLaunchKernelGGL((k_apply_linv<NTM, true>), dim3(gx, b.n), dim3(256), lds, s, b);
-    else hipLaunchKernelGGL((k_apply_linv<NTM, false>), dim3(gx, b.n), dim3(256), lds, s, b);
+    hipLaunchKernelGGL(k_apply_linv<NTM>, dim3(gx, b.n), dim3(256), lds, s, b);
 }
 
-hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s, bool split) {
+hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s) {
     if (b.n <= 0) return hipSuccess;
     if (maxK > kCholWideMaxK) return hipErrorInvalidValue;
     for (int i = 0; i < b.n; ++i)
@@ -623,15 +548,15 @@ hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream
     const int ncb = (maxLen + kApplyCols - 1) / kApplyCols;
     const int gx = std::max(1, std::min(ncb, (256 + b.n - 1) / b.n));
     switch (ntm) {
-        case 1: apply_launch<1>(b, gx, split, s); break;
-        case 2: apply_launch<2>(b, gx, split, s); break;
-        case 3: apply_launch<3>(b, gx, split, s); break;
-        case 4: apply_launch<4>(b, gx, split, s); break;
-        case 5: apply_launch<5>(b, gx, split, s); break;
-        case 6: apply_launch<6>(b, gx, split, s); break;
-        case 7: apply_launch<7>(b, gx, split, s); break;
-        case 8: apply_launch<8>(b, gx, split, s); break;
-        default: apply_launch<9>(b, gx, split, s); break;
+        case 1: apply_launch<1>(b, gx, s); break;
+        case 2: apply_launch<2>(b, gx, s); break;
+        case 3: apply_launch<3>(b, gx, s); break;
+        case 4: apply_launch<4>(b, gx, s); break;
+        case 5: apply_launch<5>(b, gx, s); break;
+        case 6: apply_launch<6>(b, gx, s); break;
+        case 7: apply_launch<7>(b, gx, s); break;
+        case 8: apply_launch<8>(b, gx, s); break;
+        default: apply_launch<9>(b, gx, s); break;
     }
     return hipGetLastError();
 }

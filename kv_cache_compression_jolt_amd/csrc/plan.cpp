@@ -618,9 +618,7 @@ jolt_status orth_rows(const Ctx &c, int nb, float **y, float **gram, float **gpa
                        }
                    },
                    [&](const TrsmBatch &b) {
-                       // the second pass of CholeskyQR2 applies an L^-1 close to the identity
-                       // to rows orthonormal to a few ulp: split operands on the bf16 MFMA
-                       return maxK <= kCholWideMaxK ? launch_apply_linv(b, maxK, maxLen, c.st, pass == 1)
+                       return maxK <= kCholWideMaxK ? launch_apply_linv(b, maxK, maxLen, c.st)
                                                     : launch_trsm(b, maxK, maxLen, c.st);
                    })),
                "orth L^-1 Y");

@@ -106,9 +106,7 @@ struct TrsmItem {
 struct TrsmBatch { TrsmItem it[kMaxBatch]; int n; };
 hipError_t launch_trsm(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
 // y <- X y with X = L^{-1} lower triangular (in place; k <= 600)
-// split: the products on the bf16 MFMA from hi/lo-split operands, for inputs
-// already orthonormal to a few ulp (the second pass of CholeskyQR2)
-hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s, bool split = false);
+hipError_t launch_apply_linv(const TrsmBatch &b, int maxK, int maxLen, hipStream_t s);
 constexpr int kCholInverseMaxK = 192;     // the inverse factor's working square in LDS
 constexpr int kCholWideMaxK = 288;        // ... or in the item's work buffer
 // the fused elimination behind launch_cholesky for the inverse != 0 items
