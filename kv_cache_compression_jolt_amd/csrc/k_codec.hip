@@ -1022,10 +1022,14 @@ struct CodecShape {
     static bool wl(int maxRtp) { return wt_lds(maxRtp) + 2 * D / 16 * 16 <= 160 * 1024; }
 };
 
+// Token ranges per (item, layer-head): split only as far as about 512
+// workgroups per launch (two per CU), each staging W~ once; at 512 pairs and
+// more a workgroup takes all of a layer-head's tokens (measured against 1024
+// and 2048 workgroups: fewer stagings, longer tile loops win).
 static dim3 codec_grid(const CodecBatch &b, int maxT, int maxLH, int nw, int &tpw) {
     const int tiles = (maxT + 31) / 32;
     const int pairs = std::max(1, maxLH * b.n);
-    const int split = std::max(1, std::min((1024 + pairs - 1) / pairs, tiles / nw));
+    const int split = std::max(1, std::min((512 + pairs - 1) / pairs, tiles / nw));
     tpw = 32 * ((tiles + split - 1) / split);
     return dim3((maxT + tpw - 1) / tpw, maxLH, b.n);
 }
